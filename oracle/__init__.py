@@ -1,0 +1,124 @@
+"""fp64 CPU oracle of the PFA layer chain (ctypes wrapper over ``pfa_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test-suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may use it; the HIP library never does.
+
+``layer`` computes one PFA layer (steps listed in ``pfa_oracle.c``) for a list of
+window-heads; ``chain`` runs the layers of one chain for a list of window-heads,
+feeding each layer's (I, A) to the next, all in fp64.
+"""
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_DIR, "pfa_oracle.c")
+_LIB = os.path.join(_DIR, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (OpenMP over window-heads)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        lib.oracle_layer.argtypes = [i32] * 7 + [P, P, P, P, i32, P, i32, i32, i32, P, i64, P, P, P, P, P]
+        lib.oracle_layer.restype = ctypes.c_int
+        lib.oracle_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def threads() -> int:
+    return _load().oracle_threads()
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def layer(Q, K, V, *, win, shift, K_l, I_prev=None, A_prev=None, i_shared=False,
+          prev_compact=False, wh_list=None, forced_keep=None, want_keys=False, O_out=None):
+    """One PFA layer in fp64.
+
+    Q, K, V: [B, heads, H, W, d] arrays (any float dtype; widened to fp64).
+    I_prev: [B, heads|1, nwin, N, K_prev] int32 or None (all slots, K_prev = N).
+    A_prev: [B, heads, nwin, N, K_prev] or None (all ones).
+    prev_compact: I_prev/A_prev are [n_wh, N, K_prev], aligned with wh_list.
+    Returns dict with I [n_wh, N, K_l] int32, A [n_wh, N, K_l] fp64,
+    O [B, heads, H, W, d] fp64 (NaN where not computed), optionally keys
+    [n_wh, N, K_prev] = ln P'.
+    """
+    lib = _load()
+    Q = np.ascontiguousarray(Q, dtype=np.float64)
+    K = np.ascontiguousarray(K, dtype=np.float64)
+    V = np.ascontiguousarray(V, dtype=np.float64)
+    B, heads, H, W, d = Q.shape
+    N = win * win if win else H * W
+    nwin = (H // win) * (W // win) if win else 1
+    if I_prev is not None:
+        I_prev = np.ascontiguousarray(I_prev, dtype=np.int32)
+        K_prev = I_prev.shape[-1]
+    else:
+        K_prev = N
+    if A_prev is not None:
+        A_prev = np.ascontiguousarray(A_prev, dtype=np.float64)
+        assert A_prev.shape[-1] == K_prev
+    if wh_list is None:
+        wl = None
+        n_wh = B * heads * nwin
+    else:
+        wl = np.ascontiguousarray(wh_list, dtype=np.int64)
+        n_wh = len(wl)
+    fk = None if forced_keep is None else np.ascontiguousarray(forced_keep, dtype=np.int32)
+    I_out = np.empty((n_wh, N, K_l), dtype=np.int32)
+    A_out = np.empty((n_wh, N, K_l), dtype=np.float64)
+    keys = np.empty((n_wh, N, K_prev), dtype=np.float64) if want_keys else None
+    if O_out is None:
+        O_out = np.full(Q.shape, np.nan, dtype=np.float64)
+    rc = lib.oracle_layer(B, heads, H, W, d, win, shift, _ptr(Q), _ptr(K), _ptr(V),
+                          _ptr(I_prev), int(bool(i_shared)), _ptr(A_prev), int(bool(prev_compact)),
+                          K_prev, K_l,
+                          _ptr(wl), n_wh, _ptr(fk), _ptr(I_out), _ptr(A_out), _ptr(keys),
+                          _ptr(O_out))
+    if rc != 0:
+        raise ValueError("oracle_layer rejected the sizes")
+    out = {"I": I_out, "A": A_out, "O": O_out}
+    if want_keys:
+        out["keys"] = keys
+    return out
+
+
+def chain(layers_qkv, *, win, shifts, Ks, wh_list=None):
+    """Run a whole chain: layer 0 dense (K^1 = Ks[0], no previous map), then each
+    later layer on the previous layer's (I, A). ``layers_qkv`` is a list of
+    (Q, K, V) arrays. Returns the list of per-layer output dicts (compact rows
+    over ``wh_list``)."""
+    Q0 = layers_qkv[0][0]
+    B, heads, H, W, _ = Q0.shape
+    nwin = (H // win) * (W // win) if win else 1
+    wl = np.arange(B * heads * nwin) if wh_list is None else np.asarray(wh_list)
+    outs = []
+    I_prev = A_prev = None
+    for l, (Q, K, V) in enumerate(layers_qkv):
+        r = layer(Q, K, V, win=win, shift=shifts[l], K_l=Ks[l], I_prev=I_prev, A_prev=A_prev,
+                  prev_compact=True, wh_list=wl)
+        outs.append(r)
+        I_prev, A_prev = r["I"], r["A"]
+    return outs

@@ -1,0 +1,414 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test names the mistake it is there to catch. Sources: "Progressive Focused
+Transformer for Single Image Super-Resolution" paper notes (sections "Progressive
+attention across layers", "Sparse matrix multiplication", "Progressive focused
+resource allocation strategy", "Key findings"), and "From Local Windows to
+Adaptive Candidates via Individualized Exploratory" (individualized-attention
+paragraph: the index-matrix attention reduces to global self-attention when I
+covers all tokens and to window self-attention when I is one window).
+"""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_progressive_window_amd import inputs, workloads
+from tests.brute import masked_dense_layer, window_rows
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TOL = 1e-11
+
+
+def rnd(shape, seed):
+    return np.random.Generator(np.random.PCG64(seed)).standard_normal(shape)
+
+
+def rand_candidates(N, K_prev, seed, sort=False):
+    g = np.random.Generator(np.random.PCG64(seed))
+    C = np.stack([g.permutation(N)[:K_prev] for _ in range(N)]).astype(np.int32)
+    return np.sort(C, axis=1).astype(np.int32) if sort else C
+
+
+def rand_prev_map(N, K_prev, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    a = g.random((N, K_prev)) + 1e-3
+    return a / a.sum(axis=1, keepdims=True)
+
+
+def one_wh(N_side, d, seed):
+    """Q, K, V for one unshifted window-head: [1, 1, w, w, d]."""
+    return [rnd((1, 1, N_side, N_side, d), seed + t) for t in range(3)]
+
+
+def oracle_rows(r, n, K_l):
+    return r["I"][n], r["A"][n]
+
+
+def dense_from_rows(I, A, N):
+    D = np.zeros((I.shape[0], N))
+    for i in range(I.shape[0]):
+        D[i, I[i]] = A[i]
+    return D
+
+
+# --------------------------------------------------------------------------
+# P1: with K^l = N and no previous map the layer is textbook softmax attention.
+# Catches: a dropped or wrong 1/sqrt(d) scale, a transposed Q/K, a softmax over
+# the wrong axis, an O written to the wrong pixel.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("w,d", [(4, 8), (8, 16), (16, 32)])
+def test_dense_equals_sdpa(w, d):
+    Q, K, V = (rnd((2, 3, 2 * w, w, d), 10 + t) for t in range(3))
+    r = oracle.layer(Q, K, V, win=w, shift=0, K_l=w * w)
+    # independent reference: torch SDPA in float64 on each window
+    for b in range(2):
+        for h in range(3):
+            for wy in range(2):
+                q = torch.from_numpy(window_rows(Q, b, h, wy, 0, w))
+                k = torch.from_numpy(window_rows(K, b, h, wy, 0, w))
+                v = torch.from_numpy(window_rows(V, b, h, wy, 0, w))
+                ref = torch.nn.functional.scaled_dot_product_attention(q[None], k[None], v[None])[0]
+                got = window_rows(r["O"], b, h, wy, 0, w)
+                np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-12)
+                n = ((b * 3 + h) * 2 + wy) * 1
+                att = torch.softmax(q @ k.T / np.sqrt(d), dim=1).numpy()
+                np.testing.assert_allclose(dense_from_rows(r["I"][n], r["A"][n], w * w), att,
+                                           rtol=0, atol=1e-14)
+                assert (r["I"][n] == np.arange(w * w)[None, :]).all()
+
+
+# --------------------------------------------------------------------------
+# P2: the SMM over the candidate list equals masked dense attention (brute force)
+# on tiny windows, across keep pairs. Catches: scores taken at the wrong
+# candidate, a missing Hadamard factor, a wrong Norm, a wrong renormalisation,
+# a top-K that keeps the smallest entries.
+# --------------------------------------------------------------------------
+CASES = [
+    # (w, d, K_prev or None for dense, K_l, sorted candidates)
+    (4, 8, None, 16, True), (4, 8, None, 5, True), (4, 8, None, 1, True),
+    (4, 8, 8, 8, False), (4, 8, 8, 4, False), (4, 8, 12, 3, True),
+    (8, 16, None, 64, True), (8, 16, None, 16, True), (8, 16, 32, 16, False),
+    (8, 16, 16, 8, True), (8, 16, 64, 7, False),
+    (16, 16, None, 256, True), (16, 16, None, 64, True), (16, 16, 64, 32, True),
+    (16, 16, 128, 1, False),
+]
+
+
+@pytest.mark.parametrize("w,d,K_prev,K_l,sort", CASES)
+def test_smm_equals_masked_dense(w, d, K_prev, K_l, sort):
+    N = w * w
+    Q, K, V = one_wh(w, d, 100 + w + d + K_l)
+    if K_prev is None:
+        C = a = None
+    else:
+        C = rand_candidates(N, K_prev, 7 * K_prev + K_l, sort=sort)
+        a = rand_prev_map(N, K_prev, 3 * K_prev + K_l)
+    r = oracle.layer(Q, K, V, win=w, shift=0, K_l=K_l,
+                     I_prev=None if C is None else C.reshape(1, 1, 1, N, -1),
+                     A_prev=None if a is None else a.reshape(1, 1, 1, N, -1))
+    q, k, v = (window_rows(x, 0, 0, 0, 0, w) for x in (Q, K, V))
+    keep, Ad, Od = masked_dense_layer(q, k, v, C, a, K_l)
+    I, A = r["I"][0], r["A"][0]
+    for i in range(N):
+        assert sorted(I[i].tolist()) == sorted(np.nonzero(keep[i])[0].tolist())
+    np.testing.assert_allclose(A, np.take_along_axis(Ad, I.astype(np.int64), axis=1), rtol=TOL, atol=0)
+    np.testing.assert_allclose(window_rows(r["O"], 0, 0, 0, 0, w), Od, rtol=0, atol=TOL)
+
+
+# --------------------------------------------------------------------------
+# P3: closed form of the chain. Every A_cal is a softmax and every Norm divides
+# by a row constant, so A^l = softmax over I^l of the cumulative score
+# S^l = s^1 + ... + s^l, and I^l = top-K_l of S^l within I^{l-1}. Catches: a
+# Hadamard product with the wrong layer's map, a Norm that is not a row scaling,
+# a renormalisation over the wrong set, a dropped exponent.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("w,d,Ks", [(8, 8, [64, 16, 8, 4]), (16, 16, [256, 64, 32, 16, 8]),
+                                    (8, 4, [64, 32, 32, 5, 1])])
+def test_chain_equals_cumulative_score(w, d, Ks):
+    N = w * w
+    layers = [one_wh(w, d, 1000 + 10 * l) for l in range(len(Ks))]
+    outs = oracle.chain(layers, win=w, shifts=[0] * len(Ks), Ks=Ks)
+    S = np.zeros((N, N))
+    cand = np.ones((N, N), bool)
+    for l, (Q, K, V) in enumerate(layers):
+        q, k, v = (window_rows(x, 0, 0, 0, 0, w) for x in (Q, K, V))
+        S = S + (q @ k.T) / np.sqrt(d)
+        new = np.zeros((N, N), bool)
+        for i in range(N):
+            c = np.nonzero(cand[i])[0]
+            order = c[np.lexsort((c, -S[i, c]))]
+            new[i, order[:Ks[l]]] = True
+        cand = new
+        E = np.where(cand, np.exp(S - np.where(cand, S, -np.inf).max(1, keepdims=True)), 0.0)
+        A = E / E.sum(1, keepdims=True)
+        I_o, A_o = outs[l]["I"][0], outs[l]["A"][0]
+        for i in range(N):
+            assert set(I_o[i].tolist()) == set(np.nonzero(cand[i])[0].tolist()), (l, i)
+        np.testing.assert_allclose(A_o, np.take_along_axis(A, I_o.astype(np.int64), 1), rtol=1e-9)
+        np.testing.assert_allclose(window_rows(outs[l]["O"], 0, 0, 0, 0, w), A @ v, atol=1e-11)
+
+
+# --------------------------------------------------------------------------
+# P4/P5: invariants on a multi-window, multi-head chain: rows sum to 1, I^l is a
+# subset of I^{l-1} kept in its order, |I^l| = K_l, indices distinct and in
+# range, A > 0, and every kept weight >= every dropped weight (ties: lower j).
+# --------------------------------------------------------------------------
+def test_chain_invariants_and_topk_optimality():
+    w, d, Ks = 8, 16, [64, 32, 16, 8]
+    B, heads, H, W = 2, 2, 16, 24
+    layers = [tuple(rnd((B, heads, H, W, d), 50 + 3 * l + t) for t in range(3)) for l in range(4)]
+    shifts = [0, 4, 0, 4]
+    prevI = None
+    I_prev = A_prev = None
+    n_wh = B * heads * (H // w) * (W // w)
+    for l, (Q, K, V) in enumerate(layers):
+        r = oracle.layer(Q, K, V, win=w, shift=shifts[l], K_l=Ks[l], I_prev=I_prev, A_prev=A_prev,
+                         prev_compact=True, wh_list=np.arange(n_wh), want_keys=True)
+        I, A, keys = r["I"], r["A"], r["keys"]
+        assert I.shape == (n_wh, w * w, Ks[l])
+        np.testing.assert_allclose(A.sum(-1), 1.0, rtol=1e-13)
+        assert (A > 0).all() and (I >= 0).all() and (I < w * w).all()
+        for n in range(n_wh):
+            for i in range(0, w * w, 7):
+                row = I[n, i].tolist()
+                assert len(set(row)) == len(row)
+                C = list(range(w * w)) if prevI is None else prevI[n, i].tolist()
+                pos = [C.index(j) for j in row]
+                assert pos == sorted(pos)          # kept subsequence of C_i, C_i order
+                kept = set(row)
+                kk = [keys[n, i, c] for c in range(len(C)) if C[c] in kept]
+                dk = [(keys[n, i, c], C[c]) for c in range(len(C)) if C[c] not in kept]
+                if dk:
+                    assert min(kk) >= max(x for x, _ in dk)
+        assert np.isfinite(r["O"]).all()
+        prevI, I_prev, A_prev = I, I, A
+
+
+# --------------------------------------------------------------------------
+# P6: K_l = K_prev keeps every candidate in order and A^l = P' = exp(key).
+# --------------------------------------------------------------------------
+def test_full_keep_is_identity_selection():
+    w, d, N = 8, 8, 64
+    Q, K, V = one_wh(w, d, 77)
+    C = rand_candidates(N, 20, 5)
+    a = rand_prev_map(N, 20, 6)
+    r = oracle.layer(Q, K, V, win=w, shift=0, K_l=20, I_prev=C.reshape(1, 1, 1, N, 20),
+                     A_prev=a.reshape(1, 1, 1, N, 20), want_keys=True)
+    assert (r["I"][0] == C).all()
+    np.testing.assert_allclose(r["A"][0], np.exp(r["keys"][0]), rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# P7: metamorphic invariances. (a) permuting a row's (I_prev, A_prev) slots leaves
+# the kept set and weights unchanged and the output order follows I_prev;
+# (b) scaling a row of A_prev by c > 0 changes nothing (Norm); (c) adding one
+# vector u to every key adds a per-row constant q_i.u/sqrt(d) to the scores,
+# which the softmax and Norm remove. Catches: ties or outputs that depend on
+# storage order, an unnormalised Hadamard product, a softmax domain that is not a
+# row-constant-free set.
+# --------------------------------------------------------------------------
+def test_metamorphic_permute_scale_shiftkeys():
+    w, d, N, Kp, Kl = 8, 16, 64, 32, 9
+    Q, K, V = one_wh(w, d, 91)
+    C = rand_candidates(N, Kp, 12, sort=True)
+    a = rand_prev_map(N, Kp, 13)
+    base = oracle.layer(Q, K, V, win=w, shift=0, K_l=Kl, I_prev=C.reshape(1, 1, 1, N, Kp),
+                        A_prev=a.reshape(1, 1, 1, N, Kp))
+    g = np.random.Generator(np.random.PCG64(3))
+    perm = np.stack([g.permutation(Kp) for _ in range(N)])
+    Cp = np.take_along_axis(C, perm, 1)
+    ap = np.take_along_axis(a, perm, 1) * (1.0 + np.arange(N))[:, None]     # (a) + (b)
+    Ku = K + rnd((d,), 4)[None, None, None, None, :]                           # (c)
+    r = oracle.layer(Q, Ku, V, win=w, shift=0, K_l=Kl, I_prev=Cp.reshape(1, 1, 1, N, Kp),
+                     A_prev=ap.reshape(1, 1, 1, N, Kp))
+    for i in range(N):
+        m0 = dict(zip(base["I"][0, i].tolist(), base["A"][0, i].tolist()))
+        m1 = dict(zip(r["I"][0, i].tolist(), r["A"][0, i].tolist()))
+        assert m0.keys() == m1.keys()
+        for j in m0:
+            assert abs(m0[j] - m1[j]) <= 1e-12 * m0[j]
+        order = [Cp[i].tolist().index(j) for j in r["I"][0, i]]
+        assert order == sorted(order)
+    np.testing.assert_allclose(r["O"], base["O"], atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# P8: a cyclic shift applied by index remap equals rolling Q/K/V by -s, running
+# the unshifted layer and rolling O back by +s (slot-for-slot passing of I/A).
+# Catches: the shift applied in the wrong direction or on one axis only.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("s", [2, 4])
+def test_shift_equals_roll(s):
+    w, d, Kp, Kl = 8, 8, 16, 6
+    B, heads, H, W = 1, 2, 16, 24
+    Q, K, V = (rnd((B, heads, H, W, d), 200 + t) for t in range(3))
+    n_wh = B * heads * (H // w) * (W // w)
+    N = w * w
+    C = np.stack([rand_candidates(N, Kp, 30 + n) for n in range(n_wh)])
+    a = np.stack([rand_prev_map(N, Kp, 60 + n) for n in range(n_wh)])
+    shifted = oracle.layer(Q, K, V, win=w, shift=s, K_l=Kl, I_prev=C, A_prev=a,
+                           prev_compact=True, wh_list=np.arange(n_wh))
+    roll = lambda x, k: np.roll(x, (k, k), axis=(2, 3))
+    plain = oracle.layer(roll(Q, -s), roll(K, -s), roll(V, -s), win=w, shift=0, K_l=Kl,
+                         I_prev=C, A_prev=a, prev_compact=True, wh_list=np.arange(n_wh))
+    assert (shifted["I"] == plain["I"]).all()
+    np.testing.assert_allclose(shifted["A"], plain["A"], rtol=1e-13)
+    np.testing.assert_allclose(shifted["O"], roll(plain["O"], s), atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# P9: global mode. I covering all tokens gives global self-attention; I listing
+# the query's own window gives window self-attention.
+# --------------------------------------------------------------------------
+def test_global_mode_reductions():
+    B, heads, H, W, d = 1, 2, 8, 8, 8
+    N = H * W
+    Q, K, V = (rnd((B, heads, H, W, d), 300 + t) for t in range(3))
+    allI = np.tile(np.arange(N, dtype=np.int32), (N, 1)).reshape(1, 1, 1, N, N)
+    r = oracle.layer(Q, K, V, win=0, shift=0, K_l=N, I_prev=allI, i_shared=True)
+    for h in range(heads):
+        q, k, v = (torch.from_numpy(x[0, h].reshape(N, d)) for x in (Q, K, V))
+        ref = torch.nn.functional.scaled_dot_product_attention(q[None], k[None], v[None])[0]
+        np.testing.assert_allclose(r["O"][0, h].reshape(N, d), ref.numpy(), atol=1e-12)
+    w = 4
+    winI = np.empty((N, w * w), dtype=np.int32)
+    for y in range(H):
+        for x in range(W):
+            wy, wx = y // w, x // w
+            winI[y * W + x] = [(wy * w + t // w) * W + wx * w + t % w for t in range(w * w)]
+    g = oracle.layer(Q, K, V, win=0, shift=0, K_l=5, I_prev=winI.reshape(1, 1, 1, N, w * w),
+                     i_shared=True)
+    wm = oracle.layer(Q, K, V, win=w, shift=0, K_l=5)
+    np.testing.assert_allclose(g["O"], wm["O"], atol=1e-13)
+    # map window-mode slot indices to raster indices and compare the kept sets
+    nwx = W // w
+    for n in range(heads * (H // w) * nwx):
+        h, wy, wx = n // ((H // w) * nwx), (n // nwx) % (H // w), n % nwx
+        for t in range(w * w):
+            y, x = wy * w + t // w, wx * w + t % w
+            want = [(wy * w + j // w) * W + wx * w + j % w for j in wm["I"][n, t]]
+            assert g["I"][h, y * W + x].tolist() == want
+            np.testing.assert_allclose(g["A"][h, y * W + x], wm["A"][n, t], rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Hand-derived rational example (d = 1, scores are logs of integers, so every
+# softmax weight is a ratio of integers). Derivation:
+#  layer 1 (dense, K=4): q = [1,2,1,2], k = ln[1,2,3,4], v = [10,20,30,40]
+#     q=1 rows: A = [1,2,3,4]/10, O = 300/10 = 30
+#     q=2 rows: A = [1,4,9,16]/30, O = 1000/30
+#  layer 2 (K=2): q = 1, k = ln[4,3,2,1], v = [1,2,3,4]
+#     q=1 rows: P ~ [1*4, 2*3, 3*2, 4*1] -> keep j=1,2, A = [1/2, 1/2], O = 5/2
+#     q=2 rows: P ~ [4, 12, 18, 16]       -> keep j=2,3, A = [18, 16]/34, O = 118/34
+#  layer 3 (K=1): q = 1, k = ln[1,1,5,1], v = [7,8,9,10]
+#     all rows keep j=2 (weight 5x the other candidate's), A = [1], O = 9
+# Catches any slip in Hadamard/Norm/renorm bookkeeping with exact expected values.
+# --------------------------------------------------------------------------
+def test_hand_derived_rational_chain():
+    F = Fraction
+    def t(vals):
+        return np.array(vals, np.float64).reshape(1, 1, 2, 2, 1)
+    layers = [
+        (t([1, 2, 1, 2]), t(np.log([1, 2, 3, 4])), t([10, 20, 30, 40])),
+        (t([1, 1, 1, 1]), t(np.log([4, 3, 2, 1])), t([1, 2, 3, 4])),
+        (t([1, 1, 1, 1]), t(np.log([1, 1, 5, 1])), t([7, 8, 9, 10])),
+    ]
+    outs = oracle.chain(layers, win=2, shifts=[0, 0, 0], Ks=[4, 2, 1])
+    exp1 = {1: ([0, 1, 2, 3], [F(1, 10), F(2, 10), F(3, 10), F(4, 10)], F(30)),
+            2: ([0, 1, 2, 3], [F(1, 30), F(4, 30), F(9, 30), F(16, 30)], F(1000, 30))}
+    exp2 = {1: ([1, 2], [F(1, 2), F(1, 2)], F(5, 2)), 2: ([2, 3], [F(18, 34), F(16, 34)], F(118, 34))}
+    exp3 = {1: ([2], [F(1)], F(9)), 2: ([2], [F(1)], F(9))}
+    qs = [1, 2, 1, 2]
+    for l, ex in enumerate([exp1, exp2, exp3]):
+        for i in range(4):
+            I_w, A_w, O_w = ex[qs[i]]
+            assert outs[l]["I"][0, i].tolist() == I_w
+            np.testing.assert_allclose(outs[l]["A"][0, i], [float(x) for x in A_w], rtol=1e-14)
+            np.testing.assert_allclose(outs[l]["O"].reshape(4)[i], float(O_w), rtol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Ties go to the lower index value j, whatever the storage order of I_prev, and
+# the output lists kept entries in I_prev order. All scores are 0 (k = 0), so
+# every softmax weight is exactly 1/K_prev and the ties below are exact.
+# --------------------------------------------------------------------------
+def test_ties_break_to_lower_index():
+    z = np.zeros((1, 1, 2, 2, 1))
+    V = np.array([1.0, 2.0, 3.0, 4.0]).reshape(1, 1, 2, 2, 1)
+    C = np.array([[3, 1, 0, 2], [0, 3, 2, 1], [2, 0, 3, 1], [1, 2, 3, 0]], np.int32)
+    a = np.array([[.25, .25, .25, .25], [.1, .3, .3, .3], [.5, .5, .5, .5], [.2, .4, .2, .2]])
+    r = oracle.layer(z + 1.0, z, V, win=2, shift=0, K_l=2, I_prev=C.reshape(1, 1, 1, 4, 4),
+                     A_prev=a.reshape(1, 1, 1, 4, 4))
+    assert r["I"][0].tolist() == [[1, 0], [2, 1], [0, 1], [2, 0]]
+    np.testing.assert_allclose(r["A"][0], [[.5, .5], [.5, .5], [.5, .5], [2 / 3, 1 / 3]], rtol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# Conditional mode: forcing the oracle's own kept set reproduces it; forcing an
+# arbitrary set matches the brute-force renormalisation over that set.
+# --------------------------------------------------------------------------
+def test_conditional_mode():
+    w, d, N, Kp, Kl = 8, 8, 64, 24, 6
+    Q, K, V = (x for x in one_wh(w, d, 400))
+    C = rand_candidates(N, Kp, 41)
+    a = rand_prev_map(N, Kp, 42)
+    kw = dict(win=w, shift=0, K_l=Kl, I_prev=C.reshape(1, 1, 1, N, Kp), A_prev=a.reshape(1, 1, 1, N, Kp))
+    base = oracle.layer(Q, K, V, **kw)
+    same = oracle.layer(Q, K, V, forced_keep=base["I"], **kw)
+    assert (same["I"] == base["I"]).all()
+    np.testing.assert_allclose(same["A"], base["A"], rtol=1e-15)
+    forced = np.stack([C[i, [0, 3, 5, 7, 11, 13]] for i in range(N)])
+    f = oracle.layer(Q, K, V, forced_keep=forced[None], **kw)
+    keep = np.zeros((N, N), bool)
+    for i in range(N):
+        keep[i, forced[i]] = True
+    q, k, v = (window_rows(x, 0, 0, 0, 0, w) for x in (Q, K, V))
+    _, Ad, Od = masked_dense_layer(q, k, v, C, a, keep_override=keep)
+    np.testing.assert_allclose(f["A"][0], np.take_along_axis(Ad, f["I"][0].astype(np.int64), 1), rtol=1e-12)
+    np.testing.assert_allclose(window_rows(f["O"], 0, 0, 0, 0, w), Od, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# The numbers the pages print: the keep schedule of the workloads and the 6.25%
+# of the compute left after four alpha = 0.5 decay steps (kept counts 256 -> 16).
+# --------------------------------------------------------------------------
+def test_pages_numbers():
+    g = json.load(open(os.path.join(HERE, "golden", "pages_numbers.json")))
+    for wl in (workloads.MAP256, workloads.PATCH64, workloads.MAP640):
+        assert wl.K == g["keep_schedule"]["value"]
+        assert wl.win == g["window_side"]["value"] and wl.K[0] == wl.N
+    f = g["compute_after_four_half_steps"]
+    assert g["keep_schedule"]["value"][5] / g["keep_schedule"]["value"][1] == f["fraction"]
+    assert f["alpha"] ** f["steps"] == f["fraction"]
+    wl = workloads.MAP256
+    assert wl.pairs(5) / wl.pairs(1) == 32 / 1024        # layer 6 evaluates K^5 = 32 candidates
+    assert [wl.pairs(l) for l in range(6)] == [384 * 1024 * k for k in [1024, 1024, 256, 128, 64, 32]]
+
+
+# --------------------------------------------------------------------------
+# Host logic of the input recipe: bf16 rounding is round-to-nearest-even, and the
+# global index matrix has 64 distinct in-range indices per row with the token
+# itself and its in-map dilated neighbours present.
+# --------------------------------------------------------------------------
+def test_input_recipes():
+    x = np.array([1.0, 1.00390625, 1.005859375, 1.0078125 + 2 ** -9, -3.0e-3], np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    assert (inputs.bf16_round_bits(x) == ref).all()
+    wl = workloads.GLOBAL64
+    I = inputs.global_index(wl)
+    assert I.shape == (4096, 64) and I.min() >= 0 and I.max() < 4096
+    assert all(len(set(r.tolist())) == 64 for r in I)
+    for (y, x_) in [(0, 0), (31, 17), (63, 63), (20, 40)]:
+        row = set(I[y * 64 + x_].tolist())
+        for a in range(8):
+            for b in range(8):
+                yy, xx = y + 4 * (a - 4), x_ + 4 * (b - 4)
+                if 0 <= yy < 64 and 0 <= xx < 64:
+                    assert yy * 64 + xx in row
+    assert (inputs.global_index(wl) == I).all()     # seeded
