@@ -1,0 +1,120 @@
+/*
+ * pfa.h -- C ABI of the MI355X (gfx950) progressive focused attention (PFA)
+ * layer library, libpfa.so.
+ *
+ * A PFA layer (sources: "Progressive Focused Transformer for Single Image
+ * Super-Resolution" paper notes, sections "Progressive attention across layers",
+ * "Sparse matrix multiplication" and "Progressive focused resource allocation
+ * strategy"; "From Local Windows to Adaptive Candidates via Individualized
+ * Exploratory", individualized-attention paragraph) maps
+ *     (Q, K, V, I^{l-1}, A^{l-1})  ->  (I^l, A^l, O)
+ * per window-head: scaled scores q_i.k_j / sqrt(d) only over the candidate
+ * list I^{l-1}(i), a softmax over that list, the Hadamard product with
+ * A^{l-1}, an L1 row normalisation, the K^l largest entries kept (ties to the
+ * lower slot index j), a second row normalisation, and O_i = sum_j A_ij v_j.
+ * The first layer is dense in-window softmax attention (K^1 = N).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors are dense, C-contiguous, and live in device memory of the current HIP
+ * device; the caller allocates all of them. The library never allocates,
+ * frees or synchronises: it validates the arguments, enqueues kernels on
+ * `stream` (a hipStream_t; NULL = the null stream) and returns.
+ *
+ *   Q, K, V   [B, heads, H, W, d], element type `dtype` (fp32, or bf16 bits).
+ *   O         [B, heads, H, W, d] fp32.
+ *   window mode (win > 0): N = win*win tokens per window, nwin = (H/win)*(W/win)
+ *     windows; slot t of window (a, b) is pixel
+ *       ((a*win + t/win + shift) mod H, (b*win + t%win + shift) mod W),
+ *     i.e. the cyclic shift is applied by index remap, never by moving data.
+ *     I and A rows are indexed [B, heads, H/win, W/win, N, K] and hold slot
+ *     indices j in [0, N). I/A are passed slot-for-slot from layer to layer.
+ *   global mode (win = 0): one window of N = H*W tokens per (image, head),
+ *     slot = raster index y*W + x; I and A rows are [B, heads, N, K].
+ *
+ * Output rows of I^l list the kept candidates in their I^{l-1} order (as a
+ * subsequence), with A^l aligned; each A^l row sums to 1.
+ *
+ * Preconditions (not checked on the device): I^{l-1} values lie in [0, N) and
+ * are distinct within a row; A^{l-1} entries are finite, >= 0, and each row
+ * has a positive entry; outputs do not alias inputs.
+ *
+ * Errors: every entry point returns PFA_OK (0) or a negative code; nothing is
+ * enqueued when a code other than PFA_OK / PFA_ERR_HIP is returned.
+ * PFA_ERR_HIP reports a failed launch (hipGetLastError after the launch).
+ */
+#ifndef PFA_H
+#define PFA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PFA_OK 0
+#define PFA_ERR_INVALID (-1)     /* inconsistent sizes, NULL where required */
+#define PFA_ERR_UNSUPPORTED (-2) /* valid, but outside what the kernels handle */
+#define PFA_ERR_HIP (-3)         /* the HIP runtime reported an error */
+
+typedef enum { PFA_F32 = 0, PFA_BF16 = 1 } pfa_dtype;
+
+typedef struct {
+    int32_t B, heads, H, W, d; /* d must be 16 or 32 */
+    int32_t win;               /* window side (N = win*win <= 1024), 0 = global mode */
+    int32_t shift;             /* cyclic shift in [0, win); 0 in global mode */
+    int32_t dtype;             /* pfa_dtype of Q, K and V */
+} pfa_shape;
+
+/*
+ * Dense first layer (window mode only): softmax(q_i.k_j / sqrt(d)) over all N
+ * slots of the window ("Progressive focused resource allocation strategy":
+ * the first layer keeps every token and computes the complete map).
+ *
+ * K1 == N:  A_out  [B, heads, nwin, N, N] fp32 or NULL (then the map is not
+ *                  written: O-only mode);
+ *           I_out  [B, heads, nwin, N, N] int32 or NULL (row i is 0..N-1);
+ *           O_out  required. Needs win to be a multiple of 4.
+ * K1 <  N:  the K1 largest weights are kept and renormalised (as in a sparse
+ *           layer whose previous map is all ones); I_out and A_out
+ *           [.., N, K1] are required.
+ * Errors: PFA_ERR_INVALID for K1 outside [1, N], NULL Q/K/V/O, NULL I_out or
+ * A_out when K1 < N, H or W not a multiple of win, shift outside [0, win);
+ * PFA_ERR_UNSUPPORTED for win == 0, win > 32, win not a multiple of 4 when
+ * K1 == N, d not 16/32, unknown dtype.
+ */
+int pfa_dense_layer(const pfa_shape* shape, const void* Q, const void* K, const void* V,
+                    int32_t K1, int32_t* I_out, float* A_out, float* O_out, void* stream);
+
+/*
+ * Sparse layer l > 1 ("Sparse matrix multiplication": scores only where
+ * I^{l-1}(i, j) = 1; keep the top K^l).
+ *
+ * I_prev  [B, heads, nwin, N, K_prev] int32, or [B, 1, nwin, N, K_prev] when
+ *         i_prev_shared != 0 (one index matrix for every head), or NULL:
+ *         every slot 0..N-1 in order (then K_prev must equal N).
+ * A_prev  [B, heads, nwin, N, K_prev] fp32, or NULL (all ones: plain softmax
+ *         over the candidate list, e.g. the global individualized attention).
+ * K_l     kept per row, 1 <= K_l <= K_prev <= min(N, 1024).
+ * I_out, A_out  [B, heads, nwin, N, K_l] int32 / fp32, required.
+ * O_out   [B, heads, H, W, d] fp32, required.
+ * Errors: PFA_ERR_INVALID for inconsistent sizes or NULL outputs;
+ * PFA_ERR_UNSUPPORTED for d not 16/32, win > 32, K_prev > 1024, N >= 2^24 in
+ * global mode, unknown dtype.
+ */
+int pfa_sparse_layer(const pfa_shape* shape, const void* Q, const void* K, const void* V,
+                     const int32_t* I_prev, int32_t i_prev_shared, const float* A_prev,
+                     int32_t K_prev, int32_t K_l, int32_t* I_out, float* A_out, float* O_out,
+                     void* stream);
+
+/* Static string for a return code; never NULL. */
+const char* pfa_strerror(int code);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int pfa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PFA_H */

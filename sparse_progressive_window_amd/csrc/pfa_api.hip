@@ -1,0 +1,157 @@
+// C ABI of libpfa.so: argument validation, launch geometry, error mapping.
+// The calls and their contracts are documented in include/pfa.h.
+#include <math.h>
+
+#include "pfa.h"
+#include "pfa_kernels.h"
+
+namespace {
+
+using pfa::Geom;
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+bool geom_from_shape(const pfa_shape* s, Geom* g, int* code) {
+    *code = PFA_ERR_INVALID;
+    if (!s) return false;
+    if (s->B < 1 || s->heads < 1 || s->H < 1 || s->W < 1 || s->d < 1) return false;
+    if (s->dtype != PFA_F32 && s->dtype != PFA_BF16) {
+        *code = PFA_ERR_UNSUPPORTED;
+        return false;
+    }
+    if (s->d != 16 && s->d != 32) {
+        *code = PFA_ERR_UNSUPPORTED;
+        return false;
+    }
+    if (s->win < 0) return false;
+    g->B = s->B; g->heads = s->heads; g->H = s->H; g->W = s->W; g->d = s->d;
+    g->win = s->win; g->shift = s->shift;
+    if (s->win > 0) {
+        if (s->H % s->win || s->W % s->win) return false;
+        if (s->shift < 0 || s->shift >= s->win) return false;
+        if (s->win > 32) {
+            *code = PFA_ERR_UNSUPPORTED;
+            return false;
+        }
+        g->N = s->win * s->win;
+        g->nwy = s->H / s->win;
+        g->nwx = s->W / s->win;
+    } else {
+        if (s->shift != 0) return false;
+        if ((int64_t)s->H * s->W >= (1 << 24)) {
+            *code = PFA_ERR_UNSUPPORTED;
+            return false;
+        }
+        g->N = s->H * s->W;
+        g->nwy = g->nwx = 1;
+    }
+    *code = PFA_OK;
+    return true;
+}
+
+int elem_bytes(int dtype) { return dtype == PFA_F32 ? 4 : 2; }
+
+int kpt_for(int k_prev) {
+    int kpt = 1;
+    while (kpt * pfa::kWave < k_prev) kpt *= 2;
+    return kpt;
+}
+
+int64_t n_wh(const Geom& g) { return (int64_t)g.B * g.heads * g.nwy * g.nwx; }
+
+int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const void* V,
+               const int32_t* I_prev, int i_shared, const float* A_prev, int K_prev, int K_l,
+               int32_t* I_out, float* A_out, float* O_out, hipStream_t stream) {
+    pfa::SparseArgs a;
+    a.Q = Q; a.K = K; a.V = V;
+    a.I_prev = I_prev; a.A_prev = A_prev;
+    a.I_out = I_out; a.A_out = A_out; a.O_out = O_out;
+    a.g = g;
+    a.K_prev = K_prev; a.K_l = K_l;
+    a.i_shared = i_shared ? 1 : 0;
+    a.scale2 = (float)(1.4426950408889634 / sqrt((double)g.d));
+
+    const int rowb = g.d * elem_bytes(dtype);
+    const int scratch = pfa::kSparseWaves * pfa::kScratchEntries * 8;
+    pfa::SparseMode mode;
+    int lds = scratch;
+    if (g.win == 0) {
+        mode = pfa::kKVglobal;
+        a.rows_per_block = pfa::kSparseWaves * 16;
+    } else {
+        a.rows_per_block = g.N;
+        if (2 * g.N * rowb + scratch <= pfa::kLdsBytes) {
+            mode = pfa::kKVinLDS;
+            lds += 2 * g.N * rowb;
+        } else {
+            mode = pfa::kKinLDS;
+            lds += g.N * rowb;
+        }
+    }
+    a.blocks_per_wh = (g.N + a.rows_per_block - 1) / a.rows_per_block;
+    const int64_t grid = n_wh(g) * a.blocks_per_wh;
+    if (grid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
+    const hipError_t e =
+        pfa::launch_sparse(a, dtype, g.d, kpt_for(K_prev), mode, lds, (int)grid, stream);
+    return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pfa_sparse_layer(const pfa_shape* shape, const void* Q, const void* K, const void* V,
+                     const int32_t* I_prev, int32_t i_prev_shared, const float* A_prev,
+                     int32_t K_prev, int32_t K_l, int32_t* I_out, float* A_out, float* O_out,
+                     void* stream) {
+    Geom g;
+    int code;
+    if (!geom_from_shape(shape, &g, &code)) return code;
+    if (!Q || !K || !V || !I_out || !A_out || !O_out) return PFA_ERR_INVALID;
+    if (K_prev < 1 || K_prev > g.N || K_l < 1 || K_l > K_prev) return PFA_ERR_INVALID;
+    if (!I_prev && K_prev != g.N) return PFA_ERR_INVALID;
+    if (K_prev > 1024) return PFA_ERR_UNSUPPORTED;
+    return run_sparse(g, shape->dtype, Q, K, V, I_prev, i_prev_shared, A_prev, K_prev, K_l, I_out,
+                      A_out, O_out, static_cast<hipStream_t>(stream));
+}
+
+int pfa_dense_layer(const pfa_shape* shape, const void* Q, const void* K, const void* V, int32_t K1,
+                    int32_t* I_out, float* A_out, float* O_out, void* stream) {
+    Geom g;
+    int code;
+    if (!geom_from_shape(shape, &g, &code)) return code;
+    if (g.win == 0) return PFA_ERR_UNSUPPORTED;
+    if (!Q || !K || !V || !O_out) return PFA_ERR_INVALID;
+    if (K1 < 1 || K1 > g.N) return PFA_ERR_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K1 < g.N) {
+        if (!I_out || !A_out) return PFA_ERR_INVALID;
+        return run_sparse(g, shape->dtype, Q, K, V, nullptr, 0, nullptr, g.N, K1, I_out, A_out,
+                          O_out, s);
+    }
+    if (g.win % 4) return PFA_ERR_UNSUPPORTED;
+    pfa::DenseArgs a;
+    a.Q = Q; a.K = K; a.V = V;
+    a.A_out = A_out; a.O_out = O_out;
+    a.g = g;
+    a.scale2 = (float)(1.4426950408889634 / sqrt((double)g.d));
+    const int64_t grid = n_wh(g) * ((g.N + 63) / 64);
+    if (grid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
+    hipError_t e = pfa::launch_dense(a, shape->dtype, g.d, (int)grid, s);
+    if (e == hipSuccess && I_out) e = pfa::launch_iota_rows(I_out, n_wh(g) * g.N, g.N, s);
+    return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
+}
+
+const char* pfa_strerror(int code) {
+    switch (code) {
+        case PFA_OK: return "ok";
+        case PFA_ERR_INVALID: return "invalid argument";
+        case PFA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case PFA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown error code";
+    }
+}
+
+int pfa_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Kernel argument blocks and launchers (internal to libpfa.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pfa_device.h"
+
+namespace pfa {
+
+constexpr int kSparseWaves = 8;        // waves per sparse-layer workgroup
+constexpr int kScratchEntries = 512;   // (j, weight) entries per wave for the aggregation
+constexpr int kLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
+
+struct SparseArgs {
+    const void* Q;
+    const void* K;
+    const void* V;
+    const int32_t* I_prev;   // nullptr: all slots in order
+    const float* A_prev;     // nullptr: all ones
+    int32_t* I_out;
+    float* A_out;
+    float* O_out;
+    Geom g;
+    int K_prev, K_l;
+    int i_shared;
+    int rows_per_block, blocks_per_wh;
+    float scale2;            // log2(e) / sqrt(d): scores are kept in base-2 units
+};
+
+// Where K and V rows are read from.
+enum SparseMode { kKVinLDS = 0, kKinLDS = 1, kKVglobal = 2 };
+
+struct DenseArgs {
+    const void* Q;
+    const void* K;
+    const void* V;
+    float* A_out;            // nullptr: O-only
+    float* O_out;
+    Geom g;
+    float scale2;
+};
+
+hipError_t launch_sparse(const SparseArgs& a, int dtype, int D, int kpt, SparseMode mode,
+                         int lds_bytes, int grid, hipStream_t stream);
+hipError_t launch_dense(const DenseArgs& a, int dtype, int D, int grid, hipStream_t stream);
+hipError_t launch_iota_rows(int32_t* I, int64_t rows, int N, hipStream_t stream);
+
+}  // namespace pfa

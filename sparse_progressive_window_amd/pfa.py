@@ -1,0 +1,165 @@
+"""Thin Python binding of libpfa.so (ctypes): argument marshalling only.
+
+Every step of a layer runs in the HIP kernels behind the C ABI declared in
+``include/pfa.h``; this module allocates output tensors with torch, passes raw
+device pointers and the current HIP stream, and turns error codes into
+exceptions. There is no fallback: without the built library every call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpfa.so")
+_lib = None
+
+PFA_F32, PFA_BF16 = 0, 1
+
+
+class PfaShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "heads", "H", "W", "d", "win", "shift", "dtype")]
+
+
+class PfaError(RuntimeError):
+    def __init__(self, fn, code):
+        msg = load().pfa_strerror(code).decode()
+        super().__init__(f"{fn} failed with code {code}: {msg}")
+        self.code = code
+
+
+def load():
+    """Load libpfa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m sparse_progressive_window_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, i32 = ctypes.c_void_p, ctypes.c_int32
+        lib.pfa_dense_layer.argtypes = [ctypes.POINTER(PfaShape), P, P, P, i32, P, P, P, P]
+        lib.pfa_dense_layer.restype = ctypes.c_int
+        lib.pfa_sparse_layer.argtypes = [ctypes.POINTER(PfaShape), P, P, P, P, i32, P, i32, i32, P, P, P, P]
+        lib.pfa_sparse_layer.restype = ctypes.c_int
+        lib.pfa_strerror.argtypes = [ctypes.c_int]
+        lib.pfa_strerror.restype = ctypes.c_char_p
+        lib.pfa_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def version() -> int:
+    return load().pfa_version()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PFA_F32
+    if t.dtype == torch.bfloat16:
+        return PFA_BF16
+    raise TypeError(f"Q/K/V must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_qkv(Q, K, V):
+    for t in (Q, K, V):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 5:
+            raise ValueError("Q, K, V must be contiguous 5-d [B, heads, H, W, d] device tensors")
+        if t.shape != Q.shape or t.dtype != Q.dtype:
+            raise ValueError("Q, K, V must share shape and dtype")
+
+
+def make_shape(Q: torch.Tensor, win: int, shift: int) -> PfaShape:
+    B, heads, H, W, d = Q.shape
+    return PfaShape(B, heads, H, W, d, win, shift, _dtype_code(Q))
+
+
+def _prod(xs):
+    r = 1
+    for x in xs:
+        r *= x
+    return r
+
+
+def _geometry(Q, win):
+    B, heads, H, W, _ = Q.shape
+    if win:
+        return (B, heads, (H // win) * (W // win)), win * win
+    return (B, heads), H * W
+
+
+def _expect(t, numel, dtype, name):
+    """The C ABI sees raw pointers only: check every buffer's size here."""
+    if t is None:
+        return
+    if not t.is_cuda or not t.is_contiguous() or t.dtype != dtype or t.numel() != numel:
+        raise ValueError(f"{name} must be a contiguous {dtype} device tensor with {numel} elements, got "
+                         f"{tuple(t.shape)} {t.dtype}")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def dense_layer(Q, K, V, K1=None, *, win, shift=0, want_A=True, want_I=False, out=None):
+    """First (dense) layer. Returns (I, A, O); I and A are None when not requested
+    (K1 == N) and always returned when K1 < N. ``out`` = optional preallocated
+    (I or None, A or None, O)."""
+    _check_qkv(Q, K, V)
+    lead, N = _geometry(Q, win)
+    K1 = N if K1 is None else K1
+    dev = Q.device
+    if out is not None:
+        I, A, O = out
+    else:
+        if K1 < N:
+            want_A = want_I = True
+        O = torch.empty(Q.shape, dtype=torch.float32, device=dev)
+        A = torch.empty(lead + (N, K1), dtype=torch.float32, device=dev) if want_A else None
+        I = torch.empty(lead + (N, K1), dtype=torch.int32, device=dev) if want_I else None
+    rows = _prod(lead) * N
+    _expect(I, rows * K1, torch.int32, "I_out")
+    _expect(A, rows * K1, torch.float32, "A_out")
+    _expect(O, Q.numel(), torch.float32, "O_out")
+    shape = make_shape(Q, win, shift)
+    rc = load().pfa_dense_layer(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), K1, _ptr(I), _ptr(A),
+                                _ptr(O), _stream())
+    if rc != 0:
+        raise PfaError("pfa_dense_layer", rc)
+    return I, A, O
+
+
+def sparse_layer(Q, K, V, I_prev, A_prev, K_l, *, win, shift=0, i_shared=False, K_prev=None, out=None):
+    """Sparse layer: scores only over I_prev, Hadamard with A_prev, top-K_l.
+    I_prev None = all slots (K_prev = N); A_prev None = all ones.
+    ``out`` = optional preallocated (I, A, O). Returns (I, A, O)."""
+    _check_qkv(Q, K, V)
+    lead, N = _geometry(Q, win)
+    if I_prev is not None:
+        K_prev = I_prev.shape[-1]
+    elif K_prev is None:
+        K_prev = N
+    dev = Q.device
+    if out is None:
+        I = torch.empty(lead + (N, K_l), dtype=torch.int32, device=dev)
+        A = torch.empty(lead + (N, K_l), dtype=torch.float32, device=dev)
+        O = torch.empty(Q.shape, dtype=torch.float32, device=dev)
+    else:
+        I, A, O = out
+    rows = _prod(lead) * N
+    hI = 1 if i_shared else Q.shape[1]
+    _expect(I_prev, rows // Q.shape[1] * hI * K_prev, torch.int32, "I_prev")
+    _expect(A_prev, rows * K_prev, torch.float32, "A_prev")
+    _expect(I, rows * K_l, torch.int32, "I_out")
+    _expect(A, rows * K_l, torch.float32, "A_out")
+    _expect(O, Q.numel(), torch.float32, "O_out")
+    shape = make_shape(Q, win, shift)
+    rc = load().pfa_sparse_layer(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(I_prev),
+                                 int(bool(i_shared)), _ptr(A_prev), K_prev, K_l, _ptr(I), _ptr(A),
+                                 _ptr(O), _stream())
+    if rc != 0:
+        raise PfaError("pfa_sparse_layer", rc)
+    return I, A, O

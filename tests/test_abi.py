@@ -1,0 +1,98 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+function include/pfa.h declares, and rejects bad arguments with the documented
+codes before touching any pointer or the HIP runtime."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_progressive_window_amd import pfa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "pfa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pfa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pfa._LIB_PATH):
+        from sparse_progressive_window_amd import build
+        build.build()
+    return pfa.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"pfa_dense_layer", "pfa_sparse_layer", "pfa_strerror", "pfa_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror(lib):
+    assert lib.pfa_version() == 10000
+    assert lib.pfa_strerror(0) == b"ok"
+    assert lib.pfa_strerror(-1) == b"invalid argument"
+    assert lib.pfa_strerror(-2) == b"unsupported configuration"
+    assert lib.pfa_strerror(-3) == b"HIP runtime error"
+    assert lib.pfa_strerror(12345) == b"unknown error code"
+
+
+def shape(B=1, heads=1, H=32, W=32, d=32, win=32, shift=0, dtype=0):
+    return pfa.PfaShape(B, heads, H, W, d, win, shift, dtype)
+
+
+def sparse(lib, s, K_prev=64, K_l=16, I_prev=FAKE, outs=(FAKE, FAKE, FAKE)):
+    return lib.pfa_sparse_layer(ctypes.byref(s) if s is not None else None, FAKE, FAKE, FAKE, I_prev, 0,
+                                FAKE, K_prev, K_l, *outs, None)
+
+
+def dense(lib, s, K1=1024, I=None, A=None, O=FAKE):
+    return lib.pfa_dense_layer(ctypes.byref(s) if s is not None else None, FAKE, FAKE, FAKE, K1, I, A, O, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=8), -2), (dict(d=64), -2), (dict(dtype=7), -2), (dict(win=64, H=64, W=64), -2),
+    (dict(H=33), -1), (dict(shift=32), -1), (dict(shift=-1), -1), (dict(B=0), -1), (dict(heads=0), -1),
+    (dict(win=0, shift=1), -1), (dict(win=0, H=4096, W=4096), -2), (dict(win=-1), -1),
+])
+def test_sparse_shape_validation(lib, kw, code):
+    assert sparse(lib, shape(**kw)) == code
+
+
+def test_sparse_size_validation(lib):
+    assert sparse(lib, None) == -1
+    assert sparse(lib, shape(), K_l=0) == -1
+    assert sparse(lib, shape(), K_l=65, K_prev=64) == -1
+    assert sparse(lib, shape(), K_prev=0) == -1
+    assert sparse(lib, shape(), K_prev=2000) == -1                 # K_prev > N
+    assert sparse(lib, shape(), K_prev=64, I_prev=None) == -1      # implicit list needs K_prev == N
+    assert sparse(lib, shape(win=0, H=64, W=64), K_prev=1025, K_l=5) == -2
+    assert sparse(lib, shape(), outs=(None, FAKE, FAKE)) == -1
+    assert sparse(lib, shape(), outs=(FAKE, None, FAKE)) == -1
+    assert sparse(lib, shape(), outs=(FAKE, FAKE, None)) == -1
+
+
+def test_dense_validation(lib):
+    assert dense(lib, None) == -1
+    assert dense(lib, shape(win=0)) == -2
+    assert dense(lib, shape(d=8)) == -2
+    assert dense(lib, shape(), K1=0) == -1
+    assert dense(lib, shape(), K1=1025) == -1
+    assert dense(lib, shape(), O=None) == -1
+    assert dense(lib, shape(), K1=100) == -1                       # K1 < N needs I and A
+    assert dense(lib, shape(), K1=100, I=FAKE) == -1
+    assert dense(lib, shape(win=6, H=12, W=12), K1=36) == -2       # K1 == N needs win % 4 == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(pfa, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(pfa, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        pfa.load()

@@ -1,0 +1,233 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle on
+small inputs: free-running chains with every row compared, ragged and extreme
+sizes, exact ties, zeros in the previous map, shared index matrices, dense-layer
+variants, determinism and error codes. Rules: tests/parity.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_progressive_window_amd import inputs, pfa, workloads
+from tests import parity
+from tests.test_gpu_workloads import to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------------------
+# free-running GPU chains, every row compared
+# ---------------------------------------------------------------------------
+def run_chain(B, heads, H, W, d, win, Ks, shifts, dtype, seed):
+    """GPU chain with its own (I, A) vs the oracle chain; rows that legitimately
+    diverged at a near-tie are excluded from later layers (rows are independent)."""
+    shape = (B, heads, H, W, d)
+    qkvs = [tuple(inputs.draw(seed + 10 * l + t, shape, dtype) for t in range(3)) for l in range(len(Ks))]
+    n_wh = B * heads * (H // win) * (W // win)
+    N = win * win
+    tol = parity.TOL[dtype]
+    sel = np.arange(n_wh)
+    I_g = A_g = None
+    I_r = A_r = None
+    alive = np.ones((n_wh, N), bool)
+    for l, (qt, kt, vt) in enumerate(qkvs):
+        Qd, Kd, Vd = to_dev(qt), to_dev(kt), to_dev(vt)
+        if l == 0:
+            I, A, O = pfa.dense_layer(Qd, Kd, Vd, Ks[0], win=win, shift=shifts[0], want_A=True, want_I=True)
+        else:
+            I, A, O = pfa.sparse_layer(Qd, Kd, Vd, None if (l == 1 and Ks[0] == N) else I_g, A_g, Ks[l],
+                                       win=win, shift=shifts[l])
+        torch.cuda.synchronize()
+        # oracle on the GPU's own previous map would take GPU values: use the oracle's chain instead
+        ref = oracle.layer(qt.exact, kt.exact, vt.exact, win=win, shift=shifts[l], K_l=Ks[l], I_prev=I_r,
+                           A_prev=A_r, prev_compact=True, wh_list=sel, want_keys=True)
+        Ig = I.view(n_wh, N, Ks[l]).cpu().numpy()
+        Ag = A.view(n_wh, N, Ks[l]).cpu().numpy()
+        # compare rows still on the oracle's path; near-tie divergence retires a row
+        same = (np.sort(Ig, -1) == np.sort(ref["I"], -1)).all(-1)
+        rows = alive & same
+        diverged = alive & ~same
+        if diverged.any():
+            keys = ref["keys"]
+            kth = -np.sort(-keys, -1)[..., Ks[l] - 1]
+            for n, i in np.argwhere(diverged):
+                C = np.arange(N) if I_r is None else I_r[n, i]
+                for j in set(Ig[n, i].tolist()) ^ set(ref["I"][n, i].tolist()):
+                    c = int(np.nonzero(C == j)[0][0])
+                    assert abs(keys[n, i, c] - kth[n, i]) < parity.GAP, (l, n, i, j)
+        np.testing.assert_array_equal(Ig[rows], ref["I"][rows])
+        err = np.abs(Ag[rows] - ref["A"][rows])
+        assert (err <= tol * ref["A"][rows] + 1e-30).all(), (l, float((err / ref["A"][rows]).max()))
+        # O on the pixels of rows still on the oracle's path
+        parity.check_O(O.cpu().numpy(), _mask_O(ref["O"], rows, B, heads, H, W, win, shifts[l]), tol)
+        # invariants on every GPU row
+        np.testing.assert_allclose(Ag.sum(-1), 1.0, rtol=1e-5 if dtype == "f32" else 1e-4)
+        assert (Ig >= 0).all() and (Ig < N).all()
+        alive = rows
+        I_g, A_g = I, A
+        I_r, A_r = ref["I"], ref["A"]
+        del Qd, Kd, Vd
+    return alive
+
+
+def _mask_O(O_ref, rows, B, heads, H, W, win, shift):
+    """NaN out the O rows of retired slots (slot -> pixel under the layer's shift)."""
+    out = O_ref.copy()
+    nwy, nwx = H // win, W // win
+    for n, i in np.argwhere(~rows):
+        wx = n % nwx
+        wy = (n // nwx) % nwy
+        bh = n // (nwx * nwy)
+        y = (wy * win + i // win + shift) % H
+        x = (wx * win + i % win + shift) % W
+        out[bh // heads, bh % heads, y, x] = np.nan
+    return out
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chain_free_running_small(dtype):
+    alive = run_chain(2, 3, 64, 96, 32, 32, [1024, 256, 128, 64, 32, 16], [0, 16, 0, 16, 0, 16], dtype, 9100)
+    assert alive.mean() > 0.97
+
+
+@pytest.mark.timeout(300)
+def test_chain_tiny_workload():
+    w = workloads.TINY
+    run_chain(w.B, w.heads, w.H, w.W, w.d, w.win, w.K, w.shifts, w.dtype, 9200)
+
+
+# ---------------------------------------------------------------------------
+# edge cases: ragged and extreme sizes, ties, zeros, shared index matrices
+# ---------------------------------------------------------------------------
+def single_layer_case(B, heads, H, W, d, win, shift, K_prev, K_l, dtype, seed, *, sorted_c=False,
+                      dup_keys=False, zero_frac=0.0, no_A=False, i_shared=False):
+    shape = (B, heads, H, W, d)
+    qt, kt, vt = (inputs.draw(seed + t, shape, dtype) for t in range(3))
+    if dup_keys:   # identical key vectors on every pixel: all scores of a row tie exactly
+        kt = inputs.Tensor(np.broadcast_to(kt.device[:, :, :1, :1], shape).copy(),
+                           np.broadcast_to(kt.exact[:, :, :1, :1], shape).copy(), dtype)
+    N = win * win if win else H * W
+    nwin = (H // win) * (W // win) if win else 1
+    n_wh = B * heads * nwin
+    g = np.random.Generator(np.random.PCG64(seed + 5))
+    hI = 1 if i_shared else heads
+    C = np.stack([g.permutation(N)[:K_prev] for _ in range(B * hI * nwin * N)]).astype(np.int32)
+    if sorted_c:
+        C = np.sort(C, axis=1)
+    C = C.reshape(B, hI, nwin, N, K_prev)
+    a = (g.random((n_wh, N, K_prev)) + 0.05).astype(np.float32)
+    if zero_frac:
+        a[g.random(a.shape) < zero_frac] = 0.0
+        a[..., 0] = np.maximum(a[..., 0], 0.5)
+    a = a.reshape(B, heads, nwin, N, K_prev)
+    I, A, O = pfa.sparse_layer(to_dev(qt), to_dev(kt), to_dev(vt), torch.from_numpy(C).cuda(),
+                               None if no_A else torch.from_numpy(a).cuda(), K_l, win=win, shift=shift,
+                               i_shared=i_shared)
+    torch.cuda.synchronize()
+    sel = np.arange(n_wh)
+    kw = dict(win=win, shift=shift, K_l=K_l, I_prev=C, A_prev=None if no_A else a.astype(np.float64),
+              i_shared=i_shared, prev_compact=False, wh_list=sel)
+    ref = oracle.layer(qt.exact, kt.exact, vt.exact, want_keys=True, **kw)
+    cand = np.stack([C[n // (heads * nwin), 0 if i_shared else (n // nwin) % heads, n % nwin]
+                     for n in range(n_wh)])
+    return parity.check_layer(gpu_I=I.view(n_wh, N, K_l).cpu().numpy(), gpu_A=A.view(n_wh, N, K_l).cpu().numpy(),
+                              gpu_O=O.cpu().numpy(), ref=ref, cand=cand, wh_list=sel,
+                              tol=parity.TOL[dtype], rerun=parity.rerun_fn(qt.exact, kt.exact, vt.exact, **kw))
+
+
+EDGE = [
+    # B, heads, H, W, d, win, shift, K_prev, K_l, dtype
+    (1, 2, 8, 12, 16, 4, 2, 16, 5, "f32"),        # N = 16, shifted, tiny window
+    (1, 1, 16, 16, 32, 8, 3, 37, 36, "f32"),      # ragged K_prev, odd shift
+    (2, 2, 32, 32, 32, 16, 8, 100, 37, "bf16"),   # ragged K_prev / K_l
+    (1, 2, 32, 64, 32, 32, 16, 1024, 1024, "f32"),  # K_l = K_prev = N (two aggregation passes)
+    (1, 2, 32, 32, 32, 32, 0, 1024, 1, "bf16"),   # K_l = 1
+    (1, 3, 32, 32, 16, 32, 5, 300, 150, "bf16"),  # d = 16 bf16
+    (1, 3, 32, 32, 16, 32, 31, 64, 64, "f32"),    # K_l = K_prev, max shift
+    (1, 1, 24, 24, 32, 12, 6, 144, 20, "f32"),    # window side not a power of two
+]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("case", EDGE)
+def test_edge_cases(case):
+    single_layer_case(*case, seed=4000 + sum(case[:9]))
+
+
+@pytest.mark.timeout(300)
+def test_exact_ties_lower_index_wins():
+    # every score of a row equal and A_prev with repeated values: ties everywhere
+    st = single_layer_case(1, 2, 32, 32, 32, 32, 0, 256, 100, "f32", 51, dup_keys=True, zero_frac=0.3)
+    assert st["tie_rows"] == 0
+
+
+@pytest.mark.timeout(300)
+def test_zeros_in_previous_map():
+    single_layer_case(1, 2, 32, 32, 32, 32, 16, 128, 100, "bf16", 52, zero_frac=0.5)
+
+
+@pytest.mark.timeout(300)
+def test_shared_index_window_mode_and_global_unshared():
+    single_layer_case(2, 3, 32, 32, 32, 16, 4, 64, 16, "f32", 53, i_shared=True)
+    single_layer_case(1, 2, 16, 32, 32, 0, 0, 96, 40, "bf16", 54)
+    single_layer_case(1, 2, 16, 16, 32, 0, 0, 48, 48, "f32", 55, no_A=True, sorted_c=True)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,d,win", [("f32", 32, 32), ("bf16", 32, 32), ("f32", 16, 16), ("bf16", 16, 8)])
+def test_dense_layer_variants(dtype, d, win):
+    B, heads, H, W = 1, 2, 2 * win, 3 * win
+    shape = (B, heads, H, W, d)
+    qt, kt, vt = (inputs.draw(600 + t + d + win, shape, dtype) for t in range(3))
+    N = win * win
+    n_wh = B * heads * 6
+    sel = np.arange(n_wh)
+    for shift, K1 in [(0, N), (win // 2, N), (win // 2, N // 3)]:
+        I, A, O = pfa.dense_layer(to_dev(qt), to_dev(kt), to_dev(vt), K1, win=win, shift=shift, want_A=True,
+                                  want_I=True)
+        torch.cuda.synchronize()
+        kw = dict(win=win, shift=shift, K_l=K1, wh_list=sel)
+        ref = oracle.layer(qt.exact, kt.exact, vt.exact, want_keys=True, **kw)
+        parity.check_layer(gpu_I=I.view(n_wh, N, K1).cpu().numpy(), gpu_A=A.view(n_wh, N, K1).cpu().numpy(),
+                           gpu_O=O.cpu().numpy(), ref=ref, cand=None, wh_list=sel, tol=parity.TOL[dtype],
+                           rerun=parity.rerun_fn(qt.exact, kt.exact, vt.exact, I_prev=None, A_prev=None,
+                                                 i_shared=False, prev_compact=False, **kw))
+    # O-only mode gives the same O
+    _, A0, O0 = pfa.dense_layer(to_dev(qt), to_dev(kt), to_dev(vt), N, win=win, shift=0, want_A=False)
+    _, A1, O1 = pfa.dense_layer(to_dev(qt), to_dev(kt), to_dev(vt), N, win=win, shift=0, want_A=True)
+    assert A0 is None and torch.equal(O0, O1)
+
+
+@pytest.mark.timeout(300)
+def test_deterministic():
+    w = workloads.PATCH64
+    shape = (4, 6, 64, 64, 32)
+    qt, kt, vt = (inputs.draw(700 + t, shape, "bf16") for t in range(3))
+    Qd, Kd, Vd = to_dev(qt), to_dev(kt), to_dev(vt)
+    _, A1, O1 = pfa.dense_layer(Qd, Kd, Vd, 1024, win=32, shift=16)
+    I2, A2, O2 = pfa.sparse_layer(Qd, Kd, Vd, None, A1, 256, win=32, shift=16)
+    I3, A3, O3 = pfa.sparse_layer(Qd, Kd, Vd, I2, A2, 128, win=32, shift=0)
+    _, A1b, O1b = pfa.dense_layer(Qd, Kd, Vd, 1024, win=32, shift=16)
+    I2b, A2b, O2b = pfa.sparse_layer(Qd, Kd, Vd, None, A1b, 256, win=32, shift=16)
+    I3b, A3b, O3b = pfa.sparse_layer(Qd, Kd, Vd, I2b, A2b, 128, win=32, shift=0)
+    for x, y in [(A1, A1b), (O1, O1b), (I2, I2b), (A2, A2b), (O2, O2b), (I3, I3b), (A3, A3b), (O3, O3b)]:
+        assert torch.equal(x, y)
+
+
+def test_error_codes():
+    Q = torch.zeros((1, 1, 32, 32, 32), dtype=torch.float32, device="cuda")
+    with pytest.raises(pfa.PfaError) as e:
+        pfa.sparse_layer(Q, Q, Q, None, None, 0, win=32)            # K_l < 1
+    assert e.value.code == -1
+    with pytest.raises(pfa.PfaError) as e:
+        pfa.sparse_layer(Q, Q, Q, None, None, 10, win=32, shift=32)  # shift >= win
+    assert e.value.code == -1
+    Q5 = torch.zeros((1, 1, 32, 32, 8), dtype=torch.float32, device="cuda")
+    with pytest.raises(pfa.PfaError) as e:
+        pfa.dense_layer(Q5, Q5, Q5, win=32)                          # d = 8
+    assert e.value.code == -2
+    with pytest.raises(pfa.PfaError) as e:
+        pfa.dense_layer(Q, Q, Q, win=0)                              # dense layer in global mode
+    assert e.value.code == -2

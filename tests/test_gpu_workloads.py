@@ -1,0 +1,128 @@
+"""GPU parity at the full workload sizes (through the C ABI) against the fp64 oracle.
+
+Per-layer tests run each workload at its full size, in the launch configuration
+the benchmark times, and compare sampled window-heads: the previous map
+(I^{l-1}, A^{l-1}) of the sampled window-heads comes from the oracle's own
+chain (rounded to fp32, the dtype the C ABI takes), so both sides see identical
+inputs; the other window-heads get a valid uniform map. Chain tests run the
+GPU free-running at small sizes and compare every row. Rules: tests/parity.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_progressive_window_amd import inputs, pfa, workloads
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def to_dev(t: inputs.Tensor):
+    if t.dtype == "f32":
+        return torch.from_numpy(t.device).cuda()
+    return torch.from_numpy(t.device.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def sample_wh(w: workloads.Workload, count: int):
+    """Spread of window-heads: first, last, the wrapping window of each head
+    (last row and column of windows), and a seeded random rest."""
+    n = w.n_wh
+    nwin = w.n_windows
+    picks = {0, n - 1}
+    for h in range(w.heads):
+        picks.add(h * nwin + nwin - 1)
+    g = np.random.Generator(np.random.PCG64(w.seed_base + 77))
+    while len(picks) < min(count, n):
+        picks.add(int(g.integers(0, n)))
+    return np.array(sorted(picks), dtype=np.int64)
+
+
+def gpu_rows(x, sel):
+    t = x.reshape(-1, x.shape[-2], x.shape[-1])
+    return t[torch.from_numpy(sel).cuda()].cpu().numpy()
+
+
+def run_layer_parity(w, block, layers, count, log):
+    sel = sample_wh(w, count)
+    N, tol = w.N, parity.TOL[w.dtype]
+    I_ref = A_ref = None              # oracle's previous map on the sampled window-heads
+    for l in range(layers):
+        qkv = inputs.qkv(w, block, l)
+        Qd, Kd, Vd = (to_dev(t) for t in qkv)
+        Q, K, V = (t.exact for t in qkv)
+        shift, K_l = w.shifts[l], w.K[l]
+        A32 = None if A_ref is None else A_ref.astype(np.float32)
+        ref = oracle.layer(Q, K, V, win=w.win, shift=shift, K_l=K_l, I_prev=I_ref,
+                           A_prev=None if A32 is None else A32.astype(np.float64),
+                           prev_compact=True, wh_list=sel, want_keys=True)
+        if l == 0:
+            I, A, O = pfa.dense_layer(Qd, Kd, Vd, K_l, win=w.win, shift=shift, want_A=True,
+                                      want_I=K_l < N)
+            if I is None:
+                I = torch.arange(N, dtype=torch.int32, device="cuda").expand(A.shape).contiguous()
+        else:
+            K_prev = w.K[l - 1]
+            shape = (w.n_wh, N, K_prev)
+            A_dev = torch.full(shape, 1.0 / K_prev, dtype=torch.float32, device="cuda")
+            A_dev[torch.from_numpy(sel).cuda()] = torch.from_numpy(A32).cuda()
+            if l == 1 and K_prev == N:
+                I_dev = None
+            else:
+                I_dev = torch.arange(K_prev, dtype=torch.int32, device="cuda").expand(shape).contiguous()
+                I_dev[torch.from_numpy(sel).cuda()] = torch.from_numpy(I_ref).cuda()
+            lead = (w.B, w.heads, w.n_windows)
+            I, A, O = pfa.sparse_layer(Qd, Kd, Vd, None if I_dev is None else I_dev.view(lead + (N, K_prev)),
+                                       A_dev.view(lead + (N, K_prev)), K_l, win=w.win, shift=shift)
+        torch.cuda.synchronize()
+        rerun = parity.rerun_fn(Q, K, V, win=w.win, shift=shift, K_l=K_l, I_prev=I_ref,
+                                A_prev=None if A32 is None else A32.astype(np.float64), i_shared=False,
+                                prev_compact=True, wh_list=sel)
+        st = parity.check_layer(gpu_I=gpu_rows(I, sel), gpu_A=gpu_rows(A, sel), gpu_O=O.cpu().numpy(),
+                                ref=ref, cand=I_ref, wh_list=sel, tol=tol, rerun=rerun)
+        log(f"{w.name} block {block} layer {l + 1}: {st}")
+        I_ref, A_ref = ref["I"], ref["A"]
+        del Qd, Kd, Vd, I, A, O
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,count", [
+    (workloads.TINY.name, 1),
+    (workloads.MAP256.name, 12),
+    (workloads.PATCH64.name, 12),
+])
+def test_layers_full_size(name, count, capsys):
+    w = workloads.BY_NAME[name]
+    with capsys.disabled():
+        run_layer_parity(w, 0, w.layers, count, lambda s: print(s, flush=True))
+
+
+@pytest.mark.timeout(900)
+def test_layers_full_size_map640_block5(capsys):
+    w = workloads.MAP640
+    with capsys.disabled():
+        run_layer_parity(w, 5, w.layers, 8, lambda s: print(s, flush=True))
+
+
+@pytest.mark.timeout(300)
+def test_global_individualized(capsys):
+    w = workloads.GLOBAL64
+    Qt, Kt, Vt = inputs.qkv(w, 0, 0)
+    Iidx = inputs.global_index(w)
+    N, k = w.N, w.k_global
+    I_dev = torch.from_numpy(Iidx).cuda().view(1, 1, N, k)
+    I, A, O = pfa.sparse_layer(to_dev(Qt), to_dev(Kt), to_dev(Vt), I_dev, None, k, win=0, i_shared=True)
+    torch.cuda.synchronize()
+    sel = np.arange(w.heads)
+    Ip = Iidx.reshape(1, 1, 1, N, k)
+    ref = oracle.layer(Qt.exact, Kt.exact, Vt.exact, win=0, shift=0, K_l=k, I_prev=Ip, i_shared=True,
+                       wh_list=sel, want_keys=True)
+    st = parity.check_layer(gpu_I=gpu_rows(I, sel), gpu_A=gpu_rows(A, sel), gpu_O=O.cpu().numpy(), ref=ref,
+                            cand=np.broadcast_to(Iidx, (w.heads, N, k)), wh_list=sel,
+                            tol=parity.TOL[w.dtype],
+                            rerun=parity.rerun_fn(Qt.exact, Kt.exact, Vt.exact, win=0, shift=0, K_l=k,
+                                                  I_prev=Ip, A_prev=None, i_shared=True,
+                                                  prev_compact=False, wh_list=sel))
+    with capsys.disabled():
+        print(f"{w.name}: {st}", flush=True)
