@@ -36,6 +36,7 @@ bool geom_from_shape(const pfa_shape* s, Geom* g, int* code) {
         g->N = s->win * s->win;
         g->nwy = s->H / s->win;
         g->nwx = s->W / s->win;
+        g->win_magic = (65536 + s->win - 1) / s->win;
     } else {
         if (s->shift != 0) return false;
         if ((int64_t)s->H * s->W >= (1 << 24)) {
@@ -44,18 +45,13 @@ bool geom_from_shape(const pfa_shape* s, Geom* g, int* code) {
         }
         g->N = s->H * s->W;
         g->nwy = g->nwx = 1;
+        g->win_magic = 0;
     }
     *code = PFA_OK;
     return true;
 }
 
 int elem_bytes(int dtype) { return dtype == PFA_F32 ? 4 : 2; }
-
-int kpt_for(int k_prev) {
-    int kpt = 1;
-    while (kpt * pfa::kWave < k_prev) kpt *= 2;
-    return kpt;
-}
 
 int64_t n_wh(const Geom& g) { return (int64_t)g.B * g.heads * g.nwy * g.nwx; }
 
@@ -72,27 +68,28 @@ int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const voi
     a.scale2 = (float)(1.4426950408889634 / sqrt((double)g.d));
 
     const int rowb = g.d * elem_bytes(dtype);
-    const int scratch = pfa::kSparseWaves * pfa::kScratchEntries * 8;
     pfa::SparseMode mode;
-    int lds = scratch;
+    int lds = pfa::kScratchBytes;
+    int parts;
     if (g.win == 0) {
         mode = pfa::kKVglobal;
-        a.rows_per_block = pfa::kSparseWaves * 16;
+        parts = (g.N + 63) / 64;
     } else {
-        a.rows_per_block = g.N;
-        if (2 * g.N * rowb + scratch <= pfa::kLdsBytes) {
+        if (2 * g.N * rowb + lds <= pfa::kLdsBytes) {
             mode = pfa::kKVinLDS;
             lds += 2 * g.N * rowb;
         } else {
             mode = pfa::kKinLDS;
             lds += g.N * rowb;
         }
+        parts = g.N >= 512 ? 2 : 1;
     }
-    a.blocks_per_wh = (g.N + a.rows_per_block - 1) / a.rows_per_block;
+    a.blocks_per_wh = parts;
+    a.rows_per_block = (g.N + parts - 1) / parts;
+    a.xcd_map = (n_wh(g) % 8 == 0) ? 1 : 0;
     const int64_t grid = n_wh(g) * a.blocks_per_wh;
     if (grid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
-    const hipError_t e =
-        pfa::launch_sparse(a, dtype, g.d, kpt_for(K_prev), mode, lds, (int)grid, stream);
+    const hipError_t e = pfa::launch_sparse(a, dtype, g.d, mode, lds, (int)grid, stream);
     return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
 }
 

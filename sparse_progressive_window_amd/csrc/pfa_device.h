@@ -15,6 +15,7 @@ struct Geom {
     int shift;
     int N;       // tokens per window
     int nwy, nwx;
+    int win_magic;  // ceil(65536 / win): t / win == (t * win_magic) >> 16 for t < 1024, win <= 32
 };
 
 // Pixel (raster index inside the head's H x W plane) of slot t of window (wy, wx):
@@ -22,7 +23,7 @@ struct Geom {
 // shift is an index remap; data never moves.
 __device__ __forceinline__ int slot_pixel(const Geom& g, int wy, int wx, int t) {
     if (g.win == 0) return t;
-    const int ty = t / g.win;
+    const int ty = (t * g.win_magic) >> 16;
     const int tx = t - ty * g.win;
     int y = wy * g.win + ty + g.shift;
     int x = wx * g.win + tx + g.shift;

@@ -8,9 +8,8 @@
 
 namespace pfa {
 
-constexpr int kSparseWaves = 8;        // waves per sparse-layer workgroup
-constexpr int kScratchEntries = 512;   // (j, weight) entries per wave for the aggregation
-constexpr int kLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
+constexpr int kScratchBytes = 32 * 1024;  // per workgroup: (j, weight) entries for the aggregation
+constexpr int kLdsBytes = 160 * 1024;     // LDS per workgroup on gfx950
 
 struct SparseArgs {
     const void* Q;
@@ -25,6 +24,7 @@ struct SparseArgs {
     int K_prev, K_l;
     int i_shared;
     int rows_per_block, blocks_per_wh;
+    int xcd_map;             // 1: the parts of a window-head run on one XCD (needs #wh % 8 == 0)
     float scale2;            // log2(e) / sqrt(d): scores are kept in base-2 units
 };
 
@@ -41,8 +41,8 @@ struct DenseArgs {
     float scale2;
 };
 
-hipError_t launch_sparse(const SparseArgs& a, int dtype, int D, int kpt, SparseMode mode,
-                         int lds_bytes, int grid, hipStream_t stream);
+hipError_t launch_sparse(const SparseArgs& a, int dtype, int D, SparseMode mode, int lds_bytes, int grid,
+                         hipStream_t stream);
 hipError_t launch_dense(const DenseArgs& a, int dtype, int D, int grid, hipStream_t stream);
 hipError_t launch_iota_rows(int32_t* I, int64_t rows, int N, hipStream_t stream);
 
