@@ -68,28 +68,36 @@ int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const voi
     a.scale2 = (float)(1.4426950408889634 / sqrt((double)g.d));
 
     const int rowb = g.d * elem_bytes(dtype);
-    pfa::SparseMode mode;
-    int lds = pfa::kScratchBytes;
-    int parts;
-    if (g.win == 0) {
-        mode = pfa::kKVglobal;
-        parts = (g.N + 63) / 64;
-    } else {
-        if (2 * g.N * rowb + lds <= pfa::kLdsBytes) {
-            mode = pfa::kKVinLDS;
-            lds += 2 * g.N * rowb;
-        } else {
-            mode = pfa::kKinLDS;
-            lds += g.N * rowb;
-        }
-        parts = g.N >= 512 ? 2 : 1;
-    }
-    a.blocks_per_wh = parts;
-    a.rows_per_block = (g.N + parts - 1) / parts;
     a.xcd_map = (n_wh(g) % 8 == 0) ? 1 : 0;
-    const int64_t grid = n_wh(g) * a.blocks_per_wh;
-    if (grid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
-    const hipError_t e = pfa::launch_sparse(a, dtype, g.d, mode, lds, (int)grid, stream);
+    if (g.win == 0) {
+        a.blocks_per_wh = (g.N + 63) / 64;
+        a.rows_per_block = 64;
+        const int64_t grid = n_wh(g) * a.blocks_per_wh;
+        if (grid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
+        const hipError_t e =
+            pfa::launch_sparse(a, dtype, g.d, pfa::kKVglobal, pfa::kScratchBytes, (int)grid, stream);
+        return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
+    }
+    a.blocks_per_wh = g.N >= 512 ? 2 : 1;
+    a.rows_per_block = (g.N + a.blocks_per_wh - 1) / a.blocks_per_wh;
+    const int64_t grid64 = n_wh(g) * a.blocks_per_wh;
+    if (grid64 > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
+    const int grid = (int)grid64;
+    hipError_t e;
+    bool aggregate = false;
+    if (!I_prev && K_prev == 1024 && g.N == 1024) {
+        // every slot is a candidate: MFMA scores
+        const bool with_v = pfa::all_cand_fits_with_v(dtype, g.d);
+        e = pfa::launch_all_cand(a, dtype, g.d, with_v, grid, stream);
+        aggregate = !with_v;
+    } else if (2 * g.N * rowb + pfa::kScratchBytes <= pfa::kLdsBytes) {
+        e = pfa::launch_sparse(a, dtype, g.d, pfa::kKVinLDS, 2 * g.N * rowb + pfa::kScratchBytes, grid, stream);
+    } else {
+        // K and V do not fit in LDS together: select with K in LDS, then aggregate with V in LDS
+        e = pfa::launch_sparse(a, dtype, g.d, pfa::kKselect, g.N * rowb, grid, stream);
+        aggregate = true;
+    }
+    if (e == hipSuccess && aggregate) e = pfa::launch_aggregate(a, dtype, g.d, grid, stream);
     return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
 }
 

@@ -29,7 +29,10 @@ struct SparseArgs {
 };
 
 // Where K and V rows are read from.
-enum SparseMode { kKVinLDS = 0, kKinLDS = 1, kKVglobal = 2 };
+// kKVinLDS: K and V staged in LDS; kKinLDS: K in LDS, V read from global memory;
+// kKVglobal: both from global memory (global mode); kKselect: K in LDS, no
+// aggregation (O comes from launch_aggregate).
+enum SparseMode { kKVinLDS = 0, kKinLDS = 1, kKVglobal = 2, kKselect = 3 };
 
 struct DenseArgs {
     const void* Q;
@@ -43,6 +46,11 @@ struct DenseArgs {
 
 hipError_t launch_sparse(const SparseArgs& a, int dtype, int D, SparseMode mode, int lds_bytes, int grid,
                          hipStream_t stream);
+// All-candidates layer (I^{l-1} implicit, K_prev = N = 1024): MFMA scores.
+bool all_cand_fits_with_v(int dtype, int D);
+hipError_t launch_all_cand(const SparseArgs& a, int dtype, int D, bool with_av, int grid, hipStream_t stream);
+// O from stored (I^l, A^l) rows with V in LDS (window mode).
+hipError_t launch_aggregate(const SparseArgs& a, int dtype, int D, int grid, hipStream_t stream);
 hipError_t launch_dense(const DenseArgs& a, int dtype, int D, int grid, hipStream_t stream);
 hipError_t launch_iota_rows(int32_t* I, int64_t rows, int N, hipStream_t stream);
 

@@ -38,6 +38,9 @@ namespace {
 
 constexpr int kBand = 8;
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
 // DPP controls (GFX9 encoding)
 constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
@@ -143,18 +146,235 @@ __device__ __forceinline__ float reduce_chunk_lanes(float v) {
     return v;
 }
 
+// Where a row's V vectors come from in the aggregation.
+enum VSrc { kVlds = 0, kVwin = 1, kVraster = 2, kVnone = 3 };
+
+// Everything after the scores of one query row: u = A^{l-1} exp(s - m), the exact
+// top-K_l (ties to the lower slot index), the I^l / A^l row in I^{l-1} order and,
+// unless VS == kVnone, O_i = sum_kept A v_j. jj/av/valid/sv are this lane's
+// candidates c = gl + GL*t; sv are base-2 scores.
+template <typename T, int D, int GL, int KPT, int VS>
+__device__ __forceinline__ void finish_row(const SparseArgs& p, const Geom& g, int lane, bool active, size_t row,
+                                           int qpix, int wy, int wx, const int (&jj)[KPT], const float (&av)[KPT],
+                                           const bool (&valid)[KPT], const float (&sv)[KPT], uint2* scr, int scg,
+                                           const unsigned char* Vs, const T* Vh, float* Oh) {
+    constexpr int EPC = Chunk<T>::kElems;
+    constexpr int CH = D / EPC;
+    constexpr int ROWB = D * (int)sizeof(T);
+    constexpr int GS = GL / CH;
+    using G = Grp<GL>;
+    const int gl = lane & (GL - 1);
+    const int K_prev = p.K_prev;
+    const int K_l = p.K_l;
+
+    float smax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < KPT; ++t) smax = fmaxf(smax, sv[t]);
+    smax = G::all(smax, MaxF());
+
+    // u = A^{l-1} exp(s - m); key = bits of u (>= 0), -1 for no candidate
+    float uv[KPT];
+    int key[KPT];
+    int kmin = 0x7fffffff, kmax = -1;
+#pragma unroll
+    for (int t = 0; t < KPT; ++t) {
+        uv[t] = valid[t] ? av[t] * fast_exp2(sv[t] - smax) : 0.0f;
+        key[t] = valid[t] ? __float_as_int(uv[t]) : -1;
+        if (valid[t]) {
+            kmin = min(kmin, key[t]);
+            kmax = max(kmax, key[t]);
+        }
+    }
+    kmin = G::all_i(kmin, MinI());
+    kmax = G::all_i(kmax, MaxI());
+
+    // phase 1: narrow [lo, hi) until it holds at most kBand keys
+    int lo = kmin, hi = kmax + 1, c_lo = K_prev, c_hi = 0;
+    bool done = !active || hi - lo <= 1 || c_lo - c_hi <= kBand;
+    for (int it = 0; ballot(!done) != 0; ++it) {
+        const int span = hi - lo;
+        int mid;
+        if (it % 3 == 2) {
+            mid = lo + (span >> 1);
+        } else {
+            const float f = ((float)(c_lo - K_l) + 0.5f) / (float)max(c_lo - c_hi, 1);
+            mid = lo + (int)(f * (float)span);
+        }
+        mid = min(max(mid, lo + 1), hi - 1);
+        int cnt = 0;
+#pragma unroll
+        for (int t = 0; t < KPT; ++t) cnt += G::count(key[t] >= mid, lane);
+        if (!done) {
+            if (cnt >= K_l) { lo = mid; c_lo = cnt; } else { hi = mid; c_hi = cnt; }
+            done = hi - lo <= 1 || c_lo - c_hi <= kBand;
+        }
+    }
+
+    // phase 2: take the band's keys largest first until K_l are kept
+    int need = K_l - c_hi;
+    int tau = lo, need_tau = need, n_tau = 0;
+    bool done2 = !active;
+    while (ballot(!done2) != 0) {
+        int m = -1;
+#pragma unroll
+        for (int t = 0; t < KPT; ++t)
+            if (key[t] >= lo && key[t] < hi) m = max(m, key[t]);
+        m = G::all_i(m, MaxI());
+        int ceq = 0;
+#pragma unroll
+        for (int t = 0; t < KPT; ++t) ceq += G::count(key[t] == m, lane);
+        if (!done2) {
+            if (ceq >= need) {
+                tau = m; need_tau = need; n_tau = ceq; done2 = true;
+            } else {
+                need -= ceq; hi = m;
+            }
+        }
+    }
+
+    // exact ties at the threshold: keep the lowest slot indices
+    int jcut = 0x7fffffff;
+    const bool tie = active && n_tau > need_tau;
+    if (ballot(tie) != 0) {
+        int jl = -1, jh = g.N - 1;
+        while (ballot(tie && jh - jl > 1) != 0) {
+            const int mid = (jl + jh) >> 1;
+            int cnt = 0;
+#pragma unroll
+            for (int t = 0; t < KPT; ++t) cnt += G::count(key[t] == tau && jj[t] <= mid, lane);
+            if (tie && jh - jl > 1) {
+                if (cnt >= need_tau) jh = mid; else jl = mid;
+            }
+        }
+        if (tie) jcut = jh;
+    }
+
+    bool kept[KPT];
+    float ksum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < KPT; ++t) {
+        kept[t] = key[t] > tau || (key[t] == tau && jj[t] <= jcut);
+        ksum += kept[t] ? uv[t] : 0.0f;
+    }
+    const float inv = 1.0f / G::all(ksum, SumF());
+
+    // kept entries in I^{l-1} order
+    int pos[KPT];
+    int obase = 0;
+    int32_t* Io = p.I_out + row * K_l;
+    float* Ao = p.A_out + row * K_l;
+#pragma unroll
+    for (int t = 0; t < KPT; ++t) {
+        const uint64_t m = ballot(kept[t]);
+        pos[t] = kept[t] ? obase + G::below(m, lane) : -1;
+        if (pos[t] >= K_l) pos[t] = -1;   // only on precondition violations
+        uv[t] *= inv;
+        if (pos[t] >= 0) {
+            Io[pos[t]] = jj[t];
+            Ao[pos[t]] = uv[t];
+        }
+        obase += G::count_mask(m, lane);
+    }
+    if (VS == kVnone) {
+        __asm__ volatile("" ::: "memory");   // keeps the scheduler from overlapping rows (register pressure)
+        return;
+    }
+
+    // O_i = sum_kept A v_j: CH lanes read one V row; GS entries at a time per group
+    const int vchunk = gl % CH;
+    const int vsub = gl / CH;
+    float oacc[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) oacc[e] = 0.0f;
+    for (int P0 = 0; P0 < K_l; P0 += scg) {
+#pragma unroll
+        for (int t = 0; t < KPT; ++t)
+            if (pos[t] >= P0 && pos[t] < P0 + scg)
+                scr[pos[t] - P0] = make_uint2((uint32_t)jj[t], __float_as_uint(uv[t]));
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int cnt = active ? min(scg, K_l - P0) : 0;
+        for (int e = vsub; e < cnt; e += GS) {
+            const uint2 ent = scr[e];
+            const float w = __uint_as_float(ent.y);
+            const unsigned char* vrow;
+            if (VS == kVlds) {
+                vrow = Vs + ent.x * ROWB;
+            } else if (VS == kVwin) {
+                vrow = reinterpret_cast<const unsigned char*>(Vh + (size_t)slot_pixel(g, wy, wx, (int)ent.x) * D);
+            } else {
+                vrow = reinterpret_cast<const unsigned char*>(Vh + (size_t)ent.x * D);
+            }
+            float vf[EPC];
+            Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(vrow + vchunk * 16), vf);
+#pragma unroll
+            for (int x = 0; x < EPC; ++x) oacc[x] = fmaf(w, vf[x], oacc[x]);
+        }
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+#pragma unroll
+    for (int x = 0; x < EPC; ++x) oacc[x] = reduce_chunk_lanes<CH, GL>(oacc[x]);
+    if (active && vsub == 0) {
+        float* orow = Oh + (size_t)qpix * D + vchunk * EPC;
+#pragma unroll
+        for (int x = 0; x < EPC; x += 4)
+            *reinterpret_cast<float4*>(orow + x) = make_float4(oacc[x], oacc[x + 1], oacc[x + 2], oacc[x + 3]);
+    }
+}
+
+struct WhPart {
+    int wh, part, wy, wx, b, bh, win_id, nwin;
+};
+
+// workgroup -> (window-head, part); with xcd_map the parts of one window-head are
+// consecutive workgroups of one XCD (workgroups are dealt to the 8 XCDs in turn)
+__device__ __forceinline__ WhPart decode_block(int blocks_per_wh, int xcd_map, const Geom& g) {
+    WhPart w;
+    if (xcd_map) {
+        const int xcd = blockIdx.x & 7;
+        const int slot = blockIdx.x >> 3;
+        w.part = slot % blocks_per_wh;
+        w.wh = (slot / blocks_per_wh) * 8 + xcd;
+    } else {
+        w.wh = blockIdx.x / blocks_per_wh;
+        w.part = blockIdx.x - w.wh * blocks_per_wh;
+    }
+    w.nwin = g.nwy * g.nwx;
+    w.win_id = w.wh % w.nwin;
+    w.bh = w.wh / w.nwin;
+    w.b = w.bh / g.heads;
+    w.wy = w.win_id / g.nwx;
+    w.wx = w.win_id - w.wy * g.nwx;
+    return w;
+}
+
+// Stage rows t = 0..N-1 of a window (slot order, under the layer's shift) into LDS
+// with a row stride of `stride` bytes.
+template <typename T, int D>
+__device__ __forceinline__ void stage_rows(unsigned char* dst, int stride, const T* src_plane, const Geom& g, int wy,
+                                           int wx) {
+    constexpr int EPC = Chunk<T>::kElems;
+    constexpr int CH = D / EPC;
+    for (int u = threadIdx.x; u < g.N * CH; u += blockDim.x) {
+        const int t = u / CH;
+        const int c = u - t * CH;
+        const size_t src = (size_t)slot_pixel(g, wy, wx, t) * D + c * EPC;
+        *reinterpret_cast<uint4*>(dst + t * stride + c * 16) = *reinterpret_cast<const uint4*>(src_plane + src);
+    }
+}
+
+// Generic sparse layer: scores by LDS (or global) gathers of k_j, one group of GL
+// lanes per query row.
 template <typename T, int D, int GL, int KPT, int MODE, int NW>
 __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseArgs p) {
     constexpr int EPC = Chunk<T>::kElems;   // elements per 16-byte chunk
     constexpr int CH = D / EPC;             // chunks per K/V row
     constexpr int ROWB = D * (int)sizeof(T);
     constexpr int RPW = kWave / GL;         // rows per wavefront iteration
-    constexpr int GS = GL / CH;             // lanes sharing a V chunk in the aggregation
     constexpr bool K_LDS = MODE != kKVglobal;
     constexpr bool V_LDS = MODE == kKVinLDS;
+    constexpr int VS = MODE == kKVinLDS ? kVlds : MODE == kKinLDS ? kVwin : MODE == kKVglobal ? kVraster : kVnone;
     constexpr int SCW = kScratchBytes / (NW * 8);   // scratch entries per wave
     constexpr int SCG = SCW / RPW;                  // scratch entries per row group
-    using G = Grp<GL>;
     extern __shared__ __align__(16) unsigned char smem[];
 
     const Geom g = p.g;
@@ -163,25 +383,8 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
     const int wave = threadIdx.x / kWave;
     const int grp = lane / GL;
     const int gl = lane & (GL - 1);
-
-    // workgroup -> (window-head, part); parts of one window-head share an XCD
-    int wh, part;
-    if (p.xcd_map) {
-        const int xcd = blockIdx.x & 7;
-        const int slot = blockIdx.x >> 3;
-        part = slot % p.blocks_per_wh;
-        wh = (slot / p.blocks_per_wh) * 8 + xcd;
-    } else {
-        wh = blockIdx.x / p.blocks_per_wh;
-        part = blockIdx.x - wh * p.blocks_per_wh;
-    }
-    const int nwin = g.nwy * g.nwx;
-    const int win_id = wh % nwin;
-    const int bh = wh / nwin;
-    const int b = bh / g.heads;
-    const int wy = win_id / g.nwx;
-    const int wx = win_id - wy * g.nwx;
-    const size_t plane = (size_t)bh * g.H * g.W * D;
+    const WhPart w = decode_block(p.blocks_per_wh, p.xcd_map, g);
+    const size_t plane = (size_t)w.bh * g.H * g.W * D;
     const T* Qh = static_cast<const T*>(p.Q) + plane;
     const T* Kh = static_cast<const T*>(p.K) + plane;
     const T* Vh = static_cast<const T*>(p.V) + plane;
@@ -193,35 +396,26 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
                  wave * SCW + grp * SCG;
 
     if (K_LDS) {
-        for (int u = threadIdx.x; u < N * CH; u += blockDim.x) {
-            const int t = u / CH;
-            const int c = u - t * CH;
-            const size_t src = (size_t)slot_pixel(g, wy, wx, t) * D + c * EPC;
-            *reinterpret_cast<uint4*>(Ks + t * ROWB + c * 16) = *reinterpret_cast<const uint4*>(Kh + src);
-            if (V_LDS)
-                *reinterpret_cast<uint4*>(Vs + t * ROWB + c * 16) = *reinterpret_cast<const uint4*>(Vh + src);
-        }
+        stage_rows<T, D>(Ks, ROWB, Kh, g, w.wy, w.wx);
+        if (V_LDS) stage_rows<T, D>(Vs, ROWB, Vh, g, w.wy, w.wx);
         __syncthreads();
     }
 
     int coff[CH];   // lane-rotated chunk order for whole-row gathers
 #pragma unroll
     for (int m = 0; m < CH; ++m) coff[m] = ((m + lane) % CH) * 16;
-    const int vchunk = gl % CH;
-    const int vsub = gl / CH;
 
-    const int row0 = part * p.rows_per_block;
+    const int row0 = w.part * p.rows_per_block;
     const int row1 = min(N, row0 + p.rows_per_block);
     const int K_prev = p.K_prev;
-    const int K_l = p.K_l;
 
     for (int base = row0 + wave * RPW; base < row1; base += NW * RPW) {
         const int i_raw = base + grp;
         const bool active = i_raw < row1;
         const int i = active ? i_raw : row0;
-        const int qpix = slot_pixel(g, wy, wx, i);
-        const size_t row = (size_t)wh * N + i;
-        const size_t rowI = p.i_shared ? (size_t)(b * nwin + win_id) * N + i : row;
+        const int qpix = slot_pixel(g, w.wy, w.wx, i);
+        const size_t row = (size_t)w.wh * N + i;
+        const size_t rowI = p.i_shared ? (size_t)(w.b * w.nwin + w.win_id) * N + i : row;
 
         int jj[KPT];
         float av[KPT];
@@ -243,7 +437,6 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
 
         // SMM: scores over the candidate list only (base-2 units)
         float sv[KPT];
-        float smax = -INFINITY;
 #pragma unroll
         for (int t = 0; t < KPT; ++t) {
             const unsigned char* krow =
@@ -257,147 +450,206 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
                 for (int e = 0; e < EPC; ++e) acc = fmaf(qf[m * EPC + e], kf[e], acc);
             }
             sv[t] = valid[t] ? acc * p.scale2 : -INFINITY;
-            smax = fmaxf(smax, sv[t]);
         }
-        smax = G::all(smax, MaxF());
+        finish_row<T, D, GL, KPT, VS>(p, g, lane, active, row, qpix, w.wy, w.wx, jj, av, valid, sv, scr, SCG, Vs,
+                                      Vh, Oh);
+    }
+}
 
-        // u = A^{l-1} exp(s - m); key = bits of u (>= 0), -1 for no candidate
-        float uv[KPT];
-        int key[KPT];
-        int kmin = 0x7fffffff, kmax = -1;
+// MFMA operand helpers for the all-candidates layer: 16 independent 4x4 blocks;
+// lane l feeds row l%4 of block l/4 in the A operand and column l%4 of block l/4
+// in the B operand, and receives D[block][r][l%4] in accumulator register r.
+template <typename T>
+struct Mfma4;
+
+template <>
+struct Mfma4<float> {
+    static constexpr int kK = 1;   // contraction per instruction
+    __device__ static v4f run(const float* a, const float* b, v4f c) {
+        return __builtin_amdgcn_mfma_f32_4x4x1f32(a[0], b[0], c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mfma4<uint16_t> {
+    static constexpr int kK = 4;
+    __device__ static v4f run(const float* a, const float* b, v4f c) {
+        v4s x, y;
 #pragma unroll
-        for (int t = 0; t < KPT; ++t) {
-            uv[t] = valid[t] ? av[t] * fast_exp2(sv[t] - smax) : 0.0f;
-            key[t] = valid[t] ? __float_as_int(uv[t]) : -1;
-            if (valid[t]) {
-                kmin = min(kmin, key[t]);
-                kmax = max(kmax, key[t]);
-            }
+        for (int e = 0; e < 4; ++e) {
+            x[e] = (short)(__float_as_uint(a[e]) >> 16);   // exact: the values are bf16
+            y[e] = (short)(__float_as_uint(b[e]) >> 16);
         }
-        kmin = G::all_i(kmin, MinI());
-        kmax = G::all_i(kmax, MaxI());
+        return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(x, y, c, 0, 0, 0);
+    }
+};
 
-        // phase 1: narrow [lo, hi) until it holds at most kBand keys
-        int lo = kmin, hi = kmax + 1, c_lo = K_prev, c_hi = 0;
-        bool done = !active || hi - lo <= 1 || c_lo - c_hi <= kBand;
-        for (int it = 0; ballot(!done) != 0; ++it) {
-            const int span = hi - lo;
-            int mid;
-            if (it % 3 == 2) {
-                mid = lo + (span >> 1);
-            } else {
-                const float f = ((float)(c_lo - K_l) + 0.5f) / (float)max(c_lo - c_hi, 1);
-                mid = lo + (int)(f * (float)span);
-            }
-            mid = min(max(mid, lo + 1), hi - 1);
-            int cnt = 0;
-#pragma unroll
-            for (int t = 0; t < KPT; ++t) cnt += G::count(key[t] >= mid, lane);
-            if (!done) {
-                if (cnt >= K_l) { lo = mid; c_lo = cnt; } else { hi = mid; c_hi = cnt; }
-                done = hi - lo <= 1 || c_lo - c_hi <= kBand;
-            }
-        }
+// Layer whose candidate list is every slot of a 32x32 window (I^{l-1} implicit,
+// K_prev = N = 1024), e.g. the second layer after the dense one. Scores for 4
+// query rows x 64 candidates come from 4x4 MFMA blocks: A = the 4 query rows
+// (replicated over the blocks), B = the 64 candidate rows read from LDS, so
+// accumulator register r of lane l holds s(row r, candidate 64c + l), the
+// lane-strided layout the row finishing expects. K rows are staged with a
+// 16-byte pad so that 8 consecutive rows start in 8 different bank groups.
+template <typename T, int D, int VS>
+__global__ __launch_bounds__(8 * kWave) void all_cand_kernel(const SparseArgs p) {
+    constexpr int NW = 8;
+    constexpr int KPT = 16;
+    constexpr int GL = 64;
+    constexpr int EPC = Chunk<T>::kElems;
+    constexpr int CH = D / EPC;
+    constexpr int ROWB = D * (int)sizeof(T);
+    constexpr int KSTR = ROWB + 16;
+    constexpr int KK = Mfma4<T>::kK;
+    constexpr int SCW = kScratchBytes / 2 / (NW * 8);
+    extern __shared__ __align__(16) unsigned char smem[];
 
-        // phase 2: take the band's keys largest first until K_l are kept
-        int need = K_l - c_hi;
-        int tau = lo, need_tau = need, n_tau = 0;
-        bool done2 = !active;
-        while (ballot(!done2) != 0) {
-            int m = -1;
+    const Geom g = p.g;
+    const int N = g.N;   // 1024
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const WhPart w = decode_block(p.blocks_per_wh, p.xcd_map, g);
+    const size_t plane = (size_t)w.bh * g.H * g.W * D;
+    const T* Qh = static_cast<const T*>(p.Q) + plane;
+    const T* Kh = static_cast<const T*>(p.K) + plane;
+    const T* Vh = static_cast<const T*>(p.V) + plane;
+    float* Oh = p.O_out + plane;
+
+    unsigned char* Ks = smem;
+    unsigned char* Vs = smem + N * KSTR;
+    uint2* scr = reinterpret_cast<uint2*>(Vs + (VS == kVlds ? N * ROWB : 0)) + wave * SCW;
+    stage_rows<T, D>(Ks, KSTR, Kh, g, w.wy, w.wx);
+    if (VS == kVlds) stage_rows<T, D>(Vs, ROWB, Vh, g, w.wy, w.wx);
+    __syncthreads();
+
+    const int row0 = w.part * p.rows_per_block;
+    const int row1 = min(N, row0 + p.rows_per_block);
+    int jj[KPT];
+    bool valid[KPT];
 #pragma unroll
-            for (int t = 0; t < KPT; ++t)
-                if (key[t] >= lo && key[t] < hi) m = max(m, key[t]);
-            m = G::all_i(m, MaxI());
-            int ceq = 0;
+    for (int t = 0; t < KPT; ++t) jj[t] = lane + kWave * t;
+
+    for (int base = row0 + wave * 4; base < row1; base += NW * 4) {
+        // A operand: query row base + lane%4 (rows past row1 compute garbage, never stored)
+        const int qi = min(base + (lane & 3), row1 - 1);
+        float qf[D];
+        const unsigned char* qrow =
+            reinterpret_cast<const unsigned char*>(Qh + (size_t)slot_pixel(g, w.wy, w.wx, qi) * D);
 #pragma unroll
-            for (int t = 0; t < KPT; ++t) ceq += G::count(key[t] == m, lane);
-            if (!done2) {
-                if (ceq >= need) {
-                    tau = m; need_tau = need; n_tau = ceq; done2 = true;
-                } else {
-                    need -= ceq; hi = m;
+        for (int m = 0; m < CH; ++m) Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(qrow + 16 * m), &qf[m * EPC]);
+
+        float s4[4][KPT];
+#pragma unroll
+        for (int t = 0; t < KPT; t += 2) {
+            v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+            const unsigned char* k0 = Ks + (kWave * t + lane) * KSTR;
+            const unsigned char* k1 = k0 + kWave * KSTR;
+#pragma unroll
+            for (int m = 0; m < CH; ++m) {
+                float kf0[EPC], kf1[EPC];
+                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(k0 + 16 * m), kf0);
+                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(k1 + 16 * m), kf1);
+#pragma unroll
+                for (int e = 0; e < EPC; e += KK) {
+                    acc0 = Mfma4<T>::run(&qf[m * EPC + e], &kf0[e], acc0);
+                    acc1 = Mfma4<T>::run(&qf[m * EPC + e], &kf1[e], acc1);
                 }
             }
-        }
-
-        // exact ties at the threshold: keep the lowest slot indices
-        int jcut = 0x7fffffff;
-        const bool tie = active && n_tau > need_tau;
-        if (ballot(tie) != 0) {
-            int jl = -1, jh = N - 1;
-            while (ballot(tie && jh - jl > 1) != 0) {
-                const int mid = (jl + jh) >> 1;
-                int cnt = 0;
 #pragma unroll
-                for (int t = 0; t < KPT; ++t) cnt += G::count(key[t] == tau && jj[t] <= mid, lane);
-                if (tie && jh - jl > 1) {
-                    if (cnt >= need_tau) jh = mid; else jl = mid;
-                }
+            for (int r = 0; r < 4; ++r) {
+                s4[r][t] = acc0[r] * p.scale2;
+                s4[r][t + 1] = acc1[r] * p.scale2;
             }
-            if (tie) jcut = jh;
         }
 
-        bool kept[KPT];
-        float ksum = 0.0f;
+#pragma unroll 1
+        for (int r = 0; r < 4; ++r) {
+            const int i = base + r;
+            const bool active = i < row1;
+            const int ii = active ? i : row0;
+            const size_t row = (size_t)w.wh * N + ii;
+            float av[KPT], sv[KPT];
 #pragma unroll
-        for (int t = 0; t < KPT; ++t) {
-            kept[t] = key[t] > tau || (key[t] == tau && jj[t] <= jcut);
-            ksum += kept[t] ? uv[t] : 0.0f;
-        }
-        const float inv = 1.0f / G::all(ksum, SumF());
-
-        // kept entries in I^{l-1} order
-        int pos[KPT];
-        int obase = 0;
-        int32_t* Io = p.I_out + row * K_l;
-        float* Ao = p.A_out + row * K_l;
-#pragma unroll
-        for (int t = 0; t < KPT; ++t) {
-            const uint64_t m = ballot(kept[t]);
-            pos[t] = kept[t] ? obase + G::below(m, lane) : -1;
-            if (pos[t] >= K_l) pos[t] = -1;   // only on precondition violations
-            uv[t] *= inv;
-            if (pos[t] >= 0) {
-                Io[pos[t]] = jj[t];
-                Ao[pos[t]] = uv[t];
+            for (int t = 0; t < KPT; ++t) {
+                valid[t] = active;
+                av[t] = p.A_prev ? p.A_prev[row * N + jj[t]] : 1.0f;
+                // register select (r is a loop variable: indexing s4[r] would spill to scratch)
+                sv[t] = r == 0 ? s4[0][t] : r == 1 ? s4[1][t] : r == 2 ? s4[2][t] : s4[3][t];
             }
-            obase += G::count_mask(m, lane);
+            finish_row<T, D, GL, KPT, VS>(p, g, lane, active, row, slot_pixel(g, w.wy, w.wx, ii), w.wy, w.wx, jj,
+                                          av, valid, sv, scr, SCW, Vs, Vh, Oh);
         }
+    }
+}
 
-        // O_i = sum_kept A v_j
+// O_i = sum_j A^l_ij v_j from stored (I^l, A^l) rows, V of the window in LDS: the
+// second half of a layer whose K and V do not fit in LDS together.
+template <typename T, int D, int GL, int NW>
+__global__ __launch_bounds__(NW * kWave) void aggregate_kernel(const SparseArgs p) {
+    constexpr int EPC = Chunk<T>::kElems;
+    constexpr int CH = D / EPC;
+    constexpr int ROWB = D * (int)sizeof(T);
+    constexpr int RPW = kWave / GL;
+    constexpr int GS = GL / CH;   // entries in flight per row
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const Geom g = p.g;
+    const int N = g.N;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int grp = lane / GL;
+    const int gl = lane & (GL - 1);
+    const int vchunk = gl % CH;
+    const int vsub = gl / CH;
+    const WhPart w = decode_block(p.blocks_per_wh, p.xcd_map, g);
+    const size_t plane = (size_t)w.bh * g.H * g.W * D;
+    const T* Vh = static_cast<const T*>(p.V) + plane;
+    float* Oh = p.O_out + plane;
+    stage_rows<T, D>(smem, ROWB, Vh, g, w.wy, w.wx);
+    __syncthreads();
+
+    const int row0 = w.part * p.rows_per_block;
+    const int row1 = min(N, row0 + p.rows_per_block);
+    const int K_l = p.K_l;
+    for (int base = row0 + wave * RPW; base < row1; base += NW * RPW) {
+        const int i_raw = base + grp;
+        const bool active = i_raw < row1;
+        const int i = active ? i_raw : row0;
+        const size_t row = (size_t)w.wh * N + i;
+        const int32_t* Ir = p.I_out + row * K_l;
+        const float* Ar = p.A_out + row * K_l;
         float oacc[EPC];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) oacc[e] = 0.0f;
-        for (int P0 = 0; P0 < K_l; P0 += SCG) {
+        for (int x = 0; x < EPC; ++x) oacc[x] = 0.0f;
+        const int cnt = active ? K_l : 0;
+        for (int e0 = vsub * 4; e0 < cnt; e0 += 4 * GS) {
+            int jv[4];
+            float wv[4];
+            if ((K_l & 3) == 0 && e0 + 4 <= cnt) {   // 16-byte aligned rows
+                const int4 j4 = *reinterpret_cast<const int4*>(Ir + e0);
+                const float4 w4 = *reinterpret_cast<const float4*>(Ar + e0);
+                jv[0] = j4.x; jv[1] = j4.y; jv[2] = j4.z; jv[3] = j4.w;
+                wv[0] = w4.x; wv[1] = w4.y; wv[2] = w4.z; wv[3] = w4.w;
+            } else {
 #pragma unroll
-            for (int t = 0; t < KPT; ++t)
-                if (pos[t] >= P0 && pos[t] < P0 + SCG)
-                    scr[pos[t] - P0] = make_uint2((uint32_t)jj[t], __float_as_uint(uv[t]));
-            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            const int cnt = active ? min(SCG, K_l - P0) : 0;
-            for (int e = vsub; e < cnt; e += GS) {
-                const uint2 ent = scr[e];
-                const float w = __uint_as_float(ent.y);
-                const unsigned char* vrow;
-                if (V_LDS) {
-                    vrow = Vs + ent.x * ROWB;
-                } else if (K_LDS) {
-                    vrow = reinterpret_cast<const unsigned char*>(Vh + (size_t)slot_pixel(g, wy, wx, (int)ent.x) * D);
-                } else {
-                    vrow = reinterpret_cast<const unsigned char*>(Vh + (size_t)ent.x * D);
+                for (int x = 0; x < 4; ++x) {
+                    jv[x] = e0 + x < cnt ? Ir[e0 + x] : 0;
+                    wv[x] = e0 + x < cnt ? Ar[e0 + x] : 0.0f;
                 }
-                float vf[EPC];
-                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(vrow + vchunk * 16), vf);
-#pragma unroll
-                for (int x = 0; x < EPC; ++x) oacc[x] = fmaf(w, vf[x], oacc[x]);
             }
-            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int j = min(max(jv[x], 0), N - 1);
+                float vf[EPC];
+                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(smem + j * ROWB + vchunk * 16), vf);
+#pragma unroll
+                for (int y = 0; y < EPC; ++y) oacc[y] = fmaf(wv[x], vf[y], oacc[y]);
+            }
         }
 #pragma unroll
         for (int x = 0; x < EPC; ++x) oacc[x] = reduce_chunk_lanes<CH, GL>(oacc[x]);
         if (active && vsub == 0) {
-            float* orow = Oh + (size_t)qpix * D + vchunk * EPC;
+            float* orow = Oh + (size_t)slot_pixel(g, w.wy, w.wx, i) * D + vchunk * EPC;
 #pragma unroll
             for (int x = 0; x < EPC; x += 4)
                 *reinterpret_cast<float4*>(orow + x) = make_float4(oacc[x], oacc[x + 1], oacc[x + 2], oacc[x + 3]);
@@ -405,15 +657,19 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
     }
 }
 
+template <class F>
+hipError_t launch_fn(F fn, const SparseArgs& a, int threads, int lds, int grid, hipStream_t s) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(threads), lds, s, a);
+    return hipGetLastError();
+}
+
 template <typename T, int D, int GL, int KPT, int MODE>
 hipError_t launch_one(const SparseArgs& a, int lds, int grid, hipStream_t s) {
     constexpr int NW = KPT <= 4 ? 16 : 8;
-    auto fn = sparse_layer_kernel<T, D, GL, KPT, MODE, NW>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(NW * kWave), lds, s, a);
-    return hipGetLastError();
+    return launch_fn(sparse_layer_kernel<T, D, GL, KPT, MODE, NW>, a, NW * kWave, lds, grid, s);
 }
 
 template <typename T, int D, int GL, int KPT>
@@ -421,6 +677,7 @@ hipError_t launch_mode(const SparseArgs& a, SparseMode mode, int lds, int grid, 
     switch (mode) {
         case kKVinLDS: return launch_one<T, D, GL, KPT, kKVinLDS>(a, lds, grid, s);
         case kKinLDS: return launch_one<T, D, GL, KPT, kKinLDS>(a, lds, grid, s);
+        case kKselect: return launch_one<T, D, GL, KPT, kKselect>(a, lds, grid, s);
         default: return launch_one<T, D, GL, KPT, kKVglobal>(a, lds, grid, s);
     }
 }
@@ -437,6 +694,23 @@ hipError_t launch_shape(const SparseArgs& a, SparseMode mode, int lds, int grid,
     return launch_mode<T, D, 64, 16>(a, mode, lds, grid, s);
 }
 
+template <typename T, int D>
+hipError_t launch_all_cand_t(const SparseArgs& a, bool with_av, int grid, hipStream_t s) {
+    constexpr int ROWB = D * (int)sizeof(T);
+    const int lds_k = 1024 * (ROWB + 16);
+    if (with_av)
+        return launch_fn(all_cand_kernel<T, D, kVlds>, a, 8 * kWave, lds_k + 1024 * ROWB + kScratchBytes / 2, grid, s);
+    return launch_fn(all_cand_kernel<T, D, kVnone>, a, 8 * kWave, lds_k, grid, s);
+}
+
+template <typename T, int D>
+hipError_t launch_aggregate_t(const SparseArgs& a, int grid, hipStream_t s) {
+    const int lds = a.g.N * D * (int)sizeof(T);
+    if (a.K_l <= 16) return launch_fn(aggregate_kernel<T, D, 16, 16>, a, 16 * kWave, lds, grid, s);
+    if (a.K_l <= 32) return launch_fn(aggregate_kernel<T, D, 32, 16>, a, 16 * kWave, lds, grid, s);
+    return launch_fn(aggregate_kernel<T, D, 64, 16>, a, 16 * kWave, lds, grid, s);
+}
+
 }  // namespace
 
 hipError_t launch_sparse(const SparseArgs& a, int dtype, int D, SparseMode mode, int lds_bytes, int grid,
@@ -446,6 +720,26 @@ hipError_t launch_sparse(const SparseArgs& a, int dtype, int D, SparseMode mode,
                        : launch_shape<float, 32>(a, mode, lds_bytes, grid, stream);
     return D == 16 ? launch_shape<uint16_t, 16>(a, mode, lds_bytes, grid, stream)
                    : launch_shape<uint16_t, 32>(a, mode, lds_bytes, grid, stream);
+}
+
+bool all_cand_fits_with_v(int dtype, int D) {
+    const int rowb = D * (dtype == 0 ? 4 : 2);
+    return 1024 * (rowb + 16) + 1024 * rowb + kScratchBytes / 2 <= kLdsBytes;
+}
+
+hipError_t launch_all_cand(const SparseArgs& a, int dtype, int D, bool with_av, int grid, hipStream_t stream) {
+    if (dtype == 0)
+        return D == 16 ? launch_all_cand_t<float, 16>(a, with_av, grid, stream)
+                       : launch_all_cand_t<float, 32>(a, with_av, grid, stream);
+    return D == 16 ? launch_all_cand_t<uint16_t, 16>(a, with_av, grid, stream)
+                   : launch_all_cand_t<uint16_t, 32>(a, with_av, grid, stream);
+}
+
+hipError_t launch_aggregate(const SparseArgs& a, int dtype, int D, int grid, hipStream_t stream) {
+    if (dtype == 0)
+        return D == 16 ? launch_aggregate_t<float, 16>(a, grid, stream) : launch_aggregate_t<float, 32>(a, grid, stream);
+    return D == 16 ? launch_aggregate_t<uint16_t, 16>(a, grid, stream)
+                   : launch_aggregate_t<uint16_t, 32>(a, grid, stream);
 }
 
 }  // namespace pfa
