@@ -56,6 +56,8 @@ def main():
     ap.add_argument("--workload", default="map256x256_h6_d32_f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=64, help="window-heads timed on the CPU oracle")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -64,6 +66,15 @@ def main():
 
     import torch
     from sparse_progressive_window_amd import inputs, pfa, workloads
+
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": src.numel() * 4, "copies": 3}), flush=True)
+        return
 
     w = workloads.BY_NAME[args.workload]
     assert w.win, "the chain benchmark needs a window workload"

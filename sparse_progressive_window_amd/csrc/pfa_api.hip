@@ -140,7 +140,8 @@ int pfa_dense_layer(const pfa_shape* shape, const void* Q, const void* K, const 
     a.A_out = A_out; a.O_out = O_out;
     a.g = g;
     a.scale2 = (float)(1.4426950408889634 / sqrt((double)g.d));
-    const int64_t grid = n_wh(g) * ((g.N + 63) / 64);
+    a.xcd_map = (n_wh(g) % 8 == 0) ? 1 : 0;
+    const int64_t grid = n_wh(g) * pfa::dense_query_blocks(g.N);
     if (grid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
     hipError_t e = pfa::launch_dense(a, shape->dtype, g.d, (int)grid, s);
     if (e == hipSuccess && I_out) e = pfa::launch_iota_rows(I_out, n_wh(g) * g.N, g.N, s);

@@ -5,17 +5,22 @@
 // Super-Resolution", section "Progressive focused resource allocation
 // strategy"): A^1 = softmax(Q K^T / sqrt(d)) per window-head, O = A^1 V.
 //
-// One wave owns 16 query rows. Scores are produced transposed, S^T = K Q^T, with
-// 16x16 MFMA tiles (16 keys x 16 queries): the accumulator layout then gives each
-// lane 4 consecutive keys of one query, which is exactly the A-operand layout of
-// the following P.V MFMA, so probabilities never leave registers. The
-// contraction index of the score MFMAs is permuted so that every lane reads a
-// contiguous run of d/4 elements of its K and Q rows.
+// A workgroup of 8 waves owns 128 query rows of one window-head (16 per wave);
+// K and V stream through LDS in tiles of 64 keys, double-buffered, shared by
+// all 8 waves (rows padded by 16 bytes so the MFMA operand reads of 16
+// consecutive rows hit distinct banks). The workgroups of one window-head are
+// consecutive on one XCD, so its K/V stay in that XCD's L2.
+//
+// Scores are produced transposed, S^T = K Q^T, with 16x16 MFMA tiles (16 keys x
+// 16 queries): the accumulator gives each lane 4 consecutive keys of one query,
+// which is exactly the A-operand layout of the following P.V MFMA, so the
+// probabilities never leave registers. The contraction index of the score
+// MFMAs is permuted so every lane reads a contiguous run of d/4 elements.
 //   fp32 inputs: v_mfma_f32_16x16x4_f32 (exact products, fp32 accumulation).
 //   bf16 inputs: v_mfma_f32_16x16x16_bf16; P is split into bf16 hi + lo parts
 //   (two MFMAs) so the P.V product keeps ~16 bits of P.
 // Two passes over the keys: (1) running row max / row sum, (2) recompute the
-// scores, write A^1 (optional) and accumulate O.
+// scores, write A^1 rows (optional) and accumulate O.
 #include "pfa_kernels.h"
 
 namespace pfa {
@@ -23,6 +28,9 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
+
+constexpr int kDenseWaves = 8;
+constexpr int kQPerBlock = 16 * kDenseWaves;
 
 template <typename T, int D>
 struct DenseOps;
@@ -32,10 +40,11 @@ struct DenseOps;
 template <int D>
 struct DenseOps<float, D> {
     static constexpr int DPL = D / 4;
+    static constexpr int ROWB = D * 4;
     struct Row { float v[DPL]; };
-    __device__ static Row load(const float* row, int grp) {
+    __device__ static Row load(const unsigned char* row, int grp) {
         Row r;
-        const float* src = row + grp * DPL;
+        const float* src = reinterpret_cast<const float*>(row) + grp * DPL;
 #pragma unroll
         for (int x = 0; x < DPL; x += 4) {
             const float4 f = *reinterpret_cast<const float4*>(src + x);
@@ -49,12 +58,13 @@ struct DenseOps<float, D> {
         for (int x = 0; x < DPL; ++x) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.v[x], q.v[x], acc, 0, 0, 0);
         return acc;
     }
-    // O tile (16 queries x 16 dims) += P (16 q x 16 keys) . V (16 keys x 16 dims)
-    // p[r]: weight of key 4*grp + r for query r16. vk: V rows of keys 4*grp + r, this lane's dim.
-    __device__ static v4f pv(const float p[4], const float* vbase, size_t vstride[4], int dim, v4f acc) {
+    // O tile (16 queries x 16 dims) += P (16 q x 16 keys) . V (16 keys x 16 dims);
+    // p[r]: weight of key 4*grp + r for query r16; vrow[r]: LDS rows of those keys.
+    __device__ static v4f pv(const float p[4], const unsigned char* const vrow[4], int dim, v4f acc) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(p[r], vbase[vstride[r] + dim], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(p[r], reinterpret_cast<const float*>(vrow[r])[dim], acc, 0,
+                                                       0, 0);
         return acc;
     }
 };
@@ -64,10 +74,11 @@ struct DenseOps<float, D> {
 template <int D>
 struct DenseOps<uint16_t, D> {
     static constexpr int DPL = D / 4;
+    static constexpr int ROWB = D * 2;
     struct Row { v4s v[DPL / 4]; };
-    __device__ static Row load(const uint16_t* row, int grp) {
+    __device__ static Row load(const unsigned char* row, int grp) {
         Row r;
-        const uint16_t* src = row + grp * DPL;
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(row) + grp * DPL;
 #pragma unroll
         for (int x = 0; x < DPL / 4; ++x) {
             const uint2 u = *reinterpret_cast<const uint2*>(src + 4 * x);
@@ -83,7 +94,7 @@ struct DenseOps<uint16_t, D> {
             acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(k.v[x], q.v[x], acc, 0, 0, 0);
         return acc;
     }
-    __device__ static v4f pv(const float p[4], const uint16_t* vbase, size_t vstride[4], int dim, v4f acc) {
+    __device__ static v4f pv(const float p[4], const unsigned char* const vrow[4], int dim, v4f acc) {
         v4s hi, lo, vv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -91,7 +102,7 @@ struct DenseOps<uint16_t, D> {
             const float rem = p[r] - __uint_as_float(h << 16);
             hi[r] = (short)h;
             lo[r] = (short)f32_to_bf16_bits(rem);
-            vv[r] = (short)vbase[vstride[r] + dim];
+            vv[r] = (short)reinterpret_cast<const uint16_t*>(vrow[r])[dim];
         }
         acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, vv, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, vv, acc, 0, 0, 0);
@@ -99,44 +110,110 @@ struct DenseOps<uint16_t, D> {
     }
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void dense_layer_kernel(const DenseArgs p) {
+// Copy rows [key0, key0 + KT) of a window (slot order) into an LDS tile with a
+// padded row stride; one 16-byte chunk per thread and step.
+template <int ROWB, int KT>
+__device__ __forceinline__ void tile_load(uint4 (&reg)[(KT * ROWB / 16 + kDenseWaves * kWave - 1) /
+                                                       (kDenseWaves * kWave)],
+                                          const unsigned char* plane, const Geom& g, int wy, int wx, int key0) {
+    constexpr int CH = ROWB / 16;
+    constexpr int UNITS = KT * CH;
+    constexpr int PER = (UNITS + kDenseWaves * kWave - 1) / (kDenseWaves * kWave);
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+        const int u = threadIdx.x + x * kDenseWaves * kWave;
+        if (u < UNITS) {
+            const int t = u / CH;
+            const int c = u - t * CH;
+            reg[x] = *reinterpret_cast<const uint4*>(plane + (size_t)slot_pixel(g, wy, wx, key0 + t) * ROWB + c * 16);
+        }
+    }
+}
+template <int ROWB, int KT, int STRIDE>
+__device__ __forceinline__ void tile_store(unsigned char* dst,
+                                           const uint4 (&reg)[(KT * ROWB / 16 + kDenseWaves * kWave - 1) /
+                                                              (kDenseWaves * kWave)]) {
+    constexpr int CH = ROWB / 16;
+    constexpr int UNITS = KT * CH;
+    constexpr int PER = (UNITS + kDenseWaves * kWave - 1) / (kDenseWaves * kWave);
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+        const int u = threadIdx.x + x * kDenseWaves * kWave;
+        if (u < UNITS) {
+            const int t = u / CH;
+            const int c = u - t * CH;
+            *reinterpret_cast<uint4*>(dst + t * STRIDE + c * 16) = reg[x];
+        }
+    }
+}
+
+template <typename T, int D, int KT>
+__global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const DenseArgs p) {
     using Ops = DenseOps<T, D>;
+    constexpr int ROWB = Ops::ROWB;
+    constexpr int STRIDE = ROWB + 16;             // padded LDS row
+    constexpr int SUB = KT / 16;                   // 16-key MFMA tiles per LDS tile
+    constexpr int CT = D / 16;                     // 16-dim output tiles
+    constexpr int PER = (KT * ROWB / 16 + kDenseWaves * kWave - 1) / (kDenseWaves * kWave);
+    __shared__ __align__(16) unsigned char Ks[2][KT * STRIDE];
+    __shared__ __align__(16) unsigned char Vs[2][KT * STRIDE];
+
     const Geom g = p.g;
     const int N = g.N;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int r16 = lane & 15;
     const int grp = lane >> 4;
-    const int qblocks = (N + 63) / 64;
-    const int wh = blockIdx.x / qblocks;
-    const int q0 = (blockIdx.x - wh * qblocks) * 64 + wave * 16;
-    if (q0 >= N) return;
+    const int qblocks = (N + kQPerBlock - 1) / kQPerBlock;
+    int wh, qb;
+    if (p.xcd_map) {   // the query blocks of one window-head are consecutive workgroups of one XCD
+        const int xcd = blockIdx.x & 7;
+        const int slot = blockIdx.x >> 3;
+        qb = slot % qblocks;
+        wh = (slot / qblocks) * 8 + xcd;
+    } else {
+        wh = blockIdx.x / qblocks;
+        qb = blockIdx.x - wh * qblocks;
+    }
+    const int q0 = qb * kQPerBlock + wave * 16;
+    const bool wave_active = q0 < N;   // idle waves still take part in the tile barriers
     const int nwin = g.nwy * g.nwx;
     const int win_id = wh % nwin;
     const int bh = wh / nwin;
     const int wy = win_id / g.nwx;
     const int wx = win_id - wy * g.nwx;
     const size_t plane = (size_t)bh * g.H * g.W * D;
-    const T* Qh = static_cast<const T*>(p.Q) + plane;
-    const T* Kh = static_cast<const T*>(p.K) + plane;
-    const T* Vh = static_cast<const T*>(p.V) + plane;
+    const unsigned char* Qh = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.Q) + plane);
+    const unsigned char* Kh = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.K) + plane);
+    const unsigned char* Vh = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.V) + plane);
     float* Oh = p.O_out + plane;
     const float sc = p.scale2;
 
-    const typename Ops::Row qop = Ops::load(Qh + (size_t)slot_pixel(g, wy, wx, q0 + r16) * D, grp);
-    const int ntiles = N / 16;
+    const int qrow = wave_active ? q0 + r16 : 0;
+    const typename Ops::Row qop = Ops::load(Qh + (size_t)slot_pixel(g, wy, wx, qrow) * ROWB, grp);
+    const int ntiles = N / KT;
+    uint4 kreg[PER], vreg[PER];
 
-    // pass 1: per-lane running max / sum over the keys 4*grp + r of every tile
+    // pass 1: per-lane running max / sum over the keys 4*grp + r of every 16-key tile
     float m = -INFINITY, l = 0.0f;
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const typename Ops::Row kop = Ops::load(Kh + (size_t)slot_pixel(g, wy, wx, kt * 16 + r16) * D, grp);
-        const v4f acc = Ops::scores(kop, qop);
-        const float s0 = acc[0] * sc, s1 = acc[1] * sc, s2 = acc[2] * sc, s3 = acc[3] * sc;
-        const float mn = fmaxf(m, fmaxf(fmaxf(s0, s1), fmaxf(s2, s3)));
-        l = l * fast_exp2(m - mn) + fast_exp2(s0 - mn) + fast_exp2(s1 - mn) + fast_exp2(s2 - mn) +
-            fast_exp2(s3 - mn);
-        m = mn;
+    tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, 0);
+    tile_store<ROWB, KT, STRIDE>(Ks[0], kreg);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles) tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, (t + 1) * KT);
+        const unsigned char* kt = Ks[t & 1];
+#pragma unroll
+        for (int s = 0; s < SUB; ++s) {
+            const typename Ops::Row kop = Ops::load(kt + (s * 16 + r16) * STRIDE, grp);
+            const v4f acc = Ops::scores(kop, qop);
+            const float s0 = acc[0] * sc, s1 = acc[1] * sc, s2 = acc[2] * sc, s3 = acc[3] * sc;
+            const float mn = fmaxf(m, fmaxf(fmaxf(s0, s1), fmaxf(s2, s3)));
+            l = l * fast_exp2(m - mn) + fast_exp2(s0 - mn) + fast_exp2(s1 - mn) + fast_exp2(s2 - mn) +
+                fast_exp2(s3 - mn);
+            m = mn;
+        }
+        if (t + 1 < ntiles) tile_store<ROWB, KT, STRIDE>(Ks[(t + 1) & 1], kreg);
+        __syncthreads();
     }
     // combine the 4 lane groups holding the same query
 #pragma unroll
@@ -150,25 +227,44 @@ __global__ __launch_bounds__(256) void dense_layer_kernel(const DenseArgs p) {
     const float inv_l = 1.0f / l;
 
     // pass 2: probabilities, A^1 rows, O += P V
-    constexpr int CT = D / 16;
     v4f oacc[CT];
 #pragma unroll
     for (int c = 0; c < CT; ++c) oacc[c] = v4f{0.f, 0.f, 0.f, 0.f};
-    float* Arow = p.A_out ? p.A_out + ((size_t)wh * N + q0 + r16) * N : nullptr;
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const typename Ops::Row kop = Ops::load(Kh + (size_t)slot_pixel(g, wy, wx, kt * 16 + r16) * D, grp);
-        const v4f acc = Ops::scores(kop, qop);
-        float pr[4];
+    float* Arow = (p.A_out && wave_active) ? p.A_out + ((size_t)wh * N + q0 + r16) * N : nullptr;
+    tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, 0);
+    tile_load<ROWB, KT>(vreg, Vh, g, wy, wx, 0);
+    tile_store<ROWB, KT, STRIDE>(Ks[0], kreg);
+    tile_store<ROWB, KT, STRIDE>(Vs[0], vreg);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles) {
+            tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, (t + 1) * KT);
+            tile_load<ROWB, KT>(vreg, Vh, g, wy, wx, (t + 1) * KT);
+        }
+        const unsigned char* kt = Ks[t & 1];
+        const unsigned char* vt = Vs[t & 1];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(acc[r] * sc - m) * inv_l;
-        if (Arow)
-            *reinterpret_cast<float4*>(Arow + kt * 16 + 4 * grp) = make_float4(pr[0], pr[1], pr[2], pr[3]);
-        size_t vrow[4];
+        for (int s = 0; s < SUB; ++s) {
+            const typename Ops::Row kop = Ops::load(kt + (s * 16 + r16) * STRIDE, grp);
+            const v4f acc = Ops::scores(kop, qop);
+            float pr[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vrow[r] = (size_t)slot_pixel(g, wy, wx, kt * 16 + 4 * grp + r) * D;
+            for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(acc[r] * sc - m) * inv_l;
+            if (Arow)
+                *reinterpret_cast<float4*>(Arow + t * KT + s * 16 + 4 * grp) = make_float4(pr[0], pr[1], pr[2], pr[3]);
+            const unsigned char* vrow[4];
 #pragma unroll
-        for (int c = 0; c < CT; ++c) oacc[c] = Ops::pv(pr, Vh, vrow, c * 16 + r16, oacc[c]);
+            for (int r = 0; r < 4; ++r) vrow[r] = vt + (s * 16 + 4 * grp + r) * STRIDE;
+#pragma unroll
+            for (int c = 0; c < CT; ++c) oacc[c] = Ops::pv(pr, vrow, c * 16 + r16, oacc[c]);
+        }
+        if (t + 1 < ntiles) {
+            tile_store<ROWB, KT, STRIDE>(Ks[(t + 1) & 1], kreg);
+            tile_store<ROWB, KT, STRIDE>(Vs[(t + 1) & 1], vreg);
+        }
+        __syncthreads();
     }
+    if (!wave_active) return;
     // lane holds O[query q0 + 4*grp + r][dim 16c + r16]
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -184,15 +280,25 @@ __global__ void iota_rows_kernel(int32_t* I, int64_t total, int N) {
         I[x] = (int32_t)(x % N);
 }
 
+template <typename T, int D>
+void launch_dense_t(const DenseArgs& a, int grid, hipStream_t s) {
+    if (a.g.N % 64 == 0)
+        hipLaunchKernelGGL((dense_layer_kernel<T, D, 64>), dim3(grid), dim3(kDenseWaves * kWave), 0, s, a);
+    else
+        hipLaunchKernelGGL((dense_layer_kernel<T, D, 16>), dim3(grid), dim3(kDenseWaves * kWave), 0, s, a);
+}
+
 }  // namespace
+
+int dense_query_blocks(int N) { return (N + kQPerBlock - 1) / kQPerBlock; }
 
 hipError_t launch_dense(const DenseArgs& a, int dtype, int D, int grid, hipStream_t stream) {
     if (dtype == 0) {
-        if (D == 16) hipLaunchKernelGGL((dense_layer_kernel<float, 16>), dim3(grid), dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((dense_layer_kernel<float, 32>), dim3(grid), dim3(256), 0, stream, a);
+        if (D == 16) launch_dense_t<float, 16>(a, grid, stream);
+        else launch_dense_t<float, 32>(a, grid, stream);
     } else {
-        if (D == 16) hipLaunchKernelGGL((dense_layer_kernel<uint16_t, 16>), dim3(grid), dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((dense_layer_kernel<uint16_t, 32>), dim3(grid), dim3(256), 0, stream, a);
+        if (D == 16) launch_dense_t<uint16_t, 16>(a, grid, stream);
+        else launch_dense_t<uint16_t, 32>(a, grid, stream);
     }
     return hipGetLastError();
 }

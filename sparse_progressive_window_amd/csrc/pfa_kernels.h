@@ -42,6 +42,7 @@ struct DenseArgs {
     float* O_out;
     Geom g;
     float scale2;
+    int xcd_map;             // 1: the query blocks of a window-head run on one XCD (needs #wh % 8 == 0)
 };
 
 hipError_t launch_sparse(const SparseArgs& a, int dtype, int D, SparseMode mode, int lds_bytes, int grid,
@@ -51,6 +52,7 @@ bool all_cand_fits_with_v(int dtype, int D);
 hipError_t launch_all_cand(const SparseArgs& a, int dtype, int D, bool with_av, int grid, hipStream_t stream);
 // O from stored (I^l, A^l) rows with V in LDS (window mode).
 hipError_t launch_aggregate(const SparseArgs& a, int dtype, int D, int grid, hipStream_t stream);
+int dense_query_blocks(int N);   // workgroups per window-head of the dense layer
 hipError_t launch_dense(const DenseArgs& a, int dtype, int D, int grid, hipStream_t stream);
 hipError_t launch_iota_rows(int32_t* I, int64_t rows, int N, hipStream_t stream);
 
