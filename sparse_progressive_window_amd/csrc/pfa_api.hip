@@ -94,7 +94,7 @@ int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const voi
         e = pfa::launch_sparse(a, dtype, g.d, pfa::kKVinLDS, 2 * g.N * rowb + pfa::kScratchBytes, grid, stream);
     } else {
         // K and V do not fit in LDS together: select with K in LDS, then aggregate with V in LDS
-        e = pfa::launch_sparse(a, dtype, g.d, pfa::kKselect, g.N * rowb, grid, stream);
+        e = pfa::launch_sparse(a, dtype, g.d, pfa::kKselect, g.N * rowb + pfa::kScratchBytes, grid, stream);
         aggregate = true;
     }
     if (e == hipSuccess && aggregate) e = pfa::launch_aggregate(a, dtype, g.d, grid, stream);

@@ -19,13 +19,13 @@
 // 8 different chunks and a 128-byte row never bank-conflicts.
 //
 // Top-K. Keys are the fp32 bit patterns of u (u >= 0, so integer order = float
-// order). A search on the key interval [lo, hi) with count(key >= lo) >= K_l >
-// count(key >= hi) narrows the interval by interpolation in bit space (that is,
-// in log u), with a bisection step every third iteration, until at most kBand
-// keys remain in it; those are then extracted largest first. Counts use wave
-// ballots; every reduction inside a group uses DPP (quad permutes, row
-// rotations), ds_swizzle for the 16-lane half swap and readlane across halves.
-// Ties at the threshold keep the lowest slot indices (bisection on j).
+// order). The K_l-th largest key is found exactly by radix descent: the current
+// key interval is split into GL bit-field bins counted with LDS atomics, a DPP
+// prefix scan over the bins (descending) locates the bin holding the K_l-th key,
+// and the search recurses into it; keys in higher bins are kept, lower ones are
+// dropped. Reductions inside a group use DPP (quad permutes, row rotations, row
+// broadcasts), ds_swizzle for the 16-lane half swap and readlane across halves.
+// Exact ties at the threshold keep the lowest slot indices (bisection on j).
 //
 // Kept entries are compacted in I^{l-1} order (ballot + lane-prefix counts) and
 // staged in LDS as (j, weight); the aggregation then gives each V row chunk to
@@ -36,7 +36,6 @@
 namespace pfa {
 namespace {
 
-constexpr int kBand = 8;
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -89,6 +88,18 @@ struct Grp {
         if (GL >= 32) v = op(v, swap16(v));
         if (GL == 64) v = op(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 32));
         return v;
+    }
+    static constexpr int kLog2 = GL == 64 ? 6 : GL == 32 ? 5 : 4;
+    // inclusive prefix sum over the lanes of the group (row_shr steps, then row
+    // broadcasts across the 16-lane rows)
+    __device__ static unsigned incl_scan(unsigned x) {
+        x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+        x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+        x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+        x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+        if (GL >= 32) x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+        if (GL == 64) x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+        return x;
     }
     // bits of the wave mask m that belong to this lane's group
     __device__ static uint32_t bits(uint64_t m, int lane) {
@@ -149,15 +160,30 @@ __device__ __forceinline__ float reduce_chunk_lanes(float v) {
 // Where a row's V vectors come from in the aggregation.
 enum VSrc { kVlds = 0, kVwin = 1, kVraster = 2, kVnone = 3 };
 
-// Everything after the scores of one query row: u = A^{l-1} exp(s - m), the exact
-// top-K_l (ties to the lower slot index), the I^l / A^l row in I^{l-1} order and,
-// unless VS == kVnone, O_i = sum_kept A v_j. jj/av/valid/sv are this lane's
-// candidates c = gl + GL*t; sv are base-2 scores.
+// u = A^{l-1} exp(s - m) for one query row held by a group of GL lanes, in place
+// over the base-2 scores sv (m = the row maximum). fmaxf maps NaN and negative
+// products (invalid previous maps) to 0, so keys always lie in [0, +inf] and
+// every search in select_emit terminates.
+template <int GL, int KPT>
+__device__ __forceinline__ void keys_from_scores(const float (&av)[KPT], const bool (&valid)[KPT],
+                                                 float (&sv)[KPT]) {
+    float smax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < KPT; ++t) smax = fmaxf(smax, sv[t]);
+    smax = Grp<GL>::all(smax, MaxF());
+#pragma unroll
+    for (int t = 0; t < KPT; ++t) sv[t] = valid[t] ? fmaxf(av[t] * fast_exp2(sv[t] - smax), 0.0f) : 0.0f;
+}
+
+// Everything after the keys of one query row: the exact top-K_l (ties to the
+// lower slot index), the I^l / A^l row in I^{l-1} order and, unless
+// VS == kVnone, O_i = sum_kept A v_j. jj/valid/uv are this lane's candidates
+// c = gl + GL*t; uv = A^{l-1} exp(s - m) >= 0.
 template <typename T, int D, int GL, int KPT, int VS>
-__device__ __forceinline__ void finish_row(const SparseArgs& p, const Geom& g, int lane, bool active, size_t row,
-                                           int qpix, int wy, int wx, const int (&jj)[KPT], const float (&av)[KPT],
-                                           const bool (&valid)[KPT], const float (&sv)[KPT], uint2* scr, int scg,
-                                           const unsigned char* Vs, const T* Vh, float* Oh) {
+__device__ __forceinline__ void select_emit(const SparseArgs& p, const Geom& g, int lane, bool active, size_t row,
+                                            int qpix, int wy, int wx, const int (&jj)[KPT], const bool (&valid)[KPT],
+                                            const float (&uv_in)[KPT], unsigned* hb, uint2* scr, int scg,
+                                            const unsigned char* Vs, const T* Vh, float* Oh) {
     constexpr int EPC = Chunk<T>::kElems;
     constexpr int CH = D / EPC;
     constexpr int ROWB = D * (int)sizeof(T);
@@ -167,18 +193,12 @@ __device__ __forceinline__ void finish_row(const SparseArgs& p, const Geom& g, i
     const int K_prev = p.K_prev;
     const int K_l = p.K_l;
 
-    float smax = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < KPT; ++t) smax = fmaxf(smax, sv[t]);
-    smax = G::all(smax, MaxF());
-
-    // u = A^{l-1} exp(s - m); key = bits of u (>= 0), -1 for no candidate
     float uv[KPT];
     int key[KPT];
     int kmin = 0x7fffffff, kmax = -1;
 #pragma unroll
     for (int t = 0; t < KPT; ++t) {
-        uv[t] = valid[t] ? av[t] * fast_exp2(sv[t] - smax) : 0.0f;
+        uv[t] = uv_in[t];
         key[t] = valid[t] ? __float_as_int(uv[t]) : -1;
         if (valid[t]) {
             kmin = min(kmin, key[t]);
@@ -188,46 +208,51 @@ __device__ __forceinline__ void finish_row(const SparseArgs& p, const Geom& g, i
     kmin = G::all_i(kmin, MinI());
     kmax = G::all_i(kmax, MaxI());
 
-    // phase 1: narrow [lo, hi) until it holds at most kBand keys
-    int lo = kmin, hi = kmax + 1, c_lo = K_prev, c_hi = 0;
-    bool done = !active || hi - lo <= 1 || c_lo - c_hi <= kBand;
-    for (int it = 0; ballot(!done) != 0; ++it) {
-        const int span = hi - lo;
-        int mid;
-        if (it % 3 == 2) {
-            mid = lo + (span >> 1);
-        } else {
-            const float f = ((float)(c_lo - K_l) + 0.5f) / (float)max(c_lo - c_hi, 1);
-            mid = lo + (int)(f * (float)span);
-        }
-        mid = min(max(mid, lo + 1), hi - 1);
-        int cnt = 0;
-#pragma unroll
-        for (int t = 0; t < KPT; ++t) cnt += G::count(key[t] >= mid, lane);
-        if (!done) {
-            if (cnt >= K_l) { lo = mid; c_lo = cnt; } else { hi = mid; c_hi = cnt; }
-            done = hi - lo <= 1 || c_lo - c_hi <= kBand;
-        }
+    // Exact K_l-th largest key by radix descent: the key interval [lo, hi) is cut
+    // into GL bins of 2^shift consecutive keys (bit-field slices), counted with LDS
+    // atomics; a prefix scan over the bins in descending order finds the bin that
+    // holds the K_l-th key; keys in higher bins are kept, keys in lower bins are
+    // dropped, and the search descends into that bin. Each level removes log2(GL)
+    // bits from the interval, so it ends after at most 8 levels (usually 3).
+    int lo = kmin, hi = kmax + 1, need = K_l;
+    int tau = lo, need_tau = K_l, n_tau = 0;
+    bool done = !active;
+    if (active && hi - lo <= 1) {   // all keys equal
+        done = true;
+        n_tau = K_prev;
     }
-
-    // phase 2: take the band's keys largest first until K_l are kept
-    int need = K_l - c_hi;
-    int tau = lo, need_tau = need, n_tau = 0;
-    bool done2 = !active;
-    while (ballot(!done2) != 0) {
-        int m = -1;
+    while (ballot(!done) != 0) {
+        const int span = max(hi - lo, 2);
+        const int shift = max(32 - __clz(span - 1) - G::kLog2, 0);
+        hb[gl] = 0u;
 #pragma unroll
-        for (int t = 0; t < KPT; ++t)
-            if (key[t] >= lo && key[t] < hi) m = max(m, key[t]);
-        m = G::all_i(m, MaxI());
-        int ceq = 0;
-#pragma unroll
-        for (int t = 0; t < KPT; ++t) ceq += G::count(key[t] == m, lane);
-        if (!done2) {
-            if (ceq >= need) {
-                tau = m; need_tau = need; n_tau = ceq; done2 = true;
-            } else {
-                need -= ceq; hi = m;
+        for (int t = 0; t < KPT; ++t) {
+            const unsigned dk = (unsigned)(key[t] - lo);
+            if (!done && dk < (unsigned)(hi - lo)) atomicAdd(&hb[dk >> shift], 1u);
+        }
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const unsigned c = hb[GL - 1 - gl];          // bins in descending key order
+        const unsigned incl = G::incl_scan(c);
+        const unsigned excl = incl - c;
+        if (!done && excl < (unsigned)need && incl >= (unsigned)need) {   // exactly one lane per group
+            hb[GL] = (unsigned)(GL - 1 - gl);
+            hb[GL + 1] = excl;
+            hb[GL + 2] = c;
+        }
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int bin = (int)hb[GL];
+        const int above = (int)hb[GL + 1];
+        const int in_bin = (int)hb[GL + 2];
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (!done) {
+            need -= above;
+            lo += bin << shift;
+            hi = min(hi, lo + (1 << shift));
+            if (in_bin == need || hi - lo <= 1) {   // whole bin kept, or all its keys equal (ties)
+                tau = lo;
+                need_tau = need;
+                n_tau = in_bin;
+                done = true;
             }
         }
     }
@@ -251,36 +276,31 @@ __device__ __forceinline__ void finish_row(const SparseArgs& p, const Geom& g, i
 
     bool kept[KPT];
     float ksum = 0.0f;
+    if (ballot(tie) == 0) {   // usual case: every key equal to tau is kept
 #pragma unroll
-    for (int t = 0; t < KPT; ++t) {
-        kept[t] = key[t] > tau || (key[t] == tau && jj[t] <= jcut);
-        ksum += kept[t] ? uv[t] : 0.0f;
+        for (int t = 0; t < KPT; ++t) kept[t] = key[t] >= tau;
+    } else {
+#pragma unroll
+        for (int t = 0; t < KPT; ++t) kept[t] = key[t] > tau || (key[t] == tau && jj[t] <= jcut);
     }
+#pragma unroll
+    for (int t = 0; t < KPT; ++t) ksum += kept[t] ? uv[t] : 0.0f;
     const float inv = 1.0f / G::all(ksum, SumF());
 
-    // kept entries in I^{l-1} order
+    // kept entries in I^{l-1} order: positions by ballot prefix counts, staged in
+    // LDS as (j, weight), then written as contiguous row segments
     int pos[KPT];
     int obase = 0;
-    int32_t* Io = p.I_out + row * K_l;
-    float* Ao = p.A_out + row * K_l;
 #pragma unroll
     for (int t = 0; t < KPT; ++t) {
         const uint64_t m = ballot(kept[t]);
         pos[t] = kept[t] ? obase + G::below(m, lane) : -1;
         if (pos[t] >= K_l) pos[t] = -1;   // only on precondition violations
         uv[t] *= inv;
-        if (pos[t] >= 0) {
-            Io[pos[t]] = jj[t];
-            Ao[pos[t]] = uv[t];
-        }
         obase += G::count_mask(m, lane);
     }
-    if (VS == kVnone) {
-        __asm__ volatile("" ::: "memory");   // keeps the scheduler from overlapping rows (register pressure)
-        return;
-    }
-
-    // O_i = sum_kept A v_j: CH lanes read one V row; GS entries at a time per group
+    int32_t* Io = p.I_out + row * K_l;
+    float* Ao = p.A_out + row * K_l;
     const int vchunk = gl % CH;
     const int vsub = gl / CH;
     float oacc[EPC];
@@ -293,24 +313,33 @@ __device__ __forceinline__ void finish_row(const SparseArgs& p, const Geom& g, i
                 scr[pos[t] - P0] = make_uint2((uint32_t)jj[t], __float_as_uint(uv[t]));
         __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const int cnt = active ? min(scg, K_l - P0) : 0;
-        for (int e = vsub; e < cnt; e += GS) {
+        for (int e = gl; e < cnt; e += GL) {
             const uint2 ent = scr[e];
-            const float w = __uint_as_float(ent.y);
-            const unsigned char* vrow;
-            if (VS == kVlds) {
-                vrow = Vs + ent.x * ROWB;
-            } else if (VS == kVwin) {
-                vrow = reinterpret_cast<const unsigned char*>(Vh + (size_t)slot_pixel(g, wy, wx, (int)ent.x) * D);
-            } else {
-                vrow = reinterpret_cast<const unsigned char*>(Vh + (size_t)ent.x * D);
-            }
-            float vf[EPC];
-            Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(vrow + vchunk * 16), vf);
+            Io[P0 + e] = (int32_t)ent.x;
+            Ao[P0 + e] = __uint_as_float(ent.y);
+        }
+        if (VS != kVnone) {
+            // O_i = sum_kept A v_j: CH lanes read one V row; GS entries at a time per group
+            for (int e = vsub; e < cnt; e += GS) {
+                const uint2 ent = scr[e];
+                const float w = __uint_as_float(ent.y);
+                const unsigned char* vrow;
+                if (VS == kVlds) {
+                    vrow = Vs + ent.x * ROWB;
+                } else if (VS == kVwin) {
+                    vrow = reinterpret_cast<const unsigned char*>(Vh + (size_t)slot_pixel(g, wy, wx, (int)ent.x) * D);
+                } else {
+                    vrow = reinterpret_cast<const unsigned char*>(Vh + (size_t)ent.x * D);
+                }
+                float vf[EPC];
+                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(vrow + vchunk * 16), vf);
 #pragma unroll
-            for (int x = 0; x < EPC; ++x) oacc[x] = fmaf(w, vf[x], oacc[x]);
+                for (int x = 0; x < EPC; ++x) oacc[x] = fmaf(w, vf[x], oacc[x]);
+            }
         }
         __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
+    if (VS == kVnone) return;
 #pragma unroll
     for (int x = 0; x < EPC; ++x) oacc[x] = reduce_chunk_lanes<CH, GL>(oacc[x]);
     if (active && vsub == 0) {
@@ -364,7 +393,7 @@ __device__ __forceinline__ void stage_rows(unsigned char* dst, int stride, const
 
 // Generic sparse layer: scores by LDS (or global) gathers of k_j, one group of GL
 // lanes per query row.
-template <typename T, int D, int GL, int KPT, int MODE, int NW>
+template <typename T, int D, int GL, int KPT, int MODE, int NW, bool PQ>
 __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseArgs p) {
     constexpr int EPC = Chunk<T>::kElems;   // elements per 16-byte chunk
     constexpr int CH = D / EPC;             // chunks per K/V row
@@ -373,8 +402,10 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
     constexpr bool K_LDS = MODE != kKVglobal;
     constexpr bool V_LDS = MODE == kKVinLDS;
     constexpr int VS = MODE == kKVinLDS ? kVlds : MODE == kKinLDS ? kVwin : MODE == kKVglobal ? kVraster : kVnone;
-    constexpr int SCW = kScratchBytes / (NW * 8);   // scratch entries per wave
-    constexpr int SCG = SCW / RPW;                  // scratch entries per row group
+    constexpr int HISTW = RPW * (GL + 4);            // radix-select histogram words per wave
+    constexpr int HIST_BYTES = NW * HISTW * 4;
+    constexpr int SCW = (kScratchBytes - HIST_BYTES) / (NW * 8);   // (j, weight) entries per wave
+    constexpr int SCG = SCW / RPW;                                 // entries per row group
     extern __shared__ __align__(16) unsigned char smem[];
 
     const Geom g = p.g;
@@ -392,8 +423,9 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
 
     unsigned char* Ks = smem;
     unsigned char* Vs = smem + (K_LDS ? N * ROWB : 0);
-    uint2* scr = reinterpret_cast<uint2*>(smem + (K_LDS ? N * ROWB : 0) + (V_LDS ? N * ROWB : 0)) +
-                 wave * SCW + grp * SCG;
+    unsigned char* sbase = smem + (K_LDS ? N * ROWB : 0) + (V_LDS ? N * ROWB : 0);
+    unsigned* hb = reinterpret_cast<unsigned*>(sbase) + wave * HISTW + grp * (GL + 4);
+    uint2* scr = reinterpret_cast<uint2*>(sbase + HIST_BYTES) + wave * SCW + grp * SCG;
 
     if (K_LDS) {
         stage_rows<T, D>(Ks, ROWB, Kh, g, w.wy, w.wx);
@@ -409,31 +441,65 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
     const int row1 = min(N, row0 + p.rows_per_block);
     const int K_prev = p.K_prev;
 
+    // Software pipeline over the wavefront's rows: the global loads of the next
+    // row (candidate list, previous weights and, when PQ, the query vector) are in
+    // flight while the current row is scored and selected.
+    struct RowIn {
+        int j[KPT];
+        float a[KPT];
+        uint4 q[PQ ? CH : 1];
+    };
+    auto load_row = [&](RowIn& r, int base) {
+        const int i_raw = base + grp;
+        const bool active = i_raw < row1;
+        const int i = active ? i_raw : row0;
+        const size_t row = (size_t)w.wh * N + i;
+        const size_t rowI = p.i_shared ? (size_t)(w.b * w.nwin + w.win_id) * N + i : row;
+        const int32_t* Irow = p.I_prev ? p.I_prev + rowI * K_prev + gl : nullptr;
+        const float* Arow = p.A_prev ? p.A_prev + row * K_prev + gl : nullptr;
+#pragma unroll
+        for (int t = 0; t < KPT; ++t) {
+            const int c = gl + GL * t;
+            const bool v = active && c < K_prev;
+            r.j[t] = v ? (Irow ? Irow[GL * t] : c) : 0;
+            r.a[t] = (v && Arow) ? Arow[GL * t] : 1.0f;
+        }
+        if (PQ) {
+            const unsigned char* qrow =
+                reinterpret_cast<const unsigned char*>(Qh + (size_t)slot_pixel(g, w.wy, w.wx, i) * D);
+#pragma unroll
+            for (int m = 0; m < CH; ++m) r.q[m] = *reinterpret_cast<const uint4*>(qrow + coff[m]);
+        }
+    };
+    RowIn cur;
+    load_row(cur, row0 + wave * RPW);
     for (int base = row0 + wave * RPW; base < row1; base += NW * RPW) {
+        RowIn nxt;
+        if (base + NW * RPW < row1) load_row(nxt, base + NW * RPW);
         const int i_raw = base + grp;
         const bool active = i_raw < row1;
         const int i = active ? i_raw : row0;
         const int qpix = slot_pixel(g, w.wy, w.wx, i);
         const size_t row = (size_t)w.wh * N + i;
-        const size_t rowI = p.i_shared ? (size_t)(w.b * w.nwin + w.win_id) * N + i : row;
 
         int jj[KPT];
-        float av[KPT];
         bool valid[KPT];
 #pragma unroll
         for (int t = 0; t < KPT; ++t) {
-            const int c = gl + GL * t;
-            valid[t] = active && c < K_prev;
-            const int j = valid[t] ? (p.I_prev ? p.I_prev[rowI * K_prev + c] : c) : 0;
-            jj[t] = min(max(j, 0), N - 1);   // memory safety only: indices must lie in [0, N)
-            av[t] = (valid[t] && p.A_prev) ? p.A_prev[row * K_prev + c] : 1.0f;
+            valid[t] = active && gl + GL * t < K_prev;
+            jj[t] = min(max(cur.j[t], 0), N - 1);   // memory safety only: indices must lie in [0, N)
         }
 
         float qf[D];
-        const unsigned char* qrow = reinterpret_cast<const unsigned char*>(Qh + (size_t)qpix * D);
+        if (PQ) {
 #pragma unroll
-        for (int m = 0; m < CH; ++m)
-            Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(qrow + coff[m]), &qf[m * EPC]);
+            for (int m = 0; m < CH; ++m) Chunk<T>::to_f32(cur.q[m], &qf[m * EPC]);
+        } else {
+            const unsigned char* qrow = reinterpret_cast<const unsigned char*>(Qh + (size_t)qpix * D);
+#pragma unroll
+            for (int m = 0; m < CH; ++m)
+                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(qrow + coff[m]), &qf[m * EPC]);
+        }
 
         // SMM: scores over the candidate list only (base-2 units)
         float sv[KPT];
@@ -451,8 +517,10 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
             }
             sv[t] = valid[t] ? acc * p.scale2 : -INFINITY;
         }
-        finish_row<T, D, GL, KPT, VS>(p, g, lane, active, row, qpix, w.wy, w.wx, jj, av, valid, sv, scr, SCG, Vs,
-                                      Vh, Oh);
+        keys_from_scores<GL, KPT>(cur.a, valid, sv);
+        select_emit<T, D, GL, KPT, VS>(p, g, lane, active, row, qpix, w.wy, w.wx, jj, valid, sv, hb, scr, SCG, Vs,
+                                       Vh, Oh);
+        cur = nxt;
     }
 }
 
@@ -501,7 +569,9 @@ __global__ __launch_bounds__(8 * kWave) void all_cand_kernel(const SparseArgs p)
     constexpr int ROWB = D * (int)sizeof(T);
     constexpr int KSTR = ROWB + 16;
     constexpr int KK = Mfma4<T>::kK;
-    constexpr int SCW = kScratchBytes / 2 / (NW * 8);
+    constexpr int HISTW = GL + 4;
+    constexpr int HIST_BYTES = NW * HISTW * 4;
+    constexpr int SCW = (kScratchBytes / 2 - HIST_BYTES) / (NW * 8);
     extern __shared__ __align__(16) unsigned char smem[];
 
     const Geom g = p.g;
@@ -517,7 +587,9 @@ __global__ __launch_bounds__(8 * kWave) void all_cand_kernel(const SparseArgs p)
 
     unsigned char* Ks = smem;
     unsigned char* Vs = smem + N * KSTR;
-    uint2* scr = reinterpret_cast<uint2*>(Vs + (VS == kVlds ? N * ROWB : 0)) + wave * SCW;
+    unsigned char* sbase = Vs + (VS == kVlds ? N * ROWB : 0);
+    unsigned* hb = reinterpret_cast<unsigned*>(sbase) + wave * HISTW;
+    uint2* scr = reinterpret_cast<uint2*>(sbase + HIST_BYTES) + wave * SCW;
     stage_rows<T, D>(Ks, KSTR, Kh, g, w.wy, w.wx);
     if (VS == kVlds) stage_rows<T, D>(Vs, ROWB, Vh, g, w.wy, w.wx);
     __syncthreads();
@@ -527,8 +599,26 @@ __global__ __launch_bounds__(8 * kWave) void all_cand_kernel(const SparseArgs p)
     int jj[KPT];
     bool valid[KPT];
 #pragma unroll
-    for (int t = 0; t < KPT; ++t) jj[t] = lane + kWave * t;
+    for (int t = 0; t < KPT; ++t) {
+        jj[t] = lane + kWave * t;
+        valid[t] = true;
+    }
 
+    // A^{l-1} rows of the wavefront's current 4-row batch; the next batch's rows are
+    // loaded as soon as these have been folded into the keys, so ~16 KB per wave
+    // stay in flight while the batch is selected (the LDS-resident K limits the CU
+    // to 8 waves, so memory-level parallelism has to come from each wave).
+    float ab[4][KPT];
+    auto load_batch = [&](int b0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = min(b0 + r, N - 1);
+            const float* arow = p.A_prev ? p.A_prev + ((size_t)w.wh * N + i) * N + lane : nullptr;
+#pragma unroll
+            for (int t = 0; t < KPT; ++t) ab[r][t] = arow ? arow[kWave * t] : 1.0f;
+        }
+    };
+    load_batch(row0 + wave * 4);
     for (int base = row0 + wave * 4; base < row1; base += NW * 4) {
         // A operand: query row base + lane%4 (rows past row1 compute garbage, never stored)
         const int qi = min(base + (lane & 3), row1 - 1);
@@ -540,27 +630,33 @@ __global__ __launch_bounds__(8 * kWave) void all_cand_kernel(const SparseArgs p)
 
         float s4[4][KPT];
 #pragma unroll
-        for (int t = 0; t < KPT; t += 2) {
-            v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-            const unsigned char* k0 = Ks + (kWave * t + lane) * KSTR;
-            const unsigned char* k1 = k0 + kWave * KSTR;
+        for (int t = 0; t < KPT; t += 4) {   // 4 independent accumulator chains
+            v4f acc[4];
+            const unsigned char* kr[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                acc[x] = v4f{0.f, 0.f, 0.f, 0.f};
+                kr[x] = Ks + (kWave * (t + x) + lane) * KSTR;
+            }
 #pragma unroll
             for (int m = 0; m < CH; ++m) {
-                float kf0[EPC], kf1[EPC];
-                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(k0 + 16 * m), kf0);
-                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(k1 + 16 * m), kf1);
+                float kf[4][EPC];
 #pragma unroll
-                for (int e = 0; e < EPC; e += KK) {
-                    acc0 = Mfma4<T>::run(&qf[m * EPC + e], &kf0[e], acc0);
-                    acc1 = Mfma4<T>::run(&qf[m * EPC + e], &kf1[e], acc1);
-                }
+                for (int x = 0; x < 4; ++x) Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(kr[x] + 16 * m), kf[x]);
+#pragma unroll
+                for (int e = 0; e < EPC; e += KK)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) acc[x] = Mfma4<T>::run(&qf[m * EPC + e], &kf[x][e], acc[x]);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                s4[r][t] = acc0[r] * p.scale2;
-                s4[r][t + 1] = acc1[r] * p.scale2;
-            }
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) s4[r][t + x] = acc[x][r] * p.scale2;
         }
+        // keys of the 4 rows (in place), then start the next batch's loads
+#pragma unroll
+        for (int r = 0; r < 4; ++r) keys_from_scores<GL, KPT>(ab[r], valid, s4[r]);
+        if (base + NW * 4 < row1) load_batch(base + NW * 4);
 
 #pragma unroll 1
         for (int r = 0; r < 4; ++r) {
@@ -568,16 +664,15 @@ __global__ __launch_bounds__(8 * kWave) void all_cand_kernel(const SparseArgs p)
             const bool active = i < row1;
             const int ii = active ? i : row0;
             const size_t row = (size_t)w.wh * N + ii;
-            float av[KPT], sv[KPT];
+            float uv[KPT];
 #pragma unroll
             for (int t = 0; t < KPT; ++t) {
                 valid[t] = active;
-                av[t] = p.A_prev ? p.A_prev[row * N + jj[t]] : 1.0f;
                 // register select (r is a loop variable: indexing s4[r] would spill to scratch)
-                sv[t] = r == 0 ? s4[0][t] : r == 1 ? s4[1][t] : r == 2 ? s4[2][t] : s4[3][t];
+                uv[t] = r == 0 ? s4[0][t] : r == 1 ? s4[1][t] : r == 2 ? s4[2][t] : s4[3][t];
             }
-            finish_row<T, D, GL, KPT, VS>(p, g, lane, active, row, slot_pixel(g, w.wy, w.wx, ii), w.wy, w.wx, jj,
-                                          av, valid, sv, scr, SCW, Vs, Vh, Oh);
+            select_emit<T, D, GL, KPT, VS>(p, g, lane, active, row, slot_pixel(g, w.wy, w.wx, ii), w.wy, w.wx, jj,
+                                           valid, uv, hb, scr, SCW, Vs, Vh, Oh);
         }
     }
 }
@@ -669,7 +764,8 @@ hipError_t launch_fn(F fn, const SparseArgs& a, int threads, int lds, int grid, 
 template <typename T, int D, int GL, int KPT, int MODE>
 hipError_t launch_one(const SparseArgs& a, int lds, int grid, hipStream_t s) {
     constexpr int NW = KPT <= 4 ? 16 : 8;
-    return launch_fn(sparse_layer_kernel<T, D, GL, KPT, MODE, NW>, a, NW * kWave, lds, grid, s);
+    constexpr bool PQ = KPT <= 4 && D * sizeof(T) <= 64;   // prefetch q when registers allow
+    return launch_fn(sparse_layer_kernel<T, D, GL, KPT, MODE, NW, PQ>, a, NW * kWave, lds, grid, s);
 }
 
 template <typename T, int D, int GL, int KPT>
@@ -700,7 +796,7 @@ hipError_t launch_all_cand_t(const SparseArgs& a, bool with_av, int grid, hipStr
     const int lds_k = 1024 * (ROWB + 16);
     if (with_av)
         return launch_fn(all_cand_kernel<T, D, kVlds>, a, 8 * kWave, lds_k + 1024 * ROWB + kScratchBytes / 2, grid, s);
-    return launch_fn(all_cand_kernel<T, D, kVnone>, a, 8 * kWave, lds_k, grid, s);
+    return launch_fn(all_cand_kernel<T, D, kVnone>, a, 8 * kWave, lds_k + kScratchBytes / 2, grid, s);
 }
 
 template <typename T, int D>

@@ -231,3 +231,24 @@ def test_error_codes():
     with pytest.raises(pfa.PfaError) as e:
         pfa.dense_layer(Q, Q, Q, win=0)                              # dense layer in global mode
     assert e.value.code == -2
+
+
+@pytest.mark.timeout(120)
+@pytest.mark.parametrize("K_prev,K_l", [(1024, 256), (256, 128), (64, 32)])
+def test_nonfinite_previous_map_terminates(K_prev, K_l):
+    # NaN, negative and infinite previous weights violate the preconditions; the
+    # kernels must still return (such keys count as weight 0) with valid indices.
+    shape = (1, 2, 32, 32, 32)
+    qt, kt, vt = (inputs.draw(800 + t, shape, "f32") for t in range(3))
+    g = np.random.Generator(np.random.PCG64(801))
+    n_wh, N = 2, 1024
+    a = g.standard_normal((n_wh, N, K_prev)).astype(np.float32)
+    a[..., ::7] = np.nan
+    a[..., 3::11] = np.inf
+    C = None if K_prev == N else torch.from_numpy(
+        np.stack([g.permutation(N)[:K_prev] for _ in range(n_wh * N)]).astype(np.int32)).cuda()
+    I, A, O = pfa.sparse_layer(to_dev(qt), to_dev(kt), to_dev(vt), C, torch.from_numpy(a).cuda(), K_l, win=32,
+                               shift=0)
+    torch.cuda.synchronize()
+    Ig = I.cpu().numpy()
+    assert (Ig >= 0).all() and (Ig < N).all()
