@@ -26,26 +26,68 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+COUNTERS_FILE = "hbm_counters_{workload}.md"
+
+# kernel kinds of the library's timing calls (pfa_kernel_kind)
+DENSE, ALL_CAND, SPARSE, SELECT, AGGREGATE, IOTA = range(6)
 
 
-def layer_bytes(w, l):
-    """Algorithmic HBM bytes of layer l (0-based) per window-head."""
+def kernel_bytes(w, l, kind, i_prev_implicit, split):
+    """Algorithmic HBM bytes of one launch of kernel `kind` in layer l (0-based),
+    per window-head: every input read once, every output written once. `split`:
+    the layer ran a separate aggregation kernel, so this one does not touch V or O."""
     N, d = w.N, w.d
     b_in = 4 if w.dtype == "f32" else 2
-    qkv = 3 * N * d * b_in
+    x = N * d * b_in                      # one of Q, K, V
     O = N * d * 4
-    if l == 0:
-        return qkv + O + N * N * 4                   # A^1 materialised (I^1 implicit)
+    if kind == DENSE:
+        return 3 * x + O + N * N * 4      # A^1 materialised; I^1 implicit
+    if kind == IOTA:
+        return N * N * 4
     K_prev, K_l = w.K[l - 1], w.K[l]
-    I_prev = 0 if (l == 1 and K_prev == N) else N * K_prev * 4
-    return qkv + O + I_prev + N * K_prev * 4 + N * K_l * 8
+    I_prev = 0 if i_prev_implicit else N * K_prev * 4
+    kept = N * K_l * 8                    # I^l and A^l rows
+    if kind == AGGREGATE:
+        return x + kept + O
+    sel = 2 * x + I_prev + N * K_prev * 4 + kept
+    if split:
+        return sel
+    return sel + x + O
 
 
-def layer_flops(w, l):
-    """Algorithmic flops per window-head: 2d per candidate pair (score) + 2d per kept pair (A.V)."""
+def kernel_flops(w, l, kind, split):
+    """Algorithmic flops per window-head: 2d per scored pair, 2d per aggregated pair."""
     N, d = w.N, w.d
-    K_prev = N if l == 0 else w.K[l - 1]
-    return 2 * d * N * K_prev + 2 * d * N * w.K[l]
+    if kind == DENSE:
+        return 4 * d * N * N
+    if kind == IOTA:
+        return 0
+    K_prev, K_l = w.K[l - 1], w.K[l]
+    if kind == AGGREGATE:
+        return 2 * d * N * K_l
+    if split:
+        return 2 * d * N * K_prev
+    return 2 * d * N * K_prev + 2 * d * N * K_l
+
+
+def stored_traffic(workload, kernel, layer):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel sources changed since it was taken."""
+    from sparse_progressive_window_amd import build
+    path = os.path.join(ROOT, "profiles", COUNTERS_FILE.format(workload=workload))
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    try:
+        blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (IndexError, ValueError):
+        return None
+    if blob.get("source_sha256") != build.source_digest():
+        return None
+    for k in blob.get("kernels", []):
+        if k["kernel"] == kernel and k["layer"] == layer:
+            return k["traffic_bytes"]
+    return None
 
 
 def main():
@@ -55,7 +97,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="map256x256_h6_d32_f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=64, help="window-heads timed on the CPU oracle")
+    ap.add_argument("--cpu-sample", type=int, default=256, help="window-heads timed on the CPU oracle")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -99,65 +141,82 @@ def main():
         A = torch.empty(lead + (N, K_l), dtype=torch.float32, device=dev)
         O = torch.empty((w.B, w.heads, w.H, w.W, w.d), dtype=torch.float32, device=dev)
         outs.append((I, A, O))
-    stream = torch.cuda.current_stream()
+    implicit = [l == 1 and w.K[0] == N for l in range(L)]
 
-    def step(events=None):
+    def step(marks=None):
         for l in range(L):
             Q, K, V = qkv[l]
-            if events is not None:
-                events[l][0].record(stream)
             if l == 0:
                 pfa.dense_layer(Q, K, V, w.K[0], win=w.win, shift=w.shifts[0], out=outs[0])
             else:
-                I_prev = None if (l == 1 and w.K[0] == N) else outs[l - 1][0]
+                I_prev = None if implicit[l] else outs[l - 1][0]
                 pfa.sparse_layer(Q, K, V, I_prev, outs[l - 1][1], w.K[l], win=w.win, shift=w.shifts[l],
                                  out=outs[l])
-            if events is not None:
-                events[l][1].record(stream)
+            if marks is not None:
+                marks.append(pfa.timing_count())
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # whole-step timing (no per-layer events inside)
+    # Timed region: K steps; every kernel is bracketed by HIP events on its launch
+    # stream (the library's timing calls), read back after the final synchronize.
+    pfa.timing_enable(args.steps * L * 2 + 64)
+    marks = []
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        step(marks)
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    recs, dropped = pfa.timing_read(len(marks) * 4 + 64)
+    pfa.timing_enable(0)
+    assert dropped == 0 and len(recs) == marks[-1], (dropped, len(recs), marks[-1])
 
-    # per-layer timing with HIP events on the launch stream
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)] for _ in range(args.steps)]
-    for s in range(args.steps):
-        step(ev[s])
-    torch.cuda.synchronize()
-    layer_ms = [float(np.mean([ev[s][l][0].elapsed_time(ev[s][l][1]) for s in range(args.steps)]))
-                for l in range(L)]
+    # per (layer, kernel kind): launch durations
+    per = {}
+    start = 0
+    for i, end in enumerate(marks):
+        l = i % L
+        for kind, ms in recs[start:end]:
+            per.setdefault((l, kind), []).append(ms)
+        start = end
+    layer_ms = [sum(float(np.mean(v)) for (ll, _), v in per.items() if ll == l) for l in range(L)]
 
-    layers = []
+    layers, kernels = [], []
     total_pairs = 0
     for l in range(L):
         pairs = w.pairs(l)
         total_pairs += pairs
-        by = layer_bytes(w, l) * w.n_wh
-        fl = layer_flops(w, l) * w.n_wh
-        gbs = by / (layer_ms[l] * 1e-3) / 1e9
         layers.append({"layer": l + 1, "K_prev": N if l == 0 else w.K[l - 1], "K_l": w.K[l],
-                       "ms": round(layer_ms[l], 4), "pairs_per_s": pairs / (layer_ms[l] * 1e-3),
-                       "alg_bytes": by, "GB_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                       "alg_flops": fl, "TFLOP_per_s": round(fl / (layer_ms[l] * 1e-3) / 1e12, 2)})
+                       "ms": round(layer_ms[l], 4), "pairs_per_s": pairs / (layer_ms[l] * 1e-3)})
+    peak_mfma = FP32_MFMA_PEAK_TFLOPS if w.dtype == "f32" else BF16_MFMA_PEAK_TFLOPS
+    for (l, kind), v in sorted(per.items()):
+        ms = float(np.mean(v))
+        split = (l, AGGREGATE) in per
+        by = kernel_bytes(w, l, kind, implicit[l], split) * w.n_wh
+        fl = kernel_flops(w, l, kind, split) * w.n_wh
+        gbs = by / (ms * 1e-3) / 1e9
+        tfs = fl / (ms * 1e-3) / 1e12
+        mfma = kind in (DENSE, ALL_CAND)
+        # the bound is whichever roofline time is longer for the algorithmic work
+        t_hbm = by / (HBM_PEAK_GBS * 1e9)
+        t_mfma = fl / (peak_mfma * 1e12) if mfma else 0.0
+        bound = "mfma" if t_mfma > t_hbm else "hbm"
+        kernels.append({"layer": l + 1, "kernel": pfa.kernel_name(kind), "launches": len(v), "ms": round(ms, 4),
+                        "alg_bytes": by, "GB_per_s": round(gbs, 1), "alg_flops": fl, "TFLOP_per_s": round(tfs, 2),
+                        "bound": bound,
+                        "frac": round(tfs / peak_mfma if bound == "mfma" else gbs / HBM_PEAK_GBS, 4)})
 
-    dom = max(range(L), key=lambda l: layer_ms[l])
-    if dom == 0 and w.dtype == "f32":
-        ach = layers[0]["TFLOP_per_s"]
-        roof = {"bound": "mfma", "kernel": "dense_layer_kernel<float,32>", "layer": 1, "achieved": ach,
-                "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / FP32_MFMA_PEAK_TFLOPS, 4),
-                "traffic": None}
+    dom = max(kernels, key=lambda k: k["ms"])
+    if dom["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": dom["TFLOP_per_s"], "peak": peak_mfma, "unit": "TFLOP/s"}
     else:
-        ach = layers[dom]["GB_per_s"]
-        roof = {"bound": "hbm", "kernel": "dense_layer_kernel" if dom == 0 else "sparse_layer_kernel",
-                "layer": dom + 1, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+        roof = {"bound": "hbm", "achieved": dom["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = dom["frac"]
+    roof["traffic"] = stored_traffic(w.name, dom["kernel"], dom["layer"])
+    roof.update({"kernel": dom["kernel"], "layer": dom["layer"], "ms_per_launch": dom["ms"],
+                 "alg_bytes_per_launch": dom["alg_bytes"], "alg_flops_per_launch": dom["alg_flops"]})
 
     value = total_pairs / (ms_per_step * 1e-3)
     result = {
@@ -167,7 +226,7 @@ def main():
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "heads": w.heads, "H": w.H, "W": w.W, "d": w.d, "win": w.win,
                    "K": w.K, "shifts": w.shifts, "window_heads": w.n_wh, "pairs_per_step": total_pairs},
-        "layers": layers, "roofline": roof,
+        "roofline": roof, "layers": layers, "kernels": kernels,
     }
 
     if not args.no_cpu_baseline:

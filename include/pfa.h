@@ -17,9 +17,10 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Tensors are dense, C-contiguous, and live in device memory of the current HIP
- * device; the caller allocates all of them. The library never allocates,
- * frees or synchronises: it validates the arguments, enqueues kernels on
- * `stream` (a hipStream_t; NULL = the null stream) and returns.
+ * device; the caller allocates all of them. The layer calls never allocate,
+ * free or synchronise: they validate the arguments, enqueue kernels on
+ * `stream` (a hipStream_t; NULL = the null stream) and return. (Only the
+ * optional timing calls at the end of this header create HIP events.)
  *
  *   Q, K, V   [B, heads, H, W, d], element type `dtype` (fp32, or bf16 bits).
  *   O         [B, heads, H, W, d] fp32.
@@ -112,6 +113,44 @@ const char* pfa_strerror(int code);
 
 /* Library version, major*10000 + minor*100 + patch. */
 int pfa_version(void);
+
+/*
+ * Kernel timing (instrumentation; off by default). While enabled, every kernel
+ * the two layer calls enqueue is bracketed by a pair of HIP events recorded on
+ * the stream it is launched on, so that a caller can attribute device time to
+ * the individual kernels of a layer (a sparse layer may run a selection kernel
+ * followed by an aggregation kernel). Not thread-safe: one host thread drives
+ * the layer calls while timing is on.
+ */
+typedef enum {
+    PFA_KERNEL_DENSE = 0,          /* dense first layer, all N candidates, MFMA */
+    PFA_KERNEL_ALL_CANDIDATES = 1, /* sparse layer whose candidate list is every slot (MFMA scores) */
+    PFA_KERNEL_SPARSE = 2,         /* sparse layer, selection and aggregation in one kernel */
+    PFA_KERNEL_SELECT = 3,         /* sparse layer, selection only (I^l, A^l) */
+    PFA_KERNEL_AGGREGATE = 4,      /* O from stored (I^l, A^l) rows */
+    PFA_KERNEL_IOTA = 5            /* I rows 0..N-1 of the dense layer */
+} pfa_kernel_kind;
+
+/* capacity > 0: create 2*capacity events and start recording (earlier records
+ * are discarded); capacity == 0: stop and destroy the events. Launches past the
+ * capacity run untimed and are counted as dropped. Errors: PFA_ERR_INVALID for
+ * capacity < 0 or > 2^20; PFA_ERR_HIP if event creation fails (timing stays off). */
+int pfa_timing_enable(int32_t capacity);
+
+/* Number of launches recorded since the last read (no synchronisation). */
+int32_t pfa_timing_count(void);
+
+/* Wait for the recorded events and copy up to `cap` records, in launch order:
+ * kinds[i] (pfa_kernel_kind) and ms[i] (elapsed milliseconds between the two
+ * events around launch i). *n_out = records copied; *dropped (may be NULL) =
+ * launches not returned (past the capacity or past `cap`). The record list is
+ * then cleared. kinds/ms are host arrays owned by the caller.
+ * Errors: PFA_ERR_INVALID for NULL n_out, cap < 0, NULL arrays with cap > 0;
+ * PFA_ERR_HIP if an event query fails. */
+int pfa_timing_read(int32_t* kinds, float* ms, int32_t cap, int32_t* n_out, int32_t* dropped);
+
+/* Kernel symbol name (prefix, as profilers show it) of a pfa_kernel_kind; never NULL. */
+const char* pfa_kernel_name(int32_t kind);
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,20 @@ FLAGS = [
 ]
 
 
+def source_digest() -> str:
+    """sha256 over the kernel sources and headers (names and contents), used to
+    tell whether stored profiler counters still describe the current kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    files = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith((".hip", ".h"))]
+    files.append(os.path.join(ROOT, "include", "pfa.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, src.replace(".hip", ".o"))
     cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]

@@ -2,12 +2,48 @@
 // The calls and their contracts are documented in include/pfa.h.
 #include <math.h>
 
+#include <vector>
+
 #include "pfa.h"
 #include "pfa_kernels.h"
 
 namespace {
 
 using pfa::Geom;
+
+// Kernel timing: when enabled, each launch below is bracketed by two events
+// recorded on its own stream. Records beyond the capacity are counted, not kept.
+struct Timing {
+    bool on = false;
+    std::vector<hipEvent_t> ev;   // 2 per record
+    std::vector<int32_t> kind;
+    int32_t n = 0;
+    int32_t dropped = 0;
+};
+Timing g_timing;
+
+template <class F>
+hipError_t timed(int32_t kind, hipStream_t s, F&& launch) {
+    Timing& t = g_timing;
+    if (!t.on) return launch();
+    if (t.n >= (int32_t)t.kind.size()) {
+        ++t.dropped;
+        return launch();
+    }
+    hipError_t e = hipEventRecord(t.ev[2 * t.n], s);
+    if (e != hipSuccess) return e;
+    e = launch();
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(t.ev[2 * t.n + 1], s);
+    if (e != hipSuccess) return e;
+    t.kind[t.n++] = kind;
+    return hipSuccess;
+}
+
+void timing_release() {
+    for (hipEvent_t e : g_timing.ev) (void)hipEventDestroy(e);
+    g_timing = Timing();
+}
 
 constexpr int kVersion = 10000;  // 1.0.0
 
@@ -74,8 +110,9 @@ int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const voi
         a.rows_per_block = 64;
         const int64_t grid = n_wh(g) * a.blocks_per_wh;
         if (grid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
-        const hipError_t e =
-            pfa::launch_sparse(a, dtype, g.d, pfa::kKVglobal, pfa::kScratchBytes, (int)grid, stream);
+        const hipError_t e = timed(PFA_KERNEL_SPARSE, stream, [&] {
+            return pfa::launch_sparse(a, dtype, g.d, pfa::kKVglobal, pfa::kScratchBytes, (int)grid, stream);
+        });
         return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
     }
     a.blocks_per_wh = g.N >= 512 ? 2 : 1;
@@ -88,16 +125,23 @@ int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const voi
     if (!I_prev && K_prev == 1024 && g.N == 1024) {
         // every slot is a candidate: MFMA scores
         const bool with_v = pfa::all_cand_fits_with_v(dtype, g.d);
-        e = pfa::launch_all_cand(a, dtype, g.d, with_v, grid, stream);
+        e = timed(PFA_KERNEL_ALL_CANDIDATES, stream,
+                  [&] { return pfa::launch_all_cand(a, dtype, g.d, with_v, grid, stream); });
         aggregate = !with_v;
     } else if (2 * g.N * rowb + pfa::kScratchBytes <= pfa::kLdsBytes) {
-        e = pfa::launch_sparse(a, dtype, g.d, pfa::kKVinLDS, 2 * g.N * rowb + pfa::kScratchBytes, grid, stream);
+        e = timed(PFA_KERNEL_SPARSE, stream, [&] {
+            return pfa::launch_sparse(a, dtype, g.d, pfa::kKVinLDS, 2 * g.N * rowb + pfa::kScratchBytes, grid,
+                                      stream);
+        });
     } else {
         // K and V do not fit in LDS together: select with K in LDS, then aggregate with V in LDS
-        e = pfa::launch_sparse(a, dtype, g.d, pfa::kKselect, g.N * rowb + pfa::kScratchBytes, grid, stream);
+        e = timed(PFA_KERNEL_SELECT, stream, [&] {
+            return pfa::launch_sparse(a, dtype, g.d, pfa::kKselect, g.N * rowb + pfa::kScratchBytes, grid, stream);
+        });
         aggregate = true;
     }
-    if (e == hipSuccess && aggregate) e = pfa::launch_aggregate(a, dtype, g.d, grid, stream);
+    if (e == hipSuccess && aggregate)
+        e = timed(PFA_KERNEL_AGGREGATE, stream, [&] { return pfa::launch_aggregate(a, dtype, g.d, grid, stream); });
     return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
 }
 
@@ -143,8 +187,9 @@ int pfa_dense_layer(const pfa_shape* shape, const void* Q, const void* K, const 
     a.xcd_map = (n_wh(g) % 8 == 0) ? 1 : 0;
     const int64_t grid = n_wh(g) * pfa::dense_query_blocks(g.N);
     if (grid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
-    hipError_t e = pfa::launch_dense(a, shape->dtype, g.d, (int)grid, s);
-    if (e == hipSuccess && I_out) e = pfa::launch_iota_rows(I_out, n_wh(g) * g.N, g.N, s);
+    hipError_t e = timed(PFA_KERNEL_DENSE, s, [&] { return pfa::launch_dense(a, shape->dtype, g.d, (int)grid, s); });
+    if (e == hipSuccess && I_out)
+        e = timed(PFA_KERNEL_IOTA, s, [&] { return pfa::launch_iota_rows(I_out, n_wh(g) * g.N, g.N, s); });
     return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
 }
 
@@ -159,5 +204,52 @@ const char* pfa_strerror(int code) {
 }
 
 int pfa_version(void) { return kVersion; }
+
+int pfa_timing_enable(int32_t capacity) {
+    if (capacity < 0 || capacity > (1 << 20)) return PFA_ERR_INVALID;
+    timing_release();
+    if (capacity == 0) return PFA_OK;
+    g_timing.ev.assign(2 * (size_t)capacity, nullptr);
+    g_timing.kind.assign(capacity, -1);
+    for (hipEvent_t& e : g_timing.ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            e = nullptr;
+            timing_release();
+            return PFA_ERR_HIP;
+        }
+    }
+    g_timing.on = true;
+    return PFA_OK;
+}
+
+int32_t pfa_timing_count(void) { return g_timing.n; }
+
+int pfa_timing_read(int32_t* kinds, float* ms, int32_t cap, int32_t* n_out, int32_t* dropped) {
+    if (!n_out || (cap > 0 && (!kinds || !ms)) || cap < 0) return PFA_ERR_INVALID;
+    Timing& t = g_timing;
+    const int32_t n = t.n < cap ? t.n : cap;
+    for (int32_t i = 0; i < n; ++i) {
+        if (hipEventSynchronize(t.ev[2 * i + 1]) != hipSuccess) return PFA_ERR_HIP;
+        if (hipEventElapsedTime(&ms[i], t.ev[2 * i], t.ev[2 * i + 1]) != hipSuccess) return PFA_ERR_HIP;
+        kinds[i] = t.kind[i];
+    }
+    *n_out = n;
+    if (dropped) *dropped = t.dropped + (t.n - n);
+    t.n = 0;
+    t.dropped = 0;
+    return PFA_OK;
+}
+
+const char* pfa_kernel_name(int32_t kind) {
+    switch (kind) {
+        case PFA_KERNEL_DENSE: return "dense_layer_kernel";
+        case PFA_KERNEL_ALL_CANDIDATES: return "all_cand_kernel";
+        case PFA_KERNEL_SPARSE: return "sparse_layer_kernel";
+        case PFA_KERNEL_SELECT: return "sparse_layer_kernel(select)";
+        case PFA_KERNEL_AGGREGATE: return "aggregate_kernel";
+        case PFA_KERNEL_IOTA: return "iota_rows_kernel";
+        default: return "unknown";
+    }
+}
 
 }  // extern "C"

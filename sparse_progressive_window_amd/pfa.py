@@ -44,6 +44,13 @@ def load():
         lib.pfa_strerror.argtypes = [ctypes.c_int]
         lib.pfa_strerror.restype = ctypes.c_char_p
         lib.pfa_version.restype = ctypes.c_int
+        lib.pfa_timing_enable.argtypes = [i32]
+        lib.pfa_timing_enable.restype = ctypes.c_int
+        lib.pfa_timing_count.restype = i32
+        lib.pfa_timing_read.argtypes = [P, P, i32, P, P]
+        lib.pfa_timing_read.restype = ctypes.c_int
+        lib.pfa_kernel_name.argtypes = [i32]
+        lib.pfa_kernel_name.restype = ctypes.c_char_p
         _lib = lib
     return _lib
 
@@ -163,3 +170,33 @@ def sparse_layer(Q, K, V, I_prev, A_prev, K_l, *, win, shift=0, i_shared=False, 
     if rc != 0:
         raise PfaError("pfa_sparse_layer", rc)
     return I, A, O
+
+
+KERNEL_KINDS = ("dense", "all_candidates", "sparse", "select", "aggregate", "iota")
+
+
+def kernel_name(kind: int) -> str:
+    return load().pfa_kernel_name(kind).decode()
+
+
+def timing_enable(capacity: int) -> None:
+    """Bracket every kernel the layer calls launch with HIP events on its stream
+    (capacity = launches kept until the next read; 0 switches timing off)."""
+    rc = load().pfa_timing_enable(int(capacity))
+    if rc != 0:
+        raise PfaError("pfa_timing_enable", rc)
+
+
+def timing_count() -> int:
+    return int(load().pfa_timing_count())
+
+
+def timing_read(cap: int = 4096):
+    """Wait for the recorded launches; returns ([(kind, ms), ...] in launch order, dropped)."""
+    kinds = (ctypes.c_int32 * max(cap, 1))()
+    ms = (ctypes.c_float * max(cap, 1))()
+    n, dropped = ctypes.c_int32(0), ctypes.c_int32(0)
+    rc = load().pfa_timing_read(kinds, ms, int(cap), ctypes.byref(n), ctypes.byref(dropped))
+    if rc != 0:
+        raise PfaError("pfa_timing_read", rc)
+    return [(int(kinds[i]), float(ms[i])) for i in range(n.value)], int(dropped.value)

@@ -35,6 +35,24 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_timing_calls_without_device(lib):
+    # enabling with 0 / reading an empty record list touch no HIP state
+    assert lib.pfa_timing_enable(-1) == -1
+    assert lib.pfa_timing_enable(1 << 21) == -1
+    assert lib.pfa_timing_enable(0) == 0
+    assert lib.pfa_timing_count() == 0
+    n, dropped = ctypes.c_int32(7), ctypes.c_int32(7)
+    assert lib.pfa_timing_read(None, None, 0, ctypes.byref(n), ctypes.byref(dropped)) == 0
+    assert (n.value, dropped.value) == (0, 0)
+    assert lib.pfa_timing_read(None, None, 0, None, None) == -1
+    assert lib.pfa_timing_read(None, None, 4, ctypes.byref(n), None) == -1
+    assert lib.pfa_timing_read(None, None, -1, ctypes.byref(n), None) == -1
+    names = [lib.pfa_kernel_name(k).decode() for k in range(6)]
+    assert names == ["dense_layer_kernel", "all_cand_kernel", "sparse_layer_kernel",
+                     "sparse_layer_kernel(select)", "aggregate_kernel", "iota_rows_kernel"]
+    assert lib.pfa_kernel_name(99) == b"unknown"
+
+
 def test_version_and_strerror(lib):
     assert lib.pfa_version() == 10000
     assert lib.pfa_strerror(0) == b"ok"

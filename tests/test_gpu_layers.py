@@ -234,6 +234,32 @@ def test_error_codes():
 
 
 @pytest.mark.timeout(120)
+def test_kernel_timing_records():
+    # every launch of the layer calls is bracketed by events while timing is on
+    shape = (1, 2, 64, 64, 32)
+    Qd, Kd, Vd = (to_dev(inputs.draw(900 + t, shape, "f32")) for t in range(3))
+    pfa.timing_enable(8)
+    try:
+        I1, A1, O1 = pfa.dense_layer(Qd, Kd, Vd, 1024, win=32, want_I=True)
+        n1 = pfa.timing_count()
+        I2, A2, O2 = pfa.sparse_layer(Qd, Kd, Vd, None, A1, 256, win=32, shift=16)
+        I3, A3, O3 = pfa.sparse_layer(Qd, Kd, Vd, I2, A2, 128, win=32)
+        recs, dropped = pfa.timing_read()
+        assert pfa.timing_count() == 0
+    finally:
+        pfa.timing_enable(0)
+    kinds = [k for k, _ in recs]
+    names = [pfa.kernel_name(k) for k in kinds]
+    assert n1 == 2 and dropped == 0
+    assert names[:3] == ["dense_layer_kernel", "iota_rows_kernel", "all_cand_kernel"], names
+    assert names[-1] == "aggregate_kernel", names
+    assert all(ms > 0 for _, ms in recs)
+    # results with timing on equal those with timing off
+    _, A2b, O2b = pfa.sparse_layer(Qd, Kd, Vd, None, A1, 256, win=32, shift=16)
+    assert torch.equal(A2, A2b) and torch.equal(O2, O2b)
+
+
+@pytest.mark.timeout(120)
 @pytest.mark.parametrize("K_prev,K_l", [(1024, 256), (256, 128), (64, 32)])
 def test_nonfinite_previous_map_terminates(K_prev, K_l):
     # NaN, negative and infinite previous weights violate the preconditions; the
