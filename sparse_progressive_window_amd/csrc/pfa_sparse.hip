@@ -752,6 +752,95 @@ __global__ __launch_bounds__(NW * kWave) void aggregate_kernel(const SparseArgs 
     }
 }
 
+// Same result for K_l <= 256 and K_l % 4 == 0, organised for memory-level
+// parallelism: a wavefront takes R consecutive query rows per step, whose I^l /
+// A^l entries are one contiguous run of R*K_l <= 256 entries, loaded with one
+// 16-byte load per lane for I and one for A, a step ahead of their use. The
+// entries are staged in a per-wave LDS buffer; a group of GL = 64/R lanes then
+// accumulates one row, CH lanes per V row (one 16-byte chunk each), GS = GL/CH
+// entries of the row at a time, 4 consecutive entries per LDS read.
+template <typename T, int D, int R, int NW>
+__global__ __launch_bounds__(NW * kWave) void aggregate_rows_kernel(const SparseArgs p) {
+    constexpr int EPC = Chunk<T>::kElems;
+    constexpr int CH = D / EPC;
+    constexpr int ROWB = D * (int)sizeof(T);
+    constexpr int GL = kWave / R;
+    constexpr int GS = GL / CH;
+    static_assert(GS >= 1, "a row needs at least CH lanes");
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const Geom g = p.g;
+    const int N = g.N;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int grp = lane / GL;
+    const int gl = lane & (GL - 1);
+    const int vchunk = gl % CH;
+    const int vsub = gl / CH;
+    const WhPart w = decode_block(p.blocks_per_wh, p.xcd_map, g);
+    const size_t plane = (size_t)w.bh * g.H * g.W * D;
+    const T* Vh = static_cast<const T*>(p.V) + plane;
+    float* Oh = p.O_out + plane;
+    int* sj = reinterpret_cast<int*>(smem + N * ROWB) + wave * 512;   // 256 indices, then 256 weights
+    float* sw = reinterpret_cast<float*>(sj + 256);
+    stage_rows<T, D>(smem, ROWB, Vh, g, w.wy, w.wx);
+    __syncthreads();
+
+    const int K_l = p.K_l;
+    const int row0 = w.part * p.rows_per_block;
+    const int row1 = min(N, row0 + p.rows_per_block);
+    const int32_t* Iw = p.I_out + (size_t)w.wh * N * K_l;
+    const float* Aw = p.A_out + (size_t)w.wh * N * K_l;
+    int4 jn = make_int4(0, 0, 0, 0);
+    float4 wn = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto load = [&](int base) {   // entries [base*K_l, min(base+R, row1)*K_l) of the window-head
+        const int e = base * K_l + lane * 4;
+        if (e < min(base + R, row1) * K_l) {
+            jn = *reinterpret_cast<const int4*>(Iw + e);
+            wn = *reinterpret_cast<const float4*>(Aw + e);
+        }
+    };
+    int base = row0 + wave * R;
+    if (base < row1) load(base);
+    for (; base < row1; base += NW * R) {
+        *reinterpret_cast<int4*>(sj + lane * 4) = jn;
+        *reinterpret_cast<float4*>(sw + lane * 4) = wn;
+        if (base + NW * R < row1) load(base + NW * R);
+        const int i = base + grp;
+        float oacc[EPC];
+#pragma unroll
+        for (int x = 0; x < EPC; ++x) oacc[x] = 0.0f;
+        if (i < row1) {
+            const int* rj = sj + grp * K_l;
+            const float* rw = sw + grp * K_l;
+            for (int e = vsub * 4; e < K_l; e += GS * 4) {
+                const int4 j4 = *reinterpret_cast<const int4*>(rj + e);
+                const float4 w4 = *reinterpret_cast<const float4*>(rw + e);
+                const int jv[4] = {j4.x, j4.y, j4.z, j4.w};
+                const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+                float vf[4][EPC];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int j = min(max(jv[x], 0), N - 1);
+                    Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(smem + j * ROWB + vchunk * 16), vf[x]);
+                }
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+#pragma unroll
+                    for (int y = 0; y < EPC; ++y) oacc[y] = fmaf(wv[x], vf[x][y], oacc[y]);
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < EPC; ++x) oacc[x] = reduce_chunk_lanes<CH, GL>(oacc[x]);
+        if (i < row1 && vsub == 0) {
+            float* orow = Oh + (size_t)slot_pixel(g, w.wy, w.wx, i) * D + vchunk * EPC;
+#pragma unroll
+            for (int x = 0; x < EPC; x += 4)
+                *reinterpret_cast<float4*>(orow + x) = make_float4(oacc[x], oacc[x + 1], oacc[x + 2], oacc[x + 3]);
+        }
+    }
+}
+
 template <class F>
 hipError_t launch_fn(F fn, const SparseArgs& a, int threads, int lds, int grid, hipStream_t s) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -802,6 +891,17 @@ hipError_t launch_all_cand_t(const SparseArgs& a, bool with_av, int grid, hipStr
 template <typename T, int D>
 hipError_t launch_aggregate_t(const SparseArgs& a, int grid, hipStream_t s) {
     const int lds = a.g.N * D * (int)sizeof(T);
+    constexpr int RMAX = kWave / (D / Chunk<T>::kElems);   // rows per step with CH lanes per row
+    if (a.K_l <= 256 && a.K_l % 4 == 0 && lds + 16 * 2048 <= kLdsBytes) {
+        const int l2 = lds + 16 * 2048;
+        const int r = 256 / a.K_l;   // rows whose entries fill one 16-byte load per lane
+        if (r >= 16 && RMAX >= 16) return launch_fn(aggregate_rows_kernel<T, D, (RMAX >= 16 ? 16 : 1), 16>, a,
+                                                    16 * kWave, l2, grid, s);
+        if (r >= 8 && RMAX >= 8) return launch_fn(aggregate_rows_kernel<T, D, 8, 16>, a, 16 * kWave, l2, grid, s);
+        if (r >= 4) return launch_fn(aggregate_rows_kernel<T, D, 4, 16>, a, 16 * kWave, l2, grid, s);
+        if (r >= 2) return launch_fn(aggregate_rows_kernel<T, D, 2, 16>, a, 16 * kWave, l2, grid, s);
+        return launch_fn(aggregate_rows_kernel<T, D, 1, 16>, a, 16 * kWave, l2, grid, s);
+    }
     if (a.K_l <= 16) return launch_fn(aggregate_kernel<T, D, 16, 16>, a, 16 * kWave, lds, grid, s);
     if (a.K_l <= 32) return launch_fn(aggregate_kernel<T, D, 32, 16>, a, 16 * kWave, lds, grid, s);
     return launch_fn(aggregate_kernel<T, D, 64, 16>, a, 16 * kWave, lds, grid, s);
