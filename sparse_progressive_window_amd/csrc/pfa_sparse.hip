@@ -62,6 +62,7 @@ struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf
 struct SumF { __device__ float operator()(float a, float b) const { return a + b; } };
 struct MaxI { __device__ int operator()(int a, int b) const { return max(a, b); } };
 struct MinI { __device__ int operator()(int a, int b) const { return min(a, b); } };
+struct SumI { __device__ int operator()(int a, int b) const { return a + b; } };
 
 // Reductions and counts over a group of GL consecutive lanes; every lane of the
 // group receives the result.
@@ -175,11 +176,135 @@ __device__ __forceinline__ void keys_from_scores(const float (&av)[KPT], const b
     for (int t = 0; t < KPT; ++t) sv[t] = valid[t] ? fmaxf(av[t] * fast_exp2(sv[t] - smax), 0.0f) : 0.0f;
 }
 
+// Exact K_l-th largest key of one query row held by a group of GL lanes (key(t)
+// = this lane's t-th key, -1 for no candidate) by radix descent: the key
+// interval [lo, hi) is cut into NB = BPL*GL bins of 2^shift consecutive keys
+// (bit-field slices), counted with LDS atomics; a prefix scan over the bins in
+// descending order (BPL bins per lane) finds the bin that holds the K_l-th key;
+// keys in higher bins are kept, keys in lower bins are dropped, and the search
+// descends into that bin. Each level removes log2(NB) bits from the interval, so
+// it ends after at most 8 levels (usually 2 or 3). Result: every key > tau is
+// kept, need_tau more are needed among the n_tau keys equal to tau.
+template <int GL, int BPL, int KPT, class KF>
+__device__ __forceinline__ void radix_threshold(KF key, int kmin, int kmax, bool active, int K_prev, int K_l,
+                                                unsigned* hb, int gl, int& tau, int& need_tau, int& n_tau) {
+    using G = Grp<GL>;
+    constexpr int NB = BPL * GL;
+    constexpr int LOG2NB = G::kLog2 + (BPL == 8 ? 3 : BPL == 4 ? 2 : BPL == 2 ? 1 : 0);
+    static_assert(BPL == 1 || BPL == 2 || BPL == 4 || BPL == 8, "bins per lane");
+    int lo = kmin, hi = kmax + 1, need = K_l;
+    tau = lo;
+    need_tau = K_l;
+    n_tau = 0;
+    bool done = !active;
+    if (active && hi - lo <= 1) {   // all keys equal
+        done = true;
+        n_tau = K_prev;
+    }
+    while (ballot(!done) != 0) {
+        const int span = max(hi - lo, 2);
+        const int shift = max(32 - __clz(span - 1) - LOG2NB, 0);
+        if (BPL >= 4) {
+#pragma unroll
+            for (int b = 0; b < BPL; b += 4) *reinterpret_cast<uint4*>(hb + BPL * gl + b) = make_uint4(0u, 0u, 0u, 0u);
+        } else if (BPL == 2) {
+            *reinterpret_cast<uint2*>(hb + 2 * gl) = make_uint2(0u, 0u);
+        } else {
+            hb[gl] = 0u;
+        }
+#pragma unroll
+        for (int t = 0; t < KPT; ++t) {
+            const unsigned dk = (unsigned)(key(t) - lo);
+            if (!done && dk < (unsigned)(hi - lo)) atomicAdd(&hb[dk >> shift], 1u);
+        }
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // this lane's bins in descending key order: NB-1-BPL*gl-b, b = 0..BPL-1
+        unsigned cb[BPL];
+        if (BPL >= 4) {
+#pragma unroll
+            for (int b = 0; b < BPL; b += 4) {
+                const uint4 c4 = *reinterpret_cast<const uint4*>(hb + NB - BPL * (gl + 1) + b);
+                cb[BPL - 1 - b] = c4.x;
+                cb[BPL - 2 - b] = c4.y;
+                cb[BPL - 3 - b] = c4.z;
+                cb[BPL - 4 - b] = c4.w;
+            }
+        } else if (BPL == 2) {
+            const uint2 c2 = *reinterpret_cast<const uint2*>(hb + NB - 2 - 2 * gl);
+            cb[0] = c2.y;
+            cb[BPL - 1] = c2.x;
+        } else {
+            cb[0] = hb[NB - 1 - gl];
+        }
+        unsigned lsum = 0;
+#pragma unroll
+        for (int b = 0; b < BPL; ++b) lsum += cb[b];
+        const unsigned incl = G::incl_scan(lsum);
+        unsigned run = incl - lsum;
+#pragma unroll
+        for (int b = 0; b < BPL; ++b) {
+            if (!done && run < (unsigned)need && run + cb[b] >= (unsigned)need) {   // exactly one bin per group
+                hb[NB] = (unsigned)(NB - 1 - BPL * gl - b);
+                hb[NB + 1] = run;
+                hb[NB + 2] = cb[b];
+            }
+            run += cb[b];
+        }
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int bin = (int)hb[NB];
+        const int above = (int)hb[NB + 1];
+        const int in_bin = (int)hb[NB + 2];
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (!done) {
+            need -= above;
+            lo += bin << shift;
+            hi = min(hi, lo + (1 << shift));
+            if (in_bin == need || hi - lo <= 1) {   // whole bin kept, or all its keys equal (ties)
+                tau = lo;
+                need_tau = need;
+                n_tau = in_bin;
+                done = true;
+            }
+        }
+    }
+}
+
+// Exact ties at the threshold keep the lowest slot indices: the smallest jcut
+// such that need_tau keys equal to tau have j <= jcut (bisection on j), or
+// INT_MAX when the row has no tie to break. any_tie: some row of the wave has.
+template <int GL, int KPT, class KF, class JF>
+__device__ __forceinline__ int tie_cut(KF key, JF jf, int tau, int need_tau, int n_tau, bool active, int N,
+                                       int lane, bool& any_tie) {
+    using G = Grp<GL>;
+    int jcut = 0x7fffffff;
+    const bool tie = active && n_tau > need_tau;
+    any_tie = ballot(tie) != 0;
+    if (any_tie) {
+        int jl = -1, jh = N - 1;
+        while (ballot(tie && jh - jl > 1) != 0) {
+            const int mid = (jl + jh) >> 1;
+            // a copy of tau made inside the loop keeps the KPT comparisons from being
+            // hoisted out of it as KPT live lane masks
+            int tq = tau, mq = mid;
+            __asm__ volatile("" : "+v"(tq), "+v"(mq));
+            int cl = 0;   // per-lane count, then one group sum
+#pragma unroll
+            for (int t = 0; t < KPT; ++t) cl += (key(t) == tq && jf(t) <= mq) ? 1 : 0;
+            const int cnt = G::all_i(cl, SumI());
+            if (tie && jh - jl > 1) {
+                if (cnt >= need_tau) jh = mid; else jl = mid;
+            }
+        }
+        if (tie) jcut = jh;
+    }
+    return jcut;
+}
+
 // Everything after the keys of one query row: the exact top-K_l (ties to the
 // lower slot index), the I^l / A^l row in I^{l-1} order and, unless
 // VS == kVnone, O_i = sum_kept A v_j. jj/valid/uv are this lane's candidates
 // c = gl + GL*t; uv = A^{l-1} exp(s - m) >= 0.
-template <typename T, int D, int GL, int KPT, int VS>
+template <typename T, int D, int GL, int KPT, int VS, int BPL>
 __device__ __forceinline__ void select_emit(const SparseArgs& p, const Geom& g, int lane, bool active, size_t row,
                                             int qpix, int wy, int wx, const int (&jj)[KPT], const bool (&valid)[KPT],
                                             const float (&uv_in)[KPT], unsigned* hb, uint2* scr, int scg,
@@ -208,75 +333,16 @@ __device__ __forceinline__ void select_emit(const SparseArgs& p, const Geom& g, 
     kmin = G::all_i(kmin, MinI());
     kmax = G::all_i(kmax, MaxI());
 
-    // Exact K_l-th largest key by radix descent: the key interval [lo, hi) is cut
-    // into GL bins of 2^shift consecutive keys (bit-field slices), counted with LDS
-    // atomics; a prefix scan over the bins in descending order finds the bin that
-    // holds the K_l-th key; keys in higher bins are kept, keys in lower bins are
-    // dropped, and the search descends into that bin. Each level removes log2(GL)
-    // bits from the interval, so it ends after at most 8 levels (usually 3).
-    int lo = kmin, hi = kmax + 1, need = K_l;
-    int tau = lo, need_tau = K_l, n_tau = 0;
-    bool done = !active;
-    if (active && hi - lo <= 1) {   // all keys equal
-        done = true;
-        n_tau = K_prev;
-    }
-    while (ballot(!done) != 0) {
-        const int span = max(hi - lo, 2);
-        const int shift = max(32 - __clz(span - 1) - G::kLog2, 0);
-        hb[gl] = 0u;
-#pragma unroll
-        for (int t = 0; t < KPT; ++t) {
-            const unsigned dk = (unsigned)(key[t] - lo);
-            if (!done && dk < (unsigned)(hi - lo)) atomicAdd(&hb[dk >> shift], 1u);
-        }
-        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        const unsigned c = hb[GL - 1 - gl];          // bins in descending key order
-        const unsigned incl = G::incl_scan(c);
-        const unsigned excl = incl - c;
-        if (!done && excl < (unsigned)need && incl >= (unsigned)need) {   // exactly one lane per group
-            hb[GL] = (unsigned)(GL - 1 - gl);
-            hb[GL + 1] = excl;
-            hb[GL + 2] = c;
-        }
-        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        const int bin = (int)hb[GL];
-        const int above = (int)hb[GL + 1];
-        const int in_bin = (int)hb[GL + 2];
-        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (!done) {
-            need -= above;
-            lo += bin << shift;
-            hi = min(hi, lo + (1 << shift));
-            if (in_bin == need || hi - lo <= 1) {   // whole bin kept, or all its keys equal (ties)
-                tau = lo;
-                need_tau = need;
-                n_tau = in_bin;
-                done = true;
-            }
-        }
-    }
-
-    // exact ties at the threshold: keep the lowest slot indices
-    int jcut = 0x7fffffff;
-    const bool tie = active && n_tau > need_tau;
-    if (ballot(tie) != 0) {
-        int jl = -1, jh = g.N - 1;
-        while (ballot(tie && jh - jl > 1) != 0) {
-            const int mid = (jl + jh) >> 1;
-            int cnt = 0;
-#pragma unroll
-            for (int t = 0; t < KPT; ++t) cnt += G::count(key[t] == tau && jj[t] <= mid, lane);
-            if (tie && jh - jl > 1) {
-                if (cnt >= need_tau) jh = mid; else jl = mid;
-            }
-        }
-        if (tie) jcut = jh;
-    }
+    int tau, need_tau, n_tau;
+    radix_threshold<GL, BPL, KPT>([&](int t) { return key[t]; }, kmin, kmax, active, K_prev, K_l, hb, gl, tau,
+                                  need_tau, n_tau);
+    bool tie;
+    const int jcut = tie_cut<GL, KPT>([&](int t) { return key[t]; }, [&](int t) { return jj[t]; }, tau, need_tau,
+                                      n_tau, active, g.N, lane, tie);
 
     bool kept[KPT];
     float ksum = 0.0f;
-    if (ballot(tie) == 0) {   // usual case: every key equal to tau is kept
+    if (!tie) {   // usual case: every key equal to tau is kept
 #pragma unroll
         for (int t = 0; t < KPT; ++t) kept[t] = key[t] >= tau;
     } else {
@@ -350,6 +416,103 @@ __device__ __forceinline__ void select_emit(const SparseArgs& p, const Geom& g, 
     }
 }
 
+// Top-K_l of one query row held by a group of GL lanes, written straight from
+// registers (no aggregation in this kernel): lane gl's t-th candidate is slot
+// jf(t), present when vf(t), with weight uv[t] = A^{l-1} exp(s - m) >= 0. The
+// kept entries of register t occupy consecutive positions across the group's
+// lanes (ballot prefix counts), so the t-loop emits I^l / A^l in candidate order
+// with one store per register through buffer resources (32-bit offsets).
+// ORDERED: jf is increasing in (t, lane) order, so exact ties at the threshold
+// are resolved by rank in that order (the lowest slots first) within the store
+// loop; otherwise by bisection on j.
+template <int GL, int KPT, int BPL, bool ORDERED, class JF, class VF>
+__device__ __forceinline__ void select_store(const SparseArgs& p, int lane, bool active, int N, JF jf, VF vf,
+                                             const float (&uv)[KPT], unsigned* hb, __amdgpu_buffer_rsrc_t rI,
+                                             __amdgpu_buffer_rsrc_t rA, int row_off) {
+    using G = Grp<GL>;
+    const int gl = lane & (GL - 1);
+    const int K_prev = p.K_prev;
+    const int K_l = p.K_l;
+    auto key = [&](int t) { return vf(t) ? __float_as_int(uv[t]) : -1; };
+
+    int kmin = 0x7fffffff, kmax = -1;
+#pragma unroll
+    for (int t = 0; t < KPT; ++t) {
+        if (vf(t)) {
+            kmin = min(kmin, key(t));
+            kmax = max(kmax, key(t));
+        }
+    }
+    kmin = G::all_i(kmin, MinI());
+    kmax = G::all_i(kmax, MaxI());
+
+    int tau, need_tau, n_tau;
+    radix_threshold<GL, BPL, KPT>(key, kmin, kmax, active, K_prev, K_l, hb, gl, tau, need_tau, n_tau);
+    // tie: more keys equal tau (the interval shrank to one key value) than are needed
+    const bool tie = active && n_tau > need_tau;
+    const bool any_tie = ballot(tie) != 0;
+    int jcut = 0x7fffffff;
+    if (!ORDERED && any_tie) {
+        bool unused;
+        jcut = tie_cut<GL, KPT>(key, jf, tau, need_tau, n_tau, active, N, lane, unused);
+    }
+
+    float ksum = 0.0f;
+    if (!any_tie) {
+#pragma unroll
+        for (int t = 0; t < KPT; ++t) ksum += key(t) >= tau ? uv[t] : 0.0f;
+    } else if (ORDERED) {
+        // the need_tau kept keys equal to tau all weigh the same
+#pragma unroll
+        for (int t = 0; t < KPT; ++t) ksum += (tie ? key(t) > tau : key(t) >= tau) ? uv[t] : 0.0f;
+    } else {
+#pragma unroll
+        for (int t = 0; t < KPT; ++t) ksum += (key(t) > tau || (key(t) == tau && jf(t) <= jcut)) ? uv[t] : 0.0f;
+    }
+    ksum = G::all(ksum, SumF());
+    if (ORDERED && tie) ksum += (float)need_tau * __int_as_float(tau);
+    const float inv = 1.0f / ksum;
+
+    // the store loop compares with a copy of tau the compiler cannot see through,
+    // so it does not keep KPT comparison masks alive from the sums above
+    int tau2 = tau;
+    __asm__ volatile("" : "+v"(tau2));
+    int obase = 0;
+    int tbase = 0;   // ORDERED ties: keys equal to tau met so far in the group
+    auto emit = [&](int t, bool k) {
+        const uint64_t m = ballot(k);
+        const int pos = obase + G::below(m, lane);
+        if (active && k && pos < K_l) {   // pos >= K_l only on precondition violations
+            const int off = (row_off + pos) * 4;
+            __builtin_amdgcn_raw_buffer_store_b32(jf(t), rI, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(uv[t] * inv), rA, off, 0, 0);
+        }
+        obase += G::count_mask(m, lane);
+    };
+    if (!any_tie) {
+#pragma unroll
+        for (int t = 0; t < KPT; ++t) emit(t, key(t) >= tau2);
+    } else if (ORDERED) {
+#pragma unroll
+        for (int t = 0; t < KPT; ++t) {
+            const bool eq = tie && key(t) == tau2;
+            const uint64_t me = ballot(eq);
+            const int rank = tbase + G::below(me, lane);
+            tbase += G::count_mask(me, lane);
+            emit(t, tie ? key(t) > tau2 || (eq && rank < need_tau) : key(t) >= tau2);
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < KPT; ++t) emit(t, key(t) > tau2 || (key(t) == tau2 && jf(t) <= jcut));
+    }
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw, 32-bit elements); accesses
+// past the end are dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
 struct WhPart {
     int wh, part, wy, wx, b, bh, win_id, nwin;
 };
@@ -402,16 +565,19 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
     constexpr bool K_LDS = MODE != kKVglobal;
     constexpr bool V_LDS = MODE == kKVinLDS;
     constexpr int VS = MODE == kKVinLDS ? kVlds : MODE == kKinLDS ? kVwin : MODE == kKVglobal ? kVraster : kVnone;
-    constexpr int HISTW = RPW * (GL + 4);            // radix-select histogram words per wave
+    constexpr int BPL = VS == kVnone ? 4 : 1;        // radix bins per lane (no (j, weight) staging: more bins)
+    constexpr int HISTG = BPL * GL + 4;              // histogram words per row group
+    constexpr int HISTW = RPW * HISTG;               // radix-select histogram words per wave
     constexpr int HIST_BYTES = NW * HISTW * 4;
-    constexpr int SCW = (kScratchBytes - HIST_BYTES) / (NW * 8);   // (j, weight) entries per wave
-    constexpr int SCG = SCW / RPW;                                 // entries per row group
+    static_assert(HIST_BYTES <= kScratchBytes, "histograms exceed the scratch area");
+    constexpr int SCW = VS == kVnone ? 0 : (kScratchBytes - HIST_BYTES) / (NW * 8);   // (j, weight) entries per wave
+    constexpr int SCG = SCW / RPW;                                                   // entries per row group
     extern __shared__ __align__(16) unsigned char smem[];
 
     const Geom g = p.g;
     const int N = g.N;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int grp = lane / GL;
     const int gl = lane & (GL - 1);
     const WhPart w = decode_block(p.blocks_per_wh, p.xcd_map, g);
@@ -424,7 +590,7 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
     unsigned char* Ks = smem;
     unsigned char* Vs = smem + (K_LDS ? N * ROWB : 0);
     unsigned char* sbase = smem + (K_LDS ? N * ROWB : 0) + (V_LDS ? N * ROWB : 0);
-    unsigned* hb = reinterpret_cast<unsigned*>(sbase) + wave * HISTW + grp * (GL + 4);
+    unsigned* hb = reinterpret_cast<unsigned*>(sbase) + wave * HISTW + grp * HISTG;
     uint2* scr = reinterpret_cast<uint2*>(sbase + HIST_BYTES) + wave * SCW + grp * SCG;
 
     if (K_LDS) {
@@ -518,8 +684,16 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
             sv[t] = valid[t] ? acc * p.scale2 : -INFINITY;
         }
         keys_from_scores<GL, KPT>(cur.a, valid, sv);
-        select_emit<T, D, GL, KPT, VS>(p, g, lane, active, row, qpix, w.wy, w.wx, jj, valid, sv, hb, scr, SCG, Vs,
-                                       Vh, Oh);
+        if constexpr (VS == kVnone) {
+            const size_t rbase = ((size_t)w.wh * N + base) * p.K_l;
+            const int nbytes = max(0, min(RPW, row1 - base)) * p.K_l * 4;
+            select_store<GL, KPT, BPL, false>(
+                p, lane, active, N, [&](int t) { return jj[t]; }, [&](int t) { return valid[t]; }, sv, hb,
+                make_rsrc(p.I_out + rbase, nbytes), make_rsrc(p.A_out + rbase, nbytes), grp * p.K_l);
+        } else {
+            select_emit<T, D, GL, KPT, VS, BPL>(p, g, lane, active, row, qpix, w.wy, w.wx, jj, valid, sv, hb, scr,
+                                                SCG, Vs, Vh, Oh);
+        }
         cur = nxt;
     }
 }
@@ -569,9 +743,11 @@ __global__ __launch_bounds__(8 * kWave) void all_cand_kernel(const SparseArgs p)
     constexpr int ROWB = D * (int)sizeof(T);
     constexpr int KSTR = ROWB + 16;
     constexpr int KK = Mfma4<T>::kK;
-    constexpr int HISTW = GL + 4;
+    constexpr int BPL = VS == kVnone ? 4 : 1;
+    constexpr int HISTW = BPL * GL + 4;
     constexpr int HIST_BYTES = NW * HISTW * 4;
-    constexpr int SCW = (kScratchBytes / 2 - HIST_BYTES) / (NW * 8);
+    static_assert(HIST_BYTES <= kScratchBytes / 2, "histograms exceed the scratch area");
+    constexpr int SCW = VS == kVnone ? 0 : (kScratchBytes / 2 - HIST_BYTES) / (NW * 8);
     extern __shared__ __align__(16) unsigned char smem[];
 
     const Geom g = p.g;
@@ -671,9 +847,150 @@ __global__ __launch_bounds__(8 * kWave) void all_cand_kernel(const SparseArgs p)
                 // register select (r is a loop variable: indexing s4[r] would spill to scratch)
                 uv[t] = r == 0 ? s4[0][t] : r == 1 ? s4[1][t] : r == 2 ? s4[2][t] : s4[3][t];
             }
-            select_emit<T, D, GL, KPT, VS>(p, g, lane, active, row, slot_pixel(g, w.wy, w.wx, ii), w.wy, w.wx, jj,
-                                           valid, uv, hb, scr, SCW, Vs, Vh, Oh);
+            select_emit<T, D, GL, KPT, VS, BPL>(p, g, lane, active, row, slot_pixel(g, w.wy, w.wx, ii), w.wy, w.wx,
+                                                jj, valid, uv, hb, scr, SCW, Vs, Vh, Oh);
         }
+    }
+}
+
+// Chunk permutation of the LDS-resident K rows of the all-candidates kernel
+// (128-byte rows, no pad): chunk c of row r is stored at position c ^ kswz(r),
+// so the MFMA operand reads of 16 consecutive rows at one chunk position touch
+// 16 different bank groups.
+__device__ __forceinline__ int kswz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// Selection-only layer whose candidate list is every slot of a 32x32 window
+// (I^{l-1} implicit, K_prev = N = 1024). Scores of a batch of 4 query rows x 64
+// candidates come from 4x4 MFMA blocks (A = the 4 query rows, B = 64 K rows from
+// LDS), which leaves candidate 64t + l of all 4 rows in lane l. A 4x4 transpose
+// across the wave's lane quarters (v_permlane32_swap, v_permlane16_swap) then
+// gives each 16-lane quarter one query row: lane 16g + b holds row g's candidates
+// 16k + b, k = 0..63, so the 4 rows are selected together, one per 16-lane group.
+template <typename T, int D, bool HAS_A>
+__global__ __launch_bounds__(8 * kWave) void all_cand_rows_kernel(const SparseArgs p) {
+    constexpr int NW = 8;
+    constexpr int GL = 16;
+    constexpr int KPT = 64;
+    constexpr int BPL = 8;                   // 128 radix bins per row
+    constexpr int EPC = Chunk<T>::kElems;
+    constexpr int CH = D / EPC;
+    constexpr int ROWB = D * (int)sizeof(T);
+    constexpr bool SWZ = CH == 8;            // 128-byte rows: chunk-swizzled, unpadded
+    constexpr int KSTR = SWZ ? ROWB : ROWB + 16;
+    constexpr int KK = Mfma4<T>::kK;
+    constexpr int HISTG = BPL * GL + 4;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const Geom g = p.g;
+    const int N = g.N;   // 1024
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int grp = lane >> 4;
+    const int gl = lane & (GL - 1);
+    const WhPart w = decode_block(p.blocks_per_wh, p.xcd_map, g);
+    const size_t plane = (size_t)w.bh * g.H * g.W * D;
+    const T* Qh = static_cast<const T*>(p.Q) + plane;
+    const T* Kh = static_cast<const T*>(p.K) + plane;
+
+    unsigned char* Ks = smem;
+    unsigned* hb = reinterpret_cast<unsigned*>(smem + N * KSTR) + (wave * 4 + grp) * HISTG;
+    if (SWZ) {
+        for (int u = threadIdx.x; u < N * CH; u += blockDim.x) {
+            const int t = u / CH;
+            const int c = u - t * CH;
+            const size_t src = (size_t)slot_pixel(g, w.wy, w.wx, t) * D + c * EPC;
+            *reinterpret_cast<uint4*>(Ks + t * ROWB + ((c ^ kswz(t)) * 16)) = *reinterpret_cast<const uint4*>(Kh + src);
+        }
+    } else {
+        stage_rows<T, D>(Ks, KSTR, Kh, g, w.wy, w.wx);
+    }
+    __syncthreads();
+
+    const int row0 = w.part * p.rows_per_block;
+    const int row1 = min(N, row0 + p.rows_per_block);
+    const int K_l = p.K_l;
+    const int swl = SWZ ? kswz(lane) : 0;   // B-operand rows 64t + lane all share this permutation
+    const float scale2 = p.scale2;
+
+    // A^{l-1} of the batch in the transposed layout: lane (g, b) holds row base+g,
+    // slots 16k + b; the next batch is loaded while this one is selected
+    float ab[KPT];
+    auto load_batch = [&](int b0) {
+        const int i = min(b0 + grp, N - 1);
+        if (HAS_A) {
+            const float* arow = p.A_prev + ((size_t)w.wh * N + i) * N + gl;
+#pragma unroll
+            for (int k = 0; k < KPT; ++k) ab[k] = arow[GL * k];
+        }
+    };
+    load_batch(row0 + wave * 4);
+    for (int base = row0 + wave * 4; base < row1; base += NW * 4) {
+        const int qi = min(base + (lane & 3), row1 - 1);
+        float qf[D];
+        const unsigned char* qrow =
+            reinterpret_cast<const unsigned char*>(Qh + (size_t)slot_pixel(g, w.wy, w.wx, qi) * D);
+#pragma unroll
+        for (int m = 0; m < CH; ++m) Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(qrow + 16 * m), &qf[m * EPC]);
+
+        float uv[KPT];   // raw scores q.k, then the keys
+#pragma unroll
+        for (int t = 0; t < 16; t += 4) {   // 4 independent accumulator chains
+            v4f acc[4];
+            const unsigned char* kr[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                acc[x] = v4f{0.f, 0.f, 0.f, 0.f};
+                kr[x] = Ks + (kWave * (t + x) + lane) * KSTR;
+            }
+#pragma unroll
+            for (int m = 0; m < CH; ++m) {
+                float kf[4][EPC];
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(kr[x] + (SWZ ? (m ^ swl) : m) * 16), kf[x]);
+#pragma unroll
+                for (int e = 0; e < EPC; e += KK)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) acc[x] = Mfma4<T>::run(&qf[m * EPC + e], &kf[x][e], acc[x]);
+            }
+            // acc[x][r] = s(row r, candidate 64(t+x) + lane): transpose (lane quarter, r)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const auto p02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[x][0]),
+                                                                  __float_as_uint(acc[x][2]), false, false);
+                const auto p13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[x][1]),
+                                                                  __float_as_uint(acc[x][3]), false, false);
+                const auto q01 = __builtin_amdgcn_permlane16_swap(p02[0], p13[0], false, false);
+                const auto q23 = __builtin_amdgcn_permlane16_swap(p02[1], p13[1], false, false);
+                uv[4 * (t + x) + 0] = __uint_as_float(q01[0]);   // candidate 64(t+x) + 16q + gl of row grp
+                uv[4 * (t + x) + 1] = __uint_as_float(q01[1]);
+                uv[4 * (t + x) + 2] = __uint_as_float(q23[0]);
+                uv[4 * (t + x) + 3] = __uint_as_float(q23[1]);
+            }
+        }
+        // keys u = A^{l-1} exp2(scale2 (s - max s)), then the next batch's loads
+        float smax = uv[0];
+#pragma unroll
+        for (int k = 1; k < KPT; ++k) smax = fmaxf(smax, uv[k]);
+        const float c = -Grp<GL>::all(smax, MaxF()) * scale2;
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            const float e = fast_exp2(fmaf(uv[k], scale2, c));
+            uv[k] = HAS_A ? fmaxf(ab[k] * e, 0.0f) : e;
+        }
+        // the next batch's loads go out only once this batch's weights are consumed
+        // (keeps two batches of A^{l-1} from being live at once)
+        __asm__ volatile("" ::: "memory");
+        if (base + NW * 4 < row1) load_batch(base + NW * 4);
+
+        // rows past row1 (last batch) are selected but never stored: every group's
+        // ballots and reductions are its own
+        const bool active = base + grp < row1;
+        const size_t rbase = ((size_t)w.wh * N + base) * K_l;
+        const int nbytes = max(0, min(4, row1 - base)) * K_l * 4;
+        select_store<GL, KPT, BPL, true>(
+            p, lane, active, N, [&](int k) { return GL * k + gl; }, [&](int) { return true; }, uv, hb,
+            make_rsrc(p.I_out + rbase, nbytes), make_rsrc(p.A_out + rbase, nbytes), grp * K_l);
     }
 }
 
@@ -885,7 +1202,10 @@ hipError_t launch_all_cand_t(const SparseArgs& a, bool with_av, int grid, hipStr
     const int lds_k = 1024 * (ROWB + 16);
     if (with_av)
         return launch_fn(all_cand_kernel<T, D, kVlds>, a, 8 * kWave, lds_k + 1024 * ROWB + kScratchBytes / 2, grid, s);
-    return launch_fn(all_cand_kernel<T, D, kVnone>, a, 8 * kWave, lds_k + kScratchBytes / 2, grid, s);
+    constexpr int KSTR = ROWB == 128 ? ROWB : ROWB + 16;
+    const int lds = 1024 * KSTR + 8 * 4 * (8 * 16 + 4) * 4;
+    if (a.A_prev) return launch_fn(all_cand_rows_kernel<T, D, true>, a, 8 * kWave, lds, grid, s);
+    return launch_fn(all_cand_rows_kernel<T, D, false>, a, 8 * kWave, lds, grid, s);
 }
 
 template <typename T, int D>

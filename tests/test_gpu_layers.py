@@ -101,11 +101,27 @@ def test_chain_tiny_workload():
 # ---------------------------------------------------------------------------
 # edge cases: ragged and extreme sizes, ties, zeros, shared index matrices
 # ---------------------------------------------------------------------------
+def _on_grid(t):
+    """The tensor's values rounded to multiples of 1/8 (exact in bf16 and fp32)."""
+    v = np.round(t.exact.astype(np.float64) * 8) / 8
+    if t.dtype == "f32":
+        return inputs.Tensor(v.astype(np.float32), v.astype(np.float32), "f32")
+    bits = inputs.bf16_round_bits(v.astype(np.float32))
+    return inputs.Tensor(bits, inputs.bf16_bits_to_f32(bits), "bf16")
+
+
 def single_layer_case(B, heads, H, W, d, win, shift, K_prev, K_l, dtype, seed, *, sorted_c=False,
-                      dup_keys=False, zero_frac=0.0, no_A=False, i_shared=False):
+                      dup_keys=False, zero_frac=0.0, no_A=False, i_shared=False, implicit=False):
+    """One sparse layer on random candidate lists (implicit: every slot, K_prev = N)
+    and a random previous map, checked against the oracle."""
     shape = (B, heads, H, W, d)
     qt, kt, vt = (inputs.draw(seed + t, shape, dtype) for t in range(3))
-    if dup_keys:   # identical key vectors on every pixel: all scores of a row tie exactly
+    if dup_keys:
+        # identical key vectors on every pixel, and q, k on a 1/8 grid so that every
+        # product and partial sum of q.k is exact in fp32: all scores of a row are
+        # then equal bit for bit whatever the summation order
+        qt = _on_grid(qt)
+        kt = _on_grid(kt)
         kt = inputs.Tensor(np.broadcast_to(kt.device[:, :, :1, :1], shape).copy(),
                            np.broadcast_to(kt.exact[:, :, :1, :1], shape).copy(), dtype)
     N = win * win if win else H * W
@@ -117,21 +133,26 @@ def single_layer_case(B, heads, H, W, d, win, shift, K_prev, K_l, dtype, seed, *
     if sorted_c:
         C = np.sort(C, axis=1)
     C = C.reshape(B, hI, nwin, N, K_prev)
+    if implicit:
+        assert K_prev == N
+        C = None
     a = (g.random((n_wh, N, K_prev)) + 0.05).astype(np.float32)
+    if dup_keys:   # a coarse previous map: many exactly equal weights in a row
+        a = (np.floor(a * 4) / 4 + 0.25).astype(np.float32)
     if zero_frac:
         a[g.random(a.shape) < zero_frac] = 0.0
         a[..., 0] = np.maximum(a[..., 0], 0.5)
     a = a.reshape(B, heads, nwin, N, K_prev)
-    I, A, O = pfa.sparse_layer(to_dev(qt), to_dev(kt), to_dev(vt), torch.from_numpy(C).cuda(),
+    I, A, O = pfa.sparse_layer(to_dev(qt), to_dev(kt), to_dev(vt), None if C is None else torch.from_numpy(C).cuda(),
                                None if no_A else torch.from_numpy(a).cuda(), K_l, win=win, shift=shift,
-                               i_shared=i_shared)
+                               i_shared=i_shared, K_prev=K_prev)
     torch.cuda.synchronize()
     sel = np.arange(n_wh)
     kw = dict(win=win, shift=shift, K_l=K_l, I_prev=C, A_prev=None if no_A else a.astype(np.float64),
               i_shared=i_shared, prev_compact=False, wh_list=sel)
     ref = oracle.layer(qt.exact, kt.exact, vt.exact, want_keys=True, **kw)
-    cand = np.stack([C[n // (heads * nwin), 0 if i_shared else (n // nwin) % heads, n % nwin]
-                     for n in range(n_wh)])
+    cand = None if C is None else np.stack([C[n // (heads * nwin), 0 if i_shared else (n // nwin) % heads, n % nwin]
+                                            for n in range(n_wh)])
     return parity.check_layer(gpu_I=I.view(n_wh, N, K_l).cpu().numpy(), gpu_A=A.view(n_wh, N, K_l).cpu().numpy(),
                               gpu_O=O.cpu().numpy(), ref=ref, cand=cand, wh_list=sel,
                               tol=parity.TOL[dtype], rerun=parity.rerun_fn(qt.exact, kt.exact, vt.exact, **kw))
@@ -161,6 +182,25 @@ def test_exact_ties_lower_index_wins():
     # every score of a row equal and A_prev with repeated values: ties everywhere
     st = single_layer_case(1, 2, 32, 32, 32, 32, 0, 256, 100, "f32", 51, dup_keys=True, zero_frac=0.3)
     assert st["tie_rows"] == 0
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,K_l,no_A", [("f32", 256, False), ("f32", 1000, False), ("f32", 1, True),
+                                            ("f32", 1024, False), ("bf16", 256, False), ("bf16", 100, True)])
+def test_all_candidates_layer_exact_ties(dtype, K_l, no_A):
+    # candidate list = every slot (the layer after the dense one): identical key
+    # vectors make every score of a row equal, so the ranking comes from a coarse
+    # previous map with many equal weights (or, without one, every key ties)
+    st = single_layer_case(1, 2, 32, 32, 32, 32, 16, 1024, K_l, dtype, 53, dup_keys=True, no_A=no_A,
+                           implicit=True)
+    assert st["tie_rows"] == 0
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_all_candidates_layer_random(dtype):
+    # ragged row split: N = 1024 rows over 2 parts of 512, 4-row batches; zeros in the map
+    single_layer_case(1, 3, 32, 64, 32, 32, 16, 1024, 256, dtype, 54, zero_frac=0.2, implicit=True)
 
 
 @pytest.mark.timeout(300)
