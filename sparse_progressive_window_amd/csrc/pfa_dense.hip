@@ -16,7 +16,14 @@
 // which is exactly the A-operand layout of the following P.V MFMA, so the
 // probabilities never leave registers. The contraction index of the score
 // MFMAs is permuted so every lane reads a contiguous run of d/4 elements.
-//   fp32 inputs: v_mfma_f32_16x16x4_f32 (exact products, fp32 accumulation).
+//   fp32 inputs, d = 32, 64-key tiles: the scores use v_mfma_f32_16x16x32_bf16
+//   on a three-way bf16 split of q and k (x = x_hi + x_mid + x_lo, each part the
+//   round-to-nearest bf16 of what is left, so |x - sum| <= 2^-24 |x|); the six
+//   products down to order 2^-16 are accumulated smallest first and the dropped
+//   ones are below 2^-26 of |q||k|: scores as accurate as fp32 products, at 6
+//   bf16 MFMAs instead of 8 fp32 ones per 16x16 tile. K is split once, when its
+//   tile is staged in LDS (three bf16 planes). P.V stays on fp32 MFMA.
+//   fp32 inputs otherwise: v_mfma_f32_16x16x4_f32 (exact products, fp32 accumulation).
 //   bf16 inputs: v_mfma_f32_16x16x16_bf16; P is split into bf16 hi + lo parts
 //   (two MFMAs) so the P.V product keeps ~16 bits of P.
 // Two passes over the keys: (1) running row max / row sum, (2) recompute the
@@ -28,6 +35,36 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+
+// x = hi + mid + lo with each part the round-to-nearest-even bf16 of the
+// remainder (the subtractions are exact in fp32).
+template <int NE, class V>
+__device__ __forceinline__ void split3(const float* x, V& hi, V& mid, V& lo) {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        hi[i] = (__bf16)x[i];
+        const float r = x[i] - (float)hi[i];
+        mid[i] = (__bf16)r;
+        lo[i] = (__bf16)(r - (float)mid[i]);
+    }
+}
+
+// Scores of 16 keys x 16 queries from split operands (d = 32: one MFMA per pair
+// of parts), the small products first.
+__device__ __forceinline__ v4f scores_split3(const bf8& kh, const bf8& km, const bf8& kl, const bf8& qh,
+                                             const bf8& qm, const bf8& ql) {
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(km, qm, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(km, qh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qm, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh, acc, 0, 0, 0);
+    return acc;
+}
+constexpr int kSplitRow = 80;   // bytes per key row in each bf16 K plane (64 + 16 pad)
 
 constexpr int kDenseWaves = 8;
 constexpr int kQPerBlock = 16 * kDenseWaves;
@@ -147,6 +184,32 @@ __device__ __forceinline__ void tile_store(unsigned char* dst,
     }
 }
 
+// K tile of fp32 rows (d = 32) stored as three bf16 planes of KT rows x 80 bytes.
+template <int KT>
+__device__ __forceinline__ void tile_store_split(unsigned char* dst,
+                                                 const uint4 (&reg)[(KT * 128 / 16 + kDenseWaves * kWave - 1) /
+                                                                    (kDenseWaves * kWave)]) {
+    constexpr int CH = 8;
+    constexpr int UNITS = KT * CH;
+    constexpr int PER = (UNITS + kDenseWaves * kWave - 1) / (kDenseWaves * kWave);
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+        const int u = threadIdx.x + x * kDenseWaves * kWave;
+        if (u < UNITS) {
+            const int t = u / CH;
+            const int c = u - t * CH;
+            const float f[4] = {__uint_as_float(reg[x].x), __uint_as_float(reg[x].y), __uint_as_float(reg[x].z),
+                                __uint_as_float(reg[x].w)};
+            bf4 h, m, l;
+            split3<4>(f, h, m, l);
+            unsigned char* row = dst + t * kSplitRow + c * 8;
+            *reinterpret_cast<bf4*>(row) = h;
+            *reinterpret_cast<bf4*>(row + KT * kSplitRow) = m;
+            *reinterpret_cast<bf4*>(row + 2 * KT * kSplitRow) = l;
+        }
+    }
+}
+
 template <typename T, int D, int KT>
 __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const DenseArgs p) {
     using Ops = DenseOps<T, D>;
@@ -155,7 +218,10 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
     constexpr int SUB = KT / 16;                   // 16-key MFMA tiles per LDS tile
     constexpr int CT = D / 16;                     // 16-dim output tiles
     constexpr int PER = (KT * ROWB / 16 + kDenseWaves * kWave - 1) / (kDenseWaves * kWave);
-    __shared__ __align__(16) unsigned char Ks[2][KT * STRIDE];
+    // fp32, d = 32, 64-key tiles: scores from the three-way bf16 split
+    constexpr bool SPLIT = sizeof(T) == 4 && D == 32 && KT == 64;
+    constexpr int KBUF = SPLIT ? 3 * KT * kSplitRow : KT * STRIDE;
+    __shared__ __align__(16) unsigned char Ks[2][KBUF];
     __shared__ __align__(16) unsigned char Vs[2][KT * STRIDE];
 
     const Geom g = p.g;
@@ -191,28 +257,46 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
 
     const int qrow = wave_active ? q0 + r16 : 0;
     const typename Ops::Row qop = Ops::load(Qh + (size_t)slot_pixel(g, wy, wx, qrow) * ROWB, grp);
+    bf8 qh, qm, ql;   // SPLIT: lane's 8 dims of its query in three parts
+    if constexpr (SPLIT) split3<8>(reinterpret_cast<const float*>(&qop), qh, qm, ql);
+    // 16 keys x 16 queries of scores from LDS tile kt, subtile s
+    auto tile_scores = [&](const unsigned char* kt, int s) -> v4f {
+        if constexpr (SPLIT) {
+            const unsigned char* row = kt + (s * 16 + r16) * kSplitRow + grp * 16;
+            const bf8 kh = *reinterpret_cast<const bf8*>(row);
+            const bf8 km = *reinterpret_cast<const bf8*>(row + KT * kSplitRow);
+            const bf8 kl = *reinterpret_cast<const bf8*>(row + 2 * KT * kSplitRow);
+            return scores_split3(kh, km, kl, qh, qm, ql);
+        } else {
+            const typename Ops::Row kop = Ops::load(kt + (s * 16 + r16) * STRIDE, grp);
+            return Ops::scores(kop, qop);
+        }
+    };
+    auto store_k = [&](unsigned char* dst, const uint4 (&reg)[PER]) {
+        if constexpr (SPLIT) tile_store_split<KT>(dst, reg);
+        else tile_store<ROWB, KT, STRIDE>(dst, reg);
+    };
     const int ntiles = N / KT;
     uint4 kreg[PER], vreg[PER];
 
     // pass 1: per-lane running max / sum over the keys 4*grp + r of every 16-key tile
     float m = -INFINITY, l = 0.0f;
     tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, 0);
-    tile_store<ROWB, KT, STRIDE>(Ks[0], kreg);
+    store_k(Ks[0], kreg);
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
         if (t + 1 < ntiles) tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, (t + 1) * KT);
         const unsigned char* kt = Ks[t & 1];
 #pragma unroll
         for (int s = 0; s < SUB; ++s) {
-            const typename Ops::Row kop = Ops::load(kt + (s * 16 + r16) * STRIDE, grp);
-            const v4f acc = Ops::scores(kop, qop);
+            const v4f acc = tile_scores(kt, s);
             const float s0 = acc[0] * sc, s1 = acc[1] * sc, s2 = acc[2] * sc, s3 = acc[3] * sc;
             const float mn = fmaxf(m, fmaxf(fmaxf(s0, s1), fmaxf(s2, s3)));
             l = l * fast_exp2(m - mn) + fast_exp2(s0 - mn) + fast_exp2(s1 - mn) + fast_exp2(s2 - mn) +
                 fast_exp2(s3 - mn);
             m = mn;
         }
-        if (t + 1 < ntiles) tile_store<ROWB, KT, STRIDE>(Ks[(t + 1) & 1], kreg);
+        if (t + 1 < ntiles) store_k(Ks[(t + 1) & 1], kreg);
         __syncthreads();
     }
     // combine the 4 lane groups holding the same query
@@ -233,7 +317,7 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
     float* Arow = (p.A_out && wave_active) ? p.A_out + ((size_t)wh * N + q0 + r16) * N : nullptr;
     tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, 0);
     tile_load<ROWB, KT>(vreg, Vh, g, wy, wx, 0);
-    tile_store<ROWB, KT, STRIDE>(Ks[0], kreg);
+    store_k(Ks[0], kreg);
     tile_store<ROWB, KT, STRIDE>(Vs[0], vreg);
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
@@ -245,8 +329,7 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
         const unsigned char* vt = Vs[t & 1];
 #pragma unroll
         for (int s = 0; s < SUB; ++s) {
-            const typename Ops::Row kop = Ops::load(kt + (s * 16 + r16) * STRIDE, grp);
-            const v4f acc = Ops::scores(kop, qop);
+            const v4f acc = tile_scores(kt, s);
             float pr[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(acc[r] * sc - m) * inv_l;
@@ -259,7 +342,7 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
             for (int c = 0; c < CT; ++c) oacc[c] = Ops::pv(pr, vrow, c * 16 + r16, oacc[c]);
         }
         if (t + 1 < ntiles) {
-            tile_store<ROWB, KT, STRIDE>(Ks[(t + 1) & 1], kreg);
+            store_k(Ks[(t + 1) & 1], kreg);
             tile_store<ROWB, KT, STRIDE>(Vs[(t + 1) & 1], vreg);
         }
         __syncthreads();

@@ -1169,7 +1169,7 @@ hipError_t launch_fn(F fn, const SparseArgs& a, int threads, int lds, int grid, 
 
 template <typename T, int D, int GL, int KPT, int MODE>
 hipError_t launch_one(const SparseArgs& a, int lds, int grid, hipStream_t s) {
-    constexpr int NW = KPT <= 4 ? 16 : 8;
+    constexpr int NW = (KPT <= 4 || (MODE == kKselect && KPT <= 8)) ? 16 : 8;
     constexpr bool PQ = KPT <= 4 && D * sizeof(T) <= 64;   // prefetch q when registers allow
     return launch_fn(sparse_layer_kernel<T, D, GL, KPT, MODE, NW, PQ>, a, NW * kWave, lds, grid, s);
 }
@@ -1187,6 +1187,15 @@ hipError_t launch_mode(const SparseArgs& a, SparseMode mode, int lds, int grid, 
 template <typename T, int D>
 hipError_t launch_shape(const SparseArgs& a, SparseMode mode, int lds, int grid, hipStream_t s) {
     const int kp = a.K_prev;
+    if (mode == kKselect && kp <= 256) {
+        // selection only: 16- and 32-lane row groups (4 or 2 rows per wavefront)
+        // amortise the per-row reductions and scans over more candidates per lane
+        if (kp <= 16) return launch_one<T, D, 16, 1, kKselect>(a, lds, grid, s);
+        if (kp <= 32) return launch_one<T, D, 16, 2, kKselect>(a, lds, grid, s);
+        if (kp <= 64) return launch_one<T, D, 16, 4, kKselect>(a, lds, grid, s);
+        if (kp <= 128) return launch_one<T, D, 16, 8, kKselect>(a, lds, grid, s);
+        return launch_one<T, D, 32, 8, kKselect>(a, lds, grid, s);
+    }
     if (kp <= 16) return launch_mode<T, D, 16, 1>(a, mode, lds, grid, s);
     if (kp <= 32) return launch_mode<T, D, 16, 2>(a, mode, lds, grid, s);
     if (kp <= 64) return launch_mode<T, D, 16, 4>(a, mode, lds, grid, s);
