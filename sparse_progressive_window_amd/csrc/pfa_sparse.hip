@@ -556,7 +556,10 @@ __device__ __forceinline__ void stage_rows(unsigned char* dst, int stride, const
 
 // Generic sparse layer: scores by LDS (or global) gathers of k_j, one group of GL
 // lanes per query row.
-template <typename T, int D, int GL, int KPT, int MODE, int NW, bool PQ>
+// FULL: K_prev == GL*KPT, so every candidate slot of an active row exists (no
+// per-candidate validity), scores stay raw until the exponent; inactive row
+// groups of the last iteration are scored on row0's data and never stored.
+template <typename T, int D, int GL, int KPT, int MODE, int NW, bool PQ, bool FULL>
 __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseArgs p) {
     constexpr int EPC = Chunk<T>::kElems;   // elements per 16-byte chunk
     constexpr int CH = D / EPC;             // chunks per K/V row
@@ -623,12 +626,24 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
         const size_t rowI = p.i_shared ? (size_t)(w.b * w.nwin + w.win_id) * N + i : row;
         const int32_t* Irow = p.I_prev ? p.I_prev + rowI * K_prev + gl : nullptr;
         const float* Arow = p.A_prev ? p.A_prev + row * K_prev + gl : nullptr;
+        if (FULL) {
 #pragma unroll
-        for (int t = 0; t < KPT; ++t) {
-            const int c = gl + GL * t;
-            const bool v = active && c < K_prev;
-            r.j[t] = v ? (Irow ? Irow[GL * t] : c) : 0;
-            r.a[t] = (v && Arow) ? Arow[GL * t] : 1.0f;
+            for (int t = 0; t < KPT; ++t) r.j[t] = Irow ? Irow[GL * t] : gl + GL * t;
+            if (Arow) {
+#pragma unroll
+                for (int t = 0; t < KPT; ++t) r.a[t] = Arow[GL * t];
+            } else {
+#pragma unroll
+                for (int t = 0; t < KPT; ++t) r.a[t] = 1.0f;
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < KPT; ++t) {
+                const int c = gl + GL * t;
+                const bool v = active && c < K_prev;
+                r.j[t] = v ? (Irow ? Irow[GL * t] : c) : 0;
+                r.a[t] = (v && Arow) ? Arow[GL * t] : 1.0f;
+            }
         }
         if (PQ) {
             const unsigned char* qrow =
@@ -652,8 +667,8 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
         bool valid[KPT];
 #pragma unroll
         for (int t = 0; t < KPT; ++t) {
-            valid[t] = active && gl + GL * t < K_prev;
-            jj[t] = min(max(cur.j[t], 0), N - 1);   // memory safety only: indices must lie in [0, N)
+            valid[t] = FULL || (active && gl + GL * t < K_prev);
+            jj[t] = (int)min((unsigned)cur.j[t], (unsigned)(N - 1));   // memory safety only: indices lie in [0, N)
         }
 
         float qf[D];
@@ -681,14 +696,24 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) acc = fmaf(qf[m * EPC + e], kf[e], acc);
             }
-            sv[t] = valid[t] ? acc * p.scale2 : -INFINITY;
+            sv[t] = FULL ? acc : (valid[t] ? acc * p.scale2 : -INFINITY);
         }
-        keys_from_scores<GL, KPT>(cur.a, valid, sv);
+        if (FULL) {
+            // u = A^{l-1} exp2(scale2 (s - max s)); fmaxf maps invalid previous weights to 0
+            float smax = sv[0];
+#pragma unroll
+            for (int t = 1; t < KPT; ++t) smax = fmaxf(smax, sv[t]);
+            const float c = -Grp<GL>::all(smax, MaxF()) * p.scale2;
+#pragma unroll
+            for (int t = 0; t < KPT; ++t) sv[t] = fmaxf(cur.a[t] * fast_exp2(fmaf(sv[t], p.scale2, c)), 0.0f);
+        } else {
+            keys_from_scores<GL, KPT>(cur.a, valid, sv);
+        }
         if constexpr (VS == kVnone) {
             const size_t rbase = ((size_t)w.wh * N + base) * p.K_l;
             const int nbytes = max(0, min(RPW, row1 - base)) * p.K_l * 4;
             select_store<GL, KPT, BPL, false>(
-                p, lane, active, N, [&](int t) { return jj[t]; }, [&](int t) { return valid[t]; }, sv, hb,
+                p, lane, active, N, [&](int t) { return jj[t]; }, [&](int t) { return FULL || valid[t]; }, sv, hb,
                 make_rsrc(p.I_out + rbase, nbytes), make_rsrc(p.A_out + rbase, nbytes), grp * p.K_l);
         } else {
             select_emit<T, D, GL, KPT, VS, BPL>(p, g, lane, active, row, qpix, w.wy, w.wx, jj, valid, sv, hb, scr,
@@ -1098,7 +1123,7 @@ __global__ __launch_bounds__(NW * kWave) void aggregate_rows_kernel(const Sparse
     const size_t plane = (size_t)w.bh * g.H * g.W * D;
     const T* Vh = static_cast<const T*>(p.V) + plane;
     float* Oh = p.O_out + plane;
-    int* sj = reinterpret_cast<int*>(smem + N * ROWB) + wave * 512;   // 256 indices, then 256 weights
+    int* sj = reinterpret_cast<int*>(smem + N * ROWB) + wave * 512;   // 256 V-row offsets, then 256 weights
     float* sw = reinterpret_cast<float*>(sj + 256);
     stage_rows<T, D>(smem, ROWB, Vh, g, w.wy, w.wx);
     __syncthreads();
@@ -1119,8 +1144,12 @@ __global__ __launch_bounds__(NW * kWave) void aggregate_rows_kernel(const Sparse
     };
     int base = row0 + wave * R;
     if (base < row1) load(base);
+    const unsigned char* vbase = smem + vchunk * 16;   // this lane's 16-byte chunk of every V row
     for (; base < row1; base += NW * R) {
-        *reinterpret_cast<int4*>(sj + lane * 4) = jn;
+        // stage byte offsets of the V rows (slot clamped to the window: memory safety only)
+        const int4 off = make_int4(min(max(jn.x, 0), N - 1) * ROWB, min(max(jn.y, 0), N - 1) * ROWB,
+                                   min(max(jn.z, 0), N - 1) * ROWB, min(max(jn.w, 0), N - 1) * ROWB);
+        *reinterpret_cast<int4*>(sj + lane * 4) = off;
         *reinterpret_cast<float4*>(sw + lane * 4) = wn;
         if (base + NW * R < row1) load(base + NW * R);
         const int i = base + grp;
@@ -1131,16 +1160,14 @@ __global__ __launch_bounds__(NW * kWave) void aggregate_rows_kernel(const Sparse
             const int* rj = sj + grp * K_l;
             const float* rw = sw + grp * K_l;
             for (int e = vsub * 4; e < K_l; e += GS * 4) {
-                const int4 j4 = *reinterpret_cast<const int4*>(rj + e);
+                const int4 o4 = *reinterpret_cast<const int4*>(rj + e);
                 const float4 w4 = *reinterpret_cast<const float4*>(rw + e);
-                const int jv[4] = {j4.x, j4.y, j4.z, j4.w};
+                const int ov[4] = {o4.x, o4.y, o4.z, o4.w};
                 const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
                 float vf[4][EPC];
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int j = min(max(jv[x], 0), N - 1);
-                    Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(smem + j * ROWB + vchunk * 16), vf[x]);
-                }
+                for (int x = 0; x < 4; ++x)
+                    Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(vbase + ov[x]), vf[x]);
 #pragma unroll
                 for (int x = 0; x < 4; ++x)
 #pragma unroll
@@ -1171,7 +1198,9 @@ template <typename T, int D, int GL, int KPT, int MODE>
 hipError_t launch_one(const SparseArgs& a, int lds, int grid, hipStream_t s) {
     constexpr int NW = (KPT <= 4 || (MODE == kKselect && KPT <= 8)) ? 16 : 8;
     constexpr bool PQ = KPT <= 4 && D * sizeof(T) <= 64;   // prefetch q when registers allow
-    return launch_fn(sparse_layer_kernel<T, D, GL, KPT, MODE, NW, PQ>, a, NW * kWave, lds, grid, s);
+    if (MODE == kKselect && a.K_prev == GL * KPT)
+        return launch_fn(sparse_layer_kernel<T, D, GL, KPT, MODE, NW, PQ, true>, a, NW * kWave, lds, grid, s);
+    return launch_fn(sparse_layer_kernel<T, D, GL, KPT, MODE, NW, PQ, false>, a, NW * kWave, lds, grid, s);
 }
 
 template <typename T, int D, int GL, int KPT>

@@ -168,6 +168,12 @@ EDGE = [
     (1, 3, 32, 32, 16, 32, 5, 300, 150, "bf16"),  # d = 16 bf16
     (1, 3, 32, 32, 16, 32, 31, 64, 64, "f32"),    # K_l = K_prev, max shift
     (1, 1, 24, 24, 32, 12, 6, 144, 20, "f32"),    # window side not a power of two
+    # fp32, N = 1024 (K and V do not fit LDS together: selection + aggregation kernels)
+    (1, 2, 32, 32, 32, 32, 16, 200, 77, "f32"),   # ragged K_prev, 32-lane rows
+    (1, 2, 32, 32, 32, 32, 0, 100, 50, "f32"),    # ragged K_prev, 16-lane rows
+    (1, 1, 32, 32, 32, 32, 5, 20, 7, "f32"),      # ragged small K_prev
+    (1, 2, 32, 32, 32, 32, 16, 256, 128, "f32"),  # rows filled exactly (as in the chain)
+    (1, 2, 32, 32, 32, 32, 16, 512, 200, "f32"),  # 64-lane rows
 ]
 
 
