@@ -149,7 +149,9 @@ int32_t pfa_timing_count(void);
  * PFA_ERR_HIP if an event query fails. */
 int pfa_timing_read(int32_t* kinds, float* ms, int32_t cap, int32_t* n_out, int32_t* dropped);
 
-/* Kernel symbol name (prefix, as profilers show it) of a pfa_kernel_kind; never NULL. */
+/* Family name of a pfa_kernel_kind: profilers show the family's kernel symbols
+ * beginning with it ("sparse_layer_kernel(select)" names the selection-only
+ * instantiations of sparse_layer_kernel); "unknown" for other values. Never NULL. */
 const char* pfa_kernel_name(int32_t kind);
 
 #ifdef __cplusplus

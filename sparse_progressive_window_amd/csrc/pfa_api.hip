@@ -243,10 +243,10 @@ int pfa_timing_read(int32_t* kinds, float* ms, int32_t cap, int32_t* n_out, int3
 const char* pfa_kernel_name(int32_t kind) {
     switch (kind) {
         case PFA_KERNEL_DENSE: return "dense_layer_kernel";
-        case PFA_KERNEL_ALL_CANDIDATES: return "all_cand_kernel";
+        case PFA_KERNEL_ALL_CANDIDATES: return "all_cand";
         case PFA_KERNEL_SPARSE: return "sparse_layer_kernel";
         case PFA_KERNEL_SELECT: return "sparse_layer_kernel(select)";
-        case PFA_KERNEL_AGGREGATE: return "aggregate_kernel";
+        case PFA_KERNEL_AGGREGATE: return "aggregate";
         case PFA_KERNEL_IOTA: return "iota_rows_kernel";
         default: return "unknown";
     }

@@ -48,8 +48,8 @@ def test_timing_calls_without_device(lib):
     assert lib.pfa_timing_read(None, None, 4, ctypes.byref(n), None) == -1
     assert lib.pfa_timing_read(None, None, -1, ctypes.byref(n), None) == -1
     names = [lib.pfa_kernel_name(k).decode() for k in range(6)]
-    assert names == ["dense_layer_kernel", "all_cand_kernel", "sparse_layer_kernel",
-                     "sparse_layer_kernel(select)", "aggregate_kernel", "iota_rows_kernel"]
+    assert names == ["dense_layer_kernel", "all_cand", "sparse_layer_kernel",
+                     "sparse_layer_kernel(select)", "aggregate", "iota_rows_kernel"]
     assert lib.pfa_kernel_name(99) == b"unknown"
 
 

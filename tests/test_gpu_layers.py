@@ -297,8 +297,8 @@ def test_kernel_timing_records():
     kinds = [k for k, _ in recs]
     names = [pfa.kernel_name(k) for k in kinds]
     assert n1 == 2 and dropped == 0
-    assert names[:3] == ["dense_layer_kernel", "iota_rows_kernel", "all_cand_kernel"], names
-    assert names[-1] == "aggregate_kernel", names
+    assert names[:3] == ["dense_layer_kernel", "iota_rows_kernel", "all_cand"], names
+    assert names[-1] == "aggregate", names
     assert all(ms > 0 for _, ms in recs)
     # results with timing on equal those with timing off
     _, A2b, O2b = pfa.sparse_layer(Qd, Kd, Vd, None, A1, 256, win=32, shift=16)
