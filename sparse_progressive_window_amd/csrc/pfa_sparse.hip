@@ -102,6 +102,11 @@ struct Grp {
         if (GL == 64) x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
         return x;
     }
+    // lanes of this lane's group as a wave mask
+    __device__ static uint64_t group_mask(int lane) {
+        if (GL == 64) return ~0ull;
+        return (GL == 32 ? 0xFFFFFFFFull : 0xFFFFull) << (lane & (64 - GL));
+    }
     // bits of the wave mask m that belong to this lane's group
     __device__ static uint32_t bits(uint64_t m, int lane) {
         if (GL == 64) return 0;  // unused
@@ -457,41 +462,46 @@ __device__ __forceinline__ void select_store(const SparseArgs& p, int lane, bool
         jcut = tie_cut<GL, KPT>(key, jf, tau, need_tau, n_tau, active, N, lane, unused);
     }
 
+    // kept = key > thr, plus (ties) some keys equal to tau: thr = tau - 1 keeps every
+    // key equal to tau; on an ORDERED tie row thr = tau and the tied keys are added
+    // by rank below (they all weigh u_tau)
+    const int thr = (ORDERED && tie) ? tau : tau - 1;
     float ksum = 0.0f;
-    if (!any_tie) {
-#pragma unroll
-        for (int t = 0; t < KPT; ++t) ksum += key(t) >= tau ? uv[t] : 0.0f;
-    } else if (ORDERED) {
-        // the need_tau kept keys equal to tau all weigh the same
-#pragma unroll
-        for (int t = 0; t < KPT; ++t) ksum += (tie ? key(t) > tau : key(t) >= tau) ? uv[t] : 0.0f;
-    } else {
+    if (!ORDERED && any_tie) {
 #pragma unroll
         for (int t = 0; t < KPT; ++t) ksum += (key(t) > tau || (key(t) == tau && jf(t) <= jcut)) ? uv[t] : 0.0f;
+    } else {
+#pragma unroll
+        for (int t = 0; t < KPT; ++t) ksum += key(t) > thr ? uv[t] : 0.0f;
     }
     ksum = G::all(ksum, SumF());
     if (ORDERED && tie) ksum += (float)need_tau * __int_as_float(tau);
     const float inv = 1.0f / ksum;
 
-    // the store loop compares with a copy of tau the compiler cannot see through,
-    // so it does not keep KPT comparison masks alive from the sums above
-    int tau2 = tau;
-    __asm__ volatile("" : "+v"(tau2));
+    // Store loop. Positions: group-masked ballots counted with mbcnt, the running
+    // group count folded into the accumulator. Entries not to be stored (not kept,
+    // rows past the end, positions past K_l on precondition violations) get an
+    // offset past the buffer resource's range, which the hardware drops. The loop
+    // compares with copies of thr/tau the compiler cannot see through, so it does
+    // not keep KPT comparison masks alive from the sums above.
+    int thr2 = thr, tau2 = tau;
+    __asm__ volatile("" : "+v"(thr2), "+v"(tau2));
+    const uint64_t gmask = G::group_mask(lane);
+    const uint32_t gm_lo = (uint32_t)gmask, gm_hi = (uint32_t)(gmask >> 32);
     int obase = 0;
     int tbase = 0;   // ORDERED ties: keys equal to tau met so far in the group
     auto emit = [&](int t, bool k) {
         const uint64_t m = ballot(k);
-        const int pos = obase + G::below(m, lane);
-        if (active && k && pos < K_l) {   // pos >= K_l only on precondition violations
-            const int off = (row_off + pos) * 4;
-            __builtin_amdgcn_raw_buffer_store_b32(jf(t), rI, off, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(uv[t] * inv), rA, off, 0, 0);
-        }
-        obase += G::count_mask(m, lane);
+        const uint32_t ml = (uint32_t)m & gm_lo, mh = (uint32_t)(m >> 32) & gm_hi;
+        const int pos = (int)__builtin_amdgcn_mbcnt_hi(mh, __builtin_amdgcn_mbcnt_lo(ml, (uint32_t)obase));
+        const int off = (k && pos < K_l) ? (row_off + pos) * 4 : 0x7FFFFFF0;
+        __builtin_amdgcn_raw_buffer_store_b32(jf(t), rI, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(uv[t] * inv), rA, off, 0, 0);
+        obase += __builtin_popcount(ml) + __builtin_popcount(mh);
     };
     if (!any_tie) {
 #pragma unroll
-        for (int t = 0; t < KPT; ++t) emit(t, key(t) >= tau2);
+        for (int t = 0; t < KPT; ++t) emit(t, key(t) > thr2);
     } else if (ORDERED) {
 #pragma unroll
         for (int t = 0; t < KPT; ++t) {
@@ -499,7 +509,7 @@ __device__ __forceinline__ void select_store(const SparseArgs& p, int lane, bool
             const uint64_t me = ballot(eq);
             const int rank = tbase + G::below(me, lane);
             tbase += G::count_mask(me, lane);
-            emit(t, tie ? key(t) > tau2 || (eq && rank < need_tau) : key(t) >= tau2);
+            emit(t, key(t) > thr2 || (eq && rank < need_tau));
         }
     } else {
 #pragma unroll
