@@ -203,10 +203,11 @@ def test_all_candidates_layer_exact_ties(dtype, K_l, no_A):
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_all_candidates_layer_random(dtype):
-    # ragged row split: N = 1024 rows over 2 parts of 512, 4-row batches; zeros in the map
-    single_layer_case(1, 3, 32, 64, 32, 32, 16, 1024, 256, dtype, 54, zero_frac=0.2, implicit=True)
+@pytest.mark.parametrize("dtype,d", [("f32", 32), ("bf16", 32), ("f32", 16), ("bf16", 16)])
+def test_all_candidates_layer_random(dtype, d):
+    # N = 1024 rows over 2 parts of 512, 4-row batches; zeros in the map; d = 16
+    # takes the padded (unswizzled) K layout
+    single_layer_case(1, 3, 32, 64, d, 32, 16, 1024, 256, dtype, 54 + d, zero_frac=0.2, implicit=True)
 
 
 @pytest.mark.timeout(300)
@@ -222,7 +223,8 @@ def test_shared_index_window_mode_and_global_unshared():
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("dtype,d,win", [("f32", 32, 32), ("bf16", 32, 32), ("f32", 16, 16), ("bf16", 16, 8)])
+@pytest.mark.parametrize("dtype,d,win", [("f32", 32, 32), ("bf16", 32, 32), ("f32", 16, 16), ("bf16", 16, 8),
+                                         ("f32", 32, 12), ("f32", 32, 8)])
 def test_dense_layer_variants(dtype, d, win):
     B, heads, H, W = 1, 2, 2 * win, 3 * win
     shape = (B, heads, H, W, d)
