@@ -220,7 +220,7 @@ def main():
 
     value = total_pairs / (ms_per_step * 1e-3)
     result = {
-        "metric": "PFA candidate-pairs/sec per layer (32x32 win, d=32); % HBM/MFMA roofline",
+        "metric": "PFA candidate-pairs/sec per layer (32\u00d732 win, d=32); % HBM/MFMA roofline",
         "value": value, "unit": "candidate pairs/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
