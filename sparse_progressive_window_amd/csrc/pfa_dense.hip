@@ -210,7 +210,7 @@ __device__ __forceinline__ void tile_store_split(unsigned char* dst,
     }
 }
 
-template <typename T, int D, int KT>
+template <typename T, int D, int KT, bool WA>
 __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const DenseArgs p) {
     using Ops = DenseOps<T, D>;
     constexpr int ROWB = Ops::ROWB;
@@ -287,15 +287,24 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
     for (int t = 0; t < ntiles; ++t) {
         if (t + 1 < ntiles) tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, (t + 1) * KT);
         const unsigned char* kt = Ks[t & 1];
+        // the whole tile's scores, then one rescale of the running sum (m is in
+        // scaled base-2 units; sc > 0, so the raw maximum gives the scaled one)
+        v4f acc[SUB];
 #pragma unroll
-        for (int s = 0; s < SUB; ++s) {
-            const v4f acc = tile_scores(kt, s);
-            const float s0 = acc[0] * sc, s1 = acc[1] * sc, s2 = acc[2] * sc, s3 = acc[3] * sc;
-            const float mn = fmaxf(m, fmaxf(fmaxf(s0, s1), fmaxf(s2, s3)));
-            l = l * fast_exp2(m - mn) + fast_exp2(s0 - mn) + fast_exp2(s1 - mn) + fast_exp2(s2 - mn) +
-                fast_exp2(s3 - mn);
-            m = mn;
-        }
+        for (int s = 0; s < SUB; ++s) acc[s] = tile_scores(kt, s);
+        float amax = acc[0][0];
+#pragma unroll
+        for (int s = 0; s < SUB; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) amax = fmaxf(amax, acc[s][r]);
+        const float mn = fmaxf(m, amax * sc);
+        float lt = 0.0f;
+#pragma unroll
+        for (int s = 0; s < SUB; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) lt += fast_exp2(fmaf(acc[s][r], sc, -mn));
+        l = l * fast_exp2(m - mn) + lt;
+        m = mn;
         if (t + 1 < ntiles) store_k(Ks[(t + 1) & 1], kreg);
         __syncthreads();
     }
@@ -314,7 +323,11 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
     v4f oacc[CT];
 #pragma unroll
     for (int c = 0; c < CT; ++c) oacc[c] = v4f{0.f, 0.f, 0.f, 0.f};
-    float* Arow = (p.A_out && wave_active) ? p.A_out + ((size_t)wh * N + q0 + r16) * N : nullptr;
+    // A^1 rows of the wave's 16 queries through a buffer resource (an empty range
+    // for an idle wave, so its stores are dropped)
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc(WA ? p.A_out + ((size_t)wh * N + (wave_active ? q0 : 0)) * N : nullptr,
+                  (WA && wave_active) ? 16 * N * 4 : 0);
     tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, 0);
     tile_load<ROWB, KT>(vreg, Vh, g, wy, wx, 0);
     store_k(Ks[0], kreg);
@@ -332,9 +345,13 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
             const v4f acc = tile_scores(kt, s);
             float pr[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(acc[r] * sc - m) * inv_l;
-            if (Arow)
-                *reinterpret_cast<float4*>(Arow + t * KT + s * 16 + 4 * grp) = make_float4(pr[0], pr[1], pr[2], pr[3]);
+            for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(fmaf(acc[r], sc, -m)) * inv_l;
+            if (WA) {
+                typedef int v4i __attribute__((ext_vector_type(4)));
+                const v4i pv = {__float_as_int(pr[0]), __float_as_int(pr[1]), __float_as_int(pr[2]),
+                                __float_as_int(pr[3])};
+                __builtin_amdgcn_raw_buffer_store_b128(pv, rA, (r16 * N + t * KT + s * 16 + 4 * grp) * 4, 0, 0);
+            }
             const unsigned char* vrow[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) vrow[r] = vt + (s * 16 + 4 * grp + r) * STRIDE;
@@ -363,12 +380,18 @@ __global__ void iota_rows_kernel(int32_t* I, int64_t total, int N) {
         I[x] = (int32_t)(x % N);
 }
 
+template <typename T, int D, bool WA>
+void launch_dense_w(const DenseArgs& a, int grid, hipStream_t s) {
+    if (a.g.N % 64 == 0)
+        hipLaunchKernelGGL((dense_layer_kernel<T, D, 64, WA>), dim3(grid), dim3(kDenseWaves * kWave), 0, s, a);
+    else
+        hipLaunchKernelGGL((dense_layer_kernel<T, D, 16, WA>), dim3(grid), dim3(kDenseWaves * kWave), 0, s, a);
+}
+
 template <typename T, int D>
 void launch_dense_t(const DenseArgs& a, int grid, hipStream_t s) {
-    if (a.g.N % 64 == 0)
-        hipLaunchKernelGGL((dense_layer_kernel<T, D, 64>), dim3(grid), dim3(kDenseWaves * kWave), 0, s, a);
-    else
-        hipLaunchKernelGGL((dense_layer_kernel<T, D, 16>), dim3(grid), dim3(kDenseWaves * kWave), 0, s, a);
+    if (a.A_out) launch_dense_w<T, D, true>(a, grid, s);
+    else launch_dense_w<T, D, false>(a, grid, s);
 }
 
 }  // namespace

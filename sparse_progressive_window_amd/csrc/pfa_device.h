@@ -72,4 +72,10 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Buffer resource over `bytes` bytes at `base` (raw, 32-bit elements); accesses
+// past the end are dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
 }  // namespace pfa

@@ -517,11 +517,6 @@ __device__ __forceinline__ void select_store(const SparseArgs& p, int lane, bool
     }
 }
 
-// Buffer resource over `bytes` bytes at `base` (raw, 32-bit elements); accesses
-// past the end are dropped by the hardware.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
 
 struct WhPart {
     int wh, part, wy, wx, b, bh, win_id, nwin;
