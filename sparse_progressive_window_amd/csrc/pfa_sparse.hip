@@ -190,11 +190,15 @@ __device__ __forceinline__ void keys_from_scores(const float (&av)[KPT], const b
 // descends into that bin. Each level removes log2(NB) bits from the interval, so
 // it ends after at most 8 levels (usually 2 or 3). Result: every key > tau is
 // kept, need_tau more are needed among the n_tau keys equal to tau.
-template <int GL, int BPL, int KPT, class KF>
+// RES0: the level's result (bin, count above, count in bin) is passed through
+// words 0..2 of the histogram itself (their counts have been read by then)
+// instead of three words past its end.
+template <int GL, int BPL, int KPT, bool RES0 = false, class KF>
 __device__ __forceinline__ void radix_threshold(KF key, int kmin, int kmax, bool active, int K_prev, int K_l,
                                                 unsigned* hb, int gl, int& tau, int& need_tau, int& n_tau) {
     using G = Grp<GL>;
     constexpr int NB = BPL * GL;
+    constexpr int RES = RES0 ? 0 : NB;
     constexpr int LOG2NB = G::kLog2 + (BPL == 8 ? 3 : BPL == 4 ? 2 : BPL == 2 ? 1 : 0);
     static_assert(BPL == 1 || BPL == 2 || BPL == 4 || BPL == 8, "bins per lane");
     int lo = kmin, hi = kmax + 1, need = K_l;
@@ -249,16 +253,16 @@ __device__ __forceinline__ void radix_threshold(KF key, int kmin, int kmax, bool
 #pragma unroll
         for (int b = 0; b < BPL; ++b) {
             if (!done && run < (unsigned)need && run + cb[b] >= (unsigned)need) {   // exactly one bin per group
-                hb[NB] = (unsigned)(NB - 1 - BPL * gl - b);
-                hb[NB + 1] = run;
-                hb[NB + 2] = cb[b];
+                hb[RES] = (unsigned)(NB - 1 - BPL * gl - b);
+                hb[RES + 1] = run;
+                hb[RES + 2] = cb[b];
             }
             run += cb[b];
         }
         __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        const int bin = (int)hb[NB];
-        const int above = (int)hb[NB + 1];
-        const int in_bin = (int)hb[NB + 2];
+        const int bin = (int)hb[RES];
+        const int above = (int)hb[RES + 1];
+        const int in_bin = (int)hb[RES + 2];
         __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (!done) {
             need -= above;
@@ -430,7 +434,7 @@ __device__ __forceinline__ void select_emit(const SparseArgs& p, const Geom& g, 
 // ORDERED: jf is increasing in (t, lane) order, so exact ties at the threshold
 // are resolved by rank in that order (the lowest slots first) within the store
 // loop; otherwise by bisection on j.
-template <int GL, int KPT, int BPL, bool ORDERED, class JF, class VF>
+template <int GL, int KPT, int BPL, bool ORDERED, bool RES0 = false, class JF, class VF>
 __device__ __forceinline__ void select_store(const SparseArgs& p, int lane, bool active, int N, JF jf, VF vf,
                                              const float (&uv)[KPT], unsigned* hb, __amdgpu_buffer_rsrc_t rI,
                                              __amdgpu_buffer_rsrc_t rA, int row_off) {
@@ -452,7 +456,7 @@ __device__ __forceinline__ void select_store(const SparseArgs& p, int lane, bool
     kmax = G::all_i(kmax, MaxI());
 
     int tau, need_tau, n_tau;
-    radix_threshold<GL, BPL, KPT>(key, kmin, kmax, active, K_prev, K_l, hb, gl, tau, need_tau, n_tau);
+    radix_threshold<GL, BPL, KPT, RES0>(key, kmin, kmax, active, K_prev, K_l, hb, gl, tau, need_tau, n_tau);
     // tie: more keys equal tau (the interval shrank to one key value) than are needed
     const bool tie = active && n_tau > need_tau;
     const bool any_tie = ballot(tie) != 0;
@@ -897,8 +901,8 @@ __device__ __forceinline__ int kswz(int r) { return (r ^ (r >> 3)) & 7; }
 // gives each 16-lane quarter one query row: lane 16g + b holds row g's candidates
 // 16k + b, k = 0..63, so the 4 rows are selected together, one per 16-lane group.
 template <typename T, int D, bool HAS_A>
-__global__ __launch_bounds__(8 * kWave) void all_cand_rows_kernel(const SparseArgs p) {
-    constexpr int NW = 8;
+__global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseArgs p) {
+    constexpr int NW = 16;
     constexpr int GL = 16;
     constexpr int KPT = 64;
     constexpr int BPL = 8;                   // 128 radix bins per row
@@ -908,7 +912,7 @@ __global__ __launch_bounds__(8 * kWave) void all_cand_rows_kernel(const SparseAr
     constexpr bool SWZ = CH == 8;            // 128-byte rows: chunk-swizzled, unpadded
     constexpr int KSTR = SWZ ? ROWB : ROWB + 16;
     constexpr int KK = Mfma4<T>::kK;
-    constexpr int HISTG = BPL * GL + 4;
+    constexpr int HISTG = BPL * GL;       // the level results reuse words 0..2
     extern __shared__ __align__(16) unsigned char smem[];
 
     const Geom g = p.g;
@@ -939,87 +943,84 @@ __global__ __launch_bounds__(8 * kWave) void all_cand_rows_kernel(const SparseAr
     const int row0 = w.part * p.rows_per_block;
     const int row1 = min(N, row0 + p.rows_per_block);
     const int K_l = p.K_l;
-    const int swl = SWZ ? kswz(lane) : 0;   // B-operand rows 64t + lane all share this permutation
     const float scale2 = p.scale2;
 
-    // A^{l-1} of the batch in the transposed layout: lane (g, b) holds row base+g,
-    // slots 16k + b; the next batch is loaded while this one is selected
-    float ab[KPT];
-    auto load_batch = [&](int b0) {
-        const int i = min(b0 + grp, N - 1);
-        if (HAS_A) {
-            const float* arow = p.A_prev + ((size_t)w.wh * N + i) * N + gl;
-#pragma unroll
-            for (int k = 0; k < KPT; ++k) ab[k] = arow[GL * k];
-        }
-    };
-    load_batch(row0 + wave * 4);
+    // A^{l-1} of the batch in the transposed layout: lane (g, b) needs row base+g,
+    // slots 16k + b
+    constexpr int AH = KPT / 2;   // loaded and consumed in two halves (register budget)
     for (int base = row0 + wave * 4; base < row1; base += NW * 4) {
-        const int qi = min(base + (lane & 3), row1 - 1);
-        float qf[D];
+        // per-lane values are re-derived every batch from an opaque copy of the lane
+        // index: hoisted out of the loop, the KPT slot indices and the LDS addresses
+        // would not fit the register budget of 4 waves per SIMD
+        int lv = lane;
+        __asm__ volatile("" : "+v"(lv));
+        const int glv = lv & (GL - 1);
+        const int qi = min(base + (lv & 3), row1 - 1);
         const unsigned char* qrow =
             reinterpret_cast<const unsigned char*>(Qh + (size_t)slot_pixel(g, w.wy, w.wx, qi) * D);
+        // 16 accumulator chains (one per 64-candidate tile), contraction chunk outer:
+        // one 16-byte chunk of the query is live at a time
+        v4f acc[16];
 #pragma unroll
-        for (int m = 0; m < CH; ++m) Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(qrow + 16 * m), &qf[m * EPC]);
-
-        float uv[KPT];   // raw scores q.k, then the keys
+        for (int t = 0; t < 16; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+        const unsigned char* kr0 = Ks + lv * KSTR;
 #pragma unroll
-        for (int t = 0; t < 16; t += 4) {   // 4 independent accumulator chains
-            v4f acc[4];
-            const unsigned char* kr[4];
+        for (int m = 0; m < CH; ++m) {
+            float qv[EPC];
+            Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(qrow + 16 * m), qv);
+            const int koff = (SWZ ? (m ^ kswz(lv)) : m) * 16;
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                acc[x] = v4f{0.f, 0.f, 0.f, 0.f};
-                kr[x] = Ks + (kWave * (t + x) + lane) * KSTR;
-            }
+            for (int t = 0; t < 16; ++t) {
+                float kf[EPC];
+                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(kr0 + kWave * t * KSTR + koff), kf);
 #pragma unroll
-            for (int m = 0; m < CH; ++m) {
-                float kf[4][EPC];
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(kr[x] + (SWZ ? (m ^ swl) : m) * 16), kf[x]);
-#pragma unroll
-                for (int e = 0; e < EPC; e += KK)
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) acc[x] = Mfma4<T>::run(&qf[m * EPC + e], &kf[x][e], acc[x]);
-            }
-            // acc[x][r] = s(row r, candidate 64(t+x) + lane): transpose (lane quarter, r)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const auto p02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[x][0]),
-                                                                  __float_as_uint(acc[x][2]), false, false);
-                const auto p13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[x][1]),
-                                                                  __float_as_uint(acc[x][3]), false, false);
-                const auto q01 = __builtin_amdgcn_permlane16_swap(p02[0], p13[0], false, false);
-                const auto q23 = __builtin_amdgcn_permlane16_swap(p02[1], p13[1], false, false);
-                uv[4 * (t + x) + 0] = __uint_as_float(q01[0]);   // candidate 64(t+x) + 16q + gl of row grp
-                uv[4 * (t + x) + 1] = __uint_as_float(q01[1]);
-                uv[4 * (t + x) + 2] = __uint_as_float(q23[0]);
-                uv[4 * (t + x) + 3] = __uint_as_float(q23[1]);
+                for (int e = 0; e < EPC; e += KK) acc[t] = Mfma4<T>::run(&qv[e], &kf[e], acc[t]);
             }
         }
-        // keys u = A^{l-1} exp2(scale2 (s - max s)), then the next batch's loads
+        float uv[KPT];   // raw scores q.k, then the keys
+        // acc[t][r] = s(row r, candidate 64t + lane): transpose (lane quarter, r)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const auto p02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[t][0]),
+                                                              __float_as_uint(acc[t][2]), false, false);
+            const auto p13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[t][1]),
+                                                              __float_as_uint(acc[t][3]), false, false);
+            const auto q01 = __builtin_amdgcn_permlane16_swap(p02[0], p13[0], false, false);
+            const auto q23 = __builtin_amdgcn_permlane16_swap(p02[1], p13[1], false, false);
+            uv[4 * t + 0] = __uint_as_float(q01[0]);   // candidate 64t + 16q + gl of row grp
+            uv[4 * t + 1] = __uint_as_float(q01[1]);
+            uv[4 * t + 2] = __uint_as_float(q23[0]);
+            uv[4 * t + 3] = __uint_as_float(q23[1]);
+        }
+        // keys u = A^{l-1} exp2(scale2 (s - max s)); A^{l-1} is loaded now, half a
+        // batch at a time (16 waves per CU cover the load latency)
         float smax = uv[0];
 #pragma unroll
         for (int k = 1; k < KPT; ++k) smax = fmaxf(smax, uv[k]);
         const float c = -Grp<GL>::all(smax, MaxF()) * scale2;
+        const float* arow = HAS_A ? p.A_prev + ((size_t)w.wh * N + min(base + grp, N - 1)) * N + glv : nullptr;
 #pragma unroll
-        for (int k = 0; k < KPT; ++k) {
-            const float e = fast_exp2(fmaf(uv[k], scale2, c));
-            uv[k] = HAS_A ? fmaxf(ab[k] * e, 0.0f) : e;
+        for (int h = 0; h < KPT; h += AH) {
+            float ab[AH];
+            if (HAS_A) {
+#pragma unroll
+                for (int k = 0; k < AH; ++k) ab[k] = arow[GL * (h + k)];
+            }
+#pragma unroll
+            for (int k = 0; k < AH; ++k) {
+                const float e = fast_exp2(fmaf(uv[h + k], scale2, c));
+                uv[h + k] = HAS_A ? fmaxf(ab[k] * e, 0.0f) : e;
+            }
+            __asm__ volatile("" ::: "memory");   // the second half's loads go out after the first is used
         }
-        // the next batch's loads go out only once this batch's weights are consumed
-        // (keeps two batches of A^{l-1} from being live at once)
-        __asm__ volatile("" ::: "memory");
-        if (base + NW * 4 < row1) load_batch(base + NW * 4);
 
         // rows past row1 (last batch) are selected but never stored: every group's
         // ballots and reductions are its own
         const bool active = base + grp < row1;
         const size_t rbase = ((size_t)w.wh * N + base) * K_l;
         const int nbytes = max(0, min(4, row1 - base)) * K_l * 4;
-        select_store<GL, KPT, BPL, true>(
-            p, lane, active, N, [&](int k) { return GL * k + gl; }, [&](int) { return true; }, uv, hb,
+        select_store<GL, KPT, BPL, true, true>(
+            p, lane, active, N, [&](int k) { return GL * k + glv; }, [&](int) { return true; }, uv, hb,
             make_rsrc(p.I_out + rbase, nbytes), make_rsrc(p.A_out + rbase, nbytes), grp * K_l);
     }
 }
@@ -1246,9 +1247,9 @@ hipError_t launch_all_cand_t(const SparseArgs& a, bool with_av, int grid, hipStr
     if (with_av)
         return launch_fn(all_cand_kernel<T, D, kVlds>, a, 8 * kWave, lds_k + 1024 * ROWB + kScratchBytes / 2, grid, s);
     constexpr int KSTR = ROWB == 128 ? ROWB : ROWB + 16;
-    const int lds = 1024 * KSTR + 8 * 4 * (8 * 16 + 4) * 4;
-    if (a.A_prev) return launch_fn(all_cand_rows_kernel<T, D, true>, a, 8 * kWave, lds, grid, s);
-    return launch_fn(all_cand_rows_kernel<T, D, false>, a, 8 * kWave, lds, grid, s);
+    const int lds = 1024 * KSTR + 16 * 4 * (8 * 16) * 4;
+    if (a.A_prev) return launch_fn(all_cand_rows_kernel<T, D, true>, a, 16 * kWave, lds, grid, s);
+    return launch_fn(all_cand_rows_kernel<T, D, false>, a, 16 * kWave, lds, grid, s);
 }
 
 template <typename T, int D>
