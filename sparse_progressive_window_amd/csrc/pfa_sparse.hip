@@ -636,15 +636,9 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
         const int32_t* Irow = p.I_prev ? p.I_prev + rowI * K_prev + gl : nullptr;
         const float* Arow = p.A_prev ? p.A_prev + row * K_prev + gl : nullptr;
         if (FULL) {
+            // the weights of a FULL row are loaded after its scores (late_a)
 #pragma unroll
             for (int t = 0; t < KPT; ++t) r.j[t] = Irow ? Irow[GL * t] : gl + GL * t;
-            if (Arow) {
-#pragma unroll
-                for (int t = 0; t < KPT; ++t) r.a[t] = Arow[GL * t];
-            } else {
-#pragma unroll
-                for (int t = 0; t < KPT; ++t) r.a[t] = 1.0f;
-            }
         } else {
 #pragma unroll
             for (int t = 0; t < KPT; ++t) {
@@ -708,13 +702,24 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
             sv[t] = FULL ? acc : (valid[t] ? acc * p.scale2 : -INFINITY);
         }
         if (FULL) {
-            // u = A^{l-1} exp2(scale2 (s - max s)); fmaxf maps invalid previous weights to 0
+            // u = A^{l-1} exp2(scale2 (s - max s)); fmaxf maps invalid previous weights to 0.
+            // A^{l-1} is loaded only now: no prefetched weights occupy registers
+            // during the scoring (the other waves of the SIMD cover the latency)
             float smax = sv[0];
 #pragma unroll
             for (int t = 1; t < KPT; ++t) smax = fmaxf(smax, sv[t]);
             const float c = -Grp<GL>::all(smax, MaxF()) * p.scale2;
+            const float* Arow = p.A_prev ? p.A_prev + row * K_prev + gl : nullptr;
+            float a[KPT];
+            if (Arow) {
 #pragma unroll
-            for (int t = 0; t < KPT; ++t) sv[t] = fmaxf(cur.a[t] * fast_exp2(fmaf(sv[t], p.scale2, c)), 0.0f);
+                for (int t = 0; t < KPT; ++t) a[t] = Arow[GL * t];
+            } else {
+#pragma unroll
+                for (int t = 0; t < KPT; ++t) a[t] = 1.0f;
+            }
+#pragma unroll
+            for (int t = 0; t < KPT; ++t) sv[t] = fmaxf(a[t] * fast_exp2(fmaf(sv[t], p.scale2, c)), 0.0f);
         } else {
             keys_from_scores<GL, KPT>(cur.a, valid, sv);
         }
