@@ -125,9 +125,9 @@ int pfa_version(void);
 typedef enum {
     PFA_KERNEL_DENSE = 0,          /* dense first layer, all N candidates, MFMA */
     PFA_KERNEL_ALL_CANDIDATES = 1, /* sparse layer whose candidate list is every slot (MFMA scores) */
-    PFA_KERNEL_SPARSE = 2,         /* sparse layer, selection and aggregation in one kernel */
-    PFA_KERNEL_SELECT = 3,         /* sparse layer, selection only (I^l, A^l) */
-    PFA_KERNEL_AGGREGATE = 4,      /* O from stored (I^l, A^l) rows */
+    PFA_KERNEL_SPARSE = 2,         /* global mode: selection and aggregation in one kernel */
+    PFA_KERNEL_SELECT = 3,         /* window mode: selection only (I^l, A^l) */
+    PFA_KERNEL_AGGREGATE = 4,      /* window mode: O from the stored (I^l, A^l) rows */
     PFA_KERNEL_IOTA = 5            /* I rows 0..N-1 of the dense layer */
 } pfa_kernel_kind;
 

@@ -120,27 +120,21 @@ int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const voi
     const int64_t grid64 = n_wh(g) * a.blocks_per_wh;
     if (grid64 > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
     const int grid = (int)grid64;
+    // Window mode: a selection kernel writes I^l / A^l (K of the window staged in
+    // LDS), then the aggregation kernel forms O with V staged in LDS. Measured
+    // faster than one kernel doing both, also where K and V fit in LDS together
+    // (bf16): each kernel then runs with more waves and the selection with more
+    // radix bins.
     hipError_t e;
-    bool aggregate = false;
     if (!I_prev && K_prev == 1024 && g.N == 1024) {
         // every slot is a candidate: MFMA scores
-        const bool with_v = pfa::all_cand_fits_with_v(dtype, g.d);
-        e = timed(PFA_KERNEL_ALL_CANDIDATES, stream,
-                  [&] { return pfa::launch_all_cand(a, dtype, g.d, with_v, grid, stream); });
-        aggregate = !with_v;
-    } else if (2 * g.N * rowb + pfa::kScratchBytes <= pfa::kLdsBytes) {
-        e = timed(PFA_KERNEL_SPARSE, stream, [&] {
-            return pfa::launch_sparse(a, dtype, g.d, pfa::kKVinLDS, 2 * g.N * rowb + pfa::kScratchBytes, grid,
-                                      stream);
-        });
+        e = timed(PFA_KERNEL_ALL_CANDIDATES, stream, [&] { return pfa::launch_all_cand(a, dtype, g.d, grid, stream); });
     } else {
-        // K and V do not fit in LDS together: select with K in LDS, then aggregate with V in LDS
         e = timed(PFA_KERNEL_SELECT, stream, [&] {
             return pfa::launch_sparse(a, dtype, g.d, pfa::kKselect, g.N * rowb + pfa::kScratchBytes, grid, stream);
         });
-        aggregate = true;
     }
-    if (e == hipSuccess && aggregate)
+    if (e == hipSuccess)
         e = timed(PFA_KERNEL_AGGREGATE, stream, [&] { return pfa::launch_aggregate(a, dtype, g.d, grid, stream); });
     return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
 }

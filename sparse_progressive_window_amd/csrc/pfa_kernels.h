@@ -28,11 +28,10 @@ struct SparseArgs {
     float scale2;            // log2(e) / sqrt(d): scores are kept in base-2 units
 };
 
-// Where K and V rows are read from.
-// kKVinLDS: K and V staged in LDS; kKinLDS: K in LDS, V read from global memory;
-// kKVglobal: both from global memory (global mode); kKselect: K in LDS, no
-// aggregation (O comes from launch_aggregate).
-enum SparseMode { kKVinLDS = 0, kKinLDS = 1, kKVglobal = 2, kKselect = 3 };
+// kKselect: window mode, K staged in LDS, selection only (O comes from
+// launch_aggregate); kKVglobal: global mode, K and V read from global memory,
+// selection and aggregation in one kernel.
+enum SparseMode { kKVglobal = 0, kKselect = 1 };
 
 struct DenseArgs {
     const void* Q;
@@ -47,9 +46,8 @@ struct DenseArgs {
 
 hipError_t launch_sparse(const SparseArgs& a, int dtype, int D, SparseMode mode, int lds_bytes, int grid,
                          hipStream_t stream);
-// All-candidates layer (I^{l-1} implicit, K_prev = N = 1024): MFMA scores.
-bool all_cand_fits_with_v(int dtype, int D);
-hipError_t launch_all_cand(const SparseArgs& a, int dtype, int D, bool with_av, int grid, hipStream_t stream);
+// All-candidates layer (I^{l-1} implicit, K_prev = N = 1024): MFMA scores, selection only.
+hipError_t launch_all_cand(const SparseArgs& a, int dtype, int D, int grid, hipStream_t stream);
 // O from stored (I^l, A^l) rows with V in LDS (window mode).
 hipError_t launch_aggregate(const SparseArgs& a, int dtype, int D, int grid, hipStream_t stream);
 int dense_query_blocks(int N);   // workgroups per window-head of the dense layer

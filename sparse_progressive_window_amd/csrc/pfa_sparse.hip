@@ -155,6 +155,14 @@ struct Chunk<uint16_t> {  // bf16 bit patterns
 // sum the lanes of a group that own the same chunk (lane bits [log2 CH, log2 GL))
 template <int CH, int GL>
 __device__ __forceinline__ float reduce_chunk_lanes(float v) {
+    if (GL <= 8) {
+        // groups narrower than a 16-lane DPP row: xor exchanges stay inside the group
+        // (a row rotate would pull lanes of the neighbouring group)
+        if (CH <= 1 && GL >= 2) v += dppf<kQuadXor1>(v);
+        if (CH <= 2 && GL >= 4) v += dppf<kQuadXor2>(v);
+        if (CH <= 4 && GL >= 8) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));  // xor 4
+        return v;
+    }
     if (CH <= 2) v += dppf<kRowRor2>(v);
     if (CH <= 4 && GL >= 8) v += dppf<kRowRor4>(v);
     if (CH <= 8 && GL >= 16) v += dppf<kRowRor8>(v);
@@ -163,8 +171,9 @@ __device__ __forceinline__ float reduce_chunk_lanes(float v) {
     return v;
 }
 
-// Where a row's V vectors come from in the aggregation.
-enum VSrc { kVlds = 0, kVwin = 1, kVraster = 2, kVnone = 3 };
+// Where a row's V vectors come from in a fused aggregation (global mode: the
+// raster rows of the map), or none.
+enum VSrc { kVraster = 0, kVnone = 1 };
 
 // u = A^{l-1} exp(s - m) for one query row held by a group of GL lanes, in place
 // over the base-2 scores sv (m = the row maximum). fmaxf maps NaN and negative
@@ -315,9 +324,9 @@ __device__ __forceinline__ int tie_cut(KF key, JF jf, int tau, int need_tau, int
 // c = gl + GL*t; uv = A^{l-1} exp(s - m) >= 0.
 template <typename T, int D, int GL, int KPT, int VS, int BPL>
 __device__ __forceinline__ void select_emit(const SparseArgs& p, const Geom& g, int lane, bool active, size_t row,
-                                            int qpix, int wy, int wx, const int (&jj)[KPT], const bool (&valid)[KPT],
+                                            int qpix, const int (&jj)[KPT], const bool (&valid)[KPT],
                                             const float (&uv_in)[KPT], unsigned* hb, uint2* scr, int scg,
-                                            const unsigned char* Vs, const T* Vh, float* Oh) {
+                                            const T* Vh, float* Oh) {
     constexpr int EPC = Chunk<T>::kElems;
     constexpr int CH = D / EPC;
     constexpr int ROWB = D * (int)sizeof(T);
@@ -398,14 +407,7 @@ __device__ __forceinline__ void select_emit(const SparseArgs& p, const Geom& g, 
             for (int e = vsub; e < cnt; e += GS) {
                 const uint2 ent = scr[e];
                 const float w = __uint_as_float(ent.y);
-                const unsigned char* vrow;
-                if (VS == kVlds) {
-                    vrow = Vs + ent.x * ROWB;
-                } else if (VS == kVwin) {
-                    vrow = reinterpret_cast<const unsigned char*>(Vh + (size_t)slot_pixel(g, wy, wx, (int)ent.x) * D);
-                } else {
-                    vrow = reinterpret_cast<const unsigned char*>(Vh + (size_t)ent.x * D);
-                }
+                const unsigned char* vrow = reinterpret_cast<const unsigned char*>(Vh + (size_t)ent.x * D);
                 float vf[EPC];
                 Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(vrow + vchunk * 16), vf);
 #pragma unroll
@@ -574,9 +576,8 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
     constexpr int CH = D / EPC;             // chunks per K/V row
     constexpr int ROWB = D * (int)sizeof(T);
     constexpr int RPW = kWave / GL;         // rows per wavefront iteration
-    constexpr bool K_LDS = MODE != kKVglobal;
-    constexpr bool V_LDS = MODE == kKVinLDS;
-    constexpr int VS = MODE == kKVinLDS ? kVlds : MODE == kKinLDS ? kVwin : MODE == kKVglobal ? kVraster : kVnone;
+    constexpr bool K_LDS = MODE == kKselect;
+    constexpr int VS = MODE == kKVglobal ? kVraster : kVnone;
     constexpr int BPL = VS == kVnone ? 4 : 1;        // radix bins per lane (no (j, weight) staging: more bins)
     constexpr int HISTG = BPL * GL + 4;              // histogram words per row group
     constexpr int HISTW = RPW * HISTG;               // radix-select histogram words per wave
@@ -600,14 +601,12 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
     float* Oh = p.O_out + plane;
 
     unsigned char* Ks = smem;
-    unsigned char* Vs = smem + (K_LDS ? N * ROWB : 0);
-    unsigned char* sbase = smem + (K_LDS ? N * ROWB : 0) + (V_LDS ? N * ROWB : 0);
+    unsigned char* sbase = smem + (K_LDS ? N * ROWB : 0);
     unsigned* hb = reinterpret_cast<unsigned*>(sbase) + wave * HISTW + grp * HISTG;
     uint2* scr = reinterpret_cast<uint2*>(sbase + HIST_BYTES) + wave * SCW + grp * SCG;
 
     if (K_LDS) {
         stage_rows<T, D>(Ks, ROWB, Kh, g, w.wy, w.wx);
-        if (V_LDS) stage_rows<T, D>(Vs, ROWB, Vh, g, w.wy, w.wx);
         __syncthreads();
     }
 
@@ -730,8 +729,8 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
                 p, lane, active, N, [&](int t) { return jj[t]; }, [&](int t) { return FULL || valid[t]; }, sv, hb,
                 make_rsrc(p.I_out + rbase, nbytes), make_rsrc(p.A_out + rbase, nbytes), grp * p.K_l);
         } else {
-            select_emit<T, D, GL, KPT, VS, BPL>(p, g, lane, active, row, qpix, w.wy, w.wx, jj, valid, sv, hb, scr,
-                                                SCG, Vs, Vh, Oh);
+            select_emit<T, D, GL, KPT, VS, BPL>(p, g, lane, active, row, qpix, jj, valid, sv, hb, scr, SCG, Vh,
+                                                Oh);
         }
         cur = nxt;
     }
@@ -764,133 +763,6 @@ struct Mfma4<uint16_t> {
         return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(x, y, c, 0, 0, 0);
     }
 };
-
-// Layer whose candidate list is every slot of a 32x32 window (I^{l-1} implicit,
-// K_prev = N = 1024), e.g. the second layer after the dense one. Scores for 4
-// query rows x 64 candidates come from 4x4 MFMA blocks: A = the 4 query rows
-// (replicated over the blocks), B = the 64 candidate rows read from LDS, so
-// accumulator register r of lane l holds s(row r, candidate 64c + l), the
-// lane-strided layout the row finishing expects. K rows are staged with a
-// 16-byte pad so that 8 consecutive rows start in 8 different bank groups.
-template <typename T, int D, int VS>
-__global__ __launch_bounds__(8 * kWave) void all_cand_kernel(const SparseArgs p) {
-    constexpr int NW = 8;
-    constexpr int KPT = 16;
-    constexpr int GL = 64;
-    constexpr int EPC = Chunk<T>::kElems;
-    constexpr int CH = D / EPC;
-    constexpr int ROWB = D * (int)sizeof(T);
-    constexpr int KSTR = ROWB + 16;
-    constexpr int KK = Mfma4<T>::kK;
-    constexpr int BPL = VS == kVnone ? 4 : 1;
-    constexpr int HISTW = BPL * GL + 4;
-    constexpr int HIST_BYTES = NW * HISTW * 4;
-    static_assert(HIST_BYTES <= kScratchBytes / 2, "histograms exceed the scratch area");
-    constexpr int SCW = VS == kVnone ? 0 : (kScratchBytes / 2 - HIST_BYTES) / (NW * 8);
-    extern __shared__ __align__(16) unsigned char smem[];
-
-    const Geom g = p.g;
-    const int N = g.N;   // 1024
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const WhPart w = decode_block(p.blocks_per_wh, p.xcd_map, g);
-    const size_t plane = (size_t)w.bh * g.H * g.W * D;
-    const T* Qh = static_cast<const T*>(p.Q) + plane;
-    const T* Kh = static_cast<const T*>(p.K) + plane;
-    const T* Vh = static_cast<const T*>(p.V) + plane;
-    float* Oh = p.O_out + plane;
-
-    unsigned char* Ks = smem;
-    unsigned char* Vs = smem + N * KSTR;
-    unsigned char* sbase = Vs + (VS == kVlds ? N * ROWB : 0);
-    unsigned* hb = reinterpret_cast<unsigned*>(sbase) + wave * HISTW;
-    uint2* scr = reinterpret_cast<uint2*>(sbase + HIST_BYTES) + wave * SCW;
-    stage_rows<T, D>(Ks, KSTR, Kh, g, w.wy, w.wx);
-    if (VS == kVlds) stage_rows<T, D>(Vs, ROWB, Vh, g, w.wy, w.wx);
-    __syncthreads();
-
-    const int row0 = w.part * p.rows_per_block;
-    const int row1 = min(N, row0 + p.rows_per_block);
-    int jj[KPT];
-    bool valid[KPT];
-#pragma unroll
-    for (int t = 0; t < KPT; ++t) {
-        jj[t] = lane + kWave * t;
-        valid[t] = true;
-    }
-
-    // A^{l-1} rows of the wavefront's current 4-row batch; the next batch's rows are
-    // loaded as soon as these have been folded into the keys, so ~16 KB per wave
-    // stay in flight while the batch is selected (the LDS-resident K limits the CU
-    // to 8 waves, so memory-level parallelism has to come from each wave).
-    float ab[4][KPT];
-    auto load_batch = [&](int b0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = min(b0 + r, N - 1);
-            const float* arow = p.A_prev ? p.A_prev + ((size_t)w.wh * N + i) * N + lane : nullptr;
-#pragma unroll
-            for (int t = 0; t < KPT; ++t) ab[r][t] = arow ? arow[kWave * t] : 1.0f;
-        }
-    };
-    load_batch(row0 + wave * 4);
-    for (int base = row0 + wave * 4; base < row1; base += NW * 4) {
-        // A operand: query row base + lane%4 (rows past row1 compute garbage, never stored)
-        const int qi = min(base + (lane & 3), row1 - 1);
-        float qf[D];
-        const unsigned char* qrow =
-            reinterpret_cast<const unsigned char*>(Qh + (size_t)slot_pixel(g, w.wy, w.wx, qi) * D);
-#pragma unroll
-        for (int m = 0; m < CH; ++m) Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(qrow + 16 * m), &qf[m * EPC]);
-
-        float s4[4][KPT];
-#pragma unroll
-        for (int t = 0; t < KPT; t += 4) {   // 4 independent accumulator chains
-            v4f acc[4];
-            const unsigned char* kr[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                acc[x] = v4f{0.f, 0.f, 0.f, 0.f};
-                kr[x] = Ks + (kWave * (t + x) + lane) * KSTR;
-            }
-#pragma unroll
-            for (int m = 0; m < CH; ++m) {
-                float kf[4][EPC];
-#pragma unroll
-                for (int x = 0; x < 4; ++x) Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(kr[x] + 16 * m), kf[x]);
-#pragma unroll
-                for (int e = 0; e < EPC; e += KK)
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) acc[x] = Mfma4<T>::run(&qf[m * EPC + e], &kf[x][e], acc[x]);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int x = 0; x < 4; ++x) s4[r][t + x] = acc[x][r] * p.scale2;
-        }
-        // keys of the 4 rows (in place), then start the next batch's loads
-#pragma unroll
-        for (int r = 0; r < 4; ++r) keys_from_scores<GL, KPT>(ab[r], valid, s4[r]);
-        if (base + NW * 4 < row1) load_batch(base + NW * 4);
-
-#pragma unroll 1
-        for (int r = 0; r < 4; ++r) {
-            const int i = base + r;
-            const bool active = i < row1;
-            const int ii = active ? i : row0;
-            const size_t row = (size_t)w.wh * N + ii;
-            float uv[KPT];
-#pragma unroll
-            for (int t = 0; t < KPT; ++t) {
-                valid[t] = active;
-                // register select (r is a loop variable: indexing s4[r] would spill to scratch)
-                uv[t] = r == 0 ? s4[0][t] : r == 1 ? s4[1][t] : r == 2 ? s4[2][t] : s4[3][t];
-            }
-            select_emit<T, D, GL, KPT, VS, BPL>(p, g, lane, active, row, slot_pixel(g, w.wy, w.wx, ii), w.wy, w.wx,
-                                                jj, valid, uv, hb, scr, SCW, Vs, Vh, Oh);
-        }
-    }
-}
 
 // Chunk permutation of the LDS-resident K rows of the all-candidates kernel
 // (128-byte rows, no pad): chunk c of row r is stored at position c ^ kswz(r),
@@ -1217,8 +1089,6 @@ hipError_t launch_one(const SparseArgs& a, int lds, int grid, hipStream_t s) {
 template <typename T, int D, int GL, int KPT>
 hipError_t launch_mode(const SparseArgs& a, SparseMode mode, int lds, int grid, hipStream_t s) {
     switch (mode) {
-        case kKVinLDS: return launch_one<T, D, GL, KPT, kKVinLDS>(a, lds, grid, s);
-        case kKinLDS: return launch_one<T, D, GL, KPT, kKinLDS>(a, lds, grid, s);
         case kKselect: return launch_one<T, D, GL, KPT, kKselect>(a, lds, grid, s);
         default: return launch_one<T, D, GL, KPT, kKVglobal>(a, lds, grid, s);
     }
@@ -1246,11 +1116,8 @@ hipError_t launch_shape(const SparseArgs& a, SparseMode mode, int lds, int grid,
 }
 
 template <typename T, int D>
-hipError_t launch_all_cand_t(const SparseArgs& a, bool with_av, int grid, hipStream_t s) {
+hipError_t launch_all_cand_t(const SparseArgs& a, int grid, hipStream_t s) {
     constexpr int ROWB = D * (int)sizeof(T);
-    const int lds_k = 1024 * (ROWB + 16);
-    if (with_av)
-        return launch_fn(all_cand_kernel<T, D, kVlds>, a, 8 * kWave, lds_k + 1024 * ROWB + kScratchBytes / 2, grid, s);
     constexpr int KSTR = ROWB == 128 ? ROWB : ROWB + 16;
     const int lds = 1024 * KSTR + 16 * 4 * (8 * 16) * 4;
     if (a.A_prev) return launch_fn(all_cand_rows_kernel<T, D, true>, a, 16 * kWave, lds, grid, s);
@@ -1287,17 +1154,12 @@ hipError_t launch_sparse(const SparseArgs& a, int dtype, int D, SparseMode mode,
                    : launch_shape<uint16_t, 32>(a, mode, lds_bytes, grid, stream);
 }
 
-bool all_cand_fits_with_v(int dtype, int D) {
-    const int rowb = D * (dtype == 0 ? 4 : 2);
-    return 1024 * (rowb + 16) + 1024 * rowb + kScratchBytes / 2 <= kLdsBytes;
-}
-
-hipError_t launch_all_cand(const SparseArgs& a, int dtype, int D, bool with_av, int grid, hipStream_t stream) {
+hipError_t launch_all_cand(const SparseArgs& a, int dtype, int D, int grid, hipStream_t stream) {
     if (dtype == 0)
-        return D == 16 ? launch_all_cand_t<float, 16>(a, with_av, grid, stream)
-                       : launch_all_cand_t<float, 32>(a, with_av, grid, stream);
-    return D == 16 ? launch_all_cand_t<uint16_t, 16>(a, with_av, grid, stream)
-                   : launch_all_cand_t<uint16_t, 32>(a, with_av, grid, stream);
+        return D == 16 ? launch_all_cand_t<float, 16>(a, grid, stream)
+                       : launch_all_cand_t<float, 32>(a, grid, stream);
+    return D == 16 ? launch_all_cand_t<uint16_t, 16>(a, grid, stream)
+                   : launch_all_cand_t<uint16_t, 32>(a, grid, stream);
 }
 
 hipError_t launch_aggregate(const SparseArgs& a, int dtype, int D, int grid, hipStream_t stream) {
