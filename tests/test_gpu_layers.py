@@ -203,11 +203,13 @@ def test_all_candidates_layer_exact_ties(dtype, K_l, no_A):
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("dtype,d", [("f32", 32), ("bf16", 32), ("f32", 16), ("bf16", 16)])
-def test_all_candidates_layer_random(dtype, d):
+@pytest.mark.parametrize("dtype,d,K_l", [("f32", 32, 256), ("bf16", 32, 256), ("f32", 16, 256), ("bf16", 16, 256),
+                                         ("f32", 16, 32), ("bf16", 16, 32), ("bf16", 32, 32), ("f32", 32, 12)])
+def test_all_candidates_layer_random(dtype, d, K_l):
     # N = 1024 rows over 2 parts of 512, 4-row batches; zeros in the map; d = 16
-    # takes the padded (unswizzled) K layout
-    single_layer_case(1, 3, 32, 64, d, 32, 16, 1024, 256, dtype, 54 + d, zero_frac=0.2, implicit=True)
+    # takes the padded (unswizzled) K layout; small K_l puts 8 or 16 rows in one
+    # aggregation step (groups of 8 or 4 lanes, narrower than a DPP row)
+    single_layer_case(1, 3, 32, 64, d, 32, 16, 1024, K_l, dtype, 54 + d + K_l, zero_frac=0.2, implicit=True)
 
 
 @pytest.mark.timeout(300)
