@@ -76,16 +76,19 @@ typedef struct {
  *                  written: O-only mode);
  *           I_out  [B, heads, nwin, N, N] int32 or NULL (row i is 0..N-1);
  *           O_out  required. Needs win to be a multiple of 4.
+ *           lse_out [B, heads, nwin, N] fp32 or NULL: ln sum_j exp(q_i.k_j/sqrt(d)),
+ *                  the log of row i's softmax denominator (what O-only callers
+ *                  keep instead of the map: A_ij = exp(s_ij - lse_i)).
  * K1 <  N:  the K1 largest weights are kept and renormalised (as in a sparse
  *           layer whose previous map is all ones); I_out and A_out
- *           [.., N, K1] are required.
+ *           [.., N, K1] are required; lse_out must be NULL.
  * Errors: PFA_ERR_INVALID for K1 outside [1, N], NULL Q/K/V/O, NULL I_out or
  * A_out when K1 < N, H or W not a multiple of win, shift outside [0, win);
  * PFA_ERR_UNSUPPORTED for win == 0, win > 32, win not a multiple of 4 when
- * K1 == N, d not 16/32, unknown dtype.
+ * K1 == N, d not 16/32, unknown dtype, lse_out with K1 < N.
  */
 int pfa_dense_layer(const pfa_shape* shape, const void* Q, const void* K, const void* V,
-                    int32_t K1, int32_t* I_out, float* A_out, float* O_out, void* stream);
+                    int32_t K1, int32_t* I_out, float* A_out, float* lse_out, float* O_out, void* stream);
 
 /*
  * Sparse layer l > 1 ("Sparse matrix multiplication": scores only where

@@ -5,7 +5,8 @@ CPU-baseline leg of ``bench.py`` may use it; the HIP library never does.
 
 ``layer`` computes one PFA layer (steps listed in ``pfa_oracle.c``) for a list of
 window-heads; ``chain`` runs the layers of one chain for a list of window-heads,
-feeding each layer's (I, A) to the next, all in fp64.
+feeding each layer's (I, A) to the next, all in fp64. ``dense_lse`` gives the
+first layer's log softmax denominators.
 """
 
 import ctypes
@@ -122,3 +123,31 @@ def chain(layers_qkv, *, win, shifts, Ks, wh_list=None):
         outs.append(r)
         I_prev, A_prev = r["I"], r["A"]
     return outs
+
+
+def dense_lse(Q, K, *, win, shift, wh_list=None):
+    """ln sum_j exp(q_i . k_j / sqrt(d)) over the N slots of each window, per query
+    slot i: the denominator of the first layer's full softmax map (paper notes,
+    "Progressive focused resource allocation strategy": the first layer computes
+    the complete map), i.e. A^1_ij = exp(s_ij - lse_i). Slot t of window (a, b)
+    reads pixel ((a*win + t//win + shift) mod H, (b*win + t%win + shift) mod W).
+    Returns [n_wh, N] fp64 in window-head order (b, head, window row, window col)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    B, heads, H, W, d = Q.shape
+    N = win * win
+    nwy, nwx = H // win, W // win
+    n_all = B * heads * nwy * nwx
+    wl = np.arange(n_all) if wh_list is None else np.asarray(wh_list)
+    t = np.arange(N)
+    out = np.empty((len(wl), N), dtype=np.float64)
+    for n, wh in enumerate(wl):
+        b, rest = divmod(int(wh), heads * nwy * nwx)
+        h, win_id = divmod(rest, nwy * nwx)
+        wy, wx = divmod(win_id, nwx)
+        y = (wy * win + t // win + shift) % H
+        x = (wx * win + t % win + shift) % W
+        s = Q[b, h, y, x] @ K[b, h, y, x].T / np.sqrt(d)
+        m = s.max(axis=1, keepdims=True)
+        out[n] = (m + np.log(np.exp(s - m).sum(axis=1, keepdims=True)))[:, 0]
+    return out

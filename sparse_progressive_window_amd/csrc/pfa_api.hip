@@ -159,7 +159,7 @@ int pfa_sparse_layer(const pfa_shape* shape, const void* Q, const void* K, const
 }
 
 int pfa_dense_layer(const pfa_shape* shape, const void* Q, const void* K, const void* V, int32_t K1,
-                    int32_t* I_out, float* A_out, float* O_out, void* stream) {
+                    int32_t* I_out, float* A_out, float* lse_out, float* O_out, void* stream) {
     Geom g;
     int code;
     if (!geom_from_shape(shape, &g, &code)) return code;
@@ -169,13 +169,14 @@ int pfa_dense_layer(const pfa_shape* shape, const void* Q, const void* K, const 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (K1 < g.N) {
         if (!I_out || !A_out) return PFA_ERR_INVALID;
+        if (lse_out) return PFA_ERR_UNSUPPORTED;
         return run_sparse(g, shape->dtype, Q, K, V, nullptr, 0, nullptr, g.N, K1, I_out, A_out,
                           O_out, s);
     }
     if (g.win % 4) return PFA_ERR_UNSUPPORTED;
     pfa::DenseArgs a;
     a.Q = Q; a.K = K; a.V = V;
-    a.A_out = A_out; a.O_out = O_out;
+    a.A_out = A_out; a.lse_out = lse_out; a.O_out = O_out;
     a.g = g;
     a.scale2 = (float)(1.4426950408889634 / sqrt((double)g.d));
     a.xcd_map = (n_wh(g) % 8 == 0) ? 1 : 0;

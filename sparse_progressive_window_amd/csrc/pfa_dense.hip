@@ -318,6 +318,9 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
         m = mn;
     }
     const float inv_l = 1.0f / l;
+    // ln of the softmax denominator: sum_j exp(s_ij) = 2^m * l with s in natural units
+    if (p.lse_out && wave_active && grp == 0 && q0 + r16 < N)
+        p.lse_out[(size_t)wh * N + q0 + r16] = (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
 
     // pass 2: probabilities, A^1 rows, O += P V
     v4f oacc[CT];

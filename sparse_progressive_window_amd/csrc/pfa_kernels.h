@@ -38,6 +38,7 @@ struct DenseArgs {
     const void* K;
     const void* V;
     float* A_out;            // nullptr: O-only
+    float* lse_out;          // nullptr: no log-normaliser output
     float* O_out;
     Geom g;
     float scale2;

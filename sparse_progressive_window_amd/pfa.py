@@ -37,7 +37,7 @@ def load():
                                "`python -m sparse_progressive_window_amd.build`")
         lib = ctypes.CDLL(_LIB_PATH)
         P, i32 = ctypes.c_void_p, ctypes.c_int32
-        lib.pfa_dense_layer.argtypes = [ctypes.POINTER(PfaShape), P, P, P, i32, P, P, P, P]
+        lib.pfa_dense_layer.argtypes = [ctypes.POINTER(PfaShape), P, P, P, i32, P, P, P, P, P]
         lib.pfa_dense_layer.restype = ctypes.c_int
         lib.pfa_sparse_layer.argtypes = [ctypes.POINTER(PfaShape), P, P, P, P, i32, P, i32, i32, P, P, P, P]
         lib.pfa_sparse_layer.restype = ctypes.c_int
@@ -111,10 +111,11 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def dense_layer(Q, K, V, K1=None, *, win, shift=0, want_A=True, want_I=False, out=None):
+def dense_layer(Q, K, V, K1=None, *, win, shift=0, want_A=True, want_I=False, out=None, lse_out=None):
     """First (dense) layer. Returns (I, A, O); I and A are None when not requested
     (K1 == N) and always returned when K1 < N. ``out`` = optional preallocated
-    (I or None, A or None, O)."""
+    (I or None, A or None, O). ``lse_out``: optional [B, heads, nwin, N] fp32
+    tensor filled with each row's log softmax denominator (K1 == N only)."""
     _check_qkv(Q, K, V)
     lead, N = _geometry(Q, win)
     K1 = N if K1 is None else K1
@@ -131,9 +132,10 @@ def dense_layer(Q, K, V, K1=None, *, win, shift=0, want_A=True, want_I=False, ou
     _expect(I, rows * K1, torch.int32, "I_out")
     _expect(A, rows * K1, torch.float32, "A_out")
     _expect(O, Q.numel(), torch.float32, "O_out")
+    _expect(lse_out, rows, torch.float32, "lse_out")
     shape = make_shape(Q, win, shift)
     rc = load().pfa_dense_layer(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), K1, _ptr(I), _ptr(A),
-                                _ptr(O), _stream())
+                                _ptr(lse_out), _ptr(O), _stream())
     if rc != 0:
         raise PfaError("pfa_dense_layer", rc)
     return I, A, O

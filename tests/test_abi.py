@@ -71,8 +71,9 @@ def sparse(lib, s, K_prev=64, K_l=16, I_prev=FAKE, outs=(FAKE, FAKE, FAKE)):
                                 FAKE, K_prev, K_l, *outs, None)
 
 
-def dense(lib, s, K1=1024, I=None, A=None, O=FAKE):
-    return lib.pfa_dense_layer(ctypes.byref(s) if s is not None else None, FAKE, FAKE, FAKE, K1, I, A, O, None)
+def dense(lib, s, K1=1024, I=None, A=None, O=FAKE, lse=None):
+    return lib.pfa_dense_layer(ctypes.byref(s) if s is not None else None, FAKE, FAKE, FAKE, K1, I, A, lse, O,
+                               None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -105,6 +106,7 @@ def test_dense_validation(lib):
     assert dense(lib, shape(), K1=1025) == -1
     assert dense(lib, shape(), O=None) == -1
     assert dense(lib, shape(), K1=100) == -1                       # K1 < N needs I and A
+    assert dense(lib, shape(), K1=100, I=FAKE, A=FAKE, lse=FAKE) == -2   # no log-normaliser when K1 < N
     assert dense(lib, shape(), K1=100, I=FAKE) == -1
     assert dense(lib, shape(win=6, H=12, W=12), K1=36) == -2       # K1 == N needs win % 4 == 0
 

@@ -244,10 +244,16 @@ def test_dense_layer_variants(dtype, d, win):
                            gpu_O=O.cpu().numpy(), ref=ref, cand=None, wh_list=sel, tol=parity.TOL[dtype],
                            rerun=parity.rerun_fn(qt.exact, kt.exact, vt.exact, I_prev=None, A_prev=None,
                                                  i_shared=False, prev_compact=False, **kw))
-    # O-only mode gives the same O
-    _, A0, O0 = pfa.dense_layer(to_dev(qt), to_dev(kt), to_dev(vt), N, win=win, shift=0, want_A=False)
-    _, A1, O1 = pfa.dense_layer(to_dev(qt), to_dev(kt), to_dev(vt), N, win=win, shift=0, want_A=True)
+    # O-only mode gives the same O, and the log softmax denominators match the
+    # oracle's (absolute error in the log domain = relative error of the denominator)
+    lse = torch.empty((n_wh, N), dtype=torch.float32, device="cuda")
+    _, A0, O0 = pfa.dense_layer(to_dev(qt), to_dev(kt), to_dev(vt), N, win=win, shift=win // 2, want_A=False,
+                                lse_out=lse)
+    _, A1, O1 = pfa.dense_layer(to_dev(qt), to_dev(kt), to_dev(vt), N, win=win, shift=win // 2, want_A=True)
     assert A0 is None and torch.equal(O0, O1)
+    lse_ref = oracle.dense_lse(qt.exact, kt.exact, win=win, shift=win // 2)
+    err = np.abs(lse.cpu().numpy().astype(np.float64) - lse_ref)
+    assert err.max() <= parity.TOL[dtype], float(err.max())
 
 
 @pytest.mark.timeout(300)

@@ -412,3 +412,33 @@ def test_input_recipes():
                 if 0 <= yy < 64 and 0 <= xx < 64:
                     assert yy * 64 + xx in row
     assert (inputs.global_index(wl) == I).all()     # seeded
+
+
+# --------------------------------------------------------------------------
+# The first layer's log softmax denominators: closed forms. Scores chosen as
+# logs (d = 1, q = 1, k_j = ln c_j) give lse = ln sum c_j; identical keys give
+# lse = s + ln N; and exp(s - lse) reproduces the oracle's dense map.
+# --------------------------------------------------------------------------
+def test_dense_lse_closed_forms():
+    c = np.array([1.0, 2.0, 3.0, 4.0])
+    Q = np.ones((1, 1, 2, 2, 1))
+    K = np.log(c).reshape(1, 1, 2, 2, 1)
+    lse = oracle.dense_lse(Q, K, win=2, shift=0)
+    np.testing.assert_allclose(lse, np.log(10.0), rtol=0, atol=1e-14)
+    g = np.random.Generator(np.random.PCG64(77))
+    Q = g.standard_normal((1, 2, 8, 8, 4))
+    k = g.standard_normal(4)
+    K = np.broadcast_to(k, (1, 2, 8, 8, 4)).copy()
+    lse = oracle.dense_lse(Q, K, win=4, shift=1)
+    s = np.stack([np.concatenate([Q[0, h, (4 * (wid // 2) + np.arange(16) // 4 + 1) % 8,
+                                    (4 * (wid % 2) + np.arange(16) % 4 + 1) % 8] @ k / 2.0])
+                  for h in range(2) for wid in range(4)])
+    np.testing.assert_allclose(lse, s + np.log(16.0), rtol=1e-13)
+    # the layer oracle's dense map is exp(s - lse): with one slot's key set to 0,
+    # that slot's score is 0 and its weight must be exp(-lse)
+    Q = g.standard_normal((1, 1, 8, 8, 4))
+    K = g.standard_normal((1, 1, 8, 8, 4))
+    K[0, 0, 2, 2] = 0.0                      # slot 0 of window (0, 0) under shift 2
+    ref = oracle.layer(Q, K, K, win=4, shift=2, K_l=16, wh_list=[0])
+    lse = oracle.dense_lse(Q, K, win=4, shift=2, wh_list=[0])
+    np.testing.assert_allclose(ref["A"][0, :, 0], np.exp(-lse[0]), rtol=1e-12)
