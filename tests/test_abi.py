@@ -116,3 +116,16 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(pfa, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         pfa.load()
+
+
+def test_plain_c_client(lib, tmp_path):
+    # the header is plain C99 and the library links into a C program
+    import subprocess
+    src = os.path.join(ROOT, "tests", "c", "abi_check.c")
+    exe = str(tmp_path / "abi_check")
+    libdir = os.path.dirname(pfa._LIB_PATH)
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                           src, "-o", exe, "-L", libdir, "-lpfa", "-Wl,-rpath," + libdir])
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "FAIL" not in r.stdout
