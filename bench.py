@@ -32,16 +32,20 @@ COUNTERS_FILE = "hbm_counters_{workload}.md"
 DENSE, ALL_CAND, SPARSE, SELECT, AGGREGATE, IOTA = range(6)
 
 
-def kernel_bytes(w, l, kind, i_prev_implicit, split):
+def kernel_bytes(w, l, kind, i_prev_implicit, split, fused=False):
     """Algorithmic HBM bytes of one launch of kernel `kind` in layer l (0-based),
     per window-head: every input read once, every output written once. `split`:
-    the layer ran a separate aggregation kernel, so this one does not touch V or O."""
+    the layer ran a separate aggregation kernel, so this one does not touch V or O.
+    `fused`: layers 1-2 ran fused (no A^1: the dense layer writes O only, the
+    second layer reads the first layer's Q and K instead of A^1)."""
     N, d = w.N, w.d
     b_in = 4 if w.dtype == "f32" else 2
     x = N * d * b_in                      # one of Q, K, V
     O = N * d * 4
     if kind == DENSE:
-        return 3 * x + O + N * N * 4      # A^1 materialised; I^1 implicit
+        return 3 * x + O + (0 if fused else N * N * 4)   # A^1 materialised unless fused; I^1 implicit
+    if fused and l == 1 and kind == ALL_CAND:
+        return 4 * x + N * w.K[1] * 8
     if kind == IOTA:
         return N * N * 4
     K_prev, K_l = w.K[l - 1], w.K[l]
@@ -98,6 +102,8 @@ def main():
     ap.add_argument("--workload", default="map256x256_h6_d32_f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=256, help="window-heads timed on the CPU oracle")
+    ap.add_argument("--fused12", action="store_true",
+                    help="run layers 1-2 fused without materialising A^1 (bf16, or fp32 with d = 16)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -135,10 +141,11 @@ def main():
     lead = (w.B, w.heads, w.n_windows)
     N = w.N
     outs = []
+    fused = args.fused12
     for l in range(L):
         K_l = w.K[l]
         I = None if l == 0 else torch.empty(lead + (N, K_l), dtype=torch.int32, device=dev)
-        A = torch.empty(lead + (N, K_l), dtype=torch.float32, device=dev)
+        A = None if (fused and l == 0) else torch.empty(lead + (N, K_l), dtype=torch.float32, device=dev)
         O = torch.empty((w.B, w.heads, w.H, w.W, w.d), dtype=torch.float32, device=dev)
         outs.append((I, A, O))
     implicit = [l == 1 and w.K[0] == N for l in range(L)]
@@ -146,7 +153,12 @@ def main():
     def step(marks=None):
         for l in range(L):
             Q, K, V = qkv[l]
-            if l == 0:
+            if fused and l == 0:
+                pfa.first_two_layers(Q, K, V, *qkv[1], w.K[1], win=w.win, shift1=w.shifts[0], shift2=w.shifts[1],
+                                     out=(outs[0][2],) + outs[1])
+            elif fused and l == 1:
+                pass   # done with layer 1
+            elif l == 0:
                 pfa.dense_layer(Q, K, V, w.K[0], win=w.win, shift=w.shifts[0], out=outs[0])
             else:
                 I_prev = None if implicit[l] else outs[l - 1][0]
@@ -179,7 +191,8 @@ def main():
     for i, end in enumerate(marks):
         l = i % L
         for kind, ms in recs[start:end]:
-            per.setdefault((l, kind), []).append(ms)
+            ll = 1 if (fused and l == 0 and kind != DENSE) else l   # fused call: dense = layer 1, rest = layer 2
+            per.setdefault((ll, kind), []).append(ms)
         start = end
     layer_ms = [sum(float(np.mean(v)) for (ll, _), v in per.items() if ll == l) for l in range(L)]
 
@@ -194,7 +207,7 @@ def main():
     for (l, kind), v in sorted(per.items()):
         ms = float(np.mean(v))
         split = (l, AGGREGATE) in per
-        by = kernel_bytes(w, l, kind, implicit[l], split) * w.n_wh
+        by = kernel_bytes(w, l, kind, implicit[l], split, fused) * w.n_wh
         fl = kernel_flops(w, l, kind, split) * w.n_wh
         gbs = by / (ms * 1e-3) / 1e9
         tfs = fl / (ms * 1e-3) / 1e12
@@ -224,7 +237,8 @@ def main():
         "value": value, "unit": "candidate pairs/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "heads": w.heads, "H": w.H, "W": w.W, "d": w.d, "win": w.win,
+        "config": {"workload": w.name, "fused_layers_1_2": fused, "B": w.B, "heads": w.heads, "H": w.H, "W": w.W,
+                   "d": w.d, "win": w.win,
                    "K": w.K, "shifts": w.shifts, "window_heads": w.n_wh, "pairs_per_step": total_pairs},
         "roofline": roof, "layers": layers, "kernels": kernels,
     }

@@ -111,6 +111,32 @@ int pfa_sparse_layer(const pfa_shape* shape, const void* Q, const void* K, const
                      int32_t K_prev, int32_t K_l, int32_t* I_out, float* A_out, float* O_out,
                      void* stream);
 
+/*
+ * The first two layers of a chain fused, with the first layer's map never
+ * written to memory. Computes what pfa_dense_layer (K1 = N) followed by
+ * pfa_sparse_layer (I_prev = NULL, A_prev = that map, K_l = K2_keep) compute,
+ * using the closed form of the chain ("Progressive attention across layers":
+ * A^2 = Norm(A^1 (.) A_cal^2) with both maps softmaxes, so the second layer
+ * keeps the top K2_keep of exp(s1_ij + s2_ij) and A^2 is that quantity
+ * renormalised over the kept set).
+ *
+ * shape   B, heads, H, W, d, win, dtype of both layers; shape->shift must be 0,
+ *         the two layers' shifts are shift1 and shift2 (each in [0, win)).
+ * Q1, K1, V1 / Q2, K2, V2   the two layers' inputs, [B, heads, H, W, d].
+ * O1_out  [B, heads, H, W, d] fp32: layer 1's output (required).
+ * lse1_out [B, heads, nwin, N] fp32 or NULL: layer 1's log softmax denominators.
+ * I2_out, A2_out  [B, heads, nwin, N, K2_keep] int32 / fp32; O2_out as O1_out.
+ * Window mode with win = 32 (N = 1024) only; both layers' K must fit in LDS
+ * together: bf16 (d = 16, 32) and fp32 with d = 16.
+ * Errors: PFA_ERR_INVALID for NULL inputs or outputs, shifts outside [0, win),
+ * shape->shift != 0, K2_keep outside [1, N]; PFA_ERR_UNSUPPORTED for global mode,
+ * win != 32, fp32 with d = 32, d not 16/32, unknown dtype.
+ */
+int pfa_first_two_layers(const pfa_shape* shape, int32_t shift1, int32_t shift2, const void* Q1,
+                         const void* K1, const void* V1, const void* Q2, const void* K2, const void* V2,
+                         int32_t K2_keep, float* lse1_out, float* O1_out, int32_t* I2_out, float* A2_out,
+                         float* O2_out, void* stream);
+
 /* Static string for a return code; never NULL. */
 const char* pfa_strerror(int code);
 

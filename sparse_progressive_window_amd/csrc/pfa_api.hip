@@ -102,6 +102,7 @@ int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const voi
     a.K_prev = K_prev; a.K_l = K_l;
     a.i_shared = i_shared ? 1 : 0;
     a.scale2 = (float)(1.4426950408889634 / sqrt((double)g.d));
+    a.Q1 = nullptr; a.K1 = nullptr; a.shift1 = 0;
 
     const int rowb = g.d * elem_bytes(dtype);
     a.xcd_map = (n_wh(g) % 8 == 0) ? 1 : 0;
@@ -185,6 +186,59 @@ int pfa_dense_layer(const pfa_shape* shape, const void* Q, const void* K, const 
     hipError_t e = timed(PFA_KERNEL_DENSE, s, [&] { return pfa::launch_dense(a, shape->dtype, g.d, (int)grid, s); });
     if (e == hipSuccess && I_out)
         e = timed(PFA_KERNEL_IOTA, s, [&] { return pfa::launch_iota_rows(I_out, n_wh(g) * g.N, g.N, s); });
+    return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
+}
+
+int pfa_first_two_layers(const pfa_shape* shape, int32_t shift1, int32_t shift2, const void* Q1,
+                         const void* K1, const void* V1, const void* Q2, const void* K2, const void* V2,
+                         int32_t K2_keep, float* lse1_out, float* O1_out, int32_t* I2_out, float* A2_out,
+                         float* O2_out, void* stream) {
+    Geom g;
+    int code;
+    if (!geom_from_shape(shape, &g, &code)) return code;
+    if (shape->shift != 0) return PFA_ERR_INVALID;
+    if (g.win == 0 || g.N != 1024) return PFA_ERR_UNSUPPORTED;
+    if (shift1 < 0 || shift1 >= g.win || shift2 < 0 || shift2 >= g.win) return PFA_ERR_INVALID;
+    if (!Q1 || !K1 || !V1 || !Q2 || !K2 || !V2 || !O1_out || !I2_out || !A2_out || !O2_out) return PFA_ERR_INVALID;
+    if (K2_keep < 1 || K2_keep > g.N) return PFA_ERR_INVALID;
+    if (!pfa::all_cand_dual_fits(shape->dtype, g.d)) return PFA_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const float scale2 = (float)(1.4426950408889634 / sqrt((double)g.d));
+    const int xcd = (n_wh(g) % 8 == 0) ? 1 : 0;
+
+    // layer 1: dense softmax attention, O (and optionally the log denominators) only
+    pfa::DenseArgs d;
+    d.Q = Q1; d.K = K1; d.V = V1;
+    d.A_out = nullptr; d.lse_out = lse1_out; d.O_out = O1_out;
+    d.g = g;
+    d.g.shift = shift1;
+    d.scale2 = scale2;
+    d.xcd_map = xcd;
+    const int64_t dgrid = n_wh(g) * pfa::dense_query_blocks(g.N);
+    if (dgrid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
+    hipError_t e = timed(PFA_KERNEL_DENSE, s, [&] { return pfa::launch_dense(d, shape->dtype, g.d, (int)dgrid, s); });
+    if (e != hipSuccess) return PFA_ERR_HIP;
+
+    // layer 2: keys from q1.k1 + q2.k2 over every slot, then the aggregation with V2
+    pfa::SparseArgs a;
+    a.Q = Q2; a.K = K2; a.V = V2;
+    a.I_prev = nullptr; a.A_prev = nullptr;
+    a.I_out = I2_out; a.A_out = A2_out; a.O_out = O2_out;
+    a.g = g;
+    a.g.shift = shift2;
+    a.K_prev = g.N; a.K_l = K2_keep;
+    a.i_shared = 0;
+    a.scale2 = scale2;
+    a.Q1 = Q1; a.K1 = K1; a.shift1 = shift1;
+    a.xcd_map = xcd;
+    a.blocks_per_wh = 2;
+    a.rows_per_block = g.N / 2;
+    const int64_t grid = n_wh(g) * a.blocks_per_wh;
+    if (grid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
+    e = timed(PFA_KERNEL_ALL_CANDIDATES, s,
+              [&] { return pfa::launch_all_cand_dual(a, shape->dtype, g.d, (int)grid, s); });
+    if (e == hipSuccess)
+        e = timed(PFA_KERNEL_AGGREGATE, s, [&] { return pfa::launch_aggregate(a, shape->dtype, g.d, (int)grid, s); });
     return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
 }
 

@@ -26,6 +26,11 @@ struct SparseArgs {
     int rows_per_block, blocks_per_wh;
     int xcd_map;             // 1: the parts of a window-head run on one XCD (needs #wh % 8 == 0)
     float scale2;            // log2(e) / sqrt(d): scores are kept in base-2 units
+    // fused first two layers only: the first layer's Q and K (window slots under
+    // shift1); the candidate scores are then q1.k1 + q.k
+    const void* Q1;
+    const void* K1;
+    int shift1;
 };
 
 // kKselect: window mode, K staged in LDS, selection only (O comes from
@@ -49,6 +54,9 @@ hipError_t launch_sparse(const SparseArgs& a, int dtype, int D, SparseMode mode,
                          hipStream_t stream);
 // All-candidates layer (I^{l-1} implicit, K_prev = N = 1024): MFMA scores, selection only.
 hipError_t launch_all_cand(const SparseArgs& a, int dtype, int D, int grid, hipStream_t stream);
+// Same with the first layer's scores added (fused first two layers, no A^1).
+bool all_cand_dual_fits(int dtype, int D);
+hipError_t launch_all_cand_dual(const SparseArgs& a, int dtype, int D, int grid, hipStream_t stream);
 // O from stored (I^l, A^l) rows with V in LDS (window mode).
 hipError_t launch_aggregate(const SparseArgs& a, int dtype, int D, int grid, hipStream_t stream);
 int dense_query_blocks(int N);   // workgroups per window-head of the dense layer

@@ -765,10 +765,14 @@ struct Mfma4<uint16_t> {
 };
 
 // Chunk permutation of the LDS-resident K rows of the all-candidates kernel
-// (128-byte rows, no pad): chunk c of row r is stored at position c ^ kswz(r),
-// so the MFMA operand reads of 16 consecutive rows at one chunk position touch
-// 16 different bank groups.
-__device__ __forceinline__ int kswz(int r) { return (r ^ (r >> 3)) & 7; }
+// (128- or 64-byte rows, no pad): chunk c of row r is stored at position
+// c ^ kswz(r), so the MFMA operand reads of 16 consecutive rows at one chunk
+// position touch 16 different 16-byte bank groups (and 8 consecutive rows 8).
+template <int CH>
+__device__ __forceinline__ int kswz(int r) {
+    if (CH == 8) return (r ^ (r >> 3)) & 7;
+    return (r ^ (r >> 2)) & 3;
+}
 
 // Selection-only layer whose candidate list is every slot of a 32x32 window
 // (I^{l-1} implicit, K_prev = N = 1024). Scores of a batch of 4 query rows x 64
@@ -777,7 +781,11 @@ __device__ __forceinline__ int kswz(int r) { return (r ^ (r >> 3)) & 7; }
 // across the wave's lane quarters (v_permlane32_swap, v_permlane16_swap) then
 // gives each 16-lane quarter one query row: lane 16g + b holds row g's candidates
 // 16k + b, k = 0..63, so the 4 rows are selected together, one per 16-lane group.
-template <typename T, int D, bool HAS_A>
+// DUAL: fused first two layers; the scores are q1.k1 + q.k (the first layer's Q/K
+// under shift1 as a second K region in LDS), with no previous map: by the
+// closed form of the chain, the second layer keeps the top K_l of
+// A^1 (.) softmax(s2), i.e. of exp(s1 + s2) up to a row constant.
+template <typename T, int D, bool HAS_A, bool DUAL>
 __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseArgs p) {
     constexpr int NW = 16;
     constexpr int GL = 16;
@@ -786,7 +794,8 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
     constexpr int EPC = Chunk<T>::kElems;
     constexpr int CH = D / EPC;
     constexpr int ROWB = D * (int)sizeof(T);
-    constexpr bool SWZ = CH == 8;            // 128-byte rows: chunk-swizzled, unpadded
+    constexpr bool SWZ = CH == 8 || CH == 4;   // 128- and 64-byte rows: chunk-swizzled, unpadded
+    constexpr int NK = DUAL ? 2 : 1;            // K regions in LDS
     constexpr int KSTR = SWZ ? ROWB : ROWB + 16;
     constexpr int KK = Mfma4<T>::kK;
     constexpr int HISTG = BPL * GL;       // the level results reuse words 0..2
@@ -803,18 +812,28 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
     const T* Qh = static_cast<const T*>(p.Q) + plane;
     const T* Kh = static_cast<const T*>(p.K) + plane;
 
+    Geom g1 = g;   // DUAL: the first layer's slot geometry
+    g1.shift = p.shift1;
+    const T* Q1h = DUAL ? static_cast<const T*>(p.Q1) + plane : nullptr;
+    const T* K1h = DUAL ? static_cast<const T*>(p.K1) + plane : nullptr;
+
     unsigned char* Ks = smem;
-    unsigned* hb = reinterpret_cast<unsigned*>(smem + N * KSTR) + (wave * 4 + grp) * HISTG;
-    if (SWZ) {
-        for (int u = threadIdx.x; u < N * CH; u += blockDim.x) {
-            const int t = u / CH;
-            const int c = u - t * CH;
-            const size_t src = (size_t)slot_pixel(g, w.wy, w.wx, t) * D + c * EPC;
-            *reinterpret_cast<uint4*>(Ks + t * ROWB + ((c ^ kswz(t)) * 16)) = *reinterpret_cast<const uint4*>(Kh + src);
+    unsigned* hb = reinterpret_cast<unsigned*>(smem + NK * N * KSTR) + (wave * 4 + grp) * HISTG;
+    auto stage_k = [&](unsigned char* dst, const T* src_plane, const Geom& gg) {
+        if (SWZ) {
+            for (int u = threadIdx.x; u < N * CH; u += blockDim.x) {
+                const int t = u / CH;
+                const int c = u - t * CH;
+                const size_t src = (size_t)slot_pixel(gg, w.wy, w.wx, t) * D + c * EPC;
+                *reinterpret_cast<uint4*>(dst + t * ROWB + ((c ^ kswz<CH>(t)) * 16)) =
+                    *reinterpret_cast<const uint4*>(src_plane + src);
+            }
+        } else {
+            stage_rows<T, D>(dst, KSTR, src_plane, gg, w.wy, w.wx);
         }
-    } else {
-        stage_rows<T, D>(Ks, KSTR, Kh, g, w.wy, w.wx);
-    }
+    };
+    stage_k(Ks, Kh, g);
+    if (DUAL) stage_k(Ks + N * KSTR, K1h, g1);
     __syncthreads();
 
     const int row0 = w.part * p.rows_per_block;
@@ -833,25 +852,29 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
         __asm__ volatile("" : "+v"(lv));
         const int glv = lv & (GL - 1);
         const int qi = min(base + (lv & 3), row1 - 1);
-        const unsigned char* qrow =
-            reinterpret_cast<const unsigned char*>(Qh + (size_t)slot_pixel(g, w.wy, w.wx, qi) * D);
         // 16 accumulator chains (one per 64-candidate tile), contraction chunk outer:
         // one 16-byte chunk of the query is live at a time
         v4f acc[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-        const unsigned char* kr0 = Ks + lv * KSTR;
 #pragma unroll
-        for (int m = 0; m < CH; ++m) {
-            float qv[EPC];
-            Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(qrow + 16 * m), qv);
-            const int koff = (SWZ ? (m ^ kswz(lv)) : m) * 16;
+        for (int set = 0; set < NK; ++set) {   // DUAL: the first layer's q1.k1, then q.k
+            const bool first = DUAL && set == 0;
+            const unsigned char* qrow = reinterpret_cast<const unsigned char*>(
+                (first ? Q1h : Qh) + (size_t)slot_pixel(first ? g1 : g, w.wy, w.wx, qi) * D);
+            const unsigned char* kr0 = Ks + (first ? N * KSTR : 0) + lv * KSTR;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                float kf[EPC];
-                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(kr0 + kWave * t * KSTR + koff), kf);
+            for (int m = 0; m < CH; ++m) {
+                float qv[EPC];
+                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(qrow + 16 * m), qv);
+                const int koff = (SWZ ? (m ^ kswz<CH>(lv)) : m) * 16;
 #pragma unroll
-                for (int e = 0; e < EPC; e += KK) acc[t] = Mfma4<T>::run(&qv[e], &kf[e], acc[t]);
+                for (int t = 0; t < 16; ++t) {
+                    float kf[EPC];
+                    Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(kr0 + kWave * t * KSTR + koff), kf);
+#pragma unroll
+                    for (int e = 0; e < EPC; e += KK) acc[t] = Mfma4<T>::run(&qv[e], &kf[e], acc[t]);
+                }
             }
         }
         float uv[KPT];   // raw scores q.k, then the keys
@@ -1116,12 +1139,27 @@ hipError_t launch_shape(const SparseArgs& a, SparseMode mode, int lds, int grid,
 }
 
 template <typename T, int D>
-hipError_t launch_all_cand_t(const SparseArgs& a, int grid, hipStream_t s) {
+constexpr int all_cand_kstr() {
     constexpr int ROWB = D * (int)sizeof(T);
-    constexpr int KSTR = ROWB == 128 ? ROWB : ROWB + 16;
-    const int lds = 1024 * KSTR + 16 * 4 * (8 * 16) * 4;
-    if (a.A_prev) return launch_fn(all_cand_rows_kernel<T, D, true>, a, 16 * kWave, lds, grid, s);
-    return launch_fn(all_cand_rows_kernel<T, D, false>, a, 16 * kWave, lds, grid, s);
+    return (ROWB == 128 || ROWB == 64) ? ROWB : ROWB + 16;
+}
+constexpr int kAllCandHistBytes = 16 * 4 * (8 * 16) * 4;   // 16 waves x 4 rows x 128 bins
+
+template <typename T, int D>
+hipError_t launch_all_cand_t(const SparseArgs& a, int grid, hipStream_t s) {
+    const int lds = 1024 * all_cand_kstr<T, D>() + kAllCandHistBytes;
+    if (a.A_prev) return launch_fn(all_cand_rows_kernel<T, D, true, false>, a, 16 * kWave, lds, grid, s);
+    return launch_fn(all_cand_rows_kernel<T, D, false, false>, a, 16 * kWave, lds, grid, s);
+}
+
+template <typename T, int D>
+hipError_t launch_all_cand_dual_t(const SparseArgs& a, int grid, hipStream_t s) {
+    if constexpr (2 * 1024 * all_cand_kstr<T, D>() + kAllCandHistBytes > kLdsBytes) {
+        return hipErrorInvalidValue;   // rejected by the caller beforehand
+    } else {
+        const int lds = 2 * 1024 * all_cand_kstr<T, D>() + kAllCandHistBytes;
+        return launch_fn(all_cand_rows_kernel<T, D, false, true>, a, 16 * kWave, lds, grid, s);
+    }
 }
 
 template <typename T, int D>
@@ -1152,6 +1190,20 @@ hipError_t launch_sparse(const SparseArgs& a, int dtype, int D, SparseMode mode,
                        : launch_shape<float, 32>(a, mode, lds_bytes, grid, stream);
     return D == 16 ? launch_shape<uint16_t, 16>(a, mode, lds_bytes, grid, stream)
                    : launch_shape<uint16_t, 32>(a, mode, lds_bytes, grid, stream);
+}
+
+bool all_cand_dual_fits(int dtype, int D) {
+    const int kstr = dtype == 0 ? (D == 16 ? all_cand_kstr<float, 16>() : all_cand_kstr<float, 32>())
+                                : (D == 16 ? all_cand_kstr<uint16_t, 16>() : all_cand_kstr<uint16_t, 32>());
+    return 2 * 1024 * kstr + kAllCandHistBytes <= kLdsBytes;
+}
+
+hipError_t launch_all_cand_dual(const SparseArgs& a, int dtype, int D, int grid, hipStream_t stream) {
+    if (dtype == 0)
+        return D == 16 ? launch_all_cand_dual_t<float, 16>(a, grid, stream)
+                       : launch_all_cand_dual_t<float, 32>(a, grid, stream);
+    return D == 16 ? launch_all_cand_dual_t<uint16_t, 16>(a, grid, stream)
+                   : launch_all_cand_dual_t<uint16_t, 32>(a, grid, stream);
 }
 
 hipError_t launch_all_cand(const SparseArgs& a, int dtype, int D, int grid, hipStream_t stream) {

@@ -41,6 +41,9 @@ def load():
         lib.pfa_dense_layer.restype = ctypes.c_int
         lib.pfa_sparse_layer.argtypes = [ctypes.POINTER(PfaShape), P, P, P, P, i32, P, i32, i32, P, P, P, P]
         lib.pfa_sparse_layer.restype = ctypes.c_int
+        lib.pfa_first_two_layers.argtypes = [ctypes.POINTER(PfaShape), i32, i32, P, P, P, P, P, P, i32, P, P, P, P,
+                                             P, P]
+        lib.pfa_first_two_layers.restype = ctypes.c_int
         lib.pfa_strerror.argtypes = [ctypes.c_int]
         lib.pfa_strerror.restype = ctypes.c_char_p
         lib.pfa_version.restype = ctypes.c_int
@@ -172,6 +175,39 @@ def sparse_layer(Q, K, V, I_prev, A_prev, K_l, *, win, shift=0, i_shared=False, 
     if rc != 0:
         raise PfaError("pfa_sparse_layer", rc)
     return I, A, O
+
+
+def first_two_layers(Q1, K1, V1, Q2, K2, V2, K2_keep, *, win, shift1=0, shift2=0, out=None, lse_out=None):
+    """Layers 1 and 2 of a chain without materialising layer 1's map. Returns
+    (O1, I2, A2, O2); ``out`` = optional preallocated (O1, I2, A2, O2);
+    ``lse_out`` = optional [B, heads, nwin, N] fp32 tensor for layer 1's log
+    softmax denominators."""
+    _check_qkv(Q1, K1, V1)
+    _check_qkv(Q2, K2, V2)
+    if Q2.shape != Q1.shape or Q2.dtype != Q1.dtype:
+        raise ValueError("both layers' Q/K/V must share shape and dtype")
+    lead, N = _geometry(Q1, win)
+    dev = Q1.device
+    if out is None:
+        O1 = torch.empty(Q1.shape, dtype=torch.float32, device=dev)
+        I2 = torch.empty(lead + (N, K2_keep), dtype=torch.int32, device=dev)
+        A2 = torch.empty(lead + (N, K2_keep), dtype=torch.float32, device=dev)
+        O2 = torch.empty(Q1.shape, dtype=torch.float32, device=dev)
+    else:
+        O1, I2, A2, O2 = out
+    rows = _prod(lead) * N
+    _expect(O1, Q1.numel(), torch.float32, "O1_out")
+    _expect(I2, rows * K2_keep, torch.int32, "I2_out")
+    _expect(A2, rows * K2_keep, torch.float32, "A2_out")
+    _expect(O2, Q1.numel(), torch.float32, "O2_out")
+    _expect(lse_out, rows, torch.float32, "lse1_out")
+    shape = make_shape(Q1, win, 0)
+    rc = load().pfa_first_two_layers(ctypes.byref(shape), shift1, shift2, _ptr(Q1), _ptr(K1), _ptr(V1), _ptr(Q2),
+                                     _ptr(K2), _ptr(V2), K2_keep, _ptr(lse_out), _ptr(O1), _ptr(I2), _ptr(A2),
+                                     _ptr(O2), _stream())
+    if rc != 0:
+        raise PfaError("pfa_first_two_layers", rc)
+    return O1, I2, A2, O2
 
 
 KERNEL_KINDS = ("dense", "all_candidates", "sparse", "select", "aggregate", "iota")

@@ -30,7 +30,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"pfa_dense_layer", "pfa_sparse_layer", "pfa_strerror", "pfa_version"} <= set(names)
+    assert {"pfa_dense_layer", "pfa_sparse_layer", "pfa_first_two_layers", "pfa_strerror",
+            "pfa_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -129,3 +130,21 @@ def test_plain_c_client(lib, tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "FAIL" not in r.stdout
+
+
+def test_first_two_layers_validation(lib):
+    def fused(s, shift1=0, shift2=16, K2=256, outs=(FAKE, FAKE, FAKE, FAKE)):
+        return lib.pfa_first_two_layers(ctypes.byref(s) if s is not None else None, shift1, shift2, FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, FAKE, K2, None, *outs, None)
+    bf = dict(dtype=1)
+    assert fused(None) == -1
+    assert fused(shape(shift=16, **bf)) == -1                     # shifts go in shift1/shift2
+    assert fused(shape(**bf), shift1=32) == -1
+    assert fused(shape(**bf), shift2=-1) == -1
+    assert fused(shape(**bf), K2=0) == -1
+    assert fused(shape(**bf), K2=1025) == -1
+    assert fused(shape(**bf), outs=(None, FAKE, FAKE, FAKE)) == -1
+    assert fused(shape(**bf), outs=(FAKE, FAKE, FAKE, None)) == -1
+    assert fused(shape()) == -2                                   # fp32, d = 32: K1 and K2 exceed LDS together
+    assert fused(shape(win=16, H=32, W=32, **bf)) == -2           # N != 1024
+    assert fused(shape(win=0, H=32, W=32, **bf)) == -2            # global mode

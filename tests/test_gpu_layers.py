@@ -334,3 +334,39 @@ def test_nonfinite_previous_map_terminates(K_prev, K_l):
     torch.cuda.synchronize()
     Ig = I.cpu().numpy()
     assert (Ig >= 0).all() and (Ig < N).all()
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,d,K2,shifts", [("bf16", 32, 256, (0, 16)), ("bf16", 16, 256, (16, 0)),
+                                              ("f32", 16, 256, (0, 16)), ("bf16", 32, 1000, (3, 29)),
+                                              ("bf16", 32, 1, (0, 0))])
+def test_first_two_layers_fused(dtype, d, K2, shifts):
+    # fused layers 1-2 (no A^1 in memory) against the fp64 oracle chain run unfused
+    shape = (1, 2, 64, 96, d)
+    q1, k1, v1, q2, k2, v2 = (inputs.draw(950 + t + d, shape, dtype) for t in range(6))
+    n_wh, N = 2 * 6, 1024
+    sel = np.arange(n_wh)
+    tol = parity.TOL[dtype]
+    lse = torch.empty((n_wh, N), dtype=torch.float32, device="cuda")
+    O1, I2, A2, O2 = pfa.first_two_layers(*(to_dev(t) for t in (q1, k1, v1, q2, k2, v2)), K2, win=32,
+                                          shift1=shifts[0], shift2=shifts[1], lse_out=lse)
+    torch.cuda.synchronize()
+    ref1 = oracle.layer(q1.exact, k1.exact, v1.exact, win=32, shift=shifts[0], K_l=N, wh_list=sel)
+    parity.check_O(O1.cpu().numpy(), ref1["O"], tol)
+    lse_ref = oracle.dense_lse(q1.exact, k1.exact, win=32, shift=shifts[0])
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() <= tol
+    kw = dict(win=32, shift=shifts[1], K_l=K2, I_prev=None, A_prev=ref1["A"], i_shared=False, prev_compact=True,
+              wh_list=sel)
+    ref2 = oracle.layer(q2.exact, k2.exact, v2.exact, want_keys=True, **kw)
+    st = parity.check_layer(gpu_I=I2.view(n_wh, N, K2).cpu().numpy(), gpu_A=A2.view(n_wh, N, K2).cpu().numpy(),
+                            gpu_O=O2.cpu().numpy(), ref=ref2, cand=None, wh_list=sel, tol=tol,
+                            rerun=parity.rerun_fn(q2.exact, k2.exact, v2.exact, **kw))
+    assert st["rows"] == n_wh * N
+
+
+@pytest.mark.timeout(120)
+def test_first_two_layers_rejects_fp32_d32():
+    Q = torch.zeros((1, 1, 32, 32, 32), dtype=torch.float32, device="cuda")
+    with pytest.raises(pfa.PfaError) as e:
+        pfa.first_two_layers(Q, Q, Q, Q, Q, Q, 256, win=32)
+    assert e.value.code == -2
