@@ -126,3 +126,26 @@ def test_global_individualized(capsys):
                                                   prev_compact=False, wh_list=sel))
     with capsys.disabled():
         print(f"{w.name}: {st}", flush=True)
+
+
+@pytest.mark.timeout(600)
+def test_first_two_layers_fused_full_size(capsys):
+    # the bf16 training-patch batch at full size with layers 1-2 fused (no A^1),
+    # sampled window-heads against the fp64 oracle's unfused chain
+    w = workloads.PATCH64
+    sel = sample_wh(w, 12)
+    q1, k1, v1 = inputs.qkv(w, 0, 0)
+    q2, k2, v2 = inputs.qkv(w, 0, 1)
+    O1, I2, A2, O2 = pfa.first_two_layers(*(to_dev(t) for t in (q1, k1, v1, q2, k2, v2)), w.K[1], win=w.win,
+                                          shift1=w.shifts[0], shift2=w.shifts[1])
+    torch.cuda.synchronize()
+    tol = parity.TOL[w.dtype]
+    ref1 = oracle.layer(q1.exact, k1.exact, v1.exact, win=w.win, shift=w.shifts[0], K_l=w.N, wh_list=sel)
+    st1 = parity.check_O(O1.cpu().numpy(), ref1["O"], tol)
+    kw = dict(win=w.win, shift=w.shifts[1], K_l=w.K[1], I_prev=None, A_prev=ref1["A"], i_shared=False,
+              prev_compact=True, wh_list=sel)
+    ref2 = oracle.layer(q2.exact, k2.exact, v2.exact, want_keys=True, **kw)
+    st2 = parity.check_layer(gpu_I=gpu_rows(I2, sel), gpu_A=gpu_rows(A2, sel), gpu_O=O2.cpu().numpy(), ref=ref2,
+                             cand=None, wh_list=sel, tol=tol, rerun=parity.rerun_fn(q2.exact, k2.exact, v2.exact, **kw))
+    with capsys.disabled():
+        print(f"{w.name} fused layers 1-2: layer 1 {st1}; layer 2 {st2}", flush=True)
