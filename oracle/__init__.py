@@ -6,7 +6,8 @@ CPU-baseline leg of ``bench.py`` may use it; the HIP library never does.
 ``layer`` computes one PFA layer (steps listed in ``pfa_oracle.c``) for a list of
 window-heads; ``chain`` runs the layers of one chain for a list of window-heads,
 feeding each layer's (I, A) to the next, all in fp64. ``dense_lse`` gives the
-first layer's log softmax denominators.
+first layer's log softmax denominators. ``layer_backward`` is the reverse-mode
+derivative of ``layer`` with the kept sets held fixed.
 """
 
 import ctypes
@@ -42,6 +43,9 @@ def _load():
         lib.oracle_layer.argtypes = [i32] * 7 + [P, P, P, P, i32, P, i32, i32, i32, P, i64, P, P, P, P, P]
         lib.oracle_layer.restype = ctypes.c_int
         lib.oracle_threads.restype = ctypes.c_int
+        lib.oracle_layer_backward.argtypes = ([i32] * 7 + [P, P, P, P, P, i32, i32, i32, P, i64, P, P, P]
+                                              + [P, P, P, P])
+        lib.oracle_layer_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -103,6 +107,60 @@ def layer(Q, K, V, *, win, shift, K_l, I_prev=None, A_prev=None, i_shared=False,
     out = {"I": I_out, "A": A_out, "O": O_out}
     if want_keys:
         out["keys"] = keys
+    return out
+
+
+def layer_backward(Q, K, V, *, win, shift, keep, dO, dA=None, I_prev=None, A_prev=None,
+                   prev_compact=False, wh_list=None, want_dA_prev=True):
+    """Gradients of one PFA layer in fp64 with the kept sets held fixed.
+
+    keep: [n_wh, N, K_l] kept slot indices (the layer's I^l, compact over
+    wh_list). dO: [B, heads, H, W, d] gradient of O. dA: [n_wh, N, K_l] gradient
+    of A^l aligned with keep, or None. I_prev / A_prev / prev_compact as in
+    ``layer``. Returns dict dQ, dK, dV ([B, heads, H, W, d], zero outside the
+    listed window-heads) and dA_prev ([n_wh, N, K_prev] in I^{l-1} order, when
+    A_prev is given and want_dA_prev)."""
+    lib = _load()
+    Q = np.ascontiguousarray(Q, dtype=np.float64)
+    K = np.ascontiguousarray(K, dtype=np.float64)
+    V = np.ascontiguousarray(V, dtype=np.float64)
+    dO = np.ascontiguousarray(dO, dtype=np.float64)
+    B, heads, H, W, d = Q.shape
+    N = win * win if win else H * W
+    nwin = (H // win) * (W // win) if win else 1
+    if I_prev is not None:
+        I_prev = np.ascontiguousarray(I_prev, dtype=np.int32)
+        K_prev = I_prev.shape[-1]
+    else:
+        K_prev = N
+    if A_prev is not None:
+        A_prev = np.ascontiguousarray(A_prev, dtype=np.float64)
+        assert A_prev.shape[-1] == K_prev
+    if wh_list is None:
+        wl = None
+        n_wh = B * heads * nwin
+    else:
+        wl = np.ascontiguousarray(wh_list, dtype=np.int64)
+        n_wh = len(wl)
+    keep = np.ascontiguousarray(keep, dtype=np.int32)
+    K_l = keep.shape[-1]
+    assert keep.shape == (n_wh, N, K_l)
+    if dA is not None:
+        dA = np.ascontiguousarray(dA, dtype=np.float64)
+        assert dA.shape == keep.shape
+    dQ = np.zeros(Q.shape)
+    dK = np.zeros(Q.shape)
+    dV = np.zeros(Q.shape)
+    dA_prev = (np.zeros((n_wh, N, K_prev)) if (A_prev is not None and want_dA_prev) else None)
+    rc = lib.oracle_layer_backward(B, heads, H, W, d, win, shift, _ptr(Q), _ptr(K), _ptr(V),
+                                   _ptr(I_prev), _ptr(A_prev), int(bool(prev_compact)), K_prev, K_l,
+                                   _ptr(wl), n_wh, _ptr(keep), _ptr(dO), _ptr(dA),
+                                   _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dA_prev))
+    if rc != 0:
+        raise ValueError("oracle_layer_backward rejected the sizes or the kept sets")
+    out = {"dQ": dQ, "dK": dK, "dV": dV}
+    if dA_prev is not None:
+        out["dA_prev"] = dA_prev
     return out
 
 

@@ -200,3 +200,153 @@ int oracle_layer(int B, int heads, int H, int W, int d, int win, int shift,
     }
     return 0;
 }
+
+/*
+ * Reverse-mode derivative of one PFA layer with its kept sets held fixed (the
+ * selection is piecewise constant, so the kept set is a constant of the
+ * backward pass). It reruns steps 1-6 and 8-10 above for each row, then walks
+ * them backwards with the chain rule, one step at a time:
+ *
+ *   step 9  O_i = sum_kept A_c v_j      gA_c  = dA_c + dO_i . v_j,  dV_j += A_c dO_i
+ *   step 8  A_c = P'_c / S (kept)       gP'_c = (gA_c - sum_kept A gA) / S, 0 if dropped
+ *   step 6  P'_c = P_c / sp             gP_c  = (gP'_c - sum_c P'_c gP'_c) / sp
+ *   step 5  P_c = a_c * Acal_c          gAcal_c = gP_c a_c,   dA^{l-1}_c = gP_c Acal_c
+ *   step 4  Acal = softmax(s) over C_i  gs_c  = Acal_c (gAcal_c - sum_c Acal gAcal)
+ *   step 3  s_c = q_i . k_j / sqrt(d)   dQ_i += gs_c k_j / sqrt(d),  dK_j += gs_c q_i / sqrt(d)
+ *
+ * keep      [n_wh, N, K_l] kept slot indices j of each row (the layer's I^l).
+ * dO        [B, heads, H, W, d] gradient of O.
+ * dA        [n_wh, N, K_l] gradient of A^l aligned with keep, or NULL (zero).
+ * dQ,dK,dV  [B, heads, H, W, d]: gradients are ADDED to them (pixels of the
+ *           listed window-heads only).
+ * dA_prev   [n_wh, N, K_prev] gradient of A^{l-1} in C_i order (written), or
+ *           NULL. Requires A_prev.
+ * Window mode or global mode with one index matrix per head; other arguments as
+ * in oracle_layer. Returns 0, or -1 on inconsistent sizes or a kept slot that is
+ * not a candidate.
+ */
+int oracle_layer_backward(int B, int heads, int H, int W, int d, int win, int shift,
+                          const double* Q, const double* K, const double* V,
+                          const int32_t* I_prev, const double* A_prev, int prev_compact, int K_prev, int K_l,
+                          const int64_t* wh_list, int64_t n_wh, const int32_t* keep,
+                          const double* dO, const double* dA,
+                          double* dQ, double* dK, double* dV, double* dA_prev) {
+    const int N = win ? win * win : H * W;
+    const int nwy = win ? H / win : 1, nwx = win ? W / win : 1;
+    const int64_t total_wh = (int64_t)B * heads * nwy * nwx;
+    if (win && (H % win || W % win)) return -1;
+    if (K_l < 1 || K_l > K_prev || K_prev > N) return -1;
+    if (!I_prev && K_prev != N) return -1;
+    if (dA_prev && !A_prev) return -1;
+    if (!wh_list) n_wh = total_wh;
+    const double scale = 1.0 / sqrt((double)d);
+    int bad = 0;
+
+    int64_t w;
+#pragma omp parallel for schedule(dynamic) reduction(| : bad)
+    for (w = 0; w < n_wh; ++w) {
+        const int64_t id = wh_list ? wh_list[w] : w;
+        const int wx = (int)(id % nwx);
+        const int wy = (int)((id / nwx) % nwy);
+        const int h = (int)((id / ((int64_t)nwx * nwy)) % heads);
+        const int b = (int)(id / ((int64_t)nwx * nwy * heads));
+        const int64_t plane = (int64_t)H * W * d;
+        const int64_t off = ((int64_t)b * heads + h) * plane;
+        const int64_t win_id = (int64_t)wy * nwx + wx;
+
+        double* s = (double*)malloc(sizeof(double) * K_prev);
+        double* acal = (double*)malloc(sizeof(double) * K_prev);
+        double* pp = (double*)malloc(sizeof(double) * K_prev);     /* P' */
+        double* gpp = (double*)malloc(sizeof(double) * K_prev);    /* gradient of P' */
+        int* slot = (int*)malloc(sizeof(int) * K_prev);            /* position in keep, -1 dropped */
+
+        for (int i = 0; i < N; ++i) {
+            const int64_t qpix = pixel_of(win, shift, H, W, wy, wx, i);
+            const double* q = Q + off + qpix * d;
+            const double* go = dO + off + qpix * d;
+            const int64_t row = prev_compact ? (int64_t)w * N + i
+                : (((int64_t)b * heads + h) * nwy * nwx + win_id) * N + i;
+            const int32_t* C = I_prev ? I_prev + row * K_prev : NULL;
+            const double* a = A_prev ? A_prev + row * K_prev : NULL;
+            const int32_t* kp = keep + ((int64_t)w * N + i) * K_l;
+            const double* dAr = dA ? dA + ((int64_t)w * N + i) * K_l : NULL;
+
+            /* forward steps 3-6 */
+            for (int c = 0; c < K_prev; ++c) {
+                const int j = C ? C[c] : c;
+                const double* k = K + off + pixel_of(win, shift, H, W, wy, wx, j) * d;
+                double acc = 0.0;
+                for (int e = 0; e < d; ++e) acc += q[e] * k[e];
+                s[c] = acc * scale;
+            }
+            double m = s[0];
+            for (int c = 1; c < K_prev; ++c) if (s[c] > m) m = s[c];
+            double z = 0.0;
+            for (int c = 0; c < K_prev; ++c) z += exp(s[c] - m);
+            double sp = 0.0;
+            for (int c = 0; c < K_prev; ++c) {
+                acal[c] = exp(s[c] - m) / z;
+                pp[c] = (a ? a[c] : 1.0) * acal[c];
+                sp += pp[c];
+            }
+            for (int c = 0; c < K_prev; ++c) pp[c] /= sp;
+            /* step 7 replaced by the given kept set */
+            int n_kept = 0;
+            for (int c = 0; c < K_prev; ++c) {
+                const int j = C ? C[c] : c;
+                slot[c] = -1;
+                for (int t = 0; t < K_l; ++t)
+                    if (kp[t] == j) slot[c] = t;
+                if (slot[c] >= 0) ++n_kept;
+            }
+            if (n_kept != K_l) { bad = 1; continue; }
+            double S = 0.0;
+            for (int c = 0; c < K_prev; ++c) if (slot[c] >= 0) S += pp[c];
+
+            /* step 9 backwards: gA, dV; then step 8 */
+            double sum_AgA = 0.0;
+            for (int c = 0; c < K_prev; ++c) {
+                gpp[c] = 0.0;
+                if (slot[c] < 0) continue;
+                const int j = C ? C[c] : c;
+                const int64_t jpix = pixel_of(win, shift, H, W, wy, wx, j);
+                const double* v = V + off + jpix * d;
+                const double Ac = pp[c] / S;
+                double gA = dAr ? dAr[slot[c]] : 0.0;
+                for (int e = 0; e < d; ++e) gA += go[e] * v[e];
+                double* dv = dV + off + jpix * d;
+                for (int e = 0; e < d; ++e) dv[e] += Ac * go[e];
+                gpp[c] = gA;           /* holds gA until the sum is known */
+                sum_AgA += Ac * gA;
+            }
+            for (int c = 0; c < K_prev; ++c)
+                if (slot[c] >= 0) gpp[c] = (gpp[c] - sum_AgA) / S;
+            /* step 6 backwards */
+            double sum_PgP = 0.0;
+            for (int c = 0; c < K_prev; ++c) sum_PgP += pp[c] * gpp[c];
+            /* steps 5 and 4 backwards: reuse gpp for gP, then s for gAcal */
+            double sum_AcalgAcal = 0.0;
+            for (int c = 0; c < K_prev; ++c) {
+                const double gP = (gpp[c] - sum_PgP) / sp;
+                if (dA_prev) dA_prev[((int64_t)w * N + i) * K_prev + c] = gP * acal[c];
+                s[c] = gP * (a ? a[c] : 1.0);    /* gAcal */
+                sum_AcalgAcal += acal[c] * s[c];
+            }
+            /* step 3 backwards */
+            double* dq = dQ + off + qpix * d;
+            for (int c = 0; c < K_prev; ++c) {
+                const double gs = acal[c] * (s[c] - sum_AcalgAcal);
+                const int j = C ? C[c] : c;
+                const int64_t jpix = pixel_of(win, shift, H, W, wy, wx, j);
+                const double* k = K + off + jpix * d;
+                double* dk = dK + off + jpix * d;
+                for (int e = 0; e < d; ++e) {
+                    dq[e] += gs * k[e] * scale;
+                    dk[e] += gs * q[e] * scale;
+                }
+            }
+        }
+        free(s); free(acal); free(pp); free(gpp); free(slot);
+    }
+    return bad ? -1 : 0;
+}
