@@ -20,7 +20,8 @@
  * device; the caller allocates all of them. The layer calls never allocate,
  * free or synchronise: they validate the arguments, enqueue kernels on
  * `stream` (a hipStream_t; NULL = the null stream) and return. (Only the
- * optional timing calls at the end of this header create HIP events.)
+ * optional timing calls at the end of this header create HIP events; the
+ * backward pass takes its scratch memory as a caller-owned workspace.)
  *
  *   Q, K, V   [B, heads, H, W, d], element type `dtype` (fp32, or bf16 bits).
  *   O         [B, heads, H, W, d] fp32.
@@ -137,6 +138,50 @@ int pfa_first_two_layers(const pfa_shape* shape, int32_t shift1, int32_t shift2,
                          int32_t K2_keep, float* lse1_out, float* O1_out, int32_t* I2_out, float* A2_out,
                          float* O2_out, void* stream);
 
+/*
+ * Backward pass of a window-mode sparse layer ("Progressive attention across
+ * layers" and "Sparse matrix multiplication": the layer is differentiated
+ * through its renormalisation, the Hadamard product with A^{l-1}, the softmax
+ * and the two sparse products; the kept sets I^l are constants, as top-K is
+ * piecewise constant). Gradients of the loss with respect to the forward
+ * inputs, given those with respect to its outputs:
+ *
+ *   G_ij = dA_ij + dO_i . v_j,   g_ij = G_ij - sum_j' A_ij' G_ij'   (j, j' kept)
+ *   dQ_i = sum_j A_ij g_ij k_j / sqrt(d)
+ *   dK_j = sum_i A_ij g_ij q_i / sqrt(d),   dV_j = sum_i A_ij dO_i
+ *   dA_prev_ij = A_ij g_ij / A_prev_ij at kept slots, 0 at dropped ones
+ *
+ * Q, K, V, I_prev, A_prev, K_prev, K_l  the forward call's arguments (window
+ *         mode, one index matrix per head; I_prev NULL = every slot, K_prev = N).
+ * I_l, A_l  [B, heads, nwin, N, K_l] the forward call's outputs I^l, A^l.
+ *         I_l must be a subsequence of I_prev in I_prev's order (what
+ *         pfa_sparse_layer and pfa_dense_layer write).
+ * dO      [B, heads, H, W, d] fp32 gradient of O (required).
+ * dA_l    [B, heads, nwin, N, K_l] fp32 gradient of A^l (from the next layer's
+ *         backward), or NULL for zero.
+ * dQ, dK, dV  [B, heads, H, W, d] fp32 outputs, every element written.
+ * dA_prev [B, heads, nwin, N, K_prev] fp32 output aligned with I_prev, or NULL
+ *         (not computed). Requires A_prev. A kept slot whose A_prev is 0 gets 0.
+ * workspace  device buffer of at least pfa_sparse_layer_backward_workspace()
+ *         bytes (one fp32 per kept pair), owned by the caller; its contents on
+ *         entry do not matter and are overwritten.
+ * Accumulation order in dK, dV is not fixed (LDS atomics): results may differ
+ * between runs in the last bits.
+ * Errors: PFA_ERR_INVALID for NULL required pointers, inconsistent sizes,
+ * dA_prev without A_prev, a workspace that is too small; PFA_ERR_UNSUPPORTED
+ * for global mode, K_l > 256, and the shape limits of pfa_sparse_layer.
+ */
+int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void* K, const void* V,
+                              const int32_t* I_prev, const float* A_prev, int32_t K_prev, int32_t K_l,
+                              const int32_t* I_l, const float* A_l, const float* dO, const float* dA_l,
+                              float* dQ, float* dK, float* dV, float* dA_prev, void* workspace,
+                              int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes pfa_sparse_layer_backward needs for this shape and K_l, or a
+ * negative error code (PFA_ERR_INVALID / PFA_ERR_UNSUPPORTED as for the shape,
+ * PFA_ERR_INVALID for K_l outside [1, N]). Host only, no device work. */
+int64_t pfa_sparse_layer_backward_workspace(const pfa_shape* shape, int32_t K_l);
+
 /* Static string for a return code; never NULL. */
 const char* pfa_strerror(int code);
 
@@ -157,7 +202,9 @@ typedef enum {
     PFA_KERNEL_SPARSE = 2,         /* global mode: selection and aggregation in one kernel */
     PFA_KERNEL_SELECT = 3,         /* window mode: selection only (I^l, A^l) */
     PFA_KERNEL_AGGREGATE = 4,      /* window mode: O from the stored (I^l, A^l) rows */
-    PFA_KERNEL_IOTA = 5            /* I rows 0..N-1 of the dense layer */
+    PFA_KERNEL_IOTA = 5,           /* I rows 0..N-1 of the dense layer */
+    PFA_KERNEL_BWD_ROWS = 6,       /* backward: per-row pass(es) -> g, dQ, dA_prev */
+    PFA_KERNEL_BWD_SCATTER = 7     /* backward: dK, dV accumulated per window-head */
 } pfa_kernel_kind;
 
 /* capacity > 0: create 2*capacity events and start recording (earlier records

@@ -242,6 +242,69 @@ int pfa_first_two_layers(const pfa_shape* shape, int32_t shift1, int32_t shift2,
     return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
 }
 
+int64_t pfa_sparse_layer_backward_workspace(const pfa_shape* shape, int32_t K_l) {
+    Geom g;
+    int code;
+    if (!geom_from_shape(shape, &g, &code)) return code;
+    if (K_l < 1 || K_l > g.N) return PFA_ERR_INVALID;
+    return n_wh(g) * g.N * (int64_t)K_l * 4;
+}
+
+int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void* K, const void* V,
+                              const int32_t* I_prev, const float* A_prev, int32_t K_prev, int32_t K_l,
+                              const int32_t* I_l, const float* A_l, const float* dO, const float* dA_l,
+                              float* dQ, float* dK, float* dV, float* dA_prev, void* workspace,
+                              int64_t workspace_bytes, void* stream) {
+    Geom g;
+    int code;
+    if (!geom_from_shape(shape, &g, &code)) return code;
+    if (g.win == 0) return PFA_ERR_UNSUPPORTED;
+    if (!Q || !K || !V || !I_l || !A_l || !dO || !dQ || !dK || !dV || !workspace) return PFA_ERR_INVALID;
+    if (K_prev < 1 || K_prev > g.N || K_l < 1 || K_l > K_prev) return PFA_ERR_INVALID;
+    if (!I_prev && K_prev != g.N) return PFA_ERR_INVALID;
+    if (dA_prev && !A_prev) return PFA_ERR_INVALID;
+    if (workspace_bytes < n_wh(g) * g.N * (int64_t)K_l * 4) return PFA_ERR_INVALID;
+    if (K_l > 256) return PFA_ERR_UNSUPPORTED;
+    if ((int64_t)g.N * K_l * 4 > 0x7FFFFFF0) return PFA_ERR_UNSUPPORTED;
+    const int parts = pfa::backward_scatter_parts(g.d, g.N, K_l);
+    if (parts == 0) return PFA_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    pfa::BackwardArgs a;
+    a.Q = Q; a.K = K; a.V = V;
+    a.I_prev = I_prev; a.A_prev = A_prev;
+    a.I_l = I_l; a.A_l = A_l;
+    a.dO = dO; a.dA_l = dA_l;
+    a.dQ = dQ; a.dK = dK; a.dV = dV; a.dA_prev = dA_prev;
+    a.g_buf = static_cast<float*>(workspace);
+    a.g = g;
+    a.K_prev = K_prev; a.K_l = K_l;
+    a.xcd_map = (n_wh(g) % 8 == 0) ? 1 : 0;
+    a.scale = (float)(1.0 / sqrt((double)g.d));
+    a.blocks_per_wh = g.N >= 512 ? 2 : 1;
+    a.rows_per_block = (g.N + a.blocks_per_wh - 1) / a.blocks_per_wh;
+    const int64_t rgrid = n_wh(g) * a.blocks_per_wh;
+    const int64_t sgrid = n_wh(g) * parts;
+    if (rgrid > 0x7fffffff || sgrid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
+    const int dt = shape->dtype;
+    hipError_t e;
+    if (pfa::backward_fused_rows(dt, g.d, g.N, K_l, dA_prev != nullptr)) {
+        e = timed(PFA_KERNEL_BWD_ROWS, s, [&] { return pfa::launch_backward_rows(a, dt, g.d, true, true, (int)rgrid, s); });
+    } else {
+        e = timed(PFA_KERNEL_BWD_ROWS, s, [&] { return pfa::launch_backward_rows(a, dt, g.d, true, false, (int)rgrid, s); });
+        if (e == hipSuccess)
+            e = timed(PFA_KERNEL_BWD_ROWS, s,
+                      [&] { return pfa::launch_backward_rows(a, dt, g.d, false, true, (int)rgrid, s); });
+    }
+    if (e == hipSuccess) {
+        pfa::BackwardArgs b = a;
+        b.blocks_per_wh = parts;
+        b.rows_per_block = g.N;
+        e = timed(PFA_KERNEL_BWD_SCATTER, s, [&] { return pfa::launch_backward_scatter(b, dt, g.d, (int)sgrid, s); });
+    }
+    return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
+}
+
 const char* pfa_strerror(int code) {
     switch (code) {
         case PFA_OK: return "ok";
@@ -297,6 +360,8 @@ const char* pfa_kernel_name(int32_t kind) {
         case PFA_KERNEL_SELECT: return "sparse_layer_kernel(select)";
         case PFA_KERNEL_AGGREGATE: return "aggregate";
         case PFA_KERNEL_IOTA: return "iota_rows_kernel";
+        case PFA_KERNEL_BWD_ROWS: return "bwd_rows_kernel";
+        case PFA_KERNEL_BWD_SCATTER: return "bwd_scatter_kernel";
         default: return "unknown";
     }
 }

@@ -1,0 +1,442 @@
+// Backward pass of a window-mode sparse PFA layer on gfx950, kept sets fixed.
+//
+// Forward, per query slot i with kept slots r = 1..K_l (paper notes "Progressive
+// Focused Transformer for Single Image Super-Resolution", sections "Progressive
+// attention across layers" and "Sparse matrix multiplication"):
+//   A_ir = A^{l-1}_ir exp(s_ir) / sum_kept A^{l-1} exp(s),  s_ir = q_i.k_j / sqrt(d),
+//   O_i  = sum_r A_ir v_j.
+// Both normalisations and the softmax denominator over the candidate list are
+// row constants, so A^l is a softmax over the kept slots of the log-domain key
+// s + ln A^{l-1}. With G_ir = dA_ir + dO_i.v_j and g_ir = G_ir - sum_r A_ir G_ir:
+//   dkey_ir     = A_ir g_ir                     (softmax backward)
+//   dQ_i        = sum_r dkey_ir k_j / sqrt(d)
+//   dK_j       += dkey_ir q_i / sqrt(d)
+//   dV_j       += A_ir dO_i
+//   dA^{l-1}_ir = dkey_ir / A^{l-1}_ir  at kept slots, 0 at dropped ones.
+//
+// Kernels.
+// * bwd_rows_kernel: one group of GL lanes per query row; CH lanes split each
+//   16-byte chunked V/K row (CH = row bytes / 16) and a subgroup of CH lanes
+//   takes 4 consecutive kept slots at a time. Pass V: gather v_j from LDS, dot
+//   with dO_i (chunk sums by DPP quad exchanges and a half-row mirror), row sum
+//   D_i, g written to a workspace. Pass K: gather k_j from LDS, dQ_i, and
+//   dA^{l-1}: kept tokens are marked in a per-row LDS bitmap, the I^{l-1} row is
+//   scanned in slot order, and the r-th marked slot takes kept entry r (I^l is
+//   a subsequence of I^{l-1} in its order). When K and V fit in LDS together
+//   both passes run in one kernel, keeping G in registers.
+// * bwd_scatter_kernel: dK and dV accumulate in LDS (fp32, DH of the d columns
+//   per workgroup) with ds_add_f32; each wave stages one row's (j, A, A g/sqrt(d))
+//   in LDS and its lanes cover (4 or 2 kept slots) x DH columns per atomic.
+#include "pfa_kernels.h"
+#include "pfa_rows.h"
+
+namespace pfa {
+namespace {
+
+constexpr int kBwdRowWaves = 16;
+constexpr int kBwdScatterWaves = 8;
+
+// sum over the CH consecutive lanes that share a kept slot (CH = 2, 4 or 8)
+template <int CH>
+__device__ __forceinline__ float chunk_sum(float v) {
+    if (CH >= 2) v += dppf<kQuadXor1>(v);
+    if (CH >= 4) v += dppf<kQuadXor2>(v);
+    if (CH >= 8) v += dppf<kRowHalfMirror>(v);
+    return v;
+}
+
+// sum over the lanes of a GL-lane group that hold the same chunk (lane bits
+// [log2 CH, log2 GL)); once per row, so plain cross-lane shuffles
+template <int CH, int GL>
+__device__ __forceinline__ float subgroup_sum(float v) {
+#pragma unroll
+    for (int o = CH; o < GL; o <<= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// bits of the wave mask m that belong to this lane's GL-lane group, and the
+// number of them below this lane
+template <int GL>
+__device__ __forceinline__ uint64_t group_bits(uint64_t m, int lane) {
+    if (GL == 64) return m;
+    return (m >> (lane & (64 - GL))) & ((1ull << GL) - 1ull);
+}
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_row_chunk(const T* row, int chunk, float (&o)[Chunk<T>::kElems]) {
+    Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(row) + chunk * 16), o);
+}
+
+template <typename T, int D, int GL, int NST, bool HAS_V, bool HAS_K>
+__global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const BackwardArgs p) {
+    constexpr int NW = kBwdRowWaves;
+    constexpr int EPC = Chunk<T>::kElems;   // elements per 16-byte chunk
+    constexpr int CH = D / EPC;             // chunks (lanes) per K/V row
+    constexpr int ROWB = D * (int)sizeof(T);
+    constexpr int GS = GL / CH;             // subgroups per row group
+    constexpr int RPW = kWave / GL;         // rows per wavefront
+    constexpr int KPL = 4 * NST;            // kept slots per lane
+    static_assert(CH >= 2 && CH <= 8 && GS >= 1, "row split");
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const Geom g = p.g;
+    const int N = g.N;
+    const int K_l = p.K_l;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int grp = lane / GL;
+    const int gl = lane & (GL - 1);
+    const int vchunk = gl % CH;
+    const int vsub = gl / CH;
+    const WhPart w = decode_block(p.blocks_per_wh, p.xcd_map, g);
+    const size_t plane = (size_t)w.bh * g.H * g.W * D;
+
+    unsigned char* Vs = smem;
+    unsigned char* Ks = smem + (HAS_V ? N * ROWB : 0);
+    const bool want_dap = HAS_K && p.dA_prev != nullptr;
+    const int bmw = (N + 31) >> 5;                       // bitmap words per row
+    const int rsw = bmw + ((K_l + 3) & ~3);              // row scratch words
+    uint32_t* bitmap = reinterpret_cast<uint32_t*>(smem + (HAS_V + HAS_K) * N * ROWB) + (wave * RPW + grp) * rsw;
+    float* vals = reinterpret_cast<float*>(bitmap + bmw);
+    if (HAS_V) stage_rows<T, D>(Vs, ROWB, static_cast<const T*>(p.V) + plane, g, w.wy, w.wx);
+    if (HAS_K) stage_rows<T, D>(Ks, ROWB, static_cast<const T*>(p.K) + plane, g, w.wy, w.wx);
+    __syncthreads();
+
+    const size_t wh_pairs = (size_t)w.wh * N * K_l;
+    const int pair_bytes = N * K_l * 4;
+    const __amdgpu_buffer_rsrc_t rI = make_rsrc(p.I_l + wh_pairs, pair_bytes);
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A_l + wh_pairs, pair_bytes);
+    const __amdgpu_buffer_rsrc_t rdA = make_rsrc(p.dA_l ? p.dA_l + wh_pairs : p.A_l, p.dA_l ? pair_bytes : 0);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g_buf + wh_pairs, pair_bytes);
+    const int row0 = w.part * p.rows_per_block;
+    const int row1 = min(N, row0 + p.rows_per_block);
+
+    for (int base = row0 + wave * RPW; base < row1; base += NW * RPW) {
+        const int i = base + grp;
+        const bool active = i < row1;
+        const int ii = active ? i : row0;          // idle groups work on a valid row and store nothing
+        const int qpix = slot_pixel(g, w.wy, w.wx, ii);
+        const int roff = ii * K_l * 4;             // byte offset of the row's kept slots
+
+        float G[HAS_V ? KPL : 1];
+        if (HAS_V) {
+            float dov[EPC];
+            const float* dor = p.dO + plane + (size_t)qpix * D + vchunk * EPC;
+#pragma unroll
+            for (int y = 0; y < EPC; y += 4) {
+                const float4 f = *reinterpret_cast<const float4*>(dor + y);
+                dov[y] = f.x; dov[y + 1] = f.y; dov[y + 2] = f.z; dov[y + 3] = f.w;
+            }
+            float dsum = 0.0f;
+#pragma unroll
+            for (int t = 0; t < NST; ++t) {
+                const int e0 = 4 * (vsub + GS * t);
+                const int off = roff + e0 * 4;
+                const uint4 j4 = load16(rI, off);
+                const uint4 a4 = load16(rA, off);
+                const uint4 d4 = p.dA_l ? load16(rdA, off) : make_uint4(0u, 0u, 0u, 0u);
+                const unsigned jv[4] = {j4.x, j4.y, j4.z, j4.w};
+                const float av[4] = {__uint_as_float(a4.x), __uint_as_float(a4.y), __uint_as_float(a4.z),
+                                     __uint_as_float(a4.w)};
+                const float dv[4] = {__uint_as_float(d4.x), __uint_as_float(d4.y), __uint_as_float(d4.z),
+                                     __uint_as_float(d4.w)};
+                float part[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int j = (int)min(jv[x], (unsigned)(N - 1));   // memory safety only
+                    float vf[EPC];
+                    Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(Vs + j * ROWB + vchunk * 16), vf);
+                    float s = 0.0f;
+#pragma unroll
+                    for (int y = 0; y < EPC; ++y) s = fmaf(dov[y], vf[y], s);
+                    part[x] = s;
+                }
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const bool valid = e0 + x < K_l;
+                    const float gx = valid ? dv[x] + chunk_sum<CH>(part[x]) : 0.0f;
+                    G[4 * t + x] = gx;
+                    dsum = fmaf(valid ? av[x] : 0.0f, gx, dsum);
+                }
+            }
+            const float Dsum = subgroup_sum<CH, GL>(dsum);
+#pragma unroll
+            for (int k = 0; k < KPL; ++k) G[k] -= Dsum;
+            // g for the scatter pass (and the K pass): lane x % CH of a subgroup stores slot x
+#pragma unroll
+            for (int t = 0; t < NST; ++t) {
+                const int e0 = 4 * (vsub + GS * t);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    if (x % CH != vchunk) continue;
+                    const bool st = active && e0 + x < K_l;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(G[4 * t + x]), rg,
+                                                          st ? roff + (e0 + x) * 4 : 0x7FFFFFF0, 0, 0);
+                }
+            }
+        }
+
+        if (HAS_K) {
+            float qv[EPC];
+            load_row_chunk<T, D>(static_cast<const T*>(p.Q) + plane + (size_t)qpix * D, vchunk, qv);
+            float dq[EPC];
+#pragma unroll
+            for (int y = 0; y < EPC; ++y) dq[y] = 0.0f;
+            if (want_dap) {
+                for (int u = gl; u < bmw; u += GL) bitmap[u] = 0u;
+            }
+            // without V in this kernel g comes from the workspace, one step at a time
+            // (a rolled loop keeps the loads of later steps from being hoisted)
+#pragma unroll (HAS_V ? NST : 1)
+            for (int t = 0; t < NST; ++t) {
+                const int e0 = 4 * (vsub + GS * t);
+                const int off = roff + e0 * 4;
+                const uint4 j4 = load16(rI, off);
+                const uint4 a4 = load16(rA, off);
+                float gv[4];
+                if (HAS_V) {
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) gv[x] = G[(4 * t + x) % KPL];
+                } else {
+                    const uint4 g4 = load16(rg, off);
+                    gv[0] = __uint_as_float(g4.x);
+                    gv[1] = __uint_as_float(g4.y);
+                    gv[2] = __uint_as_float(g4.z);
+                    gv[3] = __uint_as_float(g4.w);
+                }
+                const unsigned jv[4] = {j4.x, j4.y, j4.z, j4.w};
+                const float av[4] = {__uint_as_float(a4.x), __uint_as_float(a4.y), __uint_as_float(a4.z),
+                                     __uint_as_float(a4.w)};
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const bool valid = e0 + x < K_l;
+                    const int j = (int)min(jv[x], (unsigned)(N - 1));
+                    const float dkey = valid ? av[x] * gv[x] : 0.0f;
+                    float kf[EPC];
+                    Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(Ks + j * ROWB + vchunk * 16), kf);
+#pragma unroll
+                    for (int y = 0; y < EPC; ++y) dq[y] = fmaf(dkey, kf[y], dq[y]);
+                    if (want_dap && valid && x % CH == vchunk) {
+                        vals[e0 + x] = dkey;
+                        atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+                    }
+                }
+            }
+#pragma unroll
+            for (int y = 0; y < EPC; ++y) dq[y] = subgroup_sum<CH, GL>(dq[y]) * p.scale;
+            if (active && vsub == 0) {
+                float* qr = p.dQ + plane + (size_t)qpix * D + vchunk * EPC;
+#pragma unroll
+                for (int y = 0; y < EPC; y += 4)
+                    *reinterpret_cast<float4*>(qr + y) = make_float4(dq[y], dq[y + 1], dq[y + 2], dq[y + 3]);
+            }
+            if (want_dap) {
+                // the wave's LDS writes above complete before the scan reads them
+                __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                const int K_prev = p.K_prev;
+                const size_t srow = ((size_t)w.wh * N + ii) * K_prev;
+                int run = 0;
+                for (int s0 = 0; s0 < K_prev; s0 += GL) {
+                    const int slot = s0 + gl;
+                    const bool sv = slot < K_prev;
+                    int j = slot;
+                    float ap = 0.0f;
+                    if (sv) {
+                        if (p.I_prev) j = p.I_prev[srow + slot];
+                        ap = p.A_prev[srow + slot];
+                    }
+                    j = (int)min((unsigned)j, (unsigned)(N - 1));
+                    const bool kept = sv && ((bitmap[j >> 5] >> (j & 31)) & 1u);
+                    const uint64_t m = group_bits<GL>(ballot(kept), lane);
+                    const int rank = run + __builtin_popcountll(m & ((1ull << gl) - 1ull));
+                    run += __builtin_popcountll(m);
+                    float val = 0.0f;
+                    if (kept && rank < K_l && ap > 0.0f) val = vals[rank] / ap;
+                    if (active && sv) p.dA_prev[srow + slot] = val;
+                }
+            }
+        }
+    }
+}
+
+template <typename T, int D, int DH>
+__global__ __launch_bounds__(kBwdScatterWaves * kWave) void bwd_scatter_kernel(const BackwardArgs p) {
+    constexpr int NW = kBwdScatterWaves;
+    constexpr int PPI = kWave / DH;         // kept slots per atomic instruction
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const Geom g = p.g;
+    const int N = g.N;
+    const int K_l = p.K_l;
+    const int KLP = (K_l + 3) & ~3;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const WhPart w = decode_block(p.blocks_per_wh, p.xcd_map, g);   // part = column block
+    const size_t plane = (size_t)w.bh * g.H * g.W * D;
+    const int col0 = w.part * DH;
+
+    float* accV = reinterpret_cast<float*>(smem);
+    float* accK = accV + N * DH;
+    int* st_j = reinterpret_cast<int*>(accK + N * DH) + wave * 3 * KLP;
+    float* st_a = reinterpret_cast<float*>(st_j + KLP);
+    float* st_k = st_a + KLP;
+    for (int u = threadIdx.x * 4; u < 2 * N * DH; u += blockDim.x * 4)
+        *reinterpret_cast<float4*>(accV + u) = make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+
+    const size_t wh_pairs = (size_t)w.wh * N * K_l;
+    const int pair_bytes = N * K_l * 4;
+    const __amdgpu_buffer_rsrc_t rI = make_rsrc(p.I_l + wh_pairs, pair_bytes);
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A_l + wh_pairs, pair_bytes);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g_buf + wh_pairs, pair_bytes);
+    const int c = lane % DH;
+    const int ps = lane / DH;
+    const T* Qh = static_cast<const T*>(p.Q) + plane;
+    for (int i = wave; i < N; i += NW) {
+        const int qpix = slot_pixel(g, w.wy, w.wx, i);
+        const float dov = p.dO[plane + (size_t)qpix * D + col0 + c];
+        float qv;
+        if constexpr (sizeof(T) == 4) {
+            qv = reinterpret_cast<const float*>(Qh)[(size_t)qpix * D + col0 + c];
+        } else {
+            qv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(Qh)[(size_t)qpix * D + col0 + c] << 16);
+        }
+        const int roff = i * K_l * 4;
+        for (int e = lane * 4; e < K_l; e += 4 * kWave) {
+            const uint4 j4 = load16(rI, roff + e * 4);
+            const uint4 a4 = load16(rA, roff + e * 4);
+            const uint4 g4 = load16(rg, roff + e * 4);
+            const float a[4] = {__uint_as_float(a4.x), __uint_as_float(a4.y), __uint_as_float(a4.z),
+                                __uint_as_float(a4.w)};
+            const float gg[4] = {__uint_as_float(g4.x), __uint_as_float(g4.y), __uint_as_float(g4.z),
+                                 __uint_as_float(g4.w)};
+            *reinterpret_cast<uint4*>(st_j + e) = j4;
+            *reinterpret_cast<float4*>(st_a + e) = make_float4(a[0], a[1], a[2], a[3]);
+            *reinterpret_cast<float4*>(st_k + e) = make_float4(a[0] * gg[0] * p.scale, a[1] * gg[1] * p.scale,
+                                                               a[2] * gg[2] * p.scale, a[3] * gg[3] * p.scale);
+        }
+        for (int e0 = 0; e0 < K_l; e0 += PPI) {
+            const int e = e0 + ps;
+            if (e < K_l) {
+                const int j = (int)min((unsigned)st_j[e], (unsigned)(N - 1));
+                __hip_atomic_fetch_add(accV + j * DH + c, st_a[e] * dov, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_add(accK + j * DH + c, st_k[e] * qv, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
+    }
+    __syncthreads();
+    constexpr int C4 = DH / 4;
+    for (int u = threadIdx.x; u < N * C4; u += blockDim.x) {
+        const int t = u / C4;
+        const int cc = (u - t * C4) * 4;
+        const size_t o = plane + (size_t)slot_pixel(g, w.wy, w.wx, t) * D + col0 + cc;
+        *reinterpret_cast<float4*>(p.dV + o) = *reinterpret_cast<const float4*>(accV + t * DH + cc);
+        *reinterpret_cast<float4*>(p.dK + o) = *reinterpret_cast<const float4*>(accK + t * DH + cc);
+    }
+}
+
+template <class F>
+hipError_t launch_bwd(F fn, const BackwardArgs& a, int threads, int lds, int grid, hipStream_t s) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(threads), lds, s, a);
+    return hipGetLastError();
+}
+
+int chunks_per_row(int dtype, int D) { return D * (dtype == 0 ? 4 : 2) / 16; }
+
+// lanes per query row: the smallest of 16, 32, 64 covering ceil(K_l / 4) subgroups
+int rows_group(int CH, int K_l) {
+    const int need = CH * ((K_l + 3) / 4);
+    return need <= 16 ? 16 : need <= 32 ? 32 : 64;
+}
+
+int rows_lds(int dtype, int D, int N, int K_l, bool has_v, bool has_k, bool want_dap) {
+    const int rowb = D * (dtype == 0 ? 4 : 2);
+    const int gl = rows_group(chunks_per_row(dtype, D), K_l);
+    const int rsw = (N + 31) / 32 + ((K_l + 3) & ~3);
+    return ((has_v ? 1 : 0) + (has_k ? 1 : 0)) * N * rowb +
+           ((has_k && want_dap) ? kBwdRowWaves * (64 / gl) * rsw * 4 : 0);
+}
+
+template <typename T, int D, bool HV, bool HK>
+hipError_t launch_rows_mode(const BackwardArgs& a, int grid, hipStream_t s) {
+    constexpr int CH = D * (int)sizeof(T) / 16;
+    const int gl = rows_group(CH, a.K_l);
+    const int lds = rows_lds(sizeof(T) == 4 ? 0 : 1, D, a.g.N, a.K_l, HV, HK, a.dA_prev != nullptr);
+    const int th = kBwdRowWaves * kWave;
+    if (gl == 16) return launch_bwd(bwd_rows_kernel<T, D, 16, 1, HV, HK>, a, th, lds, grid, s);
+    if (gl == 32) return launch_bwd(bwd_rows_kernel<T, D, 32, 1, HV, HK>, a, th, lds, grid, s);
+    const int nst = (a.K_l + 4 * (64 / CH) - 1) / (4 * (64 / CH));
+    if (nst <= 1) return launch_bwd(bwd_rows_kernel<T, D, 64, 1, HV, HK>, a, th, lds, grid, s);
+    if (nst <= 2) return launch_bwd(bwd_rows_kernel<T, D, 64, 2, HV, HK>, a, th, lds, grid, s);
+    if (nst <= 4) return launch_bwd(bwd_rows_kernel<T, D, 64, 4, HV, HK>, a, th, lds, grid, s);
+    if constexpr (CH >= 8) {
+        if (nst <= 8) return launch_bwd(bwd_rows_kernel<T, D, 64, 8, HV, HK>, a, th, lds, grid, s);
+    }
+    return hipErrorInvalidValue;   // K_l beyond what the caller admits
+}
+
+template <typename T, int D>
+hipError_t launch_rows_t(const BackwardArgs& a, bool has_v, bool has_k, int grid, hipStream_t s) {
+    if (has_v && has_k) return launch_rows_mode<T, D, true, true>(a, grid, s);
+    if (has_v) return launch_rows_mode<T, D, true, false>(a, grid, s);
+    return launch_rows_mode<T, D, false, true>(a, grid, s);
+}
+
+int scatter_lds(int DH, int N, int K_l) {
+    return 2 * N * DH * 4 + kBwdScatterWaves * 3 * ((K_l + 3) & ~3) * 4;
+}
+
+template <typename T, int D>
+hipError_t launch_scatter_t(const BackwardArgs& a, int grid, hipStream_t s) {
+    const int th = kBwdScatterWaves * kWave;
+    if (a.blocks_per_wh == 1)
+        return launch_bwd(bwd_scatter_kernel<T, D, D>, a, th, scatter_lds(D, a.g.N, a.K_l), grid, s);
+    if (a.blocks_per_wh == 2)
+        return launch_bwd(bwd_scatter_kernel<T, D, D / 2>, a, th, scatter_lds(D / 2, a.g.N, a.K_l), grid, s);
+    return launch_bwd(bwd_scatter_kernel<T, D, D / 4>, a, th, scatter_lds(D / 4, a.g.N, a.K_l), grid, s);
+}
+
+}  // namespace
+
+int backward_fused_rows(int dtype, int D, int N, int K_l, bool want_dap) {
+    // one kernel when K and V fit in LDS together and G stays within registers
+    // (at most 16 kept slots per lane)
+    const int CH = chunks_per_row(dtype, D);
+    const int per_lane = 4 * ((K_l + 4 * (64 / CH) - 1) / (4 * (64 / CH)));
+    if (per_lane > 16) return 0;
+    return rows_lds(dtype, D, N, K_l, true, true, want_dap) <= kLdsBytes ? 1 : 0;
+}
+
+int backward_scatter_parts(int D, int N, int K_l) {
+    for (int parts = 1; parts <= 4; parts *= 2)
+        if (scatter_lds(D / parts, N, K_l) <= kLdsBytes) return parts;
+    return 0;
+}
+
+hipError_t launch_backward_rows(const BackwardArgs& a, int dtype, int D, bool has_v, bool has_k, int grid,
+                                hipStream_t stream) {
+    if (rows_lds(dtype, D, a.g.N, a.K_l, has_v, has_k, a.dA_prev != nullptr) > kLdsBytes) return hipErrorInvalidValue;
+    if (dtype == 0)
+        return D == 16 ? launch_rows_t<float, 16>(a, has_v, has_k, grid, stream)
+                       : launch_rows_t<float, 32>(a, has_v, has_k, grid, stream);
+    return D == 16 ? launch_rows_t<uint16_t, 16>(a, has_v, has_k, grid, stream)
+                   : launch_rows_t<uint16_t, 32>(a, has_v, has_k, grid, stream);
+}
+
+hipError_t launch_backward_scatter(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream) {
+    if (dtype == 0)
+        return D == 16 ? launch_scatter_t<float, 16>(a, grid, stream) : launch_scatter_t<float, 32>(a, grid, stream);
+    return D == 16 ? launch_scatter_t<uint16_t, 16>(a, grid, stream) : launch_scatter_t<uint16_t, 32>(a, grid, stream);
+}
+
+}  // namespace pfa

@@ -50,6 +50,39 @@ struct DenseArgs {
     int xcd_map;             // 1: the query blocks of a window-head run on one XCD (needs #wh % 8 == 0)
 };
 
+// Backward pass of a window-mode sparse layer with the kept sets held fixed.
+struct BackwardArgs {
+    const void* Q;
+    const void* K;
+    const void* V;
+    const int32_t* I_prev;   // nullptr: slot p holds token p (K_prev == N)
+    const float* A_prev;     // read only when dA_prev is written
+    const int32_t* I_l;      // the layer's kept slots [wh, N, K_l]
+    const float* A_l;        // the layer's map [wh, N, K_l]
+    const float* dO;         // [B, heads, H, W, d]
+    const float* dA_l;       // [wh, N, K_l] or nullptr (zero)
+    float* dQ;
+    float* dK;
+    float* dV;
+    float* dA_prev;          // [wh, N, K_prev] or nullptr (not wanted)
+    float* g_buf;            // workspace [wh, N, K_l]: G_ij - sum_j A_ij G_ij
+    Geom g;
+    int K_prev, K_l;
+    int rows_per_block, blocks_per_wh;
+    int xcd_map;
+    float scale;             // 1 / sqrt(d)
+};
+
+// Row pass: with both K and V staged (when they fit in LDS together), or as a
+// V pass (g rows) followed by a K pass (dQ, dA_prev). `parts` = workgroups per
+// window-head for the scatter pass.
+int backward_fused_rows(int dtype, int D, int N, int K_l, bool want_dA_prev);
+hipError_t launch_backward_rows(const BackwardArgs& a, int dtype, int D, bool has_v, bool has_k, int grid,
+                                hipStream_t stream);
+// dK and dV: per window-head LDS accumulators, D/parts columns per workgroup.
+int backward_scatter_parts(int D, int N, int K_l);
+hipError_t launch_backward_scatter(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream);
+
 hipError_t launch_sparse(const SparseArgs& a, int dtype, int D, SparseMode mode, int lds_bytes, int grid,
                          hipStream_t stream);
 // All-candidates layer (I^{l-1} implicit, K_prev = N = 1024): MFMA scores, selection only.

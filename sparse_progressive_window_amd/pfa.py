@@ -44,6 +44,11 @@ def load():
         lib.pfa_first_two_layers.argtypes = [ctypes.POINTER(PfaShape), i32, i32, P, P, P, P, P, P, i32, P, P, P, P,
                                              P, P]
         lib.pfa_first_two_layers.restype = ctypes.c_int
+        lib.pfa_sparse_layer_backward.argtypes = ([ctypes.POINTER(PfaShape), P, P, P, P, P, i32, i32]
+                                                  + [P] * 9 + [ctypes.c_int64, P])
+        lib.pfa_sparse_layer_backward.restype = ctypes.c_int
+        lib.pfa_sparse_layer_backward_workspace.argtypes = [ctypes.POINTER(PfaShape), i32]
+        lib.pfa_sparse_layer_backward_workspace.restype = ctypes.c_int64
         lib.pfa_strerror.argtypes = [ctypes.c_int]
         lib.pfa_strerror.restype = ctypes.c_char_p
         lib.pfa_version.restype = ctypes.c_int
@@ -210,7 +215,64 @@ def first_two_layers(Q1, K1, V1, Q2, K2, V2, K2_keep, *, win, shift1=0, shift2=0
     return O1, I2, A2, O2
 
 
-KERNEL_KINDS = ("dense", "all_candidates", "sparse", "select", "aggregate", "iota")
+def sparse_layer_backward(Q, K, V, I_prev, A_prev, I_l, A_l, dO, dA_l=None, *, win, shift=0, K_prev=None,
+                          want_dA_prev=True, out=None, workspace=None):
+    """Backward pass of a window-mode sparse layer with its kept sets fixed.
+
+    Q, K, V, I_prev (None = every slot), A_prev: the forward call's inputs;
+    I_l, A_l: its outputs; dO: fp32 gradient of O; dA_l: fp32 gradient of A^l or
+    None. Returns (dQ, dK, dV, dA_prev) in fp32; dA_prev is None when not wanted
+    (or A_prev is None). ``out`` = optional preallocated (dQ, dK, dV, dA_prev or
+    None); ``workspace`` = optional uint8 device tensor of at least
+    ``backward_workspace_bytes`` bytes."""
+    _check_qkv(Q, K, V)
+    lead, N = _geometry(Q, win)
+    K_l = I_l.shape[-1]
+    if I_prev is not None:
+        K_prev = I_prev.shape[-1]
+    elif K_prev is None:
+        K_prev = N
+    dev = Q.device
+    want = want_dA_prev and A_prev is not None
+    if out is None:
+        dQ, dK, dV = (torch.empty(Q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+        dAp = torch.empty(lead + (N, K_prev), dtype=torch.float32, device=dev) if want else None
+    else:
+        dQ, dK, dV, dAp = out
+    rows = _prod(lead) * N
+    _expect(I_prev, rows * K_prev, torch.int32, "I_prev")
+    _expect(A_prev, rows * K_prev, torch.float32, "A_prev")
+    _expect(I_l, rows * K_l, torch.int32, "I_l")
+    _expect(A_l, rows * K_l, torch.float32, "A_l")
+    _expect(dO, Q.numel(), torch.float32, "dO")
+    _expect(dA_l, rows * K_l, torch.float32, "dA_l")
+    for t, n in ((dQ, "dQ"), (dK, "dK"), (dV, "dV")):
+        _expect(t, Q.numel(), torch.float32, n)
+    _expect(dAp, rows * K_prev, torch.float32, "dA_prev")
+    shape = make_shape(Q, win, shift)
+    need = backward_workspace_bytes(Q, K_l, win=win, shift=shift)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must be a device tensor of at least {need} bytes")
+    rc = load().pfa_sparse_layer_backward(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(I_prev),
+                                          _ptr(A_prev), K_prev, K_l, _ptr(I_l), _ptr(A_l), _ptr(dO), _ptr(dA_l),
+                                          _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dAp), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream())
+    if rc != 0:
+        raise PfaError("pfa_sparse_layer_backward", rc)
+    return dQ, dK, dV, dAp
+
+
+def backward_workspace_bytes(Q, K_l, *, win, shift=0) -> int:
+    shape = make_shape(Q, win, shift)
+    n = int(load().pfa_sparse_layer_backward_workspace(ctypes.byref(shape), int(K_l)))
+    if n < 0:
+        raise PfaError("pfa_sparse_layer_backward_workspace", n)
+    return n
+
+
+KERNEL_KINDS = ("dense", "all_candidates", "sparse", "select", "aggregate", "iota", "bwd_rows", "bwd_scatter")
 
 
 def kernel_name(kind: int) -> str:

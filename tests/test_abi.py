@@ -30,8 +30,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"pfa_dense_layer", "pfa_sparse_layer", "pfa_first_two_layers", "pfa_strerror",
-            "pfa_version"} <= set(names)
+    assert {"pfa_dense_layer", "pfa_sparse_layer", "pfa_first_two_layers", "pfa_sparse_layer_backward",
+            "pfa_sparse_layer_backward_workspace", "pfa_strerror", "pfa_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -48,9 +48,10 @@ def test_timing_calls_without_device(lib):
     assert lib.pfa_timing_read(None, None, 0, None, None) == -1
     assert lib.pfa_timing_read(None, None, 4, ctypes.byref(n), None) == -1
     assert lib.pfa_timing_read(None, None, -1, ctypes.byref(n), None) == -1
-    names = [lib.pfa_kernel_name(k).decode() for k in range(6)]
+    names = [lib.pfa_kernel_name(k).decode() for k in range(8)]
     assert names == ["dense_layer_kernel", "all_cand", "sparse_layer_kernel",
-                     "sparse_layer_kernel(select)", "aggregate", "iota_rows_kernel"]
+                     "sparse_layer_kernel(select)", "aggregate", "iota_rows_kernel", "bwd_rows_kernel",
+                     "bwd_scatter_kernel"]
     assert lib.pfa_kernel_name(99) == b"unknown"
 
 
@@ -148,3 +149,30 @@ def test_first_two_layers_validation(lib):
     assert fused(shape()) == -2                                   # fp32, d = 32: K1 and K2 exceed LDS together
     assert fused(shape(win=16, H=32, W=32, **bf)) == -2           # N != 1024
     assert fused(shape(win=0, H=32, W=32, **bf)) == -2            # global mode
+
+
+def test_backward_validation(lib):
+    ws_full = 1 * 1 * 1024 * 64 * 4
+
+    def bwd(s, K_prev=256, K_l=64, I_prev=FAKE, A_prev=FAKE, dA_prev=FAKE, ws=FAKE, ws_bytes=ws_full,
+            grads=(FAKE, FAKE, FAKE), dO=FAKE):
+        return lib.pfa_sparse_layer_backward(ctypes.byref(s) if s is not None else None, FAKE, FAKE, FAKE, I_prev,
+                                             A_prev, K_prev, K_l, FAKE, FAKE, dO, None, *grads, dA_prev, ws,
+                                             ws_bytes, None)
+    assert bwd(None) == -1
+    assert bwd(shape(win=0)) == -2                               # window mode only
+    assert bwd(shape(d=8)) == -2
+    assert bwd(shape(), K_l=0) == -1
+    assert bwd(shape(), K_l=300, K_prev=256) == -1               # K_l > K_prev
+    assert bwd(shape(), K_prev=512, I_prev=None) == -1           # implicit list needs K_prev == N
+    assert bwd(shape(), A_prev=None) == -1                       # dA_prev needs A_prev
+    assert bwd(shape(), ws=None) == -1
+    assert bwd(shape(), ws_bytes=ws_full - 4) == -1              # workspace too small
+    assert bwd(shape(), dO=None) == -1
+    assert bwd(shape(), grads=(FAKE, None, FAKE)) == -1
+    assert bwd(shape(), K_prev=1024, K_l=512, I_prev=None, ws_bytes=1 << 30) == -2   # K_l > 256
+    assert lib.pfa_sparse_layer_backward_workspace(ctypes.byref(shape()), 64) == ws_full
+    assert lib.pfa_sparse_layer_backward_workspace(ctypes.byref(shape(B=2, heads=3, H=64, W=32)), 16) == \
+        2 * 3 * 2 * 1024 * 16 * 4
+    assert lib.pfa_sparse_layer_backward_workspace(ctypes.byref(shape()), 0) == -1
+    assert lib.pfa_sparse_layer_backward_workspace(ctypes.byref(shape(d=8)), 16) == -2

@@ -1,0 +1,209 @@
+"""GPU parity of the sparse-layer backward pass (through the C ABI) against the
+fp64 backward oracle (``oracle.layer_backward``), whose pins are in
+tests/test_oracle_backward_pins.py.
+
+Both sides take the GPU forward's kept sets I^l (the backward holds them
+fixed); the GPU also takes the forward's A^l, the oracle recomputes it in fp64
+from Q, K and A^{l-1}.
+
+Rules (a reading of the forward's tolerances for gradients, which the pages do
+not cover): tol = 1e-5 for fp32 inputs, 2e-3 for bf16 inputs;
+  * dQ, dK, dV: per window-head, max |gpu - ref| over the window's pixels and
+    the d columns <= tol * max |ref| over the same set (norm-relative: the
+    gradients are sums with cancellation, so elementwise relative error is
+    ill-posed where an entry is near zero);
+  * dA^{l-1}: per row, max |gpu - ref| <= tol * max |ref row|, and exactly 0
+    at every slot the layer dropped.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_progressive_window_amd import inputs, pfa, workloads
+from tests import parity
+from tests.test_gpu_workloads import sample_wh, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def window_pixels(wh, heads, H, W, win, shift):
+    """(b, h, y, x) index arrays of the N slots of window-head `wh`, slot order."""
+    nwy, nwx = H // win, W // win
+    wx = wh % nwx
+    wy = (wh // nwx) % nwy
+    h = (wh // (nwx * nwy)) % heads
+    b = wh // (nwx * nwy * heads)
+    t = np.arange(win * win)
+    y = (wy * win + t // win + shift) % H
+    x = (wx * win + t % win + shift) % W
+    return b, h, y, x
+
+
+def check_grads(gpu, ref, wh_list, heads, win, shift, tol):
+    """dQ/dK/dV dicts of [B, heads, H, W, d] arrays; returns the worst ratios."""
+    H, W = ref["dQ"].shape[2:4]
+    worst = {}
+    for name in ("dQ", "dK", "dV"):
+        g = np.asarray(gpu[name], dtype=np.float64)
+        r = ref[name]
+        w_max = 0.0
+        for wh in wh_list:
+            b, h, y, x = window_pixels(int(wh), heads, H, W, win, shift)
+            err = np.abs(g[b, h, y, x] - r[b, h, y, x]).max()
+            scale = np.abs(r[b, h, y, x]).max()
+            assert err <= tol * scale + 1e-30, f"{name} window-head {wh}: {err / scale:.3e} > {tol}"
+            w_max = max(w_max, float(err / max(scale, 1e-30)))
+        worst[name] = w_max
+    return worst
+
+
+def check_dA_prev(gpu, ref, tol):
+    """gpu, ref: [n, N, K_prev] (ref fp64)."""
+    g = np.asarray(gpu, dtype=np.float64)
+    dropped = ref == 0.0
+    assert (g[dropped] == 0.0).all(), "nonzero gradient at a dropped slot"
+    err = np.abs(g - ref).max(axis=-1)
+    scale = np.abs(ref).max(axis=-1)
+    ok = err <= tol * scale + 1e-30
+    worst = float((err / np.maximum(scale, 1e-30)).max())
+    assert ok.all(), f"dA_prev mismatch: worst row {worst:.3e} > {tol}"
+    return worst
+
+
+def rand_lists(n_rows, N, K_prev, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    return np.stack([g.permutation(N)[:K_prev] for _ in range(n_rows)]).astype(np.int32)
+
+
+def rand_map(shape, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    a = g.random(shape) + 1e-3
+    return (a / a.sum(axis=-1, keepdims=True)).astype(np.float32)
+
+
+def run_case(B, heads, H, W, d, win, shift, K_prev, K_l, dtype, seed, *, implicit=False, with_dA=True,
+             want_dA_prev=True):
+    shape = (B, heads, H, W, d)
+    qt, kt, vt = (inputs.draw(seed + t, shape, dtype) for t in range(3))
+    N = win * win
+    nwin = (H // win) * (W // win)
+    n_wh = B * heads * nwin
+    lead = (B, heads, nwin)
+    I_prev = None if implicit else rand_lists(n_wh * N, N, K_prev, seed + 5).reshape(lead + (N, K_prev))
+    A_prev = rand_map(lead + (N, K_prev), seed + 6)
+    Qd, Kd, Vd = to_dev(qt), to_dev(kt), to_dev(vt)
+    Ipd = None if I_prev is None else torch.from_numpy(I_prev).cuda()
+    Apd = torch.from_numpy(A_prev).cuda()
+    I_l, A_l, _ = pfa.sparse_layer(Qd, Kd, Vd, Ipd, Apd, K_l, win=win, shift=shift, K_prev=K_prev)
+    dO = inputs.draw(seed + 7, shape, "f32").exact
+    dA = inputs.draw(seed + 8, lead + (N, K_l), "f32").exact if with_dA else None
+    dQ, dK, dV, dAp = pfa.sparse_layer_backward(
+        Qd, Kd, Vd, Ipd, Apd, I_l, A_l, torch.from_numpy(dO).cuda(),
+        None if dA is None else torch.from_numpy(dA).cuda(), win=win, shift=shift, K_prev=K_prev,
+        want_dA_prev=want_dA_prev)
+    torch.cuda.synchronize()
+    keep = I_l.view(n_wh, N, K_l).cpu().numpy()
+    ref = oracle.layer_backward(qt.exact, kt.exact, vt.exact, win=win, shift=shift, keep=keep, dO=dO,
+                                dA=None if dA is None else dA.reshape(n_wh, N, K_l),
+                                I_prev=None if I_prev is None else I_prev.reshape(n_wh, N, K_prev),
+                                A_prev=A_prev.reshape(n_wh, N, K_prev), prev_compact=True)
+    tol = parity.TOL[dtype]
+    gpu = {"dQ": dQ.cpu().numpy(), "dK": dK.cpu().numpy(), "dV": dV.cpu().numpy()}
+    st = check_grads(gpu, ref, range(n_wh), heads, win, shift, tol)
+    if want_dA_prev:
+        st["dA_prev"] = check_dA_prev(dAp.view(n_wh, N, K_prev).cpu().numpy(), ref["dA_prev"], tol)
+    else:
+        assert dAp is None
+    return st
+
+
+CASES = [
+    # dtype, d, win, shift, K_prev, K_l, implicit, with_dA
+    ("f32", 32, 32, 16, 1024, 256, True, True),     # K and V passes in two kernels, dK/dV in column halves
+    ("bf16", 32, 32, 16, 1024, 256, True, True),    # one row kernel with K and V in LDS
+    ("f32", 16, 32, 0, 1024, 256, True, False),
+    ("bf16", 16, 32, 16, 256, 128, False, True),
+    ("f32", 32, 32, 16, 256, 128, False, True),
+    ("f32", 32, 32, 0, 128, 64, False, True),
+    ("bf16", 32, 32, 16, 64, 32, False, True),
+    ("f32", 32, 32, 16, 32, 16, False, True),
+    ("bf16", 32, 32, 0, 12, 5, False, True),        # ragged K_l (rows not 16-byte aligned)
+    ("f32", 32, 16, 8, 256, 256, False, True),      # N = 256, nothing dropped
+    ("f32", 16, 8, 4, 64, 13, False, False),        # N = 64
+    ("bf16", 16, 16, 0, 100, 37, False, True),
+]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,d,win,shift,K_prev,K_l,implicit,with_dA", CASES)
+def test_backward_random(dtype, d, win, shift, K_prev, K_l, implicit, with_dA, capsys):
+    H = W = 2 * win
+    st = run_case(1, 2, H, W, d, win, shift, K_prev, K_l, dtype, 700 + K_l + d, implicit=implicit,
+                  with_dA=with_dA)
+    with capsys.disabled():
+        print(f"  backward {dtype} d={d} win={win} K {K_prev}->{K_l}: {st}", flush=True)
+
+
+@pytest.mark.timeout(300)
+def test_backward_without_dA_prev():
+    run_case(1, 2, 64, 64, 32, 32, 16, 256, 64, "f32", 811, want_dA_prev=False)
+
+
+@pytest.mark.timeout(300)
+def test_backward_kernel_timing_records():
+    pfa.timing_enable(16)
+    try:
+        run_case(1, 1, 32, 32, 32, 32, 0, 1024, 256, "f32", 901, implicit=True)
+        recs, dropped = pfa.timing_read()
+    finally:
+        pfa.timing_enable(0)
+    kinds = [k for k, _ in recs]
+    assert kinds[-3:] == [6, 6, 7], kinds          # V pass, K pass, scatter (fp32, d = 32)
+    assert dropped == 0 and all(ms > 0 for _, ms in recs)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,layers", [(workloads.PATCH64.name, (1, 2)), (workloads.MAP256.name, (1, 2))])
+def test_backward_full_size(name, layers, capsys):
+    """Full-size workload: the GPU runs the forward chain through each listed
+    layer and that layer's backward for every window-head; the oracle checks 12
+    sampled window-heads."""
+    w = workloads.BY_NAME[name]
+    sel = sample_wh(w, 12)
+    N = w.N
+    lead = (w.B, w.heads, w.n_windows)
+    tol = parity.TOL[w.dtype]
+    I_g = A_g = None
+    for l in range(max(layers) + 1):
+        qkv = inputs.qkv(w, 0, l)
+        Qd, Kd, Vd = (to_dev(t) for t in qkv)
+        if l == 0:
+            _, A, _ = pfa.dense_layer(Qd, Kd, Vd, win=w.win, shift=w.shifts[0], want_A=True)
+            I = None
+        else:
+            I, A, _ = pfa.sparse_layer(Qd, Kd, Vd, I_g, A_g, w.K[l], win=w.win, shift=w.shifts[l],
+                                       K_prev=w.K[l - 1])
+        if l in layers:
+            K_prev, K_l = w.K[l - 1], w.K[l]
+            dO = torch.randn(Qd.shape, generator=torch.Generator().manual_seed(50 + l)).cuda()
+            dA = torch.randn(lead + (N, K_l), generator=torch.Generator().manual_seed(60 + l)).cuda()
+            dQ, dK, dV, dAp = pfa.sparse_layer_backward(Qd, Kd, Vd, I_g, A_g, I, A, dO, dA, win=w.win,
+                                                        shift=w.shifts[l], K_prev=K_prev)
+            torch.cuda.synchronize()
+            selt = torch.from_numpy(sel).cuda()
+            keep = I.view(-1, N, K_l)[selt].cpu().numpy()
+            Ip = None if I_g is None else I_g.view(-1, N, K_prev)[selt].cpu().numpy()
+            Ap = A_g.view(-1, N, K_prev)[selt].cpu().numpy()
+            ref = oracle.layer_backward(qkv[0].exact, qkv[1].exact, qkv[2].exact, win=w.win, shift=w.shifts[l],
+                                        keep=keep, dO=dO.cpu().numpy(), dA=dA.view(-1, N, K_l)[selt].cpu().numpy(),
+                                        I_prev=Ip, A_prev=Ap, prev_compact=True, wh_list=sel)
+            gpu = {"dQ": dQ.cpu().numpy(), "dK": dK.cpu().numpy(), "dV": dV.cpu().numpy()}
+            st = check_grads(gpu, ref, sel, w.heads, w.win, w.shifts[l], tol)
+            st["dA_prev"] = check_dA_prev(dAp.view(-1, N, K_prev)[selt].cpu().numpy(), ref["dA_prev"], tol)
+            with capsys.disabled():
+                print(f"  {w.name} layer {l + 1} backward: {st}", flush=True)
+            del dQ, dK, dV, dAp
+        I_g, A_g = I, A
+        del Qd, Kd, Vd
