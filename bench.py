@@ -29,7 +29,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 COUNTERS_FILE = "hbm_counters_{workload}.md"
 
 # kernel kinds of the library's timing calls (pfa_kernel_kind)
-DENSE, ALL_CAND, SPARSE, SELECT, AGGREGATE, IOTA = range(6)
+DENSE, ALL_CAND, SPARSE, SELECT, AGGREGATE, IOTA, BWD_ROWS, BWD_SCATTER = range(8)
 
 
 def kernel_bytes(w, l, kind, i_prev_implicit, split, fused=False):
@@ -74,6 +74,28 @@ def kernel_flops(w, l, kind, split):
     return 2 * d * N * K_prev + 2 * d * N * K_l
 
 
+def bwd_kernel_bytes(w, l, part, i_prev_implicit):
+    """Algorithmic HBM bytes per window-head of one backward launch of layer l
+    (0-based): each kernel's own inputs read once and outputs written once,
+    including the per-pair workspace g. part: "V" (G, g), "K" (dQ, dA^{l-1}),
+    "KV" (both in one kernel) or "scatter" (dK, dV from A, g, Q, dO)."""
+    N, d = w.N, w.d
+    x = N * d * (4 if w.dtype == "f32" else 2)
+    f = N * d * 4
+    K_prev, K_l = w.K[l - 1], w.K[l]
+    pairs = N * K_l * 4
+    prev = N * K_prev * 4
+    ip = 0 if i_prev_implicit else prev
+    dA = pairs if l < w.layers - 1 else 0      # the last layer's map has no consumer
+    if part == "V":
+        return x + 2 * pairs + dA + f + pairs
+    if part == "K":
+        return 2 * x + 3 * pairs + ip + prev + f + prev
+    if part == "KV":
+        return 3 * x + 2 * pairs + dA + f + pairs + ip + prev + f + prev
+    return x + 3 * pairs + f + 2 * f
+
+
 def stored_traffic(workload, kernel, layer):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when there is none or the kernel sources changed since it was taken."""
@@ -104,6 +126,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=256, help="window-heads timed on the CPU oracle")
     ap.add_argument("--fused12", action="store_true",
                     help="run layers 1-2 fused without materialising A^1 (bf16, or fp32 with d = 16)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward leg (layers L..2 of the sparse-layer backward, timed separately)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -243,9 +267,86 @@ def main():
         "roofline": roof, "layers": layers, "kernels": kernels,
     }
 
+    if not args.no_backward and not fused:
+        try:
+            result["backward"] = backward_leg(w, qkv, outs, implicit, args, torch, pfa)
+        except Exception as e:   # the forward line stands on its own
+            result["backward"] = {"error": repr(e)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_sample)
     print(json.dumps(result), flush=True)
+
+
+def backward_leg(w, qkv, outs, implicit, args, torch, pfa):
+    """Backward of the sparse layers L..2 of the chain just run (kept sets from
+    its forward outputs), each layer taking the next one's dA^{l} output and a
+    seeded dO; timed like the forward step, per kernel with HIP events."""
+    dev = qkv[0][0].device
+    L, N = w.layers, w.N
+    lead = (w.B, w.heads, w.n_windows)
+    g = torch.Generator(device="cpu").manual_seed(4242)
+    dO = [torch.randn(qkv[l][0].shape, generator=g).to(dev) for l in range(L)]
+    grads = [tuple(torch.empty(qkv[l][0].shape, dtype=torch.float32, device=dev) for _ in range(3))
+             for l in range(L)]
+    dA_prev = [None] + [torch.empty(lead + (N, w.K[l - 1]), dtype=torch.float32, device=dev) for l in range(1, L)]
+    ws = torch.empty(max(pfa.backward_workspace_bytes(qkv[l][0], w.K[l], win=w.win) for l in range(1, L)),
+                     dtype=torch.uint8, device=dev)
+
+    def bstep(marks=None):
+        for l in range(L - 1, 0, -1):
+            Q, K, V = qkv[l]
+            I_prev = None if implicit[l] else outs[l - 1][0]
+            dA = dA_prev[l + 1] if l + 1 < L else None
+            pfa.sparse_layer_backward(Q, K, V, I_prev, outs[l - 1][1], outs[l][0], outs[l][1], dO[l], dA,
+                                      win=w.win, shift=w.shifts[l], K_prev=w.K[l - 1],
+                                      out=grads[l] + (dA_prev[l],), workspace=ws)
+            if marks is not None:
+                marks.append(pfa.timing_count())
+
+    for _ in range(args.warmup):
+        bstep()
+    torch.cuda.synchronize()
+    pfa.timing_enable(args.steps * L * 3 + 64)
+    marks = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        bstep(marks)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    recs, dropped = pfa.timing_read(len(marks) * 4 + 64)
+    pfa.timing_enable(0)
+    assert dropped == 0 and len(recs) == marks[-1], (dropped, len(recs), marks[-1])
+    per = {}
+    start = 0
+    for i, end in enumerate(marks):
+        l = L - 1 - (i % (L - 1))
+        rows = [ms for kind, ms in recs[start:end] if kind == BWD_ROWS]
+        parts = ["V", "K"] if len(rows) == 2 else ["KV"]
+        for part, ms in zip(parts, rows):
+            per.setdefault((l, part), []).append(ms)
+        for kind, ms in recs[start:end]:
+            if kind == BWD_SCATTER:
+                per.setdefault((l, "scatter"), []).append(ms)
+        start = end
+    kernels = []
+    for (l, part), v in sorted(per.items()):
+        ms = float(np.mean(v))
+        by = bwd_kernel_bytes(w, l, part, implicit[l]) * w.n_wh
+        gbs = by / (ms * 1e-3) / 1e9
+        name = "bwd_dkv_kernel" if part == "scatter" else f"bwd_rows_kernel({part})"
+        kernels.append({"layer": l + 1, "kernel": name, "launches": len(v), "ms": round(ms, 4), "alg_bytes": by,
+                        "GB_per_s": round(gbs, 1), "bound": "hbm", "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    layer_ms = {l + 1: round(sum(k["ms"] for k in kernels if k["layer"] == l + 1), 4) for l in range(1, L)}
+    kept = sum(w.n_wh * N * w.K[l] for l in range(1, L))
+    dom = max(kernels, key=lambda k: k["ms"])
+    return {"ms_per_step": round(ms_per_step, 4), "layers": f"{L}..2", "layer_ms": layer_ms,
+            "kept_pairs_per_s": kept / (ms_per_step * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": dom["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dom["frac"], "traffic": stored_traffic(w.name, dom["kernel"], dom["layer"]),
+                         "kernel": dom["kernel"], "layer": dom["layer"], "ms_per_launch": dom["ms"],
+                         "alg_bytes_per_launch": dom["alg_bytes"]},
+            "kernels": kernels}
 
 
 def cpu_baseline(w, host, sample):

@@ -165,8 +165,9 @@ int pfa_first_two_layers(const pfa_shape* shape, int32_t shift1, int32_t shift2,
  * workspace  device buffer of at least pfa_sparse_layer_backward_workspace()
  *         bytes (one fp32 per kept pair), owned by the caller; its contents on
  *         entry do not matter and are overwritten.
- * Accumulation order in dK, dV is not fixed (LDS atomics): results may differ
- * between runs in the last bits.
+ * When N is not a multiple of 16, dK and dV are accumulated with LDS atomics
+ * in no fixed order, so results may differ between runs in the last bits;
+ * otherwise the backward pass is deterministic.
  * Errors: PFA_ERR_INVALID for NULL required pointers, inconsistent sizes,
  * dA_prev without A_prev, a workspace that is too small; PFA_ERR_UNSUPPORTED
  * for global mode, K_l > 256, and the shape limits of pfa_sparse_layer.
@@ -204,7 +205,8 @@ typedef enum {
     PFA_KERNEL_AGGREGATE = 4,      /* window mode: O from the stored (I^l, A^l) rows */
     PFA_KERNEL_IOTA = 5,           /* I rows 0..N-1 of the dense layer */
     PFA_KERNEL_BWD_ROWS = 6,       /* backward: per-row pass(es) -> g, dQ, dA_prev */
-    PFA_KERNEL_BWD_SCATTER = 7     /* backward: dK, dV accumulated per window-head */
+    PFA_KERNEL_BWD_SCATTER = 7     /* backward: dK, dV per window-head ("bwd_dkv_kernel" on MFMA,
+                                      "bwd_scatter_kernel" by LDS adds when N % 16 != 0) */
 } pfa_kernel_kind;
 
 /* capacity > 0: create 2*capacity events and start recording (earlier records

@@ -298,9 +298,16 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
     }
     if (e == hipSuccess) {
         pfa::BackwardArgs b = a;
-        b.blocks_per_wh = parts;
         b.rows_per_block = g.N;
-        e = timed(PFA_KERNEL_BWD_SCATTER, s, [&] { return pfa::launch_backward_scatter(b, dt, g.d, (int)sgrid, s); });
+        if (pfa::backward_dkv_mfma(g.d, g.N, K_l)) {
+            b.blocks_per_wh = 1;
+            e = timed(PFA_KERNEL_BWD_SCATTER, s,
+                      [&] { return pfa::launch_backward_dkv(b, dt, g.d, (int)n_wh(g), s); });
+        } else {
+            b.blocks_per_wh = parts;
+            e = timed(PFA_KERNEL_BWD_SCATTER, s,
+                      [&] { return pfa::launch_backward_scatter(b, dt, g.d, (int)sgrid, s); });
+        }
     }
     return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
 }
@@ -361,7 +368,7 @@ const char* pfa_kernel_name(int32_t kind) {
         case PFA_KERNEL_AGGREGATE: return "aggregate";
         case PFA_KERNEL_IOTA: return "iota_rows_kernel";
         case PFA_KERNEL_BWD_ROWS: return "bwd_rows_kernel";
-        case PFA_KERNEL_BWD_SCATTER: return "bwd_scatter_kernel";
+        case PFA_KERNEL_BWD_SCATTER: return "bwd_dkv";
         default: return "unknown";
     }
 }

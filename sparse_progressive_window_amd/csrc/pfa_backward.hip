@@ -24,9 +24,16 @@
 //   scanned in slot order, and the r-th marked slot takes kept entry r (I^l is
 //   a subsequence of I^{l-1} in its order). When K and V fit in LDS together
 //   both passes run in one kernel, keeping G in registers.
-// * bwd_scatter_kernel: dK and dV accumulate in LDS (fp32, DH of the d columns
-//   per workgroup) with ds_add_f32; each wave stages one row's (j, A, A g/sqrt(d))
-//   in LDS and its lanes cover (4 or 2 kept slots) x DH columns per atomic.
+// * bwd_dkv_kernel (N a multiple of 16): dV = A^T dO and dK = (A g)^T Q / sqrt(d)
+//   as dense fp32 MFMA products over row blocks densified in LDS, the dV / dK
+//   tiles of each wave's tokens held in registers. At the densities of the keep
+//   schedule (K_l / N from 1/4 down to 1/64) this beats accumulating through
+//   LDS: on gfx950 an LDS fp32 atomic add retires at ~190 clocks per wavefront
+//   instruction and a compare-and-swap loop still costs tens.
+// * bwd_scatter_kernel (other N): dK and dV accumulate in LDS (fp32, DH of the
+//   d columns per workgroup) by compare-and-swap adds; each wave stages one
+//   row's (j, A, A g/sqrt(d)) in LDS and its lanes cover (64/DH kept slots) x
+//   DH columns per instruction.
 #include "pfa_kernels.h"
 #include "pfa_rows.h"
 
@@ -60,6 +67,29 @@ template <int GL>
 __device__ __forceinline__ uint64_t group_bits(uint64_t m, int lane) {
     if (GL == 64) return m;
     return (m >> (lane & (64 - GL))) & ((1ull << GL) - 1ull);
+}
+
+// Two fp32 adds into LDS words by compare-and-swap (ds_cmpst_rtn_b32): on gfx950
+// LDS fp32 atomic adds (ds_add_f32) retire at ~190 clocks per wavefront
+// instruction, 32-bit integer atomics at ~4.5. The lanes of one instruction
+// target distinct words, so a retry only follows an update by another wave.
+__device__ __forceinline__ void lds_add2(unsigned* a, float va, unsigned* b, float vb) {
+    unsigned oa = *a, ob = *b;
+    bool da = false, db = false;
+    do {
+        if (!da) {
+            unsigned e = oa;
+            da = __hip_atomic_compare_exchange_strong(a, &e, __float_as_uint(__uint_as_float(oa) + va),
+                                                      __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            oa = e;
+        }
+        if (!db) {
+            unsigned e = ob;
+            db = __hip_atomic_compare_exchange_strong(b, &e, __float_as_uint(__uint_as_float(ob) + vb),
+                                                      __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            ob = e;
+        }
+    } while (!(da && db));
 }
 
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
@@ -192,18 +222,27 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
             }
             // without V in this kernel g comes from the workspace, one step at a time
             // (a rolled loop keeps the loads of later steps from being hoisted)
+            // (the next step's loads are issued before this step's gathers)
+            uint4 j4n = load16(rI, roff + 16 * vsub);
+            uint4 a4n = load16(rA, roff + 16 * vsub);
+            uint4 g4n = HAS_V ? make_uint4(0u, 0u, 0u, 0u) : load16(rg, roff + 16 * vsub);
 #pragma unroll (HAS_V ? NST : 1)
             for (int t = 0; t < NST; ++t) {
                 const int e0 = 4 * (vsub + GS * t);
-                const int off = roff + e0 * 4;
-                const uint4 j4 = load16(rI, off);
-                const uint4 a4 = load16(rA, off);
+                const uint4 j4 = j4n;
+                const uint4 a4 = a4n;
+                const uint4 g4 = g4n;
+                if (t + 1 < NST) {
+                    const int offn = roff + (e0 + 4 * GS) * 4;
+                    j4n = load16(rI, offn);
+                    a4n = load16(rA, offn);
+                    if (!HAS_V) g4n = load16(rg, offn);
+                }
                 float gv[4];
                 if (HAS_V) {
 #pragma unroll
                     for (int x = 0; x < 4; ++x) gv[x] = G[(4 * t + x) % KPL];
                 } else {
-                    const uint4 g4 = load16(rg, off);
                     gv[0] = __uint_as_float(g4.x);
                     gv[1] = __uint_as_float(g4.y);
                     gv[2] = __uint_as_float(g4.z);
@@ -238,26 +277,37 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
             if (want_dap) {
                 // the wave's LDS writes above complete before the scan reads them
                 __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                // the row's slots in chunks of SU x GL, each chunk's loads issued together
+                constexpr int SU = 4;
                 const int K_prev = p.K_prev;
                 const size_t srow = ((size_t)w.wh * N + ii) * K_prev;
                 int run = 0;
-                for (int s0 = 0; s0 < K_prev; s0 += GL) {
-                    const int slot = s0 + gl;
-                    const bool sv = slot < K_prev;
-                    int j = slot;
-                    float ap = 0.0f;
-                    if (sv) {
-                        if (p.I_prev) j = p.I_prev[srow + slot];
-                        ap = p.A_prev[srow + slot];
+                for (int s0 = 0; s0 < K_prev; s0 += SU * GL) {
+                    int jj[SU];
+                    float ap[SU];
+#pragma unroll
+                    for (int u = 0; u < SU; ++u) {
+                        const int slot = s0 + u * GL + gl;
+                        jj[u] = slot;
+                        ap[u] = 0.0f;
+                        if (slot < K_prev) {
+                            if (p.I_prev) jj[u] = p.I_prev[srow + slot];
+                            ap[u] = p.A_prev[srow + slot];
+                        }
                     }
-                    j = (int)min((unsigned)j, (unsigned)(N - 1));
-                    const bool kept = sv && ((bitmap[j >> 5] >> (j & 31)) & 1u);
-                    const uint64_t m = group_bits<GL>(ballot(kept), lane);
-                    const int rank = run + __builtin_popcountll(m & ((1ull << gl) - 1ull));
-                    run += __builtin_popcountll(m);
-                    float val = 0.0f;
-                    if (kept && rank < K_l && ap > 0.0f) val = vals[rank] / ap;
-                    if (active && sv) p.dA_prev[srow + slot] = val;
+#pragma unroll
+                    for (int u = 0; u < SU; ++u) {
+                        const int slot = s0 + u * GL + gl;
+                        const bool sv = slot < K_prev;
+                        const int j = (int)min((unsigned)jj[u], (unsigned)(N - 1));
+                        const bool kept = sv && ((bitmap[j >> 5] >> (j & 31)) & 1u);
+                        const uint64_t m = group_bits<GL>(ballot(kept), lane);
+                        const int rank = run + __builtin_popcountll(m & ((1ull << gl) - 1ull));
+                        run += __builtin_popcountll(m);
+                        float val = 0.0f;
+                        if (kept && rank < K_l && ap[u] > 0.0f) val = vals[rank] / ap[u];
+                        if (active && sv) p.dA_prev[srow + slot] = val;
+                    }
                 }
             }
         }
@@ -324,10 +374,8 @@ __global__ __launch_bounds__(kBwdScatterWaves * kWave) void bwd_scatter_kernel(c
             const int e = e0 + ps;
             if (e < K_l) {
                 const int j = (int)min((unsigned)st_j[e], (unsigned)(N - 1));
-                __hip_atomic_fetch_add(accV + j * DH + c, st_a[e] * dov, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
-                __hip_atomic_fetch_add(accK + j * DH + c, st_k[e] * qv, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+                lds_add2(reinterpret_cast<unsigned*>(accV + j * DH + c), st_a[e] * dov,
+                         reinterpret_cast<unsigned*>(accK + j * DH + c), st_k[e] * qv);
             }
         }
     }
@@ -339,6 +387,177 @@ __global__ __launch_bounds__(kBwdScatterWaves * kWave) void bwd_scatter_kernel(c
         const size_t o = plane + (size_t)slot_pixel(g, w.wy, w.wx, t) * D + col0 + cc;
         *reinterpret_cast<float4*>(p.dV + o) = *reinterpret_cast<const float4*>(accV + t * DH + cc);
         *reinterpret_cast<float4*>(p.dK + o) = *reinterpret_cast<const float4*>(accK + t * DH + cc);
+    }
+}
+
+// dV = A^T dO and dK = (A g / sqrt(d))^T Q for one window-head on fp32 MFMA
+// (v_mfma_f32_16x16x4_f32: exact products, fp32 accumulation). The kept rows are
+// densified in LDS, KB = 16 rows at a time (two [KB][N] fp32 planes: A and
+// A g / sqrt(d), zero off the kept slots), next to the block's dO and Q rows;
+// wave w owns tokens [16 MTW w, 16 MTW (w + 1)) and keeps their dV and dK tiles in
+// registers over all blocks, so nothing is accumulated through memory. The next
+// block's (j, A, g) entries are loaded into registers during the current block's
+// MFMAs; after the MFMAs the written slots are reset to zero.
+template <typename T, int D, int EPT, int MTW>
+__global__ __launch_bounds__(16 * kWave) void bwd_dkv_kernel(const BackwardArgs p) {
+    constexpr int KB = 16;                  // rows per block (4 MFMA k-steps)
+    constexpr int NT = D / 16;              // 16-column tiles of d
+    constexpr int XS = D == 32 ? 48 : 16;   // X row stride: 4 rows x 16 columns cover 64 distinct banks
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const Geom g = p.g;
+    const int N = g.N;
+    const int K_l = p.K_l;
+    const int NP = N + 16;                  // dense row stride: 4 rows x 16 columns cover 64 distinct banks
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int r16 = lane & 15;
+    const int q4 = lane >> 4;
+    const WhPart w = decode_block(1, p.xcd_map, g);
+    const size_t plane = (size_t)w.bh * g.H * g.W * D;
+    const T* Qh = static_cast<const T*>(p.Q) + plane;
+    const float* dOh = p.dO + plane;
+
+    float* Md = reinterpret_cast<float*>(smem);      // [2][KB][NP]
+    float* Xs = Md + 2 * KB * NP;                    // [2][KB][XS]: dO rows, Q rows
+    for (int u = threadIdx.x * 4; u < 2 * KB * NP; u += blockDim.x * 4)
+        *reinterpret_cast<float4*>(Md + u) = make_float4(0.f, 0.f, 0.f, 0.f);
+
+    const size_t wh_pairs = (size_t)w.wh * N * K_l;
+    const int pair_bytes = N * K_l * 4;
+    const __amdgpu_buffer_rsrc_t rI = make_rsrc(p.I_l + wh_pairs, pair_bytes);
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A_l + wh_pairs, pair_bytes);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g_buf + wh_pairs, pair_bytes);
+    const int mtiles = N / 16;                       // a multiple of MTW, at most 16 MTW
+    const bool wave_active = wave * MTW < mtiles;
+    const int nblk = N / KB;
+    const int blk_entries = KB * K_l;
+
+    // entries of block b: e = threadIdx.x + 1024 u, row b*KB + e / K_l, slot e % K_l
+    // (the row inside the block is the same for every block)
+    int erow[EPT];
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+        const int e = threadIdx.x + 1024 * u;
+        erow[u] = e < blk_entries ? e / K_l : -1;
+    }
+    unsigned ej[EPT];
+    float ea[EPT], ek[EPT];
+    auto load_block = [&](int b) {
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const int e = threadIdx.x + 1024 * u;
+            const int off = erow[u] >= 0 ? (b * blk_entries + e) * 4 : 0x7FFFFFF0;   // dropped past the rows
+            ej[u] = __builtin_amdgcn_raw_buffer_load_b32(rI, off, 0, 0);
+            const float a = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rA, off, 0, 0));
+            const float gg = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, off, 0, 0));
+            ea[u] = a;
+            ek[u] = a * gg * p.scale;
+        }
+    };
+    // the block's dO and Q rows (fp32), one value per thread while D * 2 * KB <= 1024
+    float xv = 0.0f;
+    int xoff = -1;
+    auto load_x = [&](int b) {
+        const int t = threadIdx.x;
+        xoff = -1;
+        if (t < 2 * KB * D) {
+            const int mat = t / (KB * D);
+            const int rr = (t / D) % KB;
+            const int c = t % D;
+            const size_t pix = (size_t)slot_pixel(g, w.wy, w.wx, b * KB + rr) * D + c;
+            if (mat == 0) {
+                xv = dOh[pix];
+            } else if constexpr (sizeof(T) == 4) {
+                xv = reinterpret_cast<const float*>(Qh)[pix];
+            } else {
+                xv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(Qh)[pix] << 16);
+            }
+            xoff = (mat * KB + rr) * XS + c;
+        }
+    };
+
+    v4f accV[MTW][NT], accK[MTW][NT];
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            accV[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+            accK[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+    load_block(0);
+    load_x(0);
+    __syncthreads();   // zero fill done
+
+    unsigned cj[EPT];
+    for (int b = 0; b < nblk; ++b) {
+        // scatter this block's kept entries into the dense planes
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const int j = (int)min(ej[u], (unsigned)(N - 1));
+            cj[u] = j;
+            if (erow[u] >= 0) {
+                Md[erow[u] * NP + j] = ea[u];
+                Md[(KB + erow[u]) * NP + j] = ek[u];
+            }
+        }
+        if (xoff >= 0) Xs[xoff] = xv;
+        __syncthreads();
+        if (b + 1 < nblk) {
+            load_block(b + 1);
+            load_x(b + 1);
+        }
+        if (wave_active) {
+#pragma unroll 1
+            for (int ks = 0; ks < KB / 4; ++ks) {
+                const int row = 4 * ks + q4;
+                float bO[NT], bQ[NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    bO[nt] = Xs[row * XS + 16 * nt + r16];
+                    bQ[nt] = Xs[(KB + row) * XS + 16 * nt + r16];
+                }
+#pragma unroll
+                for (int mt = 0; mt < MTW; ++mt) {
+                    const int tile = wave * MTW + mt;
+                    const float aA = Md[row * NP + 16 * tile + r16];
+                    const float aK = Md[(KB + row) * NP + 16 * tile + r16];
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        accV[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aA, bO[nt], accV[mt][nt], 0, 0, 0);
+                        accK[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aK, bQ[nt], accK[mt][nt], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        // reset the slots this thread wrote (the planes are all zero again)
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            if (erow[u] >= 0) {
+                Md[erow[u] * NP + cj[u]] = 0.0f;
+                Md[(KB + erow[u]) * NP + cj[u]] = 0.0f;
+            }
+        }
+        __syncthreads();
+    }
+    // lane holds token 16*tile + 4*q4 + r, column 16*nt + r16 of each tile
+    if (!wave_active) return;
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt) {
+        const int tile = wave * MTW + mt;
+        {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const size_t o = plane + (size_t)slot_pixel(g, w.wy, w.wx, 16 * tile + 4 * q4 + r) * D + r16;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    p.dV[o + 16 * nt] = accV[mt][nt][r];
+                    p.dK[o + 16 * nt] = accK[mt][nt][r];
+                }
+            }
+        }
     }
 }
 
@@ -396,6 +615,37 @@ int scatter_lds(int DH, int N, int K_l) {
     return 2 * N * DH * 4 + kBwdScatterWaves * 3 * ((K_l + 3) & ~3) * 4;
 }
 
+int dkv_lds(int D, int N) { return (2 * 16 * (N + 16) + 2 * 16 * (D == 32 ? 48 : 16)) * 4; }
+
+// m-tiles (16 tokens) per wave: a divisor of N/16 that needs at most 16 waves
+int dkv_tiles_per_wave(int N) {
+    const int mtiles = N / 16;
+    for (int mtw = 1; mtw <= 4; mtw *= 2)
+        if (mtiles % mtw == 0 && mtiles <= 16 * mtw) return mtw;
+    return 0;
+}
+
+template <typename T, int D, int EPT>
+hipError_t launch_dkv_e(const BackwardArgs& a, int grid, hipStream_t s) {
+    const int th = 16 * kWave;
+    const int lds = dkv_lds(D, a.g.N);
+    switch (dkv_tiles_per_wave(a.g.N)) {
+        case 1: return launch_bwd(bwd_dkv_kernel<T, D, EPT, 1>, a, th, lds, grid, s);
+        case 2: return launch_bwd(bwd_dkv_kernel<T, D, EPT, 2>, a, th, lds, grid, s);
+        case 4: return launch_bwd(bwd_dkv_kernel<T, D, EPT, 4>, a, th, lds, grid, s);
+        default: return hipErrorInvalidValue;   // rejected by backward_dkv_mfma
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_dkv_t(const BackwardArgs& a, int grid, hipStream_t s) {
+    const int ept = (16 * a.K_l + 1023) / 1024;
+    if (ept <= 1) return launch_dkv_e<T, D, 1>(a, grid, s);
+    if (ept <= 2) return launch_dkv_e<T, D, 2>(a, grid, s);
+    if (ept <= 4) return launch_dkv_e<T, D, 4>(a, grid, s);
+    return hipErrorInvalidValue;   // K_l beyond what the caller admits
+}
+
 template <typename T, int D>
 hipError_t launch_scatter_t(const BackwardArgs& a, int grid, hipStream_t s) {
     const int th = kBwdScatterWaves * kWave;
@@ -415,6 +665,16 @@ int backward_fused_rows(int dtype, int D, int N, int K_l, bool want_dap) {
     const int per_lane = 4 * ((K_l + 4 * (64 / CH) - 1) / (4 * (64 / CH)));
     if (per_lane > 16) return 0;
     return rows_lds(dtype, D, N, K_l, true, true, want_dap) <= kLdsBytes ? 1 : 0;
+}
+
+bool backward_dkv_mfma(int D, int N, int K_l) {
+    return N % 16 == 0 && N <= 1024 && K_l <= 256 && dkv_tiles_per_wave(N) > 0 && dkv_lds(D, N) <= kLdsBytes;
+}
+
+hipError_t launch_backward_dkv(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream) {
+    if (dtype == 0)
+        return D == 16 ? launch_dkv_t<float, 16>(a, grid, stream) : launch_dkv_t<float, 32>(a, grid, stream);
+    return D == 16 ? launch_dkv_t<uint16_t, 16>(a, grid, stream) : launch_dkv_t<uint16_t, 32>(a, grid, stream);
 }
 
 int backward_scatter_parts(int D, int N, int K_l) {

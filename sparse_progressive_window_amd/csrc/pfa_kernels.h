@@ -79,7 +79,10 @@ struct BackwardArgs {
 int backward_fused_rows(int dtype, int D, int N, int K_l, bool want_dA_prev);
 hipError_t launch_backward_rows(const BackwardArgs& a, int dtype, int D, bool has_v, bool has_k, int grid,
                                 hipStream_t stream);
-// dK and dV: per window-head LDS accumulators, D/parts columns per workgroup.
+// dK and dV as dense MFMA products over LDS-densified row blocks (N % 16 == 0).
+bool backward_dkv_mfma(int D, int N, int K_l);
+hipError_t launch_backward_dkv(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream);
+// dK and dV otherwise: per window-head LDS accumulators, D/parts columns per workgroup.
 int backward_scatter_parts(int D, int N, int K_l);
 hipError_t launch_backward_scatter(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream);
 

@@ -51,7 +51,7 @@ def test_timing_calls_without_device(lib):
     names = [lib.pfa_kernel_name(k).decode() for k in range(8)]
     assert names == ["dense_layer_kernel", "all_cand", "sparse_layer_kernel",
                      "sparse_layer_kernel(select)", "aggregate", "iota_rows_kernel", "bwd_rows_kernel",
-                     "bwd_scatter_kernel"]
+                     "bwd_dkv"]
     assert lib.pfa_kernel_name(99) == b"unknown"
 
 

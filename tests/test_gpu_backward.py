@@ -133,6 +133,7 @@ CASES = [
     ("f32", 32, 16, 8, 256, 256, False, True),      # N = 256, nothing dropped
     ("f32", 16, 8, 4, 64, 13, False, False),        # N = 64
     ("bf16", 16, 16, 0, 100, 37, False, True),
+    ("f32", 16, 6, 3, 20, 7, False, True),          # N = 36: dK/dV by LDS compare-and-swap adds
 ]
 
 
@@ -160,7 +161,7 @@ def test_backward_kernel_timing_records():
     finally:
         pfa.timing_enable(0)
     kinds = [k for k, _ in recs]
-    assert kinds[-3:] == [6, 6, 7], kinds          # V pass, K pass, scatter (fp32, d = 32)
+    assert kinds[-3:] == [6, 6, 7], kinds          # V pass, K pass, dK/dV (fp32, d = 32)
     assert dropped == 0 and all(ms > 0 for _, ms in recs)
 
 
