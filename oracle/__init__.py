@@ -7,7 +7,8 @@ CPU-baseline leg of ``bench.py`` may use it; the HIP library never does.
 window-heads; ``chain`` runs the layers of one chain for a list of window-heads,
 feeding each layer's (I, A) to the next, all in fp64. ``dense_lse`` gives the
 first layer's log softmax denominators. ``layer_backward`` is the reverse-mode
-derivative of ``layer`` with the kept sets held fixed.
+derivative of ``layer`` with the kept sets held fixed. ``iet_propagate`` is the
+index-matrix propagation and sparsification step between attention blocks.
 """
 
 import ctypes
@@ -209,3 +210,50 @@ def dense_lse(Q, K, *, win, shift, wh_list=None):
         m = s.max(axis=1, keepdims=True)
         out[n] = (m + np.log(np.exp(s - m).sum(axis=1, keepdims=True)))[:, 0]
     return out
+
+
+def iet_select_scores(A):
+    """Selection score of each candidate: the maps of all heads added in fp32, in
+    head order (one index matrix serves every head). A: [n_maps, N, k]."""
+    A = np.asarray(A, dtype=np.float32)
+    S = A[0].copy()
+    for h in range(1, A.shape[0]):
+        S = (S + A[h]).astype(np.float32)
+    return S
+
+
+def iet_propagate(I, A, k1, k2):
+    """Propagation and sparsification of an individualized index matrix
+    ("From Local Windows to Adaptive Candidates via Individualized Exploratory",
+    the paragraphs on propagation and sparsification and on the architecture:
+    one-hop neighbours are merged with the neighbours of neighbours and
+    de-duplicated; low-similarity connections are pruned; per-block k1 / k2).
+
+    Reading of the lost equation: T_k(i) = the k candidates of row i with the
+    largest score (ties to the lower token index). The new candidate set is
+        Dedup( T_k1(i)  U  union over u in T_k2(i) of T_k2(u) ).
+    I: [N, k] token indices in [0, N); A: [n_maps, N, k] attention weights
+    aligned with I (scores: ``iet_select_scores``). Returns (I_out, count):
+    I_out [N, k1 + k2*k2] int32 with each row's set in ascending order, padded
+    with -1; count [N] int32 = set sizes. Plain Python loops (test sizes)."""
+    I = np.asarray(I)
+    S = iet_select_scores(A)
+    N, k = I.shape
+    assert 1 <= k2 <= k1 <= k
+    T1 = np.empty((N, k1), dtype=np.int64)
+    T2 = np.empty((N, k2), dtype=np.int64)
+    for i in range(N):
+        order = sorted(range(k), key=lambda c: (-float(S[i, c]), int(I[i, c])))
+        T1[i] = I[i, order[:k1]]
+        T2[i] = I[i, order[:k2]]
+    width = k1 + k2 * k2
+    out = np.full((N, width), -1, dtype=np.int32)
+    count = np.empty(N, dtype=np.int32)
+    for i in range(N):
+        cand = set(T1[i].tolist())
+        for u in T2[i]:
+            cand.update(T2[u].tolist())
+        v = sorted(cand)
+        out[i, :len(v)] = v
+        count[i] = len(v)
+    return out, count
