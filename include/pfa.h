@@ -183,6 +183,37 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
  * PFA_ERR_INVALID for K_l outside [1, N]). Host only, no device work. */
 int64_t pfa_sparse_layer_backward_workspace(const pfa_shape* shape, int32_t K_l);
 
+/*
+ * Propagation and sparsification of an individualized index matrix between
+ * attention blocks ("From Local Windows to Adaptive Candidates via
+ * Individualized Exploratory": propagation and sparsification paragraphs,
+ * architecture paragraph with k1 = [22, 20, 14, 12], k2 = [12, 10, 7, 6]).
+ * Each token's candidates are pruned to the most similar ones and extended by
+ * the neighbours of its neighbours, duplicates removed. With T_k(i) = the k
+ * candidates of row i with the largest score (score = the n_maps maps added in
+ * fp32 in map order; equal scores keep the lower token index):
+ *     I_out(i) = Dedup( T_k1(i)  U  union over u in T_k2(i) of T_k2(u) ).
+ *
+ * I       [B, N, k] int32 token indices in [0, N), distinct within a row
+ *         (global mode: token = raster index of the map).
+ * A       [B, n_maps, N, k] fp32 attention weights aligned with I (e.g. the
+ *         heads' maps of the block's last layer; finite).
+ * I_out   [B, N, k1 + k2*k2] int32: each row's set in ascending order, then -1.
+ * count_out [B, N] int32: the set sizes.
+ * workspace  at least pfa_iet_propagate_workspace(B, N, k1, k2) bytes of
+ *         device memory (the rows' T_k1 and T_k2), owned by the caller.
+ * The result is exact (integer), the same on every run.
+ * Errors: PFA_ERR_INVALID for sizes < 1, k2 > k1, k1 > k, NULL pointers, a
+ * small workspace; PFA_ERR_UNSUPPORTED for k > 64 or N > 65536.
+ */
+int pfa_iet_propagate(int32_t B, int32_t N, int32_t k, int32_t n_maps, const int32_t* I, const float* A,
+                      int32_t k1, int32_t k2, int32_t* I_out, int32_t* count_out, void* workspace,
+                      int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes pfa_iet_propagate needs, or PFA_ERR_INVALID for sizes < 1.
+ * Host only. */
+int64_t pfa_iet_propagate_workspace(int32_t B, int32_t N, int32_t k1, int32_t k2);
+
 /* Static string for a return code; never NULL. */
 const char* pfa_strerror(int code);
 
@@ -205,8 +236,10 @@ typedef enum {
     PFA_KERNEL_AGGREGATE = 4,      /* window mode: O from the stored (I^l, A^l) rows */
     PFA_KERNEL_IOTA = 5,           /* I rows 0..N-1 of the dense layer */
     PFA_KERNEL_BWD_ROWS = 6,       /* backward: per-row pass(es) -> g, dQ, dA_prev */
-    PFA_KERNEL_BWD_SCATTER = 7     /* backward: dK, dV per window-head ("bwd_dkv_kernel" on MFMA,
+    PFA_KERNEL_BWD_SCATTER = 7,    /* backward: dK, dV per window-head ("bwd_dkv_kernel" on MFMA,
                                       "bwd_scatter_kernel" by LDS adds when N % 16 != 0) */
+    PFA_KERNEL_IET_RANK = 8,       /* index propagation: top-k1 / top-k2 of each row */
+    PFA_KERNEL_IET_UNION = 9       /* index propagation: de-duplicated union per row */
 } pfa_kernel_kind;
 
 /* capacity > 0: create 2*capacity events and start recording (earlier records

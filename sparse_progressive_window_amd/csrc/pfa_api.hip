@@ -312,6 +312,30 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
     return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
 }
 
+int64_t pfa_iet_propagate_workspace(int32_t B, int32_t N, int32_t k1, int32_t k2) {
+    if (B < 1 || N < 1 || k1 < 1 || k2 < 1) return PFA_ERR_INVALID;
+    return (int64_t)B * N * (k1 + k2) * 4;
+}
+
+int pfa_iet_propagate(int32_t B, int32_t N, int32_t k, int32_t n_maps, const int32_t* I, const float* A,
+                      int32_t k1, int32_t k2, int32_t* I_out, int32_t* count_out, void* workspace,
+                      int64_t workspace_bytes, void* stream) {
+    if (B < 1 || N < 1 || k < 1 || n_maps < 1) return PFA_ERR_INVALID;
+    if (k2 < 1 || k1 < k2 || k1 > k) return PFA_ERR_INVALID;
+    if (!I || !A || !I_out || !count_out || !workspace) return PFA_ERR_INVALID;
+    if (workspace_bytes < (int64_t)B * N * (k1 + k2) * 4) return PFA_ERR_INVALID;
+    if (k > 64 || N > 65536) return PFA_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    pfa::IetArgs a;
+    a.I = I; a.A = A; a.I_out = I_out; a.count_out = count_out;
+    a.T1 = static_cast<int32_t*>(workspace);
+    a.T2 = a.T1 + (int64_t)B * N * k1;
+    a.B = B; a.N = N; a.k = k; a.n_maps = n_maps; a.k1 = k1; a.k2 = k2;
+    hipError_t e = timed(PFA_KERNEL_IET_RANK, s, [&] { return pfa::launch_iet_rank(a, s); });
+    if (e == hipSuccess) e = timed(PFA_KERNEL_IET_UNION, s, [&] { return pfa::launch_iet_union(a, s); });
+    return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
+}
+
 const char* pfa_strerror(int code) {
     switch (code) {
         case PFA_OK: return "ok";
@@ -369,6 +393,8 @@ const char* pfa_kernel_name(int32_t kind) {
         case PFA_KERNEL_IOTA: return "iota_rows_kernel";
         case PFA_KERNEL_BWD_ROWS: return "bwd_rows_kernel";
         case PFA_KERNEL_BWD_SCATTER: return "bwd_dkv";
+        case PFA_KERNEL_IET_RANK: return "iet_rank_kernel";
+        case PFA_KERNEL_IET_UNION: return "iet_union_kernel";
         default: return "unknown";
     }
 }

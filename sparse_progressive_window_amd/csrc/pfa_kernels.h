@@ -86,6 +86,20 @@ hipError_t launch_backward_dkv(const BackwardArgs& a, int dtype, int D, int grid
 int backward_scatter_parts(int D, int N, int K_l);
 hipError_t launch_backward_scatter(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream);
 
+// Propagation / sparsification of an individualized index matrix.
+struct IetArgs {
+    const int32_t* I;        // [B, N, k] token indices
+    const float* A;          // [B, n_maps, N, k] maps aligned with I
+    int32_t* I_out;          // [B, N, k1 + k2*k2] ascending, -1 padded
+    int32_t* count_out;      // [B, N]
+    int32_t* T1;             // workspace [B, N, k1]: top-k1 tokens of each row
+    int32_t* T2;             // workspace [B, N, k2]
+    int B, N, k, n_maps, k1, k2;
+};
+int iet_union_lds(int N);
+hipError_t launch_iet_rank(const IetArgs& a, hipStream_t stream);
+hipError_t launch_iet_union(const IetArgs& a, hipStream_t stream);
+
 hipError_t launch_sparse(const SparseArgs& a, int dtype, int D, SparseMode mode, int lds_bytes, int grid,
                          hipStream_t stream);
 // All-candidates layer (I^{l-1} implicit, K_prev = N = 1024): MFMA scores, selection only.

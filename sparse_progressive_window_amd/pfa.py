@@ -49,6 +49,10 @@ def load():
         lib.pfa_sparse_layer_backward.restype = ctypes.c_int
         lib.pfa_sparse_layer_backward_workspace.argtypes = [ctypes.POINTER(PfaShape), i32]
         lib.pfa_sparse_layer_backward_workspace.restype = ctypes.c_int64
+        lib.pfa_iet_propagate.argtypes = [i32, i32, i32, i32, P, P, i32, i32, P, P, P, ctypes.c_int64, P]
+        lib.pfa_iet_propagate.restype = ctypes.c_int
+        lib.pfa_iet_propagate_workspace.argtypes = [i32, i32, i32, i32]
+        lib.pfa_iet_propagate_workspace.restype = ctypes.c_int64
         lib.pfa_strerror.argtypes = [ctypes.c_int]
         lib.pfa_strerror.restype = ctypes.c_char_p
         lib.pfa_version.restype = ctypes.c_int
@@ -272,7 +276,48 @@ def backward_workspace_bytes(Q, K_l, *, win, shift=0) -> int:
     return n
 
 
-KERNEL_KINDS = ("dense", "all_candidates", "sparse", "select", "aggregate", "iota", "bwd_rows", "bwd_scatter")
+def iet_propagate(I, A, k1, k2, *, out=None, workspace=None):
+    """Propagation and sparsification of an index matrix: I [B, N, k] (or [N, k])
+    int32, A [B, n_maps, N, k] (or [n_maps, N, k]) fp32. Returns (I_out
+    [.., N, k1 + k2*k2] int32 ascending and -1 padded, count [.., N] int32)."""
+    squeeze = I.dim() == 2
+    if squeeze:
+        I, A = I.unsqueeze(0), A.unsqueeze(0)
+    if I.dim() != 3 or A.dim() != 4:
+        raise ValueError("I must be [B, N, k] and A [B, n_maps, N, k]")
+    B, N, k = I.shape
+    n_maps = A.shape[1]
+    if A.shape != (B, n_maps, N, k):
+        raise ValueError(f"A must be [{B}, n_maps, {N}, {k}], got {tuple(A.shape)}")
+    width = k1 + k2 * k2
+    dev = I.device
+    if out is None:
+        I_out = torch.empty((B, N, width), dtype=torch.int32, device=dev)
+        count = torch.empty((B, N), dtype=torch.int32, device=dev)
+    else:
+        I_out, count = out
+    _expect(I, B * N * k, torch.int32, "I")
+    _expect(A, B * n_maps * N * k, torch.float32, "A")
+    _expect(I_out, B * N * width, torch.int32, "I_out")
+    _expect(count, B * N, torch.int32, "count_out")
+    need = int(load().pfa_iet_propagate_workspace(B, N, k1, k2))
+    if need < 0:
+        raise PfaError("pfa_iet_propagate_workspace", need)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must be a device tensor of at least {need} bytes")
+    rc = load().pfa_iet_propagate(B, N, k, n_maps, _ptr(I), _ptr(A), k1, k2, _ptr(I_out), _ptr(count),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
+    if rc != 0:
+        raise PfaError("pfa_iet_propagate", rc)
+    if squeeze:
+        return I_out[0], count[0]
+    return I_out, count
+
+
+KERNEL_KINDS = ("dense", "all_candidates", "sparse", "select", "aggregate", "iota", "bwd_rows", "bwd_scatter",
+                "iet_rank", "iet_union")
 
 
 def kernel_name(kind: int) -> str:

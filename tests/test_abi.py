@@ -31,7 +31,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"pfa_dense_layer", "pfa_sparse_layer", "pfa_first_two_layers", "pfa_sparse_layer_backward",
-            "pfa_sparse_layer_backward_workspace", "pfa_strerror", "pfa_version"} <= set(names)
+            "pfa_sparse_layer_backward_workspace", "pfa_iet_propagate", "pfa_iet_propagate_workspace",
+            "pfa_strerror", "pfa_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -48,10 +49,10 @@ def test_timing_calls_without_device(lib):
     assert lib.pfa_timing_read(None, None, 0, None, None) == -1
     assert lib.pfa_timing_read(None, None, 4, ctypes.byref(n), None) == -1
     assert lib.pfa_timing_read(None, None, -1, ctypes.byref(n), None) == -1
-    names = [lib.pfa_kernel_name(k).decode() for k in range(8)]
+    names = [lib.pfa_kernel_name(k).decode() for k in range(10)]
     assert names == ["dense_layer_kernel", "all_cand", "sparse_layer_kernel",
                      "sparse_layer_kernel(select)", "aggregate", "iota_rows_kernel", "bwd_rows_kernel",
-                     "bwd_dkv"]
+                     "bwd_dkv", "iet_rank_kernel", "iet_union_kernel"]
     assert lib.pfa_kernel_name(99) == b"unknown"
 
 
@@ -176,3 +177,24 @@ def test_backward_validation(lib):
         2 * 3 * 2 * 1024 * 16 * 4
     assert lib.pfa_sparse_layer_backward_workspace(ctypes.byref(shape()), 0) == -1
     assert lib.pfa_sparse_layer_backward_workspace(ctypes.byref(shape(d=8)), 16) == -2
+
+
+def test_iet_validation(lib):
+    def prop(B=1, N=4096, k=64, n_maps=6, k1=22, k2=12, ptrs=(FAKE, FAKE, FAKE, FAKE), ws=FAKE,
+             ws_bytes=4096 * 34 * 4):
+        return lib.pfa_iet_propagate(B, N, k, n_maps, ptrs[0], ptrs[1], k1, k2, ptrs[2], ptrs[3], ws, ws_bytes,
+                                     None)
+    assert prop(B=0) == -1
+    assert prop(N=0) == -1
+    assert prop(n_maps=0) == -1
+    assert prop(k1=10, k2=12) == -1                              # k2 > k1
+    assert prop(k=16) == -1                                      # k1 > k
+    assert prop(k2=0) == -1
+    assert prop(ptrs=(None, FAKE, FAKE, FAKE)) == -1
+    assert prop(ptrs=(FAKE, FAKE, FAKE, None)) == -1
+    assert prop(ws=None) == -1
+    assert prop(ws_bytes=4096 * 34 * 4 - 4) == -1
+    assert prop(k=65, ws_bytes=1 << 20) == -2
+    assert prop(N=65537, ws_bytes=1 << 30) == -2
+    assert lib.pfa_iet_propagate_workspace(2, 4096, 22, 12) == 2 * 4096 * 34 * 4
+    assert lib.pfa_iet_propagate_workspace(1, 0, 22, 12) == -1
