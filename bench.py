@@ -29,7 +29,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 COUNTERS_FILE = "hbm_counters_{workload}.md"
 
 # kernel kinds of the library's timing calls (pfa_kernel_kind)
-DENSE, ALL_CAND, SPARSE, SELECT, AGGREGATE, IOTA, BWD_ROWS, BWD_SCATTER = range(8)
+DENSE, ALL_CAND, SPARSE, SELECT, AGGREGATE, IOTA, BWD_ROWS, BWD_SCATTER, IET_RANK, IET_UNION = range(10)
 
 
 def kernel_bytes(w, l, kind, i_prev_implicit, split, fused=False):
@@ -128,6 +128,8 @@ def main():
                     help="run layers 1-2 fused without materialising A^1 (bf16, or fp32 with d = 16)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward leg (layers L..2 of the sparse-layer backward, timed separately)")
+    ap.add_argument("--no-global", action="store_true",
+                    help="skip the global-mode leg (individualized attention + index propagation, 64x64 map)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -272,6 +274,11 @@ def main():
             result["backward"] = backward_leg(w, qkv, outs, implicit, args, torch, pfa)
         except Exception as e:   # the forward line stands on its own
             result["backward"] = {"error": repr(e)}
+    if not args.no_global:
+        try:
+            result["global"] = global_leg(args, torch, pfa)
+        except Exception as e:   # the forward line stands on its own
+            result["global"] = {"error": repr(e)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_sample)
     print(json.dumps(result), flush=True)
@@ -347,6 +354,68 @@ def backward_leg(w, qkv, outs, implicit, args, torch, pfa):
                          "kernel": dom["kernel"], "layer": dom["layer"], "ms_per_launch": dom["ms"],
                          "alg_bytes_per_launch": dom["alg_bytes"]},
             "kernels": kernels}
+
+
+def global_leg(args, torch, pfa):
+    """Global individualized attention (one index matrix of k candidates per token,
+    shared by the heads; softmax over them; O) on the 64x64 global workload,
+    followed by the index propagation with each IET block's (k1, k2). Each
+    kernel is timed with HIP events over `steps` repetitions; the whole working
+    set (~9 MB) fits the 256 MB MALL, so these are latency-bound figures."""
+    from sparse_progressive_window_amd import inputs, workloads
+    w = workloads.GLOBAL64
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(t.device.view(np.int16)).to(dev).view(torch.bfloat16) for t in inputs.qkv(w, 0, 0))
+    N, kk, H = w.N, w.k_global, w.heads
+    Iidx = torch.from_numpy(inputs.global_index(w)).to(dev).view(1, 1, N, kk)
+    outs = (torch.empty((1, H, N, kk), dtype=torch.int32, device=dev),
+            torch.empty((1, H, N, kk), dtype=torch.float32, device=dev),
+            torch.empty(q.shape, dtype=torch.float32, device=dev))
+    blocks = list(zip((22, 20, 14, 12), (12, 10, 7, 6)))
+    iet_out = [(torch.empty((1, N, k1 + k2 * k2), dtype=torch.int32, device=dev),
+                torch.empty((1, N), dtype=torch.int32, device=dev)) for k1, k2 in blocks]
+    ws = torch.empty(max(int(pfa.load().pfa_iet_propagate_workspace(1, N, k1, k2)) for k1, k2 in blocks),
+                     dtype=torch.uint8, device=dev)
+    I_map = Iidx.view(1, N, kk)
+
+    def gstep():
+        pfa.sparse_layer(q, k, v, Iidx, None, kk, win=0, i_shared=True, out=outs)
+        A4 = outs[1].view(1, H, N, kk)
+        for (k1, k2), o in zip(blocks, iet_out):
+            pfa.iet_propagate(I_map, A4, k1, k2, out=o, workspace=ws)
+
+    for _ in range(args.warmup):
+        gstep()
+    torch.cuda.synchronize()
+    pfa.timing_enable(args.steps * (1 + 2 * len(blocks)) + 16)
+    for _ in range(args.steps):
+        gstep()
+    torch.cuda.synchronize()
+    recs, dropped = pfa.timing_read(args.steps * (1 + 2 * len(blocks)) + 16)
+    pfa.timing_enable(0)
+    assert dropped == 0
+    per = {}
+    for kind, ms in recs:
+        per.setdefault(kind, []).append(ms)
+    attn_bytes = H * (3 * N * w.d * 2 + 2 * N * kk * 4 + N * w.d * 4) + N * kk * 4
+    rank_bytes = len(blocks) * (N * kk * 4 + H * N * kk * 4) + sum(N * (k1 + k2) * 4 for k1, k2 in blocks)
+    union_bytes = sum(N * (k1 + k2) * 4 + N * (k1 + k2 * k2 + 1) * 4 for k1, k2 in blocks)
+    kernels = []
+    for kind, by, launches_per_step in ((SPARSE, attn_bytes, 1), (IET_RANK, rank_bytes, len(blocks)),
+                                        (IET_UNION, union_bytes, len(blocks))):
+        v_ = per.get(kind, [])
+        if not v_:
+            continue
+        ms = float(np.mean(v_)) * launches_per_step      # per step (all blocks)
+        gbs = by / (ms * 1e-3) / 1e9
+        kernels.append({"kernel": pfa.kernel_name(kind), "launches_per_step": launches_per_step,
+                        "ms_per_step": round(ms, 4), "alg_bytes": by, "GB_per_s": round(gbs, 1),
+                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+    pairs = H * N * kk
+    attn_ms = next(k_["ms_per_step"] for k_ in kernels if k_["kernel"] == pfa.kernel_name(SPARSE))
+    return {"workload": w.name, "pairs": pairs, "attention_pairs_per_s": pairs / (attn_ms * 1e-3),
+            "iet_blocks_k1_k2": blocks, "kernels": kernels,
+            "note": "working set fits the MALL: latency-bound, HBM fraction not meaningful"}
 
 
 def cpu_baseline(w, host, sample):
