@@ -41,11 +41,11 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i32, i64 = ctypes.c_int32, ctypes.c_int64
-        lib.oracle_layer.argtypes = [i32] * 7 + [P, P, P, P, i32, P, i32, i32, i32, P, i64, P, P, P, P, P]
+        lib.oracle_layer.argtypes = [i32] * 7 + [P, P, P, P, i32, P, i32, i32, i32, P, i64, P, P, P, P, P, P]
         lib.oracle_layer.restype = ctypes.c_int
         lib.oracle_threads.restype = ctypes.c_int
-        lib.oracle_layer_backward.argtypes = ([i32] * 7 + [P, P, P, P, P, i32, i32, i32, P, i64, P, P, P]
-                                              + [P, P, P, P])
+        lib.oracle_layer_backward.argtypes = ([i32] * 7 + [P, P, P, P, P, i32, i32, i32, P, i64, P, P, P, P]
+                                              + [P, P, P, P, P])
         lib.oracle_layer_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -60,13 +60,15 @@ def _ptr(a):
 
 
 def layer(Q, K, V, *, win, shift, K_l, I_prev=None, A_prev=None, i_shared=False,
-          prev_compact=False, wh_list=None, forced_keep=None, want_keys=False, O_out=None):
+          prev_compact=False, wh_list=None, forced_keep=None, want_keys=False, O_out=None, bias=None):
     """One PFA layer in fp64.
 
     Q, K, V: [B, heads, H, W, d] arrays (any float dtype; widened to fp64).
     I_prev: [B, heads|1, nwin, N, K_prev] int32 or None (all slots, K_prev = N).
     A_prev: [B, heads, nwin, N, K_prev] or None (all ones).
     prev_compact: I_prev/A_prev are [n_wh, N, K_prev], aligned with wh_list.
+    bias: [heads, (2 win - 1)^2] relative position bias added to the scores
+    (window mode), or None.
     Returns dict with I [n_wh, N, K_l] int32, A [n_wh, N, K_l] fp64,
     O [B, heads, H, W, d] fp64 (NaN where not computed), optionally keys
     [n_wh, N, K_prev] = ln P'.
@@ -93,6 +95,9 @@ def layer(Q, K, V, *, win, shift, K_l, I_prev=None, A_prev=None, i_shared=False,
         wl = np.ascontiguousarray(wh_list, dtype=np.int64)
         n_wh = len(wl)
     fk = None if forced_keep is None else np.ascontiguousarray(forced_keep, dtype=np.int32)
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float64)
+        assert win and bias.shape == (heads, (2 * win - 1) ** 2)
     I_out = np.empty((n_wh, N, K_l), dtype=np.int32)
     A_out = np.empty((n_wh, N, K_l), dtype=np.float64)
     keys = np.empty((n_wh, N, K_prev), dtype=np.float64) if want_keys else None
@@ -101,7 +106,7 @@ def layer(Q, K, V, *, win, shift, K_l, I_prev=None, A_prev=None, i_shared=False,
     rc = lib.oracle_layer(B, heads, H, W, d, win, shift, _ptr(Q), _ptr(K), _ptr(V),
                           _ptr(I_prev), int(bool(i_shared)), _ptr(A_prev), int(bool(prev_compact)),
                           K_prev, K_l,
-                          _ptr(wl), n_wh, _ptr(fk), _ptr(I_out), _ptr(A_out), _ptr(keys),
+                          _ptr(wl), n_wh, _ptr(fk), _ptr(bias), _ptr(I_out), _ptr(A_out), _ptr(keys),
                           _ptr(O_out))
     if rc != 0:
         raise ValueError("oracle_layer rejected the sizes")
@@ -112,7 +117,7 @@ def layer(Q, K, V, *, win, shift, K_l, I_prev=None, A_prev=None, i_shared=False,
 
 
 def layer_backward(Q, K, V, *, win, shift, keep, dO, dA=None, I_prev=None, A_prev=None,
-                   prev_compact=False, wh_list=None, want_dA_prev=True):
+                   prev_compact=False, wh_list=None, want_dA_prev=True, bias=None):
     """Gradients of one PFA layer in fp64 with the kept sets held fixed.
 
     keep: [n_wh, N, K_l] kept slot indices (the layer's I^l, compact over
@@ -120,7 +125,8 @@ def layer_backward(Q, K, V, *, win, shift, keep, dO, dA=None, I_prev=None, A_pre
     of A^l aligned with keep, or None. I_prev / A_prev / prev_compact as in
     ``layer``. Returns dict dQ, dK, dV ([B, heads, H, W, d], zero outside the
     listed window-heads) and dA_prev ([n_wh, N, K_prev] in I^{l-1} order, when
-    A_prev is given and want_dA_prev)."""
+    A_prev is given and want_dA_prev), and dbias ([heads, (2 win - 1)^2]) when
+    a bias is given."""
     lib = _load()
     Q = np.ascontiguousarray(Q, dtype=np.float64)
     K = np.ascontiguousarray(K, dtype=np.float64)
@@ -153,16 +159,32 @@ def layer_backward(Q, K, V, *, win, shift, keep, dO, dA=None, I_prev=None, A_pre
     dK = np.zeros(Q.shape)
     dV = np.zeros(Q.shape)
     dA_prev = (np.zeros((n_wh, N, K_prev)) if (A_prev is not None and want_dA_prev) else None)
+    dbias = None
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float64)
+        assert win and bias.shape == (heads, (2 * win - 1) ** 2)
+        dbias = np.zeros(bias.shape)
     rc = lib.oracle_layer_backward(B, heads, H, W, d, win, shift, _ptr(Q), _ptr(K), _ptr(V),
                                    _ptr(I_prev), _ptr(A_prev), int(bool(prev_compact)), K_prev, K_l,
-                                   _ptr(wl), n_wh, _ptr(keep), _ptr(dO), _ptr(dA),
-                                   _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dA_prev))
+                                   _ptr(wl), n_wh, _ptr(keep), _ptr(dO), _ptr(dA), _ptr(bias),
+                                   _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dA_prev), _ptr(dbias))
     if rc != 0:
         raise ValueError("oracle_layer_backward rejected the sizes or the kept sets")
     out = {"dQ": dQ, "dK": dK, "dV": dV}
     if dA_prev is not None:
         out["dA_prev"] = dA_prev
+    if dbias is not None:
+        out["dbias"] = dbias
     return out
+
+
+def rel_index(win):
+    """[N, N] index into a (2 win - 1)^2 relative position bias table for slots
+    (i, j) of a window: (i/w - j/w + w - 1) (2w - 1) + (i%w - j%w + w - 1)."""
+    t = np.arange(win * win)
+    dy = (t // win)[:, None] - (t // win)[None, :]
+    dx = (t % win)[:, None] - (t % win)[None, :]
+    return (dy + win - 1) * (2 * win - 1) + (dx + win - 1)
 
 
 def chain(layers_qkv, *, win, shifts, Ks, wh_list=None):

@@ -60,6 +60,16 @@ static int64_t pixel_of(int win, int shift, int H, int W, int wy, int wx, int t)
     return (int64_t)y * W + x;
 }
 
+/* Relative position of slot j seen from slot i inside a win x win window, as
+ * an index into a (2 win - 1)^2 bias table: (dy + win - 1) (2 win - 1) + (dx + win - 1)
+ * with dy = i/win - j/win, dx = i%win - j%win (window-local coordinates, the same
+ * under every cyclic shift). */
+static int rel_index(int win, int i, int j) {
+    const int dy = i / win - j / win;
+    const int dx = i % win - j % win;
+    return (dy + win - 1) * (2 * win - 1) + (dx + win - 1);
+}
+
 int oracle_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();
@@ -83,6 +93,9 @@ int oracle_threads(void) {
  *                n_wh of them; NULL means all, in order.
  * forced_keep    optional [n_wh, N, K_l]: the kept set is given instead of
  *                selected (conditional mode; steps 8-10 only use it).
+ * bias           optional [heads, (2 win - 1)^2] relative position bias added
+ *                to every score s_ij at index rel_index(win, i, j) (window
+ *                mode only).
  * I_out, A_out   [n_wh, N, K_l] outputs (compact over wh_list).
  * key_out        optional [n_wh, N, K_prev]: ln P' per candidate in C_i order.
  * O_out          [B, heads, H, W, d]; only the pixels of listed window-heads are
@@ -94,7 +107,7 @@ int oracle_layer(int B, int heads, int H, int W, int d, int win, int shift,
                  const int32_t* I_prev, int i_shared, const double* A_prev,
                  int prev_compact, int K_prev, int K_l,
                  const int64_t* wh_list, int64_t n_wh,
-                 const int32_t* forced_keep,
+                 const int32_t* forced_keep, const double* bias,
                  int32_t* I_out, double* A_out, double* key_out, double* O_out) {
     const int N = win ? win * win : H * W;
     const int nwy = win ? H / win : 1, nwx = win ? W / win : 1;
@@ -102,8 +115,10 @@ int oracle_layer(int B, int heads, int H, int W, int d, int win, int shift,
     if (win && (H % win || W % win)) return -1;
     if (K_l < 1 || K_l > K_prev || K_prev > N) return -1;
     if (!I_prev && K_prev != N) return -1;
+    if (bias && !win) return -1;
     if (!wh_list) n_wh = total_wh;
     const double scale = 1.0 / sqrt((double)d);
+    const int nrel = (2 * win - 1) * (2 * win - 1);
 
     int64_t w;
 #pragma omp parallel for schedule(dynamic)
@@ -135,13 +150,15 @@ int oracle_layer(int B, int heads, int H, int W, int d, int win, int shift,
                 : (((int64_t)b * heads + h) * nwy * nwx + win_id) * N + i;
             const double* a = A_prev ? A_prev + arow * K_prev : NULL;
 
-            /* step 3: scaled scores over the candidate list only */
+            /* step 3: scaled scores over the candidate list only, plus the
+             * relative position bias of (i, j) when given */
             for (int c = 0; c < K_prev; ++c) {
                 const int j = C ? C[c] : c;
                 const double* k = Kh + pixel_of(win, shift, H, W, wy, wx, j) * d;
                 double acc = 0.0;
                 for (int e = 0; e < d; ++e) acc += q[e] * k[e];
                 s[c] = acc * scale;
+                if (bias) s[c] += bias[(int64_t)h * nrel + rel_index(win, i, j)];
             }
             /* step 4: softmax over C_i */
             double m = s[0];
@@ -221,6 +238,8 @@ int oracle_layer(int B, int heads, int H, int W, int d, int win, int shift,
  *           listed window-heads only).
  * dA_prev   [n_wh, N, K_prev] gradient of A^{l-1} in C_i order (written), or
  *           NULL. Requires A_prev.
+ * bias      [heads, (2 win - 1)^2] relative position bias of the forward, or NULL.
+ * dbias     [heads, (2 win - 1)^2] gradient of the bias: ADDED to, or NULL.
  * Window mode or global mode with one index matrix per head; other arguments as
  * in oracle_layer. Returns 0, or -1 on inconsistent sizes or a kept slot that is
  * not a candidate.
@@ -229,8 +248,8 @@ int oracle_layer_backward(int B, int heads, int H, int W, int d, int win, int sh
                           const double* Q, const double* K, const double* V,
                           const int32_t* I_prev, const double* A_prev, int prev_compact, int K_prev, int K_l,
                           const int64_t* wh_list, int64_t n_wh, const int32_t* keep,
-                          const double* dO, const double* dA,
-                          double* dQ, double* dK, double* dV, double* dA_prev) {
+                          const double* dO, const double* dA, const double* bias,
+                          double* dQ, double* dK, double* dV, double* dA_prev, double* dbias) {
     const int N = win ? win * win : H * W;
     const int nwy = win ? H / win : 1, nwx = win ? W / win : 1;
     const int64_t total_wh = (int64_t)B * heads * nwy * nwx;
@@ -238,8 +257,10 @@ int oracle_layer_backward(int B, int heads, int H, int W, int d, int win, int sh
     if (K_l < 1 || K_l > K_prev || K_prev > N) return -1;
     if (!I_prev && K_prev != N) return -1;
     if (dA_prev && !A_prev) return -1;
+    if ((bias || dbias) && !win) return -1;
     if (!wh_list) n_wh = total_wh;
     const double scale = 1.0 / sqrt((double)d);
+    const int nrel = (2 * win - 1) * (2 * win - 1);
     int bad = 0;
 
     int64_t w;
@@ -278,6 +299,7 @@ int oracle_layer_backward(int B, int heads, int H, int W, int d, int win, int sh
                 double acc = 0.0;
                 for (int e = 0; e < d; ++e) acc += q[e] * k[e];
                 s[c] = acc * scale;
+                if (bias) s[c] += bias[(int64_t)h * nrel + rel_index(win, i, j)];
             }
             double m = s[0];
             for (int c = 1; c < K_prev; ++c) if (s[c] > m) m = s[c];
@@ -332,11 +354,16 @@ int oracle_layer_backward(int B, int heads, int H, int W, int d, int win, int sh
                 s[c] = gP * (a ? a[c] : 1.0);    /* gAcal */
                 sum_AcalgAcal += acal[c] * s[c];
             }
-            /* step 3 backwards */
+            /* step 3 backwards (the bias gradient is summed over rows and windows
+             * of each head: updates are serialised) */
             double* dq = dQ + off + qpix * d;
             for (int c = 0; c < K_prev; ++c) {
                 const double gs = acal[c] * (s[c] - sum_AcalgAcal);
                 const int j = C ? C[c] : c;
+                if (dbias) {
+#pragma omp atomic
+                    dbias[(int64_t)h * nrel + rel_index(win, i, j)] += gs;
+                }
                 const int64_t jpix = pixel_of(win, shift, H, W, wy, wx, j);
                 const double* k = K + off + jpix * d;
                 double* dk = dK + off + jpix * d;

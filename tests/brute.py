@@ -9,16 +9,19 @@ with a lexicographic sort. Only practical for tiny windows.
 import numpy as np
 
 
-def masked_dense_layer(q, k, v, C=None, a=None, K_l=None, keep_override=None):
+def masked_dense_layer(q, k, v, C=None, a=None, K_l=None, keep_override=None, bias=None):
     """q, k, v: [N, d] slot-ordered rows of one window-head.
     C: [N, K_prev] candidate slots (None = all); a: [N, K_prev] previous map (None = 1).
     keep_override: [N, N] bool, replaces the top-K choice when given.
+    bias: [N, N] dense additive score bias (None = 0).
     Returns (keep [N, N] bool, A [N, N] dense, O [N, d])."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     N, d = q.shape
     S = (q @ k.T) / np.sqrt(d)
+    if bias is not None:
+        S = S + np.asarray(bias, np.float64)
     mask = np.zeros((N, N), bool)
     prev = np.zeros((N, N))
     if C is None:
