@@ -126,6 +126,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=256, help="window-heads timed on the CPU oracle")
     ap.add_argument("--fused12", action="store_true",
                     help="run layers 1-2 fused without materialising A^1 (bf16, or fp32 with d = 16)")
+    ap.add_argument("--rpb", action="store_true",
+                    help="add a seeded relative position bias table per layer to the scores (not with --fused12)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward leg (layers L..2 of the sparse-layer backward, timed separately)")
     ap.add_argument("--no-global", action="store_true",
@@ -175,6 +177,13 @@ def main():
         O = torch.empty((w.B, w.heads, w.H, w.W, w.d), dtype=torch.float32, device=dev)
         outs.append((I, A, O))
     implicit = [l == 1 and w.K[0] == N for l in range(L)]
+    bias = [None] * L
+    if args.rpb:
+        if fused:
+            print("--rpb does not combine with --fused12", file=sys.stderr)
+            sys.exit(2)
+        gb = torch.Generator().manual_seed(777)
+        bias = [torch.randn((w.heads, (2 * w.win - 1) ** 2), generator=gb).to(dev) for _ in range(L)]
 
     def step(marks=None):
         for l in range(L):
@@ -185,11 +194,11 @@ def main():
             elif fused and l == 1:
                 pass   # done with layer 1
             elif l == 0:
-                pfa.dense_layer(Q, K, V, w.K[0], win=w.win, shift=w.shifts[0], out=outs[0])
+                pfa.dense_layer(Q, K, V, w.K[0], win=w.win, shift=w.shifts[0], out=outs[0], bias=bias[0])
             else:
                 I_prev = None if implicit[l] else outs[l - 1][0]
                 pfa.sparse_layer(Q, K, V, I_prev, outs[l - 1][1], w.K[l], win=w.win, shift=w.shifts[l],
-                                 out=outs[l])
+                                 out=outs[l], bias=bias[l])
             if marks is not None:
                 marks.append(pfa.timing_count())
 
@@ -263,7 +272,7 @@ def main():
         "value": value, "unit": "candidate pairs/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "fused_layers_1_2": fused, "B": w.B, "heads": w.heads, "H": w.H, "W": w.W,
+        "config": {"workload": w.name, "fused_layers_1_2": fused, "relative_position_bias": bool(args.rpb), "B": w.B, "heads": w.heads, "H": w.H, "W": w.W,
                    "d": w.d, "win": w.win,
                    "K": w.K, "shifts": w.shifts, "window_heads": w.n_wh, "pairs_per_step": total_pairs},
         "roofline": roof, "layers": layers, "kernels": kernels,

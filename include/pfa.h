@@ -113,6 +113,29 @@ int pfa_sparse_layer(const pfa_shape* shape, const void* Q, const void* K, const
                      void* stream);
 
 /*
+ * The same two layer calls with a relative position bias in the score
+ * ("Progressive Focused Transformer" notes describe the network as relative
+ * position bias based; IET applies relative positional encoding in its first
+ * block): s_ij = q_i.k_j / sqrt(d) + bias[h][(dy + win - 1)(2 win - 1) + dx + win - 1]
+ * with (dy, dx) = (i/win - j/win, i%win - j%win), the window-local offset of
+ * slot i from slot j (the same under every cyclic shift).
+ *
+ * bias    [heads, (2 win - 1)^2] fp32 device table of this layer, or NULL (then
+ *         the calls are exactly pfa_dense_layer / pfa_sparse_layer). Window mode
+ *         only. With a bias, the sparse layer whose candidate list is every
+ *         slot scores by gathers instead of MFMA.
+ * Errors: as pfa_dense_layer / pfa_sparse_layer, and PFA_ERR_UNSUPPORTED for a
+ * bias in global mode or, in pfa_dense_layer_rpb with K1 == N, win not a
+ * multiple of 16.
+ */
+int pfa_dense_layer_rpb(const pfa_shape* shape, const void* Q, const void* K, const void* V, const float* bias,
+                        int32_t K1, int32_t* I_out, float* A_out, float* lse_out, float* O_out, void* stream);
+int pfa_sparse_layer_rpb(const pfa_shape* shape, const void* Q, const void* K, const void* V, const float* bias,
+                         const int32_t* I_prev, int32_t i_prev_shared, const float* A_prev,
+                         int32_t K_prev, int32_t K_l, int32_t* I_out, float* A_out, float* O_out,
+                         void* stream);
+
+/*
  * The first two layers of a chain fused, with the first layer's map never
  * written to memory. Computes what pfa_dense_layer (K1 = N) followed by
  * pfa_sparse_layer (I_prev = NULL, A_prev = that map, K_l = K2_keep) compute,

@@ -206,13 +206,15 @@ def chain(layers_qkv, *, win, shifts, Ks, wh_list=None):
     return outs
 
 
-def dense_lse(Q, K, *, win, shift, wh_list=None):
+def dense_lse(Q, K, *, win, shift, wh_list=None, bias=None):
     """ln sum_j exp(q_i . k_j / sqrt(d)) over the N slots of each window, per query
     slot i: the denominator of the first layer's full softmax map (paper notes,
     "Progressive focused resource allocation strategy": the first layer computes
     the complete map), i.e. A^1_ij = exp(s_ij - lse_i). Slot t of window (a, b)
     reads pixel ((a*win + t//win + shift) mod H, (b*win + t%win + shift) mod W).
-    Returns [n_wh, N] fp64 in window-head order (b, head, window row, window col)."""
+    With ``bias`` ([heads, (2 win - 1)^2]) the scores carry the relative position
+    bias of ``layer``. Returns [n_wh, N] fp64 in window-head order (b, head,
+    window row, window col)."""
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     B, heads, H, W, d = Q.shape
@@ -229,6 +231,8 @@ def dense_lse(Q, K, *, win, shift, wh_list=None):
         y = (wy * win + t // win + shift) % H
         x = (wx * win + t % win + shift) % W
         s = Q[b, h, y, x] @ K[b, h, y, x].T / np.sqrt(d)
+        if bias is not None:
+            s = s + np.asarray(bias, np.float64)[h][rel_index(win)]
         m = s.max(axis=1, keepdims=True)
         out[n] = (m + np.log(np.exp(s - m).sum(axis=1, keepdims=True)))[:, 0]
     return out

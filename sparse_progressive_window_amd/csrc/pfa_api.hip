@@ -91,7 +91,7 @@ int elem_bytes(int dtype) { return dtype == PFA_F32 ? 4 : 2; }
 
 int64_t n_wh(const Geom& g) { return (int64_t)g.B * g.heads * g.nwy * g.nwx; }
 
-int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const void* V,
+int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const void* V, const float* bias,
                const int32_t* I_prev, int i_shared, const float* A_prev, int K_prev, int K_l,
                int32_t* I_out, float* A_out, float* O_out, hipStream_t stream) {
     pfa::SparseArgs a;
@@ -103,6 +103,7 @@ int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const voi
     a.i_shared = i_shared ? 1 : 0;
     a.scale2 = (float)(1.4426950408889634 / sqrt((double)g.d));
     a.Q1 = nullptr; a.K1 = nullptr; a.shift1 = 0;
+    a.bias = bias;
 
     const int rowb = g.d * elem_bytes(dtype);
     a.xcd_map = (n_wh(g) % 8 == 0) ? 1 : 0;
@@ -127,8 +128,8 @@ int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const voi
     // (bf16): each kernel then runs with more waves and the selection with more
     // radix bins.
     hipError_t e;
-    if (!I_prev && K_prev == 1024 && g.N == 1024) {
-        // every slot is a candidate: MFMA scores
+    if (!I_prev && K_prev == 1024 && g.N == 1024 && !bias) {
+        // every slot is a candidate: MFMA scores (with a bias, the gather kernel)
         e = timed(PFA_KERNEL_ALL_CANDIDATES, stream, [&] { return pfa::launch_all_cand(a, dtype, g.d, grid, stream); });
     } else {
         e = timed(PFA_KERNEL_SELECT, stream, [&] {
@@ -144,10 +145,10 @@ int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const voi
 
 extern "C" {
 
-int pfa_sparse_layer(const pfa_shape* shape, const void* Q, const void* K, const void* V,
-                     const int32_t* I_prev, int32_t i_prev_shared, const float* A_prev,
-                     int32_t K_prev, int32_t K_l, int32_t* I_out, float* A_out, float* O_out,
-                     void* stream) {
+int pfa_sparse_layer_rpb(const pfa_shape* shape, const void* Q, const void* K, const void* V, const float* bias,
+                         const int32_t* I_prev, int32_t i_prev_shared, const float* A_prev,
+                         int32_t K_prev, int32_t K_l, int32_t* I_out, float* A_out, float* O_out,
+                         void* stream) {
     Geom g;
     int code;
     if (!geom_from_shape(shape, &g, &code)) return code;
@@ -155,12 +156,21 @@ int pfa_sparse_layer(const pfa_shape* shape, const void* Q, const void* K, const
     if (K_prev < 1 || K_prev > g.N || K_l < 1 || K_l > K_prev) return PFA_ERR_INVALID;
     if (!I_prev && K_prev != g.N) return PFA_ERR_INVALID;
     if (K_prev > 1024) return PFA_ERR_UNSUPPORTED;
-    return run_sparse(g, shape->dtype, Q, K, V, I_prev, i_prev_shared, A_prev, K_prev, K_l, I_out,
+    if (bias && g.win == 0) return PFA_ERR_UNSUPPORTED;
+    return run_sparse(g, shape->dtype, Q, K, V, bias, I_prev, i_prev_shared, A_prev, K_prev, K_l, I_out,
                       A_out, O_out, static_cast<hipStream_t>(stream));
 }
 
-int pfa_dense_layer(const pfa_shape* shape, const void* Q, const void* K, const void* V, int32_t K1,
-                    int32_t* I_out, float* A_out, float* lse_out, float* O_out, void* stream) {
+int pfa_sparse_layer(const pfa_shape* shape, const void* Q, const void* K, const void* V,
+                     const int32_t* I_prev, int32_t i_prev_shared, const float* A_prev,
+                     int32_t K_prev, int32_t K_l, int32_t* I_out, float* A_out, float* O_out,
+                     void* stream) {
+    return pfa_sparse_layer_rpb(shape, Q, K, V, nullptr, I_prev, i_prev_shared, A_prev, K_prev, K_l, I_out, A_out,
+                                O_out, stream);
+}
+
+int pfa_dense_layer_rpb(const pfa_shape* shape, const void* Q, const void* K, const void* V, const float* bias,
+                        int32_t K1, int32_t* I_out, float* A_out, float* lse_out, float* O_out, void* stream) {
     Geom g;
     int code;
     if (!geom_from_shape(shape, &g, &code)) return code;
@@ -171,13 +181,15 @@ int pfa_dense_layer(const pfa_shape* shape, const void* Q, const void* K, const 
     if (K1 < g.N) {
         if (!I_out || !A_out) return PFA_ERR_INVALID;
         if (lse_out) return PFA_ERR_UNSUPPORTED;
-        return run_sparse(g, shape->dtype, Q, K, V, nullptr, 0, nullptr, g.N, K1, I_out, A_out,
+        return run_sparse(g, shape->dtype, Q, K, V, bias, nullptr, 0, nullptr, g.N, K1, I_out, A_out,
                           O_out, s);
     }
     if (g.win % 4) return PFA_ERR_UNSUPPORTED;
+    if (bias && g.win % 16) return PFA_ERR_UNSUPPORTED;
     pfa::DenseArgs a;
     a.Q = Q; a.K = K; a.V = V;
     a.A_out = A_out; a.lse_out = lse_out; a.O_out = O_out;
+    a.bias = bias;
     a.g = g;
     a.scale2 = (float)(1.4426950408889634 / sqrt((double)g.d));
     a.xcd_map = (n_wh(g) % 8 == 0) ? 1 : 0;
@@ -187,6 +199,11 @@ int pfa_dense_layer(const pfa_shape* shape, const void* Q, const void* K, const 
     if (e == hipSuccess && I_out)
         e = timed(PFA_KERNEL_IOTA, s, [&] { return pfa::launch_iota_rows(I_out, n_wh(g) * g.N, g.N, s); });
     return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
+}
+
+int pfa_dense_layer(const pfa_shape* shape, const void* Q, const void* K, const void* V, int32_t K1,
+                    int32_t* I_out, float* A_out, float* lse_out, float* O_out, void* stream) {
+    return pfa_dense_layer_rpb(shape, Q, K, V, nullptr, K1, I_out, A_out, lse_out, O_out, stream);
 }
 
 int pfa_first_two_layers(const pfa_shape* shape, int32_t shift1, int32_t shift2, const void* Q1,
@@ -210,6 +227,7 @@ int pfa_first_two_layers(const pfa_shape* shape, int32_t shift1, int32_t shift2,
     pfa::DenseArgs d;
     d.Q = Q1; d.K = K1; d.V = V1;
     d.A_out = nullptr; d.lse_out = lse1_out; d.O_out = O1_out;
+    d.bias = nullptr;
     d.g = g;
     d.g.shift = shift1;
     d.scale2 = scale2;
@@ -230,6 +248,7 @@ int pfa_first_two_layers(const pfa_shape* shape, int32_t shift1, int32_t shift2,
     a.i_shared = 0;
     a.scale2 = scale2;
     a.Q1 = Q1; a.K1 = K1; a.shift1 = shift1;
+    a.bias = nullptr;
     a.xcd_map = xcd;
     a.blocks_per_wh = 2;
     a.rows_per_block = g.N / 2;

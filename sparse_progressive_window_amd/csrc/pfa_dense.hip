@@ -210,7 +210,10 @@ __device__ __forceinline__ void tile_store_split(unsigned char* dst,
     }
 }
 
-template <typename T, int D, int KT, bool WA>
+// BIAS: the head's relative position bias (a (2w - 1)^2 table, staged in LDS
+// in base-2 units) is added to every scaled score; needs win % 16 == 0 so that
+// the 16 keys of an MFMA tile share one window row.
+template <typename T, int D, int KT, bool WA, bool BIAS = false>
 __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const DenseArgs p) {
     using Ops = DenseOps<T, D>;
     constexpr int ROWB = Ops::ROWB;
@@ -223,6 +226,7 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
     constexpr int KBUF = SPLIT ? 3 * KT * kSplitRow : KT * STRIDE;
     __shared__ __align__(16) unsigned char Ks[2][KBUF];
     __shared__ __align__(16) unsigned char Vs[2][KT * STRIDE];
+    __shared__ float btab[BIAS ? 63 * 63 : 1];
 
     const Geom g = p.g;
     const int N = g.N;
@@ -255,6 +259,25 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
     float* Oh = p.O_out + plane;
     const float sc = p.scale2;
 
+    // bias: this lane's query i = q0 + r16 at window row/column (iy, ix); key j
+    // of a tile at (jy, jx) reads btab[ibase - jy (2w - 1) - jx]
+    int ibase = 0;
+    const int wrow = 2 * g.win - 1;
+    if constexpr (BIAS) {
+        const int nrel = wrow * wrow;
+        const float* src = p.bias + (size_t)(bh % g.heads) * nrel;
+        for (int u = threadIdx.x; u < nrel; u += blockDim.x) btab[u] = src[u] * 1.4426950408889634f;
+        const int i = wave_active ? q0 + r16 : 0;
+        const int iy = i / g.win;
+        ibase = (iy + g.win - 1) * wrow + (i - iy * g.win) + g.win - 1;
+    }
+    // bias of keys key0 + 4 grp + r, r = 0..3 (one window row)
+    auto tile_bias = [&](int key0, float (&b)[4]) {
+        const int jy = key0 / g.win;
+        const int idx0 = ibase - jy * wrow - (key0 - jy * g.win) - 4 * grp;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) b[r] = btab[idx0 - r];
+    };
     const int qrow = wave_active ? q0 + r16 : 0;
     const typename Ops::Row qop = Ops::load(Qh + (size_t)slot_pixel(g, wy, wx, qrow) * ROWB, grp);
     bf8 qh, qm, ql;   // SPLIT: lane's 8 dims of its query in three parts
@@ -292,17 +315,39 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
         v4f acc[SUB];
 #pragma unroll
         for (int s = 0; s < SUB; ++s) acc[s] = tile_scores(kt, s);
-        float amax = acc[0][0];
-#pragma unroll
-        for (int s = 0; s < SUB; ++s)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) amax = fmaxf(amax, acc[s][r]);
-        const float mn = fmaxf(m, amax * sc);
         float lt = 0.0f;
+        float mn;
+        if constexpr (BIAS) {
+            // biased scores in scaled units, then the same running max / sum
 #pragma unroll
-        for (int s = 0; s < SUB; ++s)
+            for (int s = 0; s < SUB; ++s) {
+                float b[4];
+                tile_bias(t * KT + s * 16, b);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) lt += fast_exp2(fmaf(acc[s][r], sc, -mn));
+                for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(acc[s][r], sc, b[r]);
+            }
+            float amax = acc[0][0];
+#pragma unroll
+            for (int s = 0; s < SUB; ++s)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) amax = fmaxf(amax, acc[s][r]);
+            mn = fmaxf(m, amax);
+#pragma unroll
+            for (int s = 0; s < SUB; ++s)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) lt += fast_exp2(acc[s][r] - mn);
+        } else {
+            float amax = acc[0][0];
+#pragma unroll
+            for (int s = 0; s < SUB; ++s)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) amax = fmaxf(amax, acc[s][r]);
+            mn = fmaxf(m, amax * sc);
+#pragma unroll
+            for (int s = 0; s < SUB; ++s)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) lt += fast_exp2(fmaf(acc[s][r], sc, -mn));
+        }
         l = l * fast_exp2(m - mn) + lt;
         m = mn;
         if (t + 1 < ntiles) store_k(Ks[(t + 1) & 1], kreg);
@@ -347,8 +392,15 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
         for (int s = 0; s < SUB; ++s) {
             const v4f acc = tile_scores(kt, s);
             float pr[4];
+            if constexpr (BIAS) {
+                float b[4];
+                tile_bias(t * KT + s * 16, b);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(fmaf(acc[r], sc, -m)) * inv_l;
+                for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(fmaf(acc[r], sc, b[r] - m)) * inv_l;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(fmaf(acc[r], sc, -m)) * inv_l;
+            }
             if (WA) {
                 typedef int v4i __attribute__((ext_vector_type(4)));
                 const v4i pv = {__float_as_int(pr[0]), __float_as_int(pr[1]), __float_as_int(pr[2]),
@@ -385,6 +437,15 @@ __global__ void iota_rows_kernel(int32_t* I, int64_t total, int N) {
 
 template <typename T, int D, bool WA>
 void launch_dense_w(const DenseArgs& a, int grid, hipStream_t s) {
+    if (a.bias) {   // win % 16 == 0 (checked by the caller)
+        if (a.g.N % 64 == 0)
+            hipLaunchKernelGGL((dense_layer_kernel<T, D, 64, WA, true>), dim3(grid), dim3(kDenseWaves * kWave), 0, s,
+                               a);
+        else
+            hipLaunchKernelGGL((dense_layer_kernel<T, D, 16, WA, true>), dim3(grid), dim3(kDenseWaves * kWave), 0, s,
+                               a);
+        return;
+    }
     if (a.g.N % 64 == 0)
         hipLaunchKernelGGL((dense_layer_kernel<T, D, 64, WA>), dim3(grid), dim3(kDenseWaves * kWave), 0, s, a);
     else

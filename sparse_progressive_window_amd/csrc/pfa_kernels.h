@@ -31,6 +31,9 @@ struct SparseArgs {
     const void* Q1;
     const void* K1;
     int shift1;
+    // window mode, selection kernels: the layer's relative position bias, one
+    // (2 win - 1)^2 table per head (nullptr: none)
+    const float* bias;
 };
 
 // kKselect: window mode, K staged in LDS, selection only (O comes from
@@ -48,6 +51,7 @@ struct DenseArgs {
     Geom g;
     float scale2;
     int xcd_map;             // 1: the query blocks of a window-head run on one XCD (needs #wh % 8 == 0)
+    const float* bias;       // relative position bias, one (2 win - 1)^2 table per head, or nullptr
 };
 
 // Backward pass of a window-mode sparse layer with the kept sets held fixed.

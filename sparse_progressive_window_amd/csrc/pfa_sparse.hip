@@ -489,7 +489,11 @@ __device__ __forceinline__ void select_store(const SparseArgs& p, int lane, bool
 // FULL: K_prev == GL*KPT, so every candidate slot of an active row exists (no
 // per-candidate validity), scores stay raw until the exponent; inactive row
 // groups of the last iteration are scored on row0's data and never stored.
-template <typename T, int D, int GL, int KPT, int MODE, int NW, bool PQ, bool FULL>
+// BIAS (window mode): the head's relative position bias b[(dy + w - 1)(2w - 1) +
+// dx + w - 1] of (i, j) is added to the scaled score; the (2w - 1)^2-entry table
+// is read through a range-checked buffer resource (it stays in L1), because at
+// fp32 d = 32 the staged K rows and the histograms fill the LDS.
+template <typename T, int D, int GL, int KPT, int MODE, int NW, bool PQ, bool FULL, bool BIAS = false>
 __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseArgs p) {
     constexpr int EPC = Chunk<T>::kElems;   // elements per 16-byte chunk
     constexpr int CH = D / EPC;             // chunks per K/V row
@@ -603,6 +607,23 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
                 Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(qrow + coff[m]), &qf[m * EPC]);
         }
 
+        // relative position bias of (i, j_t) in base-2 units, loads issued before the scores
+        float b2[BIAS ? KPT : 1];
+        if constexpr (BIAS) {
+            const int nrel = (2 * g.win - 1) * (2 * g.win - 1);
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bias + (size_t)(w.bh % g.heads) * nrel, nrel * 4);
+            const int iy = (i * g.win_magic) >> 16;
+            const int ibase = (iy + g.win - 1) * (2 * g.win - 1) + (i - iy * g.win) + g.win - 1;
+#pragma unroll
+            for (int t = 0; t < KPT; ++t) {
+                const int jy = (jj[t] * g.win_magic) >> 16;
+                const int idx = ibase - jy * (2 * g.win - 1) - (jj[t] - jy * g.win);
+                b2[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, idx * 4, 0, 0));
+            }
+#pragma unroll
+            for (int t = 0; t < KPT; ++t) b2[t] *= 1.4426950408889634f;
+        }
+
         // SMM: scores over the candidate list only (base-2 units)
         float sv[KPT];
 #pragma unroll
@@ -617,9 +638,24 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) acc = fmaf(qf[m * EPC + e], kf[e], acc);
             }
-            sv[t] = FULL ? acc : (valid[t] ? acc * p.scale2 : -INFINITY);
+            if constexpr (BIAS)
+                sv[t] = (FULL || valid[t]) ? fmaf(acc, p.scale2, b2[t]) : -INFINITY;
+            else
+                sv[t] = FULL ? acc : (valid[t] ? acc * p.scale2 : -INFINITY);
         }
-        if (FULL) {
+        if (FULL && BIAS) {
+            // scores already scaled and biased: u = A^{l-1} exp2(s - max s)
+            float smax = sv[0];
+#pragma unroll
+            for (int t = 1; t < KPT; ++t) smax = fmaxf(smax, sv[t]);
+            const float c = -Grp<GL>::all(smax, MaxF());
+            const float* Arow = p.A_prev ? p.A_prev + row * K_prev + gl : nullptr;
+            float a[KPT];
+#pragma unroll
+            for (int t = 0; t < KPT; ++t) a[t] = Arow ? Arow[GL * t] : 1.0f;
+#pragma unroll
+            for (int t = 0; t < KPT; ++t) sv[t] = fmaxf(a[t] * fast_exp2(sv[t] + c), 0.0f);
+        } else if (FULL) {
             // u = A^{l-1} exp2(scale2 (s - max s)); fmaxf maps invalid previous weights to 0.
             // A^{l-1} is loaded only now: no prefetched weights occupy registers
             // during the scoring (the other waves of the SIMD cover the latency)
@@ -1023,6 +1059,15 @@ template <typename T, int D, int GL, int KPT, int MODE>
 hipError_t launch_one(const SparseArgs& a, int lds, int grid, hipStream_t s) {
     constexpr int NW = (KPT <= 4 || (MODE == kKselect && KPT <= 8)) ? 16 : 8;
     constexpr bool PQ = KPT <= 4 && D * sizeof(T) <= 64;   // prefetch q when registers allow
+    if constexpr (MODE == kKselect) {
+        if (a.bias) {
+            if (a.K_prev == GL * KPT)
+                return launch_fn(sparse_layer_kernel<T, D, GL, KPT, MODE, NW, PQ, true, true>, a, NW * kWave, lds,
+                                 grid, s);
+            return launch_fn(sparse_layer_kernel<T, D, GL, KPT, MODE, NW, PQ, false, true>, a, NW * kWave, lds, grid,
+                             s);
+        }
+    }
     if (MODE == kKselect && a.K_prev == GL * KPT)
         return launch_fn(sparse_layer_kernel<T, D, GL, KPT, MODE, NW, PQ, true>, a, NW * kWave, lds, grid, s);
     return launch_fn(sparse_layer_kernel<T, D, GL, KPT, MODE, NW, PQ, false>, a, NW * kWave, lds, grid, s);

@@ -41,6 +41,10 @@ def load():
         lib.pfa_dense_layer.restype = ctypes.c_int
         lib.pfa_sparse_layer.argtypes = [ctypes.POINTER(PfaShape), P, P, P, P, i32, P, i32, i32, P, P, P, P]
         lib.pfa_sparse_layer.restype = ctypes.c_int
+        lib.pfa_dense_layer_rpb.argtypes = [ctypes.POINTER(PfaShape), P, P, P, P, i32, P, P, P, P, P]
+        lib.pfa_dense_layer_rpb.restype = ctypes.c_int
+        lib.pfa_sparse_layer_rpb.argtypes = [ctypes.POINTER(PfaShape), P, P, P, P, P, i32, P, i32, i32, P, P, P, P]
+        lib.pfa_sparse_layer_rpb.restype = ctypes.c_int
         lib.pfa_first_two_layers.argtypes = [ctypes.POINTER(PfaShape), i32, i32, P, P, P, P, P, P, i32, P, P, P, P,
                                              P, P]
         lib.pfa_first_two_layers.restype = ctypes.c_int
@@ -123,11 +127,20 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def dense_layer(Q, K, V, K1=None, *, win, shift=0, want_A=True, want_I=False, out=None, lse_out=None):
+def _check_bias(bias, Q, win):
+    if bias is None:
+        return
+    if not win:
+        raise ValueError("a relative position bias needs window mode")
+    _expect(bias, Q.shape[1] * (2 * win - 1) ** 2, torch.float32, "bias")
+
+
+def dense_layer(Q, K, V, K1=None, *, win, shift=0, want_A=True, want_I=False, out=None, lse_out=None, bias=None):
     """First (dense) layer. Returns (I, A, O); I and A are None when not requested
     (K1 == N) and always returned when K1 < N. ``out`` = optional preallocated
     (I or None, A or None, O). ``lse_out``: optional [B, heads, nwin, N] fp32
-    tensor filled with each row's log softmax denominator (K1 == N only)."""
+    tensor filled with each row's log softmax denominator (K1 == N only).
+    ``bias``: optional [heads, (2 win - 1)^2] fp32 relative position bias."""
     _check_qkv(Q, K, V)
     lead, N = _geometry(Q, win)
     K1 = N if K1 is None else K1
@@ -145,18 +158,20 @@ def dense_layer(Q, K, V, K1=None, *, win, shift=0, want_A=True, want_I=False, ou
     _expect(A, rows * K1, torch.float32, "A_out")
     _expect(O, Q.numel(), torch.float32, "O_out")
     _expect(lse_out, rows, torch.float32, "lse_out")
+    _check_bias(bias, Q, win)
     shape = make_shape(Q, win, shift)
-    rc = load().pfa_dense_layer(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), K1, _ptr(I), _ptr(A),
-                                _ptr(lse_out), _ptr(O), _stream())
+    rc = load().pfa_dense_layer_rpb(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(bias), K1, _ptr(I), _ptr(A),
+                                    _ptr(lse_out), _ptr(O), _stream())
     if rc != 0:
         raise PfaError("pfa_dense_layer", rc)
     return I, A, O
 
 
-def sparse_layer(Q, K, V, I_prev, A_prev, K_l, *, win, shift=0, i_shared=False, K_prev=None, out=None):
+def sparse_layer(Q, K, V, I_prev, A_prev, K_l, *, win, shift=0, i_shared=False, K_prev=None, out=None, bias=None):
     """Sparse layer: scores only over I_prev, Hadamard with A_prev, top-K_l.
     I_prev None = all slots (K_prev = N); A_prev None = all ones.
-    ``out`` = optional preallocated (I, A, O). Returns (I, A, O)."""
+    ``out`` = optional preallocated (I, A, O); ``bias`` = optional [heads,
+    (2 win - 1)^2] fp32 relative position bias. Returns (I, A, O)."""
     _check_qkv(Q, K, V)
     lead, N = _geometry(Q, win)
     if I_prev is not None:
@@ -177,10 +192,11 @@ def sparse_layer(Q, K, V, I_prev, A_prev, K_l, *, win, shift=0, i_shared=False, 
     _expect(I, rows * K_l, torch.int32, "I_out")
     _expect(A, rows * K_l, torch.float32, "A_out")
     _expect(O, Q.numel(), torch.float32, "O_out")
+    _check_bias(bias, Q, win)
     shape = make_shape(Q, win, shift)
-    rc = load().pfa_sparse_layer(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(I_prev),
-                                 int(bool(i_shared)), _ptr(A_prev), K_prev, K_l, _ptr(I), _ptr(A),
-                                 _ptr(O), _stream())
+    rc = load().pfa_sparse_layer_rpb(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(bias), _ptr(I_prev),
+                                     int(bool(i_shared)), _ptr(A_prev), K_prev, K_l, _ptr(I), _ptr(A),
+                                     _ptr(O), _stream())
     if rc != 0:
         raise PfaError("pfa_sparse_layer", rc)
     return I, A, O

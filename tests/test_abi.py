@@ -32,6 +32,7 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"pfa_dense_layer", "pfa_sparse_layer", "pfa_first_two_layers", "pfa_sparse_layer_backward",
             "pfa_sparse_layer_backward_workspace", "pfa_iet_propagate", "pfa_iet_propagate_workspace",
+            "pfa_dense_layer_rpb", "pfa_sparse_layer_rpb",
             "pfa_strerror", "pfa_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -198,3 +199,17 @@ def test_iet_validation(lib):
     assert prop(N=65537, ws_bytes=1 << 30) == -2
     assert lib.pfa_iet_propagate_workspace(2, 4096, 22, 12) == 2 * 4096 * 34 * 4
     assert lib.pfa_iet_propagate_workspace(1, 0, 22, 12) == -1
+
+
+def test_rpb_validation(lib):
+    def sp(s, bias=FAKE, K_prev=64, K_l=16):
+        return lib.pfa_sparse_layer_rpb(ctypes.byref(s), FAKE, FAKE, FAKE, bias, FAKE, 0, FAKE, K_prev, K_l,
+                                        FAKE, FAKE, FAKE, None)
+
+    def de(s, bias=FAKE, K1=1024):
+        return lib.pfa_dense_layer_rpb(ctypes.byref(s), FAKE, FAKE, FAKE, bias, K1, None, None, None, FAKE, None)
+    assert sp(shape(win=0, H=64, W=64)) == -2                   # no bias in global mode
+    assert sp(shape(), K_l=0) == -1
+    assert de(shape(win=12, H=24, W=24), K1=144) == -2          # dense with a bias needs win % 16 == 0
+    assert de(shape(d=8)) == -2
+    assert de(shape(), K1=0) == -1
