@@ -351,18 +351,27 @@ def backward_leg(w, qkv, outs, implicit, args, torch, pfa):
         by = bwd_kernel_bytes(w, l, part, implicit[l]) * w.n_wh
         gbs = by / (ms * 1e-3) / 1e9
         name = "bwd_dkv_kernel" if part == "scatter" else f"bwd_rows_kernel({part})"
-        kernels.append({"layer": l + 1, "kernel": name, "launches": len(v), "ms": round(ms, 4), "alg_bytes": by,
-                        "GB_per_s": round(gbs, 1), "bound": "hbm", "frac": round(gbs / HBM_PEAK_GBS, 4)})
+        k = {"layer": l + 1, "kernel": name, "launches": len(v), "ms": round(ms, 4), "alg_bytes": by,
+             "GB_per_s": round(gbs, 1), "bound": "hbm", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if part == "scatter" and w.N % 16 == 0:
+            # dV = A^T dO and dK = (A g)^T Q as dense fp32 MFMA products: 4 N^2 d flops per window-head
+            fl = 4 * w.N * w.N * w.d * w.n_wh
+            tfs = fl / (ms * 1e-3) / 1e12
+            k.update({"alg_flops": fl, "TFLOP_per_s": round(tfs, 2)})
+            if fl / (FP32_MFMA_PEAK_TFLOPS * 1e12) > by / (HBM_PEAK_GBS * 1e9):
+                k.update({"bound": "mfma", "frac": round(tfs / FP32_MFMA_PEAK_TFLOPS, 4)})
+        kernels.append(k)
     layer_ms = {l + 1: round(sum(k["ms"] for k in kernels if k["layer"] == l + 1), 4) for l in range(1, L)}
     kept = sum(w.n_wh * N * w.K[l] for l in range(1, L))
     dom = max(kernels, key=lambda k: k["ms"])
+    if dom["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": dom["TFLOP_per_s"], "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": dom["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof.update({"frac": dom["frac"], "traffic": None, "kernel": dom["kernel"], "layer": dom["layer"],
+                 "ms_per_launch": dom["ms"], "alg_bytes_per_launch": dom["alg_bytes"]})
     return {"ms_per_step": round(ms_per_step, 4), "layers": f"{L}..2", "layer_ms": layer_ms,
-            "kept_pairs_per_s": kept / (ms_per_step * 1e-3),
-            "roofline": {"bound": "hbm", "achieved": dom["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": dom["frac"], "traffic": stored_traffic(w.name, dom["kernel"], dom["layer"]),
-                         "kernel": dom["kernel"], "layer": dom["layer"], "ms_per_launch": dom["ms"],
-                         "alg_bytes_per_launch": dom["alg_bytes"]},
-            "kernels": kernels}
+            "kept_pairs_per_s": kept / (ms_per_step * 1e-3), "roofline": roof, "kernels": kernels}
 
 
 def global_leg(args, torch, pfa):
