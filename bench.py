@@ -29,7 +29,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 COUNTERS_FILE = "hbm_counters_{workload}.md"
 
 # kernel kinds of the library's timing calls (pfa_kernel_kind)
-DENSE, ALL_CAND, SPARSE, SELECT, AGGREGATE, IOTA, BWD_ROWS, BWD_SCATTER, IET_RANK, IET_UNION = range(10)
+DENSE, ALL_CAND, SPARSE, SELECT, AGGREGATE, IOTA, BWD_ROWS, BWD_SCATTER, IET_RANK, IET_UNION, DENSE_BWD = range(11)
 
 
 def kernel_bytes(w, l, kind, i_prev_implicit, split, fused=False):
@@ -281,11 +281,15 @@ def main():
     if not args.no_backward and not fused:
         try:
             result["backward"] = backward_leg(w, qkv, outs, implicit, args, torch, pfa)
+            if not args.no_cpu_baseline:
+                result["backward"]["cpu_baseline"] = cpu_baseline_backward(w, host, outs, implicit)
         except Exception as e:   # the forward line stands on its own
             result["backward"] = {"error": repr(e)}
     if not args.no_global:
         try:
             result["global"] = global_leg(args, torch, pfa)
+            if not args.no_cpu_baseline:
+                result["global"]["cpu_baseline"] = cpu_baseline_global()
         except Exception as e:   # the forward line stands on its own
             result["global"] = {"error": repr(e)}
     if not args.no_cpu_baseline:
@@ -294,9 +298,10 @@ def main():
 
 
 def backward_leg(w, qkv, outs, implicit, args, torch, pfa):
-    """Backward of the sparse layers L..2 of the chain just run (kept sets from
-    its forward outputs), each layer taking the next one's dA^{l} output and a
-    seeded dO; timed like the forward step, per kernel with HIP events."""
+    """Backward of the whole chain just run: the sparse layers L..2 (kept sets
+    from its forward outputs), each taking the next one's dA^{l} output and a
+    seeded dO, then the dense first layer with the second layer's dA^1; timed
+    like the forward step, per kernel with HIP events."""
     dev = qkv[0][0].device
     L, N = w.layers, w.N
     lead = (w.B, w.heads, w.n_windows)
@@ -307,6 +312,11 @@ def backward_leg(w, qkv, outs, implicit, args, torch, pfa):
     dA_prev = [None] + [torch.empty(lead + (N, w.K[l - 1]), dtype=torch.float32, device=dev) for l in range(1, L)]
     ws = torch.empty(max(pfa.backward_workspace_bytes(qkv[l][0], w.K[l], win=w.win) for l in range(1, L)),
                      dtype=torch.uint8, device=dev)
+    # the dense layer's log denominators (its forward in the timed step writes A^1, not these)
+    dense_bwd = w.K[0] == N and implicit[1]
+    lse = torch.empty(lead + (N,), dtype=torch.float32, device=dev)
+    if dense_bwd:
+        pfa.dense_layer(*qkv[0], win=w.win, shift=w.shifts[0], want_A=False, lse_out=lse)
 
     def bstep(marks=None):
         for l in range(L - 1, 0, -1):
@@ -316,6 +326,11 @@ def backward_leg(w, qkv, outs, implicit, args, torch, pfa):
             pfa.sparse_layer_backward(Q, K, V, I_prev, outs[l - 1][1], outs[l][0], outs[l][1], dO[l], dA,
                                       win=w.win, shift=w.shifts[l], K_prev=w.K[l - 1],
                                       out=grads[l] + (dA_prev[l],), workspace=ws)
+            if marks is not None:
+                marks.append(pfa.timing_count())
+        if dense_bwd:
+            pfa.dense_layer_backward(*qkv[0], lse, dO[0], dA_prev[1], win=w.win, shift=w.shifts[0], out=grads[0],
+                                     workspace=ws)
             if marks is not None:
                 marks.append(pfa.timing_count())
 
@@ -335,8 +350,14 @@ def backward_leg(w, qkv, outs, implicit, args, torch, pfa):
     assert dropped == 0 and len(recs) == marks[-1], (dropped, len(recs), marks[-1])
     per = {}
     start = 0
+    nlay = L if dense_bwd else L - 1
     for i, end in enumerate(marks):
-        l = L - 1 - (i % (L - 1))
+        l = L - 1 - (i % nlay)
+        if l == 0:
+            for kind, ms in recs[start:end]:
+                per.setdefault((0, "dense"), []).append(ms)
+            start = end
+            continue
         rows = [ms for kind, ms in recs[start:end] if kind == BWD_ROWS]
         parts = ["V", "K"] if len(rows) == 2 else ["KV"]
         for part, ms in zip(parts, rows):
@@ -348,6 +369,19 @@ def backward_leg(w, qkv, outs, implicit, args, torch, pfa):
     kernels = []
     for (l, part), v in sorted(per.items()):
         ms = float(np.mean(v))
+        if part == "dense":
+            # Q, K, V, lse, dO, dA^1 read; dQ, dK, dV written; 5 products of 2 N^2 d flops
+            x = N * w.d * (4 if w.dtype == "f32" else 2)
+            by = (3 * x + N * 4 + N * w.d * 4 + N * N * 4 + 3 * N * w.d * 4) * w.n_wh
+            fl = 10 * N * N * w.d * w.n_wh
+            tfs = fl / (ms * 1e-3) / 1e12
+            gbs = by / (ms * 1e-3) / 1e9
+            mfma = fl / (FP32_MFMA_PEAK_TFLOPS * 1e12) > by / (HBM_PEAK_GBS * 1e9)
+            kernels.append({"layer": 1, "kernel": "dense_bwd(dq+dkv)", "launches": len(v), "ms": round(ms, 4),
+                            "alg_bytes": by, "GB_per_s": round(gbs, 1), "alg_flops": fl,
+                            "TFLOP_per_s": round(tfs, 2), "bound": "mfma" if mfma else "hbm",
+                            "frac": round(tfs / FP32_MFMA_PEAK_TFLOPS if mfma else gbs / HBM_PEAK_GBS, 4)})
+            continue
         by = bwd_kernel_bytes(w, l, part, implicit[l]) * w.n_wh
         gbs = by / (ms * 1e-3) / 1e9
         name = "bwd_dkv_kernel" if part == "scatter" else f"bwd_rows_kernel({part})"
@@ -361,8 +395,9 @@ def backward_leg(w, qkv, outs, implicit, args, torch, pfa):
             if fl / (FP32_MFMA_PEAK_TFLOPS * 1e12) > by / (HBM_PEAK_GBS * 1e9):
                 k.update({"bound": "mfma", "frac": round(tfs / FP32_MFMA_PEAK_TFLOPS, 4)})
         kernels.append(k)
-    layer_ms = {l + 1: round(sum(k["ms"] for k in kernels if k["layer"] == l + 1), 4) for l in range(1, L)}
-    kept = sum(w.n_wh * N * w.K[l] for l in range(1, L))
+    layer_ms = {l + 1: round(sum(k["ms"] for k in kernels if k["layer"] == l + 1), 4)
+                for l in range(0 if dense_bwd else 1, L)}
+    kept = sum(w.n_wh * N * w.K[l] for l in range(0 if dense_bwd else 1, L))
     dom = max(kernels, key=lambda k: k["ms"])
     if dom["bound"] == "mfma":
         roof = {"bound": "mfma", "achieved": dom["TFLOP_per_s"], "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
@@ -370,7 +405,7 @@ def backward_leg(w, qkv, outs, implicit, args, torch, pfa):
         roof = {"bound": "hbm", "achieved": dom["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof.update({"frac": dom["frac"], "traffic": None, "kernel": dom["kernel"], "layer": dom["layer"],
                  "ms_per_launch": dom["ms"], "alg_bytes_per_launch": dom["alg_bytes"]})
-    return {"ms_per_step": round(ms_per_step, 4), "layers": f"{L}..2", "layer_ms": layer_ms,
+    return {"ms_per_step": round(ms_per_step, 4), "layers": f"{L}..1" if dense_bwd else f"{L}..2", "layer_ms": layer_ms,
             "kept_pairs_per_s": kept / (ms_per_step * 1e-3), "roofline": roof, "kernels": kernels}
 
 
@@ -434,6 +469,54 @@ def global_leg(args, torch, pfa):
     return {"workload": w.name, "pairs": pairs, "attention_pairs_per_s": pairs / (attn_ms * 1e-3),
             "iet_blocks_k1_k2": blocks, "kernels": kernels,
             "note": "working set fits the MALL: latency-bound, HBM fraction not meaningful"}
+
+
+def cpu_baseline_backward(w, host, outs, implicit, sample=64):
+    """fp64 backward oracle on `sample` window-heads of each sparse layer, with
+    the GPU forward's kept sets (the backward holds them fixed): kept pairs/s."""
+    import oracle
+    sel = np.linspace(0, w.n_wh - 1, sample).astype(np.int64)
+    N = w.N
+    g = np.random.Generator(np.random.PCG64(4243))
+    t_total, kept = 0.0, 0
+    for l in range(1, w.layers):
+        Q, K, V = (t.exact for t in host[l])
+        keep = outs[l][0].view(-1, N, w.K[l])[sel].cpu().numpy()
+        Ip = None if implicit[l] else outs[l - 1][0].view(-1, N, w.K[l - 1])[sel].cpu().numpy()
+        Ap = outs[l - 1][1].view(-1, N, w.K[l - 1])[sel].cpu().numpy()
+        dO = g.standard_normal(Q.shape)
+        dA = g.standard_normal(keep.shape) if l < w.layers - 1 else None
+        t0 = time.perf_counter()
+        oracle.layer_backward(Q, K, V, win=w.win, shift=w.shifts[l], keep=keep, dO=dO, dA=dA, I_prev=Ip, A_prev=Ap,
+                              prev_compact=True, wh_list=sel)
+        t_total += time.perf_counter() - t0
+        kept += len(sel) * N * w.K[l]
+    return {"value": kept / t_total, "unit": "kept pairs/s (backward, layers 6..2)", "cores": oracle.threads(),
+            "kind": "oracle", "sample": f"{len(sel)} of {w.n_wh} window-heads per layer ({kept} kept pairs, "
+                                        f"{t_total:.1f} s of oracle time)"}
+
+
+def cpu_baseline_global():
+    """fp64 oracle of the global individualized attention (6 heads) and the
+    index propagation of the first IET block, on the whole 64x64 workload."""
+    import oracle
+    from sparse_progressive_window_amd import inputs, workloads
+    w = workloads.GLOBAL64
+    Qt, Kt, Vt = inputs.qkv(w, 0, 0)
+    Iidx = inputs.global_index(w)
+    N, k = w.N, w.k_global
+    t0 = time.perf_counter()
+    r = oracle.layer(Qt.exact, Kt.exact, Vt.exact, win=0, shift=0, K_l=k, I_prev=Iidx.reshape(1, 1, 1, N, k),
+                     i_shared=True, wh_list=np.arange(w.heads))
+    t_attn = time.perf_counter() - t0
+    A = r["A"].astype(np.float32).reshape(w.heads, N, k)
+    t0 = time.perf_counter()
+    oracle.iet_propagate(Iidx, A, 22, 12)
+    t_prop = time.perf_counter() - t0
+    return {"value": w.heads * N * k / t_attn, "unit": "candidate pairs/s (global attention)",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"whole workload: attention {t_attn:.2f} s; one propagation (k1 = 22, k2 = 12, single-threaded "
+                      f"Python oracle) {t_prop:.2f} s"}
 
 
 def cpu_baseline(w, host, sample):

@@ -207,6 +207,34 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
 int64_t pfa_sparse_layer_backward_workspace(const pfa_shape* shape, int32_t K_l);
 
 /*
+ * Backward pass of the dense first layer (window mode): softmax attention over
+ * the window's N slots, P_ij = exp(s_ij - lse_i), O = P V ("Progressive focused
+ * resource allocation strategy": the first layer keeps every slot). Its map
+ * A^1 = P also feeds the second layer, so dA (the second layer's dA_prev, with
+ * I_prev = NULL) is an input besides dO:
+ *   G_ij = dA_ij + dO_i . v_j,   D_i = sum_j P_ij G_ij,   dS_ij = P_ij (G_ij - D_i)
+ *   dQ = dS K / sqrt(d),   dK = dS^T Q / sqrt(d),   dV = P^T dO.
+ *
+ * Q, K, V, bias  the forward call's inputs (bias: as pfa_dense_layer_rpb, or NULL).
+ * lse     [B, heads, nwin, N] fp32: the forward's lse_out (P is recomputed).
+ * dO      [B, heads, H, W, d] fp32 gradient of O.
+ * dA      [B, heads, nwin, N, N] fp32 gradient of A^1, or NULL (zero).
+ * dQ, dK, dV  [B, heads, H, W, d] fp32 outputs, every element written.
+ * workspace  at least pfa_dense_layer_backward_workspace() bytes (one fp32
+ *         per query slot), owned by the caller.
+ * Deterministic (no atomics). Window sides that are multiples of 8 (of 16 with
+ * a bias). Errors: PFA_ERR_INVALID for NULL required pointers or a small
+ * workspace; PFA_ERR_UNSUPPORTED for global mode, win % 8 != 0, a bias with
+ * win % 16 != 0, and the shape limits of pfa_dense_layer.
+ */
+int pfa_dense_layer_backward(const pfa_shape* shape, const void* Q, const void* K, const void* V, const float* bias,
+                             const float* lse, const float* dO, const float* dA, float* dQ, float* dK, float* dV,
+                             void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes pfa_dense_layer_backward needs, or a negative shape error. Host only. */
+int64_t pfa_dense_layer_backward_workspace(const pfa_shape* shape);
+
+/*
  * Propagation and sparsification of an individualized index matrix between
  * attention blocks ("From Local Windows to Adaptive Candidates via
  * Individualized Exploratory": propagation and sparsification paragraphs,
@@ -262,7 +290,9 @@ typedef enum {
     PFA_KERNEL_BWD_SCATTER = 7,    /* backward: dK, dV per window-head ("bwd_dkv_kernel" on MFMA,
                                       "bwd_scatter_kernel" by LDS adds when N % 16 != 0) */
     PFA_KERNEL_IET_RANK = 8,       /* index propagation: top-k1 / top-k2 of each row */
-    PFA_KERNEL_IET_UNION = 9       /* index propagation: de-duplicated union per row */
+    PFA_KERNEL_IET_UNION = 9,      /* index propagation: de-duplicated union per row */
+    PFA_KERNEL_DENSE_BWD = 10      /* backward of the dense layer ("dense_bwd_dq_kernel" then
+                                      "dense_bwd_dkv_kernel", one record for both) */
 } pfa_kernel_kind;
 
 /* capacity > 0: create 2*capacity events and start recording (earlier records

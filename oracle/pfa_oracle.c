@@ -280,6 +280,8 @@ int oracle_layer_backward(int B, int heads, int H, int W, int d, int win, int sh
         double* pp = (double*)malloc(sizeof(double) * K_prev);     /* P' */
         double* gpp = (double*)malloc(sizeof(double) * K_prev);    /* gradient of P' */
         int* slot = (int*)malloc(sizeof(int) * K_prev);            /* position in keep, -1 dropped */
+        int* pos_of = (int*)malloc(sizeof(int) * N);               /* token -> position in keep */
+        for (int t = 0; t < N; ++t) pos_of[t] = -1;
 
         for (int i = 0; i < N; ++i) {
             const int64_t qpix = pixel_of(win, shift, H, W, wy, wx, i);
@@ -314,14 +316,19 @@ int oracle_layer_backward(int B, int heads, int H, int W, int d, int win, int sh
             for (int c = 0; c < K_prev; ++c) pp[c] /= sp;
             /* step 7 replaced by the given kept set */
             int n_kept = 0;
+            int ok = 1;
+            for (int t = 0; t < K_l; ++t) {
+                if (kp[t] < 0 || kp[t] >= N) ok = 0;
+                else pos_of[kp[t]] = t;
+            }
             for (int c = 0; c < K_prev; ++c) {
                 const int j = C ? C[c] : c;
-                slot[c] = -1;
-                for (int t = 0; t < K_l; ++t)
-                    if (kp[t] == j) slot[c] = t;
+                slot[c] = (j >= 0 && j < N) ? pos_of[j] : -1;
                 if (slot[c] >= 0) ++n_kept;
             }
-            if (n_kept != K_l) { bad = 1; continue; }
+            for (int t = 0; t < K_l; ++t)
+                if (kp[t] >= 0 && kp[t] < N) pos_of[kp[t]] = -1;
+            if (!ok || n_kept != K_l) { bad = 1; continue; }
             double S = 0.0;
             for (int c = 0; c < K_prev; ++c) if (slot[c] >= 0) S += pp[c];
 
@@ -373,7 +380,7 @@ int oracle_layer_backward(int B, int heads, int H, int W, int d, int win, int sh
                 }
             }
         }
-        free(s); free(acal); free(pp); free(gpp); free(slot);
+        free(s); free(acal); free(pp); free(gpp); free(slot); free(pos_of);
     }
     return bad ? -1 : 0;
 }

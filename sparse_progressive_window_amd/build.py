@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpfa.so")
 OBJ = os.path.join(ROOT, "_build")
-SOURCES = ["pfa_api.hip", "pfa_sparse.hip", "pfa_dense.hip", "pfa_backward.hip", "pfa_iet.hip"]
+SOURCES = ["pfa_api.hip", "pfa_sparse.hip", "pfa_dense.hip", "pfa_backward.hip", "pfa_iet.hip", "pfa_dense_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -331,6 +331,41 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
     return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
 }
 
+int64_t pfa_dense_layer_backward_workspace(const pfa_shape* shape) {
+    Geom g;
+    int code;
+    if (!geom_from_shape(shape, &g, &code)) return code;
+    return n_wh(g) * g.N * 4;
+}
+
+int pfa_dense_layer_backward(const pfa_shape* shape, const void* Q, const void* K, const void* V, const float* bias,
+                             const float* lse, const float* dO, const float* dA, float* dQ, float* dK, float* dV,
+                             void* workspace, int64_t workspace_bytes, void* stream) {
+    Geom g;
+    int code;
+    if (!geom_from_shape(shape, &g, &code)) return code;
+    if (g.win == 0) return PFA_ERR_UNSUPPORTED;
+    if (!Q || !K || !V || !lse || !dO || !dQ || !dK || !dV || !workspace) return PFA_ERR_INVALID;
+    if (workspace_bytes < n_wh(g) * g.N * 4) return PFA_ERR_INVALID;
+    if (g.win % 8) return PFA_ERR_UNSUPPORTED;
+    if (bias && g.win % 16) return PFA_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    pfa::DenseBwdArgs a;
+    a.Q = Q; a.K = K; a.V = V;
+    a.bias = bias; a.lse = lse; a.dO = dO; a.dA = dA;
+    a.dQ = dQ; a.dK = dK; a.dV = dV;
+    a.Dws = static_cast<float*>(workspace);
+    a.g = g;
+    a.scale2 = (float)(1.4426950408889634 / sqrt((double)g.d));
+    a.scale = (float)(1.0 / sqrt((double)g.d));
+    a.xcd_map = (n_wh(g) % 8 == 0) ? 1 : 0;
+    const int64_t grid = n_wh(g) * pfa::dense_bwd_blocks(g.N);
+    if (grid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
+    const hipError_t e = timed(PFA_KERNEL_DENSE_BWD, s,
+                               [&] { return pfa::launch_dense_backward(a, shape->dtype, g.d, (int)grid, s); });
+    return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
+}
+
 int64_t pfa_iet_propagate_workspace(int32_t B, int32_t N, int32_t k1, int32_t k2) {
     if (B < 1 || N < 1 || k1 < 1 || k2 < 1) return PFA_ERR_INVALID;
     return (int64_t)B * N * (k1 + k2) * 4;
@@ -414,6 +449,7 @@ const char* pfa_kernel_name(int32_t kind) {
         case PFA_KERNEL_BWD_SCATTER: return "bwd_dkv";
         case PFA_KERNEL_IET_RANK: return "iet_rank_kernel";
         case PFA_KERNEL_IET_UNION: return "iet_union_kernel";
+        case PFA_KERNEL_DENSE_BWD: return "dense_bwd";
         default: return "unknown";
     }
 }

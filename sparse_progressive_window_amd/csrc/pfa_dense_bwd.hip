@@ -1,0 +1,338 @@
+// Backward pass of the dense first layer on gfx950 (fp32 MFMA throughout).
+//
+// The first layer is softmax attention over the N slots of a window (paper notes
+// "Progressive Focused Transformer for Single Image Super-Resolution", section
+// "Progressive focused resource allocation strategy"): P_ij = exp(s_ij - lse_i),
+// s_ij = q_i.k_j / sqrt(d) (+ the relative position bias), O = P V. Its map A^1 = P
+// also feeds the second layer, so the gradient of the loss reaches it both
+// through O and directly (dA = the second layer's gradient of A^{l-1}):
+//   G_ij = dA_ij + dO_i.v_j,   D_i = sum_j P_ij G_ij,   dS_ij = P_ij (G_ij - D_i)
+//   dQ = dS K / sqrt(d),   dK = dS^T Q / sqrt(d),   dV = P^T dO.
+// P is recomputed from Q, K and the forward's log denominators lse (what the
+// dense layer writes to lse_out).
+//
+// dense_bwd_dq_kernel: 8 waves x 16 queries per workgroup; K/V tiles of 64 slots
+//   staged in LDS as fp32. Pass 1 accumulates D_i, pass 2 forms dS and dQ. Scores
+//   and dO.v come transposed (16 keys x 16 queries per v_mfma_f32_16x16x4_f32
+//   chain), which leaves lane (query r16, keys 4 grp + r): the A-operand layout
+//   of dS K.
+// dense_bwd_dkv_kernel: 8 waves x 16 keys per workgroup; Q/dO tiles of 64 slots
+//   (with their lse and D) staged in LDS. Scores as (query 4 grp + r, key r16)
+//   per lane: the A-operand layout of P^T dO and dS^T Q. dV, dK stay in
+//   registers over all query tiles.
+#include "pfa_kernels.h"
+#include "pfa_rows.h"
+
+namespace pfa {
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kBwdWaves = 8;
+constexpr int kTile = 64;          // slots per LDS tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+// rows [r0, r0 + kTile) of a window (slot order) as fp32 into LDS, row stride STR floats
+template <typename T, int D, int STR>
+__device__ __forceinline__ void stage_f32(float* dst, const T* plane, const Geom& g, int wy, int wx, int r0) {
+    constexpr int EPC = Chunk<T>::kElems;
+    constexpr int CH = D / EPC;
+    for (int u = threadIdx.x; u < kTile * CH; u += blockDim.x) {
+        const int t = u / CH;
+        const int c = u - t * CH;
+        const unsigned char* src = reinterpret_cast<const unsigned char*>(plane) +
+                                   ((size_t)slot_pixel(g, wy, wx, r0 + t) * D) * sizeof(T) + c * 16;
+        float f[EPC];
+        Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(src), f);
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4)
+            *reinterpret_cast<float4*>(dst + t * STR + c * EPC + e) = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
+    }
+}
+
+// this lane's DPL dims [DPL grp, DPL grp + DPL) of one row of a [.., D] array of type T
+template <typename T, int D>
+__device__ __forceinline__ void row_dims(const T* row, int grp, float (&o)[D / 4]) {
+    constexpr int DPL = D / 4;
+    if constexpr (sizeof(T) == 4) {
+        const float* src = reinterpret_cast<const float*>(row) + grp * DPL;
+#pragma unroll
+        for (int x = 0; x < DPL; x += 4) {
+            const float4 f = *reinterpret_cast<const float4*>(src + x);
+            o[x] = f.x; o[x + 1] = f.y; o[x + 2] = f.z; o[x + 3] = f.w;
+        }
+    } else {
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(row) + grp * DPL;
+#pragma unroll
+        for (int x = 0; x < DPL; ++x) o[x] = __uint_as_float((uint32_t)src[x] << 16);
+    }
+}
+
+struct BlockPos {
+    int wh, blk, wy, wx, bh;
+};
+__device__ __forceinline__ BlockPos decode(const Geom& g, int blocks, int xcd_map) {
+    BlockPos b;
+    if (xcd_map) {   // the blocks of one window-head are consecutive workgroups of one XCD
+        const int xcd = blockIdx.x & 7;
+        const int slot = blockIdx.x >> 3;
+        b.blk = slot % blocks;
+        b.wh = (slot / blocks) * 8 + xcd;
+    } else {
+        b.wh = blockIdx.x / blocks;
+        b.blk = blockIdx.x - b.wh * blocks;
+    }
+    const int nwin = g.nwy * g.nwx;
+    const int win_id = b.wh % nwin;
+    b.bh = b.wh / nwin;
+    b.wy = win_id / g.nwx;
+    b.wx = win_id - b.wy * g.nwx;
+    return b;
+}
+
+template <typename T, int D, bool BIAS, bool HAS_DA>
+__global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const DenseBwdArgs p) {
+    constexpr int DPL = D / 4;
+    constexpr int CT = D / 16;
+    constexpr int STR = D + 4;   // padded fp32 LDS row
+    constexpr int SUB = kTile / 16;
+    __shared__ __align__(16) float Kt[kTile * STR];
+    __shared__ __align__(16) float Vt[kTile * STR];
+    __shared__ float btab[BIAS ? 63 * 63 : 1];
+
+    const Geom g = p.g;
+    const int N = g.N;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int r16 = lane & 15;
+    const int grp = lane >> 4;
+    const BlockPos bp = decode(g, (N + 16 * kBwdWaves - 1) / (16 * kBwdWaves), p.xcd_map);
+    const int q0 = bp.blk * 16 * kBwdWaves + wave * 16;
+    const bool wave_active = q0 < N;
+    const size_t plane = (size_t)bp.bh * g.H * g.W * D;
+    const T* Qh = static_cast<const T*>(p.Q) + plane;
+    const T* Kh = static_cast<const T*>(p.K) + plane;
+    const T* Vh = static_cast<const T*>(p.V) + plane;
+    const float sc = p.scale2;
+
+    const int qi = wave_active ? q0 + r16 : 0;   // this lane's query (operand layout)
+    float qv[DPL], dov[DPL];
+    row_dims<T, D>(Qh + (size_t)slot_pixel(g, bp.wy, bp.wx, qi) * D, grp, qv);
+    row_dims<float, D>(p.dO + plane + (size_t)slot_pixel(g, bp.wy, bp.wx, qi) * D, grp, dov);
+    const float lse2 = p.lse[(size_t)bp.wh * N + qi] * kLog2e;
+    const int wrow = 2 * g.win - 1;
+    int ibase = 0;
+    if constexpr (BIAS) {
+        const int nrel = wrow * wrow;
+        const float* src = p.bias + (size_t)(bp.bh % g.heads) * nrel;
+        for (int u = threadIdx.x; u < nrel; u += blockDim.x) btab[u] = src[u] * kLog2e;
+        const int iy = qi / g.win;
+        ibase = (iy + g.win - 1) * wrow + (qi - iy * g.win) + g.win - 1;
+    }
+    const float* dArow = HAS_DA ? p.dA + ((size_t)bp.wh * N + qi) * N : nullptr;
+
+    float Dq = 0.0f;
+    v4f dq[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) dq[c] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int t0 = 0; t0 < N; t0 += kTile) {
+            __syncthreads();   // the previous tile is consumed (and the bias table staged)
+            stage_f32<T, D, STR>(Kt, Kh, g, bp.wy, bp.wx, t0);
+            stage_f32<T, D, STR>(Vt, Vh, g, bp.wy, bp.wx, t0);
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < SUB; ++s) {
+                const int key0 = t0 + s * 16;
+                v4f st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
+                const float* kr = Kt + (s * 16 + r16) * STR + DPL * grp;
+                const float* vr = Vt + (s * 16 + r16) * STR + DPL * grp;
+#pragma unroll
+                for (int x = 0; x < DPL; ++x) {
+                    st = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[x], qv[x], st, 0, 0, 0);
+                    dpt = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[x], dov[x], dpt, 0, 0, 0);
+                }
+                // lane: query qi, keys key0 + 4 grp + r
+                float b[4] = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (BIAS) {
+                    const int jy = key0 / g.win;
+                    const int idx0 = ibase - jy * wrow - (key0 - jy * g.win) - 4 * grp;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) b[r] = btab[idx0 - r];
+                }
+                float4 da = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (HAS_DA) da = *reinterpret_cast<const float4*>(dArow + key0 + 4 * grp);
+                const float dav[4] = {da.x, da.y, da.z, da.w};
+                float P[4], G[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    P[r] = fast_exp2(fmaf(st[r], sc, b[r] - lse2));
+                    G[r] = dpt[r] + dav[r];
+                }
+                if (pass == 0) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Dq = fmaf(P[r], G[r], Dq);
+                } else {
+                    float dS[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dS[r] = P[r] * (G[r] - Dq);
+#pragma unroll
+                    for (int c = 0; c < CT; ++c)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            dq[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                dS[r], Kt[(s * 16 + 4 * grp + r) * STR + 16 * c + r16], dq[c], 0, 0, 0);
+                }
+            }
+        }
+        if (pass == 0) {
+            // the 4 lane groups hold the same query: full row sum D_i
+            Dq += __shfl_xor(Dq, 16);
+            Dq += __shfl_xor(Dq, 32);
+            if (wave_active && grp == 0) p.Dws[(size_t)bp.wh * N + qi] = Dq;
+        }
+    }
+    if (!wave_active) return;
+    // lane holds dQ[query q0 + 4 grp + r][dim 16 c + r16]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float* orow = p.dQ + plane + (size_t)slot_pixel(g, bp.wy, bp.wx, q0 + 4 * grp + r) * D;
+#pragma unroll
+        for (int c = 0; c < CT; ++c) orow[16 * c + r16] = dq[c][r] * p.scale;
+    }
+}
+
+template <typename T, int D, bool BIAS, bool HAS_DA>
+__global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dkv_kernel(const DenseBwdArgs p) {
+    constexpr int DPL = D / 4;
+    constexpr int CT = D / 16;
+    constexpr int STR = D + 4;
+    constexpr int SUB = kTile / 16;
+    __shared__ __align__(16) float Qt[kTile * STR];
+    __shared__ __align__(16) float dOt[kTile * STR];
+    __shared__ float lset[kTile];
+    __shared__ float Dt[kTile];
+    __shared__ float btab[BIAS ? 63 * 63 : 1];
+
+    const Geom g = p.g;
+    const int N = g.N;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int r16 = lane & 15;
+    const int grp = lane >> 4;
+    const BlockPos bp = decode(g, (N + 16 * kBwdWaves - 1) / (16 * kBwdWaves), p.xcd_map);
+    const int k0 = bp.blk * 16 * kBwdWaves + wave * 16;
+    const bool wave_active = k0 < N;
+    const size_t plane = (size_t)bp.bh * g.H * g.W * D;
+    const T* Qh = static_cast<const T*>(p.Q) + plane;
+    const T* Kh = static_cast<const T*>(p.K) + plane;
+    const T* Vh = static_cast<const T*>(p.V) + plane;
+    const float* dOh = p.dO + plane;
+    const float sc = p.scale2;
+
+    const int kj = wave_active ? k0 + r16 : 0;   // this lane's key (operand layout)
+    float kv[DPL], vv[DPL];
+    row_dims<T, D>(Kh + (size_t)slot_pixel(g, bp.wy, bp.wx, kj) * D, grp, kv);
+    row_dims<T, D>(Vh + (size_t)slot_pixel(g, bp.wy, bp.wx, kj) * D, grp, vv);
+    const int wrow = 2 * g.win - 1;
+    int kbase = 0;   // bias index of (query at window row/col (0, 0), this key)
+    if constexpr (BIAS) {
+        const int nrel = wrow * wrow;
+        const float* src = p.bias + (size_t)(bp.bh % g.heads) * nrel;
+        for (int u = threadIdx.x; u < nrel; u += blockDim.x) btab[u] = src[u] * kLog2e;
+        const int ky = kj / g.win;
+        kbase = (g.win - 1 - ky) * wrow + g.win - 1 - (kj - ky * g.win);
+    }
+    const float* dAcol = HAS_DA ? p.dA + (size_t)bp.wh * N * N + kj : nullptr;
+
+    v4f dv[CT], dk[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        dv[c] = v4f{0.f, 0.f, 0.f, 0.f};
+        dk[c] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int t0 = 0; t0 < N; t0 += kTile) {
+        __syncthreads();
+        stage_f32<T, D, STR>(Qt, Qh, g, bp.wy, bp.wx, t0);
+        stage_f32<float, D, STR>(dOt, dOh, g, bp.wy, bp.wx, t0);
+        for (int u = threadIdx.x; u < kTile; u += blockDim.x) {
+            lset[u] = p.lse[(size_t)bp.wh * N + t0 + u] * kLog2e;
+            Dt[u] = p.Dws[(size_t)bp.wh * N + t0 + u];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < SUB; ++s) {
+            const int qs = t0 + s * 16;   // queries qs + 4 grp + r of this lane
+            v4f st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
+            const float* qr = Qt + (s * 16 + r16) * STR + DPL * grp;
+            const float* dr = dOt + (s * 16 + r16) * STR + DPL * grp;
+#pragma unroll
+            for (int x = 0; x < DPL; ++x) {
+                st = __builtin_amdgcn_mfma_f32_16x16x4f32(qr[x], kv[x], st, 0, 0, 0);
+                dpt = __builtin_amdgcn_mfma_f32_16x16x4f32(dr[x], vv[x], dpt, 0, 0, 0);
+            }
+            float b[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (BIAS) {
+                const int qa = qs + 4 * grp;
+                const int qy = qa / g.win;
+                const int idx0 = kbase + qy * wrow + (qa - qy * g.win);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) b[r] = btab[idx0 + r];
+            }
+            float P[4], dS[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ql = s * 16 + 4 * grp + r;   // query within the tile
+                P[r] = fast_exp2(fmaf(st[r], sc, b[r] - lset[ql]));
+                const float G = dpt[r] + (HAS_DA ? dAcol[(size_t)(t0 + ql) * N] : 0.0f);
+                dS[r] = P[r] * (G - Dt[ql]);
+            }
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int ql = s * 16 + 4 * grp + r;
+                    dv[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(P[r], dOt[ql * STR + 16 * c + r16], dv[c], 0, 0, 0);
+                    dk[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(dS[r], Qt[ql * STR + 16 * c + r16], dk[c], 0, 0, 0);
+                }
+        }
+    }
+    if (!wave_active) return;
+    // lane holds dV / dK[key k0 + 4 grp + r][dim 16 c + r16]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const size_t o = plane + (size_t)slot_pixel(g, bp.wy, bp.wx, k0 + 4 * grp + r) * D;
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            p.dV[o + 16 * c + r16] = dv[c][r];
+            p.dK[o + 16 * c + r16] = dk[c][r] * p.scale;
+        }
+    }
+}
+
+template <typename T, int D, bool BIAS, bool HAS_DA>
+hipError_t launch_dbwd_t(const DenseBwdArgs& a, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((dense_bwd_dq_kernel<T, D, BIAS, HAS_DA>), dim3(grid), dim3(kBwdWaves * kWave), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dense_bwd_dkv_kernel<T, D, BIAS, HAS_DA>), dim3(grid), dim3(kBwdWaves * kWave), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_dbwd_d(const DenseBwdArgs& a, int grid, hipStream_t s) {
+    if (a.bias) return a.dA ? launch_dbwd_t<T, D, true, true>(a, grid, s) : launch_dbwd_t<T, D, true, false>(a, grid, s);
+    return a.dA ? launch_dbwd_t<T, D, false, true>(a, grid, s) : launch_dbwd_t<T, D, false, false>(a, grid, s);
+}
+
+}  // namespace
+
+int dense_bwd_blocks(int N) { return (N + 16 * kBwdWaves - 1) / (16 * kBwdWaves); }
+
+hipError_t launch_dense_backward(const DenseBwdArgs& a, int dtype, int D, int grid, hipStream_t stream) {
+    if (dtype == 0)
+        return D == 16 ? launch_dbwd_d<float, 16>(a, grid, stream) : launch_dbwd_d<float, 32>(a, grid, stream);
+    return D == 16 ? launch_dbwd_d<uint16_t, 16>(a, grid, stream) : launch_dbwd_d<uint16_t, 32>(a, grid, stream);
+}
+
+}  // namespace pfa

@@ -90,6 +90,27 @@ hipError_t launch_backward_dkv(const BackwardArgs& a, int dtype, int D, int grid
 int backward_scatter_parts(int D, int N, int K_l);
 hipError_t launch_backward_scatter(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream);
 
+// Backward pass of the dense first layer.
+struct DenseBwdArgs {
+    const void* Q;
+    const void* K;
+    const void* V;
+    const float* bias;       // relative position bias, one (2 win - 1)^2 table per head, or nullptr
+    const float* lse;        // [wh, N] the forward's ln sum_j exp(s_ij)
+    const float* dO;         // [B, heads, H, W, d]
+    const float* dA;         // [wh, N, N] gradient of the map, or nullptr
+    float* dQ;
+    float* dK;
+    float* dV;
+    float* Dws;              // workspace [wh, N]: D_i = sum_j P_ij G_ij
+    Geom g;
+    float scale2;            // log2(e) / sqrt(d)
+    float scale;             // 1 / sqrt(d)
+    int xcd_map;
+};
+int dense_bwd_blocks(int N);   // workgroups per window-head (each kernel)
+hipError_t launch_dense_backward(const DenseBwdArgs& a, int dtype, int D, int grid, hipStream_t stream);
+
 // Propagation / sparsification of an individualized index matrix.
 struct IetArgs {
     const int32_t* I;        // [B, N, k] token indices

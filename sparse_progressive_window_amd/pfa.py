@@ -53,6 +53,10 @@ def load():
         lib.pfa_sparse_layer_backward.restype = ctypes.c_int
         lib.pfa_sparse_layer_backward_workspace.argtypes = [ctypes.POINTER(PfaShape), i32]
         lib.pfa_sparse_layer_backward_workspace.restype = ctypes.c_int64
+        lib.pfa_dense_layer_backward.argtypes = [ctypes.POINTER(PfaShape)] + [P] * 11 + [ctypes.c_int64, P]
+        lib.pfa_dense_layer_backward.restype = ctypes.c_int
+        lib.pfa_dense_layer_backward_workspace.argtypes = [ctypes.POINTER(PfaShape)]
+        lib.pfa_dense_layer_backward_workspace.restype = ctypes.c_int64
         lib.pfa_iet_propagate.argtypes = [i32, i32, i32, i32, P, P, i32, i32, P, P, P, ctypes.c_int64, P]
         lib.pfa_iet_propagate.restype = ctypes.c_int
         lib.pfa_iet_propagate_workspace.argtypes = [i32, i32, i32, i32]
@@ -284,6 +288,38 @@ def sparse_layer_backward(Q, K, V, I_prev, A_prev, I_l, A_l, dO, dA_l=None, *, w
     return dQ, dK, dV, dAp
 
 
+def dense_layer_backward(Q, K, V, lse, dO, dA=None, *, win, shift=0, bias=None, out=None, workspace=None):
+    """Backward of the dense first layer: lse = the forward's lse_out
+    [B, heads, nwin, N]; dO fp32; dA = gradient of A^1 [B, heads, nwin, N, N]
+    or None. Returns (dQ, dK, dV) in fp32."""
+    _check_qkv(Q, K, V)
+    lead, N = _geometry(Q, win)
+    dev = Q.device
+    if out is None:
+        dQ, dK, dV = (torch.empty(Q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+    else:
+        dQ, dK, dV = out
+    rows = _prod(lead) * N
+    _expect(lse, rows, torch.float32, "lse")
+    _expect(dO, Q.numel(), torch.float32, "dO")
+    _expect(dA, rows * N, torch.float32, "dA")
+    for t, n in ((dQ, "dQ"), (dK, "dK"), (dV, "dV")):
+        _expect(t, Q.numel(), torch.float32, n)
+    _check_bias(bias, Q, win)
+    shape = make_shape(Q, win, shift)
+    need = int(load().pfa_dense_layer_backward_workspace(ctypes.byref(shape)))
+    if need < 0:
+        raise PfaError("pfa_dense_layer_backward_workspace", need)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = load().pfa_dense_layer_backward(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(bias), _ptr(lse),
+                                         _ptr(dO), _ptr(dA), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream())
+    if rc != 0:
+        raise PfaError("pfa_dense_layer_backward", rc)
+    return dQ, dK, dV
+
+
 def backward_workspace_bytes(Q, K_l, *, win, shift=0) -> int:
     shape = make_shape(Q, win, shift)
     n = int(load().pfa_sparse_layer_backward_workspace(ctypes.byref(shape), int(K_l)))
@@ -333,7 +369,7 @@ def iet_propagate(I, A, k1, k2, *, out=None, workspace=None):
 
 
 KERNEL_KINDS = ("dense", "all_candidates", "sparse", "select", "aggregate", "iota", "bwd_rows", "bwd_scatter",
-                "iet_rank", "iet_union")
+                "iet_rank", "iet_union", "dense_bwd")
 
 
 def kernel_name(kind: int) -> str:

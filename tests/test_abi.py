@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"pfa_dense_layer", "pfa_sparse_layer", "pfa_first_two_layers", "pfa_sparse_layer_backward",
             "pfa_sparse_layer_backward_workspace", "pfa_iet_propagate", "pfa_iet_propagate_workspace",
-            "pfa_dense_layer_rpb", "pfa_sparse_layer_rpb",
+            "pfa_dense_layer_rpb", "pfa_sparse_layer_rpb", "pfa_dense_layer_backward",
+            "pfa_dense_layer_backward_workspace",
             "pfa_strerror", "pfa_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -50,10 +51,10 @@ def test_timing_calls_without_device(lib):
     assert lib.pfa_timing_read(None, None, 0, None, None) == -1
     assert lib.pfa_timing_read(None, None, 4, ctypes.byref(n), None) == -1
     assert lib.pfa_timing_read(None, None, -1, ctypes.byref(n), None) == -1
-    names = [lib.pfa_kernel_name(k).decode() for k in range(10)]
+    names = [lib.pfa_kernel_name(k).decode() for k in range(11)]
     assert names == ["dense_layer_kernel", "all_cand", "sparse_layer_kernel",
                      "sparse_layer_kernel(select)", "aggregate", "iota_rows_kernel", "bwd_rows_kernel",
-                     "bwd_dkv", "iet_rank_kernel", "iet_union_kernel"]
+                     "bwd_dkv", "iet_rank_kernel", "iet_union_kernel", "dense_bwd"]
     assert lib.pfa_kernel_name(99) == b"unknown"
 
 
@@ -213,3 +214,17 @@ def test_rpb_validation(lib):
     assert de(shape(win=12, H=24, W=24), K1=144) == -2          # dense with a bias needs win % 16 == 0
     assert de(shape(d=8)) == -2
     assert de(shape(), K1=0) == -1
+
+
+def test_dense_backward_validation(lib):
+    def db(s, bias=None, ptr=FAKE, ws=FAKE, ws_bytes=1 << 20):
+        return lib.pfa_dense_layer_backward(ctypes.byref(s), FAKE, FAKE, FAKE, bias, ptr, FAKE, None, FAKE, FAKE, FAKE,
+                                            ws, ws_bytes, None)
+    assert db(shape(win=0, H=32, W=32)) == -2
+    assert db(shape(win=12, H=24, W=24)) == -2                  # win % 8 != 0
+    assert db(shape(win=8, H=16, W=16), bias=FAKE) == -2        # a bias needs win % 16 == 0
+    assert db(shape(), ptr=None) == -1                          # lse required
+    assert db(shape(), ws=None) == -1
+    assert db(shape(), ws_bytes=1024 * 4 - 4) == -1
+    assert db(shape(d=8)) == -2
+    assert lib.pfa_dense_layer_backward_workspace(ctypes.byref(shape(B=2, heads=3))) == 2 * 3 * 1024 * 4

@@ -2,9 +2,10 @@
 fp64 backward oracle (``oracle.layer_backward``), whose pins are in
 tests/test_oracle_backward_pins.py.
 
-Both sides take the GPU forward's kept sets I^l (the backward holds them
-fixed); the GPU also takes the forward's A^l, the oracle recomputes it in fp64
-from Q, K and A^{l-1}.
+Every input comes from the seeded generators or from the oracle: the kept sets
+I^l are the oracle forward's (the backward holds them fixed) and the GPU takes
+the oracle's A^l rounded to fp32, while the oracle backward recomputes A^l in
+fp64 from Q, K and A^{l-1}.
 
 Rules (a reading of the forward's tolerances for gradients, which the pages do
 not cover): tol = 1e-5 for fp32 inputs, 2e-3 for bf16 inputs;
@@ -96,7 +97,10 @@ def run_case(B, heads, H, W, d, win, shift, K_prev, K_l, dtype, seed, *, implici
     Qd, Kd, Vd = to_dev(qt), to_dev(kt), to_dev(vt)
     Ipd = None if I_prev is None else torch.from_numpy(I_prev).cuda()
     Apd = torch.from_numpy(A_prev).cuda()
-    I_l, A_l, _ = pfa.sparse_layer(Qd, Kd, Vd, Ipd, Apd, K_l, win=win, shift=shift, K_prev=K_prev)
+    fwd = oracle.layer(qt.exact, kt.exact, vt.exact, win=win, shift=shift, K_l=K_l, I_prev=I_prev,
+                       A_prev=A_prev.astype(np.float64))
+    I_l = torch.from_numpy(fwd["I"].reshape(lead + (N, K_l))).cuda()
+    A_l = torch.from_numpy(fwd["A"].astype(np.float32).reshape(lead + (N, K_l))).cuda()
     dO = inputs.draw(seed + 7, shape, "f32").exact
     dA = inputs.draw(seed + 8, lead + (N, K_l), "f32").exact if with_dA else None
     dQ, dK, dV, dAp = pfa.sparse_layer_backward(
@@ -104,7 +108,7 @@ def run_case(B, heads, H, W, d, win, shift, K_prev, K_l, dtype, seed, *, implici
         None if dA is None else torch.from_numpy(dA).cuda(), win=win, shift=shift, K_prev=K_prev,
         want_dA_prev=want_dA_prev)
     torch.cuda.synchronize()
-    keep = I_l.view(n_wh, N, K_l).cpu().numpy()
+    keep = fwd["I"]
     ref = oracle.layer_backward(qt.exact, kt.exact, vt.exact, win=win, shift=shift, keep=keep, dO=dO,
                                 dA=None if dA is None else dA.reshape(n_wh, N, K_l),
                                 I_prev=None if I_prev is None else I_prev.reshape(n_wh, N, K_prev),
@@ -168,43 +172,93 @@ def test_backward_kernel_timing_records():
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,layers", [(workloads.PATCH64.name, (1, 2)), (workloads.MAP256.name, (1, 2))])
 def test_backward_full_size(name, layers, capsys):
-    """Full-size workload: the GPU runs the forward chain through each listed
-    layer and that layer's backward for every window-head; the oracle checks 12
-    sampled window-heads."""
+    """Full-size workload, every window-head on the GPU; 12 sampled window-heads
+    carry the oracle chain's maps (previous map and the layer's I^l, A^l), the
+    others a valid uniform map, as in the forward full-size tests."""
     w = workloads.BY_NAME[name]
     sel = sample_wh(w, 12)
+    selt = torch.from_numpy(sel).cuda()
     N = w.N
     lead = (w.B, w.heads, w.n_windows)
     tol = parity.TOL[w.dtype]
-    I_g = A_g = None
+    I_ref = A_ref = None
     for l in range(max(layers) + 1):
         qkv = inputs.qkv(w, 0, l)
-        Qd, Kd, Vd = (to_dev(t) for t in qkv)
-        if l == 0:
-            _, A, _ = pfa.dense_layer(Qd, Kd, Vd, win=w.win, shift=w.shifts[0], want_A=True)
-            I = None
-        else:
-            I, A, _ = pfa.sparse_layer(Qd, Kd, Vd, I_g, A_g, w.K[l], win=w.win, shift=w.shifts[l],
-                                       K_prev=w.K[l - 1])
+        Q, K, V = (t.exact for t in qkv)
+        fwd = oracle.layer(Q, K, V, win=w.win, shift=w.shifts[l], K_l=w.K[l], I_prev=I_ref,
+                           A_prev=None if A_ref is None else A_ref.astype(np.float32).astype(np.float64),
+                           prev_compact=True, wh_list=sel)
         if l in layers:
             K_prev, K_l = w.K[l - 1], w.K[l]
+            Qd, Kd, Vd = (to_dev(t) for t in qkv)
+
+            def full(values, fill, dtype):   # [n_wh, N, K]: the oracle's rows at sel, `fill` elsewhere
+                t = fill.clone()
+                t[selt] = torch.from_numpy(values.astype(dtype)).cuda()
+                return t.view(lead + values.shape[1:])
+            A_prev = full(A_ref.astype(np.float32), torch.full((w.n_wh, N, K_prev), 1.0 / K_prev, device="cuda"),
+                          np.float32)
+            I_prev = None if I_ref is None else full(
+                I_ref, torch.arange(K_prev, dtype=torch.int32, device="cuda").expand(w.n_wh, N, K_prev), np.int32)
+            I_l = full(fwd["I"], torch.arange(K_l, dtype=torch.int32, device="cuda").expand(w.n_wh, N, K_l), np.int32)
+            A_l = full(fwd["A"].astype(np.float32), torch.full((w.n_wh, N, K_l), 1.0 / K_l, device="cuda"), np.float32)
             dO = torch.randn(Qd.shape, generator=torch.Generator().manual_seed(50 + l)).cuda()
             dA = torch.randn(lead + (N, K_l), generator=torch.Generator().manual_seed(60 + l)).cuda()
-            dQ, dK, dV, dAp = pfa.sparse_layer_backward(Qd, Kd, Vd, I_g, A_g, I, A, dO, dA, win=w.win,
+            dQ, dK, dV, dAp = pfa.sparse_layer_backward(Qd, Kd, Vd, I_prev, A_prev, I_l, A_l, dO, dA, win=w.win,
                                                         shift=w.shifts[l], K_prev=K_prev)
             torch.cuda.synchronize()
-            selt = torch.from_numpy(sel).cuda()
-            keep = I.view(-1, N, K_l)[selt].cpu().numpy()
-            Ip = None if I_g is None else I_g.view(-1, N, K_prev)[selt].cpu().numpy()
-            Ap = A_g.view(-1, N, K_prev)[selt].cpu().numpy()
-            ref = oracle.layer_backward(qkv[0].exact, qkv[1].exact, qkv[2].exact, win=w.win, shift=w.shifts[l],
-                                        keep=keep, dO=dO.cpu().numpy(), dA=dA.view(-1, N, K_l)[selt].cpu().numpy(),
-                                        I_prev=Ip, A_prev=Ap, prev_compact=True, wh_list=sel)
+            ref = oracle.layer_backward(Q, K, V, win=w.win, shift=w.shifts[l], keep=fwd["I"], dO=dO.cpu().numpy(),
+                                        dA=dA.view(-1, N, K_l)[selt].cpu().numpy(), I_prev=I_ref,
+                                        A_prev=A_ref.astype(np.float32).astype(np.float64), prev_compact=True,
+                                        wh_list=sel)
             gpu = {"dQ": dQ.cpu().numpy(), "dK": dK.cpu().numpy(), "dV": dV.cpu().numpy()}
             st = check_grads(gpu, ref, sel, w.heads, w.win, w.shifts[l], tol)
             st["dA_prev"] = check_dA_prev(dAp.view(-1, N, K_prev)[selt].cpu().numpy(), ref["dA_prev"], tol)
             with capsys.disabled():
                 print(f"  {w.name} layer {l + 1} backward: {st}", flush=True)
-            del dQ, dK, dV, dAp
-        I_g, A_g = I, A
-        del Qd, Kd, Vd
+            del Qd, Kd, Vd, dQ, dK, dV, dAp, I_prev, A_prev, I_l, A_l
+        I_ref, A_ref = fwd["I"], fwd["A"]
+
+
+DENSE = [
+    # dtype, d, win, shift, with_dA, with_bias
+    ("f32", 32, 32, 16, True, False),
+    ("bf16", 32, 32, 0, True, False),
+    ("f32", 16, 16, 8, False, False),
+    ("bf16", 16, 8, 4, True, False),
+    ("f32", 32, 32, 16, True, True),
+    ("bf16", 16, 16, 0, True, True),
+    ("f32", 32, 24, 12, True, False),        # N = 576: the last workgroup has idle waves
+]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,d,win,shift,with_dA,with_bias", DENSE)
+def test_dense_backward(dtype, d, win, shift, with_dA, with_bias, capsys):
+    """Backward of the dense first layer (all N slots kept, no previous map),
+    against the oracle backward with every slot kept; the GPU takes the oracle's
+    log denominators (fp64 rounded to fp32)."""
+    B, heads, H, W = 1, 2, 2 * win, 2 * win
+    shape = (B, heads, H, W, d)
+    qt, kt, vt = (inputs.draw(1300 + d + win + t, shape, dtype) for t in range(3))
+    N = win * win
+    n_wh = B * heads * 4
+    lead = (B, heads, 4)
+    table = None
+    if with_bias:
+        table = (np.random.Generator(np.random.PCG64(1310)).standard_normal((heads, (2 * win - 1) ** 2))
+                 ).astype(np.float32)
+    lse = oracle.dense_lse(qt.exact, kt.exact, win=win, shift=shift, bias=table).astype(np.float32)
+    dO = inputs.draw(1320, shape, "f32").exact
+    dA = inputs.draw(1321, lead + (N, N), "f32").exact if with_dA else None
+    dQ, dK, dV = pfa.dense_layer_backward(to_dev(qt), to_dev(kt), to_dev(vt), torch.from_numpy(lse).cuda().view(
+        lead + (N,)), torch.from_numpy(dO).cuda(), None if dA is None else torch.from_numpy(dA).cuda(), win=win,
+        shift=shift, bias=None if table is None else torch.from_numpy(table).cuda())
+    torch.cuda.synchronize()
+    keep = np.broadcast_to(np.arange(N, dtype=np.int32), (n_wh, N, N)).copy()
+    ref = oracle.layer_backward(qt.exact, kt.exact, vt.exact, win=win, shift=shift, keep=keep, dO=dO,
+                                dA=None if dA is None else dA.reshape(n_wh, N, N), bias=table)
+    gpu = {"dQ": dQ.cpu().numpy(), "dK": dK.cpu().numpy(), "dV": dV.cpu().numpy()}
+    st = check_grads(gpu, ref, range(n_wh), heads, win, shift, parity.TOL[dtype])
+    with capsys.disabled():
+        print(f"  dense backward {dtype} d={d} win={win} dA={with_dA} bias={with_bias}: {st}", flush=True)
