@@ -12,14 +12,14 @@
 // dense layer writes to lse_out).
 //
 // dense_bwd_dq_kernel: 8 waves x 16 queries per workgroup; K/V tiles of 64 slots
-//   staged in LDS as fp32. Pass 1 accumulates D_i, pass 2 forms dS and dQ. Scores
-//   and dO.v come transposed (16 keys x 16 queries per v_mfma_f32_16x16x4_f32
-//   chain), which leaves lane (query r16, keys 4 grp + r): the A-operand layout
-//   of dS K.
+//   staged in LDS as fp32, double-buffered (the next tile's loads in flight).
+//   Pass 1 accumulates D_i, pass 2 forms dS and dQ. Scores and dO.v come
+//   transposed (16 keys x 16 queries per v_mfma_f32_16x16x4_f32 chain), which
+//   leaves lane (query r16, keys 4 grp + r): the A-operand layout of dS K.
 // dense_bwd_dkv_kernel: 8 waves x 16 keys per workgroup; Q/dO tiles of 64 slots
-//   (with their lse and D) staged in LDS. Scores as (query 4 grp + r, key r16)
-//   per lane: the A-operand layout of P^T dO and dS^T Q. dV, dK stay in
-//   registers over all query tiles.
+//   (with their lse and D) staged in LDS, double-buffered. Scores as
+//   (query 4 grp + r, key r16) per lane: the A-operand layout of P^T dO and
+//   dS^T Q. dV, dK stay in registers over all query tiles.
 #include "pfa_kernels.h"
 #include "pfa_rows.h"
 
@@ -32,23 +32,48 @@ constexpr int kBwdWaves = 8;
 constexpr int kTile = 64;          // slots per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 
-// rows [r0, r0 + kTile) of a window (slot order) as fp32 into LDS, row stride STR floats
-template <typename T, int D, int STR>
-__device__ __forceinline__ void stage_f32(float* dst, const T* plane, const Geom& g, int wy, int wx, int r0) {
-    constexpr int EPC = Chunk<T>::kElems;
-    constexpr int CH = D / EPC;
-    for (int u = threadIdx.x; u < kTile * CH; u += blockDim.x) {
-        const int t = u / CH;
-        const int c = u - t * CH;
-        const unsigned char* src = reinterpret_cast<const unsigned char*>(plane) +
-                                   ((size_t)slot_pixel(g, wy, wx, r0 + t) * D) * sizeof(T) + c * 16;
-        float f[EPC];
-        Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(src), f);
+// Tiles of rows [r0, r0 + kTile) of a window (slot order): loaded from global
+// memory into registers (16-byte chunks, one or more per thread), then written
+// to LDS as fp32 with a row stride of STR floats. Splitting the two steps lets
+// the next tile's loads be in flight while the current tile is used.
+template <typename T, int D>
+struct TileRegs {
+    static constexpr int EPC = Chunk<T>::kElems;
+    static constexpr int CH = D / EPC;
+    static constexpr int UNITS = kTile * CH;
+    static constexpr int PER = (UNITS + kBwdWaves * kWave - 1) / (kBwdWaves * kWave);
+    uint4 r[PER];
+    __device__ void load(const T* plane, const Geom& g, int wy, int wx, int r0) {
 #pragma unroll
-        for (int e = 0; e < EPC; e += 4)
-            *reinterpret_cast<float4*>(dst + t * STR + c * EPC + e) = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
+        for (int x = 0; x < PER; ++x) {
+            const int u = threadIdx.x + x * kBwdWaves * kWave;
+            if (u < UNITS) {
+                const int t = u / CH;
+                const int c = u - t * CH;
+                r[x] = *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(plane) +
+                                                       ((size_t)slot_pixel(g, wy, wx, r0 + t) * D) * sizeof(T) +
+                                                       c * 16);
+            }
+        }
     }
-}
+    template <int STR>
+    __device__ void store(float* dst) const {
+#pragma unroll
+        for (int x = 0; x < PER; ++x) {
+            const int u = threadIdx.x + x * kBwdWaves * kWave;
+            if (u < UNITS) {
+                const int t = u / CH;
+                const int c = u - t * CH;
+                float f[EPC];
+                Chunk<T>::to_f32(r[x], f);
+#pragma unroll
+                for (int e = 0; e < EPC; e += 4)
+                    *reinterpret_cast<float4*>(dst + t * STR + c * EPC + e) = make_float4(f[e], f[e + 1], f[e + 2],
+                                                                                         f[e + 3]);
+            }
+        }
+    }
+};
 
 // this lane's DPL dims [DPL grp, DPL grp + DPL) of one row of a [.., D] array of type T
 template <typename T, int D>
@@ -96,8 +121,8 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const D
     constexpr int CT = D / 16;
     constexpr int STR = D + 4;   // padded fp32 LDS row
     constexpr int SUB = kTile / 16;
-    __shared__ __align__(16) float Kt[kTile * STR];
-    __shared__ __align__(16) float Vt[kTile * STR];
+    __shared__ __align__(16) float Kt2[2][kTile * STR];
+    __shared__ __align__(16) float Vt2[2][kTile * STR];
     __shared__ float btab[BIAS ? 63 * 63 : 1];
 
     const Geom g = p.g;
@@ -135,12 +160,26 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const D
     v4f dq[CT];
 #pragma unroll
     for (int c = 0; c < CT; ++c) dq[c] = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int pass = 0; pass < 2; ++pass) {
-        for (int t0 = 0; t0 < N; t0 += kTile) {
-            __syncthreads();   // the previous tile is consumed (and the bias table staged)
-            stage_f32<T, D, STR>(Kt, Kh, g, bp.wy, bp.wx, t0);
-            stage_f32<T, D, STR>(Vt, Vh, g, bp.wy, bp.wx, t0);
-            __syncthreads();
+    // the tile sequence of both passes, double-buffered: tile it + 1 is loaded
+    // into registers while tile it is used from LDS
+    const int ntiles = N / kTile;
+    TileRegs<T, D> kreg, vreg;
+    kreg.load(Kh, g, bp.wy, bp.wx, 0);
+    vreg.load(Vh, g, bp.wy, bp.wx, 0);
+    kreg.template store<STR>(Kt2[0]);
+    vreg.template store<STR>(Vt2[0]);
+    __syncthreads();
+    for (int it = 0; it < 2 * ntiles; ++it) {
+        const int pass = it / ntiles;
+        const int t0 = (it - pass * ntiles) * kTile;
+        const float* Kt = Kt2[it & 1];
+        const float* Vt = Vt2[it & 1];
+        if (it + 1 < 2 * ntiles) {
+            const int tn = ((it + 1) % ntiles) * kTile;
+            kreg.load(Kh, g, bp.wy, bp.wx, tn);
+            vreg.load(Vh, g, bp.wy, bp.wx, tn);
+        }
+        {
 #pragma unroll
             for (int s = 0; s < SUB; ++s) {
                 const int key0 = t0 + s * 16;
@@ -185,12 +224,17 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const D
                 }
             }
         }
-        if (pass == 0) {
-            // the 4 lane groups hold the same query: full row sum D_i
+        if (it == ntiles - 1) {
+            // end of pass 1: the 4 lane groups hold the same query, full row sum D_i
             Dq += __shfl_xor(Dq, 16);
             Dq += __shfl_xor(Dq, 32);
             if (wave_active && grp == 0) p.Dws[(size_t)bp.wh * N + qi] = Dq;
         }
+        if (it + 1 < 2 * ntiles) {
+            kreg.template store<STR>(Kt2[(it + 1) & 1]);
+            vreg.template store<STR>(Vt2[(it + 1) & 1]);
+        }
+        __syncthreads();
     }
     if (!wave_active) return;
     // lane holds dQ[query q0 + 4 grp + r][dim 16 c + r16]
@@ -208,10 +252,10 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dkv_kernel(const 
     constexpr int CT = D / 16;
     constexpr int STR = D + 4;
     constexpr int SUB = kTile / 16;
-    __shared__ __align__(16) float Qt[kTile * STR];
-    __shared__ __align__(16) float dOt[kTile * STR];
-    __shared__ float lset[kTile];
-    __shared__ float Dt[kTile];
+    __shared__ __align__(16) float Qt2[2][kTile * STR];
+    __shared__ __align__(16) float dOt2[2][kTile * STR];
+    __shared__ float lset2[2][kTile];
+    __shared__ float Dt2[2][kTile];
     __shared__ float btab[BIAS ? 63 * 63 : 1];
 
     const Geom g = p.g;
@@ -251,15 +295,42 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dkv_kernel(const 
         dv[c] = v4f{0.f, 0.f, 0.f, 0.f};
         dk[c] = v4f{0.f, 0.f, 0.f, 0.f};
     }
-    for (int t0 = 0; t0 < N; t0 += kTile) {
-        __syncthreads();
-        stage_f32<T, D, STR>(Qt, Qh, g, bp.wy, bp.wx, t0);
-        stage_f32<float, D, STR>(dOt, dOh, g, bp.wy, bp.wx, t0);
-        for (int u = threadIdx.x; u < kTile; u += blockDim.x) {
-            lset[u] = p.lse[(size_t)bp.wh * N + t0 + u] * kLog2e;
-            Dt[u] = p.Dws[(size_t)bp.wh * N + t0 + u];
+    // query tiles double-buffered: tile t + 1 (Q, dO, lse, D) is loaded into
+    // registers while tile t is used from LDS
+    const int ntiles = N / kTile;
+    TileRegs<T, D> qreg;
+    TileRegs<float, D> oreg;
+    float lreg = 0.0f, dreg = 0.0f;
+    auto load_small = [&](int t0) {
+        if (threadIdx.x < kTile) {
+            lreg = p.lse[(size_t)bp.wh * N + t0 + threadIdx.x] * kLog2e;
+            dreg = p.Dws[(size_t)bp.wh * N + t0 + threadIdx.x];
         }
-        __syncthreads();
+    };
+    auto store_all = [&](int b) {
+        qreg.template store<STR>(Qt2[b]);
+        oreg.template store<STR>(dOt2[b]);
+        if (threadIdx.x < kTile) {
+            lset2[b][threadIdx.x] = lreg;
+            Dt2[b][threadIdx.x] = dreg;
+        }
+    };
+    qreg.load(Qh, g, bp.wy, bp.wx, 0);
+    oreg.load(dOh, g, bp.wy, bp.wx, 0);
+    load_small(0);
+    store_all(0);
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+        const int t0 = it * kTile;
+        const float* Qt = Qt2[it & 1];
+        const float* dOt = dOt2[it & 1];
+        const float* lset = lset2[it & 1];
+        const float* Dt = Dt2[it & 1];
+        if (it + 1 < ntiles) {
+            qreg.load(Qh, g, bp.wy, bp.wx, t0 + kTile);
+            oreg.load(dOh, g, bp.wy, bp.wx, t0 + kTile);
+            load_small(t0 + kTile);
+        }
 #pragma unroll
         for (int s = 0; s < SUB; ++s) {
             const int qs = t0 + s * 16;   // queries qs + 4 grp + r of this lane
@@ -296,6 +367,8 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dkv_kernel(const 
                     dk[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(dS[r], Qt[ql * STR + 16 * c + r16], dk[c], 0, 0, 0);
                 }
         }
+        if (it + 1 < ntiles) store_all((it + 1) & 1);
+        __syncthreads();
     }
     if (!wave_active) return;
     // lane holds dV / dK[key k0 + 4 grp + r][dim 16 c + r16]
