@@ -25,9 +25,11 @@
 //   tile is staged in LDS (three bf16 planes). P.V stays on fp32 MFMA.
 //   fp32 inputs otherwise: v_mfma_f32_16x16x4_f32 (exact products, fp32 accumulation).
 //   bf16 inputs: v_mfma_f32_16x16x16_bf16; P is split into bf16 hi + lo parts
-//   (two MFMAs) so the P.V product keeps ~16 bits of P.
-// Two passes over the keys: (1) running row max / row sum, (2) recompute the
-// scores, write A^1 rows (optional) and accumulate O.
+//   (two MFMAs, the split done once per 16-key tile with the hardware
+//   conversion) so the P.V product keeps ~16 bits of P.
+// With A^1 written: two passes over the keys, (1) running row max / row sum,
+// (2) recompute the scores, write A^1 rows and accumulate O. O-only (A^1 not
+// written): one pass with an online softmax (running max, rescaled O and sum).
 #include "pfa_kernels.h"
 
 namespace pfa {
@@ -95,12 +97,15 @@ struct DenseOps<float, D> {
         for (int x = 0; x < DPL; ++x) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.v[x], q.v[x], acc, 0, 0, 0);
         return acc;
     }
+    // P operand of the P.V product: the fp32 weights themselves
+    struct PS { float p[4]; };
+    __device__ static PS prep(const float p[4]) { return PS{{p[0], p[1], p[2], p[3]}}; }
     // O tile (16 queries x 16 dims) += P (16 q x 16 keys) . V (16 keys x 16 dims);
     // p[r]: weight of key 4*grp + r for query r16; vrow[r]: LDS rows of those keys.
-    __device__ static v4f pv(const float p[4], const unsigned char* const vrow[4], int dim, v4f acc) {
+    __device__ static v4f pv(const PS& ps, const unsigned char* const vrow[4], int dim, v4f acc) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(p[r], reinterpret_cast<const float*>(vrow[r])[dim], acc, 0,
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ps.p[r], reinterpret_cast<const float*>(vrow[r])[dim], acc, 0,
                                                        0, 0);
         return acc;
     }
@@ -131,18 +136,24 @@ struct DenseOps<uint16_t, D> {
             acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(k.v[x], q.v[x], acc, 0, 0, 0);
         return acc;
     }
-    __device__ static v4f pv(const float p[4], const unsigned char* const vrow[4], int dim, v4f acc) {
-        v4s hi, lo, vv;
+    // P split once per 16-key tile into bf16 hi + lo (round to nearest even with
+    // v_cvt_pk_bf16_f32; the remainder is exact in fp32), ~16 bits of P in all
+    struct PS { v4s hi, lo; };
+    __device__ static PS prep(const float p[4]) {
+        const bf4 h = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
+        const bf4 l = {(__bf16)(p[0] - (float)h[0]), (__bf16)(p[1] - (float)h[1]), (__bf16)(p[2] - (float)h[2]),
+                       (__bf16)(p[3] - (float)h[3])};
+        PS ps;
+        ps.hi = __builtin_bit_cast(v4s, h);
+        ps.lo = __builtin_bit_cast(v4s, l);
+        return ps;
+    }
+    __device__ static v4f pv(const PS& ps, const unsigned char* const vrow[4], int dim, v4f acc) {
+        v4s vv;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint32_t h = f32_to_bf16_bits(p[r]);
-            const float rem = p[r] - __uint_as_float(h << 16);
-            hi[r] = (short)h;
-            lo[r] = (short)f32_to_bf16_bits(rem);
-            vv[r] = (short)reinterpret_cast<const uint16_t*>(vrow[r])[dim];
-        }
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, vv, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, vv, acc, 0, 0, 0);
+        for (int r = 0; r < 4; ++r) vv[r] = (short)reinterpret_cast<const uint16_t*>(vrow[r])[dim];
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ps.hi, vv, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ps.lo, vv, acc, 0, 0, 0);
         return acc;
     }
 };
@@ -302,6 +313,94 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
     const int ntiles = N / KT;
     uint4 kreg[PER], vreg[PER];
 
+    if constexpr (!WA) {
+        // O-only: one pass with an online softmax. Per K/V tile, the running max m
+        // of the lane's query (shared by its 4 lane groups) is raised to the tile's
+        // maximum; the O rows and the partial sums are rescaled by 2^(m_old - m)
+        // (an O accumulator row is another query's: its factor comes from the lane
+        // that owns that query), then P = 2^(s - m) is accumulated into O = P V.
+        float m = -INFINITY, l = 0.0f;
+        v4f oacc[CT];
+#pragma unroll
+        for (int c = 0; c < CT; ++c) oacc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+        tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, 0);
+        tile_load<ROWB, KT>(vreg, Vh, g, wy, wx, 0);
+        store_k(Ks[0], kreg);
+        tile_store<ROWB, KT, STRIDE>(Vs[0], vreg);
+        __syncthreads();
+        for (int t = 0; t < ntiles; ++t) {
+            if (t + 1 < ntiles) {
+                tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, (t + 1) * KT);
+                tile_load<ROWB, KT>(vreg, Vh, g, wy, wx, (t + 1) * KT);
+            }
+            const unsigned char* kt = Ks[t & 1];
+            const unsigned char* vt = Vs[t & 1];
+            v4f acc[SUB];
+#pragma unroll
+            for (int s = 0; s < SUB; ++s) acc[s] = tile_scores(kt, s);
+            // scaled (and biased) scores in base-2 units
+#pragma unroll
+            for (int s = 0; s < SUB; ++s) {
+                float b[4] = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (BIAS) tile_bias(t * KT + s * 16, b);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(acc[s][r], sc, b[r]);
+            }
+            float tmax = acc[0][0];
+#pragma unroll
+            for (int s = 0; s < SUB; ++s)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, acc[s][r]);
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float mn = fmaxf(m, tmax);
+            const float alpha = fast_exp2(m - mn);   // 0 on the first tile (m = -inf)
+            m = mn;
+            l *= alpha;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ar = __shfl(alpha, 4 * grp + r);   // factor of O row 4 grp + r
+#pragma unroll
+                for (int c = 0; c < CT; ++c) oacc[c][r] *= ar;
+            }
+#pragma unroll
+            for (int s = 0; s < SUB; ++s) {
+                float pr[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pr[r] = fast_exp2(acc[s][r] - m);
+                    l += pr[r];
+                }
+                const unsigned char* vrow[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vrow[r] = vt + (s * 16 + 4 * grp + r) * STRIDE;
+                const typename Ops::PS ps = Ops::prep(pr);
+#pragma unroll
+                for (int c = 0; c < CT; ++c) oacc[c] = Ops::pv(ps, vrow, c * 16 + r16, oacc[c]);
+            }
+            if (t + 1 < ntiles) {
+                store_k(Ks[(t + 1) & 1], kreg);
+                tile_store<ROWB, KT, STRIDE>(Vs[(t + 1) & 1], vreg);
+            }
+            __syncthreads();
+        }
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        if (p.lse_out && wave_active && grp == 0 && q0 + r16 < N)
+            p.lse_out[(size_t)wh * N + q0 + r16] = (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
+        if (!wave_active) return;
+        const float inv_l = 1.0f / l;
+        // lane holds O[query q0 + 4*grp + r][dim 16c + r16]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float ir = __shfl(inv_l, 4 * grp + r);
+            float* orow = Oh + (size_t)slot_pixel(g, wy, wx, q0 + 4 * grp + r) * D;
+#pragma unroll
+            for (int c = 0; c < CT; ++c) orow[c * 16 + r16] = oacc[c][r] * ir;
+        }
+        return;
+    }
+
     // pass 1: per-lane running max / sum over the keys 4*grp + r of every 16-key tile
     float m = -INFINITY, l = 0.0f;
     tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, 0);
@@ -410,8 +509,9 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
             const unsigned char* vrow[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) vrow[r] = vt + (s * 16 + 4 * grp + r) * STRIDE;
+            const typename Ops::PS ps = Ops::prep(pr);
 #pragma unroll
-            for (int c = 0; c < CT; ++c) oacc[c] = Ops::pv(pr, vrow, c * 16 + r16, oacc[c]);
+            for (int c = 0; c < CT; ++c) oacc[c] = Ops::pv(ps, vrow, c * 16 + r16, oacc[c]);
         }
         if (t + 1 < ntiles) {
             store_k(Ks[(t + 1) & 1], kreg);

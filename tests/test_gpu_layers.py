@@ -244,13 +244,16 @@ def test_dense_layer_variants(dtype, d, win):
                            gpu_O=O.cpu().numpy(), ref=ref, cand=None, wh_list=sel, tol=parity.TOL[dtype],
                            rerun=parity.rerun_fn(qt.exact, kt.exact, vt.exact, I_prev=None, A_prev=None,
                                                  i_shared=False, prev_compact=False, **kw))
-    # O-only mode gives the same O, and the log softmax denominators match the
-    # oracle's (absolute error in the log domain = relative error of the denominator)
+    # O-only mode (one pass, online softmax) matches the oracle's O, and the log
+    # softmax denominators match the oracle's (absolute error in the log domain =
+    # relative error of the denominator)
     lse = torch.empty((n_wh, N), dtype=torch.float32, device="cuda")
     _, A0, O0 = pfa.dense_layer(to_dev(qt), to_dev(kt), to_dev(vt), N, win=win, shift=win // 2, want_A=False,
                                 lse_out=lse)
-    _, A1, O1 = pfa.dense_layer(to_dev(qt), to_dev(kt), to_dev(vt), N, win=win, shift=win // 2, want_A=True)
-    assert A0 is None and torch.equal(O0, O1)
+    torch.cuda.synchronize()
+    assert A0 is None
+    ref0 = oracle.layer(qt.exact, kt.exact, vt.exact, win=win, shift=win // 2, K_l=N, wh_list=sel)
+    parity.check_O(O0.cpu().numpy(), ref0["O"], parity.TOL[dtype])
     lse_ref = oracle.dense_lse(qt.exact, kt.exact, win=win, shift=win // 2)
     err = np.abs(lse.cpu().numpy().astype(np.float64) - lse_ref)
     assert err.max() <= parity.TOL[dtype], float(err.max())
