@@ -446,8 +446,11 @@ __device__ __forceinline__ void select_store(const SparseArgs& p, int lane, bool
 
     // Store loop. Positions: group-masked ballots counted with mbcnt, the running
     // group count folded into the accumulator. Entries not to be stored (not kept,
-    // rows past the end, positions past K_l on precondition violations) get an
-    // offset past the buffer resource's range, which the hardware drops. The loop
+    // rows past the end) get an offset past the buffer resource's range, which the
+    // hardware drops. The descent keeps exactly K_l entries of an active row, so
+    // positions stay below K_l; only the bisection tie cut can keep more (repeated
+    // indices in I^{l-1}, a precondition violation), where positions past K_l are
+    // dropped too. The loop
     // compares with copies of thr/tau the compiler cannot see through, so it does
     // not keep KPT comparison masks alive from the sums above.
     int thr2 = thr, tau2 = tau;
@@ -456,18 +459,23 @@ __device__ __forceinline__ void select_store(const SparseArgs& p, int lane, bool
     const uint32_t gm_lo = (uint32_t)gmask, gm_hi = (uint32_t)(gmask >> 32);
     int obase = 0;
     int tbase = 0;   // ORDERED ties: keys equal to tau met so far in the group
-    auto emit = [&](int t, bool k) {
+    auto emit = [&](int t, bool k, bool guard) {
         const uint64_t m = ballot(k);
         const uint32_t ml = (uint32_t)m & gm_lo, mh = (uint32_t)(m >> 32) & gm_hi;
-        const int pos = (int)__builtin_amdgcn_mbcnt_hi(mh, __builtin_amdgcn_mbcnt_lo(ml, (uint32_t)obase));
-        const int off = (k && pos < K_l) ? (row_off + pos) * 4 : 0x7FFFFFF0;
+        // pos is made opaque so that the offset stays a select, not a branch
+        int pos = (int)__builtin_amdgcn_mbcnt_hi(mh, __builtin_amdgcn_mbcnt_lo(ml, (uint32_t)obase));
+        __asm__ volatile("" : "+v"(pos));
+        const int off = (k && (!guard || pos < K_l)) ? (row_off + pos) * 4 : 0x7FFFFFF0;
         __builtin_amdgcn_raw_buffer_store_b32(jf(t), rI, off, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(uv[t] * inv), rA, off, 0, 0);
-        obase += __builtin_popcount(ml) + __builtin_popcount(mh);
+        // two accumulating bit counts (v_bcnt_u32_b32 adds its second operand)
+        int part = __builtin_popcount(ml) + obase;
+        __asm__ volatile("" : "+v"(part));
+        obase = __builtin_popcount(mh) + part;
     };
     if (!any_tie) {
 #pragma unroll
-        for (int t = 0; t < KPT; ++t) emit(t, key(t) > thr2);
+        for (int t = 0; t < KPT; ++t) emit(t, key(t) > thr2, false);
     } else if (ORDERED) {
 #pragma unroll
         for (int t = 0; t < KPT; ++t) {
@@ -475,11 +483,11 @@ __device__ __forceinline__ void select_store(const SparseArgs& p, int lane, bool
             const uint64_t me = ballot(eq);
             const int rank = tbase + G::below(me, lane);
             tbase += G::count_mask(me, lane);
-            emit(t, key(t) > thr2 || (eq && rank < need_tau));
+            emit(t, key(t) > thr2 || (eq && rank < need_tau), false);
         }
     } else {
 #pragma unroll
-        for (int t = 0; t < KPT; ++t) emit(t, key(t) > tau2 || (key(t) == tau2 && jf(t) <= jcut));
+        for (int t = 0; t < KPT; ++t) emit(t, key(t) > tau2 || (key(t) == tau2 && jf(t) <= jcut), true);
     }
 }
 
