@@ -35,6 +35,14 @@ __device__ __forceinline__ int slot_pixel(const Geom& g, int wy, int wx, int t) 
 __device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
 
+// acc + a.lo * b.lo + a.hi * b.hi for two packed bf16 pairs (v_dot2c_f32_bf16: the
+// bf16 products are exact in fp32, the sum accumulates in fp32)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), acc,
+                                           false);
+}
+
 // Round to nearest even fp32 -> bf16 bits (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
     uint32_t b = __float_as_uint(x);

@@ -604,15 +604,19 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
             jj[t] = (int)min((unsigned)cur.j[t], (unsigned)(N - 1));   // memory safety only: indices lie in [0, N)
         }
 
-        float qf[D];
-        if (PQ) {
-#pragma unroll
-            for (int m = 0; m < CH; ++m) Chunk<T>::to_f32(cur.q[m], &qf[m * EPC]);
-        } else {
+        // the query row: fp32 values, or for bf16 the packed pairs themselves (v_dot2c_f32_bf16
+        // multiplies the bf16 pairs exactly and accumulates in fp32, like the fp32 FMA chain)
+        constexpr bool DOT2 = sizeof(T) == 2;
+        float qf[DOT2 ? 1 : D];
+        uint4 qp[DOT2 ? CH : 1];
+        {
             const unsigned char* qrow = reinterpret_cast<const unsigned char*>(Qh + (size_t)qpix * D);
 #pragma unroll
-            for (int m = 0; m < CH; ++m)
-                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(qrow + coff[m]), &qf[m * EPC]);
+            for (int m = 0; m < CH; ++m) {
+                const uint4 c = PQ ? cur.q[m] : *reinterpret_cast<const uint4*>(qrow + coff[m]);
+                if constexpr (DOT2) qp[m] = c;
+                else Chunk<T>::to_f32(c, &qf[m * EPC]);
+            }
         }
 
         // relative position bias of (i, j_t) in base-2 units, loads issued before the scores
@@ -641,10 +645,18 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
             float acc = 0.0f;
 #pragma unroll
             for (int m = 0; m < CH; ++m) {
-                float kf[EPC];
-                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(krow + coff[m]), kf);
+                const uint4 kc = *reinterpret_cast<const uint4*>(krow + coff[m]);
+                if constexpr (DOT2) {
+                    acc = dot2_bf16(qp[m].x, kc.x, acc);
+                    acc = dot2_bf16(qp[m].y, kc.y, acc);
+                    acc = dot2_bf16(qp[m].z, kc.z, acc);
+                    acc = dot2_bf16(qp[m].w, kc.w, acc);
+                } else {
+                    float kf[EPC];
+                    Chunk<T>::to_f32(kc, kf);
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) acc = fmaf(qf[m * EPC + e], kf[e], acc);
+                    for (int e = 0; e < EPC; ++e) acc = fmaf(qf[m * EPC + e], kf[e], acc);
+                }
             }
             if constexpr (BIAS)
                 sv[t] = (FULL || valid[t]) ? fmaf(acc, p.scale2, b2[t]) : -INFINITY;
