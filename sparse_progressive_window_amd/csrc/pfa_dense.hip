@@ -31,42 +31,13 @@
 // (2) recompute the scores, write A^1 rows and accumulate O. O-only (A^1 not
 // written): one pass with an online softmax (running max, rescaled O and sum).
 #include "pfa_kernels.h"
+#include "pfa_split.h"
 
 namespace pfa {
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
-typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
-
-// x = hi + mid + lo with each part the round-to-nearest-even bf16 of the
-// remainder (the subtractions are exact in fp32).
-template <int NE, class V>
-__device__ __forceinline__ void split3(const float* x, V& hi, V& mid, V& lo) {
-#pragma unroll
-    for (int i = 0; i < NE; ++i) {
-        hi[i] = (__bf16)x[i];
-        const float r = x[i] - (float)hi[i];
-        mid[i] = (__bf16)r;
-        lo[i] = (__bf16)(r - (float)mid[i]);
-    }
-}
-
-// Scores of 16 keys x 16 queries from split operands (d = 32: one MFMA per pair
-// of parts), the small products first.
-__device__ __forceinline__ v4f scores_split3(const bf8& kh, const bf8& km, const bf8& kl, const bf8& qh,
-                                             const bf8& qm, const bf8& ql) {
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(km, qm, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(km, qh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qm, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh, acc, 0, 0, 0);
-    return acc;
-}
-constexpr int kSplitRow = 80;   // bytes per key row in each bf16 K plane (64 + 16 pad)
 
 constexpr int kDenseWaves = 8;
 constexpr int kQPerBlock = 16 * kDenseWaves;
@@ -300,7 +271,7 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
             const bf8 kh = *reinterpret_cast<const bf8*>(row);
             const bf8 km = *reinterpret_cast<const bf8*>(row + KT * kSplitRow);
             const bf8 kl = *reinterpret_cast<const bf8*>(row + 2 * KT * kSplitRow);
-            return scores_split3(kh, km, kl, qh, qm, ql);
+            return dot_split3(kh, km, kl, qh, qm, ql, v4f{0.f, 0.f, 0.f, 0.f});
         } else {
             const typename Ops::Row kop = Ops::load(kt + (s * 16 + r16) * STRIDE, grp);
             return Ops::scores(kop, qop);

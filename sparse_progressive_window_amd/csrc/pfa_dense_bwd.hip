@@ -22,6 +22,7 @@
 //   dS^T Q. dV, dK stay in registers over all query tiles.
 #include "pfa_kernels.h"
 #include "pfa_rows.h"
+#include "pfa_split.h"
 
 namespace pfa {
 namespace {
@@ -73,6 +74,31 @@ struct TileRegs {
             }
         }
     }
+    // d = 32: the tile as bf16 planes of kTile rows x kSplitRow bytes; fp32 rows as
+    // three planes (hi, mid, lo), bf16 rows (exact) as one
+    __device__ void store_planes(unsigned char* dst) const {
+        static_assert(D == 32, "planes hold 32-wide rows");
+#pragma unroll
+        for (int x = 0; x < PER; ++x) {
+            const int u = threadIdx.x + x * kBwdWaves * kWave;
+            if (u < UNITS) {
+                const int t = u / CH;
+                const int c = u - t * CH;
+                if constexpr (sizeof(T) == 4) {
+                    const float f[4] = {__uint_as_float(r[x].x), __uint_as_float(r[x].y), __uint_as_float(r[x].z),
+                                        __uint_as_float(r[x].w)};
+                    bf4 h, m, l;
+                    split3<4>(f, h, m, l);
+                    unsigned char* row = dst + t * kSplitRow + c * 8;
+                    *reinterpret_cast<bf4*>(row) = h;
+                    *reinterpret_cast<bf4*>(row + kTile * kSplitRow) = m;
+                    *reinterpret_cast<bf4*>(row + 2 * kTile * kSplitRow) = l;
+                } else {
+                    *reinterpret_cast<uint4*>(dst + t * kSplitRow + c * 16) = r[x];
+                }
+            }
+        }
+    }
 };
 
 // this lane's DPL dims [DPL grp, DPL grp + DPL) of one row of a [.., D] array of type T
@@ -121,8 +147,15 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const D
     constexpr int CT = D / 16;
     constexpr int STR = D + 4;   // padded fp32 LDS row
     constexpr int SUB = kTile / 16;
+    // SPLIT (d = 32, no bias): scores and dO.v on bf16 MFMA from bf16 planes of the
+    // K/V tiles (three-way split of fp32 values; bf16 inputs are exact as they are)
+    constexpr bool SPLIT = D == 32 && !BIAS;
+    constexpr bool BFIN = sizeof(T) == 2;
+    constexpr int PLB = SPLIT ? (BFIN ? 1 : 3) * kTile * kSplitRow : 16;
     __shared__ __align__(16) float Kt2[2][kTile * STR];
-    __shared__ __align__(16) float Vt2[2][kTile * STR];
+    __shared__ __align__(16) float Vt2[SPLIT ? 1 : 2][SPLIT ? 4 : kTile * STR];
+    __shared__ __align__(16) unsigned char KP2[SPLIT ? 2 : 1][PLB];
+    __shared__ __align__(16) unsigned char VP2[SPLIT ? 2 : 1][PLB];
     __shared__ float btab[BIAS ? 63 * 63 : 1];
 
     const Geom g = p.g;
@@ -145,6 +178,11 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const D
     row_dims<T, D>(Qh + (size_t)slot_pixel(g, bp.wy, bp.wx, qi) * D, grp, qv);
     row_dims<float, D>(p.dO + plane + (size_t)slot_pixel(g, bp.wy, bp.wx, qi) * D, grp, dov);
     const float lse2 = p.lse[(size_t)bp.wh * N + qi] * kLog2e;
+    bf8 qh, qm, ql, dh, dm, dl;   // SPLIT: this lane's 8 dims of q and dO in parts
+    if constexpr (SPLIT) {
+        split3<8>(qv, qh, qm, ql);
+        split3<8>(dov, dh, dm, dl);
+    }
     const int wrow = 2 * g.win - 1;
     int ibase = 0;
     if constexpr (BIAS) {
@@ -164,16 +202,24 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const D
     // into registers while tile it is used from LDS
     const int ntiles = N / kTile;
     TileRegs<T, D> kreg, vreg;
+    auto store_tiles = [&](int b) {
+        kreg.template store<STR>(Kt2[b]);
+        if constexpr (SPLIT) {
+            kreg.store_planes(KP2[b]);
+            vreg.store_planes(VP2[b]);
+        } else {
+            vreg.template store<STR>(Vt2[b]);
+        }
+    };
     kreg.load(Kh, g, bp.wy, bp.wx, 0);
     vreg.load(Vh, g, bp.wy, bp.wx, 0);
-    kreg.template store<STR>(Kt2[0]);
-    vreg.template store<STR>(Vt2[0]);
+    store_tiles(0);
     __syncthreads();
     for (int it = 0; it < 2 * ntiles; ++it) {
         const int pass = it / ntiles;
         const int t0 = (it - pass * ntiles) * kTile;
         const float* Kt = Kt2[it & 1];
-        const float* Vt = Vt2[it & 1];
+        const float* Vt = Vt2[SPLIT ? 0 : (it & 1)];
         if (it + 1 < 2 * ntiles) {
             const int tn = ((it + 1) % ntiles) * kTile;
             kreg.load(Kh, g, bp.wy, bp.wx, tn);
@@ -184,12 +230,33 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const D
             for (int s = 0; s < SUB; ++s) {
                 const int key0 = t0 + s * 16;
                 v4f st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
-                const float* kr = Kt + (s * 16 + r16) * STR + DPL * grp;
-                const float* vr = Vt + (s * 16 + r16) * STR + DPL * grp;
+                if constexpr (SPLIT) {
+                    // A rows: keys s*16 + r16, dims 8 grp .. 8 grp + 7 of each plane
+                    const unsigned char* kp = KP2[it & 1] + (s * 16 + r16) * kSplitRow + grp * 16;
+                    const unsigned char* vp = VP2[it & 1] + (s * 16 + r16) * kSplitRow + grp * 16;
+                    const bf8 kh = *reinterpret_cast<const bf8*>(kp);
+                    const bf8 vh = *reinterpret_cast<const bf8*>(vp);
+                    if constexpr (BFIN) {   // k, q, v exact in bf16: one product each, dO in three parts
+                        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh, st, 0, 0, 0);
+                        dpt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, dl, dpt, 0, 0, 0);
+                        dpt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, dm, dpt, 0, 0, 0);
+                        dpt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, dh, dpt, 0, 0, 0);
+                    } else {
+                        const bf8 km = *reinterpret_cast<const bf8*>(kp + kTile * kSplitRow);
+                        const bf8 kl = *reinterpret_cast<const bf8*>(kp + 2 * kTile * kSplitRow);
+                        const bf8 vm = *reinterpret_cast<const bf8*>(vp + kTile * kSplitRow);
+                        const bf8 vl = *reinterpret_cast<const bf8*>(vp + 2 * kTile * kSplitRow);
+                        st = dot_split3(kh, km, kl, qh, qm, ql, st);
+                        dpt = dot_split3(vh, vm, vl, dh, dm, dl, dpt);
+                    }
+                } else {
+                    const float* kr = Kt + (s * 16 + r16) * STR + DPL * grp;
+                    const float* vr = Vt + (s * 16 + r16) * STR + DPL * grp;
 #pragma unroll
-                for (int x = 0; x < DPL; ++x) {
-                    st = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[x], qv[x], st, 0, 0, 0);
-                    dpt = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[x], dov[x], dpt, 0, 0, 0);
+                    for (int x = 0; x < DPL; ++x) {
+                        st = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[x], qv[x], st, 0, 0, 0);
+                        dpt = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[x], dov[x], dpt, 0, 0, 0);
+                    }
                 }
                 // lane: query qi, keys key0 + 4 grp + r
                 float b[4] = {0.f, 0.f, 0.f, 0.f};
@@ -230,10 +297,7 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const D
             Dq += __shfl_xor(Dq, 32);
             if (wave_active && grp == 0) p.Dws[(size_t)bp.wh * N + qi] = Dq;
         }
-        if (it + 1 < 2 * ntiles) {
-            kreg.template store<STR>(Kt2[(it + 1) & 1]);
-            vreg.template store<STR>(Vt2[(it + 1) & 1]);
-        }
+        if (it + 1 < 2 * ntiles) store_tiles((it + 1) & 1);
         __syncthreads();
     }
     if (!wave_active) return;
