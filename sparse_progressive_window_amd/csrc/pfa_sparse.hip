@@ -829,6 +829,10 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
         const int qi = min(base + (lv & 3), row1 - 1);
         // 16 accumulator chains (one per 64-candidate tile), contraction chunk outer:
         // one 16-byte chunk of the query is live at a time
+        // wave priority: the VALU-heavy selection of one wave issues ahead of the
+        // MFMA phase of the others on its SIMD (measured 3-4 % faster than equal
+        // priorities)
+        __builtin_amdgcn_s_setprio(0);
         v4f acc[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -852,6 +856,7 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
                 }
             }
         }
+        __builtin_amdgcn_s_setprio(2);
         float uv[KPT];   // raw scores q.k, then the keys
         // acc[t][r] = s(row r, candidate 64t + lane): transpose (lane quarter, r)
 #pragma unroll
