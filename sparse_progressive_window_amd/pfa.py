@@ -312,6 +312,8 @@ def dense_layer_backward(Q, K, V, lse, dO, dA=None, *, win, shift=0, bias=None, 
         raise PfaError("pfa_dense_layer_backward_workspace", need)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must be a device tensor of at least {need} bytes")
     rc = load().pfa_dense_layer_backward(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(bias), _ptr(lse),
                                          _ptr(dO), _ptr(dA), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(workspace),
                                          workspace.numel() * workspace.element_size(), _stream())
