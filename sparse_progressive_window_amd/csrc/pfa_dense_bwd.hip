@@ -74,6 +74,33 @@ struct TileRegs {
             }
         }
     }
+    // d = 32: the tile as bf16 planes of kTile rows x 64 bytes, 16-byte chunk m of
+    // row t stored at chunk position m ^ ((t >> 2) & 3), so the operand reads of 16
+    // consecutive rows at one chunk hit distinct banks; fp32 rows as three planes
+    // (hi, mid, lo), bf16 rows (exact) as one
+    __device__ void store_planes64(unsigned char* dst) const {
+        static_assert(D == 32, "planes hold 32-wide rows");
+#pragma unroll
+        for (int x = 0; x < PER; ++x) {
+            const int u = threadIdx.x + x * kBwdWaves * kWave;
+            if (u < UNITS) {
+                const int t = u / CH;
+                const int c = u - t * CH;
+                if constexpr (sizeof(T) == 4) {   // chunk c = dims 4c .. 4c + 3: half of a bf16 chunk
+                    const float f[4] = {__uint_as_float(r[x].x), __uint_as_float(r[x].y), __uint_as_float(r[x].z),
+                                        __uint_as_float(r[x].w)};
+                    bf4 h, m, l;
+                    split3<4>(f, h, m, l);
+                    unsigned char* row = dst + t * 64 + (((c >> 1) ^ ((t >> 2) & 3)) << 4) + (c & 1) * 8;
+                    *reinterpret_cast<bf4*>(row) = h;
+                    *reinterpret_cast<bf4*>(row + kTile * 64) = m;
+                    *reinterpret_cast<bf4*>(row + 2 * kTile * 64) = l;
+                } else {   // chunk c = dims 8c .. 8c + 7
+                    *reinterpret_cast<uint4*>(dst + t * 64 + ((c ^ ((t >> 2) & 3)) << 4)) = r[x];
+                }
+            }
+        }
+    }
     // d = 32: the tile as bf16 planes of kTile rows x kSplitRow bytes; fp32 rows as
     // three planes (hi, mid, lo), bf16 rows (exact) as one
     __device__ void store_planes(unsigned char* dst) const {
@@ -311,13 +338,24 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const D
 }
 
 template <typename T, int D, bool BIAS, bool HAS_DA>
-__global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dkv_kernel(const DenseBwdArgs p) {
+__global__ __launch_bounds__(kBwdWaves * kWave, 4) void dense_bwd_dkv_kernel(const DenseBwdArgs p) {
     constexpr int DPL = D / 4;
     constexpr int CT = D / 16;
     constexpr int STR = D + 4;
     constexpr int SUB = kTile / 16;
-    __shared__ __align__(16) float Qt2[2][kTile * STR];
-    __shared__ __align__(16) float dOt2[2][kTile * STR];
+    // SPLIT (d = 32, no bias): scores and dO.v on bf16 MFMA, the A operands (Q and dO
+    // rows) from bf16 planes of the tiles made once per tile (double-buffered), the
+    // fp32 Q/dO tiles that dV and dK multiply single-buffered (LDS for two
+    // workgroups per CU)
+    constexpr bool SPLIT = D == 32 && !BIAS;
+    constexpr bool BFIN = sizeof(T) == 2;
+    constexpr int NB32 = SPLIT ? 1 : 2;
+    constexpr int QPB = SPLIT ? (BFIN ? 1 : 3) * kTile * 64 : 16;
+    constexpr int OPB = SPLIT ? 3 * kTile * 64 : 16;
+    __shared__ __align__(16) float Qt2[NB32][kTile * STR];
+    __shared__ __align__(16) float dOt2[NB32][kTile * STR];
+    __shared__ __align__(16) unsigned char QP2[SPLIT ? 2 : 1][QPB];
+    __shared__ __align__(16) unsigned char OP2[SPLIT ? 2 : 1][OPB];
     __shared__ float lset2[2][kTile];
     __shared__ float Dt2[2][kTile];
     __shared__ float btab[BIAS ? 63 * 63 : 1];
@@ -342,6 +380,11 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dkv_kernel(const 
     float kv[DPL], vv[DPL];
     row_dims<T, D>(Kh + (size_t)slot_pixel(g, bp.wy, bp.wx, kj) * D, grp, kv);
     row_dims<T, D>(Vh + (size_t)slot_pixel(g, bp.wy, bp.wx, kj) * D, grp, vv);
+    bf8 kh, km, kl, vh, vm, vl;   // SPLIT: this lane's 8 dims of k and v in parts
+    if constexpr (SPLIT) {
+        split3<8>(kv, kh, km, kl);
+        split3<8>(vv, vh, vm, vl);
+    }
     const int wrow = 2 * g.win - 1;
     int kbase = 0;   // bias index of (query at window row/col (0, 0), this key)
     if constexpr (BIAS) {
@@ -371,23 +414,34 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dkv_kernel(const 
             dreg = p.Dws[(size_t)bp.wh * N + t0 + threadIdx.x];
         }
     };
-    auto store_all = [&](int b) {
-        qreg.template store<STR>(Qt2[b]);
-        oreg.template store<STR>(dOt2[b]);
+    // SPLIT: planes, lse and D go to buffer b; the fp32 tiles to their single buffer
+    auto store_buffered = [&](int b) {
+        if constexpr (SPLIT) {
+            qreg.store_planes64(QP2[b]);
+            oreg.store_planes64(OP2[b]);
+        } else {
+            qreg.template store<STR>(Qt2[b]);
+            oreg.template store<STR>(dOt2[b]);
+        }
         if (threadIdx.x < kTile) {
             lset2[b][threadIdx.x] = lreg;
             Dt2[b][threadIdx.x] = dreg;
         }
     };
+    auto store_fp32 = [&]() {
+        qreg.template store<STR>(Qt2[0]);
+        oreg.template store<STR>(dOt2[0]);
+    };
     qreg.load(Qh, g, bp.wy, bp.wx, 0);
     oreg.load(dOh, g, bp.wy, bp.wx, 0);
     load_small(0);
-    store_all(0);
+    store_buffered(0);
+    if constexpr (SPLIT) store_fp32();
     __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
         const int t0 = it * kTile;
-        const float* Qt = Qt2[it & 1];
-        const float* dOt = dOt2[it & 1];
+        const float* Qt = Qt2[SPLIT ? 0 : (it & 1)];
+        const float* dOt = dOt2[SPLIT ? 0 : (it & 1)];
         const float* lset = lset2[it & 1];
         const float* Dt = Dt2[it & 1];
         if (it + 1 < ntiles) {
@@ -395,16 +449,41 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dkv_kernel(const 
             oreg.load(dOh, g, bp.wy, bp.wx, t0 + kTile);
             load_small(t0 + kTile);
         }
-#pragma unroll
+        // not unrolled: the split operands of an unrolled loop spill under 128 VGPRs
+        // (measured slower unrolled by 2 or 4)
+#pragma unroll 1
         for (int s = 0; s < SUB; ++s) {
             const int qs = t0 + s * 16;   // queries qs + 4 grp + r of this lane
             v4f st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
-            const float* qr = Qt + (s * 16 + r16) * STR + DPL * grp;
-            const float* dr = dOt + (s * 16 + r16) * STR + DPL * grp;
+            if constexpr (SPLIT) {
+                // A rows: queries s*16 + r16, dims 8 grp .. 8 grp + 7 (swizzled chunk)
+                const int row = s * 16 + r16;
+                const int off = row * 64 + ((grp ^ ((row >> 2) & 3)) << 4);
+                const unsigned char* qp = QP2[it & 1] + off;
+                const unsigned char* op = OP2[it & 1] + off;
+                const bf8 qh = *reinterpret_cast<const bf8*>(qp);
+                const bf8 dh = *reinterpret_cast<const bf8*>(op);
+                const bf8 dm = *reinterpret_cast<const bf8*>(op + kTile * 64);
+                const bf8 dl = *reinterpret_cast<const bf8*>(op + 2 * kTile * 64);
+                if constexpr (BFIN) {   // q, k, v exact in bf16: one product; dO in three parts
+                    st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kh, st, 0, 0, 0);
+                    dpt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dl, vh, dpt, 0, 0, 0);
+                    dpt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dm, vh, dpt, 0, 0, 0);
+                    dpt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dh, vh, dpt, 0, 0, 0);
+                } else {
+                    const bf8 qm = *reinterpret_cast<const bf8*>(qp + kTile * 64);
+                    const bf8 ql = *reinterpret_cast<const bf8*>(qp + 2 * kTile * 64);
+                    st = dot_split3(qh, qm, ql, kh, km, kl, st);
+                    dpt = dot_split3(dh, dm, dl, vh, vm, vl, dpt);
+                }
+            } else {
+                const float* qr = Qt + (s * 16 + r16) * STR + DPL * grp;
+                const float* dr = dOt + (s * 16 + r16) * STR + DPL * grp;
 #pragma unroll
-            for (int x = 0; x < DPL; ++x) {
-                st = __builtin_amdgcn_mfma_f32_16x16x4f32(qr[x], kv[x], st, 0, 0, 0);
-                dpt = __builtin_amdgcn_mfma_f32_16x16x4f32(dr[x], vv[x], dpt, 0, 0, 0);
+                for (int x = 0; x < DPL; ++x) {
+                    st = __builtin_amdgcn_mfma_f32_16x16x4f32(qr[x], kv[x], st, 0, 0, 0);
+                    dpt = __builtin_amdgcn_mfma_f32_16x16x4f32(dr[x], vv[x], dpt, 0, 0, 0);
+                }
             }
             float b[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (BIAS) {
@@ -431,7 +510,12 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dkv_kernel(const 
                     dk[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(dS[r], Qt[ql * STR + 16 * c + r16], dk[c], 0, 0, 0);
                 }
         }
-        if (it + 1 < ntiles) store_all((it + 1) & 1);
+        if (it + 1 < ntiles) store_buffered((it + 1) & 1);
+        if constexpr (SPLIT) {
+            // every wave is done with the fp32 tile before the next one replaces it
+            __syncthreads();
+            if (it + 1 < ntiles) store_fp32();
+        }
         __syncthreads();
     }
     if (!wave_active) return;
