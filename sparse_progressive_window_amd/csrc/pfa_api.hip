@@ -89,6 +89,14 @@ bool geom_from_shape(const pfa_shape* s, Geom* g, int* code) {
 
 int elem_bytes(int dtype) { return dtype == PFA_F32 ? 4 : 2; }
 
+// compute units of the current device (0 if the query fails: no split workloads)
+int compute_units() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return cus;
+}
+
 int64_t n_wh(const Geom& g) { return (int64_t)g.B * g.heads * g.nwy * g.nwx; }
 
 int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const void* V, const float* bias,
@@ -300,6 +308,7 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
     a.K_prev = K_prev; a.K_l = K_l;
     a.xcd_map = (n_wh(g) % 8 == 0) ? 1 : 0;
     a.scale = (float)(1.0 / sqrt((double)g.d));
+    a.dkv_full = (int)n_wh(g);
     a.blocks_per_wh = g.N >= 512 ? 2 : 1;
     a.rows_per_block = (g.N + a.blocks_per_wh - 1) / a.blocks_per_wh;
     const int64_t rgrid = n_wh(g) * a.blocks_per_wh;
@@ -320,8 +329,11 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
         b.rows_per_block = g.N;
         if (pfa::backward_dkv_mfma(g.d, g.N, K_l)) {
             b.blocks_per_wh = 1;
-            e = timed(PFA_KERNEL_BWD_SCATTER, s,
-                      [&] { return pfa::launch_backward_dkv(b, dt, g.d, (int)n_wh(g), s); });
+            b.dkv_full = (int)pfa::backward_dkv_full(n_wh(g), g.N, compute_units());
+            const int64_t dgrid64 = b.dkv_full + 2 * (n_wh(g) - b.dkv_full);
+            if (dgrid64 > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
+            const int dgrid = (int)dgrid64;
+            e = timed(PFA_KERNEL_BWD_SCATTER, s, [&] { return pfa::launch_backward_dkv(b, dt, g.d, dgrid, s); });
         } else {
             b.blocks_per_wh = parts;
             e = timed(PFA_KERNEL_BWD_SCATTER, s,

@@ -414,7 +414,16 @@ __global__ __launch_bounds__(16 * kWave) void bwd_dkv_kernel(const BackwardArgs 
     const int wave = threadIdx.x / kWave;
     const int r16 = lane & 15;
     const int q4 = lane >> 4;
-    const WhPart w = decode_block(1, p.xcd_map, g);
+    // a whole window-head, or one token half of a window-head (see dkv_full)
+    WhPart w;
+    int half = -1;
+    if ((int)blockIdx.x < p.dkv_full) {
+        w = decode_block(1, p.xcd_map, g);
+    } else {
+        const int s = (int)blockIdx.x - p.dkv_full;
+        w = wh_coords(p.dkv_full + (s >> 4) * 8 + (s & 7), 0, g);
+        half = (s >> 3) & 1;
+    }
     const size_t plane = (size_t)w.bh * g.H * g.W * D;
     const T* Qh = static_cast<const T*>(p.Q) + plane;
     const float* dOh = p.dO + plane;
@@ -430,7 +439,12 @@ __global__ __launch_bounds__(16 * kWave) void bwd_dkv_kernel(const BackwardArgs 
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A_l + wh_pairs, pair_bytes);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g_buf + wh_pairs, pair_bytes);
     const int mtiles = N / 16;                       // a multiple of MTW, at most 16 MTW
-    const bool wave_active = wave * MTW < mtiles;
+    // this workgroup's token tiles [tile0, tile0 + btiles), mtw per wave (MTW even
+    // when halves are launched)
+    const int btiles = half < 0 ? mtiles : mtiles / 2;
+    const int tile0 = half < 0 ? 0 : half * btiles;
+    const int mtw = half < 0 ? MTW : MTW / 2;
+    const bool wave_active = wave * mtw < btiles;
     const int nblk = N / KB;
     const int blk_entries = KB * K_l;
 
@@ -520,7 +534,8 @@ __global__ __launch_bounds__(16 * kWave) void bwd_dkv_kernel(const BackwardArgs 
                 }
 #pragma unroll
                 for (int mt = 0; mt < MTW; ++mt) {
-                    const int tile = wave * MTW + mt;
+                    if (mt >= mtw) break;
+                    const int tile = tile0 + wave * mtw + mt;
                     const float aA = Md[row * NP + 16 * tile + r16];
                     const float aK = Md[(KB + row) * NP + 16 * tile + r16];
 #pragma unroll
@@ -546,7 +561,8 @@ __global__ __launch_bounds__(16 * kWave) void bwd_dkv_kernel(const BackwardArgs 
     if (!wave_active) return;
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt) {
-        const int tile = wave * MTW + mt;
+        if (mt >= mtw) break;
+        const int tile = tile0 + wave * mtw + mt;
         {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -669,6 +685,16 @@ int backward_fused_rows(int dtype, int D, int N, int K_l, bool want_dap) {
 
 bool backward_dkv_mfma(int D, int N, int K_l) {
     return N % 16 == 0 && N <= 1024 && K_l <= 256 && dkv_tiles_per_wave(N) > 0 && dkv_lds(D, N) <= kLdsBytes;
+}
+
+int64_t backward_dkv_full(int64_t n_wh, int N, int cus) {
+    // one workgroup per CU (its LDS); split only the window-heads of a partial last
+    // round, into pairs of halves that fit that round
+    if (cus < 16 || dkv_tiles_per_wave(N) % 2 != 0 || n_wh < cus) return n_wh;
+    const int64_t full = (n_wh / cus) * cus;
+    const int64_t rem = n_wh - full;
+    if (rem == 0 || rem % 8 != 0 || 2 * rem > cus || full % 8 != 0) return n_wh;
+    return full;
 }
 
 hipError_t launch_backward_dkv(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream) {

@@ -75,6 +75,10 @@ struct BackwardArgs {
     int rows_per_block, blocks_per_wh;
     int xcd_map;
     float scale;             // 1 / sqrt(d)
+    // dK/dV MFMA kernel: workgroups [0, dkv_full) take a whole window-head each;
+    // each further pair (workgroups 8 apart, one XCD) takes the two token halves
+    // of one window-head (balances the last round over the CUs)
+    int dkv_full;
 };
 
 // Row pass: with both K and V staged (when they fit in LDS together), or as a
@@ -85,6 +89,9 @@ hipError_t launch_backward_rows(const BackwardArgs& a, int dtype, int D, bool ha
                                 hipStream_t stream);
 // dK and dV as dense MFMA products over LDS-densified row blocks (N % 16 == 0).
 bool backward_dkv_mfma(int D, int N, int K_l);
+// whole-window-head dK/dV workgroups for n_wh window-heads on `cus` compute units
+// (n_wh when no split applies); the grid is dkv_full + 2 (n_wh - dkv_full)
+int64_t backward_dkv_full(int64_t n_wh, int N, int cus);
 hipError_t launch_backward_dkv(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream);
 // dK and dV otherwise: per window-head LDS accumulators, D/parts columns per workgroup.
 int backward_scatter_parts(int D, int N, int K_l);

@@ -55,6 +55,20 @@ struct WhPart {
     int wh, part, wy, wx, b, bh, win_id, nwin;
 };
 
+// window coordinates of window-head wh
+__device__ __forceinline__ WhPart wh_coords(int wh, int part, const Geom& g) {
+    WhPart w;
+    w.wh = wh;
+    w.part = part;
+    w.nwin = g.nwy * g.nwx;
+    w.win_id = w.wh % w.nwin;
+    w.bh = w.wh / w.nwin;
+    w.b = w.bh / g.heads;
+    w.wy = w.win_id / g.nwx;
+    w.wx = w.win_id - w.wy * g.nwx;
+    return w;
+}
+
 // workgroup -> (window-head, part); with xcd_map the parts of one window-head are
 // consecutive workgroups of one XCD (workgroups are dealt to the 8 XCDs in turn)
 __device__ __forceinline__ WhPart decode_block(int blocks_per_wh, int xcd_map, const Geom& g) {
