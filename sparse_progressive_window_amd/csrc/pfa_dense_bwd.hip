@@ -1,4 +1,4 @@
-// Backward pass of the dense first layer on gfx950 (fp32 MFMA throughout).
+// Backward pass of the dense first layer on gfx950 (matrix cores).
 //
 // The first layer is softmax attention over the N slots of a window (paper notes
 // "Progressive Focused Transformer for Single Image Super-Resolution", section
@@ -12,14 +12,18 @@
 // dense layer writes to lse_out).
 //
 // dense_bwd_dq_kernel: 8 waves x 16 queries per workgroup; K/V tiles of 64 slots
-//   staged in LDS as fp32, double-buffered (the next tile's loads in flight).
-//   Pass 1 accumulates D_i, pass 2 forms dS and dQ. Scores and dO.v come
-//   transposed (16 keys x 16 queries per v_mfma_f32_16x16x4_f32 chain), which
-//   leaves lane (query r16, keys 4 grp + r): the A-operand layout of dS K.
+//   staged in LDS, double-buffered (the next tile's loads in flight). Pass 1
+//   accumulates D_i, pass 2 forms dS and dQ. Scores and dO.v come transposed
+//   (16 keys x 16 queries per tile), which leaves lane (query r16, keys
+//   4 grp + r): the A-operand layout of dS K (v_mfma_f32_16x16x4_f32).
 // dense_bwd_dkv_kernel: 8 waves x 16 keys per workgroup; Q/dO tiles of 64 slots
-//   (with their lse and D) staged in LDS, double-buffered. Scores as
-//   (query 4 grp + r, key r16) per lane: the A-operand layout of P^T dO and
-//   dS^T Q. dV, dK stay in registers over all query tiles.
+//   (with their lse and D) staged in LDS. Scores as (query 4 grp + r, key r16)
+//   per lane: the A-operand layout of P^T dO and dS^T Q (fp32 MFMA). dV, dK stay
+//   in registers over all query tiles.
+// With d = 32 and no bias both kernels compute the scores and dO.v on
+// v_mfma_f32_16x16x32_bf16 from the three-way bf16 split of their fp32 operands
+// (as accurate as fp32 products; pfa_split.h), the tile side split once per tile
+// into bf16 planes in LDS; otherwise on v_mfma_f32_16x16x4_f32.
 #include "pfa_kernels.h"
 #include "pfa_rows.h"
 #include "pfa_split.h"
