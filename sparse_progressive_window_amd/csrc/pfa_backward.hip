@@ -153,7 +153,17 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
         const int qpix = slot_pixel(g, w.wy, w.wx, ii);
         const int roff = ii * K_l * 4;             // byte offset of the row's kept slots
 
-        float G[HAS_V ? KPL : 1];
+        // TR (V pass alone, 8 chunk lanes per row): the 4 entries of a step are summed
+        // over their 8 chunk lanes by a transposing reduction (each stage sends half
+        // of the partial sums), which leaves lane c with entry ent of the step; the
+        // entry of the upper 4 lanes is mirrored so that lanes c and 7 - c agree
+        constexpr bool TR = HAS_V && !HAS_K && CH == 8;
+        float G[HAS_V && !TR ? KPL : 1];
+        float Gt[TR ? NST : 1];
+        const int hh = (vchunk >> 2) & 1;
+        const int b0 = (vchunk & 1) ^ hh;
+        const int b1 = ((vchunk >> 1) & 1) ^ hh;
+        const int ent = 2 * b0 + b1;
         if (HAS_V) {
             float dov[EPC];
             const float* dor = p.dO + plane + (size_t)qpix * D + vchunk * EPC;
@@ -186,27 +196,55 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
                     for (int y = 0; y < EPC; ++y) s = fmaf(dov[y], vf[y], s);
                     part[x] = s;
                 }
+                if constexpr (TR) {
+                    // keep entries 2 b0, 2 b0 + 1; the other two go to lane c ^ 1
+                    const float r0 = (b0 ? part[2] : part[0]) + dppf<kQuadXor1>(b0 ? part[0] : part[2]);
+                    const float r1 = (b0 ? part[3] : part[1]) + dppf<kQuadXor1>(b0 ? part[1] : part[3]);
+                    // keep entry 2 b0 + b1; the other goes to lane c ^ 2
+                    const float r2 = (b1 ? r1 : r0) + dppf<kQuadXor2>(b1 ? r0 : r1);
+                    // lane 7 - c holds the same entry
+                    const float tot = r2 + dppf<kRowHalfMirror>(r2);
+                    const float dve = ent == 0 ? dv[0] : ent == 1 ? dv[1] : ent == 2 ? dv[2] : dv[3];
+                    const float ave = ent == 0 ? av[0] : ent == 1 ? av[1] : ent == 2 ? av[2] : av[3];
+                    const bool valid = e0 + ent < K_l;
+                    const float gx = valid ? dve + tot : 0.0f;
+                    Gt[t] = gx;
+                    dsum = fmaf((valid && hh == 0) ? ave : 0.0f, gx, dsum);   // one lane per entry
+                } else {
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const bool valid = e0 + x < K_l;
-                    const float gx = valid ? dv[x] + chunk_sum<CH>(part[x]) : 0.0f;
-                    G[4 * t + x] = gx;
-                    dsum = fmaf(valid ? av[x] : 0.0f, gx, dsum);
+                    for (int x = 0; x < 4; ++x) {
+                        const bool valid = e0 + x < K_l;
+                        const float gx = valid ? dv[x] + chunk_sum<CH>(part[x]) : 0.0f;
+                        G[(4 * t + x) % (TR ? 1 : KPL)] = gx;
+                        dsum = fmaf(valid ? av[x] : 0.0f, gx, dsum);
+                    }
                 }
             }
+            if constexpr (TR) dsum = chunk_sum<CH>(dsum);   // the 4 entries of each lane quad
             const float Dsum = subgroup_sum<CH, GL>(dsum);
+            if constexpr (TR) {
 #pragma unroll
-            for (int k = 0; k < KPL; ++k) G[k] -= Dsum;
+                for (int t = 0; t < NST; ++t) Gt[t] -= Dsum;
+            } else {
+#pragma unroll
+                for (int k = 0; k < KPL; ++k) G[k] -= Dsum;
+            }
             // g for the scatter pass (and the K pass): lane x % CH of a subgroup stores slot x
 #pragma unroll
             for (int t = 0; t < NST; ++t) {
                 const int e0 = 4 * (vsub + GS * t);
+                if constexpr (TR) {   // the lower 4 lanes of a subgroup store their entries
+                    const bool st = active && hh == 0 && e0 + ent < K_l;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Gt[t]), rg,
+                                                          st ? roff + (e0 + ent) * 4 : 0x7FFFFFF0, 0, 0);
+                } else {
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    if (x % CH != vchunk) continue;
-                    const bool st = active && e0 + x < K_l;
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(G[4 * t + x]), rg,
-                                                          st ? roff + (e0 + x) * 4 : 0x7FFFFFF0, 0, 0);
+                    for (int x = 0; x < 4; ++x) {
+                        if (x % CH != vchunk) continue;
+                        const bool st = active && e0 + x < K_l;
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(G[(4 * t + x) % (TR ? 1 : KPL)]), rg,
+                                                              st ? roff + (e0 + x) * 4 : 0x7FFFFFF0, 0, 0);
+                    }
                 }
             }
         }
@@ -242,7 +280,7 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
                 float gv[4];
                 if (HAS_V) {
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) gv[x] = G[(4 * t + x) % KPL];
+                    for (int x = 0; x < 4; ++x) gv[x] = G[(4 * t + x) % (TR ? 1 : KPL)];
                 } else {
                     gv[0] = __uint_as_float(g4.x);
                     gv[1] = __uint_as_float(g4.y);
