@@ -262,10 +262,11 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
             // the next step's loads are issued before this step's gathers, and the
             // loop is unrolled by 2 (measured 7-8 % faster than rolled; by 4 or fully
             // the hoisted loads spill)
+            constexpr int KUN = HAS_V ? NST : 2;   // steps unrolled
             uint4 j4n = load16(rI, roff + 16 * vsub);
             uint4 a4n = load16(rA, roff + 16 * vsub);
             uint4 g4n = HAS_V ? make_uint4(0u, 0u, 0u, 0u) : load16(rg, roff + 16 * vsub);
-#pragma unroll (HAS_V ? NST : 2)
+#pragma unroll KUN
             for (int t = 0; t < NST; ++t) {
                 const int e0 = 4 * (vsub + GS * t);
                 const uint4 j4 = j4n;

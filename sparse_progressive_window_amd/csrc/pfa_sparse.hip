@@ -252,7 +252,7 @@ __device__ __forceinline__ void radix_threshold(KF key, int kmin, int kmax, bool
 // INT_MAX when the row has no tie to break. any_tie: some row of the wave has.
 template <int GL, int KPT, class KF, class JF>
 __device__ __forceinline__ int tie_cut(KF key, JF jf, int tau, int need_tau, int n_tau, bool active, int N,
-                                       int lane, bool& any_tie) {
+                                       bool& any_tie) {
     using G = Grp<GL>;
     int jcut = 0x7fffffff;
     const bool tie = active && n_tau > need_tau;
@@ -289,7 +289,6 @@ __device__ __forceinline__ void select_emit(const SparseArgs& p, const Geom& g, 
                                             const T* Vh, float* Oh) {
     constexpr int EPC = Chunk<T>::kElems;
     constexpr int CH = D / EPC;
-    constexpr int ROWB = D * (int)sizeof(T);
     constexpr int GS = GL / CH;
     using G = Grp<GL>;
     const int gl = lane & (GL - 1);
@@ -316,7 +315,7 @@ __device__ __forceinline__ void select_emit(const SparseArgs& p, const Geom& g, 
                                   need_tau, n_tau);
     bool tie;
     const int jcut = tie_cut<GL, KPT>([&](int t) { return key[t]; }, [&](int t) { return jj[t]; }, tau, need_tau,
-                                      n_tau, active, g.N, lane, tie);
+                                      n_tau, active, g.N, tie);
 
     bool kept[KPT];
     float ksum = 0.0f;
@@ -425,7 +424,7 @@ __device__ __forceinline__ void select_store(const SparseArgs& p, int lane, bool
     int jcut = 0x7fffffff;
     if (!ORDERED && any_tie) {
         bool unused;
-        jcut = tie_cut<GL, KPT>(key, jf, tau, need_tau, n_tau, active, N, lane, unused);
+        jcut = tie_cut<GL, KPT>(key, jf, tau, need_tau, n_tau, active, N, unused);
     }
 
     // kept = key > thr, plus (ties) some keys equal to tau: thr = tau - 1 keeps every
@@ -781,7 +780,6 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int grp = lane >> 4;
-    const int gl = lane & (GL - 1);
     const WhPart w = decode_block(p.blocks_per_wh, p.xcd_map, g);
     const size_t plane = (size_t)w.bh * g.H * g.W * D;
     const T* Qh = static_cast<const T*>(p.Q) + plane;
