@@ -251,6 +251,13 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const D
         const int t0 = (it - pass * ntiles) * kTile;
         const float* Kt = Kt2[it & 1];
         const float* Vt = Vt2[SPLIT ? 0 : (it & 1)];
+        // this tile's dA^1 (4 keys per lane and 16-key step) before the next tile's
+        // loads: waits count loads in issue order, so the prefetch stays in flight
+        float4 dat[SUB];
+#pragma unroll
+        for (int s = 0; s < SUB; ++s)
+            dat[s] = HAS_DA ? *reinterpret_cast<const float4*>(dArow + t0 + s * 16 + 4 * grp)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
         if (it + 1 < 2 * ntiles) {
             const int tn = ((it + 1) % ntiles) * kTile;
             kreg.load(Kh, g, bp.wy, bp.wx, tn);
@@ -297,9 +304,7 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const D
 #pragma unroll
                     for (int r = 0; r < 4; ++r) b[r] = btab[idx0 - r];
                 }
-                float4 da = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (HAS_DA) da = *reinterpret_cast<const float4*>(dArow + key0 + 4 * grp);
-                const float dav[4] = {da.x, da.y, da.z, da.w};
+                const float dav[4] = {dat[s].x, dat[s].y, dat[s].z, dat[s].w};
                 float P[4], G[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -353,6 +358,7 @@ __global__ __launch_bounds__(kBwdWaves * kWave, 4) void dense_bwd_dkv_kernel(con
     // workgroups per CU)
     constexpr bool SPLIT = D == 32 && !BIAS;
     constexpr bool BFIN = sizeof(T) == 2;
+    constexpr bool HOIST_DA = HAS_DA && !BIAS;
     constexpr int NB32 = SPLIT ? 1 : 2;
     constexpr int QPB = SPLIT ? (BFIN ? 1 : 3) * kTile * 64 : 16;
     constexpr int OPB = SPLIT ? 3 * kTile * 64 : 16;
@@ -448,6 +454,13 @@ __global__ __launch_bounds__(kBwdWaves * kWave, 4) void dense_bwd_dkv_kernel(con
         const float* dOt = dOt2[SPLIT ? 0 : (it & 1)];
         const float* lset = lset2[it & 1];
         const float* Dt = Dt2[it & 1];
+        // this tile's dA^1 column values before the next tile's loads (waits count loads
+        // in issue order), moved down by one 16-query step per step; with a bias table
+        // they stay in the step (held here they spill)
+        float dac[4 * SUB];
+#pragma unroll
+        for (int e = 0; e < 4 * SUB; ++e)
+            dac[e] = HOIST_DA ? dAcol[(size_t)(t0 + (e >> 2) * 16 + 4 * grp + (e & 3)) * N] : 0.0f;
         if (it + 1 < ntiles) {
             qreg.load(Qh, g, bp.wy, bp.wx, t0 + kTile);
             oreg.load(dOh, g, bp.wy, bp.wx, t0 + kTile);
@@ -502,7 +515,7 @@ __global__ __launch_bounds__(kBwdWaves * kWave, 4) void dense_bwd_dkv_kernel(con
             for (int r = 0; r < 4; ++r) {
                 const int ql = s * 16 + 4 * grp + r;   // query within the tile
                 P[r] = fast_exp2(fmaf(st[r], sc, b[r] - lset[ql]));
-                const float G = dpt[r] + (HAS_DA ? dAcol[(size_t)(t0 + ql) * N] : 0.0f);
+                const float G = dpt[r] + (HOIST_DA ? dac[r] : HAS_DA ? dAcol[(size_t)(t0 + ql) * N] : 0.0f);
                 dS[r] = P[r] * (G - Dt[ql]);
             }
 #pragma unroll
@@ -513,6 +526,8 @@ __global__ __launch_bounds__(kBwdWaves * kWave, 4) void dense_bwd_dkv_kernel(con
                     dv[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(P[r], dOt[ql * STR + 16 * c + r16], dv[c], 0, 0, 0);
                     dk[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(dS[r], Qt[ql * STR + 16 * c + r16], dk[c], 0, 0, 0);
                 }
+#pragma unroll
+            for (int e = 0; e < 4 * (SUB - 1); ++e) dac[e] = dac[e + 4];
         }
         if (it + 1 < ntiles) store_buffered((it + 1) & 1);
         if constexpr (SPLIT) {
