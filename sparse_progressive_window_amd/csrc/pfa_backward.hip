@@ -317,24 +317,35 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
             if (want_dap) {
                 // the wave's LDS writes above complete before the scan reads them
                 __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                // the row's slots in chunks of SU x GL, each chunk's loads issued together
-                constexpr int SU = 4;
+                // the row's slots in chunks of SU x GL, each chunk's loads issued together and
+                // before the previous chunk's stores: stores count in the same in-order
+                // vector-memory counter, so loads issued after them would wait for them too
+                // (measured 17 % faster on the 1024-slot rows; 8 x GL slots beats 4 and 16)
+                constexpr int SU = NST >= 8 ? 8 : 4;
                 const int K_prev = p.K_prev;
                 const size_t srow = ((size_t)w.wh * N + ii) * K_prev;
                 int run = 0;
+                int jn[SU];
+                float an[SU];
+                auto load_chunk = [&](int s0) {
+#pragma unroll
+                    for (int u = 0; u < SU; ++u) {
+                        const int slot = s0 + u * GL + gl;
+                        jn[u] = slot;
+                        an[u] = 0.0f;
+                        if (slot < K_prev) {
+                            if (p.I_prev) jn[u] = p.I_prev[srow + slot];
+                            an[u] = p.A_prev[srow + slot];
+                        }
+                    }
+                };
+                load_chunk(0);
                 for (int s0 = 0; s0 < K_prev; s0 += SU * GL) {
                     int jj[SU];
                     float ap[SU];
 #pragma unroll
-                    for (int u = 0; u < SU; ++u) {
-                        const int slot = s0 + u * GL + gl;
-                        jj[u] = slot;
-                        ap[u] = 0.0f;
-                        if (slot < K_prev) {
-                            if (p.I_prev) jj[u] = p.I_prev[srow + slot];
-                            ap[u] = p.A_prev[srow + slot];
-                        }
-                    }
+                    for (int u = 0; u < SU; ++u) { jj[u] = jn[u]; ap[u] = an[u]; }
+                    if (s0 + SU * GL < K_prev) load_chunk(s0 + SU * GL);
 #pragma unroll
                     for (int u = 0; u < SU; ++u) {
                         const int slot = s0 + u * GL + gl;
