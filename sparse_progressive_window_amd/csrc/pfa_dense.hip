@@ -8,8 +8,10 @@
 // A workgroup of 8 waves owns 128 query rows of one window-head (16 per wave);
 // K and V stream through LDS in tiles of 64 keys, double-buffered, shared by
 // all 8 waves (rows padded by 16 bytes so the MFMA operand reads of 16
-// consecutive rows hit distinct banks). The workgroups of one window-head are
-// consecutive on one XCD, so its K/V stay in that XCD's L2.
+// consecutive rows hit distinct banks). The global loads run two tiles ahead
+// in two register sets, so each has two tiles of work to land. The workgroups
+// of one window-head are consecutive on one XCD, so its K/V stay in that XCD's
+// L2.
 //
 // Scores are produced transposed, S^T = K Q^T, with 16x16 MFMA tiles (16 keys x
 // 16 queries): the accumulator gives each lane 4 consecutive keys of one query,
@@ -283,6 +285,7 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
     };
     const int ntiles = N / KT;
     uint4 kreg[PER], vreg[PER];
+    uint4 kreg2[PER], vreg2[PER];   // the second register set (odd tiles)
 
     if constexpr (!WA) {
         // O-only: one pass with an online softmax. Per K/V tile, the running max m
@@ -298,11 +301,16 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
         tile_load<ROWB, KT>(vreg, Vh, g, wy, wx, 0);
         store_k(Ks[0], kreg);
         tile_store<ROWB, KT, STRIDE>(Vs[0], vreg);
+        if (ntiles > 1) {
+            tile_load<ROWB, KT>(kreg2, Kh, g, wy, wx, KT);
+            tile_load<ROWB, KT>(vreg2, Vh, g, wy, wx, KT);
+        }
         __syncthreads();
-        for (int t = 0; t < ntiles; ++t) {
-            if (t + 1 < ntiles) {
-                tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, (t + 1) * KT);
-                tile_load<ROWB, KT>(vreg, Vh, g, wy, wx, (t + 1) * KT);
+        auto step = [&](int t, uint4 (&kld)[PER], uint4 (&vld)[PER], const uint4 (&kst)[PER],
+                        const uint4 (&vst)[PER]) {
+            if (t + 2 < ntiles) {
+                tile_load<ROWB, KT>(kld, Kh, g, wy, wx, (t + 2) * KT);
+                tile_load<ROWB, KT>(vld, Vh, g, wy, wx, (t + 2) * KT);
             }
             const unsigned char* kt = Ks[t & 1];
             const unsigned char* vt = Vs[t & 1];
@@ -350,10 +358,14 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
                 for (int c = 0; c < CT; ++c) oacc[c] = Ops::pv(ps, vrow, c * 16 + r16, oacc[c]);
             }
             if (t + 1 < ntiles) {
-                store_k(Ks[(t + 1) & 1], kreg);
-                tile_store<ROWB, KT, STRIDE>(Vs[(t + 1) & 1], vreg);
+                store_k(Ks[(t + 1) & 1], kst);
+                tile_store<ROWB, KT, STRIDE>(Vs[(t + 1) & 1], vst);
             }
             __syncthreads();
+        };
+        for (int t = 0; t < ntiles; t += 2) {
+            step(t, kreg, vreg, kreg2, vreg2);
+            if (t + 1 < ntiles) step(t + 1, kreg2, vreg2, kreg, vreg);
         }
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
@@ -376,9 +388,11 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
     float m = -INFINITY, l = 0.0f;
     tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, 0);
     store_k(Ks[0], kreg);
+    if (ntiles > 1) tile_load<ROWB, KT>(kreg2, Kh, g, wy, wx, KT);
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles) tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, (t + 1) * KT);
+    // ld: the registers of tile t (already in LDS), refilled with tile t + 2; st: tile t + 1
+    auto pass1 = [&](int t, uint4 (&ld)[PER], const uint4 (&st)[PER]) {
+        if (t + 2 < ntiles) tile_load<ROWB, KT>(ld, Kh, g, wy, wx, (t + 2) * KT);
         const unsigned char* kt = Ks[t & 1];
         // the whole tile's scores, then one rescale of the running sum (m is in
         // scaled base-2 units; sc > 0, so the raw maximum gives the scaled one)
@@ -420,8 +434,12 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
         }
         l = l * fast_exp2(m - mn) + lt;
         m = mn;
-        if (t + 1 < ntiles) store_k(Ks[(t + 1) & 1], kreg);
+        if (t + 1 < ntiles) store_k(Ks[(t + 1) & 1], st);
         __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        pass1(t, kreg, kreg2);
+        if (t + 1 < ntiles) pass1(t + 1, kreg2, kreg);
     }
     // combine the 4 lane groups holding the same query
 #pragma unroll
@@ -450,11 +468,16 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
     tile_load<ROWB, KT>(vreg, Vh, g, wy, wx, 0);
     store_k(Ks[0], kreg);
     tile_store<ROWB, KT, STRIDE>(Vs[0], vreg);
+    if (ntiles > 1) {
+        tile_load<ROWB, KT>(kreg2, Kh, g, wy, wx, KT);
+        tile_load<ROWB, KT>(vreg2, Vh, g, wy, wx, KT);
+    }
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles) {
-            tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, (t + 1) * KT);
-            tile_load<ROWB, KT>(vreg, Vh, g, wy, wx, (t + 1) * KT);
+    auto pass2 = [&](int t, uint4 (&kld)[PER], uint4 (&vld)[PER], const uint4 (&kst)[PER],
+                     const uint4 (&vst)[PER]) {
+        if (t + 2 < ntiles) {
+            tile_load<ROWB, KT>(kld, Kh, g, wy, wx, (t + 2) * KT);
+            tile_load<ROWB, KT>(vld, Vh, g, wy, wx, (t + 2) * KT);
         }
         const unsigned char* kt = Ks[t & 1];
         const unsigned char* vt = Vs[t & 1];
@@ -485,10 +508,14 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
             for (int c = 0; c < CT; ++c) oacc[c] = Ops::pv(ps, vrow, c * 16 + r16, oacc[c]);
         }
         if (t + 1 < ntiles) {
-            store_k(Ks[(t + 1) & 1], kreg);
-            tile_store<ROWB, KT, STRIDE>(Vs[(t + 1) & 1], vreg);
+            store_k(Ks[(t + 1) & 1], kst);
+            tile_store<ROWB, KT, STRIDE>(Vs[(t + 1) & 1], vst);
         }
         __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        pass2(t, kreg, vreg, kreg2, vreg2);
+        if (t + 1 < ntiles) pass2(t + 1, kreg2, vreg2, kreg, vreg);
     }
     if (!wave_active) return;
     // lane holds O[query q0 + 4*grp + r][dim 16c + r16]

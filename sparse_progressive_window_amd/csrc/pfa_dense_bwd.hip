@@ -12,7 +12,7 @@
 // dense layer writes to lse_out).
 //
 // dense_bwd_dq_kernel: 8 waves x 16 queries per workgroup; K/V tiles of 64 slots
-//   staged in LDS, double-buffered (the next tile's loads in flight). Pass 1
+//   staged in LDS, double-buffered (the loads of the tile after next in flight). Pass 1
 //   accumulates D_i, pass 2 forms dS and dQ. Scores and dO.v come transposed
 //   (16 keys x 16 queries per tile), which leaves lane (query r16, keys
 //   4 grp + r): the A-operand layout of dS K (v_mfma_f32_16x16x4_f32).
@@ -229,24 +229,31 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const D
     v4f dq[CT];
 #pragma unroll
     for (int c = 0; c < CT; ++c) dq[c] = v4f{0.f, 0.f, 0.f, 0.f};
-    // the tile sequence of both passes, double-buffered: tile it + 1 is loaded
-    // into registers while tile it is used from LDS
+    // the tile sequence of both passes: LDS double-buffered, the global loads two
+    // tiles ahead in two register sets (tile it + 2 is loaded while tile it is used
+    // from LDS and tile it + 1 waits in registers)
     const int ntiles = N / kTile;
-    TileRegs<T, D> kreg, vreg;
-    auto store_tiles = [&](int b) {
-        kreg.template store<STR>(Kt2[b]);
+    TileRegs<T, D> kreg, vreg, kreg2, vreg2;
+    auto store_tiles = [&](int b, const TileRegs<T, D>& kr, const TileRegs<T, D>& vr) {
+        kr.template store<STR>(Kt2[b]);
         if constexpr (SPLIT) {
-            kreg.store_planes(KP2[b]);
-            vreg.store_planes(VP2[b]);
+            kr.store_planes(KP2[b]);
+            vr.store_planes(VP2[b]);
         } else {
-            vreg.template store<STR>(Vt2[b]);
+            vr.template store<STR>(Vt2[b]);
         }
     };
     kreg.load(Kh, g, bp.wy, bp.wx, 0);
     vreg.load(Vh, g, bp.wy, bp.wx, 0);
-    store_tiles(0);
+    store_tiles(0, kreg, vreg);
+    {
+        const int t1 = (1 % ntiles) * kTile;
+        kreg2.load(Kh, g, bp.wy, bp.wx, t1);
+        vreg2.load(Vh, g, bp.wy, bp.wx, t1);
+    }
     __syncthreads();
-    for (int it = 0; it < 2 * ntiles; ++it) {
+    auto step = [&](int it, TileRegs<T, D>& kld, TileRegs<T, D>& vld, const TileRegs<T, D>& kst,
+                    const TileRegs<T, D>& vst) {
         const int pass = it / ntiles;
         const int t0 = (it - pass * ntiles) * kTile;
         const float* Kt = Kt2[it & 1];
@@ -258,10 +265,10 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const D
         for (int s = 0; s < SUB; ++s)
             dat[s] = HAS_DA ? *reinterpret_cast<const float4*>(dArow + t0 + s * 16 + 4 * grp)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
-        if (it + 1 < 2 * ntiles) {
-            const int tn = ((it + 1) % ntiles) * kTile;
-            kreg.load(Kh, g, bp.wy, bp.wx, tn);
-            vreg.load(Vh, g, bp.wy, bp.wx, tn);
+        if (it + 2 < 2 * ntiles) {
+            const int tn = ((it + 2) % ntiles) * kTile;
+            kld.load(Kh, g, bp.wy, bp.wx, tn);
+            vld.load(Vh, g, bp.wy, bp.wx, tn);
         }
         {
 #pragma unroll
@@ -333,8 +340,12 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const D
             Dq += __shfl_xor(Dq, 32);
             if (wave_active && grp == 0) p.Dws[(size_t)bp.wh * N + qi] = Dq;
         }
-        if (it + 1 < 2 * ntiles) store_tiles((it + 1) & 1);
+        if (it + 1 < 2 * ntiles) store_tiles((it + 1) & 1, kst, vst);
         __syncthreads();
+    };
+    for (int it = 0; it < 2 * ntiles; it += 2) {   // 2 ntiles is even
+        step(it, kreg, vreg, kreg2, vreg2);
+        step(it + 1, kreg2, vreg2, kreg, vreg);
     }
     if (!wave_active) return;
     // lane holds dQ[query q0 + 4 grp + r][dim 16 c + r16]
