@@ -584,6 +584,41 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
             for (int m = 0; m < CH; ++m) r.q[m] = *reinterpret_cast<const uint4*>(qrow + coff[m]);
         }
     };
+    // QS: the query rows of the wave's next batch are loaded before this batch's
+    // I/A stores (loads issued after them would wait for them too: one in-order
+    // counter) and pass through the wave's histogram words, free between selections
+    // (measured 4-8 % faster with 8 candidates per lane, neutral or slower with fewer)
+    constexpr bool QS = !PQ && VS == kVnone && KPT >= 8;
+    constexpr int QW = RPW * ROWB / 4;                 // words of the batch's query rows
+    constexpr int NQ = (QW + kWave - 1) / kWave;
+    static_assert(!QS || QW <= HISTW, "query rows exceed the histogram words");
+    unsigned* qst = reinterpret_cast<unsigned*>(sbase) + wave * HISTW;
+    auto load_qs = [&](int b0, unsigned (&qd)[NQ]) {
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            const int u = lane + kWave * k;
+            qd[k] = 0u;
+            if (u < QW) {
+                const int r = u / (ROWB / 4);
+                const int ir = b0 + r;
+                const int iq = ir < row1 ? ir : row0;
+                const unsigned* qrow = reinterpret_cast<const unsigned*>(Qh + (size_t)slot_pixel(g, w.wy, w.wx, iq) * D);
+                qd[k] = qrow[u - r * (ROWB / 4)];
+            }
+        }
+    };
+    auto put_qs = [&](const unsigned (&qd)[NQ]) {
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            const int u = lane + kWave * k;
+            if (u < QW) qst[u] = qd[k];
+        }
+    };
+    if constexpr (QS) {
+        unsigned qd[NQ];
+        load_qs(row0 + wave * RPW, qd);
+        put_qs(qd);
+    }
     RowIn cur;
     load_row(cur, row0 + wave * RPW);
     for (int base = row0 + wave * RPW; base < row1; base += NW * RPW) {
@@ -612,7 +647,10 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
             const unsigned char* qrow = reinterpret_cast<const unsigned char*>(Qh + (size_t)qpix * D);
 #pragma unroll
             for (int m = 0; m < CH; ++m) {
-                const uint4 c = PQ ? cur.q[m] : *reinterpret_cast<const uint4*>(qrow + coff[m]);
+                const uint4 c = PQ   ? cur.q[m]
+                                : QS ? *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(qst) +
+                                                                        grp * ROWB + coff[m])
+                                     : *reinterpret_cast<const uint4*>(qrow + coff[m]);
                 if constexpr (DOT2) qp[m] = c;
                 else Chunk<T>::to_f32(c, &qf[m * EPC]);
             }
@@ -699,9 +737,13 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
         if constexpr (VS == kVnone) {
             const size_t rbase = ((size_t)w.wh * N + base) * p.K_l;
             const int nbytes = max(0, min(RPW, row1 - base)) * p.K_l * 4;
+            unsigned qn[NQ];
+            const bool more = base + NW * RPW < row1;
+            if (QS && more) load_qs(base + NW * RPW, qn);
             select_store<GL, KPT, BPL, false>(
                 p, lane, active, N, [&](int t) { return jj[t]; }, [&](int t) { return FULL || valid[t]; }, sv, hb,
                 make_rsrc(p.I_out + rbase, nbytes), make_rsrc(p.A_out + rbase, nbytes), grp * p.K_l);
+            if (QS && more) put_qs(qn);
         } else {
             select_emit<T, D, GL, KPT, VS, BPL>(p, g, lane, active, row, qpix, jj, valid, sv, hb, scr, SCG, Vh,
                                                 Oh);
