@@ -19,7 +19,10 @@
 //   16-byte chunked V/K row (CH = row bytes / 16) and a subgroup of CH lanes
 //   takes 4 consecutive kept slots at a time. Pass V: gather v_j from LDS, dot
 //   with dO_i (chunk sums by DPP quad exchanges and a half-row mirror), row sum
-//   D_i, g written to a workspace. Pass K: gather k_j from LDS, dQ_i, and
+//   D_i, g written to a workspace; alone with 8 chunk lanes (fp32, d = 32) a
+//   transposing reduction leaves one entry per lane, so a lane loads only that
+//   entry's A and dA, and the next row's loads go out before this row's
+//   reduction and stores. Pass K: gather k_j from LDS, dQ_i, and
 //   dA^{l-1}: kept tokens are marked in a per-row LDS bitmap, the I^{l-1} row is
 //   scanned in slot order, and the r-th marked slot takes kept entry r (I^l is
 //   a subsequence of I^{l-1} in its order). When K and V fit in LDS together
@@ -146,6 +149,90 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
     const int row0 = w.part * p.rows_per_block;
     const int row1 = min(N, row0 + p.rows_per_block);
 
+    if constexpr (HAS_V && !HAS_K && CH == 8) {
+        // V pass alone with 8 chunk lanes per row (fp32, d = 32). The 4 entries of a
+        // step are summed over their chunk lanes by a transposing reduction (each
+        // stage sends half of the partial sums), which leaves lane c with entry ent
+        // of the step; lanes c and 7 - c agree. A lane therefore loads the step's 4
+        // slot indices (all chunk lanes gather their V chunks) but only its own
+        // entry's A and dA, and a row's loads are issued while the previous row is
+        // reduced and its g stored.
+        const int hh = (vchunk >> 2) & 1;
+        const int b0 = (vchunk & 1) ^ hh;
+        const int b1 = ((vchunk >> 1) & 1) ^ hh;
+        const int ent = 2 * b0 + b1;
+        struct VRow {
+            uint4 j4[NST];
+            float av[NST], dv[NST];
+            float4 dO;
+        };
+        auto load_vrow = [&](VRow& r, int ii) {
+            const int roff = ii * K_l * 4;
+            r.dO = *reinterpret_cast<const float4*>(p.dO + plane + (size_t)slot_pixel(g, w.wy, w.wx, ii) * D +
+                                                    vchunk * EPC);
+#pragma unroll
+            for (int t = 0; t < NST; ++t) {
+                const int off = roff + 4 * (vsub + GS * t) * 4;
+                r.j4[t] = load16(rI, off);
+                r.av[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rA, off + ent * 4, 0, 0));
+                r.dv[t] = p.dA_l ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdA, off + ent * 4, 0, 0))
+                                 : 0.0f;
+            }
+        };
+        int base = row0 + wave * RPW;
+        VRow cur;
+        if (base < row1) load_vrow(cur, base + grp < row1 ? base + grp : row0);
+        for (; base < row1; base += NW * RPW) {
+            const int i = base + grp;
+            const bool active = i < row1;
+            const int roff = (active ? i : row0) * K_l * 4;
+            VRow nxt;
+            const int nb = base + NW * RPW;
+            if (nb < row1) load_vrow(nxt, nb + grp < row1 ? nb + grp : row0);
+            const float dov[4] = {cur.dO.x, cur.dO.y, cur.dO.z, cur.dO.w};
+            float Gt[NST];
+            float dsum = 0.0f;
+#pragma unroll
+            for (int t = 0; t < NST; ++t) {
+                const int e0 = 4 * (vsub + GS * t);
+                const unsigned jv[4] = {cur.j4[t].x, cur.j4[t].y, cur.j4[t].z, cur.j4[t].w};
+                float part[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int j = (int)min(jv[x], (unsigned)(N - 1));   // memory safety only
+                    float vf[EPC];
+                    Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(Vs + j * ROWB + vchunk * 16), vf);
+                    float sdot = 0.0f;
+#pragma unroll
+                    for (int y = 0; y < EPC; ++y) sdot = fmaf(dov[y], vf[y], sdot);
+                    part[x] = sdot;
+                }
+                // keep entries 2 b0, 2 b0 + 1; the other two go to lane c ^ 1
+                const float r0 = (b0 ? part[2] : part[0]) + dppf<kQuadXor1>(b0 ? part[0] : part[2]);
+                const float r1 = (b0 ? part[3] : part[1]) + dppf<kQuadXor1>(b0 ? part[1] : part[3]);
+                // keep entry 2 b0 + b1; the other goes to lane c ^ 2
+                const float r2 = (b1 ? r1 : r0) + dppf<kQuadXor2>(b1 ? r0 : r1);
+                // lane 7 - c holds the same entry
+                const float tot = r2 + dppf<kRowHalfMirror>(r2);
+                const bool valid = e0 + ent < K_l;
+                const float gx = valid ? cur.dv[t] + tot : 0.0f;
+                Gt[t] = gx;
+                dsum = fmaf((valid && hh == 0) ? cur.av[t] : 0.0f, gx, dsum);   // one lane per entry
+            }
+            dsum = chunk_sum<CH>(dsum);   // the 4 entries of each lane quad
+            const float Dsum = subgroup_sum<CH, GL>(dsum);
+#pragma unroll
+            for (int t = 0; t < NST; ++t) {
+                const int e0 = 4 * (vsub + GS * t);
+                const bool st = active && hh == 0 && e0 + ent < K_l;   // the lower 4 lanes store
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Gt[t] - Dsum), rg,
+                                                      st ? roff + (e0 + ent) * 4 : 0x7FFFFFF0, 0, 0);
+            }
+            cur = nxt;
+        }
+        return;
+    }
+
     for (int base = row0 + wave * RPW; base < row1; base += NW * RPW) {
         const int i = base + grp;
         const bool active = i < row1;
@@ -153,17 +240,7 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
         const int qpix = slot_pixel(g, w.wy, w.wx, ii);
         const int roff = ii * K_l * 4;             // byte offset of the row's kept slots
 
-        // TR (V pass alone, 8 chunk lanes per row): the 4 entries of a step are summed
-        // over their 8 chunk lanes by a transposing reduction (each stage sends half
-        // of the partial sums), which leaves lane c with entry ent of the step; the
-        // entry of the upper 4 lanes is mirrored so that lanes c and 7 - c agree
-        constexpr bool TR = HAS_V && !HAS_K && CH == 8;
-        float G[HAS_V && !TR ? KPL : 1];
-        float Gt[TR ? NST : 1];
-        const int hh = (vchunk >> 2) & 1;
-        const int b0 = (vchunk & 1) ^ hh;
-        const int b1 = ((vchunk >> 1) & 1) ^ hh;
-        const int ent = 2 * b0 + b1;
+        float G[HAS_V ? KPL : 1];
         if (HAS_V) {
             float dov[EPC];
             const float* dor = p.dO + plane + (size_t)qpix * D + vchunk * EPC;
@@ -196,55 +273,27 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
                     for (int y = 0; y < EPC; ++y) s = fmaf(dov[y], vf[y], s);
                     part[x] = s;
                 }
-                if constexpr (TR) {
-                    // keep entries 2 b0, 2 b0 + 1; the other two go to lane c ^ 1
-                    const float r0 = (b0 ? part[2] : part[0]) + dppf<kQuadXor1>(b0 ? part[0] : part[2]);
-                    const float r1 = (b0 ? part[3] : part[1]) + dppf<kQuadXor1>(b0 ? part[1] : part[3]);
-                    // keep entry 2 b0 + b1; the other goes to lane c ^ 2
-                    const float r2 = (b1 ? r1 : r0) + dppf<kQuadXor2>(b1 ? r0 : r1);
-                    // lane 7 - c holds the same entry
-                    const float tot = r2 + dppf<kRowHalfMirror>(r2);
-                    const float dve = ent == 0 ? dv[0] : ent == 1 ? dv[1] : ent == 2 ? dv[2] : dv[3];
-                    const float ave = ent == 0 ? av[0] : ent == 1 ? av[1] : ent == 2 ? av[2] : av[3];
-                    const bool valid = e0 + ent < K_l;
-                    const float gx = valid ? dve + tot : 0.0f;
-                    Gt[t] = gx;
-                    dsum = fmaf((valid && hh == 0) ? ave : 0.0f, gx, dsum);   // one lane per entry
-                } else {
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const bool valid = e0 + x < K_l;
-                        const float gx = valid ? dv[x] + chunk_sum<CH>(part[x]) : 0.0f;
-                        G[(4 * t + x) % (TR ? 1 : KPL)] = gx;
-                        dsum = fmaf(valid ? av[x] : 0.0f, gx, dsum);
-                    }
+                for (int x = 0; x < 4; ++x) {
+                    const bool valid = e0 + x < K_l;
+                    const float gx = valid ? dv[x] + chunk_sum<CH>(part[x]) : 0.0f;
+                    G[4 * t + x] = gx;
+                    dsum = fmaf(valid ? av[x] : 0.0f, gx, dsum);
                 }
             }
-            if constexpr (TR) dsum = chunk_sum<CH>(dsum);   // the 4 entries of each lane quad
             const float Dsum = subgroup_sum<CH, GL>(dsum);
-            if constexpr (TR) {
 #pragma unroll
-                for (int t = 0; t < NST; ++t) Gt[t] -= Dsum;
-            } else {
-#pragma unroll
-                for (int k = 0; k < KPL; ++k) G[k] -= Dsum;
-            }
+            for (int k = 0; k < KPL; ++k) G[k] -= Dsum;
             // g for the scatter pass (and the K pass): lane x % CH of a subgroup stores slot x
 #pragma unroll
             for (int t = 0; t < NST; ++t) {
                 const int e0 = 4 * (vsub + GS * t);
-                if constexpr (TR) {   // the lower 4 lanes of a subgroup store their entries
-                    const bool st = active && hh == 0 && e0 + ent < K_l;
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Gt[t]), rg,
-                                                          st ? roff + (e0 + ent) * 4 : 0x7FFFFFF0, 0, 0);
-                } else {
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        if (x % CH != vchunk) continue;
-                        const bool st = active && e0 + x < K_l;
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(G[(4 * t + x) % (TR ? 1 : KPL)]), rg,
-                                                              st ? roff + (e0 + x) * 4 : 0x7FFFFFF0, 0, 0);
-                    }
+                for (int x = 0; x < 4; ++x) {
+                    if (x % CH != vchunk) continue;
+                    const bool st = active && e0 + x < K_l;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(G[4 * t + x]), rg,
+                                                          st ? roff + (e0 + x) * 4 : 0x7FFFFFF0, 0, 0);
                 }
             }
         }
@@ -281,7 +330,7 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
                 float gv[4];
                 if (HAS_V) {
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) gv[x] = G[(4 * t + x) % (TR ? 1 : KPL)];
+                    for (int x = 0; x < 4; ++x) gv[x] = G[4 * t + x];
                 } else {
                     gv[0] = __uint_as_float(g4.x);
                     gv[1] = __uint_as_float(g4.y);
