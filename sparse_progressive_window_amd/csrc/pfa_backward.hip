@@ -233,6 +233,24 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
         return;
     }
 
+    // K pass alone: a row's query chunk and first-step loads are issued before the
+    // previous row's dA^{l-1} scan, whose stores would otherwise delay them (one
+    // in-order wait counter for loads and stores)
+    constexpr bool XR = HAS_K && !HAS_V;
+    float qvx[EPC];
+    uint4 j4x = make_uint4(0u, 0u, 0u, 0u), a4x = j4x, g4x = j4x;
+    auto load_first = [&](int b0) {
+        const int ix = b0 + grp < row1 ? b0 + grp : row0;
+        load_row_chunk<T, D>(static_cast<const T*>(p.Q) + plane + (size_t)slot_pixel(g, w.wy, w.wx, ix) * D, vchunk,
+                             qvx);
+        const int ro = ix * K_l * 4 + 16 * vsub;
+        j4x = load16(rI, ro);
+        a4x = load16(rA, ro);
+        g4x = load16(rg, ro);
+    };
+    if constexpr (XR) {
+        if (row0 + wave * RPW < row1) load_first(row0 + wave * RPW);
+    }
     for (int base = row0 + wave * RPW; base < row1; base += NW * RPW) {
         const int i = base + grp;
         const bool active = i < row1;
@@ -300,7 +318,12 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
 
         if (HAS_K) {
             float qv[EPC];
-            load_row_chunk<T, D>(static_cast<const T*>(p.Q) + plane + (size_t)qpix * D, vchunk, qv);
+            if constexpr (XR) {
+#pragma unroll
+                for (int y = 0; y < EPC; ++y) qv[y] = qvx[y];
+            } else {
+                load_row_chunk<T, D>(static_cast<const T*>(p.Q) + plane + (size_t)qpix * D, vchunk, qv);
+            }
             float dq[EPC];
 #pragma unroll
             for (int y = 0; y < EPC; ++y) dq[y] = 0.0f;
@@ -312,9 +335,9 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
             // loop is unrolled by 2 (measured 7-8 % faster than rolled; by 4 or fully
             // the hoisted loads spill)
             constexpr int KUN = HAS_V ? NST : 2;   // steps unrolled
-            uint4 j4n = load16(rI, roff + 16 * vsub);
-            uint4 a4n = load16(rA, roff + 16 * vsub);
-            uint4 g4n = HAS_V ? make_uint4(0u, 0u, 0u, 0u) : load16(rg, roff + 16 * vsub);
+            uint4 j4n = XR ? j4x : load16(rI, roff + 16 * vsub);
+            uint4 a4n = XR ? a4x : load16(rA, roff + 16 * vsub);
+            uint4 g4n = HAS_V ? make_uint4(0u, 0u, 0u, 0u) : XR ? g4x : load16(rg, roff + 16 * vsub);
 #pragma unroll KUN
             for (int t = 0; t < NST; ++t) {
                 const int e0 = 4 * (vsub + GS * t);
@@ -362,6 +385,9 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
 #pragma unroll
                 for (int y = 0; y < EPC; y += 4)
                     *reinterpret_cast<float4*>(qr + y) = make_float4(dq[y], dq[y + 1], dq[y + 2], dq[y + 3]);
+            }
+            if constexpr (XR) {
+                if (base + NW * RPW < row1) load_first(base + NW * RPW);
             }
             if (want_dap) {
                 // the wave's LDS writes above complete before the scan reads them
