@@ -251,6 +251,26 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
     if constexpr (XR) {
         if (row0 + wave * RPW < row1) load_first(row0 + wave * RPW);
     }
+    // K and V pass: the next row's dO chunk and first-step loads, likewise
+    constexpr bool XV = HAS_K && HAS_V && NST <= 2;   // with more steps the carried loads spill
+    float dovx[EPC];
+    uint4 j4v = make_uint4(0u, 0u, 0u, 0u), a4v = j4v, d4v = j4v;
+    auto load_first_v = [&](int b0) {
+        const int ix = b0 + grp < row1 ? b0 + grp : row0;
+        const float* dor = p.dO + plane + (size_t)slot_pixel(g, w.wy, w.wx, ix) * D + vchunk * EPC;
+#pragma unroll
+        for (int y = 0; y < EPC; y += 4) {
+            const float4 f = *reinterpret_cast<const float4*>(dor + y);
+            dovx[y] = f.x; dovx[y + 1] = f.y; dovx[y + 2] = f.z; dovx[y + 3] = f.w;
+        }
+        const int ro = ix * K_l * 4 + 16 * vsub;
+        j4v = load16(rI, ro);
+        a4v = load16(rA, ro);
+        d4v = p.dA_l ? load16(rdA, ro) : make_uint4(0u, 0u, 0u, 0u);
+    };
+    if constexpr (XV) {
+        if (row0 + wave * RPW < row1) load_first_v(row0 + wave * RPW);
+    }
     for (int base = row0 + wave * RPW; base < row1; base += NW * RPW) {
         const int i = base + grp;
         const bool active = i < row1;
@@ -261,20 +281,25 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
         float G[HAS_V ? KPL : 1];
         if (HAS_V) {
             float dov[EPC];
-            const float* dor = p.dO + plane + (size_t)qpix * D + vchunk * EPC;
+            if constexpr (XV) {
 #pragma unroll
-            for (int y = 0; y < EPC; y += 4) {
-                const float4 f = *reinterpret_cast<const float4*>(dor + y);
-                dov[y] = f.x; dov[y + 1] = f.y; dov[y + 2] = f.z; dov[y + 3] = f.w;
+                for (int y = 0; y < EPC; ++y) dov[y] = dovx[y];
+            } else {
+                const float* dor = p.dO + plane + (size_t)qpix * D + vchunk * EPC;
+#pragma unroll
+                for (int y = 0; y < EPC; y += 4) {
+                    const float4 f = *reinterpret_cast<const float4*>(dor + y);
+                    dov[y] = f.x; dov[y + 1] = f.y; dov[y + 2] = f.z; dov[y + 3] = f.w;
+                }
             }
             float dsum = 0.0f;
 #pragma unroll
             for (int t = 0; t < NST; ++t) {
                 const int e0 = 4 * (vsub + GS * t);
                 const int off = roff + e0 * 4;
-                const uint4 j4 = load16(rI, off);
-                const uint4 a4 = load16(rA, off);
-                const uint4 d4 = p.dA_l ? load16(rdA, off) : make_uint4(0u, 0u, 0u, 0u);
+                const uint4 j4 = (XV && t == 0) ? j4v : load16(rI, off);
+                const uint4 a4 = (XV && t == 0) ? a4v : load16(rA, off);
+                const uint4 d4 = (XV && t == 0) ? d4v : p.dA_l ? load16(rdA, off) : make_uint4(0u, 0u, 0u, 0u);
                 const unsigned jv[4] = {j4.x, j4.y, j4.z, j4.w};
                 const float av[4] = {__uint_as_float(a4.x), __uint_as_float(a4.y), __uint_as_float(a4.z),
                                      __uint_as_float(a4.w)};
@@ -388,6 +413,9 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
             }
             if constexpr (XR) {
                 if (base + NW * RPW < row1) load_first(base + NW * RPW);
+            }
+            if constexpr (XV) {
+                if (base + NW * RPW < row1) load_first_v(base + NW * RPW);
             }
             if (want_dap) {
                 // the wave's LDS writes above complete before the scan reads them
