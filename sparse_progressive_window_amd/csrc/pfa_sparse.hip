@@ -31,6 +31,8 @@
 // staged in LDS as (j, weight); the aggregation then gives each V row chunk to
 // a lane (CH lanes read one whole row, conflict-free) and sums the lanes of a
 // group with row rotations.
+#include <type_traits>
+
 #include "pfa_kernels.h"
 #include "pfa_rows.h"
 
@@ -1111,6 +1113,83 @@ __global__ __launch_bounds__(NW * kWave) void aggregate_rows_kernel(const Sparse
     }
 }
 
+
+// O_i = sum_j A^l_ij v_j from stored (I^l, A^l) rows, V of the window in LDS, for
+// V rows of 4 16-byte chunks (bf16 d = 32, fp32 d = 16): one quad of lanes per
+// row, one chunk each. Lane c of quad q loads step c of the quad's entries (4
+// consecutive (I, A) pairs; the wave's loads cover whole rows, coalesced), and at
+// step k the quad takes lane k's entries by a DPP broadcast, so no entry passes
+// through LDS and its bandwidth goes to the V rows alone.
+template <typename T, int D, int R, int NW>
+__global__ __launch_bounds__(NW * kWave) void aggregate_quads_kernel(const SparseArgs p) {
+    constexpr int EPC = Chunk<T>::kElems;
+    constexpr int ROWB = D * (int)sizeof(T);
+    constexpr int GL = kWave / R;   // lanes per row
+    static_assert(D / EPC == 4, "one 16-byte chunk per lane of a quad");
+    static_assert(GL >= 4, "a row needs a quad");
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const Geom g = p.g;
+    const int N = g.N;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int grp = lane / GL;
+    const int gl = lane & (GL - 1);
+    const int q = gl >> 2;
+    const int c = gl & 3;
+    const WhPart w = decode_block(p.blocks_per_wh, p.xcd_map, g);
+    const size_t plane = (size_t)w.bh * g.H * g.W * D;
+    const T* Vh = static_cast<const T*>(p.V) + plane;
+    float* Oh = p.O_out + plane;
+    stage_rows<T, D>(smem, ROWB, Vh, g, w.wy, w.wx);
+    __syncthreads();
+
+    const int K_l = p.K_l;   // a multiple of 4, at most 4 GL
+    const int row0 = w.part * p.rows_per_block;
+    const int row1 = min(N, row0 + p.rows_per_block);
+    const int32_t* Iw = p.I_out + (size_t)w.wh * N * K_l;
+    const float* Aw = p.A_out + (size_t)w.wh * N * K_l;
+    const int e0 = GL * c + 4 * q;   // this lane's entries: step c of quad q
+    for (int base = row0 + wave * R; base < row1; base += NW * R) {
+        const int i = base + grp;
+        const bool active = i < row1;
+        int4 jm = make_int4(0, 0, 0, 0);
+        float4 wm = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (active && e0 < K_l) {
+            jm = *reinterpret_cast<const int4*>(Iw + (size_t)i * K_l + e0);
+            wm = *reinterpret_cast<const float4*>(Aw + (size_t)i * K_l + e0);
+        }
+        float acc[EPC];
+#pragma unroll
+        for (int y = 0; y < EPC; ++y) acc[y] = 0.0f;
+        auto step = [&](auto kc) {
+            constexpr int BC = decltype(kc)::value * 0x55;   // quad_perm [k, k, k, k]
+            const int jk[4] = {dpp<BC>(jm.x), dpp<BC>(jm.y), dpp<BC>(jm.z), dpp<BC>(jm.w)};
+            const float wk[4] = {dppf<BC>(wm.x), dppf<BC>(wm.y), dppf<BC>(wm.z), dppf<BC>(wm.w)};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int j = min(max(jk[x], 0), N - 1);   // memory safety only
+                float vf[EPC];
+                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(smem + j * ROWB + c * 16), vf);
+#pragma unroll
+                for (int y = 0; y < EPC; ++y) acc[y] = fmaf(wk[x], vf[y], acc[y]);
+            }
+        };
+        step(std::integral_constant<int, 0>());
+        if (GL < K_l) step(std::integral_constant<int, 1>());
+        if (2 * GL < K_l) step(std::integral_constant<int, 2>());
+        if (3 * GL < K_l) step(std::integral_constant<int, 3>());
+#pragma unroll
+        for (int y = 0; y < EPC; ++y) acc[y] = reduce_chunk_lanes<4, GL>(acc[y]);   // the row's quads
+        if (active && q == 0) {
+            float* orow = Oh + (size_t)slot_pixel(g, w.wy, w.wx, i) * D + c * EPC;
+#pragma unroll
+            for (int y = 0; y < EPC; y += 4)
+                *reinterpret_cast<float4*>(orow + y) = make_float4(acc[y], acc[y + 1], acc[y + 2], acc[y + 3]);
+        }
+    }
+}
+
 template <class F>
 hipError_t launch_fn(F fn, const SparseArgs& a, int threads, int lds, int grid, hipStream_t s) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1194,6 +1273,19 @@ hipError_t launch_all_cand_dual_t(const SparseArgs& a, int grid, hipStream_t s) 
 template <typename T, int D>
 hipError_t launch_aggregate_t(const SparseArgs& a, int grid, hipStream_t s) {
     const int lds = a.g.N * D * (int)sizeof(T);
+    // 4-chunk V rows: entries broadcast within quads (4-17 % faster on the bf16 patch
+    // batch); with 8 chunks, two per lane of a quad, that was measured slower than
+    // staging the entries in LDS for 8-lane rows (0.33 against 0.30 ms at layer 2)
+    if constexpr (D / Chunk<T>::kElems == 4) {
+        if (a.K_l <= 256 && a.K_l % 4 == 0 && lds <= kLdsBytes) {
+            const int r = 256 / a.K_l;   // rows per wave: R K_l <= 256, 4 steps of 4 entries per lane
+            if (r >= 16) return launch_fn(aggregate_quads_kernel<T, D, 16, 16>, a, 16 * kWave, lds, grid, s);
+            if (r >= 8) return launch_fn(aggregate_quads_kernel<T, D, 8, 16>, a, 16 * kWave, lds, grid, s);
+            if (r >= 4) return launch_fn(aggregate_quads_kernel<T, D, 4, 16>, a, 16 * kWave, lds, grid, s);
+            if (r >= 2) return launch_fn(aggregate_quads_kernel<T, D, 2, 16>, a, 16 * kWave, lds, grid, s);
+            return launch_fn(aggregate_quads_kernel<T, D, 1, 16>, a, 16 * kWave, lds, grid, s);
+        }
+    }
     constexpr int RMAX = kWave / (D / Chunk<T>::kElems);   // rows per step with CH lanes per row
     if (a.K_l <= 256 && a.K_l % 4 == 0 && lds + 16 * 2048 <= kLdsBytes) {
         const int l2 = lds + 16 * 2048;
