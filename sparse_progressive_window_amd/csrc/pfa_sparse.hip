@@ -823,7 +823,6 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
     const int N = g.N;   // 1024
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int grp = lane >> 4;
     const WhPart w = decode_block(p.blocks_per_wh, p.xcd_map, g);
     const size_t plane = (size_t)w.bh * g.H * g.W * D;
     const T* Qh = static_cast<const T*>(p.Q) + plane;
@@ -835,7 +834,7 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
     const T* K1h = DUAL ? static_cast<const T*>(p.K1) + plane : nullptr;
 
     unsigned char* Ks = smem;
-    unsigned* hb = reinterpret_cast<unsigned*>(smem + NK * N * KSTR) + (wave * 4 + grp) * HISTG;
+    unsigned* hist0 = reinterpret_cast<unsigned*>(smem + NK * N * KSTR);
     auto stage_k = [&](unsigned char* dst, const T* src_plane, const Geom& gg) {
         if (SWZ) {
             for (int u = threadIdx.x; u < N * CH; u += blockDim.x) {
@@ -862,11 +861,16 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
     // slots 16k + b
     constexpr int AH = KPT / 2;   // loaded and consumed in two halves (register budget)
     for (int base = row0 + wave * 4; base < row1; base += NW * 4) {
-        // per-lane values are re-derived every batch from an opaque copy of the lane
-        // index: hoisted out of the loop, the KPT slot indices and the LDS addresses
-        // would not fit the register budget of 4 waves per SIMD
-        int lv = lane;
-        __asm__ volatile("" : "+v"(lv));
+        // per-lane values are re-derived every batch from the lane index, itself
+        // recomputed by v_mbcnt in an asm block the compiler cannot hoist: kept live
+        // across the loop, the lane index, its group, the histogram addresses and
+        // the KPT slot indices would not fit the register budget of 4 waves per SIMD
+        // (they were spilled and reloaded at the top of every batch, behind the
+        // previous batch's stores)
+        int lv;
+        __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lv));
+        const int gv = lv >> 4;
+        unsigned* hbv = hist0 + (wave * 4 + gv) * HISTG;
         const int glv = lv & (GL - 1);
         const int qi = min(base + (lv & 3), row1 - 1);
         // 16 accumulator chains (one per 64-candidate tile), contraction chunk outer:
@@ -920,7 +924,7 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
 #pragma unroll
         for (int k = 1; k < KPT; ++k) smax = fmaxf(smax, uv[k]);
         const float c = -Grp<GL>::all(smax, MaxF()) * scale2;
-        const float* arow = HAS_A ? p.A_prev + ((size_t)w.wh * N + min(base + grp, N - 1)) * N + glv : nullptr;
+        const float* arow = HAS_A ? p.A_prev + ((size_t)w.wh * N + min(base + gv, N - 1)) * N + glv : nullptr;
 #pragma unroll
         for (int h = 0; h < KPT; h += AH) {
             float ab[AH];
@@ -938,12 +942,12 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
 
         // rows past row1 (last batch) are selected but never stored: every group's
         // ballots and reductions are its own
-        const bool active = base + grp < row1;
+        const bool active = base + gv < row1;
         const size_t rbase = ((size_t)w.wh * N + base) * K_l;
         const int nbytes = max(0, min(4, row1 - base)) * K_l * 4;
         select_store<GL, KPT, BPL, true, true>(
-            p, lane, active, N, [&](int k) { return GL * k + glv; }, [&](int) { return true; }, uv, hb,
-            make_rsrc(p.I_out + rbase, nbytes), make_rsrc(p.A_out + rbase, nbytes), grp * K_l);
+            p, lv, active, N, [&](int k) { return GL * k + glv; }, [&](int) { return true; }, uv, hbv,
+            make_rsrc(p.I_out + rbase, nbytes), make_rsrc(p.A_out + rbase, nbytes), gv * K_l);
     }
 }
 
