@@ -537,10 +537,6 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
     unsigned* hb = reinterpret_cast<unsigned*>(sbase) + wave * HISTW + grp * HISTG;
     uint2* scr = reinterpret_cast<uint2*>(sbase + HIST_BYTES) + wave * SCW + grp * SCG;
 
-    if (K_LDS) {
-        stage_rows<T, D>(Ks, ROWB, Kh, g, w.wy, w.wx);
-        __syncthreads();
-    }
 
     int coff[CH];   // lane-rotated chunk order for whole-row gathers
 #pragma unroll
@@ -616,13 +612,17 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
             if (u < QW) qst[u] = qd[k];
         }
     };
-    if constexpr (QS) {
-        unsigned qd[NQ];
-        load_qs(row0 + wave * RPW, qd);
-        put_qs(qd);
-    }
+    // the first rows' loads go out before the window's K is staged, so their
+    // latency overlaps the staging
+    unsigned qd0[NQ];
+    if constexpr (QS) load_qs(row0 + wave * RPW, qd0);
     RowIn cur;
     load_row(cur, row0 + wave * RPW);
+    if (K_LDS) {
+        stage_rows<T, D>(Ks, ROWB, Kh, g, w.wy, w.wx);
+        __syncthreads();
+    }
+    if constexpr (QS) put_qs(qd0);
     for (int base = row0 + wave * RPW; base < row1; base += NW * RPW) {
         RowIn nxt;
         if (base + NW * RPW < row1) load_row(nxt, base + NW * RPW);
@@ -1057,9 +1057,6 @@ __global__ __launch_bounds__(NW * kWave) void aggregate_rows_kernel(const Sparse
     float* Oh = p.O_out + plane;
     int* sj = reinterpret_cast<int*>(smem + N * ROWB) + wave * 512;   // 256 V-row offsets, then 256 weights
     float* sw = reinterpret_cast<float*>(sj + 256);
-    stage_rows<T, D>(smem, ROWB, Vh, g, w.wy, w.wx);
-    __syncthreads();
-
     const int K_l = p.K_l;
     const int row0 = w.part * p.rows_per_block;
     const int row1 = min(N, row0 + p.rows_per_block);
@@ -1075,7 +1072,9 @@ __global__ __launch_bounds__(NW * kWave) void aggregate_rows_kernel(const Sparse
         }
     };
     int base = row0 + wave * R;
-    if (base < row1) load(base);
+    if (base < row1) load(base);   // before the staging: the latency overlaps it
+    stage_rows<T, D>(smem, ROWB, Vh, g, w.wy, w.wx);
+    __syncthreads();
     const unsigned char* vbase = smem + vchunk * 16;   // this lane's 16-byte chunk of every V row
     for (; base < row1; base += NW * R) {
         // stage byte offsets of the V rows (slot clamped to the window: memory safety only)
