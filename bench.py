@@ -1,15 +1,22 @@
 #!/usr/bin/env python3
 """Benchmark of the PFA layer chain on one MI355X.
 
-One step = one pass of the whole chain (dense layer 1 + sparse layers 2..6)
-over the 256x256-map workload (64 windows of 32x32, 6 heads, d = 32, fp32
-inputs, keep schedule [1024, 256, 128, 64, 32, 16], shift 16 on every second
-layer), inputs resident in HBM, outputs preallocated. Prints one JSON line.
+Headline: the 640x384 inference map (240 windows of 32x32, 6 heads, d = 32,
+bf16 inputs), a chain of 6 blocks of 6 layers each (keep schedule [1024, 256,
+128, 64, 32, 16] per block, shift 16 on every second layer, fresh Q/K/V per
+layer and block). One step = all 36 layer calls; inputs resident in HBM, outputs
+preallocated. The first two layers of each block run fused (layer 1 writes O,
+layer 2 ranks by exp(s1 + s2); the first layer's map is never materialised),
+which is the library's path for bf16 chains; `--unfused` writes A^1 instead.
+Prints one JSON line.
 
 Metric: candidate pairs per second (pairs (i, j in I^{l-1}(i)) evaluated, summed
-over the chain's layers, divided by the step time); per-layer figures and the
-roofline of the dominant kernel are attached. The CPU baseline times the fp64
-oracle on a bounded sample of window-heads of the same workload.
+over every layer of the step, divided by the step time). Attached: per-layer
+times against the layer's algorithmic bytes (inputs read once, outputs written
+once) or flops, per-kernel figures, the roofline of the longest kernel, the
+same chain unfused, the 256x256 fp32 map and the 32-image bf16 patch batch as
+extra workloads, the backward pass, the global individualized attention, and
+the fp64 CPU oracle timed on a bounded sample of the headline workload.
 """
 
 import argparse
@@ -27,17 +34,20 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 COUNTERS_FILE = "hbm_counters_{workload}.md"
+HEADLINE = "map640x384_h6_d32_bf16_6blocks"
 
 # kernel kinds of the library's timing calls (pfa_kernel_kind)
 DENSE, ALL_CAND, SPARSE, SELECT, AGGREGATE, IOTA, BWD_ROWS, BWD_SCATTER, IET_RANK, IET_UNION, DENSE_BWD = range(11)
 
 
 def kernel_bytes(w, l, kind, i_prev_implicit, split, fused=False):
-    """Algorithmic HBM bytes of one launch of kernel `kind` in layer l (0-based),
-    per window-head: every input read once, every output written once. `split`:
-    the layer ran a separate aggregation kernel, so this one does not touch V or O.
-    `fused`: layers 1-2 ran fused (no A^1: the dense layer writes O only, the
-    second layer reads the first layer's Q and K instead of A^1)."""
+    """HBM bytes of one launch of kernel `kind` in layer l (0-based) per
+    window-head: the kernel's own inputs read once and outputs written once.
+    `split`: the layer ran a separate aggregation kernel, so this one does not
+    touch V or O (the aggregation kernel's own inputs then include the I^l/A^l
+    rows the selection kernel wrote). `fused`: layers 1-2 ran fused (no A^1: the
+    dense layer writes O only, the second layer reads the first layer's Q and K
+    instead of A^1)."""
     N, d = w.N, w.d
     b_in = 4 if w.dtype == "f32" else 2
     x = N * d * b_in                      # one of Q, K, V
@@ -59,8 +69,9 @@ def kernel_bytes(w, l, kind, i_prev_implicit, split, fused=False):
     return sel + x + O
 
 
-def kernel_flops(w, l, kind, split):
-    """Algorithmic flops per window-head: 2d per scored pair, 2d per aggregated pair."""
+def kernel_flops(w, l, kind, split, fused=False):
+    """Algorithmic flops per window-head: 2d per scored pair (two products of d
+    for the fused second layer, q1.k1 + q2.k2), 2d per aggregated pair."""
     N, d = w.N, w.d
     if kind == DENSE:
         return 4 * d * N * N
@@ -69,9 +80,29 @@ def kernel_flops(w, l, kind, split):
     K_prev, K_l = w.K[l - 1], w.K[l]
     if kind == AGGREGATE:
         return 2 * d * N * K_l
+    score = (4 if (fused and l == 1 and kind == ALL_CAND) else 2) * d * N * K_prev
     if split:
-        return 2 * d * N * K_prev
-    return 2 * d * N * K_prev + 2 * d * N * K_l
+        return score
+    return score + 2 * d * N * K_l
+
+
+def layer_bytes(w, l, i_prev_implicit, fused=False):
+    """Algorithmic bytes of layer l (0-based) per window-head, whatever kernels
+    run it: Q, K, V and the previous map read once, I^l, A^l and O written once.
+    Dense layer: A^1 written unless fused (then O only). Fused second layer: the
+    first layer's Q and K replace the A^1 read."""
+    N, d = w.N, w.d
+    x = N * d * (4 if w.dtype == "f32" else 2)
+    O = N * d * 4
+    if l == 0:
+        return 3 * x + O + (0 if fused else N * N * 4)
+    K_prev, K_l = w.K[l - 1], w.K[l]
+    prev = 2 * x if (fused and l == 1) else (0 if i_prev_implicit else N * K_prev * 4) + N * K_prev * 4
+    return 3 * x + prev + N * K_l * 8 + O
+
+
+def mfma_peak(w):
+    return FP32_MFMA_PEAK_TFLOPS if w.dtype == "f32" else BF16_MFMA_PEAK_TFLOPS
 
 
 def bwd_kernel_bytes(w, l, part, i_prev_implicit):
@@ -116,20 +147,188 @@ def stored_traffic(workload, kernel, layer):
     return None
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Chain:
+    """Device inputs and outputs of one chain workload: Q/K/V per (block, layer),
+    output buffers per layer shared by the blocks (each block's chain is
+    independent of the others and overwrites them)."""
+
+    def __init__(self, w, torch, pfa, inputs, dev, fused, rpb=False, keep_host_block=None, share=None):
+        self.w, self.torch, self.pfa, self.fused = w, torch, pfa, fused
+        L, N = w.layers, w.N
+        self.host = None
+
+        def to_dev(t):
+            if t.dtype == "f32":
+                return torch.from_numpy(t.device).to(dev)
+            return torch.from_numpy(t.device.view(np.int16)).to(dev).view(torch.bfloat16)
+
+        self.qkv = [] if share is None else share.qkv   # share: another chain's inputs of the same workload
+        for b in range(w.blocks if share is None else 0):
+            layers = []
+            hl = []
+            for l in range(L):
+                ts = inputs.qkv(w, b, l)
+                layers.append(tuple(to_dev(t) for t in ts))
+                if keep_host_block == b:
+                    hl.append(ts)
+            self.qkv.append(layers)
+            if keep_host_block == b:
+                self.host = hl
+        lead = (w.B, w.heads, w.n_windows)
+        self.outs = []
+        for l in range(L):
+            K_l = w.K[l]
+            I = None if l == 0 else torch.empty(lead + (N, K_l), dtype=torch.int32, device=dev)
+            A = None if (fused and l == 0) else torch.empty(lead + (N, K_l), dtype=torch.float32, device=dev)
+            O = torch.empty((w.B, w.heads, w.H, w.W, w.d), dtype=torch.float32, device=dev)
+            self.outs.append((I, A, O))
+        self.implicit = [l == 1 and w.K[0] == N for l in range(L)]
+        self.bias = [None] * L
+        if rpb:
+            gb = torch.Generator().manual_seed(777)
+            self.bias = [torch.randn((w.heads, (2 * w.win - 1) ** 2), generator=gb).to(dev) for _ in range(L)]
+
+    def block(self, b, marks=None):
+        w, pfa, outs = self.w, self.pfa, self.outs
+        for l in range(w.layers):
+            Q, K, V = self.qkv[b][l]
+            if self.fused and l == 0:
+                pfa.first_two_layers(Q, K, V, *self.qkv[b][1], w.K[1], win=w.win, shift1=w.shifts[0],
+                                     shift2=w.shifts[1], out=(outs[0][2],) + outs[1])
+            elif self.fused and l == 1:
+                pass   # done with layer 1
+            elif l == 0:
+                pfa.dense_layer(Q, K, V, w.K[0], win=w.win, shift=w.shifts[0], out=outs[0], bias=self.bias[0])
+            else:
+                I_prev = None if self.implicit[l] else outs[l - 1][0]
+                pfa.sparse_layer(Q, K, V, I_prev, outs[l - 1][1], w.K[l], win=w.win, shift=w.shifts[l],
+                                 out=outs[l], bias=self.bias[l])
+            if marks is not None:
+                marks.append(pfa.timing_count())
+
+    def step(self, marks=None):
+        for b in range(self.w.blocks):
+            self.block(b, marks)
+
+
+def run_chain(chain, steps, warmup, torch, pfa):
+    """Time `steps` chain steps after `warmup`; per-kernel durations from the
+    library's HIP events. Returns the result dict (no CPU baseline)."""
+    w, fused = chain.w, chain.fused
+    L, N = w.layers, w.N
+    for _ in range(warmup):
+        chain.step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps; every kernel is bracketed by HIP events on its launch
+    # stream (the library's timing calls), read back after the final synchronize.
+    pfa.timing_enable(steps * w.blocks * L * 2 + 64)
+    marks = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        chain.step(marks)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    recs, dropped = pfa.timing_read(len(marks) * 4 + 64)
+    pfa.timing_enable(0)
+    assert dropped == 0 and len(recs) == marks[-1], (dropped, len(recs), marks[-1])
+
+    # per (layer, kernel kind): launch durations
+    per = {}
+    start = 0
+    for i, end in enumerate(marks):
+        l = i % L
+        for kind, ms in recs[start:end]:
+            ll = 1 if (fused and l == 0 and kind != DENSE) else l   # fused call: dense = layer 1, rest = layer 2
+            per.setdefault((ll, kind), []).append(ms)
+        start = end
+    layer_ms = [sum(float(np.mean(v)) for (ll, _), v in per.items() if ll == l) for l in range(L)]
+
+    peak_mfma = mfma_peak(w)
+    layers, kernels = [], []
+    total_pairs = 0
+    for l in range(L):
+        pairs = w.pairs(l) * w.blocks
+        total_pairs += pairs
+        by = layer_bytes(w, l, chain.implicit[l], fused) * w.n_wh
+        gbs = by / (layer_ms[l] * 1e-3) / 1e9
+        ent = {"layer": l + 1, "K_prev": N if l == 0 else w.K[l - 1], "K_l": w.K[l],
+               "ms_per_block": round(layer_ms[l], 4), "pairs_per_s": w.pairs(l) / (layer_ms[l] * 1e-3),
+               "alg_bytes_per_block": by, "GB_per_s": round(gbs, 1)}
+        if l == 0 and fused:
+            # O-only dense layer: 4 N^2 d flops per window-head against the MFMA peak
+            fl = 4 * w.d * N * N * w.n_wh
+            tfs = fl / (layer_ms[l] * 1e-3) / 1e12
+            ent.update({"bound": "mfma", "alg_flops_per_block": fl, "TFLOP_per_s": round(tfs, 2),
+                        "frac": round(tfs / peak_mfma, 4), "peak": peak_mfma})
+        else:
+            ent.update({"bound": "hbm", "frac": round(gbs / HBM_PEAK_GBS, 4), "peak": HBM_PEAK_GBS})
+        layers.append(ent)
+    for (l, kind), v in sorted(per.items()):
+        ms = float(np.mean(v))
+        split = (l, AGGREGATE) in per
+        by = kernel_bytes(w, l, kind, chain.implicit[l], split, fused) * w.n_wh
+        fl = kernel_flops(w, l, kind, split, fused) * w.n_wh
+        gbs = by / (ms * 1e-3) / 1e9
+        tfs = fl / (ms * 1e-3) / 1e12
+        mfma = kind in (DENSE, ALL_CAND)
+        # the bound is whichever roofline time is longer for the algorithmic work
+        t_hbm = by / (HBM_PEAK_GBS * 1e9)
+        t_mfma = fl / (peak_mfma * 1e12) if mfma else 0.0
+        bound = "mfma" if t_mfma > t_hbm else "hbm"
+        k = {"layer": l + 1, "kernel": pfa.kernel_name(kind), "launches": len(v), "ms": round(ms, 4),
+             "io_bytes": by, "GB_per_s": round(gbs, 1), "alg_flops": fl, "TFLOP_per_s": round(tfs, 2),
+             "bound": bound, "frac": round(tfs / peak_mfma if bound == "mfma" else gbs / HBM_PEAK_GBS, 4)}
+        if kind == DENSE and w.dtype == "f32":
+            # fp32 inputs run the scores as a three-way bf16 split on bf16 MFMA: also
+            # state the fraction of the bf16 peak, the dense-layer target's unit
+            k["frac_of_bf16_mfma_peak"] = round(tfs / BF16_MFMA_PEAK_TFLOPS, 4)
+        kernels.append(k)
+
+    dom = max(kernels, key=lambda k: k["ms"])
+    if dom["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": dom["TFLOP_per_s"], "peak": peak_mfma, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": dom["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = dom["frac"]
+    roof["traffic"] = stored_traffic(w.name + ("_fused12" if fused else ""), dom["kernel"], dom["layer"])
+    roof.update({"kernel": dom["kernel"], "layer": dom["layer"], "ms_per_launch": dom["ms"],
+                 "alg_bytes_per_launch": dom["io_bytes"], "alg_flops_per_launch": dom["alg_flops"]})
+    chain_bytes = sum(x["alg_bytes_per_block"] for x in layers) * w.blocks
+    return {
+        "value": total_pairs / (ms_per_step * 1e-3), "ms_per_step": round(ms_per_step, 4),
+        "config": {"workload": w.name, "fused_layers_1_2": fused,
+                   "relative_position_bias": chain.bias[0] is not None, "B": w.B, "heads": w.heads, "H": w.H,
+                   "W": w.W, "d": w.d, "win": w.win, "blocks": w.blocks, "K": w.K, "shifts": w.shifts,
+                   "window_heads_per_layer": w.n_wh, "pairs_per_step": total_pairs},
+        "chain_alg_bytes_per_step": chain_bytes,
+        "chain_GB_per_s": round(chain_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "roofline": roof, "layers": layers, "kernels": kernels,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="map256x256_h6_d32_f32")
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--unfused", action="store_true",
+                    help="headline chain with A^1 written and read back (the fused first two layers need bf16, "
+                         "or fp32 with d = 16)")
+    ap.add_argument("--rpb", action="store_true",
+                    help="add a seeded relative position bias table per layer to the scores (unfused only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=384, help="window-heads timed on the CPU oracle")
-    ap.add_argument("--fused12", action="store_true",
-                    help="run layers 1-2 fused without materialising A^1 (bf16, or fp32 with d = 16)")
-    ap.add_argument("--rpb", action="store_true",
-                    help="add a seeded relative position bias table per layer to the scores (not with --fused12)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the extra workloads (unfused headline, 256x256 fp32 map, bf16 patch batch)")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip the backward leg (layers L..2 of the sparse-layer backward, timed separately)")
+                    help="skip the backward leg (layers L..1 of the chain's backward, timed separately)")
     ap.add_argument("--no-global", action="store_true",
                     help="skip the global-mode leg (individualized attention + index propagation, 64x64 map)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -157,151 +356,81 @@ def main():
     pfa.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    fusable = w.N == 1024 and (w.dtype == "bf16" or w.d == 16)
+    fused = fusable and not args.unfused and not args.rpb
 
-    def to_dev(t):
-        if t.dtype == "f32":
-            return torch.from_numpy(t.device).to(dev)
-        return torch.from_numpy(t.device.view(np.int16)).to(dev).view(torch.bfloat16)
-
-    L = w.layers
-    host = [inputs.qkv(w, 0, l) for l in range(L)]
-    qkv = [tuple(to_dev(t) for t in layer) for layer in host]
-    lead = (w.B, w.heads, w.n_windows)
-    N = w.N
-    outs = []
-    fused = args.fused12
-    for l in range(L):
-        K_l = w.K[l]
-        I = None if l == 0 else torch.empty(lead + (N, K_l), dtype=torch.int32, device=dev)
-        A = None if (fused and l == 0) else torch.empty(lead + (N, K_l), dtype=torch.float32, device=dev)
-        O = torch.empty((w.B, w.heads, w.H, w.W, w.d), dtype=torch.float32, device=dev)
-        outs.append((I, A, O))
-    implicit = [l == 1 and w.K[0] == N for l in range(L)]
-    bias = [None] * L
-    if args.rpb:
-        if fused:
-            print("--rpb does not combine with --fused12", file=sys.stderr)
-            sys.exit(2)
-        gb = torch.Generator().manual_seed(777)
-        bias = [torch.randn((w.heads, (2 * w.win - 1) ** 2), generator=gb).to(dev) for _ in range(L)]
-
-    def step(marks=None):
-        for l in range(L):
-            Q, K, V = qkv[l]
-            if fused and l == 0:
-                pfa.first_two_layers(Q, K, V, *qkv[1], w.K[1], win=w.win, shift1=w.shifts[0], shift2=w.shifts[1],
-                                     out=(outs[0][2],) + outs[1])
-            elif fused and l == 1:
-                pass   # done with layer 1
-            elif l == 0:
-                pfa.dense_layer(Q, K, V, w.K[0], win=w.win, shift=w.shifts[0], out=outs[0], bias=bias[0])
-            else:
-                I_prev = None if implicit[l] else outs[l - 1][0]
-                pfa.sparse_layer(Q, K, V, I_prev, outs[l - 1][1], w.K[l], win=w.win, shift=w.shifts[l],
-                                 out=outs[l], bias=bias[l])
-            if marks is not None:
-                marks.append(pfa.timing_count())
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # Timed region: K steps; every kernel is bracketed by HIP events on its launch
-    # stream (the library's timing calls), read back after the final synchronize.
-    pfa.timing_enable(args.steps * L * 2 + 64)
-    marks = []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(marks)
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    recs, dropped = pfa.timing_read(len(marks) * 4 + 64)
-    pfa.timing_enable(0)
-    assert dropped == 0 and len(recs) == marks[-1], (dropped, len(recs), marks[-1])
-
-    # per (layer, kernel kind): launch durations
-    per = {}
-    start = 0
-    for i, end in enumerate(marks):
-        l = i % L
-        for kind, ms in recs[start:end]:
-            ll = 1 if (fused and l == 0 and kind != DENSE) else l   # fused call: dense = layer 1, rest = layer 2
-            per.setdefault((ll, kind), []).append(ms)
-        start = end
-    layer_ms = [sum(float(np.mean(v)) for (ll, _), v in per.items() if ll == l) for l in range(L)]
-
-    layers, kernels = [], []
-    total_pairs = 0
-    for l in range(L):
-        pairs = w.pairs(l)
-        total_pairs += pairs
-        layers.append({"layer": l + 1, "K_prev": N if l == 0 else w.K[l - 1], "K_l": w.K[l],
-                       "ms": round(layer_ms[l], 4), "pairs_per_s": pairs / (layer_ms[l] * 1e-3)})
-    peak_mfma = FP32_MFMA_PEAK_TFLOPS if w.dtype == "f32" else BF16_MFMA_PEAK_TFLOPS
-    for (l, kind), v in sorted(per.items()):
-        ms = float(np.mean(v))
-        split = (l, AGGREGATE) in per
-        by = kernel_bytes(w, l, kind, implicit[l], split, fused) * w.n_wh
-        fl = kernel_flops(w, l, kind, split) * w.n_wh
-        gbs = by / (ms * 1e-3) / 1e9
-        tfs = fl / (ms * 1e-3) / 1e12
-        mfma = kind in (DENSE, ALL_CAND)
-        # the bound is whichever roofline time is longer for the algorithmic work
-        t_hbm = by / (HBM_PEAK_GBS * 1e9)
-        t_mfma = fl / (peak_mfma * 1e12) if mfma else 0.0
-        bound = "mfma" if t_mfma > t_hbm else "hbm"
-        kernels.append({"layer": l + 1, "kernel": pfa.kernel_name(kind), "launches": len(v), "ms": round(ms, 4),
-                        "alg_bytes": by, "GB_per_s": round(gbs, 1), "alg_flops": fl, "TFLOP_per_s": round(tfs, 2),
-                        "bound": bound,
-                        "frac": round(tfs / peak_mfma if bound == "mfma" else gbs / HBM_PEAK_GBS, 4)})
-
-    dom = max(kernels, key=lambda k: k["ms"])
-    if dom["bound"] == "mfma":
-        roof = {"bound": "mfma", "achieved": dom["TFLOP_per_s"], "peak": peak_mfma, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": dom["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    roof["frac"] = dom["frac"]
-    roof["traffic"] = stored_traffic(w.name, dom["kernel"], dom["layer"])
-    roof.update({"kernel": dom["kernel"], "layer": dom["layer"], "ms_per_launch": dom["ms"],
-                 "alg_bytes_per_launch": dom["alg_bytes"], "alg_flops_per_launch": dom["alg_flops"]})
-
-    value = total_pairs / (ms_per_step * 1e-3)
+    log(f"generating {w.name} ({w.blocks} blocks x {w.layers} layers)")
+    chain = Chain(w, torch, pfa, inputs, dev, fused, rpb=args.rpb, keep_host_block=0)
+    log(f"timing {w.name} fused={fused}: {args.warmup} warmup + {args.steps} steps")
+    res = run_chain(chain, args.steps, args.warmup, torch, pfa)
     result = {
-        "metric": "PFA candidate-pairs/sec per layer (32\u00d732 win, d=32); % HBM/MFMA roofline",
-        "value": value, "unit": "candidate pairs/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "fused_layers_1_2": fused, "relative_position_bias": bool(args.rpb), "B": w.B, "heads": w.heads, "H": w.H, "W": w.W,
-                   "d": w.d, "win": w.win,
-                   "K": w.K, "shifts": w.shifts, "window_heads": w.n_wh, "pairs_per_step": total_pairs},
-        "roofline": roof, "layers": layers, "kernels": kernels,
+        "metric": "PFA candidate-pairs/sec per layer (32×32 win, d=32); % HBM/MFMA roofline",
+        "value": res.pop("value"), "unit": "candidate pairs/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
     }
+    result.update(res)
+    log(f"{w.name}: {result['ms_per_step']} ms/step, {result['value']:.3e} pairs/s")
 
-    if not args.no_backward and not fused:
+    extras = {}
+    if not args.no_extras:
+        if fused:
+            log(f"timing {w.name} unfused")
+            cu = Chain(w, torch, pfa, inputs, dev, False, share=chain)
+            extras["unfused"] = run_chain(cu, args.steps, args.warmup, torch, pfa)
+            log(f"unfused: {extras['unfused']['ms_per_step']} ms/step")
+            if not args.no_backward:
+                try:
+                    extras["unfused"]["backward"] = backward_leg(cu, args, torch, pfa)
+                except Exception as e:   # the forward line stands on its own
+                    extras["unfused"]["backward"] = {"error": repr(e)}
+            del cu
+            torch.cuda.empty_cache()
+        for name in ("map256x256_h6_d32_f32", "patch64x64_b32_h6_d32_bf16"):
+            if name == w.name:
+                continue
+            wx = workloads.BY_NAME[name]
+            fx = wx.N == 1024 and (wx.dtype == "bf16" or wx.d == 16)
+            log(f"timing {name} fused={fx}")
+            cx = Chain(wx, torch, pfa, inputs, dev, fx)
+            extras[name] = run_chain(cx, args.steps, args.warmup, torch, pfa)
+            if not fx and not args.no_backward:
+                try:
+                    extras[name]["backward"] = backward_leg(cx, args, torch, pfa)
+                except Exception as e:
+                    extras[name]["backward"] = {"error": repr(e)}
+            log(f"{name}: {extras[name]['ms_per_step']} ms/step")
+            del cx
+            torch.cuda.empty_cache()
+    elif not fused and not args.no_backward:
         try:
-            result["backward"] = backward_leg(w, qkv, outs, implicit, args, torch, pfa)
-            if not args.no_cpu_baseline:
-                result["backward"]["cpu_baseline"] = cpu_baseline_backward(w, host, outs, implicit)
-        except Exception as e:   # the forward line stands on its own
+            result["backward"] = backward_leg(chain, args, torch, pfa)
+        except Exception as e:
             result["backward"] = {"error": repr(e)}
+    if extras:
+        result["extra_workloads"] = extras
     if not args.no_global:
         try:
+            log("timing the global individualized attention")
             result["global"] = global_leg(args, torch, pfa)
             if not args.no_cpu_baseline:
                 result["global"]["cpu_baseline"] = cpu_baseline_global()
         except Exception as e:   # the forward line stands on its own
             result["global"] = {"error": repr(e)}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_sample)
+        log("timing the fp64 CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(w, chain.host, args.cpu_sample)
     print(json.dumps(result), flush=True)
 
 
-def backward_leg(w, qkv, outs, implicit, args, torch, pfa):
-    """Backward of the whole chain just run: the sparse layers L..2 (kept sets
-    from its forward outputs), each taking the next one's dA^{l} output and a
-    seeded dO, then the dense first layer with the second layer's dA^1; timed
-    like the forward step, per kernel with HIP events."""
+def backward_leg(chain, args, torch, pfa):
+    """Backward of the last block of the chain just run (its outputs are the ones
+    left in the buffers): the sparse layers L..2 (kept sets from the forward
+    outputs), each taking the next one's dA^{l} output and a seeded dO, then the
+    dense first layer with the second layer's dA^1; timed like the forward step,
+    per kernel with HIP events."""
+    w, outs, implicit = chain.w, chain.outs, chain.implicit
+    qkv = chain.qkv[w.blocks - 1]
     dev = qkv[0][0].device
     L, N = w.layers, w.N
     lead = (w.B, w.heads, w.n_windows)
@@ -378,18 +507,19 @@ def backward_leg(w, qkv, outs, implicit, args, torch, pfa):
             gbs = by / (ms * 1e-3) / 1e9
             mfma = fl / (FP32_MFMA_PEAK_TFLOPS * 1e12) > by / (HBM_PEAK_GBS * 1e9)
             kernels.append({"layer": 1, "kernel": "dense_bwd(dq+dkv)", "launches": len(v), "ms": round(ms, 4),
-                            "alg_bytes": by, "GB_per_s": round(gbs, 1), "alg_flops": fl,
+                            "io_bytes": by, "GB_per_s": round(gbs, 1), "alg_flops": fl,
                             "TFLOP_per_s": round(tfs, 2), "bound": "mfma" if mfma else "hbm",
                             "frac": round(tfs / FP32_MFMA_PEAK_TFLOPS if mfma else gbs / HBM_PEAK_GBS, 4)})
             continue
         by = bwd_kernel_bytes(w, l, part, implicit[l]) * w.n_wh
         gbs = by / (ms * 1e-3) / 1e9
-        name = "bwd_dkv_kernel" if part == "scatter" else f"bwd_rows_kernel({part})"
-        k = {"layer": l + 1, "kernel": name, "launches": len(v), "ms": round(ms, 4), "alg_bytes": by,
+        name = "bwd_dkv" if part == "scatter" else f"bwd_rows_kernel({part})"
+        k = {"layer": l + 1, "kernel": name, "launches": len(v), "ms": round(ms, 4), "io_bytes": by,
              "GB_per_s": round(gbs, 1), "bound": "hbm", "frac": round(gbs / HBM_PEAK_GBS, 4)}
-        if part == "scatter" and w.N % 16 == 0:
-            # dV = A^T dO and dK = (A g)^T Q as dense fp32 MFMA products: 4 N^2 d flops per window-head
-            fl = 4 * w.N * w.N * w.d * w.n_wh
+        if part == "scatter":
+            # the method's own work: dV = A^T dO and dK = (A g)^T Q over the kept pairs,
+            # 4 d flops per kept pair; the bound is whichever roofline time is longer
+            fl = 4 * w.d * N * w.K[l] * w.n_wh
             tfs = fl / (ms * 1e-3) / 1e12
             k.update({"alg_flops": fl, "TFLOP_per_s": round(tfs, 2)})
             if fl / (FP32_MFMA_PEAK_TFLOPS * 1e12) > by / (HBM_PEAK_GBS * 1e9):
@@ -404,8 +534,9 @@ def backward_leg(w, qkv, outs, implicit, args, torch, pfa):
     else:
         roof = {"bound": "hbm", "achieved": dom["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof.update({"frac": dom["frac"], "traffic": None, "kernel": dom["kernel"], "layer": dom["layer"],
-                 "ms_per_launch": dom["ms"], "alg_bytes_per_launch": dom["alg_bytes"]})
-    return {"ms_per_step": round(ms_per_step, 4), "layers": f"{L}..1" if dense_bwd else f"{L}..2", "layer_ms": layer_ms,
+                 "ms_per_launch": dom["ms"], "alg_bytes_per_launch": dom["io_bytes"]})
+    return {"ms_per_step": round(ms_per_step, 4), "block": w.blocks - 1,
+            "layers": f"{L}..1" if dense_bwd else f"{L}..2", "layer_ms": layer_ms,
             "kept_pairs_per_s": kept / (ms_per_step * 1e-3), "roofline": roof, "kernels": kernels}
 
 
@@ -471,31 +602,6 @@ def global_leg(args, torch, pfa):
             "note": "working set fits the MALL: latency-bound, HBM fraction not meaningful"}
 
 
-def cpu_baseline_backward(w, host, outs, implicit, sample=384):
-    """fp64 backward oracle on `sample` window-heads of each sparse layer, with
-    the GPU forward's kept sets (the backward holds them fixed): kept pairs/s."""
-    import oracle
-    sel = np.linspace(0, w.n_wh - 1, sample).astype(np.int64)
-    N = w.N
-    g = np.random.Generator(np.random.PCG64(4243))
-    t_total, kept = 0.0, 0
-    for l in range(1, w.layers):
-        Q, K, V = (t.exact for t in host[l])
-        keep = outs[l][0].view(-1, N, w.K[l])[sel].cpu().numpy()
-        Ip = None if implicit[l] else outs[l - 1][0].view(-1, N, w.K[l - 1])[sel].cpu().numpy()
-        Ap = outs[l - 1][1].view(-1, N, w.K[l - 1])[sel].cpu().numpy()
-        dO = g.standard_normal(Q.shape)
-        dA = g.standard_normal(keep.shape) if l < w.layers - 1 else None
-        t0 = time.perf_counter()
-        oracle.layer_backward(Q, K, V, win=w.win, shift=w.shifts[l], keep=keep, dO=dO, dA=dA, I_prev=Ip, A_prev=Ap,
-                              prev_compact=True, wh_list=sel)
-        t_total += time.perf_counter() - t0
-        kept += len(sel) * N * w.K[l]
-    return {"value": kept / t_total, "unit": "kept pairs/s (backward, layers 6..2)", "cores": oracle.threads(),
-            "kind": "oracle", "sample": f"{len(sel)} of {w.n_wh} window-heads per layer ({kept} kept pairs, "
-                                        f"{t_total:.1f} s of oracle time)"}
-
-
 def cpu_baseline_global():
     """fp64 oracle of the global individualized attention (6 heads) and the
     index propagation of the first IET block, on the whole 64x64 workload."""
@@ -522,15 +628,32 @@ def cpu_baseline_global():
                       f"single-threaded Python oracle) {t_prop:.2f} s"}
 
 
-def cpu_baseline(w, host, sample, min_seconds=10.0, max_passes=6):
-    """fp64 oracle on `sample` window-heads through the whole chain (same inputs),
-    repeated until at least `min_seconds` of oracle time (at most `max_passes`)."""
-    import oracle
-    sel = np.linspace(0, w.n_wh - 1, min(sample, w.n_wh)).astype(np.int64)
-    q64 = [tuple(t.exact.astype(np.float64) for t in layer) for layer in host]
-    t_total = 0.0
-    pairs = 0
-    passes = 0
+def host_cpu():
+    """Model name, physical cores and the logical CPUs this process may use."""
+    model, phys = "unknown", set()
+    try:
+        cur = {}
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if ":" not in line:
+                    if "core id" in cur:
+                        phys.add((cur.get("physical id", "0"), cur["core id"]))
+                    cur = {}
+                    continue
+                k, v = (x.strip() for x in line.split(":", 1))
+                cur[k] = v
+                if k == "model name":
+                    model = v
+        if "core id" in cur:
+            phys.add((cur.get("physical id", "0"), cur["core id"]))
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"model": model, "physical_cores": len(phys) or None, "usable_logical_cpus": usable}
+
+
+def _oracle_chain_time(w, q64, sel, min_seconds, max_passes, oracle):
+    t_total, pairs, passes = 0.0, 0, 0
     while passes < max_passes and (passes == 0 or t_total < min_seconds):
         I_prev = A_prev = None
         for l in range(w.layers):
@@ -543,9 +666,36 @@ def cpu_baseline(w, host, sample, min_seconds=10.0, max_passes=6):
             I_prev, A_prev = r["I"], r["A"]
             del r
         passes += 1
-    return {"value": pairs / t_total, "unit": "candidate pairs/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"{len(sel)} of {w.n_wh} window-heads through all {w.layers} layers, {passes} pass{'es' if passes > 1 else ''} "
-                      f"({pairs} pairs, {t_total:.1f} s of oracle time)"}
+    return t_total, pairs, passes
+
+
+def cpu_baseline(w, host, sample, min_seconds=10.0, max_passes=6):
+    """fp64 oracle on `sample` window-heads of the first block through all its
+    layers (same inputs), repeated until at least `min_seconds` of oracle time
+    (at most `max_passes`), on every OpenMP thread; then a smaller sample on one
+    thread."""
+    import oracle
+    q64 = [tuple(t.exact.astype(np.float64) for t in layer) for layer in host]
+    threads = oracle.threads()
+    sel = np.linspace(0, w.n_wh - 1, min(sample, w.n_wh)).astype(np.int64)
+    t_total, pairs, passes = _oracle_chain_time(w, q64, sel, min_seconds, max_passes, oracle)
+    # one thread: a sample sized for a few seconds at the measured per-thread rate
+    per_wh = pairs / passes / len(sel)
+    rate1_guess = pairs / t_total / max(threads, 1)
+    n1 = int(max(4, min(len(sel), 5.0 * rate1_guess / per_wh)))
+    sel1 = np.linspace(0, w.n_wh - 1, n1).astype(np.int64)
+    oracle.set_threads(1)
+    try:
+        t1, pairs1, passes1 = _oracle_chain_time(w, q64, sel1, 3.0, 1, oracle)
+    finally:
+        oracle.set_threads(threads)
+    return {"value": pairs / t_total, "unit": "candidate pairs/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(sel)} of {w.n_wh} window-heads of block 0 through all {w.layers} layers, {passes} "
+                      f"pass{'es' if passes > 1 else ''} ({pairs} pairs, {t_total:.1f} s of oracle time)",
+            "one_thread": {"value": pairs1 / t1, "cores": 1,
+                           "sample": f"{n1} window-heads of block 0, all {w.layers} layers ({pairs1} pairs, "
+                                     f"{t1:.1f} s)"},
+            "host": host_cpu()}
 
 
 if __name__ == "__main__":

@@ -55,6 +55,16 @@ def threads() -> int:
     return _load().oracle_threads()
 
 
+def set_threads(n: int) -> None:
+    """OpenMP threads of later oracle calls (omp_set_num_threads of the runtime the
+    library links; plumbing for timing the oracle on a given core count)."""
+    lib = _load()
+    fn = lib.omp_set_num_threads
+    fn.argtypes = [ctypes.c_int]
+    fn.restype = None
+    fn(int(n))
+
+
 def _ptr(a):
     return None if a is None else a.ctypes.data
 

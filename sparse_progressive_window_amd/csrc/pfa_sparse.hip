@@ -1008,6 +1008,7 @@ __global__ __launch_bounds__(NW * kWave) void aggregate_kernel(const SparseArgs 
             }
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
+                if (e0 + x >= cnt) break;   // padding past K_l: no term (0 * a non-finite V would be NaN)
                 const int j = min(max(jv[x], 0), N - 1);
                 float vf[EPC];
                 Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(smem + j * ROWB + vchunk * 16), vf);
@@ -1166,9 +1167,13 @@ __global__ __launch_bounds__(NW * kWave) void aggregate_quads_kernel(const Spars
 #pragma unroll
         for (int y = 0; y < EPC; ++y) acc[y] = 0.0f;
         auto step = [&](auto kc) {
-            constexpr int BC = decltype(kc)::value * 0x55;   // quad_perm [k, k, k, k]
+            constexpr int KC = decltype(kc)::value;
+            constexpr int BC = KC * 0x55;   // quad_perm [k, k, k, k]
             const int jk[4] = {dpp<BC>(jm.x), dpp<BC>(jm.y), dpp<BC>(jm.z), dpp<BC>(jm.w)};
             const float wk[4] = {dppf<BC>(wm.x), dppf<BC>(wm.y), dppf<BC>(wm.z), dppf<BC>(wm.w)};
+            // quads whose step-k entries lie past K_l (K_l not a multiple of 4 GL) add
+            // nothing: 0 * a non-finite V row would turn O into NaN
+            if (GL * KC + 4 * q >= K_l) return;
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int j = min(max(jk[x], 0), N - 1);   // memory safety only

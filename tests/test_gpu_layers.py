@@ -373,3 +373,48 @@ def test_first_two_layers_rejects_fp32_d32():
     with pytest.raises(pfa.PfaError) as e:
         pfa.first_two_layers(Q, Q, Q, Q, Q, Q, 256, win=32)
     assert e.value.code == -2
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,K_prev,K_l", [("bf16", 64, 20), ("bf16", 128, 40), ("bf16", 256, 100),
+                                              ("f32", 128, 12), ("f32", 100, 7)])
+def test_nonfinite_V_row_reaches_only_rows_that_keep_it(dtype, K_prev, K_l):
+    # V of slot 0 of every window holds +inf. Rows that did not keep slot 0 must get
+    # the oracle's finite O, also where K_l is not a multiple of the aggregation
+    # kernels' entry blocks (padding entries must add no 0 * inf term).
+    B, heads, H, W, d, win = 1, 2, 64, 64, 32, 32
+    shape = (B, heads, H, W, d)
+    qt, kt, vt = (inputs.draw(1200 + t + K_l, shape, dtype) for t in range(3))
+    vdev, vex = vt.device.copy(), vt.exact.copy()
+    vdev[:, :, ::win, ::win, 3] = np.float32(np.inf) if dtype == "f32" else np.uint16(0x7F80)
+    vex[:, :, ::win, ::win, 3] = np.inf
+    vt = inputs.Tensor(vdev, vex, dtype)
+    N, nwin = win * win, (H // win) * (W // win)
+    n_wh = B * heads * nwin
+    g = np.random.Generator(np.random.PCG64(1300 + K_l))
+    C = np.stack([np.sort(g.permutation(N)[:K_prev]) for _ in range(n_wh * N)]).astype(np.int32)
+    C = C.reshape(B, heads, nwin, N, K_prev)
+    a = (g.random((B, heads, nwin, N, K_prev)) + 0.05).astype(np.float32)
+    I, A, O = pfa.sparse_layer(to_dev(qt), to_dev(kt), to_dev(vt), torch.from_numpy(C).cuda(),
+                               torch.from_numpy(a).cuda(), K_l, win=win, shift=0)
+    torch.cuda.synchronize()
+    ref = oracle.layer(qt.exact, kt.exact, vex, win=win, shift=0, K_l=K_l, I_prev=C, A_prev=a.astype(np.float64),
+                       wh_list=np.arange(n_wh), want_keys=True)
+    Og = O.cpu().numpy()
+    fin = np.isfinite(ref["O"]).all(-1)
+    assert fin.sum() > 0.5 * fin.size and (~fin).sum() > 0, "case must mix rows with and without slot 0"
+    # near-ties would change which rows keep slot 0: compare the kept sets first
+    Ig = I.view(n_wh, N, K_l).cpu().numpy()
+    same = (np.sort(Ig, -1) == np.sort(ref["I"], -1)).all(-1)
+    assert same.mean() > 0.99
+    keeps0 = (Ig == 0).any(-1)
+    # pixel rows of window-head rows that kept slot 0 on the GPU or differ from the oracle are masked
+    O_ref = ref["O"].copy()
+    nwx = W // win
+    for n, i in np.argwhere(keeps0 | ~same):
+        b, h, wn = n // (heads * nwin), (n // nwin) % heads, n % nwin
+        y, x = (wn // nwx) * win + i // win, (wn % nwx) * win + i % win
+        O_ref[b, h, y, x] = np.nan
+    mask = ~np.isnan(O_ref[..., 0])
+    assert np.isfinite(Og[mask]).all(), "a row that did not keep slot 0 is not finite"
+    parity.check_O(Og, O_ref, parity.TOL[dtype])
