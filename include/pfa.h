@@ -21,7 +21,8 @@
  * free or synchronise: they validate the arguments, enqueue kernels on
  * `stream` (a hipStream_t; NULL = the null stream) and return. (Only the
  * optional timing calls at the end of this header create HIP events; the
- * backward pass takes its scratch memory as a caller-owned workspace.)
+ * backward passes take their scratch memory as a caller-owned workspace, or,
+ * in pfa_dense_layer_backward_noalloc, from a static device array.)
  *
  *   Q, K, V   [B, heads, H, W, d], element type `dtype` (fp32, or bf16 bits).
  *   O         [B, heads, H, W, d] fp32.
@@ -58,6 +59,12 @@ extern "C" {
 #define PFA_ERR_INVALID (-1)     /* inconsistent sizes, NULL where required */
 #define PFA_ERR_UNSUPPORTED (-2) /* valid, but outside what the kernels handle */
 #define PFA_ERR_HIP (-3)         /* the HIP runtime reported an error */
+#define PFA_ERR_TOO_LARGE (-4)   /* exceeds the static scratch memory of a no-allocation entry point */
+
+/* Size of the static scratch array behind the no-allocation entry point
+ * (pfa_dense_layer_backward_noalloc): 16 MiB per GPU, one fp32 per query slot, so
+ * at most 4194304 query slots (B * heads * (H/win) * (W/win) * win^2) per call. */
+#define PFA_STATIC_SCRATCH_BYTES (16 * 1024 * 1024)
 
 typedef enum { PFA_F32 = 0, PFA_BF16 = 1 } pfa_dtype;
 
@@ -233,6 +240,28 @@ int pfa_dense_layer_backward(const pfa_shape* shape, const void* Q, const void* 
 
 /* Workspace bytes pfa_dense_layer_backward needs, or a negative shape error. Host only. */
 int64_t pfa_dense_layer_backward_workspace(const pfa_shape* shape);
+
+/*
+ * pfa_dense_layer_backward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving or training
+ * loops, harnesses that forbid hipMalloc. It computes exactly what
+ * pfa_dense_layer_backward computes (the same kernels) and allocates nothing: its
+ * scratch memory (one fp32 per query slot) is a static device array of
+ * PFA_STATIC_SCRATCH_BYTES in the library's code object. Each GPU the library
+ * runs on holds its own copy until the process ends; the first call on a device
+ * looks up that copy's address (hipGetSymbolAddress), later calls reuse it.
+ *
+ * Arguments, layouts, outputs and the other errors are those of
+ * pfa_dense_layer_backward. PFA_ERR_TOO_LARGE: more than
+ * PFA_STATIC_SCRATCH_BYTES / 4 query slots; nothing is enqueued.
+ * Every call on one GPU shares that GPU's array, and each call writes the part it
+ * reads before reading it, so calls in order on one stream are safe; calls that
+ * overlap on one GPU (on different streams, or from several host threads
+ * without ordering) race on the array and may return wrong gradients.
+ */
+int pfa_dense_layer_backward_noalloc(const pfa_shape* shape, const void* Q, const void* K, const void* V,
+                                     const float* bias, const float* lse, const float* dO, const float* dA,
+                                     float* dQ, float* dK, float* dV, void* stream);
 
 /*
  * Propagation and sparsification of an individualized index matrix between

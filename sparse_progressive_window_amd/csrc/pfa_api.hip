@@ -2,6 +2,7 @@
 // The calls and their contracts are documented in include/pfa.h.
 #include <math.h>
 
+#include <mutex>
 #include <vector>
 
 #include "pfa.h"
@@ -147,6 +148,41 @@ int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const voi
     if (e == hipSuccess)
         e = timed(PFA_KERNEL_AGGREGATE, stream, [&] { return pfa::launch_aggregate(a, dtype, g.d, grid, stream); });
     return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
+}
+
+int run_dense_backward(const Geom& g, int dtype, const void* Q, const void* K, const void* V, const float* bias,
+                       const float* lse, const float* dO, const float* dA, float* dQ, float* dK, float* dV,
+                       float* Dws, hipStream_t s);
+
+}  // namespace
+
+// Scratch memory of the no-allocation entry point (pfa_dense_layer_backward_noalloc):
+// a static array in this file's device code object, so each GPU the library runs on
+// holds its own copy, from the code object's load until the process ends. Host code
+// never uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device (static_scratch below).
+static __device__ __align__(256) unsigned char scratch[PFA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`, looked up on the first
+// call on that device (with the device current) and kept.
+int static_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return PFA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return PFA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PFA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return PFA_OK;
 }
 
 }  // namespace
@@ -361,12 +397,40 @@ int pfa_dense_layer_backward(const pfa_shape* shape, const void* Q, const void* 
     if (workspace_bytes < n_wh(g) * g.N * 4) return PFA_ERR_INVALID;
     if (g.win % 8) return PFA_ERR_UNSUPPORTED;
     if (bias && g.win % 16) return PFA_ERR_UNSUPPORTED;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    return run_dense_backward(g, shape->dtype, Q, K, V, bias, lse, dO, dA, dQ, dK, dV,
+                              static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+int pfa_dense_layer_backward_noalloc(const pfa_shape* shape, const void* Q, const void* K, const void* V,
+                                     const float* bias, const float* lse, const float* dO, const float* dA,
+                                     float* dQ, float* dK, float* dV, void* stream) {
+    Geom g;
+    int code;
+    if (!geom_from_shape(shape, &g, &code)) return code;
+    if (g.win == 0) return PFA_ERR_UNSUPPORTED;
+    if (!Q || !K || !V || !lse || !dO || !dQ || !dK || !dV) return PFA_ERR_INVALID;
+    if (g.win % 8) return PFA_ERR_UNSUPPORTED;
+    if (bias && g.win % 16) return PFA_ERR_UNSUPPORTED;
+    if (n_wh(g) * g.N * 4 > PFA_STATIC_SCRATCH_BYTES) return PFA_ERR_TOO_LARGE;
+    float* Dws = nullptr;
+    const int rc = static_scratch(reinterpret_cast<void**>(&Dws));
+    if (rc != PFA_OK) return rc;
+    return run_dense_backward(g, shape->dtype, Q, K, V, bias, lse, dO, dA, dQ, dK, dV, Dws,
+                              static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+int run_dense_backward(const Geom& g, int dtype, const void* Q, const void* K, const void* V, const float* bias,
+                       const float* lse, const float* dO, const float* dA, float* dQ, float* dK, float* dV,
+                       float* Dws, hipStream_t s) {
     pfa::DenseBwdArgs a;
     a.Q = Q; a.K = K; a.V = V;
     a.bias = bias; a.lse = lse; a.dO = dO; a.dA = dA;
     a.dQ = dQ; a.dK = dK; a.dV = dV;
-    a.Dws = static_cast<float*>(workspace);
+    a.Dws = Dws;
     a.g = g;
     a.scale2 = (float)(1.4426950408889634 / sqrt((double)g.d));
     a.scale = (float)(1.0 / sqrt((double)g.d));
@@ -374,9 +438,13 @@ int pfa_dense_layer_backward(const pfa_shape* shape, const void* Q, const void* 
     const int64_t grid = n_wh(g) * pfa::dense_bwd_blocks(g.N);
     if (grid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
     const hipError_t e = timed(PFA_KERNEL_DENSE_BWD, s,
-                               [&] { return pfa::launch_dense_backward(a, shape->dtype, g.d, (int)grid, s); });
+                               [&] { return pfa::launch_dense_backward(a, dtype, g.d, (int)grid, s); });
     return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
 }
+
+}  // namespace
+
+extern "C" {
 
 int64_t pfa_iet_propagate_workspace(int32_t B, int32_t N, int32_t k1, int32_t k2) {
     if (B < 1 || N < 1 || k1 < 1 || k2 < 1) return PFA_ERR_INVALID;
@@ -408,6 +476,7 @@ const char* pfa_strerror(int code) {
         case PFA_ERR_INVALID: return "invalid argument";
         case PFA_ERR_UNSUPPORTED: return "unsupported configuration";
         case PFA_ERR_HIP: return "HIP runtime error";
+        case PFA_ERR_TOO_LARGE: return "problem larger than the static scratch memory of a no-allocation entry point";
         default: return "unknown error code";
     }
 }

@@ -55,6 +55,8 @@ def load():
         lib.pfa_sparse_layer_backward_workspace.restype = ctypes.c_int64
         lib.pfa_dense_layer_backward.argtypes = [ctypes.POINTER(PfaShape)] + [P] * 11 + [ctypes.c_int64, P]
         lib.pfa_dense_layer_backward.restype = ctypes.c_int
+        lib.pfa_dense_layer_backward_noalloc.argtypes = [ctypes.POINTER(PfaShape)] + [P] * 11
+        lib.pfa_dense_layer_backward_noalloc.restype = ctypes.c_int
         lib.pfa_dense_layer_backward_workspace.argtypes = [ctypes.POINTER(PfaShape)]
         lib.pfa_dense_layer_backward_workspace.restype = ctypes.c_int64
         lib.pfa_iet_propagate.argtypes = [i32, i32, i32, i32, P, P, i32, i32, P, P, P, ctypes.c_int64, P]
@@ -319,6 +321,33 @@ def dense_layer_backward(Q, K, V, lse, dO, dA=None, *, win, shift=0, bias=None, 
                                          workspace.numel() * workspace.element_size(), _stream())
     if rc != 0:
         raise PfaError("pfa_dense_layer_backward", rc)
+    return dQ, dK, dV
+
+
+def dense_layer_backward_noalloc(Q, K, V, lse, dO, dA=None, *, win, shift=0, bias=None, out=None):
+    """dense_layer_backward through the entry point that allocates nothing (its
+    scratch memory is the library's static device array). ``out`` = optional
+    preallocated (dQ, dK, dV); when given, this call allocates nothing either."""
+    _check_qkv(Q, K, V)
+    lead, N = _geometry(Q, win)
+    dev = Q.device
+    if out is None:
+        dQ, dK, dV = (torch.empty(Q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+    else:
+        dQ, dK, dV = out
+    rows = _prod(lead) * N
+    _expect(lse, rows, torch.float32, "lse")
+    _expect(dO, Q.numel(), torch.float32, "dO")
+    _expect(dA, rows * N, torch.float32, "dA")
+    for t, n in ((dQ, "dQ"), (dK, "dK"), (dV, "dV")):
+        _expect(t, Q.numel(), torch.float32, n)
+    _check_bias(bias, Q, win)
+    shape = make_shape(Q, win, shift)
+    rc = load().pfa_dense_layer_backward_noalloc(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(bias),
+                                                 _ptr(lse), _ptr(dO), _ptr(dA), _ptr(dQ), _ptr(dK), _ptr(dV),
+                                                 _stream())
+    if rc != 0:
+        raise PfaError("pfa_dense_layer_backward_noalloc", rc)
     return dQ, dK, dV
 
 

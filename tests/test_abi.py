@@ -228,3 +228,17 @@ def test_dense_backward_validation(lib):
     assert db(shape(), ws_bytes=1024 * 4 - 4) == -1
     assert db(shape(d=8)) == -2
     assert lib.pfa_dense_layer_backward_workspace(ctypes.byref(shape(B=2, heads=3))) == 2 * 3 * 1024 * 4
+
+
+def test_noalloc_dense_backward_validation(lib):
+    # The no-allocation entry point rejects, before any HIP call, what its static
+    # scratch array cannot hold: 4096 windows of 32x32 (4194304 query slots) fit,
+    # one more row of windows does not. NULL and shape errors as the workspace form.
+    def call(s, q=FAKE):
+        return lib.pfa_dense_layer_backward_noalloc(ctypes.byref(s), q, FAKE, FAKE, None, FAKE, FAKE, None, FAKE,
+                                                    FAKE, FAKE, None)
+    assert call(shape(H=2080, W=2048, d=16)) == -4
+    assert call(shape(), q=None) == -1
+    assert call(shape(win=0)) == -2
+    assert call(shape(win=12, H=24, W=24)) == -2                  # win % 8 != 0
+    assert lib.pfa_strerror(-4).startswith(b"problem larger than the static scratch")
