@@ -37,7 +37,8 @@ COUNTERS_FILE = "hbm_counters_{workload}.md"
 HEADLINE = "map640x384_h6_d32_bf16_6blocks"
 
 # kernel kinds of the library's timing calls (pfa_kernel_kind)
-DENSE, ALL_CAND, SPARSE, SELECT, AGGREGATE, IOTA, BWD_ROWS, BWD_SCATTER, IET_RANK, IET_UNION, DENSE_BWD = range(11)
+(DENSE, ALL_CAND, SPARSE, SELECT, AGGREGATE, IOTA, BWD_ROWS, BWD_SCATTER, IET_RANK, IET_UNION, DENSE_BWD,
+ BWD_EXACT) = range(12)
 
 
 def kernel_bytes(w, l, kind, i_prev_implicit, split, fused=False):
@@ -120,10 +121,11 @@ def bwd_kernel_bytes(w, l, part, i_prev_implicit):
     dA = pairs if l < w.layers - 1 else 0      # the last layer's map has no consumer
     if part == "V":
         return x + 2 * pairs + dA + f + pairs
+    flags = N * 4                             # one row flag for the exact dA^{l-1} pass
     if part == "K":
-        return 2 * x + 3 * pairs + ip + prev + f + prev
+        return 2 * x + 3 * pairs + ip + prev + f + prev + flags
     if part == "KV":
-        return 3 * x + 2 * pairs + dA + f + pairs + ip + prev + f + prev
+        return 3 * x + 2 * pairs + dA + f + pairs + ip + prev + f + prev + flags
     return x + 3 * pairs + f + 2 * f
 
 
@@ -494,6 +496,8 @@ def backward_leg(chain, args, torch, pfa):
         for kind, ms in recs[start:end]:
             if kind == BWD_SCATTER:
                 per.setdefault((l, "scatter"), []).append(ms)
+            elif kind == BWD_EXACT:
+                per.setdefault((l, "exact"), []).append(ms)
         start = end
     kernels = []
     for (l, part), v in sorted(per.items()):
@@ -510,6 +514,11 @@ def backward_leg(chain, args, torch, pfa):
                             "io_bytes": by, "GB_per_s": round(gbs, 1), "alg_flops": fl,
                             "TFLOP_per_s": round(tfs, 2), "bound": "mfma" if mfma else "hbm",
                             "frac": round(tfs / FP32_MFMA_PEAK_TFLOPS if mfma else gbs / HBM_PEAK_GBS, 4)})
+            continue
+        if part == "exact":
+            # reads one flag per row; rows that need the exact dA^{l-1} pass are rare
+            kernels.append({"layer": l + 1, "kernel": "bwd_exact_dap_kernel", "launches": len(v), "ms": round(ms, 4),
+                            "io_bytes": N * 4 * w.n_wh, "bound": "latency"})
             continue
         by = bwd_kernel_bytes(w, l, part, implicit[l]) * w.n_wh
         gbs = by / (ms * 1e-3) / 1e9

@@ -179,7 +179,9 @@ int pfa_first_two_layers(const pfa_shape* shape, int32_t shift1, int32_t shift2,
  *   G_ij = dA_ij + dO_i . v_j,   g_ij = G_ij - sum_j' A_ij' G_ij'   (j, j' kept)
  *   dQ_i = sum_j A_ij g_ij k_j / sqrt(d)
  *   dK_j = sum_i A_ij g_ij q_i / sqrt(d),   dV_j = sum_i A_ij dO_i
- *   dA_prev_ij = A_ij g_ij / A_prev_ij at kept slots, 0 at dropped ones
+ *   dA_prev_ij = exp(s_ij) / sum_j' A_prev_ij' exp(s_ij') * g_ij at kept slots
+ *                (j' kept; = A_ij g_ij / A_prev_ij where A_prev_ij > 0), 0 at
+ *                dropped ones; s_ij = q_i.k_j / sqrt(d)
  *
  * Q, K, V, I_prev, A_prev, K_prev, K_l  the forward call's arguments (window
  *         mode, one index matrix per head; I_prev NULL = every slot, K_prev = N).
@@ -191,10 +193,11 @@ int pfa_first_two_layers(const pfa_shape* shape, int32_t shift1, int32_t shift2,
  *         backward), or NULL for zero.
  * dQ, dK, dV  [B, heads, H, W, d] fp32 outputs, every element written.
  * dA_prev [B, heads, nwin, N, K_prev] fp32 output aligned with I_prev, or NULL
- *         (not computed). Requires A_prev. A kept slot whose A_prev is 0 gets 0.
+ *         (not computed). Requires A_prev. A kept slot whose A_prev is 0 (kept
+ *         when K_l exceeds the row's positive weights) gets the formula's value.
  * workspace  device buffer of at least pfa_sparse_layer_backward_workspace()
- *         bytes (one fp32 per kept pair), owned by the caller; its contents on
- *         entry do not matter and are overwritten.
+ *         bytes (one fp32 per kept pair and one int32 per query row), owned by
+ *         the caller; its contents on entry do not matter and are overwritten.
  * When N is not a multiple of 16, dK and dV are accumulated with LDS atomics
  * in no fixed order, so results may differ between runs in the last bits;
  * otherwise the backward pass is deterministic.
@@ -320,8 +323,10 @@ typedef enum {
                                       "bwd_scatter_kernel" by LDS adds when N % 16 != 0) */
     PFA_KERNEL_IET_RANK = 8,       /* index propagation: top-k1 / top-k2 of each row */
     PFA_KERNEL_IET_UNION = 9,      /* index propagation: de-duplicated union per row */
-    PFA_KERNEL_DENSE_BWD = 10      /* backward of the dense layer ("dense_bwd_dq_kernel" then
+    PFA_KERNEL_DENSE_BWD = 10,     /* backward of the dense layer ("dense_bwd_dq_kernel" then
                                       "dense_bwd_dkv_kernel", one record for both) */
+    PFA_KERNEL_BWD_EXACT = 11      /* backward with dA_prev: rows whose kept weights include zero or
+                                      subnormal values, dA_prev from the scores */
 } pfa_kernel_kind;
 
 /* capacity > 0: create 2*capacity events and start recording (earlier records

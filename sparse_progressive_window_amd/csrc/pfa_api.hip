@@ -310,7 +310,7 @@ int64_t pfa_sparse_layer_backward_workspace(const pfa_shape* shape, int32_t K_l)
     int code;
     if (!geom_from_shape(shape, &g, &code)) return code;
     if (K_l < 1 || K_l > g.N) return PFA_ERR_INVALID;
-    return n_wh(g) * g.N * (int64_t)K_l * 4;
+    return n_wh(g) * g.N * ((int64_t)K_l + 1) * 4;   // g per kept pair, then one flag per row
 }
 
 int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void* K, const void* V,
@@ -326,7 +326,7 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
     if (K_prev < 1 || K_prev > g.N || K_l < 1 || K_l > K_prev) return PFA_ERR_INVALID;
     if (!I_prev && K_prev != g.N) return PFA_ERR_INVALID;
     if (dA_prev && !A_prev) return PFA_ERR_INVALID;
-    if (workspace_bytes < n_wh(g) * g.N * (int64_t)K_l * 4) return PFA_ERR_INVALID;
+    if (workspace_bytes < n_wh(g) * g.N * ((int64_t)K_l + 1) * 4) return PFA_ERR_INVALID;
     if (K_l > 256) return PFA_ERR_UNSUPPORTED;
     if ((int64_t)g.N * K_l * 4 > 0x7FFFFFF0) return PFA_ERR_UNSUPPORTED;
     const int parts = pfa::backward_scatter_parts(g.d, g.N, K_l);
@@ -340,10 +340,12 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
     a.dO = dO; a.dA_l = dA_l;
     a.dQ = dQ; a.dK = dK; a.dV = dV; a.dA_prev = dA_prev;
     a.g_buf = static_cast<float*>(workspace);
+    a.row_flags = reinterpret_cast<int32_t*>(a.g_buf + n_wh(g) * g.N * (int64_t)K_l);
     a.g = g;
     a.K_prev = K_prev; a.K_l = K_l;
     a.xcd_map = (n_wh(g) % 8 == 0) ? 1 : 0;
     a.scale = (float)(1.0 / sqrt((double)g.d));
+    a.scale2 = (float)(1.4426950408889634 / sqrt((double)g.d));
     a.dkv_full = (int)n_wh(g);
     a.blocks_per_wh = g.N >= 512 ? 2 : 1;
     a.rows_per_block = (g.N + a.blocks_per_wh - 1) / a.blocks_per_wh;
@@ -360,6 +362,9 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
             e = timed(PFA_KERNEL_BWD_ROWS, s,
                       [&] { return pfa::launch_backward_rows(a, dt, g.d, false, true, (int)rgrid, s); });
     }
+    if (e == hipSuccess && dA_prev)
+        e = timed(PFA_KERNEL_BWD_EXACT, s,
+                  [&] { return pfa::launch_backward_exact_dap(a, dt, g.d, (int)rgrid, s); });
     if (e == hipSuccess) {
         pfa::BackwardArgs b = a;
         b.rows_per_block = g.N;
@@ -531,6 +536,7 @@ const char* pfa_kernel_name(int32_t kind) {
         case PFA_KERNEL_IET_RANK: return "iet_rank_kernel";
         case PFA_KERNEL_IET_UNION: return "iet_union_kernel";
         case PFA_KERNEL_DENSE_BWD: return "dense_bwd";
+        case PFA_KERNEL_BWD_EXACT: return "bwd_exact_dap_kernel";
         default: return "unknown";
     }
 }

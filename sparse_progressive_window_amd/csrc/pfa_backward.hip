@@ -12,7 +12,9 @@
 //   dQ_i        = sum_r dkey_ir k_j / sqrt(d)
 //   dK_j       += dkey_ir q_i / sqrt(d)
 //   dV_j       += A_ir dO_i
-//   dA^{l-1}_ir = dkey_ir / A^{l-1}_ir  at kept slots, 0 at dropped ones.
+//   dA^{l-1}_ir = exp(s_ir) / sum_kept A^{l-1} exp(s) * g_ir  at kept slots, 0 at
+//                 dropped ones; this is dkey_ir / A^{l-1}_ir wherever A^l_ir and
+//                 A^{l-1}_ir are normal floats (the usual case).
 //
 // Kernels.
 // * bwd_rows_kernel: one group of GL lanes per query row; CH lanes split each
@@ -26,7 +28,17 @@
 //   dA^{l-1}: kept tokens are marked in a per-row LDS bitmap, the I^{l-1} row is
 //   scanned in slot order, and the r-th marked slot takes kept entry r (I^l is
 //   a subsequence of I^{l-1} in its order). When K and V fit in LDS together
-//   both passes run in one kernel, keeping G in registers.
+//   both passes run in one kernel, keeping G in registers. A row with a kept
+//   slot whose A^l or A^{l-1} is zero or subnormal (allowed: a slot of weight 0
+//   is kept when K_l exceeds the row's positive weights) has no usable ratio
+//   there. Such a slot's A^l is zero or subnormal too (A^l = A^{l-1} exp(s) /
+//   sum, with a subnormal A^{l-1} and a normal A^l the true value overflows
+//   fp32 anyway), so the K pass flags its workgroup, by A^l, in the workspace.
+// * bwd_exact_dap_kernel (after the row pass, only with dA^{l-1}): in flagged
+//   workgroups, for each row with such a slot, the log normaliser C = log2 sum_kept A^{l-1} 2^{s2} from the
+//   scores themselves (s2 = s log2(e), k_j read from global memory), then
+//   dA^{l-1} = 2^{s2 - C} g at the flagged slots. Rare by construction; out of
+//   the row kernels, whose registers it would otherwise take.
 // * bwd_dkv_kernel (N a multiple of 16): dV = A^T dO and dK = (A g)^T Q / sqrt(d)
 //   as dense fp32 MFMA products over row blocks densified in LDS, the dV / dK
 //   tiles of each wave's tokens held in registers. At the densities of the keep
@@ -37,6 +49,8 @@
 //   d columns per workgroup) by compare-and-swap adds; each wave stages one
 //   row's (j, A, A g/sqrt(d)) in LDS and its lanes cover (64/DH kept slots) x
 //   DH columns per instruction.
+#include <float.h>
+
 #include "pfa_kernels.h"
 #include "pfa_rows.h"
 
@@ -136,6 +150,12 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
     const int rsw = bmw + ((K_l + 3) & ~3);              // row scratch words
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(smem + (HAS_V + HAS_K) * N * ROWB) + (wave * RPW + grp) * rsw;
     float* vals = reinterpret_cast<float*>(bitmap + bmw);
+    // workgroup flag for the exact dA^{l-1} pass, after the row scratch
+    uint32_t* wg_flag = reinterpret_cast<uint32_t*>(smem + (HAS_V + HAS_K) * N * ROWB) + NW * RPW * rsw;
+    if (want_dap && threadIdx.x == 0) *wg_flag = 0u;
+    // smallest A^l over this lane's kept entries of all its rows, as fp32 bits (A^l >= 0
+    // orders like its bits): one v_min_u32 per entry, one workgroup flag at the end
+    uint32_t amin = 0xFFFFFFFFu;
     if (HAS_V) stage_rows<T, D>(Vs, ROWB, static_cast<const T*>(p.V) + plane, g, w.wy, w.wx);
     if (HAS_K) stage_rows<T, D>(Ks, ROWB, static_cast<const T*>(p.K) + plane, g, w.wy, w.wx);
     __syncthreads();
@@ -399,6 +419,7 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
                     for (int y = 0; y < EPC; ++y) dq[y] = fmaf(dkey, kf[y], dq[y]);
                     if (want_dap && valid && x % CH == vchunk) {
                         vals[e0 + x] = dkey;
+                        amin = min(amin, __float_as_uint(av[x]));
                         atomicOr(&bitmap[j >> 5], 1u << (j & 31));
                     }
                 }
@@ -460,6 +481,8 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
                         run += __builtin_popcountll(m);
                         // v_rcp_f32 (1 ulp) and a product instead of the IEEE division
                         // sequence (~10 instructions per slot, every slot of the row)
+                        // (a kept slot with A^{l-1} = 0 has A^l = 0 as well: such rows are
+                        // flagged from A^l below and rewritten by the exact pass)
                         float val = 0.0f;
                         if (kept && rank < K_l && ap[u] > 0.0f) val = vals[rank] * __builtin_amdgcn_rcpf(ap[u]);
                         if (active && sv) p.dA_prev[srow + slot] = val;
@@ -467,6 +490,106 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
                 }
             }
         }
+    }
+    if (want_dap) {
+        // some kept A^l of this workgroup's rows below FLT_MIN (idle groups looked at
+        // row0, one of its rows): the exact pass revisits the workgroup's rows
+        if (ballot(amin < 0x00800000u) != 0 && lane == 0) atomicOr(wg_flag, 1u);
+        __syncthreads();
+        if (threadIdx.x == 0) p.row_flags[blockIdx.x] = (int32_t)*wg_flag;
+    }
+}
+
+// Exact dA^{l-1} in the workgroups the row pass flagged (one workgroup here per
+// row-pass workgroup, same rows). Each wavefront takes rows of the part; a row
+// whose kept A^l are all normal floats is skipped, for the others (the lanes
+// together):
+//   C = log2 sum over kept r with A^{l-1}_r > 0 of A^{l-1}_r 2^{s2_r}  (a running
+//       (max, sum) per lane, then over the wave), s2_r = q_i.k_j log2(e) / sqrt(d);
+//   dA^{l-1} = 2^{s2_r - C} g_r at the kept slots where A^l_r or A^{l-1}_r is zero
+//   or subnormal (the others keep the row pass's dkey / A^{l-1}).
+// The kept entry r of I^l (token j) sits at the slot of j in the row's I^{l-1},
+// found through a token -> slot table in LDS. q_i and k_j come from global
+// memory at the layer's pixels (rare rows: no staging).
+template <typename T, int D>
+__global__ __launch_bounds__(4 * kWave) void bwd_exact_dap_kernel(const BackwardArgs p) {
+    constexpr int EPC = Chunk<T>::kElems;
+    constexpr int CH = D / EPC;
+    __shared__ int16_t pos_all[4][1024];
+    if (p.row_flags[blockIdx.x] == 0) return;   // uniform: the usual case
+    const Geom g = p.g;
+    const int N = g.N;
+    const int K_prev = p.K_prev, K_l = p.K_l;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    int16_t* pos = pos_all[wave];
+    const WhPart w = decode_block(p.blocks_per_wh, p.xcd_map, g);
+    const size_t plane = (size_t)w.bh * g.H * g.W * D;
+    const T* Qh = static_cast<const T*>(p.Q) + plane;
+    const T* Kh = static_cast<const T*>(p.K) + plane;
+    const int row0 = w.part * p.rows_per_block;
+    const int row1 = min(N, row0 + p.rows_per_block);
+    for (int i = row0 + wave; i < row1; i += 4) {
+        const size_t row = (size_t)w.wh * N + i;
+        const int32_t* Il = p.I_l + row * K_l;
+        const float* Al = p.A_l + row * K_l;
+        bool low = false;
+        for (int e = lane; e < K_l; e += kWave) low |= !(Al[e] >= FLT_MIN);
+        if (ballot(low) == 0) continue;
+        float qf[D];
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+            Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(Qh + (size_t)slot_pixel(g, w.wy, w.wx, i) * D + c * EPC),
+                             &qf[c * EPC]);
+        auto score2 = [&](int j) {
+            const T* kr = Kh + (size_t)slot_pixel(g, w.wy, w.wx, j) * D;
+            float acc = 0.0f;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                float kf[EPC];
+                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(kr + c * EPC), kf);
+#pragma unroll
+                for (int y = 0; y < EPC; ++y) acc = fmaf(qf[c * EPC + y], kf[y], acc);
+            }
+            return acc * p.scale2;
+        };
+        const int32_t* Ip = p.I_prev ? p.I_prev + row * K_prev : nullptr;
+        const float* Ap = p.A_prev + row * K_prev;
+        const float* Gl = p.g_buf + row * K_l;
+        if (Ip) {
+            for (int c = lane; c < K_prev; c += kWave) pos[min((unsigned)Ip[c], (unsigned)(N - 1))] = (int16_t)c;
+            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's table writes before its reads
+        }
+        float mx = -INFINITY, sz = 0.0f;
+        for (int e = lane; e < K_l; e += kWave) {
+            const int j = (int)min((unsigned)Il[e], (unsigned)(N - 1));
+            const float a = Ap[Ip ? pos[j] : j];
+            if (a > 0.0f) {
+                const float kap = score2(j) + log2f(a);
+                if (kap > mx) {
+                    sz = sz * exp2f(mx - kap) + 1.0f;
+                    mx = kap;
+                } else {
+                    sz += exp2f(kap - mx);
+                }
+            }
+        }
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const float mo = __shfl_xor(mx, o);
+            const float so = __shfl_xor(sz, o);
+            const float mn = fmaxf(mx, mo);
+            sz = (mx == -INFINITY ? 0.0f : sz * exp2f(mx - mn)) + (mo == -INFINITY ? 0.0f : so * exp2f(mo - mn));
+            mx = mn;
+        }
+        const float C = mx + log2f(sz);
+        for (int e = lane; e < K_l; e += kWave) {
+            const int j = (int)min((unsigned)Il[e], (unsigned)(N - 1));
+            const int c = Ip ? pos[j] : j;
+            const float a = Ap[c];
+            if (!(a >= FLT_MIN) || !(Al[e] >= FLT_MIN)) p.dA_prev[row * K_prev + c] = exp2f(score2(j) - C) * Gl[e];
+        }
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // table reads done before the next row's writes
     }
 }
 
@@ -758,7 +881,7 @@ int rows_lds(int dtype, int D, int N, int K_l, bool has_v, bool has_k, bool want
     const int gl = rows_group(chunks_per_row(dtype, D), K_l);
     const int rsw = (N + 31) / 32 + ((K_l + 3) & ~3);
     return ((has_v ? 1 : 0) + (has_k ? 1 : 0)) * N * rowb +
-           ((has_k && want_dap) ? kBwdRowWaves * (64 / gl) * rsw * 4 : 0);
+           ((has_k && want_dap) ? kBwdRowWaves * (64 / gl) * rsw * 4 + 16 : 0);   // + the workgroup flag
 }
 
 template <typename T, int D, bool HV, bool HK>
@@ -882,6 +1005,16 @@ hipError_t launch_backward_rows(const BackwardArgs& a, int dtype, int D, bool ha
                        : launch_rows_t<float, 32>(a, has_v, has_k, grid, stream);
     return D == 16 ? launch_rows_t<uint16_t, 16>(a, has_v, has_k, grid, stream)
                    : launch_rows_t<uint16_t, 32>(a, has_v, has_k, grid, stream);
+}
+
+hipError_t launch_backward_exact_dap(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream) {
+    if (a.g.N > 1024) return hipErrorInvalidValue;
+    auto go = [&](auto fn) {
+        hipLaunchKernelGGL(fn, dim3(grid), dim3(4 * kWave), 0, stream, a);
+        return hipGetLastError();
+    };
+    if (dtype == 0) return D == 16 ? go(bwd_exact_dap_kernel<float, 16>) : go(bwd_exact_dap_kernel<float, 32>);
+    return D == 16 ? go(bwd_exact_dap_kernel<uint16_t, 16>) : go(bwd_exact_dap_kernel<uint16_t, 32>);
 }
 
 hipError_t launch_backward_scatter(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream) {

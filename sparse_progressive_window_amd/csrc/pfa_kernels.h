@@ -70,11 +70,14 @@ struct BackwardArgs {
     float* dV;
     float* dA_prev;          // [wh, N, K_prev] or nullptr (not wanted)
     float* g_buf;            // workspace [wh, N, K_l]: G_ij - sum_j A_ij G_ij
+    int32_t* row_flags;      // workspace, one int per row-pass workgroup (with dA_prev): 1 where a kept
+                             // A^l of its rows is zero or subnormal (those rows need the exact pass)
     Geom g;
     int K_prev, K_l;
     int rows_per_block, blocks_per_wh;
     int xcd_map;
     float scale;             // 1 / sqrt(d)
+    float scale2;            // log2(e) / sqrt(d): base-2 scores of the exact dA^{l-1} pass
     // dK/dV MFMA kernel: workgroups [0, dkv_full) take a whole window-head each;
     // each further pair (workgroups 8 apart, one XCD) takes the two token halves
     // of one window-head (balances the last round over the CUs)
@@ -87,6 +90,8 @@ struct BackwardArgs {
 int backward_fused_rows(int dtype, int D, int N, int K_l, bool want_dA_prev);
 hipError_t launch_backward_rows(const BackwardArgs& a, int dtype, int D, bool has_v, bool has_k, int grid,
                                 hipStream_t stream);
+// dA^{l-1} of the rows the row pass flagged, from the scores (after the row pass).
+hipError_t launch_backward_exact_dap(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream);
 // dK and dV as dense MFMA products over LDS-densified row blocks (N % 16 == 0).
 bool backward_dkv_mfma(int D, int N, int K_l);
 // whole-window-head dK/dV workgroups for n_wh window-heads on `cus` compute units

@@ -71,16 +71,16 @@ __device__ __forceinline__ WhPart wh_coords(int wh, int part, const Geom& g) {
 
 // workgroup -> (window-head, part); with xcd_map the parts of one window-head are
 // consecutive workgroups of one XCD (workgroups are dealt to the 8 XCDs in turn)
-__device__ __forceinline__ WhPart decode_block(int blocks_per_wh, int xcd_map, const Geom& g) {
+__device__ __forceinline__ WhPart decode_block_id(int bid, int blocks_per_wh, int xcd_map, const Geom& g) {
     WhPart w;
     if (xcd_map) {
-        const int xcd = blockIdx.x & 7;
-        const int slot = blockIdx.x >> 3;
+        const int xcd = bid & 7;
+        const int slot = bid >> 3;
         w.part = slot % blocks_per_wh;
         w.wh = (slot / blocks_per_wh) * 8 + xcd;
     } else {
-        w.wh = blockIdx.x / blocks_per_wh;
-        w.part = blockIdx.x - w.wh * blocks_per_wh;
+        w.wh = bid / blocks_per_wh;
+        w.part = bid - w.wh * blocks_per_wh;
     }
     w.nwin = g.nwy * g.nwx;
     w.win_id = w.wh % w.nwin;
@@ -89,6 +89,9 @@ __device__ __forceinline__ WhPart decode_block(int blocks_per_wh, int xcd_map, c
     w.wy = w.win_id / g.nwx;
     w.wx = w.win_id - w.wy * g.nwx;
     return w;
+}
+__device__ __forceinline__ WhPart decode_block(int blocks_per_wh, int xcd_map, const Geom& g) {
+    return decode_block_id(blockIdx.x, blocks_per_wh, xcd_map, g);
 }
 
 // Stage rows t = 0..N-1 of a window (slot order, under the layer's shift) into LDS

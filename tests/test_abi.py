@@ -51,10 +51,10 @@ def test_timing_calls_without_device(lib):
     assert lib.pfa_timing_read(None, None, 0, None, None) == -1
     assert lib.pfa_timing_read(None, None, 4, ctypes.byref(n), None) == -1
     assert lib.pfa_timing_read(None, None, -1, ctypes.byref(n), None) == -1
-    names = [lib.pfa_kernel_name(k).decode() for k in range(11)]
+    names = [lib.pfa_kernel_name(k).decode() for k in range(12)]
     assert names == ["dense_layer_kernel", "all_cand", "sparse_layer_kernel",
                      "sparse_layer_kernel(select)", "aggregate", "iota_rows_kernel", "bwd_rows_kernel",
-                     "bwd_dkv", "iet_rank_kernel", "iet_union_kernel", "dense_bwd"]
+                     "bwd_dkv", "iet_rank_kernel", "iet_union_kernel", "dense_bwd", "bwd_exact_dap_kernel"]
     assert lib.pfa_kernel_name(99) == b"unknown"
 
 
@@ -155,7 +155,7 @@ def test_first_two_layers_validation(lib):
 
 
 def test_backward_validation(lib):
-    ws_full = 1 * 1 * 1024 * 64 * 4
+    ws_full = 1 * 1 * 1024 * (64 + 1) * 4
 
     def bwd(s, K_prev=256, K_l=64, I_prev=FAKE, A_prev=FAKE, dA_prev=FAKE, ws=FAKE, ws_bytes=ws_full,
             grads=(FAKE, FAKE, FAKE), dO=FAKE):
@@ -176,7 +176,7 @@ def test_backward_validation(lib):
     assert bwd(shape(), K_prev=1024, K_l=512, I_prev=None, ws_bytes=1 << 30) == -2   # K_l > 256
     assert lib.pfa_sparse_layer_backward_workspace(ctypes.byref(shape()), 64) == ws_full
     assert lib.pfa_sparse_layer_backward_workspace(ctypes.byref(shape(B=2, heads=3, H=64, W=32)), 16) == \
-        2 * 3 * 2 * 1024 * 16 * 4
+        2 * 3 * 2 * 1024 * (16 + 1) * 4   # g per kept pair, one flag per row
     assert lib.pfa_sparse_layer_backward_workspace(ctypes.byref(shape()), 0) == -1
     assert lib.pfa_sparse_layer_backward_workspace(ctypes.byref(shape(d=8)), 16) == -2
 

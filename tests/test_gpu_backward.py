@@ -85,7 +85,7 @@ def rand_map(shape, seed):
 
 
 def run_case(B, heads, H, W, d, win, shift, K_prev, K_l, dtype, seed, *, implicit=False, with_dA=True,
-             want_dA_prev=True):
+             want_dA_prev=True, zero_frac=0.0, subnormal_frac=0.0):
     shape = (B, heads, H, W, d)
     qt, kt, vt = (inputs.draw(seed + t, shape, dtype) for t in range(3))
     N = win * win
@@ -94,6 +94,14 @@ def run_case(B, heads, H, W, d, win, shift, K_prev, K_l, dtype, seed, *, implici
     lead = (B, heads, nwin)
     I_prev = None if implicit else rand_lists(n_wh * N, N, K_prev, seed + 5).reshape(lead + (N, K_prev))
     A_prev = rand_map(lead + (N, K_prev), seed + 6)
+    if zero_frac or subnormal_frac:
+        # zero (and subnormal) previous weights; with K_l above a row's positive
+        # weights, slots of weight 0 are kept (their A^l is 0, their dA^{l-1} is not)
+        g = np.random.Generator(np.random.PCG64(seed + 9))
+        u = g.random(A_prev.shape)
+        A_prev[u < zero_frac] = 0.0
+        A_prev[(u >= zero_frac) & (u < zero_frac + subnormal_frac)] = np.float32(3e-41)
+        A_prev[..., 0] = np.maximum(A_prev[..., 0], np.float32(0.5 / K_prev))
     Qd, Kd, Vd = to_dev(qt), to_dev(kt), to_dev(vt)
     Ipd = None if I_prev is None else torch.from_numpy(I_prev).cuda()
     Apd = torch.from_numpy(A_prev).cuda()
@@ -141,6 +149,28 @@ CASES = [
 ]
 
 
+ZERO_CASES = [
+    # dtype, d, win, shift, K_prev, K_l, implicit, zero_frac, subnormal_frac
+    ("f32", 32, 32, 16, 1024, 256, True, 0.9, 0.0),   # K pass alone (fp32, d = 32), layer-2 shape
+    ("bf16", 32, 32, 16, 1024, 256, True, 0.85, 0.05),  # K and V passes in one kernel
+    ("f32", 32, 32, 0, 128, 64, False, 0.7, 0.1),
+    ("bf16", 16, 16, 0, 100, 37, False, 0.75, 0.0),
+]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,d,win,shift,K_prev,K_l,implicit,zero_frac,subnormal_frac", ZERO_CASES)
+def test_backward_zero_previous_weights(dtype, d, win, shift, K_prev, K_l, implicit, zero_frac, subnormal_frac,
+                                        capsys):
+    """Previous maps with many zero (and subnormal) weights, so that rows keep
+    slots of weight 0: their dA^{l-1} is exp(s) / sum_kept A^{l-1} exp(s) * g,
+    not 0 (pinned by finite differences in the oracle's pins)."""
+    st = run_case(1, 2, 2 * win, 2 * win, d, win, shift, K_prev, K_l, dtype, 900 + K_l + d, implicit=implicit,
+                  zero_frac=zero_frac, subnormal_frac=subnormal_frac)
+    with capsys.disabled():
+        print(f"  zero weights {dtype} d={d} win={win} K={K_prev}->{K_l}: {st}", flush=True)
+
+
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("dtype,d,win,shift,K_prev,K_l,implicit,with_dA", CASES)
 def test_backward_random(dtype, d, win, shift, K_prev, K_l, implicit, with_dA, capsys):
@@ -165,7 +195,7 @@ def test_backward_kernel_timing_records():
     finally:
         pfa.timing_enable(0)
     kinds = [k for k, _ in recs]
-    assert kinds[-3:] == [6, 6, 7], kinds          # V pass, K pass, dK/dV (fp32, d = 32)
+    assert kinds[-4:] == [6, 6, 11, 7], kinds      # V pass, K pass, exact dA^{l-1} rows, dK/dV (fp32, d = 32)
     assert dropped == 0 and all(ms > 0 for _, ms in recs)
 
 

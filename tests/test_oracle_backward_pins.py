@@ -47,6 +47,44 @@ def loss_fn(Q, K, V, A_prev, I_prev, *, win, shift, keep, dO, dA):
     return float(np.sum(dO * r["O"]) + (np.sum(dA * r["A"]) if dA is not None else 0.0))
 
 
+def test_finite_differences_zero_previous_weights():
+    """Kept slots whose previous weight is exactly 0 (kept when K_l exceeds a
+    row's positive weights; their A^l is 0) still have a nonzero derivative with
+    respect to that weight: exp(s) / sum_kept A^{l-1} exp(s) times g. Pinned by
+    central differences of the forward oracle over every entry of A^{l-1}."""
+    win, shift, d, K_prev, K_l = 4, 2, 4, 11, 8
+    Q, K, V, I_prev, A_prev = case(1, 1, 8, 8, d, win, K_prev, 91)
+    g = np.random.Generator(np.random.PCG64(92))
+    zero = g.random(A_prev.shape) < 0.6
+    zero[..., 0] = False
+    A_prev[zero] = 0.0
+    r = oracle.layer(Q, K, V, win=win, shift=shift, K_l=K_l, I_prev=I_prev, A_prev=A_prev)
+    keep = r["I"]
+    dO = rnd(Q.shape, 93)
+    dA = rnd(keep.shape, 94)
+    b = oracle.layer_backward(Q, K, V, win=win, shift=shift, keep=keep, dO=dO, dA=dA, I_prev=I_prev, A_prev=A_prev)
+    grad = b["dA_prev"].reshape(A_prev.shape)
+    # kept slots with a zero weight exist and get nonzero gradients
+    flat_I = I_prev.reshape(-1, K_prev)
+    kept_mask = np.stack([np.isin(flat_I[n], keep.reshape(-1, K_l)[n]) for n in range(flat_I.shape[0])])
+    kz = kept_mask & zero.reshape(-1, K_prev)
+    assert kz.sum() > 20
+    assert (np.abs(grad.reshape(-1, K_prev)[kz]) > 1e-6).mean() > 0.9
+    args = dict(win=win, shift=shift, keep=keep, dO=dO, dA=dA)
+    h = 1e-6
+    fd = np.empty(A_prev.shape)
+    for idx in np.ndindex(A_prev.shape):
+        x0 = A_prev[idx]
+        A_prev[idx] = x0 + h
+        lp = loss_fn(Q, K, V, A_prev, I_prev, **args)
+        A_prev[idx] = x0 - h
+        lm = loss_fn(Q, K, V, A_prev, I_prev, **args)
+        A_prev[idx] = x0
+        fd[idx] = (lp - lm) / (2 * h)
+    err = np.abs(fd - grad).max()
+    assert err < 1e-6 * (1 + np.abs(grad).max()), err
+
+
 @pytest.mark.parametrize("win,shift,with_dA", [(4, 2, True), (4, 0, False), (0, 0, True)])
 def test_finite_differences(win, shift, with_dA):
     """Every gradient entry against a central difference of the forward oracle
