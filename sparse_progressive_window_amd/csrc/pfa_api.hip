@@ -329,8 +329,8 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
     if (workspace_bytes < n_wh(g) * g.N * ((int64_t)K_l + 1) * 4) return PFA_ERR_INVALID;
     if (K_l > 256) return PFA_ERR_UNSUPPORTED;
     if ((int64_t)g.N * K_l * 4 > 0x7FFFFFF0) return PFA_ERR_UNSUPPORTED;
-    const int parts = pfa::backward_scatter_parts(g.d, g.N, K_l);
-    if (parts == 0) return PFA_ERR_UNSUPPORTED;
+    if (!pfa::backward_dkv_sorted(shape->dtype, g.d, g.N, K_l) && !pfa::backward_dkv_mfma(g.d, g.N, K_l))
+        return PFA_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     pfa::BackwardArgs a;
@@ -350,8 +350,7 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
     a.blocks_per_wh = g.N >= 512 ? 2 : 1;
     a.rows_per_block = (g.N + a.blocks_per_wh - 1) / a.blocks_per_wh;
     const int64_t rgrid = n_wh(g) * a.blocks_per_wh;
-    const int64_t sgrid = n_wh(g) * parts;
-    if (rgrid > 0x7fffffff || sgrid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
+    if (rgrid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
     const int dt = shape->dtype;
     hipError_t e;
     if (pfa::backward_fused_rows(dt, g.d, g.N, K_l, dA_prev != nullptr)) {
@@ -368,17 +367,17 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
     if (e == hipSuccess) {
         pfa::BackwardArgs b = a;
         b.rows_per_block = g.N;
-        if (pfa::backward_dkv_mfma(g.d, g.N, K_l)) {
+        if (pfa::backward_dkv_sorted(dt, g.d, g.N, K_l)) {
+            b.blocks_per_wh = 1;
+            e = timed(PFA_KERNEL_BWD_SCATTER, s,
+                      [&] { return pfa::launch_backward_dkv_sorted(b, dt, g.d, (int)n_wh(g), s); });
+        } else {
             b.blocks_per_wh = 1;
             b.dkv_full = (int)pfa::backward_dkv_full(n_wh(g), g.N, compute_units());
             const int64_t dgrid64 = b.dkv_full + 2 * (n_wh(g) - b.dkv_full);
             if (dgrid64 > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
             const int dgrid = (int)dgrid64;
             e = timed(PFA_KERNEL_BWD_SCATTER, s, [&] { return pfa::launch_backward_dkv(b, dt, g.d, dgrid, s); });
-        } else {
-            b.blocks_per_wh = parts;
-            e = timed(PFA_KERNEL_BWD_SCATTER, s,
-                      [&] { return pfa::launch_backward_scatter(b, dt, g.d, (int)sgrid, s); });
         }
     }
     return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;

@@ -39,16 +39,17 @@
 //   scores themselves (s2 = s log2(e), k_j read from global memory), then
 //   dA^{l-1} = 2^{s2 - C} g at the flagged slots. Rare by construction; out of
 //   the row kernels, whose registers it would otherwise take.
-// * bwd_dkv_kernel (N a multiple of 16): dV = A^T dO and dK = (A g)^T Q / sqrt(d)
+// * bwd_dkv_kernel (N a multiple of 16, K_l > N / 16): dV = A^T dO and dK = (A g)^T Q / sqrt(d)
 //   as dense fp32 MFMA products over row blocks densified in LDS, the dV / dK
 //   tiles of each wave's tokens held in registers. At the densities of the keep
 //   schedule (K_l / N from 1/4 down to 1/64) this beats accumulating through
 //   LDS: on gfx950 an LDS fp32 atomic add retires at ~190 clocks per wavefront
 //   instruction and a compare-and-swap loop still costs tens.
-// * bwd_scatter_kernel (other N): dK and dV accumulate in LDS (fp32, DH of the
-//   d columns per workgroup) by compare-and-swap adds; each wave stages one
-//   row's (j, A, A g/sqrt(d)) in LDS and its lanes cover (64/DH kept slots) x
-//   DH columns per instruction.
+// * bwd_dkv_sorted_kernel (K_l <= N / 16, or N not a multiple of 16): the same
+//   products with work in proportion to the kept pairs: per row chunk the kept
+//   entries are counting-sorted by token in LDS and each token's owner thread
+//   sums its records (see the kernel). Deterministic: the sort is keyed by the
+//   row, not by arrival.
 #include <float.h>
 
 #include "pfa_kernels.h"
@@ -58,7 +59,6 @@ namespace pfa {
 namespace {
 
 constexpr int kBwdRowWaves = 16;
-constexpr int kBwdScatterWaves = 8;
 
 // sum over the CH consecutive lanes that share a kept slot (CH = 2, 4 or 8)
 template <int CH>
@@ -84,29 +84,6 @@ template <int GL>
 __device__ __forceinline__ uint64_t group_bits(uint64_t m, int lane) {
     if (GL == 64) return m;
     return (m >> (lane & (64 - GL))) & ((1ull << GL) - 1ull);
-}
-
-// Two fp32 adds into LDS words by compare-and-swap (ds_cmpst_rtn_b32): on gfx950
-// LDS fp32 atomic adds (ds_add_f32) retire at ~190 clocks per wavefront
-// instruction, 32-bit integer atomics at ~4.5. The lanes of one instruction
-// target distinct words, so a retry only follows an update by another wave.
-__device__ __forceinline__ void lds_add2(unsigned* a, float va, unsigned* b, float vb) {
-    unsigned oa = *a, ob = *b;
-    bool da = false, db = false;
-    do {
-        if (!da) {
-            unsigned e = oa;
-            da = __hip_atomic_compare_exchange_strong(a, &e, __float_as_uint(__uint_as_float(oa) + va),
-                                                      __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            oa = e;
-        }
-        if (!db) {
-            unsigned e = ob;
-            db = __hip_atomic_compare_exchange_strong(b, &e, __float_as_uint(__uint_as_float(ob) + vb),
-                                                      __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            ob = e;
-        }
-    } while (!(da && db));
 }
 
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
@@ -593,90 +570,6 @@ __global__ __launch_bounds__(4 * kWave) void bwd_exact_dap_kernel(const Backward
     }
 }
 
-template <typename T, int D, int DH>
-__global__ __launch_bounds__(kBwdScatterWaves * kWave) void bwd_scatter_kernel(const BackwardArgs p) {
-    constexpr int NW = kBwdScatterWaves;
-    constexpr int PPI = kWave / DH;         // kept slots per atomic instruction
-    extern __shared__ __align__(16) unsigned char smem[];
-
-    const Geom g = p.g;
-    const int N = g.N;
-    const int K_l = p.K_l;
-    const int KLP = (K_l + 3) & ~3;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const WhPart w = decode_block(p.blocks_per_wh, p.xcd_map, g);   // part = column block
-    const size_t plane = (size_t)w.bh * g.H * g.W * D;
-    const int col0 = w.part * DH;
-
-    float* accV = reinterpret_cast<float*>(smem);
-    float* accK = accV + N * DH;
-    int* st_j = reinterpret_cast<int*>(accK + N * DH) + wave * 3 * KLP;
-    float* st_a = reinterpret_cast<float*>(st_j + KLP);
-    float* st_k = st_a + KLP;
-    for (int u = threadIdx.x * 4; u < 2 * N * DH; u += blockDim.x * 4)
-        *reinterpret_cast<float4*>(accV + u) = make_float4(0.f, 0.f, 0.f, 0.f);
-    __syncthreads();
-
-    const size_t wh_pairs = (size_t)w.wh * N * K_l;
-    const int pair_bytes = N * K_l * 4;
-    const __amdgpu_buffer_rsrc_t rI = make_rsrc(p.I_l + wh_pairs, pair_bytes);
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A_l + wh_pairs, pair_bytes);
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g_buf + wh_pairs, pair_bytes);
-    const int c = lane % DH;
-    const int ps = lane / DH;
-    const T* Qh = static_cast<const T*>(p.Q) + plane;
-    for (int i = wave; i < N; i += NW) {
-        const int qpix = slot_pixel(g, w.wy, w.wx, i);
-        const float dov = p.dO[plane + (size_t)qpix * D + col0 + c];
-        float qv;
-        if constexpr (sizeof(T) == 4) {
-            qv = reinterpret_cast<const float*>(Qh)[(size_t)qpix * D + col0 + c];
-        } else {
-            qv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(Qh)[(size_t)qpix * D + col0 + c] << 16);
-        }
-        const int roff = i * K_l * 4;
-        for (int e = lane * 4; e < K_l; e += 4 * kWave) {
-            const uint4 j4 = load16(rI, roff + e * 4);
-            const uint4 a4 = load16(rA, roff + e * 4);
-            const uint4 g4 = load16(rg, roff + e * 4);
-            const float a[4] = {__uint_as_float(a4.x), __uint_as_float(a4.y), __uint_as_float(a4.z),
-                                __uint_as_float(a4.w)};
-            const float gg[4] = {__uint_as_float(g4.x), __uint_as_float(g4.y), __uint_as_float(g4.z),
-                                 __uint_as_float(g4.w)};
-            *reinterpret_cast<uint4*>(st_j + e) = j4;
-            *reinterpret_cast<float4*>(st_a + e) = make_float4(a[0], a[1], a[2], a[3]);
-            *reinterpret_cast<float4*>(st_k + e) = make_float4(a[0] * gg[0] * p.scale, a[1] * gg[1] * p.scale,
-                                                               a[2] * gg[2] * p.scale, a[3] * gg[3] * p.scale);
-        }
-        for (int e0 = 0; e0 < K_l; e0 += PPI) {
-            const int e = e0 + ps;
-            if (e < K_l) {
-                const int j = (int)min((unsigned)st_j[e], (unsigned)(N - 1));
-                lds_add2(reinterpret_cast<unsigned*>(accV + j * DH + c), st_a[e] * dov,
-                         reinterpret_cast<unsigned*>(accK + j * DH + c), st_k[e] * qv);
-            }
-        }
-    }
-    __syncthreads();
-    constexpr int C4 = DH / 4;
-    for (int u = threadIdx.x; u < N * C4; u += blockDim.x) {
-        const int t = u / C4;
-        const int cc = (u - t * C4) * 4;
-        const size_t o = plane + (size_t)slot_pixel(g, w.wy, w.wx, t) * D + col0 + cc;
-        *reinterpret_cast<float4*>(p.dV + o) = *reinterpret_cast<const float4*>(accV + t * DH + cc);
-        *reinterpret_cast<float4*>(p.dK + o) = *reinterpret_cast<const float4*>(accK + t * DH + cc);
-    }
-}
-
-// dV = A^T dO and dK = (A g / sqrt(d))^T Q for one window-head on fp32 MFMA
-// (v_mfma_f32_16x16x4_f32: exact products, fp32 accumulation). The kept rows are
-// densified in LDS, KB = 16 rows at a time (two [KB][N] fp32 planes: A and
-// A g / sqrt(d), zero off the kept slots), next to the block's dO and Q rows;
-// wave w owns tokens [16 MTW w, 16 MTW (w + 1)) and keeps their dV and dK tiles in
-// registers over all blocks, so nothing is accumulated through memory. The next
-// block's (j, A, g) entries are loaded into registers during the current block's
-// MFMAs; after the MFMAs the written slots are reset to zero.
 template <typename T, int D, int EPT, int MTW, bool SKIP>
 __global__ __launch_bounds__(16 * kWave) void bwd_dkv_kernel(const BackwardArgs p) {
     constexpr int KB = 16;                  // rows per block (4 MFMA k-steps)
@@ -859,6 +752,175 @@ __global__ __launch_bounds__(16 * kWave) void bwd_dkv_kernel(const BackwardArgs 
     }
 }
 
+// dK and dV with work in proportion to the kept pairs (any N <= 1024): one
+// workgroup per window-head, thread t owns token t and keeps its dV and dK rows
+// in registers. The window-head's rows are taken in chunks of R = 32 MW rows:
+//   (a) the chunk's dO and Q rows are staged in LDS (16-byte chunks permuted by
+//       row, so the owners' reads of random rows spread over the banks);
+//   (b) every kept entry (row r, token j) of the chunk sets bit r of token j's
+//       R-bit row mask (LDS or: no order dependence);
+//   (c) the masks' popcounts are scanned over the tokens (wave scans, then the
+//       wave totals), giving each token a segment of the record list;
+//   (d) entry (r, j) is written to its token's segment at the rank of r in j's
+//       mask: records come out sorted by token, then by row, whatever the
+//       scheduling, so the sums below always run in the same order;
+//   (e) each owner adds A dO_r to its dV row and A g / sqrt(d) q_r to its dK row
+//       over its segment.
+// Per chunk there are about R K_l / N records per token; the work of the owners
+// is K_l d MACs per row and matrix, not N d.
+template <typename T, int D, int MW>
+__global__ __launch_bounds__(16 * kWave) void bwd_dkv_sorted_kernel(const BackwardArgs p) {
+    constexpr int R = 32 * MW;                 // rows per chunk
+    constexpr int NT = 16 * kWave;             // threads (tokens owned: the first N)
+    constexpr int EPC = Chunk<T>::kElems;
+    constexpr int QCH = D / EPC;               // 16-byte chunks of a Q row
+    constexpr int OCH = D / 4;                 // 16-byte chunks of a dO row (fp32)
+    constexpr int QROWB = D * (int)sizeof(T);
+    constexpr int OROWB = D * 4;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const Geom g = p.g;
+    const int N = g.N;
+    const int K_l = p.K_l;
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int wave = t / kWave;
+    const WhPart w = decode_block(1, p.xcd_map, g);
+    const size_t plane = (size_t)w.bh * g.H * g.W * D;
+    const T* Qh = static_cast<const T*>(p.Q) + plane;
+    const float* dOh = p.dO + plane;
+
+    unsigned char* dOs = smem;                                        // [R][OROWB]
+    unsigned char* Qs = dOs + R * OROWB;                              // [R][QROWB]
+    uint32_t* mask = reinterpret_cast<uint32_t*>(Qs + R * QROWB);     // [MW][N]: word m of token j at m N + j
+    int* seg = reinterpret_cast<int*>(mask + N * MW);                 // [N] segment starts
+    int* wsum = seg + N;                                              // [16] wave totals
+    const size_t roff = ((size_t)(R * OROWB + R * QROWB + (N * MW + N + 16) * 4) + 7) & ~(size_t)7;
+    float2* recw = reinterpret_cast<float2*>(smem + roff);            // [R K_l] (A, A g / sqrt(d))
+    uint16_t* recr = reinterpret_cast<uint16_t*>(recw + R * K_l);     // [R K_l] row in the chunk
+
+    const size_t wh_pairs = (size_t)w.wh * N * K_l;
+    const int pair_bytes = N * K_l * 4;
+    const __amdgpu_buffer_rsrc_t rI = make_rsrc(p.I_l + wh_pairs, pair_bytes);
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A_l + wh_pairs, pair_bytes);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g_buf + wh_pairs, pair_bytes);
+
+    float accV[D], accK[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) accV[c] = accK[c] = 0.0f;
+    constexpr int EPT = 8192 / NT;   // entries per thread (the launcher keeps R K_l <= 8192)
+
+    if (t < N) {
+#pragma unroll
+        for (int m = 0; m < MW; ++m) mask[m * N + t] = 0u;   // (the owners clear them again after each chunk)
+    }
+    for (int r0 = 0; r0 < N; r0 += R) {
+        const int rows = min(R, N - r0);
+        const int ne = rows * K_l;
+        // (a) stage the chunk's rows; load its entries
+        for (int u = t; u < rows * OCH; u += NT) {
+            const int r = u / OCH, c = u - r * OCH;
+            *reinterpret_cast<float4*>(dOs + r * OROWB + ((c ^ (r & (OCH - 1))) * 16)) =
+                *reinterpret_cast<const float4*>(dOh + (size_t)slot_pixel(g, w.wy, w.wx, r0 + r) * D + c * 4);
+        }
+        for (int u = t; u < rows * QCH; u += NT) {
+            const int r = u / QCH, c = u - r * QCH;
+            *reinterpret_cast<uint4*>(Qs + r * QROWB + ((c ^ (r & (QCH - 1))) * 16)) = *reinterpret_cast<const uint4*>(
+                reinterpret_cast<const unsigned char*>(Qh + (size_t)slot_pixel(g, w.wy, w.wx, r0 + r) * D) + c * 16);
+        }
+        int ej[EPT];
+        float ea[EPT], ek[EPT];
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const int e = t + NT * u;
+            const int off = e < ne ? (r0 * K_l + e) * 4 : 0x7FFFFFF0;   // past the range: not loaded
+            ej[u] = (int)min((unsigned)__builtin_amdgcn_raw_buffer_load_b32(rI, off, 0, 0), (unsigned)(N - 1));
+            ea[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rA, off, 0, 0));
+            ek[u] = ea[u] * __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, off, 0, 0)) * p.scale;
+        }
+        __syncthreads();
+        // (b) row masks per token
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const int e = t + NT * u;
+            if (e < ne) {
+                const int r = e / K_l;
+                atomicOr(&mask[(r >> 5) * N + ej[u]], 1u << (r & 31));
+            }
+        }
+        __syncthreads();
+        // (c) segment of each token: exclusive scan of the mask popcounts
+        int cnt = 0;
+        if (t < N) {
+#pragma unroll
+            for (int m = 0; m < MW; ++m) cnt += __builtin_popcount(mask[m * N + t]);
+        }
+        int incl = cnt;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        if (lane == kWave - 1) wsum[wave] = incl;
+        __syncthreads();
+        int base = 0;
+        for (int v = 0; v < wave; ++v) base += wsum[v];
+        const int st = base + incl - cnt;
+        if (t < N) seg[t] = st;
+        __syncthreads();
+        // (d) records at the rank of their row in the token's mask
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const int e = t + NT * u;
+            if (e < ne) {
+                const int r = e / K_l;
+                const uint32_t* mj = mask + ej[u];
+                int rank = __builtin_popcount(mj[(r >> 5) * N] & ((1u << (r & 31)) - 1u));
+#pragma unroll
+                for (int m = 0; m < MW; ++m)
+                    if (m < (r >> 5)) rank += __builtin_popcount(mj[m * N]);
+                const int pos = seg[ej[u]] + rank;
+                recw[pos] = make_float2(ea[u], ek[u]);
+                recr[pos] = (uint16_t)r;
+            }
+        }
+        __syncthreads();
+        // (e) owners: their segment in row order; their masks are cleared for the next chunk
+        if (t < N) {
+#pragma unroll
+            for (int m = 0; m < MW; ++m) mask[m * N + t] = 0u;
+        }
+        for (int k = st; k < st + cnt; ++k) {
+            const float2 wv = recw[k];
+            const int r = recr[k];
+#pragma unroll
+            for (int c = 0; c < OCH; ++c) {
+                const float4 o4 = *reinterpret_cast<const float4*>(dOs + r * OROWB + ((c ^ (r & (OCH - 1))) * 16));
+                accV[4 * c + 0] = fmaf(wv.x, o4.x, accV[4 * c + 0]);
+                accV[4 * c + 1] = fmaf(wv.x, o4.y, accV[4 * c + 1]);
+                accV[4 * c + 2] = fmaf(wv.x, o4.z, accV[4 * c + 2]);
+                accV[4 * c + 3] = fmaf(wv.x, o4.w, accV[4 * c + 3]);
+            }
+#pragma unroll
+            for (int c = 0; c < QCH; ++c) {
+                float qf[EPC];
+                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(Qs + r * QROWB + ((c ^ (r & (QCH - 1))) * 16)), qf);
+#pragma unroll
+                for (int y = 0; y < EPC; ++y) accK[EPC * c + y] = fmaf(wv.y, qf[y], accK[EPC * c + y]);
+            }
+        }
+        __syncthreads();   // the next chunk reuses the LDS
+    }
+    if (t < N) {
+        const size_t o = plane + (size_t)slot_pixel(g, w.wy, w.wx, t) * D;
+#pragma unroll
+        for (int c = 0; c < D; c += 4) {
+            *reinterpret_cast<float4*>(p.dV + o + c) = make_float4(accV[c], accV[c + 1], accV[c + 2], accV[c + 3]);
+            *reinterpret_cast<float4*>(p.dK + o + c) = make_float4(accK[c], accK[c + 1], accK[c + 2], accK[c + 3]);
+        }
+    }
+}
+
 template <class F>
 hipError_t launch_bwd(F fn, const BackwardArgs& a, int threads, int lds, int grid, hipStream_t s) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -909,8 +971,39 @@ hipError_t launch_rows_t(const BackwardArgs& a, bool has_v, bool has_k, int grid
     return launch_rows_mode<T, D, false, true>(a, grid, s);
 }
 
-int scatter_lds(int DH, int N, int K_l) {
-    return 2 * N * DH * 4 + kBwdScatterWaves * 3 * ((K_l + 3) & ~3) * 4;
+// rows per chunk of the sorted dK/dV kernel: the largest of 32, 64, 128, 256 rows
+// (at most N rounded up to 32) whose LDS (staged rows, token masks, records) fits
+int sorted_rows(int dtype, int D, int N, int K_l) {
+    if (N > 1024 || K_l > 256) return 0;
+    const int rowb = D * 4 + D * (dtype == 0 ? 4 : 2);
+    int best = 0;
+    for (int R = 32; R <= 256; R *= 2) {
+        if (R * K_l > 8192) break;
+        const int mw = R / 32;
+        const int lds = R * rowb + (N * mw + N + 16) * 4 + 8 + R * K_l * 10;
+        if (lds <= kLdsBytes) best = R;
+        if (R >= N) break;
+    }
+    return best;
+}
+
+int sorted_lds(int dtype, int D, int N, int K_l, int R) {
+    const int rowb = D * 4 + D * (dtype == 0 ? 4 : 2);
+    return R * rowb + (N * (R / 32) + N + 16) * 4 + 8 + R * K_l * 10;
+}
+
+template <typename T, int D>
+hipError_t launch_sorted_t(const BackwardArgs& a, int grid, hipStream_t s) {
+    const int R = sorted_rows(sizeof(T) == 4 ? 0 : 1, D, a.g.N, a.K_l);
+    const int lds = sorted_lds(sizeof(T) == 4 ? 0 : 1, D, a.g.N, a.K_l, R);
+    const int th = 16 * kWave;
+    switch (R) {
+        case 32: return launch_bwd(bwd_dkv_sorted_kernel<T, D, 1>, a, th, lds, grid, s);
+        case 64: return launch_bwd(bwd_dkv_sorted_kernel<T, D, 2>, a, th, lds, grid, s);
+        case 128: return launch_bwd(bwd_dkv_sorted_kernel<T, D, 4>, a, th, lds, grid, s);
+        case 256: return launch_bwd(bwd_dkv_sorted_kernel<T, D, 8>, a, th, lds, grid, s);
+        default: return hipErrorInvalidValue;   // rejected by backward_dkv_sorted
+    }
 }
 
 int dkv_lds(int D, int N) { return (2 * 16 * (N + 16) + 2 * 16 * (D == 32 ? 48 : 16)) * 4; }
@@ -950,16 +1043,6 @@ hipError_t launch_dkv_t(const BackwardArgs& a, int grid, hipStream_t s) {
     return hipErrorInvalidValue;   // K_l beyond what the caller admits
 }
 
-template <typename T, int D>
-hipError_t launch_scatter_t(const BackwardArgs& a, int grid, hipStream_t s) {
-    const int th = kBwdScatterWaves * kWave;
-    if (a.blocks_per_wh == 1)
-        return launch_bwd(bwd_scatter_kernel<T, D, D>, a, th, scatter_lds(D, a.g.N, a.K_l), grid, s);
-    if (a.blocks_per_wh == 2)
-        return launch_bwd(bwd_scatter_kernel<T, D, D / 2>, a, th, scatter_lds(D / 2, a.g.N, a.K_l), grid, s);
-    return launch_bwd(bwd_scatter_kernel<T, D, D / 4>, a, th, scatter_lds(D / 4, a.g.N, a.K_l), grid, s);
-}
-
 }  // namespace
 
 int backward_fused_rows(int dtype, int D, int N, int K_l, bool want_dap) {
@@ -969,6 +1052,23 @@ int backward_fused_rows(int dtype, int D, int N, int K_l, bool want_dap) {
     const int per_lane = 4 * ((K_l + 4 * (64 / CH) - 1) / (4 * (64 / CH)));
     if (per_lane > 16) return 0;
     return rows_lds(dtype, D, N, K_l, true, true, want_dap) <= kLdsBytes ? 1 : 0;
+}
+
+bool backward_dkv_sorted(int dtype, int D, int N, int K_l) {
+    // measured on the MI355X (fp32 and bf16, N = 1024): per window-head about 90 us of
+    // fixed cost (chunk loads and barriers, one workgroup per CU) plus 2.5 us per kept
+    // slot of a row; the dense MFMA form costs about N^2 whatever K_l. The sorted form
+    // wins from K_l = N / 16 down (0.66 against 1.53 ms at K_l = 16 on the 640x384 map,
+    // 1.48 against 1.87 at K_l = 64, 4.0 against 2.2 at K_l = 256), and it is the only
+    // form for N not a multiple of 16 when it fits
+    if (sorted_rows(dtype, D, N, K_l) == 0) return false;
+    return 16 * K_l <= N || !backward_dkv_mfma(D, N, K_l);
+}
+
+hipError_t launch_backward_dkv_sorted(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream) {
+    if (dtype == 0)
+        return D == 16 ? launch_sorted_t<float, 16>(a, grid, stream) : launch_sorted_t<float, 32>(a, grid, stream);
+    return D == 16 ? launch_sorted_t<uint16_t, 16>(a, grid, stream) : launch_sorted_t<uint16_t, 32>(a, grid, stream);
 }
 
 bool backward_dkv_mfma(int D, int N, int K_l) {
@@ -991,12 +1091,6 @@ hipError_t launch_backward_dkv(const BackwardArgs& a, int dtype, int D, int grid
     return D == 16 ? launch_dkv_t<uint16_t, 16>(a, grid, stream) : launch_dkv_t<uint16_t, 32>(a, grid, stream);
 }
 
-int backward_scatter_parts(int D, int N, int K_l) {
-    for (int parts = 1; parts <= 4; parts *= 2)
-        if (scatter_lds(D / parts, N, K_l) <= kLdsBytes) return parts;
-    return 0;
-}
-
 hipError_t launch_backward_rows(const BackwardArgs& a, int dtype, int D, bool has_v, bool has_k, int grid,
                                 hipStream_t stream) {
     if (rows_lds(dtype, D, a.g.N, a.K_l, has_v, has_k, a.dA_prev != nullptr) > kLdsBytes) return hipErrorInvalidValue;
@@ -1015,12 +1109,6 @@ hipError_t launch_backward_exact_dap(const BackwardArgs& a, int dtype, int D, in
     };
     if (dtype == 0) return D == 16 ? go(bwd_exact_dap_kernel<float, 16>) : go(bwd_exact_dap_kernel<float, 32>);
     return D == 16 ? go(bwd_exact_dap_kernel<uint16_t, 16>) : go(bwd_exact_dap_kernel<uint16_t, 32>);
-}
-
-hipError_t launch_backward_scatter(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream) {
-    if (dtype == 0)
-        return D == 16 ? launch_scatter_t<float, 16>(a, grid, stream) : launch_scatter_t<float, 32>(a, grid, stream);
-    return D == 16 ? launch_scatter_t<uint16_t, 16>(a, grid, stream) : launch_scatter_t<uint16_t, 32>(a, grid, stream);
 }
 
 }  // namespace pfa

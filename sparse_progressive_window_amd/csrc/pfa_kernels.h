@@ -92,15 +92,16 @@ hipError_t launch_backward_rows(const BackwardArgs& a, int dtype, int D, bool ha
                                 hipStream_t stream);
 // dA^{l-1} of the rows the row pass flagged, from the scores (after the row pass).
 hipError_t launch_backward_exact_dap(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream);
+// dK and dV from the kept pairs sorted by token per row chunk (work in proportion
+// to K_l); one workgroup per window-head.
+bool backward_dkv_sorted(int dtype, int D, int N, int K_l);
+hipError_t launch_backward_dkv_sorted(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream);
 // dK and dV as dense MFMA products over LDS-densified row blocks (N % 16 == 0).
 bool backward_dkv_mfma(int D, int N, int K_l);
 // whole-window-head dK/dV workgroups for n_wh window-heads on `cus` compute units
 // (n_wh when no split applies); the grid is dkv_full + 2 (n_wh - dkv_full)
 int64_t backward_dkv_full(int64_t n_wh, int N, int cus);
 hipError_t launch_backward_dkv(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream);
-// dK and dV otherwise: per window-head LDS accumulators, D/parts columns per workgroup.
-int backward_scatter_parts(int D, int N, int K_l);
-hipError_t launch_backward_scatter(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream);
 
 // Backward pass of the dense first layer.
 struct DenseBwdArgs {

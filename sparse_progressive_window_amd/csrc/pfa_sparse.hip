@@ -760,25 +760,27 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
 template <typename T>
 struct Mfma4;
 
+// chunk(a, b, c): c += the products of one 16-byte chunk of a query row (a) and
+// of a K row (b), as they sit in memory
 template <>
 struct Mfma4<float> {
-    static constexpr int kK = 1;   // contraction per instruction
-    __device__ static v4f run(const float* a, const float* b, v4f c) {
-        return __builtin_amdgcn_mfma_f32_4x4x1f32(a[0], b[0], c, 0, 0, 0);
+    __device__ static v4f chunk(const uint4 a, const uint4 b, v4f c) {
+        c = __builtin_amdgcn_mfma_f32_4x4x1f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_4x4x1f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_4x4x1f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_4x4x1f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
     }
 };
 
 template <>
 struct Mfma4<uint16_t> {
-    static constexpr int kK = 4;
-    __device__ static v4f run(const float* a, const float* b, v4f c) {
-        v4s x, y;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            x[e] = (short)(__float_as_uint(a[e]) >> 16);   // exact: the values are bf16
-            y[e] = (short)(__float_as_uint(b[e]) >> 16);
-        }
-        return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(x, y, c, 0, 0, 0);
+    // a 16-byte chunk holds 8 bf16 values: two operands of 4 for 4x4x4 (element e
+    // of an operand is bits 16e..16e+15 of the pair of dwords, as in memory)
+    __device__ static v4f chunk(const uint4 a, const uint4 b, v4f c) {
+        c = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(v4s, make_uint2(a.x, a.y)),
+                                                   __builtin_bit_cast(v4s, make_uint2(b.x, b.y)), c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(v4s, make_uint2(a.z, a.w)),
+                                                      __builtin_bit_cast(v4s, make_uint2(b.z, b.w)), c, 0, 0, 0);
     }
 };
 
@@ -815,7 +817,6 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
     constexpr bool SWZ = CH == 8 || CH == 4;   // 128- and 64-byte rows: chunk-swizzled, unpadded
     constexpr int NK = DUAL ? 2 : 1;            // K regions in LDS
     constexpr int KSTR = SWZ ? ROWB : ROWB + 16;
-    constexpr int KK = Mfma4<T>::kK;
     constexpr int HISTG = BPL * GL;       // the level results reuse words 0..2
     extern __shared__ __align__(16) unsigned char smem[];
 
@@ -888,17 +889,23 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
             const unsigned char* qrow = reinterpret_cast<const unsigned char*>(
                 (first ? Q1h : Qh) + (size_t)slot_pixel(first ? g1 : g, w.wy, w.wx, qi) * D);
             const unsigned char* kr0 = Ks + (first ? N * KSTR : 0) + lv * KSTR;
+            uint4 qc[CH];
 #pragma unroll
-            for (int m = 0; m < CH; ++m) {
-                float qv[EPC];
-                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(qrow + 16 * m), qv);
-                const int koff = (SWZ ? (m ^ kswz<CH>(lv)) : m) * 16;
+            for (int m = 0; m < CH; ++m) qc[m] = *reinterpret_cast<const uint4*>(qrow + 16 * m);
+            // tiles in groups of TG (TG independent accumulator chains), contraction chunk
+            // inner: at most TG x CH K chunks in flight. TG = 4 leaves the single-set
+            // kernels without spills (16 spilled up to 5 dwords); the fused kernel, with
+            // the second layer's query also live, spills least with TG = 16
+            constexpr int TG = DUAL ? 16 : 4;
 #pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    float kf[EPC];
-                    Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(kr0 + kWave * t * KSTR + koff), kf);
+            for (int t0 = 0; t0 < 16; t0 += TG) {
 #pragma unroll
-                    for (int e = 0; e < EPC; e += KK) acc[t] = Mfma4<T>::run(&qv[e], &kf[e], acc[t]);
+                for (int m = 0; m < CH; ++m) {
+                    const int koff = (SWZ ? (m ^ kswz<CH>(lv)) : m) * 16;
+#pragma unroll
+                    for (int t = t0; t < t0 + TG; ++t)
+                        acc[t] = Mfma4<T>::chunk(qc[m], *reinterpret_cast<const uint4*>(kr0 + kWave * t * KSTR + koff),
+                                                 acc[t]);
                 }
             }
         }

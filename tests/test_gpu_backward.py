@@ -200,7 +200,7 @@ def test_backward_kernel_timing_records():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,layers", [(workloads.PATCH64.name, (1, 2)), (workloads.MAP256.name, (1, 2))])
+@pytest.mark.parametrize("name,layers", [(workloads.PATCH64.name, (1, 2, 4, 5)), (workloads.MAP256.name, (1, 2, 4, 5))])
 def test_backward_full_size(name, layers, capsys):
     """Full-size workload, every window-head on the GPU; 12 sampled window-heads
     carry the oracle chain's maps (previous map and the layer's I^l, A^l), the
