@@ -1216,7 +1216,7 @@ hipError_t launch_fn(F fn, const SparseArgs& a, int threads, int lds, int grid, 
 
 template <typename T, int D, int GL, int KPT, int MODE>
 hipError_t launch_one(const SparseArgs& a, int lds, int grid, hipStream_t s) {
-    constexpr int NW = (KPT <= 4 || (MODE == kKselect && KPT <= 8)) ? 16 : 8;
+    constexpr int NW = (KPT <= 4 || (MODE == kKselect && (KPT <= 8 || (KPT <= 16 && sizeof(T) == 2)))) ? 16 : 8;
     constexpr bool PQ = KPT <= 4 && D * sizeof(T) <= 64;   // prefetch q when registers allow
     if constexpr (MODE == kKselect) {
         if (a.bias) {
@@ -1250,6 +1250,10 @@ hipError_t launch_shape(const SparseArgs& a, SparseMode mode, int lds, int grid,
         if (kp <= 32) return launch_one<T, D, 16, 2, kKselect>(a, lds, grid, s);
         if (kp <= 64) return launch_one<T, D, 16, 4, kKselect>(a, lds, grid, s);
         if (kp <= 128) return launch_one<T, D, 16, 8, kKselect>(a, lds, grid, s);
+        // K_prev <= 256: bf16 takes 4 rows of 16 candidates per lane per wavefront
+        // (more independent gathers in flight per wave); fp32 2 rows of 8 (16 would not
+        // fit the 128 VGPRs of 16-wave workgroups)
+        if constexpr (sizeof(T) == 2) return launch_one<T, D, 16, 16, kKselect>(a, lds, grid, s);
         return launch_one<T, D, 32, 8, kKselect>(a, lds, grid, s);
     }
     if (kp <= 16) return launch_mode<T, D, 16, 1>(a, mode, lds, grid, s);
