@@ -44,10 +44,9 @@ def check_layer(*, gpu_I, gpu_A, gpu_O, ref, cand, wh_list, tol, rerun, O_ref=No
     if cand is None:
         assert (np.diff(Ig, axis=-1) > 0).all(), "kept indices not in ascending slot order"
     else:
-        for n in range(n_sel):
-            eq = Ig[n][:, :, None] == cand[n][:, None, :]
-            assert eq.any(-1).all(), "GPU kept an index that is not a candidate"
-            assert (np.diff(eq.argmax(-1), axis=-1) > 0).all(), "kept entries not in candidate-list order"
+        slot = candidate_slots(Ig, cand)
+        assert (slot >= 0).all(), "GPU kept an index that is not a candidate"
+        assert (np.diff(slot, axis=-1) > 0).all(), "kept entries not in candidate-list order"
 
     # near-tie rows: every differing index must be within the gap of the K_l-th key
     if len(tie_rows):
@@ -74,6 +73,26 @@ def check_layer(*, gpu_I, gpu_A, gpu_O, ref, cand, wh_list, tol, rerun, O_ref=No
     O_ref = ref["O"] if O_ref is None else O_ref
     stats.update(check_O(gpu_O, O_ref, tol))
     return stats
+
+
+def candidate_slots(I, cand):
+    """Slot of each I[..., k] in its row's candidate list cand[..., :] (distinct
+    entries per row), -1 where it is not a candidate. One global binary search:
+    each row's values are offset by row * (max value + 1) so that the sorted
+    rows concatenate into one sorted array."""
+    I = np.asarray(I, dtype=np.int64)
+    C = np.asarray(cand, dtype=np.int64)
+    R, Kc, Kl = int(np.prod(C.shape[:-1])), C.shape[-1], I.shape[-1]
+    span = int(max(C.max(initial=0), I.max(initial=0))) + 1
+    off = (np.arange(R, dtype=np.int64) * span)[:, None]
+    c = C.reshape(R, Kc) + off
+    order = np.argsort(c, axis=-1, kind="stable")
+    cs = np.take_along_axis(c, order, axis=-1).ravel()
+    g = (I.reshape(R, Kl) + off).ravel()
+    p = np.minimum(np.searchsorted(cs, g), cs.size - 1)
+    found = (cs[p] == g) & (I.reshape(-1) >= 0)
+    slot = np.where(found, order.ravel()[p], -1)
+    return slot.reshape(I.shape)
 
 
 def check_O(gpu_O, O_ref, tol):
