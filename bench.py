@@ -38,7 +38,7 @@ HEADLINE = "map640x384_h6_d32_bf16_6blocks"
 
 # kernel kinds of the library's timing calls (pfa_kernel_kind)
 (DENSE, ALL_CAND, SPARSE, SELECT, AGGREGATE, IOTA, BWD_ROWS, BWD_SCATTER, IET_RANK, IET_UNION, DENSE_BWD,
- BWD_EXACT) = range(12)
+ BWD_EXACT, DBIAS) = range(13)
 
 
 def kernel_bytes(w, l, kind, i_prev_implicit, split, fused=False):

@@ -169,7 +169,42 @@ int pfa_first_two_layers(const pfa_shape* shape, int32_t shift1, int32_t shift2,
                          float* O2_out, void* stream);
 
 /*
- * Backward pass of a window-mode sparse layer ("Progressive attention across
+ * Backward pass of the first two layers computed by pfa_first_two_layers, which
+ * never writes the first layer's map A^1. Gives what pfa_sparse_layer_backward
+ * (I_prev = NULL, A_prev = A^1) followed by pfa_dense_layer_backward (dA = that
+ * call's dA_prev) give for the unfused pair: A^1 is recomputed at the second
+ * layer's kept slots only, from Q1, K1 and lse1 (A^1_ij = exp(s1_ij - lse1_i)).
+ *
+ * shape, shift1, shift2, Q1..V2, K2_keep  as the forward call (window mode;
+ *         shape->shift must be 0).
+ * lse1    [B, heads, nwin, N] fp32: the forward's lse1_out.
+ * I2, A2  [B, heads, nwin, N, K2_keep]: the forward's I2_out, A2_out.
+ * dO1, dO2  [B, heads, H, W, d] fp32 gradients of O1 and O2.
+ * dA2     [B, heads, nwin, N, K2_keep] fp32 gradient of A2, or NULL (zero).
+ * dQ1..dV2  [B, heads, H, W, d] fp32 outputs, every element written.
+ * workspace  at least pfa_first_two_layers_backward_workspace() bytes: two
+ *         [N, N] fp32 maps per window-head (A^1 at the kept slots, dA^1), then
+ *         the two single-layer passes' workspaces.
+ * Deterministic, as the single-layer calls.
+ * Errors: PFA_ERR_INVALID for NULL required pointers, shifts outside [0, win),
+ * shape->shift != 0, K2_keep outside [1, N], a small workspace;
+ * PFA_ERR_UNSUPPORTED for global mode, win % 8 != 0, K2_keep > 256, and the
+ * limits of the single-layer backward calls.
+ */
+int pfa_first_two_layers_backward(const pfa_shape* shape, int32_t shift1, int32_t shift2, const void* Q1,
+                                  const void* K1, const void* V1, const void* Q2, const void* K2, const void* V2,
+                                  int32_t K2_keep, const float* lse1, const int32_t* I2, const float* A2,
+                                  const float* dO1, const float* dO2, const float* dA2, float* dQ1, float* dK1,
+                                  float* dV1, float* dQ2, float* dK2, float* dV2, void* workspace,
+                                  int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes pfa_first_two_layers_backward needs, or a negative error code
+ * (shape errors, PFA_ERR_UNSUPPORTED for global mode, PFA_ERR_INVALID for K2_keep
+ * outside [1, N]). Host only. */
+int64_t pfa_first_two_layers_backward_workspace(const pfa_shape* shape, int32_t K2_keep);
+
+/*
+ * Backward pass of a sparse layer ("Progressive attention across
  * layers" and "Sparse matrix multiplication": the layer is differentiated
  * through its renormalisation, the Hadamard product with A^{l-1}, the softmax
  * and the two sparse products; the kept sets I^l are constants, as top-K is
@@ -183,8 +218,11 @@ int pfa_first_two_layers(const pfa_shape* shape, int32_t shift1, int32_t shift2,
  *                (j' kept; = A_ij g_ij / A_prev_ij where A_prev_ij > 0), 0 at
  *                dropped ones; s_ij = q_i.k_j / sqrt(d)
  *
- * Q, K, V, I_prev, A_prev, K_prev, K_l  the forward call's arguments (window
- *         mode, one index matrix per head; I_prev NULL = every slot, K_prev = N).
+ * Q, K, V, I_prev, A_prev, K_prev, K_l  the forward call's arguments, one index
+ *         matrix per head (I_prev NULL = every slot, K_prev = N). Window mode, or
+ *         global mode (shape->win = 0, tokens = raster pixels; the individualized
+ *         layer of "From Local Windows to Adaptive Candidates via Individualized
+ *         Exploratory": a list shared by the heads is passed once per head).
  * I_l, A_l  [B, heads, nwin, N, K_l] the forward call's outputs I^l, A^l.
  *         I_l must be a subsequence of I_prev in I_prev's order (what
  *         pfa_sparse_layer and pfa_dense_layer write).
@@ -202,7 +240,8 @@ int pfa_first_two_layers(const pfa_shape* shape, int32_t shift1, int32_t shift2,
  * (by row, whatever the scheduling).
  * Errors: PFA_ERR_INVALID for NULL required pointers, inconsistent sizes,
  * dA_prev without A_prev, a workspace that is too small; PFA_ERR_UNSUPPORTED
- * for global mode, K_l > 256, and the shape limits of pfa_sparse_layer.
+ * for K_l > 256, global mode with more than 2^22 tokens (8192 with dA_prev),
+ * and the shape limits of pfa_sparse_layer.
  */
 int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void* K, const void* V,
                               const int32_t* I_prev, const float* A_prev, int32_t K_prev, int32_t K_l,
@@ -214,6 +253,37 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
  * negative error code (PFA_ERR_INVALID / PFA_ERR_UNSUPPORTED as for the shape,
  * PFA_ERR_INVALID for K_l outside [1, N]). Host only, no device work. */
 int64_t pfa_sparse_layer_backward_workspace(const pfa_shape* shape, int32_t K_l);
+
+/*
+ * Backward pass of a sparse layer computed with a relative position bias
+ * (pfa_sparse_layer_rpb; the bias table is the score term of "Progressive Focused
+ * Transformer", which the notes describe as relative position bias based). The
+ * bias enters s_ij only, so dQ, dK, dV and dA_prev are those of
+ * pfa_sparse_layer_backward (s_ij includes the bias where dA_prev needs the
+ * scores), and the bias gradient is the sum of the score gradients over every kept
+ * pair of the head with the table entry's offset, across images and windows:
+ *   dbias[h][rel(i, j)] = sum over (b, window, i, kept j) of A_ij g_ij.
+ *
+ * bias    [heads, (2 win - 1)^2] fp32 device table of the forward call, or NULL.
+ * dbias   [heads, (2 win - 1)^2] fp32 output (every element written), or NULL (not
+ *         computed). Requires bias.
+ * workspace  at least pfa_sparse_layer_backward_rpb_workspace() bytes (that of
+ *         pfa_sparse_layer_backward, then one table per window-head).
+ * Other arguments as pfa_sparse_layer_backward. dbias is summed in a fixed order
+ * (no atomics): the same on every run.
+ * Errors: as pfa_sparse_layer_backward, PFA_ERR_INVALID for dbias without bias,
+ * PFA_ERR_UNSUPPORTED for a bias in global mode.
+ */
+int pfa_sparse_layer_backward_rpb(const pfa_shape* shape, const void* Q, const void* K, const void* V,
+                                  const float* bias, const int32_t* I_prev, const float* A_prev, int32_t K_prev,
+                                  int32_t K_l, const int32_t* I_l, const float* A_l, const float* dO,
+                                  const float* dA_l, float* dQ, float* dK, float* dV, float* dA_prev, float* dbias,
+                                  void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes pfa_sparse_layer_backward_rpb needs (with dbias), or a negative
+ * error code as pfa_sparse_layer_backward_workspace (and PFA_ERR_UNSUPPORTED for
+ * global mode). Host only. */
+int64_t pfa_sparse_layer_backward_rpb_workspace(const pfa_shape* shape, int32_t K_l);
 
 /*
  * Backward pass of the dense first layer (window mode): softmax attention over
@@ -242,6 +312,31 @@ int pfa_dense_layer_backward(const pfa_shape* shape, const void* Q, const void* 
 
 /* Workspace bytes pfa_dense_layer_backward needs, or a negative shape error. Host only. */
 int64_t pfa_dense_layer_backward_workspace(const pfa_shape* shape);
+
+/*
+ * pfa_dense_layer_backward with the gradient of the relative position bias table
+ * (see pfa_sparse_layer_backward_rpb): dS_ij = P_ij (G_ij - D_i) summed over every
+ * pair of the head with the entry's offset, across images and windows,
+ *   dbias[h][rel(i, j)] = sum over (b, window, i, j) of dS_ij.
+ *
+ * dbias   [heads, (2 win - 1)^2] fp32 output (every element written), or NULL
+ *         (then the call is pfa_dense_layer_backward). Requires bias.
+ * workspace  at least pfa_dense_layer_backward_rpb_workspace() bytes: one fp32 per
+ *         query slot, then, with dbias, 4 win KiB per 16 query slots (per key row
+ *         and 16-query block, the sums per column offset) and one table per
+ *         window-head.
+ * Other arguments, limits and errors as pfa_dense_layer_backward, and
+ * PFA_ERR_INVALID for dbias without bias. Deterministic: every sum of dbias runs
+ * in a fixed order.
+ */
+int pfa_dense_layer_backward_rpb(const pfa_shape* shape, const void* Q, const void* K, const void* V,
+                                 const float* bias, const float* lse, const float* dO, const float* dA, float* dQ,
+                                 float* dK, float* dV, float* dbias, void* workspace, int64_t workspace_bytes,
+                                 void* stream);
+
+/* Workspace bytes pfa_dense_layer_backward_rpb needs with dbias, or a negative
+ * shape error (PFA_ERR_UNSUPPORTED for global mode). Host only. */
+int64_t pfa_dense_layer_backward_rpb_workspace(const pfa_shape* shape);
 
 /*
  * pfa_dense_layer_backward without a workspace argument, for callers that cannot
@@ -324,8 +419,13 @@ typedef enum {
     PFA_KERNEL_IET_UNION = 9,      /* index propagation: de-duplicated union per row */
     PFA_KERNEL_DENSE_BWD = 10,     /* backward of the dense layer ("dense_bwd_dq_kernel" then
                                       "dense_bwd_dkv_kernel", one record for both) */
-    PFA_KERNEL_BWD_EXACT = 11      /* backward with dA_prev: rows whose kept weights include zero or
+    PFA_KERNEL_BWD_EXACT = 11,     /* backward with dA_prev: rows whose kept weights include zero or
                                       subnormal values, dA_prev from the scores */
+    PFA_KERNEL_DBIAS = 12,         /* backward with a bias gradient: per window-head tables
+                                      ("dbias_sparse_wh_kernel" or "dbias_dense_fold_kernel") then
+                                      "dbias_reduce_kernel", one record for both */
+    PFA_KERNEL_FIRST_MAP = 13      /* backward of the fused first two layers: the first layer's map at
+                                      the second layer's kept slots */
 } pfa_kernel_kind;
 
 /* capacity > 0: create 2*capacity events and start recording (earlier records

@@ -152,7 +152,26 @@ int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const voi
 
 int run_dense_backward(const Geom& g, int dtype, const void* Q, const void* K, const void* V, const float* bias,
                        const float* lse, const float* dO, const float* dA, float* dQ, float* dK, float* dV,
-                       float* Dws, hipStream_t s);
+                       float* Dws, hipStream_t s, float* dbias_rows = nullptr);
+int run_sparse_backward(const pfa_shape* shape, const void* Q, const void* K, const void* V, const float* bias,
+                        const int32_t* I_prev, const float* A_prev, int32_t K_prev, int32_t K_l, const int32_t* I_l,
+                        const float* A_l, const float* dO, const float* dA_l, float* dQ, float* dK, float* dV,
+                        float* dA_prev, float* dbias, void* workspace, int64_t workspace_bytes, hipStream_t s);
+
+// workspace bytes: the sparse backward's g per kept pair and flag per row
+int64_t sparse_bwd_ws(const Geom& g, int K_l) { return n_wh(g) * g.N * ((int64_t)K_l + 1) * 4; }
+// per window-head bias-gradient tables
+int64_t dbias_part_ws(const Geom& g) {
+    const int64_t wrow = 2 * (int64_t)g.win - 1;
+    return n_wh(g) * wrow * wrow * 4;
+}
+// the dense dQ kernel's per-wave rows of diagonal sums: [wh, N / 16, win, 64]
+int64_t dense_dbias_rows_ws(const Geom& g) { return n_wh(g) * (g.N / 16) * (int64_t)g.win * 64 * 4; }
+// backward of the fused first two layers: A^1 at the kept slots and dA^1 ([wh, N, N]
+// each), the sparse backward's workspace, the dense backward's (one fp32 per row)
+int64_t fused_bwd_ws(const Geom& g, int K2) {
+    return 2 * n_wh(g) * g.N * (int64_t)g.N * 4 + sparse_bwd_ws(g, K2) + n_wh(g) * g.N * 4;
+}
 
 }  // namespace
 
@@ -305,12 +324,83 @@ int pfa_first_two_layers(const pfa_shape* shape, int32_t shift1, int32_t shift2,
     return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
 }
 
+int64_t pfa_first_two_layers_backward_workspace(const pfa_shape* shape, int32_t K2_keep) {
+    Geom g;
+    int code;
+    if (!geom_from_shape(shape, &g, &code)) return code;
+    if (g.win == 0) return PFA_ERR_UNSUPPORTED;
+    if (K2_keep < 1 || K2_keep > g.N) return PFA_ERR_INVALID;
+    return fused_bwd_ws(g, K2_keep);
+}
+
+int pfa_first_two_layers_backward(const pfa_shape* shape, int32_t shift1, int32_t shift2, const void* Q1,
+                                  const void* K1, const void* V1, const void* Q2, const void* K2, const void* V2,
+                                  int32_t K2_keep, const float* lse1, const int32_t* I2, const float* A2,
+                                  const float* dO1, const float* dO2, const float* dA2, float* dQ1, float* dK1,
+                                  float* dV1, float* dQ2, float* dK2, float* dV2, void* workspace,
+                                  int64_t workspace_bytes, void* stream) {
+    Geom g;
+    int code;
+    if (!geom_from_shape(shape, &g, &code)) return code;
+    if (shape->shift != 0) return PFA_ERR_INVALID;
+    if (g.win == 0) return PFA_ERR_UNSUPPORTED;
+    if (shift1 < 0 || shift1 >= g.win || shift2 < 0 || shift2 >= g.win) return PFA_ERR_INVALID;
+    if (!Q1 || !K1 || !V1 || !Q2 || !K2 || !V2 || !lse1 || !I2 || !A2 || !dO1 || !dO2 || !dQ1 || !dK1 || !dV1 ||
+        !dQ2 || !dK2 || !dV2 || !workspace)
+        return PFA_ERR_INVALID;
+    if (K2_keep < 1 || K2_keep > g.N) return PFA_ERR_INVALID;
+    if (workspace_bytes < fused_bwd_ws(g, K2_keep)) return PFA_ERR_INVALID;
+    if (g.win % 8 || K2_keep > 256) return PFA_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // workspace: A^1 at the kept slots and dA^1, both [wh, N, N]; then the two backward passes' own
+    const int64_t map_bytes = n_wh(g) * g.N * (int64_t)g.N * 4;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* A1 = reinterpret_cast<float*>(ws);
+    float* dA1 = reinterpret_cast<float*>(ws + map_bytes);
+    unsigned char* ws_sparse = ws + 2 * map_bytes;
+    float* ws_dense = reinterpret_cast<float*>(ws_sparse + sparse_bwd_ws(g, K2_keep));
+
+    pfa::FirstMapArgs m;
+    m.Q1 = Q1; m.K1 = K1; m.I2 = I2; m.lse1 = lse1; m.A1 = A1;
+    m.g = g;
+    m.g.shift = shift1;
+    m.K2 = K2_keep;
+    m.scale2 = (float)(1.4426950408889634 / sqrt((double)g.d));
+    m.blocks_per_wh = pfa::first_map_blocks(g.N);
+    m.xcd_map = (n_wh(g) % 8 == 0) ? 1 : 0;
+    const int64_t mgrid = n_wh(g) * m.blocks_per_wh;
+    if (mgrid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
+    const hipError_t e = timed(PFA_KERNEL_FIRST_MAP, s,
+                               [&] { return pfa::launch_first_map(m, shape->dtype, g.d, (int)mgrid, s); });
+    if (e != hipSuccess) return PFA_ERR_HIP;
+
+    // layer 2 with every slot a candidate and A^{l-1} = A^1: dQ2, dK2, dV2 and the dense dA^1
+    pfa_shape s2 = *shape;
+    s2.shift = shift2;
+    int rc = run_sparse_backward(&s2, Q2, K2, V2, nullptr, nullptr, A1, g.N, K2_keep, I2, A2, dO2, dA2, dQ2, dK2, dV2,
+                                 dA1, nullptr, ws_sparse, sparse_bwd_ws(g, K2_keep), s);
+    if (rc != PFA_OK) return rc;
+    // layer 1 (dense) with that dA^1
+    Geom g1 = g;
+    g1.shift = shift1;
+    return run_dense_backward(g1, shape->dtype, Q1, K1, V1, nullptr, lse1, dO1, dA1, dQ1, dK1, dV1, ws_dense, s);
+}
+
 int64_t pfa_sparse_layer_backward_workspace(const pfa_shape* shape, int32_t K_l) {
     Geom g;
     int code;
     if (!geom_from_shape(shape, &g, &code)) return code;
     if (K_l < 1 || K_l > g.N) return PFA_ERR_INVALID;
-    return n_wh(g) * g.N * ((int64_t)K_l + 1) * 4;   // g per kept pair, then one flag per row
+    return sparse_bwd_ws(g, K_l);
+}
+
+int64_t pfa_sparse_layer_backward_rpb_workspace(const pfa_shape* shape, int32_t K_l) {
+    Geom g;
+    int code;
+    if (!geom_from_shape(shape, &g, &code)) return code;
+    if (K_l < 1 || K_l > g.N) return PFA_ERR_INVALID;
+    if (g.win == 0) return PFA_ERR_UNSUPPORTED;   // a bias needs window mode
+    return sparse_bwd_ws(g, K_l) + dbias_part_ws(g);
 }
 
 int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void* K, const void* V,
@@ -318,20 +408,44 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
                               const int32_t* I_l, const float* A_l, const float* dO, const float* dA_l,
                               float* dQ, float* dK, float* dV, float* dA_prev, void* workspace,
                               int64_t workspace_bytes, void* stream) {
+    return run_sparse_backward(shape, Q, K, V, nullptr, I_prev, A_prev, K_prev, K_l, I_l, A_l, dO, dA_l, dQ, dK, dV,
+                               dA_prev, nullptr, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int pfa_sparse_layer_backward_rpb(const pfa_shape* shape, const void* Q, const void* K, const void* V,
+                                  const float* bias, const int32_t* I_prev, const float* A_prev, int32_t K_prev,
+                                  int32_t K_l, const int32_t* I_l, const float* A_l, const float* dO,
+                                  const float* dA_l, float* dQ, float* dK, float* dV, float* dA_prev, float* dbias,
+                                  void* workspace, int64_t workspace_bytes, void* stream) {
+    return run_sparse_backward(shape, Q, K, V, bias, I_prev, A_prev, K_prev, K_l, I_l, A_l, dO, dA_l, dQ, dK, dV,
+                               dA_prev, dbias, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+int run_sparse_backward(const pfa_shape* shape, const void* Q, const void* K, const void* V, const float* bias,
+                        const int32_t* I_prev, const float* A_prev, int32_t K_prev, int32_t K_l, const int32_t* I_l,
+                        const float* A_l, const float* dO, const float* dA_l, float* dQ, float* dK, float* dV,
+                        float* dA_prev, float* dbias, void* workspace, int64_t workspace_bytes, hipStream_t s) {
     Geom g;
     int code;
     if (!geom_from_shape(shape, &g, &code)) return code;
-    if (g.win == 0) return PFA_ERR_UNSUPPORTED;
     if (!Q || !K || !V || !I_l || !A_l || !dO || !dQ || !dK || !dV || !workspace) return PFA_ERR_INVALID;
     if (K_prev < 1 || K_prev > g.N || K_l < 1 || K_l > K_prev) return PFA_ERR_INVALID;
     if (!I_prev && K_prev != g.N) return PFA_ERR_INVALID;
     if (dA_prev && !A_prev) return PFA_ERR_INVALID;
-    if (workspace_bytes < n_wh(g) * g.N * ((int64_t)K_l + 1) * 4) return PFA_ERR_INVALID;
+    if (dbias && !bias) return PFA_ERR_INVALID;
+    if (workspace_bytes < sparse_bwd_ws(g, K_l) + (dbias ? dbias_part_ws(g) : 0)) return PFA_ERR_INVALID;
     if (K_l > 256) return PFA_ERR_UNSUPPORTED;
     if ((int64_t)g.N * K_l * 4 > 0x7FFFFFF0) return PFA_ERR_UNSUPPORTED;
+    if (g.win == 0) {   // global mode: no bias; the dA_prev row bitmaps must fit in LDS
+        if (bias || g.N > (1 << 22)) return PFA_ERR_UNSUPPORTED;
+        if (dA_prev && g.N > 8192) return PFA_ERR_UNSUPPORTED;
+    }
     if (!pfa::backward_dkv_sorted(shape->dtype, g.d, g.N, K_l) && !pfa::backward_dkv_mfma(g.d, g.N, K_l))
         return PFA_ERR_UNSUPPORTED;
-    hipStream_t s = static_cast<hipStream_t>(stream);
 
     pfa::BackwardArgs a;
     a.Q = Q; a.K = K; a.V = V;
@@ -346,8 +460,11 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
     a.xcd_map = (n_wh(g) % 8 == 0) ? 1 : 0;
     a.scale = (float)(1.0 / sqrt((double)g.d));
     a.scale2 = (float)(1.4426950408889634 / sqrt((double)g.d));
+    a.bias = bias;
     a.dkv_full = (int)n_wh(g);
-    a.blocks_per_wh = g.N >= 512 ? 2 : 1;
+    // rows per workgroup: a window's rows in 1 or 2 parts (K and V staged per part);
+    // global mode beyond 1024 tokens stages nothing and takes 128 rows per workgroup
+    a.blocks_per_wh = g.N > 1024 ? (g.N + 127) / 128 : g.N >= 512 ? 2 : 1;
     a.rows_per_block = (g.N + a.blocks_per_wh - 1) / a.blocks_per_wh;
     const int64_t rgrid = n_wh(g) * a.blocks_per_wh;
     if (rgrid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
@@ -369,8 +486,10 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
         b.rows_per_block = g.N;
         if (pfa::backward_dkv_sorted(dt, g.d, g.N, K_l)) {
             b.blocks_per_wh = 1;
+            const int64_t sgrid = n_wh(g) * ((g.N + 1023) / 1024);   // 1024 tokens per workgroup
+            if (sgrid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
             e = timed(PFA_KERNEL_BWD_SCATTER, s,
-                      [&] { return pfa::launch_backward_dkv_sorted(b, dt, g.d, (int)n_wh(g), s); });
+                      [&] { return pfa::launch_backward_dkv_sorted(b, dt, g.d, (int)sgrid, s); });
         } else {
             b.blocks_per_wh = 1;
             b.dkv_full = (int)pfa::backward_dkv_full(n_wh(g), g.N, compute_units());
@@ -380,8 +499,21 @@ int pfa_sparse_layer_backward(const pfa_shape* shape, const void* Q, const void*
             e = timed(PFA_KERNEL_BWD_SCATTER, s, [&] { return pfa::launch_backward_dkv(b, dt, g.d, dgrid, s); });
         }
     }
+    if (e == hipSuccess && dbias) {
+        pfa::DbiasArgs d;
+        d.I_l = I_l; d.A_l = A_l; d.g_buf = a.g_buf; d.rows = nullptr;
+        d.part = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + sparse_bwd_ws(g, K_l));
+        d.dbias = dbias;
+        d.g = g;
+        d.K_l = K_l;
+        e = timed(PFA_KERNEL_DBIAS, s, [&] { return pfa::launch_dbias_sparse(d, s); });
+    }
     return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
 }
+
+}  // namespace
+
+extern "C" {
 
 int64_t pfa_dense_layer_backward_workspace(const pfa_shape* shape) {
     Geom g;
@@ -403,6 +535,44 @@ int pfa_dense_layer_backward(const pfa_shape* shape, const void* Q, const void* 
     if (bias && g.win % 16) return PFA_ERR_UNSUPPORTED;
     return run_dense_backward(g, shape->dtype, Q, K, V, bias, lse, dO, dA, dQ, dK, dV,
                               static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+int64_t pfa_dense_layer_backward_rpb_workspace(const pfa_shape* shape) {
+    Geom g;
+    int code;
+    if (!geom_from_shape(shape, &g, &code)) return code;
+    if (g.win == 0) return PFA_ERR_UNSUPPORTED;
+    return n_wh(g) * g.N * 4 + dense_dbias_rows_ws(g) + dbias_part_ws(g);
+}
+
+int pfa_dense_layer_backward_rpb(const pfa_shape* shape, const void* Q, const void* K, const void* V,
+                                 const float* bias, const float* lse, const float* dO, const float* dA, float* dQ,
+                                 float* dK, float* dV, float* dbias, void* workspace, int64_t workspace_bytes,
+                                 void* stream) {
+    Geom g;
+    int code;
+    if (!geom_from_shape(shape, &g, &code)) return code;
+    if (g.win == 0) return PFA_ERR_UNSUPPORTED;
+    if (!Q || !K || !V || !lse || !dO || !dQ || !dK || !dV || !workspace) return PFA_ERR_INVALID;
+    if (dbias && !bias) return PFA_ERR_INVALID;
+    const int64_t need = n_wh(g) * g.N * 4 + (dbias ? dense_dbias_rows_ws(g) + dbias_part_ws(g) : 0);
+    if (workspace_bytes < need) return PFA_ERR_INVALID;
+    if (g.win % 8) return PFA_ERR_UNSUPPORTED;
+    if (bias && g.win % 16) return PFA_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* ws = static_cast<float*>(workspace);
+    float* rows = dbias ? ws + n_wh(g) * g.N : nullptr;
+    const int rc = run_dense_backward(g, shape->dtype, Q, K, V, bias, lse, dO, dA, dQ, dK, dV, ws, s, rows);
+    if (rc != PFA_OK || !dbias) return rc;
+    pfa::DbiasArgs d;
+    d.I_l = nullptr; d.A_l = nullptr; d.g_buf = nullptr;
+    d.rows = rows;
+    d.part = rows + dense_dbias_rows_ws(g) / 4;
+    d.dbias = dbias;
+    d.g = g;
+    d.K_l = 0;
+    const hipError_t e = timed(PFA_KERNEL_DBIAS, s, [&] { return pfa::launch_dbias_dense(d, s); });
+    return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
 }
 
 int pfa_dense_layer_backward_noalloc(const pfa_shape* shape, const void* Q, const void* K, const void* V,
@@ -429,8 +599,9 @@ namespace {
 
 int run_dense_backward(const Geom& g, int dtype, const void* Q, const void* K, const void* V, const float* bias,
                        const float* lse, const float* dO, const float* dA, float* dQ, float* dK, float* dV,
-                       float* Dws, hipStream_t s) {
+                       float* Dws, hipStream_t s, float* dbias_rows) {
     pfa::DenseBwdArgs a;
+    a.dbias_rows = dbias_rows;
     a.Q = Q; a.K = K; a.V = V;
     a.bias = bias; a.lse = lse; a.dO = dO; a.dA = dA;
     a.dQ = dQ; a.dK = dK; a.dV = dV;
@@ -536,6 +707,8 @@ const char* pfa_kernel_name(int32_t kind) {
         case PFA_KERNEL_IET_UNION: return "iet_union_kernel";
         case PFA_KERNEL_DENSE_BWD: return "dense_bwd";
         case PFA_KERNEL_BWD_EXACT: return "bwd_exact_dap_kernel";
+        case PFA_KERNEL_DBIAS: return "dbias";
+        case PFA_KERNEL_FIRST_MAP: return "first_map_kept_kernel";
         default: return "unknown";
     }
 }

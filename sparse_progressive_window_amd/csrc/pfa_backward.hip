@@ -96,8 +96,11 @@ __device__ __forceinline__ void load_row_chunk(const T* row, int chunk, float (&
     Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(row) + chunk * 16), o);
 }
 
-template <typename T, int D, int GL, int NST, bool HAS_V, bool HAS_K>
+// GLOB (global mode with more than 1024 tokens): k_j and v_j are gathered from
+// global memory (L2) instead of the staged window; both passes in one kernel.
+template <typename T, int D, int GL, int NST, bool HAS_V, bool HAS_K, bool GLOB = false>
 __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const BackwardArgs p) {
+    static_assert(!GLOB || (HAS_V && HAS_K), "global gathers: one kernel");
     constexpr int NW = kBwdRowWaves;
     constexpr int EPC = Chunk<T>::kElems;   // elements per 16-byte chunk
     constexpr int CH = D / EPC;             // chunks (lanes) per K/V row
@@ -120,21 +123,32 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
     const WhPart w = decode_block(p.blocks_per_wh, p.xcd_map, g);
     const size_t plane = (size_t)w.bh * g.H * g.W * D;
 
-    unsigned char* Vs = smem;
-    unsigned char* Ks = smem + (HAS_V ? N * ROWB : 0);
+    const unsigned char* Vs;
+    const unsigned char* Ks;
+    if constexpr (GLOB) {
+        Vs = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.V) + plane);
+        Ks = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.K) + plane);
+    } else {
+        Vs = smem;
+        Ks = smem + (HAS_V ? N * ROWB : 0);
+    }
+    const int staged = GLOB ? 0 : (HAS_V + HAS_K) * N * ROWB;
     const bool want_dap = HAS_K && p.dA_prev != nullptr;
     const int bmw = (N + 31) >> 5;                       // bitmap words per row
     const int rsw = bmw + ((K_l + 3) & ~3);              // row scratch words
-    uint32_t* bitmap = reinterpret_cast<uint32_t*>(smem + (HAS_V + HAS_K) * N * ROWB) + (wave * RPW + grp) * rsw;
+    uint32_t* bitmap = reinterpret_cast<uint32_t*>(smem + staged) + (wave * RPW + grp) * rsw;
     float* vals = reinterpret_cast<float*>(bitmap + bmw);
     // workgroup flag for the exact dA^{l-1} pass, after the row scratch
-    uint32_t* wg_flag = reinterpret_cast<uint32_t*>(smem + (HAS_V + HAS_K) * N * ROWB) + NW * RPW * rsw;
+    uint32_t* wg_flag = reinterpret_cast<uint32_t*>(smem + staged) + NW * RPW * rsw;
     if (want_dap && threadIdx.x == 0) *wg_flag = 0u;
     // smallest A^l over this lane's kept entries of all its rows, as fp32 bits (A^l >= 0
     // orders like its bits): one v_min_u32 per entry, one workgroup flag at the end
     uint32_t amin = 0xFFFFFFFFu;
-    if (HAS_V) stage_rows<T, D>(Vs, ROWB, static_cast<const T*>(p.V) + plane, g, w.wy, w.wx);
-    if (HAS_K) stage_rows<T, D>(Ks, ROWB, static_cast<const T*>(p.K) + plane, g, w.wy, w.wx);
+    if constexpr (!GLOB) {
+        if (HAS_V) stage_rows<T, D>(smem, ROWB, static_cast<const T*>(p.V) + plane, g, w.wy, w.wx);
+        if (HAS_K) stage_rows<T, D>(smem + (HAS_V ? N * ROWB : 0), ROWB, static_cast<const T*>(p.K) + plane, g, w.wy,
+                                    w.wx);
+    }
     __syncthreads();
 
     const size_t wh_pairs = (size_t)w.wh * N * K_l;
@@ -487,7 +501,8 @@ __global__ __launch_bounds__(kBwdRowWaves * kWave) void bwd_rows_kernel(const Ba
 //   or subnormal (the others keep the row pass's dkey / A^{l-1}).
 // The kept entry r of I^l (token j) sits at the slot of j in the row's I^{l-1},
 // found through a token -> slot table in LDS. q_i and k_j come from global
-// memory at the layer's pixels (rare rows: no staging).
+// memory at the layer's pixels (rare rows: no staging). With a relative position
+// bias, s2_r includes the bias of the pair's offset (in base 2).
 template <typename T, int D>
 __global__ __launch_bounds__(4 * kWave) void bwd_exact_dap_kernel(const BackwardArgs p) {
     constexpr int EPC = Chunk<T>::kElems;
@@ -506,6 +521,8 @@ __global__ __launch_bounds__(4 * kWave) void bwd_exact_dap_kernel(const Backward
     const T* Kh = static_cast<const T*>(p.K) + plane;
     const int row0 = w.part * p.rows_per_block;
     const int row1 = min(N, row0 + p.rows_per_block);
+    constexpr float kLog2eB = 1.4426950408889634f;
+    const float* bt = p.bias ? p.bias + (size_t)(w.bh % g.heads) * (2 * g.win - 1) * (2 * g.win - 1) : nullptr;
     for (int i = row0 + wave; i < row1; i += 4) {
         const size_t row = (size_t)w.wh * N + i;
         const int32_t* Il = p.I_l + row * K_l;
@@ -518,6 +535,8 @@ __global__ __launch_bounds__(4 * kWave) void bwd_exact_dap_kernel(const Backward
         for (int c = 0; c < CH; ++c)
             Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(Qh + (size_t)slot_pixel(g, w.wy, w.wx, i) * D + c * EPC),
                              &qf[c * EPC]);
+        const int iy = bt ? i / g.win : 0;   // (a bias comes with window mode only)
+        const int ibase = (iy + g.win - 1) * (2 * g.win - 1) + (i - iy * g.win) + g.win - 1;
         auto score2 = [&](int j) {
             const T* kr = Kh + (size_t)slot_pixel(g, w.wy, w.wx, j) * D;
             float acc = 0.0f;
@@ -528,19 +547,31 @@ __global__ __launch_bounds__(4 * kWave) void bwd_exact_dap_kernel(const Backward
 #pragma unroll
                 for (int y = 0; y < EPC; ++y) acc = fmaf(qf[c * EPC + y], kf[y], acc);
             }
-            return acc * p.scale2;
+            if (!bt) return acc * p.scale2;
+            const int jy = j / g.win;   // + the bias of the pair's offset, in base 2
+            return fmaf(bt[ibase - jy * (2 * g.win - 1) - (j - jy * g.win)], kLog2eB, acc * p.scale2);
         };
         const int32_t* Ip = p.I_prev ? p.I_prev + row * K_prev : nullptr;
         const float* Ap = p.A_prev + row * K_prev;
         const float* Gl = p.g_buf + row * K_l;
-        if (Ip) {
+        const bool table = Ip && N <= 1024;
+        if (table) {
             for (int c = lane; c < K_prev; c += kWave) pos[min((unsigned)Ip[c], (unsigned)(N - 1))] = (int16_t)c;
             __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's table writes before its reads
         }
+        // slot of token j in the row's I^{l-1}: the LDS table, or (global mode beyond
+        // 1024 tokens, short lists) a search of the row
+        auto slot_of = [&](int j) {
+            if (!Ip) return j;
+            if (table) return (int)pos[j];
+            for (int c = 0; c < K_prev; ++c)
+                if (Ip[c] == j) return c;
+            return 0;   // not a candidate: excluded by the caller's contract
+        };
         float mx = -INFINITY, sz = 0.0f;
         for (int e = lane; e < K_l; e += kWave) {
             const int j = (int)min((unsigned)Il[e], (unsigned)(N - 1));
-            const float a = Ap[Ip ? pos[j] : j];
+            const float a = Ap[slot_of(j)];
             if (a > 0.0f) {
                 const float kap = score2(j) + log2f(a);
                 if (kap > mx) {
@@ -562,7 +593,7 @@ __global__ __launch_bounds__(4 * kWave) void bwd_exact_dap_kernel(const Backward
         const float C = mx + log2f(sz);
         for (int e = lane; e < K_l; e += kWave) {
             const int j = (int)min((unsigned)Il[e], (unsigned)(N - 1));
-            const int c = Ip ? pos[j] : j;
+            const int c = slot_of(j);
             const float a = Ap[c];
             if (!(a >= FLT_MIN) || !(Al[e] >= FLT_MIN)) p.dA_prev[row * K_prev + c] = exp2f(score2(j) - C) * Gl[e];
         }
@@ -752,9 +783,10 @@ __global__ __launch_bounds__(16 * kWave) void bwd_dkv_kernel(const BackwardArgs 
     }
 }
 
-// dK and dV with work in proportion to the kept pairs (any N <= 1024): one
-// workgroup per window-head, thread t owns token t and keeps its dV and dK rows
-// in registers. The window-head's rows are taken in chunks of R = 32 MW rows:
+// dK and dV with work in proportion to the kept pairs: one workgroup per
+// window-head and 1024 tokens (global mode: several per head, each taking the
+// entries of its token range), thread t owns token tok0 + t and keeps its dV and
+// dK rows in registers. The window-head's rows are taken in chunks of R = 32 MW rows:
 //   (a) the chunk's dO and Q rows are staged in LDS (16-byte chunks permuted by
 //       row, so the owners' reads of random rows spread over the banks);
 //   (b) every kept entry (row r, token j) of the chunk sets bit r of token j's
@@ -780,22 +812,25 @@ __global__ __launch_bounds__(16 * kWave) void bwd_dkv_sorted_kernel(const Backwa
     extern __shared__ __align__(16) unsigned char smem[];
 
     const Geom g = p.g;
-    const int N = g.N;
+    const int N = g.N;   // rows (and tokens) of the window-head
     const int K_l = p.K_l;
     const int t = threadIdx.x;
     const int lane = t & (kWave - 1);
     const int wave = t / kWave;
-    const WhPart w = decode_block(1, p.xcd_map, g);
+    const int tparts = (N + NT - 1) / NT;
+    const int tok0 = (blockIdx.x % tparts) * NT;   // this workgroup's tokens: [tok0, tok0 + NTK)
+    const int NTK = min(NT, N - tok0);
+    const WhPart w = decode_block_id(blockIdx.x / tparts, 1, p.xcd_map, g);
     const size_t plane = (size_t)w.bh * g.H * g.W * D;
     const T* Qh = static_cast<const T*>(p.Q) + plane;
     const float* dOh = p.dO + plane;
 
     unsigned char* dOs = smem;                                        // [R][OROWB]
     unsigned char* Qs = dOs + R * OROWB;                              // [R][QROWB]
-    uint32_t* mask = reinterpret_cast<uint32_t*>(Qs + R * QROWB);     // [MW][N]: word m of token j at m N + j
-    int* seg = reinterpret_cast<int*>(mask + N * MW);                 // [N] segment starts
-    int* wsum = seg + N;                                              // [16] wave totals
-    const size_t roff = ((size_t)(R * OROWB + R * QROWB + (N * MW + N + 16) * 4) + 7) & ~(size_t)7;
+    uint32_t* mask = reinterpret_cast<uint32_t*>(Qs + R * QROWB);     // [MW][NTK]: word m of token j at m NTK + j
+    int* seg = reinterpret_cast<int*>(mask + NTK * MW);               // [NTK] segment starts
+    int* wsum = seg + NTK;                                            // [16] wave totals
+    const size_t roff = ((size_t)(R * OROWB + R * QROWB + (NTK * MW + NTK + 16) * 4) + 7) & ~(size_t)7;
     float2* recw = reinterpret_cast<float2*>(smem + roff);            // [R K_l] (A, A g / sqrt(d))
     uint16_t* recr = reinterpret_cast<uint16_t*>(recw + R * K_l);     // [R K_l] row in the chunk
 
@@ -810,9 +845,9 @@ __global__ __launch_bounds__(16 * kWave) void bwd_dkv_sorted_kernel(const Backwa
     for (int c = 0; c < D; ++c) accV[c] = accK[c] = 0.0f;
     constexpr int EPT = 8192 / NT;   // entries per thread (the launcher keeps R K_l <= 8192)
 
-    if (t < N) {
+    if (t < NTK) {
 #pragma unroll
-        for (int m = 0; m < MW; ++m) mask[m * N + t] = 0u;   // (the owners clear them again after each chunk)
+        for (int m = 0; m < MW; ++m) mask[m * NTK + t] = 0u;   // (the owners clear them again after each chunk)
     }
     for (int r0 = 0; r0 < N; r0 += R) {
         const int rows = min(R, N - r0);
@@ -828,13 +863,14 @@ __global__ __launch_bounds__(16 * kWave) void bwd_dkv_sorted_kernel(const Backwa
             *reinterpret_cast<uint4*>(Qs + r * QROWB + ((c ^ (r & (QCH - 1))) * 16)) = *reinterpret_cast<const uint4*>(
                 reinterpret_cast<const unsigned char*>(Qh + (size_t)slot_pixel(g, w.wy, w.wx, r0 + r) * D) + c * 16);
         }
-        int ej[EPT];
+        int ej[EPT];   // token - tok0, or -1 (no entry, or another workgroup's token)
         float ea[EPT], ek[EPT];
 #pragma unroll
         for (int u = 0; u < EPT; ++u) {
             const int e = t + NT * u;
             const int off = e < ne ? (r0 * K_l + e) * 4 : 0x7FFFFFF0;   // past the range: not loaded
-            ej[u] = (int)min((unsigned)__builtin_amdgcn_raw_buffer_load_b32(rI, off, 0, 0), (unsigned)(N - 1));
+            const int j = (int)min((unsigned)__builtin_amdgcn_raw_buffer_load_b32(rI, off, 0, 0), (unsigned)(N - 1));
+            ej[u] = (e < ne && j >= tok0 && j - tok0 < NTK) ? j - tok0 : -1;
             ea[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rA, off, 0, 0));
             ek[u] = ea[u] * __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, off, 0, 0)) * p.scale;
         }
@@ -843,17 +879,17 @@ __global__ __launch_bounds__(16 * kWave) void bwd_dkv_sorted_kernel(const Backwa
 #pragma unroll
         for (int u = 0; u < EPT; ++u) {
             const int e = t + NT * u;
-            if (e < ne) {
+            if (ej[u] >= 0) {
                 const int r = e / K_l;
-                atomicOr(&mask[(r >> 5) * N + ej[u]], 1u << (r & 31));
+                atomicOr(&mask[(r >> 5) * NTK + ej[u]], 1u << (r & 31));
             }
         }
         __syncthreads();
         // (c) segment of each token: exclusive scan of the mask popcounts
         int cnt = 0;
-        if (t < N) {
+        if (t < NTK) {
 #pragma unroll
-            for (int m = 0; m < MW; ++m) cnt += __builtin_popcount(mask[m * N + t]);
+            for (int m = 0; m < MW; ++m) cnt += __builtin_popcount(mask[m * NTK + t]);
         }
         int incl = cnt;
 #pragma unroll
@@ -866,19 +902,19 @@ __global__ __launch_bounds__(16 * kWave) void bwd_dkv_sorted_kernel(const Backwa
         int base = 0;
         for (int v = 0; v < wave; ++v) base += wsum[v];
         const int st = base + incl - cnt;
-        if (t < N) seg[t] = st;
+        if (t < NTK) seg[t] = st;
         __syncthreads();
         // (d) records at the rank of their row in the token's mask
 #pragma unroll
         for (int u = 0; u < EPT; ++u) {
             const int e = t + NT * u;
-            if (e < ne) {
+            if (ej[u] >= 0) {
                 const int r = e / K_l;
                 const uint32_t* mj = mask + ej[u];
-                int rank = __builtin_popcount(mj[(r >> 5) * N] & ((1u << (r & 31)) - 1u));
+                int rank = __builtin_popcount(mj[(r >> 5) * NTK] & ((1u << (r & 31)) - 1u));
 #pragma unroll
                 for (int m = 0; m < MW; ++m)
-                    if (m < (r >> 5)) rank += __builtin_popcount(mj[m * N]);
+                    if (m < (r >> 5)) rank += __builtin_popcount(mj[m * NTK]);
                 const int pos = seg[ej[u]] + rank;
                 recw[pos] = make_float2(ea[u], ek[u]);
                 recr[pos] = (uint16_t)r;
@@ -886,9 +922,9 @@ __global__ __launch_bounds__(16 * kWave) void bwd_dkv_sorted_kernel(const Backwa
         }
         __syncthreads();
         // (e) owners: their segment in row order; their masks are cleared for the next chunk
-        if (t < N) {
+        if (t < NTK) {
 #pragma unroll
-            for (int m = 0; m < MW; ++m) mask[m * N + t] = 0u;
+            for (int m = 0; m < MW; ++m) mask[m * NTK + t] = 0u;
         }
         for (int k = st; k < st + cnt; ++k) {
             const float2 wv = recw[k];
@@ -911,8 +947,8 @@ __global__ __launch_bounds__(16 * kWave) void bwd_dkv_sorted_kernel(const Backwa
         }
         __syncthreads();   // the next chunk reuses the LDS
     }
-    if (t < N) {
-        const size_t o = plane + (size_t)slot_pixel(g, w.wy, w.wx, t) * D;
+    if (t < NTK) {
+        const size_t o = plane + (size_t)slot_pixel(g, w.wy, w.wx, tok0 + t) * D;
 #pragma unroll
         for (int c = 0; c < D; c += 4) {
             *reinterpret_cast<float4*>(p.dV + o + c) = make_float4(accV[c], accV[c + 1], accV[c + 2], accV[c + 3]);
@@ -938,49 +974,57 @@ int rows_group(int CH, int K_l) {
     return need <= 16 ? 16 : need <= 32 ? 32 : 64;
 }
 
+// global mode with more than 1024 tokens: nothing staged (gathers from L2)
+bool rows_global(int N) { return N > 1024; }
+
 int rows_lds(int dtype, int D, int N, int K_l, bool has_v, bool has_k, bool want_dap) {
     const int rowb = D * (dtype == 0 ? 4 : 2);
     const int gl = rows_group(chunks_per_row(dtype, D), K_l);
     const int rsw = (N + 31) / 32 + ((K_l + 3) & ~3);
-    return ((has_v ? 1 : 0) + (has_k ? 1 : 0)) * N * rowb +
-           ((has_k && want_dap) ? kBwdRowWaves * (64 / gl) * rsw * 4 + 16 : 0);   // + the workgroup flag
+    const int staged = rows_global(N) ? 0 : ((has_v ? 1 : 0) + (has_k ? 1 : 0)) * N * rowb;
+    return staged + ((has_k && want_dap) ? kBwdRowWaves * (64 / gl) * rsw * 4 + 16 : 0);   // + the workgroup flag
 }
 
-template <typename T, int D, bool HV, bool HK>
+template <typename T, int D, bool HV, bool HK, bool GLOB>
 hipError_t launch_rows_mode(const BackwardArgs& a, int grid, hipStream_t s) {
     constexpr int CH = D * (int)sizeof(T) / 16;
     const int gl = rows_group(CH, a.K_l);
     const int lds = rows_lds(sizeof(T) == 4 ? 0 : 1, D, a.g.N, a.K_l, HV, HK, a.dA_prev != nullptr);
     const int th = kBwdRowWaves * kWave;
-    if (gl == 16) return launch_bwd(bwd_rows_kernel<T, D, 16, 1, HV, HK>, a, th, lds, grid, s);
-    if (gl == 32) return launch_bwd(bwd_rows_kernel<T, D, 32, 1, HV, HK>, a, th, lds, grid, s);
+    if (gl == 16) return launch_bwd(bwd_rows_kernel<T, D, 16, 1, HV, HK, GLOB>, a, th, lds, grid, s);
+    if (gl == 32) return launch_bwd(bwd_rows_kernel<T, D, 32, 1, HV, HK, GLOB>, a, th, lds, grid, s);
     const int nst = (a.K_l + 4 * (64 / CH) - 1) / (4 * (64 / CH));
-    if (nst <= 1) return launch_bwd(bwd_rows_kernel<T, D, 64, 1, HV, HK>, a, th, lds, grid, s);
-    if (nst <= 2) return launch_bwd(bwd_rows_kernel<T, D, 64, 2, HV, HK>, a, th, lds, grid, s);
-    if (nst <= 4) return launch_bwd(bwd_rows_kernel<T, D, 64, 4, HV, HK>, a, th, lds, grid, s);
+    if (nst <= 1) return launch_bwd(bwd_rows_kernel<T, D, 64, 1, HV, HK, GLOB>, a, th, lds, grid, s);
+    if (nst <= 2) return launch_bwd(bwd_rows_kernel<T, D, 64, 2, HV, HK, GLOB>, a, th, lds, grid, s);
+    if (nst <= 4) return launch_bwd(bwd_rows_kernel<T, D, 64, 4, HV, HK, GLOB>, a, th, lds, grid, s);
     if constexpr (CH >= 8) {
-        if (nst <= 8) return launch_bwd(bwd_rows_kernel<T, D, 64, 8, HV, HK>, a, th, lds, grid, s);
+        if (nst <= 8) return launch_bwd(bwd_rows_kernel<T, D, 64, 8, HV, HK, GLOB>, a, th, lds, grid, s);
     }
     return hipErrorInvalidValue;   // K_l beyond what the caller admits
 }
 
 template <typename T, int D>
 hipError_t launch_rows_t(const BackwardArgs& a, bool has_v, bool has_k, int grid, hipStream_t s) {
-    if (has_v && has_k) return launch_rows_mode<T, D, true, true>(a, grid, s);
-    if (has_v) return launch_rows_mode<T, D, true, false>(a, grid, s);
-    return launch_rows_mode<T, D, false, true>(a, grid, s);
+    if (rows_global(a.g.N)) {
+        if (!has_v || !has_k) return hipErrorInvalidValue;   // one kernel in global mode
+        return launch_rows_mode<T, D, true, true, true>(a, grid, s);
+    }
+    if (has_v && has_k) return launch_rows_mode<T, D, true, true, false>(a, grid, s);
+    if (has_v) return launch_rows_mode<T, D, true, false, false>(a, grid, s);
+    return launch_rows_mode<T, D, false, true, false>(a, grid, s);
 }
 
 // rows per chunk of the sorted dK/dV kernel: the largest of 32, 64, 128, 256 rows
 // (at most N rounded up to 32) whose LDS (staged rows, token masks, records) fits
 int sorted_rows(int dtype, int D, int N, int K_l) {
-    if (N > 1024 || K_l > 256) return 0;
+    if (K_l > 256) return 0;
     const int rowb = D * 4 + D * (dtype == 0 ? 4 : 2);
+    const int nt = N < 1024 ? N : 1024;   // tokens per workgroup
     int best = 0;
     for (int R = 32; R <= 256; R *= 2) {
         if (R * K_l > 8192) break;
         const int mw = R / 32;
-        const int lds = R * rowb + (N * mw + N + 16) * 4 + 8 + R * K_l * 10;
+        const int lds = R * rowb + (nt * mw + nt + 16) * 4 + 8 + R * K_l * 10;
         if (lds <= kLdsBytes) best = R;
         if (R >= N) break;
     }
@@ -989,7 +1033,8 @@ int sorted_rows(int dtype, int D, int N, int K_l) {
 
 int sorted_lds(int dtype, int D, int N, int K_l, int R) {
     const int rowb = D * 4 + D * (dtype == 0 ? 4 : 2);
-    return R * rowb + (N * (R / 32) + N + 16) * 4 + 8 + R * K_l * 10;
+    const int nt = N < 1024 ? N : 1024;
+    return R * rowb + (nt * (R / 32) + nt + 16) * 4 + 8 + R * K_l * 10;
 }
 
 template <typename T, int D>
@@ -1048,8 +1093,10 @@ hipError_t launch_dkv_t(const BackwardArgs& a, int grid, hipStream_t s) {
 int backward_fused_rows(int dtype, int D, int N, int K_l, bool want_dap) {
     // one kernel when K and V fit in LDS together and G stays within registers
     // (at most 16 kept slots per lane)
+    // (global mode beyond 1024 tokens gathers both from L2: always one kernel)
     const int CH = chunks_per_row(dtype, D);
     const int per_lane = 4 * ((K_l + 4 * (64 / CH) - 1) / (4 * (64 / CH)));
+    if (rows_global(N)) return 1;
     if (per_lane > 16) return 0;
     return rows_lds(dtype, D, N, K_l, true, true, want_dap) <= kLdsBytes ? 1 : 0;
 }
@@ -1102,7 +1149,6 @@ hipError_t launch_backward_rows(const BackwardArgs& a, int dtype, int D, bool ha
 }
 
 hipError_t launch_backward_exact_dap(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream) {
-    if (a.g.N > 1024) return hipErrorInvalidValue;
     auto go = [&](auto fn) {
         hipLaunchKernelGGL(fn, dim3(grid), dim3(4 * kWave), 0, stream, a);
         return hipGetLastError();

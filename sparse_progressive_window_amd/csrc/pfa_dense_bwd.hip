@@ -172,8 +172,9 @@ __device__ __forceinline__ BlockPos decode(const Geom& g, int blocks, int xcd_ma
     return b;
 }
 
-template <typename T, int D, bool BIAS, bool HAS_DA>
+template <typename T, int D, bool BIAS, bool HAS_DA, bool DBIAS>
 __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const DenseBwdArgs p) {
+    static_assert(!DBIAS || BIAS, "the bias gradient comes with a bias");
     constexpr int DPL = D / 4;
     constexpr int CT = D / 16;
     constexpr int STR = D + 4;   // padded fp32 LDS row
@@ -188,6 +189,8 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const D
     __shared__ __align__(16) unsigned char KP2[SPLIT ? 2 : 1][PLB];
     __shared__ __align__(16) unsigned char VP2[SPLIT ? 2 : 1][PLB];
     __shared__ float btab[BIAS ? 63 * 63 : 1];
+    // DBIAS: each wave's 16 x 16 block of dS, row stride 20 floats (16-byte aligned rows)
+    __shared__ __align__(16) float dtile[DBIAS ? kBwdWaves * 16 * 20 : 4];
 
     const Geom g = p.g;
     const int N = g.N;
@@ -226,6 +229,9 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const D
     const float* dArow = HAS_DA ? p.dA + ((size_t)bp.wh * N + qi) * N : nullptr;
 
     float Dq = 0.0f;
+    // DBIAS: lane L sums dS over the pairs of this wave's queries at horizontal offset
+    // dx = L - (win - 1) and the vertical offset of the current key row (flushed per row)
+    float dacc = 0.0f;
     v4f dq[CT];
 #pragma unroll
     for (int c = 0; c < CT; ++c) dq[c] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -325,6 +331,29 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void dense_bwd_dq_kernel(const D
                     float dS[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) dS[r] = P[r] * (G[r] - Dq);
+                    if constexpr (DBIAS) {
+                        // the block's queries (one window row, columns qx0 + r16) and keys (one
+                        // window row, columns kx0 + c) pair at column offset qx0 - kx0 + (r16 - c):
+                        // diagonal m = r16 - c of the block. The wave's own LDS writes and reads
+                        // complete in issue order, so no barrier is needed.
+                        float* Tw = dtile + wave * (16 * 20);
+                        *reinterpret_cast<float4*>(Tw + r16 * 20 + 4 * grp) = make_float4(dS[0], dS[1], dS[2], dS[3]);
+                        const int jy = key0 / g.win;
+                        const int kx0 = key0 - jy * g.win;
+                        const int m = lane - (g.win - 1) - (q0 - (q0 / g.win) * g.win - kx0);
+                        if (m >= -15 && m <= 15) {
+                            const int qa = m > 0 ? m : 0;
+                            const int qb = m < 0 ? 15 + m : 15;
+                            float dsum = 0.0f;
+                            for (int q = qa; q <= qb; ++q) dsum += Tw[q * 21 - m];
+                            dacc += dsum;
+                        }
+                        if (kx0 + 16 == g.win) {   // the key row is complete
+                            if (wave_active)
+                                p.dbias_rows[(((size_t)bp.wh * (N / 16) + q0 / 16) * g.win + jy) * 64 + lane] = dacc;
+                            dacc = 0.0f;
+                        }
+                    }
 #pragma unroll
                     for (int c = 0; c < CT; ++c)
 #pragma unroll
@@ -563,7 +592,17 @@ __global__ __launch_bounds__(kBwdWaves * kWave, 4) void dense_bwd_dkv_kernel(con
 
 template <typename T, int D, bool BIAS, bool HAS_DA>
 hipError_t launch_dbwd_t(const DenseBwdArgs& a, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((dense_bwd_dq_kernel<T, D, BIAS, HAS_DA>), dim3(grid), dim3(kBwdWaves * kWave), 0, s, a);
+    if constexpr (BIAS) {
+        if (a.dbias_rows)
+            hipLaunchKernelGGL((dense_bwd_dq_kernel<T, D, true, HAS_DA, true>), dim3(grid), dim3(kBwdWaves * kWave),
+                               0, s, a);
+        else
+            hipLaunchKernelGGL((dense_bwd_dq_kernel<T, D, true, HAS_DA, false>), dim3(grid), dim3(kBwdWaves * kWave),
+                               0, s, a);
+    } else {
+        hipLaunchKernelGGL((dense_bwd_dq_kernel<T, D, false, HAS_DA, false>), dim3(grid), dim3(kBwdWaves * kWave), 0,
+                           s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((dense_bwd_dkv_kernel<T, D, BIAS, HAS_DA>), dim3(grid), dim3(kBwdWaves * kWave), 0, s, a);

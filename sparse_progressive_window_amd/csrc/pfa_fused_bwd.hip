@@ -1,0 +1,89 @@
+// Backward of the first two layers computed together (pfa_first_two_layers).
+//
+// The fused forward never writes the first layer's map A^1 = P (paper notes
+// "Progressive Focused Transformer for Single Image Super-Resolution", sections
+// "Progressive attention across layers" and "Progressive focused resource
+// allocation strategy": layer 1 keeps every slot, layer 2 selects from A^1). The
+// second layer's backward reads A^1 only at its kept slots (dA^1 = dkey / A^1 there,
+// and the exact form's normaliser), so only those entries are recomputed, from q1,
+// k1 and the first layer's log denominators:
+//   A^1_ij = exp(s1_ij - lse1_i),  s1_ij = q1_i.k1_j / sqrt(d),
+// and written at their places in a row-major [N, N] buffer whose other entries are
+// never read. The second layer's backward (candidate list = every slot) then writes
+// the dense dA^1 that the first layer's backward takes.
+//
+// first_map_kept_kernel: 4 wavefronts per workgroup of 256 rows, the window's k1
+// rows staged in LDS; a wavefront takes a row, its lanes the row's kept slots.
+#include "pfa_kernels.h"
+#include "pfa_rows.h"
+
+namespace pfa {
+namespace {
+
+constexpr int kMapWaves = 4;
+constexpr int kMapRows = 256;   // rows per workgroup
+constexpr float kLog2eF = 1.4426950408889634f;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kMapWaves * kWave) void first_map_kept_kernel(const FirstMapArgs p) {
+    constexpr int EPC = Chunk<T>::kElems;
+    constexpr int CH = D / EPC;
+    constexpr int ROWB = D * (int)sizeof(T);
+    extern __shared__ __align__(16) unsigned char smem[];
+    const Geom g = p.g;
+    const int N = g.N;
+    const int K2 = p.K2;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const WhPart w = decode_block(p.blocks_per_wh, p.xcd_map, g);
+    const size_t plane = (size_t)w.bh * g.H * g.W * D;
+    stage_rows<T, D>(smem, ROWB, static_cast<const T*>(p.K1) + plane, g, w.wy, w.wx);
+    __syncthreads();
+    const int row0 = w.part * kMapRows;
+    const int row1 = min(N, row0 + kMapRows);
+    const T* Qh = static_cast<const T*>(p.Q1) + plane;
+    for (int i = row0 + wave; i < row1; i += kMapWaves) {
+        const size_t row = (size_t)w.wh * N + i;
+        const unsigned char* qr = reinterpret_cast<const unsigned char*>(Qh + (size_t)slot_pixel(g, w.wy, w.wx, i) * D);
+        float q[D];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(qr + c * 16), &q[c * EPC]);
+        const float l2 = p.lse1[row] * kLog2eF;
+        const int32_t* Ir = p.I2 + row * K2;
+        float* Ar = p.A1 + row * N;
+        for (int e = lane; e < K2; e += kWave) {
+            const int j = (int)min((unsigned)Ir[e], (unsigned)(N - 1));
+            float acc = 0.0f;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                float kf[EPC];
+                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(smem + j * ROWB + c * 16), kf);
+#pragma unroll
+                for (int y = 0; y < EPC; ++y) acc = fmaf(q[c * EPC + y], kf[y], acc);
+            }
+            Ar[j] = fast_exp2(fmaf(acc, p.scale2, -l2));
+        }
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_map_t(const FirstMapArgs& a, int grid, hipStream_t s) {
+    const int lds = a.g.N * D * (int)sizeof(T);
+    const void* fn = reinterpret_cast<const void*>(first_map_kept_kernel<T, D>);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((first_map_kept_kernel<T, D>), dim3(grid), dim3(kMapWaves * kWave), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int first_map_blocks(int N) { return (N + kMapRows - 1) / kMapRows; }
+
+hipError_t launch_first_map(const FirstMapArgs& a, int dtype, int D, int grid, hipStream_t stream) {
+    if (a.g.N * D * (dtype == 0 ? 4 : 2) > kLdsBytes) return hipErrorInvalidValue;
+    if (dtype == 0) return D == 16 ? launch_map_t<float, 16>(a, grid, stream) : launch_map_t<float, 32>(a, grid, stream);
+    return D == 16 ? launch_map_t<uint16_t, 16>(a, grid, stream) : launch_map_t<uint16_t, 32>(a, grid, stream);
+}
+
+}  // namespace pfa

@@ -78,6 +78,7 @@ struct BackwardArgs {
     int xcd_map;
     float scale;             // 1 / sqrt(d)
     float scale2;            // log2(e) / sqrt(d): base-2 scores of the exact dA^{l-1} pass
+    const float* bias;       // the forward's relative position bias [heads, (2 win - 1)^2], or nullptr
     // dK/dV MFMA kernel: workgroups [0, dkv_full) take a whole window-head each;
     // each further pair (workgroups 8 apart, one XCD) takes the two token halves
     // of one window-head (balances the last round over the CUs)
@@ -116,6 +117,8 @@ struct DenseBwdArgs {
     float* dK;
     float* dV;
     float* Dws;              // workspace [wh, N]: D_i = sum_j P_ij G_ij
+    float* dbias_rows;       // workspace [wh, N / 16, win, 64]: per wave and key row, the dS sums per
+                             // column offset (lane dx + win - 1), or nullptr (no bias gradient)
     Geom g;
     float scale2;            // log2(e) / sqrt(d)
     float scale;             // 1 / sqrt(d)
@@ -123,6 +126,39 @@ struct DenseBwdArgs {
 };
 int dense_bwd_blocks(int N);   // workgroups per window-head (each kernel)
 hipError_t launch_dense_backward(const DenseBwdArgs& a, int dtype, int D, int grid, hipStream_t stream);
+
+// Gradient of the relative position bias table: per window-head tables (of a
+// sparse layer from its kept pairs, of the dense layer from the dQ kernel's rows),
+// then summed over images and windows per head. Fixed summation order throughout.
+struct DbiasArgs {
+    const int32_t* I_l;      // sparse: kept slots [wh, N, K_l]
+    const float* A_l;        // sparse: the layer's map [wh, N, K_l]
+    const float* g_buf;      // sparse: g per kept pair [wh, N, K_l] (the row pass's workspace)
+    const float* rows;       // dense: DenseBwdArgs::dbias_rows
+    float* part;             // workspace [wh, (2 win - 1)^2]: per window-head tables
+    float* dbias;            // [heads, (2 win - 1)^2] output
+    Geom g;
+    int K_l;
+};
+hipError_t launch_dbias_sparse(const DbiasArgs& a, hipStream_t stream);
+hipError_t launch_dbias_dense(const DbiasArgs& a, hipStream_t stream);
+int dbias_sparse_lds(int win);
+
+// Backward of the fused first two layers: the first layer's map at the second
+// layer's kept slots, recomputed into a dense-layout buffer.
+struct FirstMapArgs {
+    const void* Q1;
+    const void* K1;
+    const int32_t* I2;       // [wh, N, K2] the second layer's kept slots
+    const float* lse1;       // [wh, N] the first layer's log denominators
+    float* A1;               // [wh, N, N] written at the kept slots only
+    Geom g;                  // the first layer's geometry (its shift)
+    int K2;
+    float scale2;            // log2(e) / sqrt(d)
+    int blocks_per_wh, xcd_map;
+};
+int first_map_blocks(int N);
+hipError_t launch_first_map(const FirstMapArgs& a, int dtype, int D, int grid, hipStream_t stream);
 
 // Propagation / sparsification of an individualized index matrix.
 struct IetArgs {

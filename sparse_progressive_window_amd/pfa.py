@@ -59,6 +59,20 @@ def load():
         lib.pfa_dense_layer_backward_noalloc.restype = ctypes.c_int
         lib.pfa_dense_layer_backward_workspace.argtypes = [ctypes.POINTER(PfaShape)]
         lib.pfa_dense_layer_backward_workspace.restype = ctypes.c_int64
+        lib.pfa_sparse_layer_backward_rpb.argtypes = ([ctypes.POINTER(PfaShape), P, P, P, P, P, P, i32, i32]
+                                                      + [P] * 10 + [ctypes.c_int64, P])
+        lib.pfa_sparse_layer_backward_rpb.restype = ctypes.c_int
+        lib.pfa_sparse_layer_backward_rpb_workspace.argtypes = [ctypes.POINTER(PfaShape), i32]
+        lib.pfa_sparse_layer_backward_rpb_workspace.restype = ctypes.c_int64
+        lib.pfa_dense_layer_backward_rpb.argtypes = [ctypes.POINTER(PfaShape)] + [P] * 12 + [ctypes.c_int64, P]
+        lib.pfa_dense_layer_backward_rpb.restype = ctypes.c_int
+        lib.pfa_dense_layer_backward_rpb_workspace.argtypes = [ctypes.POINTER(PfaShape)]
+        lib.pfa_dense_layer_backward_rpb_workspace.restype = ctypes.c_int64
+        lib.pfa_first_two_layers_backward.argtypes = ([ctypes.POINTER(PfaShape), i32, i32] + [P] * 6 + [i32]
+                                                      + [P] * 13 + [ctypes.c_int64, P])
+        lib.pfa_first_two_layers_backward.restype = ctypes.c_int
+        lib.pfa_first_two_layers_backward_workspace.argtypes = [ctypes.POINTER(PfaShape), i32]
+        lib.pfa_first_two_layers_backward_workspace.restype = ctypes.c_int64
         lib.pfa_iet_propagate.argtypes = [i32, i32, i32, i32, P, P, i32, i32, P, P, P, ctypes.c_int64, P]
         lib.pfa_iet_propagate.restype = ctypes.c_int
         lib.pfa_iet_propagate_workspace.argtypes = [i32, i32, i32, i32]
@@ -241,6 +255,47 @@ def first_two_layers(Q1, K1, V1, Q2, K2, V2, K2_keep, *, win, shift1=0, shift2=0
     return O1, I2, A2, O2
 
 
+def first_two_layers_backward(Q1, K1, V1, Q2, K2, V2, lse1, I2, A2, dO1, dO2, dA2=None, *, win, shift1=0,
+                              shift2=0, out=None, workspace=None):
+    """Backward of first_two_layers: lse1, I2, A2 = the forward's outputs (lse1
+    [B, heads, nwin, N]); dO1, dO2 fp32; dA2 = gradient of A2 or None. Returns
+    (dQ1, dK1, dV1, dQ2, dK2, dV2) in fp32."""
+    _check_qkv(Q1, K1, V1)
+    _check_qkv(Q2, K2, V2)
+    if Q1.shape != Q2.shape or Q1.dtype != Q2.dtype:
+        raise ValueError("both layers' inputs must share shape and dtype")
+    lead, N = _geometry(Q1, win)
+    K2_keep = I2.shape[-1]
+    rows = _prod(lead) * N
+    _expect(lse1, rows, torch.float32, "lse1")
+    _expect(I2, rows * K2_keep, torch.int32, "I2")
+    _expect(A2, rows * K2_keep, torch.float32, "A2")
+    _expect(dO1, Q1.numel(), torch.float32, "dO1")
+    _expect(dO2, Q1.numel(), torch.float32, "dO2")
+    _expect(dA2, rows * K2_keep, torch.float32, "dA2")
+    dev = Q1.device
+    outs = out if out is not None else tuple(torch.empty(Q1.shape, dtype=torch.float32, device=dev)
+                                             for _ in range(6))
+    for t, n in zip(outs, ("dQ1", "dK1", "dV1", "dQ2", "dK2", "dV2")):
+        _expect(t, Q1.numel(), torch.float32, n)
+    shape = make_shape(Q1, win, 0)
+    need = int(load().pfa_first_two_layers_backward_workspace(ctypes.byref(shape), int(K2_keep)))
+    if need < 0:
+        raise PfaError("pfa_first_two_layers_backward_workspace", need)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must be a device tensor of at least {need} bytes")
+    rc = load().pfa_first_two_layers_backward(ctypes.byref(shape), int(shift1), int(shift2), _ptr(Q1), _ptr(K1),
+                                              _ptr(V1), _ptr(Q2), _ptr(K2), _ptr(V2), int(K2_keep), _ptr(lse1),
+                                              _ptr(I2), _ptr(A2), _ptr(dO1), _ptr(dO2), _ptr(dA2),
+                                              *(_ptr(t) for t in outs), _ptr(workspace),
+                                              workspace.numel() * workspace.element_size(), _stream())
+    if rc != 0:
+        raise PfaError("pfa_first_two_layers_backward", rc)
+    return tuple(outs)
+
+
 def sparse_layer_backward(Q, K, V, I_prev, A_prev, I_l, A_l, dO, dA_l=None, *, win, shift=0, K_prev=None,
                           want_dA_prev=True, out=None, workspace=None):
     """Backward pass of a window-mode sparse layer with its kept sets fixed.
@@ -251,6 +306,21 @@ def sparse_layer_backward(Q, K, V, I_prev, A_prev, I_l, A_l, dO, dA_l=None, *, w
     (or A_prev is None). ``out`` = optional preallocated (dQ, dK, dV, dA_prev or
     None); ``workspace`` = optional uint8 device tensor of at least
     ``backward_workspace_bytes`` bytes."""
+    return _sparse_backward(Q, K, V, I_prev, A_prev, I_l, A_l, dO, dA_l, win, shift, K_prev, want_dA_prev, out,
+                            workspace, None, False)[:4]
+
+
+def sparse_layer_backward_rpb(Q, K, V, bias, I_prev, A_prev, I_l, A_l, dO, dA_l=None, *, win, shift=0,
+                              K_prev=None, want_dA_prev=True, want_dbias=True, out=None, workspace=None):
+    """sparse_layer_backward of a layer computed with the relative position bias
+    ``bias`` [heads, (2 win - 1)^2] (fp32, device). Returns (dQ, dK, dV, dA_prev,
+    dbias); dbias [heads, (2 win - 1)^2] fp32, or None when not wanted."""
+    return _sparse_backward(Q, K, V, I_prev, A_prev, I_l, A_l, dO, dA_l, win, shift, K_prev, want_dA_prev, out,
+                            workspace, bias, want_dbias)
+
+
+def _sparse_backward(Q, K, V, I_prev, A_prev, I_l, A_l, dO, dA_l, win, shift, K_prev, want_dA_prev, out,
+                     workspace, bias, want_dbias):
     _check_qkv(Q, K, V)
     lead, N = _geometry(Q, win)
     K_l = I_l.shape[-1]
@@ -275,19 +345,39 @@ def sparse_layer_backward(Q, K, V, I_prev, A_prev, I_l, A_l, dO, dA_l=None, *, w
     for t, n in ((dQ, "dQ"), (dK, "dK"), (dV, "dV")):
         _expect(t, Q.numel(), torch.float32, n)
     _expect(dAp, rows * K_prev, torch.float32, "dA_prev")
+    _check_bias(bias, Q, win)
+    dbias = None
+    if want_dbias:
+        if bias is None:
+            raise ValueError("the bias gradient needs the forward's bias")
+        dbias = torch.empty(bias.shape, dtype=torch.float32, device=dev)
     shape = make_shape(Q, win, shift)
-    need = backward_workspace_bytes(Q, K_l, win=win, shift=shift)
+    if dbias is not None:
+        need = int(load().pfa_sparse_layer_backward_rpb_workspace(ctypes.byref(shape), int(K_l)))
+        if need < 0:
+            raise PfaError("pfa_sparse_layer_backward_rpb_workspace", need)
+    else:
+        need = backward_workspace_bytes(Q, K_l, win=win, shift=shift)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace must be a device tensor of at least {need} bytes")
-    rc = load().pfa_sparse_layer_backward(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(I_prev),
-                                          _ptr(A_prev), K_prev, K_l, _ptr(I_l), _ptr(A_l), _ptr(dO), _ptr(dA_l),
-                                          _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dAp), _ptr(workspace),
-                                          workspace.numel() * workspace.element_size(), _stream())
-    if rc != 0:
-        raise PfaError("pfa_sparse_layer_backward", rc)
-    return dQ, dK, dV, dAp
+    nbytes = workspace.numel() * workspace.element_size()
+    if bias is None:
+        rc = load().pfa_sparse_layer_backward(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(I_prev),
+                                              _ptr(A_prev), K_prev, K_l, _ptr(I_l), _ptr(A_l), _ptr(dO), _ptr(dA_l),
+                                              _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dAp), _ptr(workspace), nbytes,
+                                              _stream())
+        if rc != 0:
+            raise PfaError("pfa_sparse_layer_backward", rc)
+    else:
+        rc = load().pfa_sparse_layer_backward_rpb(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(bias),
+                                                  _ptr(I_prev), _ptr(A_prev), K_prev, K_l, _ptr(I_l), _ptr(A_l),
+                                                  _ptr(dO), _ptr(dA_l), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dAp),
+                                                  _ptr(dbias), _ptr(workspace), nbytes, _stream())
+        if rc != 0:
+            raise PfaError("pfa_sparse_layer_backward_rpb", rc)
+    return dQ, dK, dV, dAp, dbias
 
 
 def dense_layer_backward(Q, K, V, lse, dO, dA=None, *, win, shift=0, bias=None, out=None, workspace=None):
@@ -322,6 +412,42 @@ def dense_layer_backward(Q, K, V, lse, dO, dA=None, *, win, shift=0, bias=None, 
     if rc != 0:
         raise PfaError("pfa_dense_layer_backward", rc)
     return dQ, dK, dV
+
+
+def dense_layer_backward_rpb(Q, K, V, bias, lse, dO, dA=None, *, win, shift=0, out=None, workspace=None):
+    """dense_layer_backward of a layer computed with the relative position bias
+    ``bias`` [heads, (2 win - 1)^2], with its gradient: returns (dQ, dK, dV, dbias)."""
+    _check_qkv(Q, K, V)
+    lead, N = _geometry(Q, win)
+    dev = Q.device
+    if out is None:
+        dQ, dK, dV = (torch.empty(Q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+    else:
+        dQ, dK, dV = out
+    rows = _prod(lead) * N
+    _expect(lse, rows, torch.float32, "lse")
+    _expect(dO, Q.numel(), torch.float32, "dO")
+    _expect(dA, rows * N, torch.float32, "dA")
+    for t, n in ((dQ, "dQ"), (dK, "dK"), (dV, "dV")):
+        _expect(t, Q.numel(), torch.float32, n)
+    if bias is None:
+        raise ValueError("the bias gradient needs the forward's bias")
+    _check_bias(bias, Q, win)
+    dbias = torch.empty(bias.shape, dtype=torch.float32, device=dev)
+    shape = make_shape(Q, win, shift)
+    need = int(load().pfa_dense_layer_backward_rpb_workspace(ctypes.byref(shape)))
+    if need < 0:
+        raise PfaError("pfa_dense_layer_backward_rpb_workspace", need)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must be a device tensor of at least {need} bytes")
+    rc = load().pfa_dense_layer_backward_rpb(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(bias), _ptr(lse),
+                                             _ptr(dO), _ptr(dA), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dbias),
+                                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
+    if rc != 0:
+        raise PfaError("pfa_dense_layer_backward_rpb", rc)
+    return dQ, dK, dV, dbias
 
 
 def dense_layer_backward_noalloc(Q, K, V, lse, dO, dA=None, *, win, shift=0, bias=None, out=None):

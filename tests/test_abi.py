@@ -33,7 +33,10 @@ def test_exports_every_declared_symbol(lib):
     assert {"pfa_dense_layer", "pfa_sparse_layer", "pfa_first_two_layers", "pfa_sparse_layer_backward",
             "pfa_sparse_layer_backward_workspace", "pfa_iet_propagate", "pfa_iet_propagate_workspace",
             "pfa_dense_layer_rpb", "pfa_sparse_layer_rpb", "pfa_dense_layer_backward",
-            "pfa_dense_layer_backward_workspace",
+            "pfa_dense_layer_backward_workspace", "pfa_sparse_layer_backward_rpb",
+            "pfa_sparse_layer_backward_rpb_workspace", "pfa_dense_layer_backward_rpb",
+            "pfa_dense_layer_backward_rpb_workspace", "pfa_first_two_layers_backward",
+            "pfa_first_two_layers_backward_workspace",
             "pfa_strerror", "pfa_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -51,10 +54,11 @@ def test_timing_calls_without_device(lib):
     assert lib.pfa_timing_read(None, None, 0, None, None) == -1
     assert lib.pfa_timing_read(None, None, 4, ctypes.byref(n), None) == -1
     assert lib.pfa_timing_read(None, None, -1, ctypes.byref(n), None) == -1
-    names = [lib.pfa_kernel_name(k).decode() for k in range(12)]
+    names = [lib.pfa_kernel_name(k).decode() for k in range(14)]
     assert names == ["dense_layer_kernel", "all_cand", "sparse_layer_kernel",
                      "sparse_layer_kernel(select)", "aggregate", "iota_rows_kernel", "bwd_rows_kernel",
-                     "bwd_dkv", "iet_rank_kernel", "iet_union_kernel", "dense_bwd", "bwd_exact_dap_kernel"]
+                     "bwd_dkv", "iet_rank_kernel", "iet_union_kernel", "dense_bwd", "bwd_exact_dap_kernel",
+                     "dbias", "first_map_kept_kernel"]
     assert lib.pfa_kernel_name(99) == b"unknown"
 
 
@@ -163,7 +167,7 @@ def test_backward_validation(lib):
                                              A_prev, K_prev, K_l, FAKE, FAKE, dO, None, *grads, dA_prev, ws,
                                              ws_bytes, None)
     assert bwd(None) == -1
-    assert bwd(shape(win=0)) == -2                               # window mode only
+    assert bwd(shape(win=0, H=128, W=128), K_prev=64, K_l=16, ws_bytes=1 << 30) == -2   # global: dA_prev <= 8192 tokens
     assert bwd(shape(d=8)) == -2
     assert bwd(shape(), K_l=0) == -1
     assert bwd(shape(), K_l=300, K_prev=256) == -1               # K_l > K_prev
@@ -179,6 +183,53 @@ def test_backward_validation(lib):
         2 * 3 * 2 * 1024 * (16 + 1) * 4   # g per kept pair, one flag per row
     assert lib.pfa_sparse_layer_backward_workspace(ctypes.byref(shape()), 0) == -1
     assert lib.pfa_sparse_layer_backward_workspace(ctypes.byref(shape(d=8)), 16) == -2
+
+
+def test_backward_rpb_validation(lib):
+    nrel = 63 * 63
+    ws_full = 1 * 1 * 1024 * (64 + 1) * 4 + nrel * 4
+
+    def bwd(s, bias=FAKE, dbias=FAKE, ws_bytes=ws_full):
+        return lib.pfa_sparse_layer_backward_rpb(ctypes.byref(s), FAKE, FAKE, FAKE, bias, FAKE, FAKE, 256, 64, FAKE,
+                                                 FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, dbias, FAKE, ws_bytes,
+                                                 None)
+    assert bwd(shape(), bias=None) == -1                          # dbias needs the bias
+    assert bwd(shape(), ws_bytes=ws_full - 4) == -1               # no room for the per-window-head tables
+    assert bwd(shape(win=0)) == -2                                # no bias in global mode
+    assert lib.pfa_sparse_layer_backward_rpb_workspace(ctypes.byref(shape(win=0)), 64) == -2
+    assert lib.pfa_sparse_layer_backward_rpb_workspace(ctypes.byref(shape()), 64) == ws_full
+    assert lib.pfa_sparse_layer_backward_rpb_workspace(ctypes.byref(shape(B=2, heads=3, H=64, W=32, win=16)),
+                                                       16) == 2 * 3 * 8 * (256 * 17 * 4 + 31 * 31 * 4)
+
+    def db(s, bias=FAKE, dbias=FAKE, ws_bytes=1 << 30):
+        return lib.pfa_dense_layer_backward_rpb(ctypes.byref(s), FAKE, FAKE, FAKE, bias, FAKE, FAKE, None, FAKE,
+                                                FAKE, FAKE, dbias, FAKE, ws_bytes, None)
+    dws = 1024 * 4 + 64 * 32 * 64 * 4 + nrel * 4                  # D_i, per-wave rows, one table
+    assert lib.pfa_dense_layer_backward_rpb_workspace(ctypes.byref(shape())) == dws
+    assert lib.pfa_dense_layer_backward_rpb_workspace(ctypes.byref(shape(win=0))) == -2
+    assert db(shape(), bias=None) == -1
+    assert db(shape(), ws_bytes=dws - 4) == -1
+    assert db(shape(win=8, H=16, W=16)) == -2                     # a bias needs win % 16 == 0
+
+
+def test_first_two_layers_backward_validation(lib):
+    ws = 2 * 1024 * 1024 * 4 + 1024 * 257 * 4 + 1024 * 4   # A^1, dA^1, sparse and dense workspaces
+
+    def fb(s, shifts=(0, 16), K2=256, ptrs=(FAKE,) * 6, ws_ptr=FAKE, ws_bytes=ws):
+        return lib.pfa_first_two_layers_backward(ctypes.byref(s), shifts[0], shifts[1], *([FAKE] * 6), K2, FAKE,
+                                                 FAKE, FAKE, FAKE, FAKE, None, *ptrs, ws_ptr, ws_bytes, None)
+    assert lib.pfa_first_two_layers_backward_workspace(ctypes.byref(shape()), 256) == ws
+    assert lib.pfa_first_two_layers_backward_workspace(ctypes.byref(shape(win=0)), 256) == -2
+    assert lib.pfa_first_two_layers_backward_workspace(ctypes.byref(shape()), 0) == -1
+    assert fb(shape(shift=16)) == -1                              # shifts come as arguments
+    assert fb(shape(), shifts=(0, 32)) == -1
+    assert fb(shape(), K2=0) == -1
+    assert fb(shape(), ptrs=(FAKE, FAKE, None, FAKE, FAKE, FAKE)) == -1
+    assert fb(shape(), ws_bytes=ws - 4) == -1
+    assert fb(shape(), ws_ptr=None) == -1
+    assert fb(shape(win=0)) == -2
+    assert fb(shape(), K2=512, ws_bytes=1 << 30) == -2           # K2 > 256
+    assert fb(shape(win=12, H=24, W=24), shifts=(0, 6), K2=64, ws_bytes=1 << 30) == -2   # win % 8 != 0
 
 
 def test_iet_validation(lib):

@@ -14,7 +14,10 @@ not cover): tol = 1e-5 for fp32 inputs, 2e-3 for bf16 inputs;
     gradients are sums with cancellation, so elementwise relative error is
     ill-posed where an entry is near zero);
   * dA^{l-1}: per row, max |gpu - ref| <= tol * max |ref row|, and exactly 0
-    at every slot the layer dropped.
+    at every slot the layer dropped;
+  * dbias (relative position bias): per head, max |gpu - ref| over the table
+    <= tol * max |ref| over the head's table (each entry is a sum with
+    cancellation over many pairs, as dQ's are).
 """
 
 import numpy as np
@@ -73,6 +76,23 @@ def check_dA_prev(gpu, ref, tol):
     return worst
 
 
+def check_dbias(gpu, ref, tol):
+    """gpu, ref: [heads, (2 win - 1)^2]."""
+    g = np.asarray(gpu, dtype=np.float64)
+    worst = 0.0
+    for h in range(ref.shape[0]):
+        err = np.abs(g[h] - ref[h]).max()
+        scale = np.abs(ref[h]).max()
+        assert err <= tol * scale + 1e-30, f"dbias head {h}: {err / scale:.3e} > {tol}"
+        worst = max(worst, float(err / max(scale, 1e-30)))
+    return worst
+
+
+def bias_table(heads, win, seed, scale=1.0):
+    g = np.random.Generator(np.random.PCG64(seed))
+    return (g.standard_normal((heads, (2 * win - 1) ** 2)) * scale).astype(np.float32)
+
+
 def rand_lists(n_rows, N, K_prev, seed):
     g = np.random.Generator(np.random.PCG64(seed))
     return np.stack([g.permutation(N)[:K_prev] for _ in range(n_rows)]).astype(np.int32)
@@ -85,7 +105,7 @@ def rand_map(shape, seed):
 
 
 def run_case(B, heads, H, W, d, win, shift, K_prev, K_l, dtype, seed, *, implicit=False, with_dA=True,
-             want_dA_prev=True, zero_frac=0.0, subnormal_frac=0.0):
+             want_dA_prev=True, zero_frac=0.0, subnormal_frac=0.0, with_bias=False):
     shape = (B, heads, H, W, d)
     qt, kt, vt = (inputs.draw(seed + t, shape, dtype) for t in range(3))
     N = win * win
@@ -105,22 +125,28 @@ def run_case(B, heads, H, W, d, win, shift, K_prev, K_l, dtype, seed, *, implici
     Qd, Kd, Vd = to_dev(qt), to_dev(kt), to_dev(vt)
     Ipd = None if I_prev is None else torch.from_numpy(I_prev).cuda()
     Apd = torch.from_numpy(A_prev).cuda()
+    table = bias_table(heads, win, seed + 10) if with_bias else None
     fwd = oracle.layer(qt.exact, kt.exact, vt.exact, win=win, shift=shift, K_l=K_l, I_prev=I_prev,
-                       A_prev=A_prev.astype(np.float64))
+                       A_prev=A_prev.astype(np.float64), bias=table)
     I_l = torch.from_numpy(fwd["I"].reshape(lead + (N, K_l))).cuda()
     A_l = torch.from_numpy(fwd["A"].astype(np.float32).reshape(lead + (N, K_l))).cuda()
     dO = inputs.draw(seed + 7, shape, "f32").exact
     dA = inputs.draw(seed + 8, lead + (N, K_l), "f32").exact if with_dA else None
-    dQ, dK, dV, dAp = pfa.sparse_layer_backward(
-        Qd, Kd, Vd, Ipd, Apd, I_l, A_l, torch.from_numpy(dO).cuda(),
-        None if dA is None else torch.from_numpy(dA).cuda(), win=win, shift=shift, K_prev=K_prev,
-        want_dA_prev=want_dA_prev)
+    dOd = torch.from_numpy(dO).cuda()
+    dAd = None if dA is None else torch.from_numpy(dA).cuda()
+    if with_bias:
+        dQ, dK, dV, dAp, dbias = pfa.sparse_layer_backward_rpb(
+            Qd, Kd, Vd, torch.from_numpy(table).cuda(), Ipd, Apd, I_l, A_l, dOd, dAd, win=win, shift=shift,
+            K_prev=K_prev, want_dA_prev=want_dA_prev)
+    else:
+        dQ, dK, dV, dAp = pfa.sparse_layer_backward(Qd, Kd, Vd, Ipd, Apd, I_l, A_l, dOd, dAd, win=win, shift=shift,
+                                                    K_prev=K_prev, want_dA_prev=want_dA_prev)
     torch.cuda.synchronize()
     keep = fwd["I"]
     ref = oracle.layer_backward(qt.exact, kt.exact, vt.exact, win=win, shift=shift, keep=keep, dO=dO,
                                 dA=None if dA is None else dA.reshape(n_wh, N, K_l),
                                 I_prev=None if I_prev is None else I_prev.reshape(n_wh, N, K_prev),
-                                A_prev=A_prev.reshape(n_wh, N, K_prev), prev_compact=True)
+                                A_prev=A_prev.reshape(n_wh, N, K_prev), prev_compact=True, bias=table)
     tol = parity.TOL[dtype]
     gpu = {"dQ": dQ.cpu().numpy(), "dK": dK.cpu().numpy(), "dV": dV.cpu().numpy()}
     st = check_grads(gpu, ref, range(n_wh), heads, win, shift, tol)
@@ -128,6 +154,8 @@ def run_case(B, heads, H, W, d, win, shift, K_prev, K_l, dtype, seed, *, implici
         st["dA_prev"] = check_dA_prev(dAp.view(n_wh, N, K_prev).cpu().numpy(), ref["dA_prev"], tol)
     else:
         assert dAp is None
+    if with_bias:
+        st["dbias"] = check_dbias(dbias.cpu().numpy(), ref["dbias"], tol)
     return st
 
 
@@ -179,6 +207,29 @@ def test_backward_random(dtype, d, win, shift, K_prev, K_l, implicit, with_dA, c
                   with_dA=with_dA)
     with capsys.disabled():
         print(f"  backward {dtype} d={d} win={win} K {K_prev}->{K_l}: {st}", flush=True)
+
+
+RPB_CASES = [
+    # dtype, d, win, shift, K_prev, K_l, implicit, zero_frac
+    ("f32", 32, 32, 16, 256, 128, False, 0.0),
+    ("bf16", 32, 32, 0, 1024, 256, True, 0.0),
+    ("f32", 32, 32, 16, 1024, 256, True, 0.9),     # zero weights: exact dA^{l-1} from scores with the bias
+    ("bf16", 32, 32, 16, 64, 16, False, 0.0),
+    ("f32", 16, 16, 8, 100, 37, False, 0.0),
+    ("bf16", 16, 16, 0, 256, 64, True, 0.0),
+    ("f32", 16, 16, 0, 64, 40, False, 0.7),
+]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,d,win,shift,K_prev,K_l,implicit,zero_frac", RPB_CASES)
+def test_backward_with_bias(dtype, d, win, shift, K_prev, K_l, implicit, zero_frac, capsys):
+    """Sparse layer computed with a relative position bias: every gradient,
+    including the bias table's, against the oracle backward with the same bias."""
+    st = run_case(2, 2, 2 * win, 2 * win, d, win, shift, K_prev, K_l, dtype, 1500 + K_l + d, implicit=implicit,
+                  zero_frac=zero_frac, with_bias=True)
+    with capsys.disabled():
+        print(f"  backward with bias {dtype} d={d} win={win} K {K_prev}->{K_l}: {st}", flush=True)
 
 
 @pytest.mark.timeout(300)
@@ -258,6 +309,8 @@ DENSE = [
     ("bf16", 16, 8, 4, True, False),
     ("f32", 32, 32, 16, True, True),
     ("bf16", 16, 16, 0, True, True),
+    ("bf16", 32, 32, 0, False, True),
+    ("f32", 16, 16, 8, False, True),
     ("f32", 32, 24, 12, True, False),        # N = 576: the last workgroup has idle waves
 ]
 
@@ -281,14 +334,168 @@ def test_dense_backward(dtype, d, win, shift, with_dA, with_bias, capsys):
     lse = oracle.dense_lse(qt.exact, kt.exact, win=win, shift=shift, bias=table).astype(np.float32)
     dO = inputs.draw(1320, shape, "f32").exact
     dA = inputs.draw(1321, lead + (N, N), "f32").exact if with_dA else None
-    dQ, dK, dV = pfa.dense_layer_backward(to_dev(qt), to_dev(kt), to_dev(vt), torch.from_numpy(lse).cuda().view(
-        lead + (N,)), torch.from_numpy(dO).cuda(), None if dA is None else torch.from_numpy(dA).cuda(), win=win,
-        shift=shift, bias=None if table is None else torch.from_numpy(table).cuda())
+    args = (to_dev(qt), to_dev(kt), to_dev(vt))
+    lse_d = torch.from_numpy(lse).cuda().view(lead + (N,))
+    dA_d = None if dA is None else torch.from_numpy(dA).cuda()
+    if with_bias:   # with the bias gradient (the plain call is checked against it below)
+        dQ, dK, dV, dbias = pfa.dense_layer_backward_rpb(*args, torch.from_numpy(table).cuda(), lse_d,
+                                                         torch.from_numpy(dO).cuda(), dA_d, win=win, shift=shift)
+        plain = pfa.dense_layer_backward(*args, lse_d, torch.from_numpy(dO).cuda(), dA_d, win=win, shift=shift,
+                                         bias=torch.from_numpy(table).cuda())
+        torch.cuda.synchronize()
+        for x, y in zip((dQ, dK, dV), plain):
+            assert torch.equal(x, y), "the bias gradient changed the other gradients"
+    else:
+        dQ, dK, dV = pfa.dense_layer_backward(*args, lse_d, torch.from_numpy(dO).cuda(), dA_d, win=win, shift=shift)
     torch.cuda.synchronize()
     keep = np.broadcast_to(np.arange(N, dtype=np.int32), (n_wh, N, N)).copy()
     ref = oracle.layer_backward(qt.exact, kt.exact, vt.exact, win=win, shift=shift, keep=keep, dO=dO,
                                 dA=None if dA is None else dA.reshape(n_wh, N, N), bias=table)
     gpu = {"dQ": dQ.cpu().numpy(), "dK": dK.cpu().numpy(), "dV": dV.cpu().numpy()}
     st = check_grads(gpu, ref, range(n_wh), heads, win, shift, parity.TOL[dtype])
+    if with_bias:
+        st["dbias"] = check_dbias(dbias.cpu().numpy(), ref["dbias"], parity.TOL[dtype])
     with capsys.disabled():
         print(f"  dense backward {dtype} d={d} win={win} dA={with_dA} bias={with_bias}: {st}", flush=True)
+
+
+def check_grads_global(gpu, ref, tol):
+    """Global mode: per (image, head) plane, max |gpu - ref| <= tol * max |ref|."""
+    worst = {}
+    for name in ("dQ", "dK", "dV"):
+        g = np.asarray(gpu[name], dtype=np.float64)
+        r = ref[name]
+        w_max = 0.0
+        for b in range(r.shape[0]):
+            for h in range(r.shape[1]):
+                err = np.abs(g[b, h] - r[b, h]).max()
+                scale = np.abs(r[b, h]).max()
+                assert err <= tol * scale + 1e-30, f"{name} plane ({b}, {h}): {err / scale:.3e} > {tol}"
+                w_max = max(w_max, float(err / max(scale, 1e-30)))
+        worst[name] = w_max
+    return worst
+
+
+def run_global_case(B, heads, H, W, d, K_prev, K_l, dtype, seed, *, with_A_prev, with_dA=True, zero_frac=0.0,
+                    I_shared=None):
+    """Global mode (win = 0): each token's candidates are K_prev tokens of the whole
+    map (seeded distinct random lists per row and head, or I_shared [N, K_prev]
+    for every head)."""
+    shape = (B, heads, H, W, d)
+    qt, kt, vt = (inputs.draw(seed + t, shape, dtype) for t in range(3))
+    N = H * W
+    n_wh = B * heads
+    lead = (B, heads)
+    if I_shared is not None:
+        I_prev = np.broadcast_to(I_shared, lead + (N, K_prev)).copy()
+    else:
+        I_prev = rand_lists(n_wh * N, N, K_prev, seed + 5).reshape(lead + (N, K_prev))
+    A_prev = None
+    if with_A_prev:
+        A_prev = rand_map(lead + (N, K_prev), seed + 6)
+        if zero_frac:
+            u = np.random.Generator(np.random.PCG64(seed + 9)).random(A_prev.shape)
+            A_prev[u < zero_frac] = 0.0
+            A_prev[..., 0] = np.maximum(A_prev[..., 0], np.float32(0.5 / K_prev))
+    fwd = oracle.layer(qt.exact, kt.exact, vt.exact, win=0, shift=0, K_l=K_l,
+                       I_prev=I_prev.reshape(B, heads, 1, N, K_prev),
+                       A_prev=None if A_prev is None else A_prev.reshape(B, heads, 1, N, K_prev).astype(np.float64))
+    I_l = torch.from_numpy(fwd["I"].reshape(lead + (N, K_l))).cuda()
+    A_l = torch.from_numpy(fwd["A"].astype(np.float32).reshape(lead + (N, K_l))).cuda()
+    dO = inputs.draw(seed + 7, shape, "f32").exact
+    dA = inputs.draw(seed + 8, lead + (N, K_l), "f32").exact if with_dA else None
+    dQ, dK, dV, dAp = pfa.sparse_layer_backward(
+        to_dev(qt), to_dev(kt), to_dev(vt), torch.from_numpy(I_prev).cuda(),
+        None if A_prev is None else torch.from_numpy(A_prev).cuda(), I_l, A_l, torch.from_numpy(dO).cuda(),
+        None if dA is None else torch.from_numpy(dA).cuda(), win=0, shift=0, K_prev=K_prev)
+    torch.cuda.synchronize()
+    ref = oracle.layer_backward(qt.exact, kt.exact, vt.exact, win=0, shift=0, keep=fwd["I"], dO=dO,
+                                dA=None if dA is None else dA.reshape(n_wh, N, K_l),
+                                I_prev=I_prev.reshape(n_wh, N, K_prev),
+                                A_prev=None if A_prev is None else A_prev.reshape(n_wh, N, K_prev),
+                                prev_compact=True)
+    tol = parity.TOL[dtype]
+    st = check_grads_global({"dQ": dQ.cpu().numpy(), "dK": dK.cpu().numpy(), "dV": dV.cpu().numpy()}, ref, tol)
+    if with_A_prev:
+        st["dA_prev"] = check_dA_prev(dAp.view(n_wh, N, K_prev).cpu().numpy(), ref["dA_prev"], tol)
+    else:
+        assert dAp is None
+    return st
+
+
+GLOBAL_CASES = [
+    # dtype, d, H, W, K_prev, K_l, with_A_prev, zero_frac
+    ("bf16", 32, 64, 64, 64, 64, False, 0.0),      # 4096 tokens: gathers from L2, 4 token ranges for dK/dV
+    ("f32", 32, 64, 64, 64, 32, True, 0.0),        # selection and dA^{l-1}
+    ("bf16", 16, 48, 64, 100, 37, True, 0.7),      # zero weights: exact dA^{l-1}, slots found by search
+    ("f32", 32, 32, 32, 256, 64, True, 0.0),       # 1024 tokens: staged like a window
+    ("bf16", 32, 18, 18, 40, 40, False, 0.0),      # 324 tokens (not a multiple of 16)
+]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,d,H,W,K_prev,K_l,with_A_prev,zero_frac", GLOBAL_CASES)
+def test_backward_global_mode(dtype, d, H, W, K_prev, K_l, with_A_prev, zero_frac, capsys):
+    st = run_global_case(1, 2, H, W, d, K_prev, K_l, dtype, 1600 + K_l + d, with_A_prev=with_A_prev,
+                         zero_frac=zero_frac)
+    with capsys.disabled():
+        print(f"  global backward {dtype} d={d} {H}x{W} K {K_prev}->{K_l}: {st}", flush=True)
+
+
+@pytest.mark.timeout(300)
+def test_backward_global_workload(capsys):
+    """The individualized-attention workload (one index matrix shared by the 6
+    heads, k = 64 kept of 64): its backward against the oracle's."""
+    w = workloads.GLOBAL64
+    st = run_global_case(w.B, w.heads, w.H, w.W, w.d, w.k_global, w.k_global, w.dtype, 1650, with_A_prev=False,
+                         I_shared=inputs.global_index(w))
+    with capsys.disabled():
+        print(f"  {w.name} backward: {st}", flush=True)
+
+
+FUSED_BWD = [
+    # dtype, d, (shift1, shift2), K2
+    ("bf16", 32, (0, 16), 256),
+    ("bf16", 16, (16, 0), 128),
+    ("f32", 16, (0, 16), 256),
+]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,d,shifts,K2", FUSED_BWD)
+def test_first_two_layers_backward(dtype, d, shifts, K2, capsys):
+    """Backward of the fused first two layers against the oracle's unfused chain:
+    the second layer's backward (every slot a candidate, A^{l-1} = the first
+    layer's map) and then the dense first layer's with that dA^1. The GPU takes the
+    oracle's lse1, I2 and A2 (rounded to fp32), as the forward would give them."""
+    B, heads, win, H, W = 1, 2, 32, 64, 64
+    shape = (B, heads, H, W, d)
+    q1, k1, v1, q2, k2, v2 = (inputs.draw(1700 + d + K2 + t, shape, dtype) for t in range(6))
+    N, n_wh, lead = win * win, B * heads * 4, (B, heads, 4)
+    s1, s2 = shifts
+    ref1 = oracle.layer(q1.exact, k1.exact, v1.exact, win=win, shift=s1, K_l=N)
+    lse1 = oracle.dense_lse(q1.exact, k1.exact, win=win, shift=s1).astype(np.float32)
+    ref2 = oracle.layer(q2.exact, k2.exact, v2.exact, win=win, shift=s2, K_l=K2, I_prev=None, A_prev=ref1["A"],
+                        prev_compact=True)
+    dO1 = inputs.draw(1790, shape, "f32").exact
+    dO2 = inputs.draw(1791, shape, "f32").exact
+    dA2 = inputs.draw(1792, lead + (N, K2), "f32").exact
+    outs = pfa.first_two_layers_backward(
+        *(to_dev(t) for t in (q1, k1, v1, q2, k2, v2)), torch.from_numpy(lse1).cuda().view(lead + (N,)),
+        torch.from_numpy(ref2["I"].reshape(lead + (N, K2))).cuda(),
+        torch.from_numpy(ref2["A"].astype(np.float32).reshape(lead + (N, K2))).cuda(),
+        torch.from_numpy(dO1).cuda(), torch.from_numpy(dO2).cuda(), torch.from_numpy(dA2).cuda(), win=win,
+        shift1=s1, shift2=s2)
+    torch.cuda.synchronize()
+    bwd2 = oracle.layer_backward(q2.exact, k2.exact, v2.exact, win=win, shift=s2, keep=ref2["I"], dO=dO2,
+                                 dA=dA2.reshape(n_wh, N, K2), I_prev=None, A_prev=ref1["A"], prev_compact=True)
+    keep1 = np.broadcast_to(np.arange(N, dtype=np.int32), (n_wh, N, N)).copy()
+    bwd1 = oracle.layer_backward(q1.exact, k1.exact, v1.exact, win=win, shift=s1, keep=keep1, dO=dO1,
+                                 dA=bwd2["dA_prev"])
+    tol = parity.TOL[dtype]
+    g = [t.cpu().numpy() for t in outs]
+    st1 = check_grads({"dQ": g[0], "dK": g[1], "dV": g[2]}, bwd1, range(n_wh), heads, win, s1, tol)
+    st2 = check_grads({"dQ": g[3], "dK": g[4], "dV": g[5]}, bwd2, range(n_wh), heads, win, s2, tol)
+    with capsys.disabled():
+        print(f"  fused layers 1-2 backward {dtype} d={d} shifts={shifts} K2={K2}: layer 1 {st1}; layer 2 {st2}",
+              flush=True)
