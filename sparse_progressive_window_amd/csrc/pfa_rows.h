@@ -17,7 +17,7 @@ constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7 - i inside each 8-lane ha
 
 template <int CTRL>
 __device__ __forceinline__ int dpp(int v) {
-    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
 }
 template <int CTRL>
 __device__ __forceinline__ float dppf(float v) {

@@ -1016,7 +1016,7 @@ __global__ __launch_bounds__(NW * kWave) void aggregate_kernel(const SparseArgs 
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 if (e0 + x >= cnt) break;   // padding past K_l: no term (0 * a non-finite V would be NaN)
-                const int j = min(max(jv[x], 0), N - 1);
+                const int j = (int)min((unsigned)jv[x], (unsigned)(N - 1));
                 float vf[EPC];
                 Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(smem + j * ROWB + vchunk * 16), vf);
 #pragma unroll
@@ -1086,8 +1086,9 @@ __global__ __launch_bounds__(NW * kWave) void aggregate_rows_kernel(const Sparse
     const unsigned char* vbase = smem + vchunk * 16;   // this lane's 16-byte chunk of every V row
     for (; base < row1; base += NW * R) {
         // stage byte offsets of the V rows (slot clamped to the window: memory safety only)
-        const int4 off = make_int4(min(max(jn.x, 0), N - 1) * ROWB, min(max(jn.y, 0), N - 1) * ROWB,
-                                   min(max(jn.z, 0), N - 1) * ROWB, min(max(jn.w, 0), N - 1) * ROWB);
+        const unsigned nm = (unsigned)(N - 1);
+        const int4 off = make_int4((int)min((unsigned)jn.x, nm) * ROWB, (int)min((unsigned)jn.y, nm) * ROWB,
+                                   (int)min((unsigned)jn.z, nm) * ROWB, (int)min((unsigned)jn.w, nm) * ROWB);
         *reinterpret_cast<int4*>(sj + lane * 4) = off;
         *reinterpret_cast<float4*>(sw + lane * 4) = wn;
         if (base + NW * R < row1) load(base + NW * R);
@@ -1152,8 +1153,6 @@ __global__ __launch_bounds__(NW * kWave) void aggregate_quads_kernel(const Spars
     const size_t plane = (size_t)w.bh * g.H * g.W * D;
     const T* Vh = static_cast<const T*>(p.V) + plane;
     float* Oh = p.O_out + plane;
-    stage_rows<T, D>(smem, ROWB, Vh, g, w.wy, w.wx);
-    __syncthreads();
 
     const int K_l = p.K_l;   // a multiple of 4, at most 4 GL
     const int row0 = w.part * p.rows_per_block;
@@ -1161,15 +1160,28 @@ __global__ __launch_bounds__(NW * kWave) void aggregate_quads_kernel(const Spars
     const int32_t* Iw = p.I_out + (size_t)w.wh * N * K_l;
     const float* Aw = p.A_out + (size_t)w.wh * N * K_l;
     const int e0 = GL * c + 4 * q;   // this lane's entries: step c of quad q
+    // a row's entries are loaded one iteration ahead (the first before the staging)
+    auto load_entries = [&](int b, int4& jv, float4& wv) {
+        const int i = b + grp;
+        jv = make_int4(0, 0, 0, 0);
+        wv = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i < row1 && e0 < K_l) {
+            jv = *reinterpret_cast<const int4*>(Iw + (size_t)i * K_l + e0);
+            wv = *reinterpret_cast<const float4*>(Aw + (size_t)i * K_l + e0);
+        }
+    };
+    int4 jn;
+    float4 wn;
+    load_entries(row0 + wave * R, jn, wn);
+    stage_rows<T, D>(smem, ROWB, Vh, g, w.wy, w.wx);
+    __syncthreads();
+
     for (int base = row0 + wave * R; base < row1; base += NW * R) {
         const int i = base + grp;
         const bool active = i < row1;
-        int4 jm = make_int4(0, 0, 0, 0);
-        float4 wm = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (active && e0 < K_l) {
-            jm = *reinterpret_cast<const int4*>(Iw + (size_t)i * K_l + e0);
-            wm = *reinterpret_cast<const float4*>(Aw + (size_t)i * K_l + e0);
-        }
+        const int4 jm = jn;
+        const float4 wm = wn;
+        if (base + NW * R < row1) load_entries(base + NW * R, jn, wn);
         float acc[EPC];
 #pragma unroll
         for (int y = 0; y < EPC; ++y) acc[y] = 0.0f;
@@ -1183,7 +1195,7 @@ __global__ __launch_bounds__(NW * kWave) void aggregate_quads_kernel(const Spars
             if (GL * KC + 4 * q >= K_l) return;
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                const int j = min(max(jk[x], 0), N - 1);   // memory safety only
+                const int j = (int)min((unsigned)jk[x], (unsigned)(N - 1));   // memory safety only
                 float vf[EPC];
                 Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(smem + j * ROWB + c * 16), vf);
 #pragma unroll
