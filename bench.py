@@ -38,7 +38,9 @@ HEADLINE = "map640x384_h6_d32_bf16_6blocks"
 
 # kernel kinds of the library's timing calls (pfa_kernel_kind)
 (DENSE, ALL_CAND, SPARSE, SELECT, AGGREGATE, IOTA, BWD_ROWS, BWD_SCATTER, IET_RANK, IET_UNION, DENSE_BWD,
- BWD_EXACT, DBIAS) = range(13)
+ BWD_EXACT, DBIAS, FIRST_MAP) = range(14)
+FUSED_BWD_KINDS = {FIRST_MAP: "first_map", BWD_ROWS: "bwd_rows", BWD_EXACT: "bwd_exact", BWD_SCATTER: "bwd_dkv",
+                   DENSE_BWD: "dense_bwd"}
 
 
 def kernel_bytes(w, l, kind, i_prev_implicit, split, fused=False):
@@ -404,7 +406,7 @@ def main():
             log(f"{name}: {extras[name]['ms_per_step']} ms/step")
             del cx
             torch.cuda.empty_cache()
-    elif not fused and not args.no_backward:
+    if not args.no_backward:
         try:
             result["backward"] = backward_leg(chain, args, torch, pfa)
         except Exception as e:
@@ -429,7 +431,8 @@ def backward_leg(chain, args, torch, pfa):
     """Backward of the last block of the chain just run (its outputs are the ones
     left in the buffers): the sparse layers L..2 (kept sets from the forward
     outputs), each taking the next one's dA^{l} output and a seeded dO, then the
-    dense first layer with the second layer's dA^1; timed like the forward step,
+    dense first layer with the second layer's dA^1 (a fused chain: layers L..3,
+    then the fused first two layers' backward); timed like the forward step,
     per kernel with HIP events."""
     w, outs, implicit = chain.w, chain.outs, chain.implicit
     qkv = chain.qkv[w.blocks - 1]
@@ -445,12 +448,19 @@ def backward_leg(chain, args, torch, pfa):
                      dtype=torch.uint8, device=dev)
     # the dense layer's log denominators (its forward in the timed step writes A^1, not these)
     dense_bwd = w.K[0] == N and implicit[1]
+    fused = chain.fused
     lse = torch.empty(lead + (N,), dtype=torch.float32, device=dev)
-    if dense_bwd:
+    ws_f = None
+    if fused:   # the same forward again, now with lse1 (its outputs are bit-identical)
+        pfa.first_two_layers(*qkv[0], *qkv[1], w.K[1], win=w.win, shift1=w.shifts[0], shift2=w.shifts[1],
+                             out=(outs[0][2],) + outs[1], lse_out=lse)
+        ws_f = torch.empty(pfa.first_two_layers_backward_workspace_bytes(qkv[0][0], w.K[1], win=w.win),
+                           dtype=torch.uint8, device=dev)
+    elif dense_bwd:
         pfa.dense_layer(*qkv[0], win=w.win, shift=w.shifts[0], want_A=False, lse_out=lse)
 
     def bstep(marks=None):
-        for l in range(L - 1, 0, -1):
+        for l in range(L - 1, 1 if fused else 0, -1):
             Q, K, V = qkv[l]
             I_prev = None if implicit[l] else outs[l - 1][0]
             dA = dA_prev[l + 1] if l + 1 < L else None
@@ -459,7 +469,13 @@ def backward_leg(chain, args, torch, pfa):
                                       out=grads[l] + (dA_prev[l],), workspace=ws)
             if marks is not None:
                 marks.append(pfa.timing_count())
-        if dense_bwd:
+        if fused:
+            pfa.first_two_layers_backward(*qkv[0], *qkv[1], lse, outs[1][0], outs[1][1], dO[0], dO[1], dA_prev[2],
+                                          win=w.win, shift1=w.shifts[0], shift2=w.shifts[1],
+                                          out=grads[0] + grads[1], workspace=ws_f)
+            if marks is not None:
+                marks.append(pfa.timing_count())
+        elif dense_bwd:
             pfa.dense_layer_backward(*qkv[0], lse, dO[0], dA_prev[1], win=w.win, shift=w.shifts[0], out=grads[0],
                                      workspace=ws)
             if marks is not None:
@@ -481,9 +497,18 @@ def backward_leg(chain, args, torch, pfa):
     assert dropped == 0 and len(recs) == marks[-1], (dropped, len(recs), marks[-1])
     per = {}
     start = 0
-    nlay = L if dense_bwd else L - 1
+    nlay = L - 1 if fused else L if dense_bwd else L - 1
     for i, end in enumerate(marks):
         l = L - 1 - (i % nlay)
+        if fused and l == 1:   # the fused pair: its kernels by kind, summed per call
+            acc = {}
+            for kind, ms in recs[start:end]:
+                key = FUSED_BWD_KINDS.get(kind, str(kind))
+                acc[key] = acc.get(key, 0.0) + ms
+            for key, ms in acc.items():
+                per.setdefault((1, f"fused12:{key}"), []).append(ms)
+            start = end
+            continue
         if l == 0:
             for kind, ms in recs[start:end]:
                 per.setdefault((0, "dense"), []).append(ms)
@@ -502,6 +527,18 @@ def backward_leg(chain, args, torch, pfa):
     kernels = []
     for (l, part), v in sorted(per.items()):
         ms = float(np.mean(v))
+        if part.startswith("fused12:"):
+            # per window-head work of the pieces: the first map at the kept pairs (N K2
+            # scores), the second layer's row / dK dV passes, the dense layer's backward
+            k = {"layer": "1-2", "kernel": part, "launches": len(v), "ms": round(ms, 4)}
+            if part.endswith("dense_bwd"):
+                x = N * w.d * (4 if w.dtype == "f32" else 2)
+                by = (3 * x + N * 4 + N * w.d * 4 + N * N * 4 + 3 * N * w.d * 4) * w.n_wh
+                fl = 10 * N * N * w.d * w.n_wh
+                k.update({"io_bytes": by, "alg_flops": fl, "TFLOP_per_s": round(fl / (ms * 1e-3) / 1e12, 2),
+                          "bound": "mfma", "frac": round(fl / (ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)})
+            kernels.append(k)
+            continue
         if part == "dense":
             # Q, K, V, lse, dO, dA^1 read; dQ, dK, dV written; 5 products of 2 N^2 d flops
             x = N * w.d * (4 if w.dtype == "f32" else 2)
@@ -534,10 +571,14 @@ def backward_leg(chain, args, torch, pfa):
             if fl / (FP32_MFMA_PEAK_TFLOPS * 1e12) > by / (HBM_PEAK_GBS * 1e9):
                 k.update({"bound": "mfma", "frac": round(tfs / FP32_MFMA_PEAK_TFLOPS, 4)})
         kernels.append(k)
-    layer_ms = {l + 1: round(sum(k["ms"] for k in kernels if k["layer"] == l + 1), 4)
-                for l in range(0 if dense_bwd else 1, L)}
-    kept = sum(w.n_wh * N * w.K[l] for l in range(0 if dense_bwd else 1, L))
-    dom = max(kernels, key=lambda k: k["ms"])
+    if fused:
+        layer_ms = {l + 1: round(sum(k["ms"] for k in kernels if k["layer"] == l + 1), 4) for l in range(2, L)}
+        layer_ms["1-2"] = round(sum(k["ms"] for k in kernels if k["layer"] == "1-2"), 4)
+    else:
+        layer_ms = {l + 1: round(sum(k["ms"] for k in kernels if k["layer"] == l + 1), 4)
+                    for l in range(0 if dense_bwd else 1, L)}
+    kept = sum(w.n_wh * N * w.K[l] for l in range(0 if (dense_bwd or fused) else 1, L))
+    dom = max((k for k in kernels if "bound" in k), key=lambda k: k["ms"])
     if dom["bound"] == "mfma":
         roof = {"bound": "mfma", "achieved": dom["TFLOP_per_s"], "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
     else:
@@ -545,7 +586,8 @@ def backward_leg(chain, args, torch, pfa):
     roof.update({"frac": dom["frac"], "traffic": None, "kernel": dom["kernel"], "layer": dom["layer"],
                  "ms_per_launch": dom["ms"], "alg_bytes_per_launch": dom["io_bytes"]})
     return {"ms_per_step": round(ms_per_step, 4), "block": w.blocks - 1,
-            "layers": f"{L}..1" if dense_bwd else f"{L}..2", "layer_ms": layer_ms,
+            "layers": f"{L}..3 then fused 2..1" if fused else f"{L}..1" if dense_bwd else f"{L}..2",
+            "layer_ms": layer_ms,
             "kept_pairs_per_s": kept / (ms_per_step * 1e-3), "roofline": roof, "kernels": kernels}
 
 

@@ -126,7 +126,10 @@ int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const voi
         });
         return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
     }
-    a.blocks_per_wh = g.N >= 512 ? 2 : 1;
+    // two workgroups per window-head where the rows carry many candidates; one where
+    // they carry few (K_prev <= 128: measured 2-4 % faster selections, the window's K
+    // staged once per window-head instead of twice)
+    a.blocks_per_wh = (g.N >= 512 && K_prev > 128) ? 2 : 1;
     a.rows_per_block = (g.N + a.blocks_per_wh - 1) / a.blocks_per_wh;
     const int64_t grid64 = n_wh(g) * a.blocks_per_wh;
     if (grid64 > 0x7fffffff) return PFA_ERR_UNSUPPORTED;

@@ -477,6 +477,14 @@ def dense_layer_backward_noalloc(Q, K, V, lse, dO, dA=None, *, win, shift=0, bia
     return dQ, dK, dV
 
 
+def first_two_layers_backward_workspace_bytes(Q1, K2_keep, *, win) -> int:
+    shape = make_shape(Q1, win, 0)
+    n = int(load().pfa_first_two_layers_backward_workspace(ctypes.byref(shape), int(K2_keep)))
+    if n < 0:
+        raise PfaError("pfa_first_two_layers_backward_workspace", n)
+    return n
+
+
 def backward_workspace_bytes(Q, K_l, *, win, shift=0) -> int:
     shape = make_shape(Q, win, shift)
     n = int(load().pfa_sparse_layer_backward_workspace(ctypes.byref(shape), int(K_l)))

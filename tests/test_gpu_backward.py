@@ -138,6 +138,9 @@ def run_case(B, heads, H, W, d, win, shift, K_prev, K_l, dtype, seed, *, implici
         dQ, dK, dV, dAp, dbias = pfa.sparse_layer_backward_rpb(
             Qd, Kd, Vd, torch.from_numpy(table).cuda(), Ipd, Apd, I_l, A_l, dOd, dAd, win=win, shift=shift,
             K_prev=K_prev, want_dA_prev=want_dA_prev)
+        again = pfa.sparse_layer_backward_rpb(Qd, Kd, Vd, torch.from_numpy(table).cuda(), Ipd, Apd, I_l, A_l, dOd,
+                                              dAd, win=win, shift=shift, K_prev=K_prev, want_dA_prev=want_dA_prev)
+        assert torch.equal(again[4], dbias), "the bias gradient differs between two calls"
     else:
         dQ, dK, dV, dAp = pfa.sparse_layer_backward(Qd, Kd, Vd, Ipd, Apd, I_l, A_l, dOd, dAd, win=win, shift=shift,
                                                     K_prev=K_prev, want_dA_prev=want_dA_prev)
@@ -345,6 +348,9 @@ def test_dense_backward(dtype, d, win, shift, with_dA, with_bias, capsys):
         torch.cuda.synchronize()
         for x, y in zip((dQ, dK, dV), plain):
             assert torch.equal(x, y), "the bias gradient changed the other gradients"
+        again = pfa.dense_layer_backward_rpb(*args, torch.from_numpy(table).cuda(), lse_d, torch.from_numpy(dO).cuda(),
+                                             dA_d, win=win, shift=shift)
+        assert torch.equal(again[3], dbias), "the bias gradient differs between two calls"
     else:
         dQ, dK, dV = pfa.dense_layer_backward(*args, lse_d, torch.from_numpy(dO).cuda(), dA_d, win=win, shift=shift)
     torch.cuda.synchronize()
