@@ -186,7 +186,12 @@ __device__ __forceinline__ void radix_threshold(KF key, int kmin, int kmax, bool
         const int shift = max(32 - __clz(span - 1) - LOG2NB, 0);
         if (BPL >= 4) {
 #pragma unroll
-            for (int b = 0; b < BPL; b += 4) *reinterpret_cast<uint4*>(hb + BPL * gl + b) = make_uint4(0u, 0u, 0u, 0u);
+            for (int b = 0; b < BPL; b += 4) {
+                // zeros made here (a zero quad kept live across the caller's loop was spilled)
+                unsigned z;
+                __asm__ volatile("v_mov_b32 %0, 0" : "=v"(z));
+                *reinterpret_cast<uint4*>(hb + BPL * gl + b) = make_uint4(z, z, z, z);
+            }
         } else if (BPL == 2) {
             *reinterpret_cast<uint2*>(hb + 2 * gl) = make_uint2(0u, 0u);
         } else {
@@ -886,17 +891,21 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
 #pragma unroll
         for (int set = 0; set < NK; ++set) {   // DUAL: the first layer's q1.k1, then q.k
             const bool first = DUAL && set == 0;
+            // each set's row address and K offset derived here from opaque copies (kept live
+            // from the top of the batch through the first set's MFMAs, they were spilled)
+            int qis = qi, lvs = lv;
+            __asm__ volatile("" : "+v"(qis), "+v"(lvs));
             const unsigned char* qrow = reinterpret_cast<const unsigned char*>(
-                (first ? Q1h : Qh) + (size_t)slot_pixel(first ? g1 : g, w.wy, w.wx, qi) * D);
-            const unsigned char* kr0 = Ks + (first ? N * KSTR : 0) + lv * KSTR;
+                (first ? Q1h : Qh) + (size_t)slot_pixel(first ? g1 : g, w.wy, w.wx, qis) * D);
+            const unsigned char* kr0 = Ks + (first ? N * KSTR : 0) + lvs * KSTR;
             uint4 qc[CH];
 #pragma unroll
             for (int m = 0; m < CH; ++m) qc[m] = *reinterpret_cast<const uint4*>(qrow + 16 * m);
             // tiles in groups of TG (TG independent accumulator chains), contraction chunk
-            // inner: at most TG x CH K chunks in flight. TG = 4 leaves the single-set
-            // kernels without spills (16 spilled up to 5 dwords); the fused kernel, with
-            // the second layer's query also live, spills least with TG = 16
-            constexpr int TG = DUAL ? 16 : 4;
+            // inner: at most TG x CH K chunks in flight. TG = 4 leaves the kernels without
+            // spills (16 spilled up to 5 dwords; with the lane values above kept live, the
+            // fused kernel spilled at every TG, and 7 dwords per batch at TG = 16)
+            constexpr int TG = 4;
 #pragma unroll
             for (int t0 = 0; t0 < 16; t0 += TG) {
 #pragma unroll
@@ -910,6 +919,12 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
             }
         }
         __builtin_amdgcn_s_setprio(2);
+        // the selection phase re-derives its lane values (not kept across the MFMAs)
+        int lv2;
+        __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lv2));
+        const int gv2 = lv2 >> 4;
+        unsigned* hbv2 = hist0 + (wave * 4 + gv2) * HISTG;
+        const int glv2 = lv2 & (GL - 1);
         float uv[KPT];   // raw scores q.k, then the keys
         // acc[t][r] = s(row r, candidate 64t + lane): transpose (lane quarter, r)
 #pragma unroll
@@ -931,7 +946,7 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
 #pragma unroll
         for (int k = 1; k < KPT; ++k) smax = fmaxf(smax, uv[k]);
         const float c = -Grp<GL>::all(smax, MaxF()) * scale2;
-        const float* arow = HAS_A ? p.A_prev + ((size_t)w.wh * N + min(base + gv, N - 1)) * N + glv : nullptr;
+        const float* arow = HAS_A ? p.A_prev + ((size_t)w.wh * N + min(base + gv2, N - 1)) * N + glv2 : nullptr;
 #pragma unroll
         for (int h = 0; h < KPT; h += AH) {
             float ab[AH];
@@ -949,12 +964,12 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
 
         // rows past row1 (last batch) are selected but never stored: every group's
         // ballots and reductions are its own
-        const bool active = base + gv < row1;
+        const bool active = base + gv2 < row1;
         const size_t rbase = ((size_t)w.wh * N + base) * K_l;
         const int nbytes = max(0, min(4, row1 - base)) * K_l * 4;
         select_store<GL, KPT, BPL, true, true>(
-            p, lv, active, N, [&](int k) { return GL * k + glv; }, [&](int) { return true; }, uv, hbv,
-            make_rsrc(p.I_out + rbase, nbytes), make_rsrc(p.A_out + rbase, nbytes), gv * K_l);
+            p, lv2, active, N, [&](int k) { return GL * k + glv2; }, [&](int) { return true; }, uv, hbv2,
+            make_rsrc(p.I_out + rbase, nbytes), make_rsrc(p.A_out + rbase, nbytes), gv2 * K_l);
     }
 }
 
