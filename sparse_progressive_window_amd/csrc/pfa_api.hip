@@ -126,10 +126,13 @@ int run_sparse(const Geom& g, int dtype, const void* Q, const void* K, const voi
         });
         return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
     }
-    // two workgroups per window-head where the rows carry many candidates; one where
-    // they carry few (K_prev <= 128: measured 2-4 % faster selections, the window's K
-    // staged once per window-head instead of twice)
-    a.blocks_per_wh = (g.N >= 512 && K_prev > 128) ? 2 : 1;
+    // two workgroups per window-head where the rows carry many candidates, or where
+    // the window-heads are too few to fill the CUs four times over; otherwise one
+    // (K_prev <= 128 on the 640x384 map: 2-4 % faster selections, the window's K
+    // staged once per window-head instead of twice; on 384 window-heads one
+    // workgroup each left CUs idle: the 256x256 map's layer-4 aggregation 0.10 ->
+    // 0.12 ms)
+    a.blocks_per_wh = (g.N >= 512 && (K_prev > 128 || n_wh(g) < 4 * (int64_t)compute_units())) ? 2 : 1;
     a.rows_per_block = (g.N + a.blocks_per_wh - 1) / a.blocks_per_wh;
     const int64_t grid64 = n_wh(g) * a.blocks_per_wh;
     if (grid64 > 0x7fffffff) return PFA_ERR_UNSUPPORTED;

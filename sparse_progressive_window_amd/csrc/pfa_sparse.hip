@@ -1141,13 +1141,16 @@ __global__ __launch_bounds__(NW * kWave) void aggregate_rows_kernel(const Sparse
 }
 
 
-// O_i = sum_j A^l_ij v_j from stored (I^l, A^l) rows, V of the window in LDS, for
-// V rows of 4 16-byte chunks (bf16 d = 32, fp32 d = 16): one quad of lanes per
-// row, one chunk each. Lane c of quad q loads step c of the quad's entries (4
-// consecutive (I, A) pairs; the wave's loads cover whole rows, coalesced), and at
-// step k the quad takes lane k's entries by a DPP broadcast, so no entry passes
-// through LDS and its bandwidth goes to the V rows alone.
-template <typename T, int D, int R, int NW>
+// 4-chunk V rows (bf16 d = 32, fp32 d = 16): one lane quad per row group, one
+// 16-byte chunk per lane. A row takes GL = 64 / R lanes (GL / 4 quads); its entries
+// are handed out in S rounds of 4 steps: at round r, lane c of quad q loads step c
+// (4 consecutive (I, A) pairs at 4 GL r + GL c + 4 q; the wave's loads cover whole
+// row segments, coalesced), and at step k the quad takes lane k's entries by a DPP
+// quad broadcast, so LDS carries only V rows. With more rounds a row needs fewer
+// quads, and the closing sum over the row's quads (two cross-lane exchanges and an
+// add per quad halving, 8 values) is paid once per 16 S entries per quad instead
+// of per 16 (layer 2: 4 quads of 64 entries instead of 16 of 16).
+template <typename T, int D, int R, int NW, int S>
 __global__ __launch_bounds__(NW * kWave) void aggregate_quads_kernel(const SparseArgs p) {
     constexpr int EPC = Chunk<T>::kElems;
     constexpr int ROWB = D * (int)sizeof(T);
@@ -1169,58 +1172,69 @@ __global__ __launch_bounds__(NW * kWave) void aggregate_quads_kernel(const Spars
     const T* Vh = static_cast<const T*>(p.V) + plane;
     float* Oh = p.O_out + plane;
 
-    const int K_l = p.K_l;   // a multiple of 4, at most 4 GL
+    const int K_l = p.K_l;   // a multiple of 4, at most 4 GL S
     const int row0 = w.part * p.rows_per_block;
     const int row1 = min(N, row0 + p.rows_per_block);
-    const int32_t* Iw = p.I_out + (size_t)w.wh * N * K_l;
-    const float* Aw = p.A_out + (size_t)w.wh * N * K_l;
-    const int e0 = GL * c + 4 * q;   // this lane's entries: step c of quad q
-    // a row's entries are loaded one iteration ahead (the first before the staging)
-    auto load_entries = [&](int b, int4& jv, float4& wv) {
+    // the window-head's (I, A) rows through buffer resources: a load past the rows'
+    // range returns zeros (no branch around the loads)
+    const int wh_bytes = N * K_l * 4;
+    const __amdgpu_buffer_rsrc_t rI = make_rsrc(p.I_out + (size_t)w.wh * N * K_l, wh_bytes);
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A_out + (size_t)w.wh * N * K_l, wh_bytes);
+    const int e0 = GL * c + 4 * q;   // this lane's entries at round r: e0 + 4 GL r
+    // round r of the rows at b: offsets past the range for inactive rows and entries past K_l
+    auto load_round = [&](int b, int r, int4& jv, float4& wv) {
         const int i = b + grp;
-        jv = make_int4(0, 0, 0, 0);
-        wv = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i < row1 && e0 < K_l) {
-            jv = *reinterpret_cast<const int4*>(Iw + (size_t)i * K_l + e0);
-            wv = *reinterpret_cast<const float4*>(Aw + (size_t)i * K_l + e0);
-        }
+        const int e = e0 + 4 * GL * r;
+        const int off = (i < row1 && e < K_l) ? (i * K_l + e) * 4 : 0x7FFFFFF0;
+        const auto jr = __builtin_amdgcn_raw_buffer_load_b128(rI, off, 0, 0);
+        const auto wr = __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0);
+        jv = make_int4((int)jr[0], (int)jr[1], (int)jr[2], (int)jr[3]);
+        wv = make_float4(__uint_as_float(wr[0]), __uint_as_float(wr[1]), __uint_as_float(wr[2]),
+                         __uint_as_float(wr[3]));
     };
+    // the next round's entries are loaded one round ahead (the first before the staging)
     int4 jn;
     float4 wn;
-    load_entries(row0 + wave * R, jn, wn);
+    load_round(row0 + wave * R, 0, jn, wn);
     stage_rows<T, D>(smem, ROWB, Vh, g, w.wy, w.wx);
     __syncthreads();
 
     for (int base = row0 + wave * R; base < row1; base += NW * R) {
         const int i = base + grp;
         const bool active = i < row1;
-        const int4 jm = jn;
-        const float4 wm = wn;
-        if (base + NW * R < row1) load_entries(base + NW * R, jn, wn);
         float acc[EPC];
 #pragma unroll
         for (int y = 0; y < EPC; ++y) acc[y] = 0.0f;
-        auto step = [&](auto kc) {
-            constexpr int KC = decltype(kc)::value;
-            constexpr int BC = KC * 0x55;   // quad_perm [k, k, k, k]
-            const int jk[4] = {dpp<BC>(jm.x), dpp<BC>(jm.y), dpp<BC>(jm.z), dpp<BC>(jm.w)};
-            const float wk[4] = {dppf<BC>(wm.x), dppf<BC>(wm.y), dppf<BC>(wm.z), dppf<BC>(wm.w)};
-            // quads whose step-k entries lie past K_l (K_l not a multiple of 4 GL) add
-            // nothing: 0 * a non-finite V row would turn O into NaN
-            if (GL * KC + 4 * q >= K_l) return;
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int j = (int)min((unsigned)jk[x], (unsigned)(N - 1));   // memory safety only
-                float vf[EPC];
-                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(smem + j * ROWB + c * 16), vf);
+        for (int r = 0; r < S; ++r) {
+            const int4 jm = jn;
+            const float4 wm = wn;
+            if (r + 1 < S) load_round(base, r + 1, jn, wn);
+            else if (base + NW * R < row1) load_round(base + NW * R, 0, jn, wn);
+            auto step = [&](auto kc) {
+                constexpr int KC = decltype(kc)::value;
+                constexpr int BC = KC * 0x55;   // quad_perm [k, k, k, k]
+                const int jk[4] = {dpp<BC>(jm.x), dpp<BC>(jm.y), dpp<BC>(jm.z), dpp<BC>(jm.w)};
+                const float wk[4] = {dppf<BC>(wm.x), dppf<BC>(wm.y), dppf<BC>(wm.z), dppf<BC>(wm.w)};
+                // quads whose step-k entries lie past K_l add nothing: 0 * a non-finite V
+                // row would turn O into NaN
+                if (4 * GL * r + GL * KC + 4 * q >= K_l) return;
 #pragma unroll
-                for (int y = 0; y < EPC; ++y) acc[y] = fmaf(wk[x], vf[y], acc[y]);
+                for (int x = 0; x < 4; ++x) {
+                    const int j = (int)min((unsigned)jk[x], (unsigned)(N - 1));   // memory safety only
+                    float vf[EPC];
+                    Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(smem + j * ROWB + c * 16), vf);
+#pragma unroll
+                    for (int y = 0; y < EPC; ++y) acc[y] = fmaf(wk[x], vf[y], acc[y]);
+                }
+            };
+            if (4 * GL * r < K_l) {   // uniform: the round holds entries
+                step(std::integral_constant<int, 0>());
+                if (4 * GL * r + GL < K_l) step(std::integral_constant<int, 1>());
+                if (4 * GL * r + 2 * GL < K_l) step(std::integral_constant<int, 2>());
+                if (4 * GL * r + 3 * GL < K_l) step(std::integral_constant<int, 3>());
             }
-        };
-        step(std::integral_constant<int, 0>());
-        if (GL < K_l) step(std::integral_constant<int, 1>());
-        if (2 * GL < K_l) step(std::integral_constant<int, 2>());
-        if (3 * GL < K_l) step(std::integral_constant<int, 3>());
+        }
 #pragma unroll
         for (int y = 0; y < EPC; ++y) acc[y] = reduce_chunk_lanes<4, GL>(acc[y]);   // the row's quads
         if (active && q == 0) {
@@ -1324,12 +1338,13 @@ hipError_t launch_aggregate_t(const SparseArgs& a, int grid, hipStream_t s) {
     // staging the entries in LDS for 8-lane rows (0.33 against 0.30 ms at layer 2)
     if constexpr (D / Chunk<T>::kElems == 4) {
         if (a.K_l <= 256 && a.K_l % 4 == 0 && lds <= kLdsBytes) {
-            const int r = 256 / a.K_l;   // rows per wave: R K_l <= 256, 4 steps of 4 entries per lane
-            if (r >= 16) return launch_fn(aggregate_quads_kernel<T, D, 16, 16>, a, 16 * kWave, lds, grid, s);
-            if (r >= 8) return launch_fn(aggregate_quads_kernel<T, D, 8, 16>, a, 16 * kWave, lds, grid, s);
-            if (r >= 4) return launch_fn(aggregate_quads_kernel<T, D, 4, 16>, a, 16 * kWave, lds, grid, s);
-            if (r >= 2) return launch_fn(aggregate_quads_kernel<T, D, 2, 16>, a, 16 * kWave, lds, grid, s);
-            return launch_fn(aggregate_quads_kernel<T, D, 1, 16>, a, 16 * kWave, lds, grid, s);
+            // up to 64 entries per quad (4 rounds): GL = max(4, K_l / 16) lanes per row
+            const int kl = a.K_l;
+            if (kl <= 16) return launch_fn(aggregate_quads_kernel<T, D, 16, 16, 1>, a, 16 * kWave, lds, grid, s);
+            if (kl <= 32) return launch_fn(aggregate_quads_kernel<T, D, 16, 16, 2>, a, 16 * kWave, lds, grid, s);
+            if (kl <= 64) return launch_fn(aggregate_quads_kernel<T, D, 16, 16, 4>, a, 16 * kWave, lds, grid, s);
+            if (kl <= 128) return launch_fn(aggregate_quads_kernel<T, D, 8, 16, 4>, a, 16 * kWave, lds, grid, s);
+            return launch_fn(aggregate_quads_kernel<T, D, 4, 16, 4>, a, 16 * kWave, lds, grid, s);
         }
     }
     constexpr int RMAX = kWave / (D / Chunk<T>::kElems);   // rows per step with CH lanes per row
