@@ -39,7 +39,7 @@ HEADLINE = "map640x384_h6_d32_bf16_6blocks"
 # kernel kinds of the library's timing calls (pfa_kernel_kind)
 (DENSE, ALL_CAND, SPARSE, SELECT, AGGREGATE, IOTA, BWD_ROWS, BWD_SCATTER, IET_RANK, IET_UNION, DENSE_BWD,
  BWD_EXACT, DBIAS, FIRST_MAP) = range(14)
-FUSED_BWD_KINDS = {FIRST_MAP: "first_map", BWD_ROWS: "bwd_rows", BWD_EXACT: "bwd_exact", BWD_SCATTER: "bwd_dkv",
+FUSED_BWD_KINDS = {FIRST_MAP: "first_map_and_spread", BWD_ROWS: "bwd_rows", BWD_EXACT: "bwd_exact", BWD_SCATTER: "bwd_dkv",
                    DENSE_BWD: "dense_bwd"}
 
 

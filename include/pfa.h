@@ -182,9 +182,9 @@ int pfa_first_two_layers(const pfa_shape* shape, int32_t shift1, int32_t shift2,
  * dO1, dO2  [B, heads, H, W, d] fp32 gradients of O1 and O2.
  * dA2     [B, heads, nwin, N, K2_keep] fp32 gradient of A2, or NULL (zero).
  * dQ1..dV2  [B, heads, H, W, d] fp32 outputs, every element written.
- * workspace  at least pfa_first_two_layers_backward_workspace() bytes: two
- *         [N, N] fp32 maps per window-head (A^1 at the kept slots, dA^1), then
- *         the two single-layer passes' workspaces.
+ * workspace  at least pfa_first_two_layers_backward_workspace() bytes: per
+ *         window-head A^1 and dA^1 at the kept slots ([N, K2_keep] fp32 each) and
+ *         the dense dA^1 ([N, N] fp32), then the two single-layer passes' workspaces.
  * Deterministic, as the single-layer calls.
  * Errors: PFA_ERR_INVALID for NULL required pointers, shifts outside [0, win),
  * shape->shift != 0, K2_keep outside [1, N], a small workspace;
@@ -425,7 +425,8 @@ typedef enum {
                                       ("dbias_sparse_wh_kernel" or "dbias_dense_fold_kernel") then
                                       "dbias_reduce_kernel", one record for both */
     PFA_KERNEL_FIRST_MAP = 13      /* backward of the fused first two layers: the first layer's map at
-                                      the second layer's kept slots */
+                                      the second layer's kept slots ("first_map_kept_kernel"), and its
+                                      gradient spread into dense rows ("spread_rows_kernel") */
 } pfa_kernel_kind;
 
 /* capacity > 0: create 2*capacity events and start recording (earlier records

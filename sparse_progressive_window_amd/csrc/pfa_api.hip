@@ -173,10 +173,12 @@ int64_t dbias_part_ws(const Geom& g) {
 }
 // the dense dQ kernel's per-wave rows of diagonal sums: [wh, N / 16, win, 64]
 int64_t dense_dbias_rows_ws(const Geom& g) { return n_wh(g) * (g.N / 16) * (int64_t)g.win * 64 * 4; }
-// backward of the fused first two layers: A^1 at the kept slots and dA^1 ([wh, N, N]
-// each), the sparse backward's workspace, the dense backward's (one fp32 per row)
+// backward of the fused first two layers: A^1 and dA^1 at the kept slots ([wh, N, K2]
+// each), the dense dA^1 ([wh, N, N]), the sparse backward's workspace, the dense
+// backward's (one fp32 per row)
 int64_t fused_bwd_ws(const Geom& g, int K2) {
-    return 2 * n_wh(g) * g.N * (int64_t)g.N * 4 + sparse_bwd_ws(g, K2) + n_wh(g) * g.N * 4;
+    return 2 * n_wh(g) * g.N * (int64_t)K2 * 4 + n_wh(g) * g.N * (int64_t)g.N * 4 + sparse_bwd_ws(g, K2) +
+           n_wh(g) * g.N * 4;
 }
 
 }  // namespace
@@ -358,12 +360,15 @@ int pfa_first_two_layers_backward(const pfa_shape* shape, int32_t shift1, int32_
     if (workspace_bytes < fused_bwd_ws(g, K2_keep)) return PFA_ERR_INVALID;
     if (g.win % 8 || K2_keep > 256) return PFA_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // workspace: A^1 at the kept slots and dA^1, both [wh, N, N]; then the two backward passes' own
+    // workspace: A^1 and dA^1 at the kept slots ([wh, N, K2] each), the dense dA^1
+    // ([wh, N, N]), then the two backward passes' own
+    const int64_t kept_bytes = n_wh(g) * g.N * (int64_t)K2_keep * 4;
     const int64_t map_bytes = n_wh(g) * g.N * (int64_t)g.N * 4;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     float* A1 = reinterpret_cast<float*>(ws);
-    float* dA1 = reinterpret_cast<float*>(ws + map_bytes);
-    unsigned char* ws_sparse = ws + 2 * map_bytes;
+    float* dA1k = reinterpret_cast<float*>(ws + kept_bytes);
+    float* dA1 = reinterpret_cast<float*>(ws + 2 * kept_bytes);
+    unsigned char* ws_sparse = ws + 2 * kept_bytes + map_bytes;
     float* ws_dense = reinterpret_cast<float*>(ws_sparse + sparse_bwd_ws(g, K2_keep));
 
     pfa::FirstMapArgs m;
@@ -380,12 +385,19 @@ int pfa_first_two_layers_backward(const pfa_shape* shape, int32_t shift1, int32_
                                [&] { return pfa::launch_first_map(m, shape->dtype, g.d, (int)mgrid, s); });
     if (e != hipSuccess) return PFA_ERR_HIP;
 
-    // layer 2 with every slot a candidate and A^{l-1} = A^1: dQ2, dK2, dV2 and the dense dA^1
+    // layer 2 with its kept set as the candidate list and A^{l-1} = A^1 there: dQ2,
+    // dK2, dV2 and dA^1 at the kept slots (0 at the dropped ones), spread into dense rows
     pfa_shape s2 = *shape;
     s2.shift = shift2;
-    int rc = run_sparse_backward(&s2, Q2, K2, V2, nullptr, nullptr, A1, g.N, K2_keep, I2, A2, dO2, dA2, dQ2, dK2, dV2,
-                                 dA1, nullptr, ws_sparse, sparse_bwd_ws(g, K2_keep), s);
+    int rc = run_sparse_backward(&s2, Q2, K2, V2, nullptr, I2, A1, K2_keep, K2_keep, I2, A2, dO2, dA2, dQ2, dK2,
+                                 dV2, dA1k, nullptr, ws_sparse, sparse_bwd_ws(g, K2_keep), s);
     if (rc != PFA_OK) return rc;
+    pfa::SpreadArgs sp;
+    sp.I = I2; sp.vals = dA1k; sp.dense = dA1;
+    sp.rows = n_wh(g) * g.N;
+    sp.N = g.N; sp.K = K2_keep;
+    const hipError_t e2 = timed(PFA_KERNEL_FIRST_MAP, s, [&] { return pfa::launch_spread_rows(sp, s); });
+    if (e2 != hipSuccess) return PFA_ERR_HIP;
     // layer 1 (dense) with that dA^1
     Geom g1 = g;
     g1.shift = shift1;

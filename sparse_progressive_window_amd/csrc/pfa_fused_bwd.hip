@@ -5,15 +5,20 @@
 // "Progressive attention across layers" and "Progressive focused resource
 // allocation strategy": layer 1 keeps every slot, layer 2 selects from A^1). The
 // second layer's backward reads A^1 only at its kept slots (dA^1 = dkey / A^1 there,
-// and the exact form's normaliser), so only those entries are recomputed, from q1,
-// k1 and the first layer's log denominators:
+// and the exact form's normaliser), and gives dA^1 = 0 at the dropped ones. So the
+// second layer's backward runs with its own kept set as the candidate list (the
+// same gradients: the dropped slots' terms are zero) on A^1 recomputed at those
+// slots only, from q1, k1 and the first layer's log denominators:
 //   A^1_ij = exp(s1_ij - lse1_i),  s1_ij = q1_i.k1_j / sqrt(d),
-// and written at their places in a row-major [N, N] buffer whose other entries are
-// never read. The second layer's backward (candidate list = every slot) then writes
-// the dense dA^1 that the first layer's backward takes.
+// and its dA^1 rows (aligned with I^2) are spread into the dense [N, N] rows that
+// the first layer's backward reads.
 //
 // first_map_kept_kernel: 4 wavefronts per workgroup of 256 rows, the window's k1
-// rows staged in LDS; a wavefront takes a row, its lanes the row's kept slots.
+// rows staged in LDS; a wavefront takes a row, its lanes the row's kept slots;
+// A^1 is written aligned with I^2 (coalesced).
+// spread_rows_kernel: one wavefront per row: the dense row is built in the wave's
+// LDS row (zeros, then the K2 values at their slots; one wave's LDS accesses
+// complete in issue order) and written out in 16-byte stores.
 #include "pfa_kernels.h"
 #include "pfa_rows.h"
 
@@ -50,7 +55,7 @@ __global__ __launch_bounds__(kMapWaves * kWave) void first_map_kept_kernel(const
         for (int c = 0; c < CH; ++c) Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(qr + c * 16), &q[c * EPC]);
         const float l2 = p.lse1[row] * kLog2eF;
         const int32_t* Ir = p.I2 + row * K2;
-        float* Ar = p.A1 + row * N;
+        float* Ar = p.A1 + row * K2;
         for (int e = lane; e < K2; e += kWave) {
             const int j = (int)min((unsigned)Ir[e], (unsigned)(N - 1));
             float acc = 0.0f;
@@ -61,9 +66,28 @@ __global__ __launch_bounds__(kMapWaves * kWave) void first_map_kept_kernel(const
 #pragma unroll
                 for (int y = 0; y < EPC; ++y) acc = fmaf(q[c * EPC + y], kf[y], acc);
             }
-            Ar[j] = fast_exp2(fmaf(acc, p.scale2, -l2));
+            Ar[e] = fast_exp2(fmaf(acc, p.scale2, -l2));
         }
     }
+}
+
+constexpr int kSpreadWaves = 4;
+
+// dense[row][0..N) = 0, then dense[row][I[row][e]] = vals[row][e] (N <= 1024, a multiple of 4)
+__global__ __launch_bounds__(kSpreadWaves * kWave) void spread_rows_kernel(const SpreadArgs p) {
+    __shared__ __align__(16) float rowbuf[kSpreadWaves][1024];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    float* rb = rowbuf[wave];
+    const int N = p.N, K = p.K;
+    const int64_t row = (int64_t)blockIdx.x * kSpreadWaves + wave;
+    if (row >= p.rows) return;
+    for (int x = lane * 4; x < N; x += 4 * kWave) *reinterpret_cast<float4*>(rb + x) = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int32_t* Ir = p.I + row * K;
+    const float* vr = p.vals + row * K;
+    for (int e = lane; e < K; e += kWave) rb[min((unsigned)Ir[e], (unsigned)(N - 1))] = vr[e];
+    float* out = p.dense + row * N;
+    for (int x = lane * 4; x < N; x += 4 * kWave) *reinterpret_cast<float4*>(out + x) = *reinterpret_cast<const float4*>(rb + x);
 }
 
 template <typename T, int D>
@@ -79,6 +103,14 @@ hipError_t launch_map_t(const FirstMapArgs& a, int grid, hipStream_t s) {
 }  // namespace
 
 int first_map_blocks(int N) { return (N + kMapRows - 1) / kMapRows; }
+
+hipError_t launch_spread_rows(const SpreadArgs& a, hipStream_t stream) {
+    if (a.N > 1024 || a.N % 4) return hipErrorInvalidValue;
+    const int64_t grid = (a.rows + kSpreadWaves - 1) / kSpreadWaves;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(spread_rows_kernel, dim3((int)grid), dim3(kSpreadWaves * kWave), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_first_map(const FirstMapArgs& a, int dtype, int D, int grid, hipStream_t stream) {
     if (a.g.N * D * (dtype == 0 ? 4 : 2) > kLdsBytes) return hipErrorInvalidValue;

@@ -151,7 +151,7 @@ struct FirstMapArgs {
     const void* K1;
     const int32_t* I2;       // [wh, N, K2] the second layer's kept slots
     const float* lse1;       // [wh, N] the first layer's log denominators
-    float* A1;               // [wh, N, N] written at the kept slots only
+    float* A1;               // [wh, N, K2] A^1 at the kept slots, aligned with I2
     Geom g;                  // the first layer's geometry (its shift)
     int K2;
     float scale2;            // log2(e) / sqrt(d)
@@ -159,6 +159,15 @@ struct FirstMapArgs {
 };
 int first_map_blocks(int N);
 hipError_t launch_first_map(const FirstMapArgs& a, int dtype, int D, int grid, hipStream_t stream);
+// dense [rows, N] rows from [rows, K] values at the slots I (zeros elsewhere)
+struct SpreadArgs {
+    const int32_t* I;
+    const float* vals;
+    float* dense;
+    int64_t rows;
+    int N, K;
+};
+hipError_t launch_spread_rows(const SpreadArgs& a, hipStream_t stream);
 
 // Propagation / sparsification of an individualized index matrix.
 struct IetArgs {

@@ -213,7 +213,7 @@ def test_backward_rpb_validation(lib):
 
 
 def test_first_two_layers_backward_validation(lib):
-    ws = 2 * 1024 * 1024 * 4 + 1024 * 257 * 4 + 1024 * 4   # A^1, dA^1, sparse and dense workspaces
+    ws = 2 * 1024 * 256 * 4 + 1024 * 1024 * 4 + 1024 * 257 * 4 + 1024 * 4   # kept A^1, dA^1; dense dA^1; the passes
 
     def fb(s, shifts=(0, 16), K2=256, ptrs=(FAKE,) * 6, ws_ptr=FAKE, ws_bytes=ws):
         return lib.pfa_first_two_layers_backward(ctypes.byref(s), shifts[0], shifts[1], *([FAKE] * 6), K2, FAKE,
