@@ -11,9 +11,10 @@
 //
 // Dataflow. The window's K rows (and V rows when they fit) are staged once per
 // workgroup in LDS in slot order, so the cyclic shift costs nothing after
-// staging. A query row is handled by a group of GL lanes (GL = 16, 32 or 64,
-// the smallest power of two >= K_prev/4, so a wavefront handles 64/GL rows at
-// once); lane l of the group owns candidates c = l + GL*t (coalesced loads of
+// staging. A query row is handled by a group of GL lanes (GL = 4 .. 64, with KPT
+// candidates per lane, GL*KPT >= K_prev, both picked by the launcher from K_prev;
+// a wavefront handles 64/GL rows at once); lane l of the group owns candidates
+// c = l + GL*t (coalesced loads of
 // the I^{l-1} / A^{l-1} rows). k_j is gathered from LDS reading the 16-byte
 // chunks of the row in a lane-rotated order, so 8 consecutive lanes always touch
 // 8 different chunks and a 128-byte row never bank-conflicts.
@@ -50,16 +51,20 @@ struct MaxI { __device__ int operator()(int a, int b) const { return max(a, b); 
 struct MinI { __device__ int operator()(int a, int b) const { return min(a, b); } };
 struct SumI { __device__ int operator()(int a, int b) const { return a + b; } };
 
-// Reductions and counts over a group of GL consecutive lanes; every lane of the
-// group receives the result.
+// Reductions and counts over a group of GL consecutive lanes (GL = 4 .. 64); every
+// lane of the group receives the result.
 template <int GL>
 struct Grp {
+    static_assert(GL == 4 || GL == 8 || GL == 16 || GL == 32 || GL == 64, "group width");
     template <class Op>
     __device__ static float all(float v, Op op) {
         v = op(v, dppf<kQuadXor1>(v));
         v = op(v, dppf<kQuadXor2>(v));
-        v = op(v, dppf<kRowRor4>(v));
-        v = op(v, dppf<kRowRor8>(v));
+        if (GL == 8) v = op(v, dppf<kRowHalfMirror>(v));   // the other quad of the 8-lane half
+        if (GL >= 16) {
+            v = op(v, dppf<kRowRor4>(v));
+            v = op(v, dppf<kRowRor8>(v));
+        }
         if (GL >= 32) v = op(v, swap16f(v));
         if (GL == 64)
             v = op(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
@@ -70,16 +75,32 @@ struct Grp {
     __device__ static int all_i(int v, Op op) {
         v = op(v, dpp<kQuadXor1>(v));
         v = op(v, dpp<kQuadXor2>(v));
-        v = op(v, dpp<kRowRor4>(v));
-        v = op(v, dpp<kRowRor8>(v));
+        if (GL == 8) v = op(v, dpp<kRowHalfMirror>(v));
+        if (GL >= 16) {
+            v = op(v, dpp<kRowRor4>(v));
+            v = op(v, dpp<kRowRor8>(v));
+        }
         if (GL >= 32) v = op(v, swap16(v));
         if (GL == 64) v = op(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 32));
         return v;
     }
-    static constexpr int kLog2 = GL == 64 ? 6 : GL == 32 ? 5 : 4;
+    static constexpr int kLog2 = GL == 64 ? 6 : GL == 32 ? 5 : GL == 16 ? 4 : GL == 8 ? 3 : 2;
     // inclusive prefix sum over the lanes of the group (row_shr steps, then row
-    // broadcasts across the 16-lane rows)
+    // broadcasts across the 16-lane rows; narrower groups mask the steps that would
+    // reach into the previous group)
     __device__ static unsigned incl_scan(unsigned x) {
+        if (GL < 16) {
+            const unsigned l = __lane_id() & (GL - 1);
+            unsigned y = (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+            x += l >= 1 ? y : 0u;
+            y = (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);            // row_shr:2
+            x += l >= 2 ? y : 0u;
+            if (GL == 8) {
+                y = (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);        // row_shr:4
+                x += l >= 4 ? y : 0u;
+            }
+            return x;
+        }
         x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
         x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
         x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
@@ -91,14 +112,14 @@ struct Grp {
     // lanes of this lane's group as a wave mask
     __device__ static uint64_t group_mask(int lane) {
         if (GL == 64) return ~0ull;
-        return (GL == 32 ? 0xFFFFFFFFull : 0xFFFFull) << (lane & (64 - GL));
+        return ((1ull << GL) - 1ull) << (lane & (64 - GL));
     }
     // bits of the wave mask m that belong to this lane's group
     __device__ static uint32_t bits(uint64_t m, int lane) {
         if (GL == 64) return 0;  // unused
         const uint32_t half = (lane & 32) ? (uint32_t)(m >> 32) : (uint32_t)m;
         if (GL == 32) return half;
-        return (half >> (lane & 16)) & 0xFFFFu;
+        return (half >> (lane & (32 - GL))) & ((1u << GL) - 1u);
     }
     __device__ static int count_mask(uint64_t m, int lane) {
         if (GL == 64) return popc(m);
@@ -591,7 +612,7 @@ __global__ __launch_bounds__(NW * kWave) void sparse_layer_kernel(const SparseAr
     // I/A stores (loads issued after them would wait for them too: one in-order
     // counter) and pass through the wave's histogram words, free between selections
     // (measured 4-8 % faster with 8 candidates per lane, neutral or slower with fewer)
-    constexpr bool QS = !PQ && VS == kVnone && KPT >= 8;
+    constexpr bool QS = !PQ && VS == kVnone && KPT >= 8 && ROWB / 4 <= HISTG;
     constexpr int QW = RPW * ROWB / 4;                 // words of the batch's query rows
     constexpr int NQ = (QW + kWave - 1) / kWave;
     static_assert(!QS || QW <= HISTW, "query rows exceed the histogram words");
@@ -1285,11 +1306,13 @@ template <typename T, int D>
 hipError_t launch_shape(const SparseArgs& a, SparseMode mode, int lds, int grid, hipStream_t s) {
     const int kp = a.K_prev;
     if (mode == kKselect && kp <= 256) {
-        // selection only: 16- and 32-lane row groups (4 or 2 rows per wavefront)
+        // selection only: narrow row groups (4 to 16 lanes, 16 to 4 rows per wavefront)
         // amortise the per-row reductions and scans over more candidates per lane
-        if (kp <= 16) return launch_one<T, D, 16, 1, kKselect>(a, lds, grid, s);
-        if (kp <= 32) return launch_one<T, D, 16, 2, kKselect>(a, lds, grid, s);
-        if (kp <= 64) return launch_one<T, D, 16, 4, kKselect>(a, lds, grid, s);
+        // (4-lane groups for K_prev <= 32 and 8-lane groups for K_prev <= 64 measured
+        // 30 % and 11 % faster than 16-lane groups on the bf16 640x384 chain)
+        if (kp <= 16) return launch_one<T, D, 4, 4, kKselect>(a, lds, grid, s);
+        if (kp <= 32) return launch_one<T, D, 4, 8, kKselect>(a, lds, grid, s);
+        if (kp <= 64) return launch_one<T, D, 8, 8, kKselect>(a, lds, grid, s);
         if (kp <= 128) return launch_one<T, D, 16, 8, kKselect>(a, lds, grid, s);
         // K_prev <= 256: bf16 takes 4 rows of 16 candidates per lane per wavefront
         // (more independent gathers in flight per wave); fp32 2 rows of 8 (16 would not

@@ -174,6 +174,12 @@ EDGE = [
     (1, 1, 32, 32, 32, 32, 5, 20, 7, "f32"),      # ragged small K_prev
     (1, 2, 32, 32, 32, 32, 16, 256, 128, "f32"),  # rows filled exactly (as in the chain)
     (1, 2, 32, 32, 32, 32, 16, 512, 200, "f32"),  # 64-lane rows
+    # narrow row groups of the selection kernel (4 lanes up to K_prev 32, 8 up to 64)
+    (1, 2, 32, 32, 32, 32, 7, 12, 5, "bf16"),     # ragged 4-lane rows, 4 candidates per lane
+    (1, 2, 32, 32, 16, 32, 9, 29, 16, "f32"),     # ragged 4-lane rows, 8 candidates per lane
+    (1, 2, 32, 32, 32, 32, 3, 48, 20, "bf16"),    # ragged 8-lane rows
+    (1, 2, 32, 32, 32, 32, 16, 32, 16, "f32"),    # full 4-lane rows (as in the chain)
+    (1, 2, 32, 32, 32, 32, 16, 64, 32, "bf16"),   # full 8-lane rows (as in the chain)
 ]
 
 
@@ -187,6 +193,15 @@ def test_edge_cases(case):
 def test_exact_ties_lower_index_wins():
     # every score of a row equal and A_prev with repeated values: ties everywhere
     st = single_layer_case(1, 2, 32, 32, 32, 32, 0, 256, 100, "f32", 51, dup_keys=True, zero_frac=0.3)
+    assert st["tie_rows"] == 0
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,K_prev,K_l", [("f32", 16, 7), ("bf16", 32, 16), ("f32", 30, 11), ("bf16", 64, 32),
+                                             ("f32", 50, 21)])
+def test_exact_ties_narrow_row_groups(dtype, K_prev, K_l):
+    # the same tie pattern on the 4- and 8-lane row groups of small candidate lists
+    st = single_layer_case(1, 2, 32, 32, 32, 32, 5, K_prev, K_l, dtype, 52 + K_prev, dup_keys=True, zero_frac=0.3)
     assert st["tie_rows"] == 0
 
 
