@@ -465,7 +465,7 @@ int run_sparse_backward(const pfa_shape* shape, const void* Q, const void* K, co
     if (!pfa::backward_dkv_sorted(shape->dtype, g.d, g.N, K_l) && !pfa::backward_dkv_mfma(g.d, g.N, K_l))
         return PFA_ERR_UNSUPPORTED;
 
-    pfa::BackwardArgs a;
+    pfa::BackwardArgs a{};
     a.Q = Q; a.K = K; a.V = V;
     a.I_prev = I_prev; a.A_prev = A_prev;
     a.I_l = I_l; a.A_l = A_l;
@@ -504,10 +504,14 @@ int run_sparse_backward(const pfa_shape* shape, const void* Q, const void* K, co
         b.rows_per_block = g.N;
         if (pfa::backward_dkv_sorted(dt, g.d, g.N, K_l)) {
             b.blocks_per_wh = 1;
-            const int64_t sgrid = n_wh(g) * ((g.N + 1023) / 1024);   // 1024 tokens per workgroup
+            const int64_t units = n_wh(g) * ((g.N + 1023) / 1024);   // 1024 tokens per unit
+            const bool split = pfa::backward_dkv_sorted_split(dt, g.d, g.N, K_l, units, compute_units());
+            // split: a dV and a dK workgroup per unit, in groups of 8 units
+            const int64_t sgrid = split ? 2 * ((units + 7) / 8) * 8 : units;
             if (sgrid > 0x7fffffff) return PFA_ERR_UNSUPPORTED;
+            b.dkv_units = (int)units;
             e = timed(PFA_KERNEL_BWD_SCATTER, s,
-                      [&] { return pfa::launch_backward_dkv_sorted(b, dt, g.d, (int)sgrid, s); });
+                      [&] { return pfa::launch_backward_dkv_sorted(b, dt, g.d, split, (int)sgrid, s); });
         } else {
             b.blocks_per_wh = 1;
             b.dkv_full = (int)pfa::backward_dkv_full(n_wh(g), g.N, compute_units());

@@ -783,12 +783,15 @@ __global__ __launch_bounds__(16 * kWave) void bwd_dkv_kernel(const BackwardArgs 
     }
 }
 
-// dK and dV with work in proportion to the kept pairs: one workgroup per
-// window-head and 1024 tokens (global mode: several per head, each taking the
-// entries of its token range), thread t owns token tok0 + t and keeps its dV and
-// dK rows in registers. The window-head's rows are taken in chunks of R = 32 MW rows:
-//   (a) the chunk's dO and Q rows are staged in LDS (16-byte chunks permuted by
-//       row, so the owners' reads of random rows spread over the banks);
+// dK or dV with work in proportion to the kept pairs. A unit is a window-head and
+// up to 1024 of its tokens (global mode: several units per head, each taking the
+// entries of its token range); each unit has two workgroups, one for dV and one
+// for dK, 8 workgroup ids apart so that both run on one XCD and share the unit's
+// entries in its L2. Thread t owns token tok0 + t and keeps its row of the
+// workgroup's matrix in registers. The window-head's rows are taken in chunks of
+// R = 32 MW rows:
+//   (a) the chunk's rows of dO (dV) or Q (dK) are staged in LDS (16-byte chunks
+//       permuted by row, so the owners' reads of random rows spread over the banks);
 //   (b) every kept entry (row r, token j) of the chunk sets bit r of token j's
 //       R-bit row mask (LDS or: no order dependence);
 //   (c) the masks' popcounts are scanned over the tokens (wave scans, then the
@@ -796,12 +799,245 @@ __global__ __launch_bounds__(16 * kWave) void bwd_dkv_kernel(const BackwardArgs 
 //   (d) entry (r, j) is written to its token's segment at the rank of r in j's
 //       mask: records come out sorted by token, then by row, whatever the
 //       scheduling, so the sums below always run in the same order;
-//   (e) each owner adds A dO_r to its dV row and A g / sqrt(d) q_r to its dK row
-//       over its segment.
+//   (e) each owner adds A dO_r to its dV row, or A g / sqrt(d) q_r to its dK row,
+//       over its segment, while the next chunk's entries and rows are loaded.
 // Per chunk there are about R K_l / N records per token; the work of the owners
-// is K_l d MACs per row and matrix, not N d.
+// is K_l d MACs per row, not N d.
 template <typename T, int D, int MW>
 __global__ __launch_bounds__(16 * kWave) void bwd_dkv_sorted_kernel(const BackwardArgs p) {
+    constexpr int R = 32 * MW;                 // rows per chunk
+    constexpr int NT = 16 * kWave;             // threads (tokens owned: the first NTK)
+    constexpr int EPC = Chunk<T>::kElems;
+    constexpr int QCH = D / EPC;               // 16-byte chunks of a Q row
+    constexpr int OCH = D / 4;                 // 16-byte chunks of a dO row (fp32)
+    constexpr int QROWB = D * (int)sizeof(T);
+    constexpr int OROWB = D * 4;
+    constexpr int EPT = 8192 / NT;             // entries per thread (the launcher keeps R K_l <= 8192)
+    constexpr int RL = (R * OCH + NT - 1) / NT;   // 16-byte row chunks per thread
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int xcd = (int)blockIdx.x & 7;
+    const int slot = (int)blockIdx.x >> 3;
+    const bool kmat = (slot & 1) != 0;         // false: dV, true: dK (uniform)
+    const int unit = (slot >> 1) * 8 + xcd;
+    if (unit >= p.dkv_units) return;           // padding of the last group of 8 units
+
+    const Geom g = p.g;
+    const int N = g.N;   // rows (and tokens) of the window-head
+    const int K_l = p.K_l;
+    const unsigned kmagic = (unsigned)((0x100000000ull + (unsigned)K_l - 1u) / (unsigned)K_l);   // ceil(2^32 / K_l)
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int wave = t / kWave;
+    const int tparts = (N + NT - 1) / NT;
+    const int tok0 = (unit % tparts) * NT;   // this workgroup's tokens: [tok0, tok0 + NTK)
+    const int NTK = min(NT, N - tok0);
+    const WhPart w = decode_block_id(unit / tparts, 1, p.xcd_map, g);
+    const size_t plane = (size_t)w.bh * g.H * g.W * D;
+    const unsigned char* Qh = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.Q) + plane);
+    const unsigned char* dOh = reinterpret_cast<const unsigned char*>(p.dO + plane);
+
+    unsigned char* rows = smem;                                       // [R][OROWB]: dO or Q rows
+    uint32_t* mask = reinterpret_cast<uint32_t*>(rows + R * OROWB);   // [MW][NTK]: word m of token j at m NTK + j
+    int* seg = reinterpret_cast<int*>(mask + NTK * MW);               // [NTK] segment starts
+    int* wsum = seg + NTK;                                            // [16] wave totals
+    const size_t roff = ((size_t)(R * OROWB + (NTK * MW + NTK + 16) * 4) + 7) & ~(size_t)7;
+    float* recw = reinterpret_cast<float*>(smem + roff);              // [R K_l] A, or A g / sqrt(d)
+    uint16_t* recr = reinterpret_cast<uint16_t*>(recw + R * K_l);     // [R K_l] row in the chunk
+
+    const size_t wh_pairs = (size_t)w.wh * N * K_l;
+    const int pair_bytes = N * K_l * 4;
+    const __amdgpu_buffer_rsrc_t rI = make_rsrc(p.I_l + wh_pairs, pair_bytes);
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A_l + wh_pairs, pair_bytes);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g_buf + wh_pairs, pair_bytes);
+
+    // a chunk's rows and entries (raw), loaded one chunk ahead
+    int ej[EPT];
+    float ea[EPT], eg[EPT];
+    uint4 rr[RL];
+    auto load_chunk = [&](int r0) {
+        const int rows_c = min(R, N - r0);
+        const int ne = rows_c * K_l;
+        // rows first: their addresses may need a reloaded value, whose wait must not
+        // also wait for the entries
+        if (kmat) {
+#pragma unroll
+            for (int k = 0; k < RL; ++k) {
+                const int u = t + NT * k;
+                if (u < rows_c * QCH) {
+                    const int r = u / QCH, c = u - r * QCH;
+                    rr[k] = *reinterpret_cast<const uint4*>(Qh + (size_t)slot_pixel(g, w.wy, w.wx, r0 + r) * QROWB +
+                                                            c * 16);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < RL; ++k) {
+                const int u = t + NT * k;
+                if (u < rows_c * OCH) {
+                    const int r = u / OCH, c = u - r * OCH;
+                    rr[k] = *reinterpret_cast<const uint4*>(dOh + (size_t)slot_pixel(g, w.wy, w.wx, r0 + r) * OROWB +
+                                                            c * 16);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            int e = t + NT * u;
+            __asm__ volatile("" : "+v"(e));
+            const int off = e < ne ? (r0 * K_l + e) * 4 : 0x7FFFFFF0;   // past the range: not loaded
+            ej[u] = (int)__builtin_amdgcn_raw_buffer_load_b32(rI, off, 0, 0);
+            ea[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rA, off, 0, 0));
+            if (kmat) eg[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, off, 0, 0));
+        }
+    };
+    float acc[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) acc[c] = 0.0f;
+
+    load_chunk(0);
+    if (t < NTK) {
+#pragma unroll
+        for (int m = 0; m < MW; ++m) mask[m * NTK + t] = 0u;   // (the owners clear them again after each chunk)
+    }
+    __syncthreads();   // every mask is clear before any entry of the first chunk is set
+    for (int r0 = 0; r0 < N; r0 += R) {
+        const int rows_c = min(R, N - r0);
+        const int ne = rows_c * K_l;
+        // (a) the chunk's rows into LDS (the previous chunk's owners are done)
+        if (kmat) {
+#pragma unroll
+            for (int k = 0; k < RL; ++k) {
+                const int u = t + NT * k;
+                if (u < rows_c * QCH) {
+                    const int r = u / QCH, c = u - r * QCH;
+                    *reinterpret_cast<uint4*>(rows + r * QROWB + ((c ^ (r & (QCH - 1))) * 16)) = rr[k];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < RL; ++k) {
+                const int u = t + NT * k;
+                if (u < rows_c * OCH) {
+                    const int r = u / OCH, c = u - r * OCH;
+                    *reinterpret_cast<uint4*>(rows + r * OROWB + ((c ^ (r & (OCH - 1))) * 16)) = rr[k];
+                }
+            }
+        }
+        // the entries' tokens (- tok0, or -1: no entry, or another unit's token) and weights
+        int jr[EPT];
+        float wt[EPT];
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            int e = t + NT * u;
+            __asm__ volatile("" : "+v"(e));
+            const int j = (int)min((unsigned)ej[u], (unsigned)(N - 1));   // memory safety only: indices lie in [0, N)
+            jr[u] = (e < ne && j >= tok0 && j - tok0 < NTK) ? j - tok0 : -1;
+            wt[u] = kmat ? ea[u] * eg[u] * p.scale : ea[u];
+        }
+        // (b) row masks per token. The entry's row r = e / K_l comes from a multiply-high
+        // (exact for e < 2^13 and K_l <= 256); e is made opaque per chunk, so that the
+        // EPT rows and their masks are not kept live across the chunk loop.
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            int e = t + NT * u;
+            __asm__ volatile("" : "+v"(e));
+            if (jr[u] >= 0) {
+                const int r = (int)__umulhi((unsigned)e, kmagic);
+                atomicOr(&mask[(r >> 5) * NTK + jr[u]], 1u << (r & 31));
+            }
+        }
+        __syncthreads();
+        // (c) segment of each token: exclusive scan of the mask popcounts
+        int cnt = 0;
+        if (t < NTK) {
+#pragma unroll
+            for (int m = 0; m < MW; ++m) cnt += __builtin_popcount(mask[m * NTK + t]);
+        }
+        int incl = cnt;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        if (lane == kWave - 1) wsum[wave] = incl;
+        __syncthreads();
+        int base = 0;
+        for (int v = 0; v < wave; ++v) base += wsum[v];
+        const int st = base + incl - cnt;
+        if (t < NTK) seg[t] = st;
+        __syncthreads();
+        // (d) records at the rank of their row in the token's mask
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            int e = t + NT * u;
+            __asm__ volatile("" : "+v"(e));
+            if (jr[u] >= 0) {
+                const int r = (int)__umulhi((unsigned)e, kmagic);
+                const uint32_t* mj = mask + jr[u];
+                int rank = __builtin_popcount(mj[(r >> 5) * NTK] & ((1u << (r & 31)) - 1u));
+#pragma unroll
+                for (int m = 0; m < MW; ++m)
+                    if (m < (r >> 5)) rank += __builtin_popcount(mj[m * NTK]);
+                const int pos = seg[jr[u]] + rank;
+                recw[pos] = wt[u];
+                recr[pos] = (uint16_t)r;
+            }
+        }
+        __syncthreads();
+        // the next chunk's loads are in flight during the owners' sums
+        if (r0 + R < N) load_chunk(r0 + R);
+        // (e) owners: their segment in row order; their masks are cleared for the next chunk
+        if (t < NTK) {
+#pragma unroll
+            for (int m = 0; m < MW; ++m) mask[m * NTK + t] = 0u;
+        }
+        if (kmat) {
+            for (int k = st; k < st + cnt; ++k) {
+                const float wv = recw[k];
+                const int r = recr[k];
+#pragma unroll
+                for (int c = 0; c < QCH; ++c) {
+                    float qf[EPC];
+                    Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(rows + r * QROWB + ((c ^ (r & (QCH - 1))) * 16)),
+                                     qf);
+#pragma unroll
+                    for (int y = 0; y < EPC; ++y) acc[EPC * c + y] = fmaf(wv, qf[y], acc[EPC * c + y]);
+                }
+            }
+        } else {
+            for (int k = st; k < st + cnt; ++k) {
+                const float wv = recw[k];
+                const int r = recr[k];
+#pragma unroll
+                for (int c = 0; c < OCH; ++c) {
+                    const float4 o4 = *reinterpret_cast<const float4*>(rows + r * OROWB + ((c ^ (r & (OCH - 1))) * 16));
+                    acc[4 * c + 0] = fmaf(wv, o4.x, acc[4 * c + 0]);
+                    acc[4 * c + 1] = fmaf(wv, o4.y, acc[4 * c + 1]);
+                    acc[4 * c + 2] = fmaf(wv, o4.z, acc[4 * c + 2]);
+                    acc[4 * c + 3] = fmaf(wv, o4.w, acc[4 * c + 3]);
+                }
+            }
+        }
+        __syncthreads();   // the next chunk reuses the LDS
+    }
+    if (t < NTK) {
+        float* dst = (kmat ? p.dK : p.dV) + plane + (size_t)slot_pixel(g, w.wy, w.wx, tok0 + t) * D;
+#pragma unroll
+        for (int c = 0; c < D; c += 4)
+            *reinterpret_cast<float4*>(dst + c) = make_float4(acc[c], acc[c + 1], acc[c + 2], acc[c + 3]);
+    }
+}
+
+// The same with both matrices in one workgroup per unit (window-head and 1024
+// tokens): thread t owns token tok0 + t and keeps its dV and dK rows in
+// registers, with no room left to load the next chunk during the sums. Steps
+// (a)-(e) as above, with the chunk's dO and Q rows both staged and records of
+// (A, A g / sqrt(d)). Used where the units fill the CUs over several rounds
+// anyway, so that splitting the matrices over two workgroups would only repeat
+// steps (a)-(d).
+template <typename T, int D, int MW>
+__global__ __launch_bounds__(16 * kWave) void bwd_dkv_sorted_pair_kernel(const BackwardArgs p) {
     constexpr int R = 32 * MW;                 // rows per chunk
     constexpr int NT = 16 * kWave;             // threads (tokens owned: the first N)
     constexpr int EPC = Chunk<T>::kElems;
@@ -1016,38 +1252,49 @@ hipError_t launch_rows_t(const BackwardArgs& a, bool has_v, bool has_k, int grid
 
 // rows per chunk of the sorted dK/dV kernel: the largest of 32, 64, 128, 256 rows
 // (at most N rounded up to 32) whose LDS (staged rows, token masks, records) fits
-int sorted_rows(int dtype, int D, int N, int K_l) {
-    if (K_l > 256) return 0;
-    const int rowb = D * 4 + D * (dtype == 0 ? 4 : 2);
+// LDS of the sorted dK/dV kernels (staged rows, token masks, records); pair: both
+// matrices in one workgroup
+int sorted_lds(int dtype, int D, int N, int K_l, int R, bool pair) {
+    const int rowb = pair ? D * 4 + D * (dtype == 0 ? 4 : 2) : D * 4;
+    const int recb = pair ? 10 : 6;
     const int nt = N < 1024 ? N : 1024;   // tokens per workgroup
+    return R * rowb + (nt * (R / 32) + nt + 16) * 4 + 8 + R * K_l * recb;
+}
+
+// rows per chunk of the sorted dK/dV kernels: the largest of 32, 64, 128, 256 rows
+// (at most N rounded up to 32) whose LDS fits; 0: none fits
+int sorted_rows(int dtype, int D, int N, int K_l, bool pair) {
+    if (K_l > 256) return 0;
     int best = 0;
     for (int R = 32; R <= 256; R *= 2) {
         if (R * K_l > 8192) break;
-        const int mw = R / 32;
-        const int lds = R * rowb + (nt * mw + nt + 16) * 4 + 8 + R * K_l * 10;
-        if (lds <= kLdsBytes) best = R;
+        if (sorted_lds(dtype, D, N, K_l, R, pair) <= kLdsBytes) best = R;
         if (R >= N) break;
     }
     return best;
 }
 
-int sorted_lds(int dtype, int D, int N, int K_l, int R) {
-    const int rowb = D * 4 + D * (dtype == 0 ? 4 : 2);
-    const int nt = N < 1024 ? N : 1024;
-    return R * rowb + (nt * (R / 32) + nt + 16) * 4 + 8 + R * K_l * 10;
-}
-
 template <typename T, int D>
-hipError_t launch_sorted_t(const BackwardArgs& a, int grid, hipStream_t s) {
-    const int R = sorted_rows(sizeof(T) == 4 ? 0 : 1, D, a.g.N, a.K_l);
-    const int lds = sorted_lds(sizeof(T) == 4 ? 0 : 1, D, a.g.N, a.K_l, R);
+hipError_t launch_sorted_t(const BackwardArgs& a, bool split, int grid, hipStream_t s) {
+    constexpr int dt = sizeof(T) == 4 ? 0 : 1;
+    const int R = sorted_rows(dt, D, a.g.N, a.K_l, !split);
+    const int lds = sorted_lds(dt, D, a.g.N, a.K_l, R, !split);
     const int th = 16 * kWave;
+    if (split) {
+        switch (R) {
+            case 32: return launch_bwd(bwd_dkv_sorted_kernel<T, D, 1>, a, th, lds, grid, s);
+            case 64: return launch_bwd(bwd_dkv_sorted_kernel<T, D, 2>, a, th, lds, grid, s);
+            case 128: return launch_bwd(bwd_dkv_sorted_kernel<T, D, 4>, a, th, lds, grid, s);
+            case 256: return launch_bwd(bwd_dkv_sorted_kernel<T, D, 8>, a, th, lds, grid, s);
+            default: return hipErrorInvalidValue;   // rejected by backward_dkv_sorted
+        }
+    }
     switch (R) {
-        case 32: return launch_bwd(bwd_dkv_sorted_kernel<T, D, 1>, a, th, lds, grid, s);
-        case 64: return launch_bwd(bwd_dkv_sorted_kernel<T, D, 2>, a, th, lds, grid, s);
-        case 128: return launch_bwd(bwd_dkv_sorted_kernel<T, D, 4>, a, th, lds, grid, s);
-        case 256: return launch_bwd(bwd_dkv_sorted_kernel<T, D, 8>, a, th, lds, grid, s);
-        default: return hipErrorInvalidValue;   // rejected by backward_dkv_sorted
+        case 32: return launch_bwd(bwd_dkv_sorted_pair_kernel<T, D, 1>, a, th, lds, grid, s);
+        case 64: return launch_bwd(bwd_dkv_sorted_pair_kernel<T, D, 2>, a, th, lds, grid, s);
+        case 128: return launch_bwd(bwd_dkv_sorted_pair_kernel<T, D, 4>, a, th, lds, grid, s);
+        case 256: return launch_bwd(bwd_dkv_sorted_pair_kernel<T, D, 8>, a, th, lds, grid, s);
+        default: return hipErrorInvalidValue;   // the caller checks sorted_rows first
     }
 }
 
@@ -1102,20 +1349,36 @@ int backward_fused_rows(int dtype, int D, int N, int K_l, bool want_dap) {
 }
 
 bool backward_dkv_sorted(int dtype, int D, int N, int K_l) {
-    // measured on the MI355X (fp32 and bf16, N = 1024): per window-head about 90 us of
-    // fixed cost (chunk loads and barriers, one workgroup per CU) plus 2.5 us per kept
-    // slot of a row; the dense MFMA form costs about N^2 whatever K_l. The sorted form
-    // wins from K_l = N / 16 down (0.66 against 1.53 ms at K_l = 16 on the 640x384 map,
-    // 1.48 against 1.87 at K_l = 64, 4.0 against 2.2 at K_l = 256), and it is the only
-    // form for N not a multiple of 16 when it fits
-    if (sorted_rows(dtype, D, N, K_l) == 0) return false;
+    // measured on the MI355X (fp32 and bf16, N = 1024, both matrices in one
+    // workgroup): per window-head about 90 us of fixed cost (chunk loads and
+    // barriers, one workgroup per CU) plus 2.5 us per kept slot of a row; the dense
+    // MFMA form costs about N^2 whatever K_l. The sorted form wins from K_l = N / 16
+    // down (0.66 against 1.53 ms at K_l = 16 on the 640x384 map, 1.48 against 1.87
+    // at K_l = 64, 4.0 against 2.2 at K_l = 256), and it is the only form for N not
+    // a multiple of 16 when it fits
+    if (sorted_rows(dtype, D, N, K_l, false) == 0) return false;
     return 16 * K_l <= N || !backward_dkv_mfma(D, N, K_l);
 }
 
-hipError_t launch_backward_dkv_sorted(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream) {
+bool backward_dkv_sorted_split(int dtype, int D, int N, int K_l, int64_t units, int cus) {
+    // one workgroup per CU either way (1024 threads at 128 VGPRs). A one-matrix
+    // workgroup takes 0.51-0.59 of a two-matrix one (its next chunk loads during the
+    // sums), so the split pays where it needs fewer than about 1.8 times the rounds:
+    // 384 window-heads on 256 CUs (3 rounds against 2), not 1440 (12 against 6)
+    if (sorted_rows(dtype, D, N, K_l, true) == 0) return true;
+    if (cus <= 0) return false;
+    const int64_t pair_rounds = (units + cus - 1) / cus;
+    const int64_t split_rounds = (2 * units + cus - 1) / cus;
+    return split_rounds * 11 < pair_rounds * 20;
+}
+
+hipError_t launch_backward_dkv_sorted(const BackwardArgs& a, int dtype, int D, bool split, int grid,
+                                      hipStream_t stream) {
     if (dtype == 0)
-        return D == 16 ? launch_sorted_t<float, 16>(a, grid, stream) : launch_sorted_t<float, 32>(a, grid, stream);
-    return D == 16 ? launch_sorted_t<uint16_t, 16>(a, grid, stream) : launch_sorted_t<uint16_t, 32>(a, grid, stream);
+        return D == 16 ? launch_sorted_t<float, 16>(a, split, grid, stream)
+                       : launch_sorted_t<float, 32>(a, split, grid, stream);
+    return D == 16 ? launch_sorted_t<uint16_t, 16>(a, split, grid, stream)
+                   : launch_sorted_t<uint16_t, 32>(a, split, grid, stream);
 }
 
 bool backward_dkv_mfma(int D, int N, int K_l) {

@@ -83,6 +83,10 @@ struct BackwardArgs {
     // each further pair (workgroups 8 apart, one XCD) takes the two token halves
     // of one window-head (balances the last round over the CUs)
     int dkv_full;
+    // sorted dK/dV kernel, one matrix per workgroup: (window-head, token range)
+    // units; workgroups 8n + x and 8(n + 1) + x (n even) take the dV and the dK of
+    // unit 8(n / 2) + x
+    int dkv_units;
 };
 
 // Row pass: with both K and V staged (when they fit in LDS together), or as a
@@ -94,9 +98,13 @@ hipError_t launch_backward_rows(const BackwardArgs& a, int dtype, int D, bool ha
 // dA^{l-1} of the rows the row pass flagged, from the scores (after the row pass).
 hipError_t launch_backward_exact_dap(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream);
 // dK and dV from the kept pairs sorted by token per row chunk (work in proportion
-// to K_l); one workgroup per window-head.
+// to K_l). A unit is a window-head and up to 1024 of its tokens; split: two
+// workgroups per unit (dV, dK; grid 2 * units rounded up to 16, dkv_units set),
+// else one (grid = units).
 bool backward_dkv_sorted(int dtype, int D, int N, int K_l);
-hipError_t launch_backward_dkv_sorted(const BackwardArgs& a, int dtype, int D, int grid, hipStream_t stream);
+bool backward_dkv_sorted_split(int dtype, int D, int N, int K_l, int64_t units, int cus);
+hipError_t launch_backward_dkv_sorted(const BackwardArgs& a, int dtype, int D, bool split, int grid,
+                                      hipStream_t stream);
 // dK and dV as dense MFMA products over LDS-densified row blocks (N % 16 == 0).
 bool backward_dkv_mfma(int D, int N, int K_l);
 // whole-window-head dK/dV workgroups for n_wh window-heads on `cus` compute units
