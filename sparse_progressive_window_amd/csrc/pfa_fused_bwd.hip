@@ -13,8 +13,11 @@
 // and its dA^1 rows (aligned with I^2) are spread into the dense [N, N] rows that
 // the first layer's backward reads.
 //
-// first_map_kept_kernel: 4 wavefronts per workgroup of 256 rows, the window's k1
-// rows staged in LDS; a wavefront takes a row, its lanes the row's kept slots;
+// first_map_kept_kernel: 16 wavefronts per workgroup of 512 rows, the window's k1
+// rows staged in LDS; a wavefront takes a row, its lanes the row's kept slots. Each
+// lane reads the 16-byte chunks of its k1 row (and of the query) in a lane-rotated
+// order, so the gathers of random rows spread over the LDS banks; bf16 products
+// are taken on the packed pairs (v_dot2c_f32_bf16: exact products, fp32 sums).
 // A^1 is written aligned with I^2 (coalesced).
 // spread_rows_kernel: one wavefront per row: the dense row is built in the wave's
 // LDS row (zeros, then the K2 values at their slots; one wave's LDS accesses
@@ -25,8 +28,8 @@
 namespace pfa {
 namespace {
 
-constexpr int kMapWaves = 4;
-constexpr int kMapRows = 256;   // rows per workgroup
+constexpr int kMapWaves = 16;
+constexpr int kMapRows = 512;   // rows per workgroup
 constexpr float kLog2eF = 1.4426950408889634f;
 
 template <typename T, int D>
@@ -47,26 +50,49 @@ __global__ __launch_bounds__(kMapWaves * kWave) void first_map_kept_kernel(const
     const int row0 = w.part * kMapRows;
     const int row1 = min(N, row0 + kMapRows);
     const T* Qh = static_cast<const T*>(p.Q1) + plane;
+    constexpr int MAXU = 4;   // kept slots per lane (the caller admits K2 <= 256)
+    int coff[CH];   // lane-rotated chunk order
+#pragma unroll
+    for (int m = 0; m < CH; ++m) coff[m] = ((m + lane) % CH) * 16;
+    const int nu = (K2 + kWave - 1) / kWave;
     for (int i = row0 + wave; i < row1; i += kMapWaves) {
         const size_t row = (size_t)w.wh * N + i;
-        const unsigned char* qr = reinterpret_cast<const unsigned char*>(Qh + (size_t)slot_pixel(g, w.wy, w.wx, i) * D);
-        float q[D];
-#pragma unroll
-        for (int c = 0; c < CH; ++c) Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(qr + c * 16), &q[c * EPC]);
-        const float l2 = p.lse1[row] * kLog2eF;
         const int32_t* Ir = p.I2 + row * K2;
         float* Ar = p.A1 + row * K2;
-        for (int e = lane; e < K2; e += kWave) {
-            const int j = (int)min((unsigned)Ir[e], (unsigned)(N - 1));
+        // the row's kept slots first, then the query chunks: their loads overlap
+        int jv[MAXU];
+#pragma unroll
+        for (int u = 0; u < MAXU; ++u) {
+            const int e = lane + kWave * u;
+            jv[u] = (u < nu && e < K2) ? (int)min((unsigned)Ir[e], (unsigned)(N - 1)) : 0;
+        }
+        const unsigned char* qr = reinterpret_cast<const unsigned char*>(Qh + (size_t)slot_pixel(g, w.wy, w.wx, i) * D);
+        uint4 qc[CH];
+#pragma unroll
+        for (int m = 0; m < CH; ++m) qc[m] = *reinterpret_cast<const uint4*>(qr + coff[m]);
+        const float l2 = p.lse1[row] * kLog2eF;
+#pragma unroll
+        for (int u = 0; u < MAXU; ++u) {
+            if (u >= nu) break;   // uniform
+            const int e = lane + kWave * u;
+            const unsigned char* kr = smem + jv[u] * ROWB;
             float acc = 0.0f;
 #pragma unroll
-            for (int c = 0; c < CH; ++c) {
-                float kf[EPC];
-                Chunk<T>::to_f32(*reinterpret_cast<const uint4*>(smem + j * ROWB + c * 16), kf);
-#pragma unroll
-                for (int y = 0; y < EPC; ++y) acc = fmaf(q[c * EPC + y], kf[y], acc);
+            for (int m = 0; m < CH; ++m) {
+                const uint4 kc = *reinterpret_cast<const uint4*>(kr + coff[m]);
+                if constexpr (sizeof(T) == 2) {
+                    acc = dot2_bf16(qc[m].x, kc.x, acc);
+                    acc = dot2_bf16(qc[m].y, kc.y, acc);
+                    acc = dot2_bf16(qc[m].z, kc.z, acc);
+                    acc = dot2_bf16(qc[m].w, kc.w, acc);
+                } else {
+                    acc = fmaf(__uint_as_float(qc[m].x), __uint_as_float(kc.x), acc);
+                    acc = fmaf(__uint_as_float(qc[m].y), __uint_as_float(kc.y), acc);
+                    acc = fmaf(__uint_as_float(qc[m].z), __uint_as_float(kc.z), acc);
+                    acc = fmaf(__uint_as_float(qc[m].w), __uint_as_float(kc.w), acc);
+                }
             }
-            Ar[e] = fast_exp2(fmaf(acc, p.scale2, -l2));
+            if (e < K2) Ar[e] = fast_exp2(fmaf(acc, p.scale2, -l2));
         }
     }
 }
