@@ -827,13 +827,37 @@ __device__ __forceinline__ int kswz(int r) {
     return (r ^ (r >> 2)) & 3;
 }
 
+// Reduction of one value per row for the 4 rows of a wave whose values are spread
+// over all 64 lanes (v[r] = this lane's part of row r): a swap across the 32-lane
+// halves and a swap across 16-lane rows pair the rows up (v_permlane32_swap,
+// v_permlane16_swap), then a 16-lane reduction. Row g's result ends in every lane
+// of the 16-lane group g.
+template <class Op>
+__device__ __forceinline__ float rows4_to_groups(const float (&v)[4], Op op) {
+    const auto p02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[2]), false, false);
+    const auto p13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[1]), __float_as_uint(v[3]), false, false);
+    const float w02 = op(__uint_as_float(p02[0]), __uint_as_float(p02[1]));   // rows 0 | 2
+    const float w13 = op(__uint_as_float(p13[0]), __uint_as_float(p13[1]));   // rows 1 | 3
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(w02), __float_as_uint(w13), false, false);
+    return Grp<16>::all(op(__uint_as_float(q[0]), __uint_as_float(q[1])), op);
+}
+template <class Op>
+__device__ __forceinline__ int rows4_to_groups_i(const int (&v)[4], Op op) {
+    const auto p02 = __builtin_amdgcn_permlane32_swap((unsigned)v[0], (unsigned)v[2], false, false);
+    const auto p13 = __builtin_amdgcn_permlane32_swap((unsigned)v[1], (unsigned)v[3], false, false);
+    const int w02 = op((int)p02[0], (int)p02[1]);
+    const int w13 = op((int)p13[0], (int)p13[1]);
+    const auto q = __builtin_amdgcn_permlane16_swap((unsigned)w02, (unsigned)w13, false, false);
+    return Grp<16>::all_i(op((int)q[0], (int)q[1]), op);
+}
+
 // Selection-only layer whose candidate list is every slot of a 32x32 window
 // (I^{l-1} implicit, K_prev = N = 1024). Scores of a batch of 4 query rows x 64
 // candidates come from 4x4 MFMA blocks (A = the 4 query rows, B = 64 K rows from
-// LDS), which leaves candidate 64t + l of all 4 rows in lane l. A 4x4 transpose
-// across the wave's lane quarters (v_permlane32_swap, v_permlane16_swap) then
-// gives each 16-lane quarter one query row: lane 16g + b holds row g's candidates
-// 16k + b, k = 0..63, so the 4 rows are selected together, one per 16-lane group.
+// LDS), which leaves candidate 64t + l of all 4 rows in lane l. The selection
+// works in that layout: each row's keys span the whole wave, the 4 rows' radix
+// levels share their LDS round trips, and only the bin scans run one row per
+// 16-lane group.
 // DUAL: fused first two layers; the scores are q1.k1 + q.k (the first layer's Q/K
 // under shift1 as a second K region in LDS), with no previous map: by the
 // closed form of the chain, the second layer keeps the top K_l of
@@ -841,8 +865,7 @@ __device__ __forceinline__ int kswz(int r) {
 template <typename T, int D, bool HAS_A, bool DUAL>
 __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseArgs p) {
     constexpr int NW = 16;
-    constexpr int GL = 16;
-    constexpr int KPT = 64;
+    constexpr int GL = 16;                   // lanes that scan one row's bins
     constexpr int BPL = 8;                   // 128 radix bins per row
     constexpr int EPC = Chunk<T>::kElems;
     constexpr int CH = D / EPC;
@@ -891,9 +914,6 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
     const int K_l = p.K_l;
     const float scale2 = p.scale2;
 
-    // A^{l-1} of the batch in the transposed layout: lane (g, b) needs row base+g,
-    // slots 16k + b
-    constexpr int AH = KPT / 2;   // loaded and consumed in two halves (register budget)
     // The batch's query rows (NK sets x 4 rows) pass through the wave's histogram
     // words: the next batch's are loaded after this batch's keys and written there
     // once the selection is done with them, before the I/A stores. Loaded after the
@@ -991,62 +1011,246 @@ __global__ __launch_bounds__(16 * kWave) void all_cand_rows_kernel(const SparseA
             }
         }
         __builtin_amdgcn_s_setprio(2);
-        // the selection phase re-derives its lane values (not kept across the MFMAs)
+        // Selection in the MFMA output layout: acc[t][r] = s(row base + r, candidate
+        // 64t + lane), so a row's 1024 keys lie in 16 registers across the whole wave,
+        // in ascending candidate order over (t, lane). Per-row values (maximum, radix
+        // interval, sums) are wave-uniform and sit in scalar registers; a row whose
+        // threshold is found skips the remaining radix levels of the batch, and a kept
+        // entry's position is one mbcnt over the row's ballot plus a scalar count.
         int lv2;
         __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lv2));
-        const int gv2 = lv2 >> 4;
-        unsigned* hbv2 = hist0 + (wave * 4 + gv2) * HISTG;
-        const int glv2 = lv2 & (GL - 1);
-        float uv[KPT];   // raw scores q.k, then the keys
-        // acc[t][r] = s(row r, candidate 64t + lane): transpose (lane quarter, r)
+        unsigned* hw = hist0 + wave * 4 * HISTG;   // the wave's 4 row histograms
+        float uv[4][16];                            // key of row r, candidate 64t + lane
+        {
+            // keys u = A^{l-1} exp2(scale2 (s - max s)); A^{l-1} is loaded now, two rows
+            // at a time (16 waves per CU cover the load latency)
+            float mx[4];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const auto p02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[t][0]),
-                                                              __float_as_uint(acc[t][2]), false, false);
-            const auto p13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[t][1]),
-                                                              __float_as_uint(acc[t][3]), false, false);
-            const auto q01 = __builtin_amdgcn_permlane16_swap(p02[0], p13[0], false, false);
-            const auto q23 = __builtin_amdgcn_permlane16_swap(p02[1], p13[1], false, false);
-            uv[4 * t + 0] = __uint_as_float(q01[0]);   // candidate 64t + 16q + gl of row grp
-            uv[4 * t + 1] = __uint_as_float(q01[1]);
-            uv[4 * t + 2] = __uint_as_float(q23[0]);
-            uv[4 * t + 3] = __uint_as_float(q23[1]);
-        }
-        // keys u = A^{l-1} exp2(scale2 (s - max s)); A^{l-1} is loaded now, half a
-        // batch at a time (16 waves per CU cover the load latency)
-        float smax = uv[0];
+            for (int r = 0; r < 4; ++r) {
+                mx[r] = acc[0][r];
 #pragma unroll
-        for (int k = 1; k < KPT; ++k) smax = fmaxf(smax, uv[k]);
-        const float c = -Grp<GL>::all(smax, MaxF()) * scale2;
-        const float* arow = HAS_A ? p.A_prev + ((size_t)w.wh * N + min(base + gv2, N - 1)) * N + glv2 : nullptr;
-#pragma unroll
-        for (int h = 0; h < KPT; h += AH) {
-            float ab[AH];
-            if (HAS_A) {
-#pragma unroll
-                for (int k = 0; k < AH; ++k) ab[k] = arow[GL * (h + k)];
+                for (int t = 1; t < 16; ++t) mx[r] = fmaxf(mx[r], acc[t][r]);
             }
+            const float cg = -rows4_to_groups(mx, MaxF()) * scale2;   // row lane >> 4
+            float c[4];
 #pragma unroll
-            for (int k = 0; k < AH; ++k) {
-                const float e = fast_exp2(fmaf(uv[h + k], scale2, c));
-                uv[h + k] = HAS_A ? fmaxf(ab[k] * e, 0.0f) : e;
+            for (int r = 0; r < 4; ++r) c[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cg), 16 * r));
+            const float* abase = HAS_A ? p.A_prev + (size_t)w.wh * N * N + lv2 : nullptr;
+#pragma unroll
+            for (int h = 0; h < 4; h += 2) {
+                float ab[2][16];
+                if (HAS_A) {
+#pragma unroll
+                    for (int rr = 0; rr < 2; ++rr) {
+                        const float* ar = abase + (size_t)min(base + h + rr, N - 1) * N;
+#pragma unroll
+                        for (int t = 0; t < 16; ++t) ab[rr][t] = ar[kWave * t];
+                    }
+                }
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) {
+                        const float e = fast_exp2(fmaf(acc[t][h + rr], scale2, c[h + rr]));
+                        uv[h + rr][t] = HAS_A ? fmaxf(ab[rr][t] * e, 0.0f) : e;
+                    }
+                __asm__ volatile("" ::: "memory");   // the second pair's loads go out after the first is used
             }
-            __asm__ volatile("" ::: "memory");   // the second half's loads go out after the first is used
         }
 
         // the next batch's query rows: loads in flight during the selection
         unsigned qn[NQ];
         const bool more = QLDS && base + NW * 4 < row1;
         if (more) load_q(base + NW * 4, qn);
-        // rows past row1 (last batch) are selected but never stored: every group's
-        // ballots and reductions are its own
-        const bool active = base + gv2 < row1;
+
+        // Exact K_l-th largest key of each row by radix descent over the fp32 bit
+        // patterns (u >= 0, so integer order is float order): the row's interval
+        // [lo, hi) is cut into 128 bins of 2^shift keys counted with LDS atomics; the
+        // 16 lanes of group g then scan row g's bins in descending order (8 per lane)
+        // and publish the bin holding the need-th key; keys above it are kept, and the
+        // search descends into it. A row ends when the bin's keys are all needed or all
+        // equal: every key > tau = lo is kept, need more among the n_tau keys == tau.
+        const unsigned act = (1u << max(0, min(4, row1 - base))) - 1u;   // rows below row1
+        int lo[4], hi[4], need[4], ntau[4];
+        unsigned done = ~act & 0xFu;
+        {
+            int mn[4], mk[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                mn[r] = 0x7fffffff;
+                mk[r] = -1;
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    mn[r] = min(mn[r], __float_as_int(uv[r][t]));
+                    mk[r] = max(mk[r], __float_as_int(uv[r][t]));
+                }
+            }
+            const int mng = rows4_to_groups_i(mn, MinI());
+            const int mkg = rows4_to_groups_i(mk, MaxI());
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                lo[r] = __builtin_amdgcn_readlane(mng, 16 * r);
+                hi[r] = __builtin_amdgcn_readlane(mkg, 16 * r) + 1;
+                need[r] = K_l;
+                ntau[r] = 0;
+                if ((act >> r & 1u) && hi[r] - lo[r] <= 1) {   // all keys equal
+                    done |= 1u << r;
+                    ntau[r] = N;
+                }
+            }
+        }
+        {
+            const int g = lv2 >> 4;
+            const int gl = lv2 & (GL - 1);
+            unsigned* hg = hw + g * HISTG;   // the histogram this lane scans (row g)
+            while (done != 0xFu) {
+                int shift[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) shift[r] = max(32 - __clz(max(hi[r] - lo[r], 2) - 1) - 7, 0);
+                {
+                    // zeros made here (a zero quad kept live across the loop was spilled)
+                    unsigned z;
+                    __asm__ volatile("v_mov_b32 %0, 0" : "=v"(z));
+                    *reinterpret_cast<uint4*>(hg + BPL * gl) = make_uint4(z, z, z, z);
+                    *reinterpret_cast<uint4*>(hg + BPL * gl + 4) = make_uint4(z, z, z, z);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (done >> r & 1u) continue;
+                    unsigned* hr = hw + r * HISTG;
+                    const unsigned range = (unsigned)(hi[r] - lo[r]);
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) {
+                        const unsigned dk = (unsigned)(__float_as_int(uv[r][t]) - lo[r]);
+                        if (dk < range) atomicAdd(&hr[dk >> shift[r]], 1u);
+                    }
+                }
+                __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                // group g's lanes hold bins 127 - 8 gl - b, b = 0..7 (descending key order)
+                const int needl = g == 0 ? need[0] : g == 1 ? need[1] : g == 2 ? need[2] : need[3];
+                unsigned cb[BPL];
+#pragma unroll
+                for (int b = 0; b < BPL; b += 4) {
+                    const uint4 c4 = *reinterpret_cast<const uint4*>(hg + HISTG - BPL * (gl + 1) + b);
+                    cb[BPL - 1 - b] = c4.x;
+                    cb[BPL - 2 - b] = c4.y;
+                    cb[BPL - 3 - b] = c4.z;
+                    cb[BPL - 4 - b] = c4.w;
+                }
+                unsigned lsum = 0;
+#pragma unroll
+                for (int b = 0; b < BPL; ++b) lsum += cb[b];
+                unsigned run = Grp<GL>::incl_scan(lsum) - lsum;
+                // exactly one bin of a searching row matches; its result goes to the row's
+                // words 0..2 (their counts have been read by then). Rows already done
+                // have empty histograms and match nothing.
+#pragma unroll
+                for (int b = 0; b < BPL; ++b) {
+                    if (run < (unsigned)needl && run + cb[b] >= (unsigned)needl) {
+                        hg[0] = (unsigned)(HISTG - 1 - BPL * gl - b);
+                        hg[1] = run;
+                        hg[2] = cb[b];
+                    }
+                    run += cb[b];
+                }
+                __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (done >> r & 1u) continue;
+                    const unsigned* res = hw + r * HISTG;
+                    const int bin = __builtin_amdgcn_readfirstlane((int)res[0]);
+                    const int above = __builtin_amdgcn_readfirstlane((int)res[1]);
+                    const int in_bin = __builtin_amdgcn_readfirstlane((int)res[2]);
+                    need[r] -= above;
+                    lo[r] += bin << shift[r];
+                    hi[r] = min(hi[r], lo[r] + (1 << shift[r]));
+                    if (in_bin == need[r] || hi[r] - lo[r] <= 1) {   // whole bin kept, or all its keys equal
+                        ntau[r] = in_bin;
+                        done |= 1u << r;
+                    }
+                }
+                __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+        }
+
+        // tau = lo, need_tau = need. A tie (more keys equal tau than needed) keeps the
+        // lowest candidates among them, by rank in the store loop; thr = tau - 1 keeps
+        // every key equal to tau, thr = tau (tie rows) adds them by rank.
+        bool tie[4];
+        int thr[4];
+        bool any_tie = false;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            tie[r] = (act >> r & 1u) && ntau[r] > need[r];
+            thr[r] = tie[r] ? lo[r] : lo[r] - 1;
+            any_tie = any_tie || tie[r];
+        }
+        float inv[4];
+        {
+            float ks[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                ks[r] = 0.0f;
+#pragma unroll
+                for (int t = 0; t < 16; ++t) ks[r] += __float_as_int(uv[r][t]) > thr[r] ? uv[r][t] : 0.0f;
+            }
+            float ksg = rows4_to_groups(ks, SumF());   // row lane >> 4
+            if (any_tie) {
+                const int g = lv2 >> 4;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (tie[r] && g == r) ksg += (float)need[r] * __int_as_float(lo[r]);
+            }
+            const float invg = 1.0f / ksg;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) inv[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(invg), 16 * r));
+        }
+        if (more) put_q(qn);   // the histogram words are free again
+
+        // Stores: one buffer store of I and of A per register and row; entries not
+        // kept get an offset past the resource's range, which the hardware drops.
+        // Rows past row1 (last batch) are not stored.
         const size_t rbase = ((size_t)w.wh * N + base) * K_l;
         const int nbytes = max(0, min(4, row1 - base)) * K_l * 4;
-        select_store<GL, KPT, BPL, true, true>(
-            p, lv2, active, N, [&](int k) { return GL * k + glv2; }, [&](int) { return true; }, uv, hbv2,
-            make_rsrc(p.I_out + rbase, nbytes), make_rsrc(p.A_out + rbase, nbytes), gv2 * K_l,
-            [&] { if (more) put_q(qn); });
+        const __amdgpu_buffer_rsrc_t rI = make_rsrc(p.I_out + rbase, nbytes);
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A_out + rbase, nbytes);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (!(act >> r & 1u)) continue;
+            // copies the compiler cannot see through, so the comparisons are not kept
+            // alive as lane masks from the sums above
+            int thr2 = thr[r], tau2 = lo[r];
+            __asm__ volatile("" : "+s"(thr2), "+s"(tau2));
+            const int roff = r * K_l;
+            const float ir = inv[r];
+            int ob = 0;   // entries of the row stored so far
+            auto emit = [&](int t, bool k) {
+                const uint64_t m = ballot(k);
+                // pos is made opaque so that the offset stays a select, not a branch
+                int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)ob));
+                __asm__ volatile("" : "+v"(pos));
+                const int off = k ? (roff + pos) * 4 : 0x7FFFFFF0;
+                __builtin_amdgcn_raw_buffer_store_b32(kWave * t + lv2, rI, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(uv[r][t] * ir), rA, off, 0, 0);
+                ob += popc(m);
+            };
+            if (!tie[r]) {
+#pragma unroll
+                for (int t = 0; t < 16; ++t) emit(t, __float_as_int(uv[r][t]) > thr2);
+            } else {
+                int tb = 0;   // keys equal to tau met so far in the row
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    const bool eq = __float_as_int(uv[r][t]) == tau2;
+                    const uint64_t me = ballot(eq);
+                    const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32),
+                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)me, (uint32_t)tb));
+                    tb += popc(me);
+                    emit(t, __float_as_int(uv[r][t]) > thr2 || (eq && rank < need[r]));
+                }
+            }
+        }
     }
 }
 
