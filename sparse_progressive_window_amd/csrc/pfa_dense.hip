@@ -40,6 +40,8 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 constexpr int kDenseWaves = 8;
 constexpr int kQPerBlock = 16 * kDenseWaves;
@@ -111,14 +113,18 @@ struct DenseOps<uint16_t, D> {
     }
     // P split once per 16-key tile into bf16 hi + lo (round to nearest even with
     // v_cvt_pk_bf16_f32; the remainder is exact in fp32), ~16 bits of P in all
+    // (values converted in pairs, so each conversion is one v_cvt_pk_bf16_f32 and the
+    // packed hi words unpack with one shift or mask per value: 3 VALU per value)
     struct PS { v4s hi, lo; };
     __device__ static PS prep(const float p[4]) {
-        const bf4 h = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
-        const bf4 l = {(__bf16)(p[0] - (float)h[0]), (__bf16)(p[1] - (float)h[1]), (__bf16)(p[2] - (float)h[2]),
-                       (__bf16)(p[3] - (float)h[3])};
+        const bf2 h01 = __builtin_convertvector(f2{p[0], p[1]}, bf2);
+        const bf2 h23 = __builtin_convertvector(f2{p[2], p[3]}, bf2);
+        const uint32_t u01 = __builtin_bit_cast(uint32_t, h01), u23 = __builtin_bit_cast(uint32_t, h23);
+        const bf2 l01 = __builtin_convertvector(f2{p[0] - bf16_lo(u01), p[1] - bf16_hi(u01)}, bf2);
+        const bf2 l23 = __builtin_convertvector(f2{p[2] - bf16_lo(u23), p[3] - bf16_hi(u23)}, bf2);
         PS ps;
-        ps.hi = __builtin_bit_cast(v4s, h);
-        ps.lo = __builtin_bit_cast(v4s, l);
+        ps.hi = __builtin_bit_cast(v4s, make_uint2(u01, u23));
+        ps.lo = __builtin_bit_cast(v4s, make_uint2(__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)));
         return ps;
     }
     __device__ static v4f pv(const PS& ps, const unsigned char* const vrow[4], int dim, v4f acc) {
@@ -317,13 +323,17 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
             v4f acc[SUB];
 #pragma unroll
             for (int s = 0; s < SUB; ++s) acc[s] = tile_scores(kt, s);
-            // scaled (and biased) scores in base-2 units
+            // scaled and biased scores in base-2 units; without a bias the scores stay
+            // raw and the scale is folded into the exponent's argument below (the row
+            // maximum scales with them: rounding of x * sc is monotone for sc > 0)
+            if constexpr (BIAS) {
 #pragma unroll
-            for (int s = 0; s < SUB; ++s) {
-                float b[4] = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (BIAS) tile_bias(t * KT + s * 16, b);
+                for (int s = 0; s < SUB; ++s) {
+                    float b[4] = {0.f, 0.f, 0.f, 0.f};
+                    tile_bias(t * KT + s * 16, b);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(acc[s][r], sc, b[r]);
+                    for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(acc[s][r], sc, b[r]);
+                }
             }
             float tmax = acc[0][0];
 #pragma unroll
@@ -332,6 +342,7 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
                 for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, acc[s][r]);
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            if constexpr (!BIAS) tmax *= sc;
             const float mn = fmaxf(m, tmax);
             const float alpha = fast_exp2(m - mn);   // 0 on the first tile (m = -inf)
             m = mn;
@@ -347,7 +358,7 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
                 float pr[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    pr[r] = fast_exp2(acc[s][r] - m);
+                    pr[r] = BIAS ? fast_exp2(acc[s][r] - m) : fast_exp2(fmaf(acc[s][r], sc, -m));
                     l += pr[r];
                 }
                 const unsigned char* vrow[4];
