@@ -75,13 +75,29 @@ struct DenseOps<float, D> {
     // P operand of the P.V product: the fp32 weights themselves
     struct PS { float p[4]; };
     __device__ static PS prep(const float p[4]) { return PS{{p[0], p[1], p[2], p[3]}}; }
+    // V tile in LDS: KT rows of ROWB bytes, padded by 16
+    template <int KT>
+    static constexpr int vbuf() { return KT * (ROWB + 16); }
+    template <int KT, int PER>
+    __device__ static void store_v(unsigned char* dst, const uint4 (&reg)[PER]) {
+        constexpr int CH = ROWB / 16;
+#pragma unroll
+        for (int x = 0; x < PER; ++x) {
+            const int u = threadIdx.x + x * kDenseWaves * kWave;
+            if (u < KT * CH) {
+                const int t = u / CH;
+                *reinterpret_cast<uint4*>(dst + t * (ROWB + 16) + (u - t * CH) * 16) = reg[x];
+            }
+        }
+    }
     // O tile (16 queries x 16 dims) += P (16 q x 16 keys) . V (16 keys x 16 dims);
-    // p[r]: weight of key 4*grp + r for query r16; vrow[r]: LDS rows of those keys.
-    __device__ static v4f pv(const PS& ps, const unsigned char* const vrow[4], int dim, v4f acc) {
+    // p[r]: weight of key key0 + r for query r16 (key0 = 16 s + 4 grp).
+    template <int KT>
+    __device__ static v4f pv(const PS& ps, const unsigned char* vt, int key0, int dim, v4f acc) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ps.p[r], reinterpret_cast<const float*>(vrow[r])[dim], acc, 0,
-                                                       0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                ps.p[r], reinterpret_cast<const float*>(vt + (key0 + r) * (ROWB + 16))[dim], acc, 0, 0, 0);
         return acc;
     }
 };
@@ -127,10 +143,31 @@ struct DenseOps<uint16_t, D> {
         ps.lo = __builtin_bit_cast(v4s, make_uint2(__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)));
         return ps;
     }
-    __device__ static v4f pv(const PS& ps, const unsigned char* const vrow[4], int dim, v4f acc) {
-        v4s vv;
+    // V tile in LDS transposed: D rows (dims) of KT keys, 8 bytes of padding, so the
+    // B operand of the P.V MFMA (4 consecutive keys of one dim) is one 8-byte read
+    template <int KT>
+    static constexpr int vts() { return KT * 2 + 8; }
+    template <int KT>
+    static constexpr int vbuf() { return D * vts<KT>(); }
+    template <int KT, int PER>
+    __device__ static void store_v(unsigned char* dst, const uint4 (&reg)[PER]) {
+        constexpr int CH = ROWB / 16;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vv[r] = (short)reinterpret_cast<const uint16_t*>(vrow[r])[dim];
+        for (int x = 0; x < PER; ++x) {
+            const int u = threadIdx.x + x * kDenseWaves * kWave;
+            if (u < KT * CH) {
+                const int t = u / CH;
+                unsigned char* col = dst + (u - t * CH) * 8 * vts<KT>() + t * 2;   // dim 8c, key t
+                const uint32_t wv[4] = {reg[x].x, reg[x].y, reg[x].z, reg[x].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    *reinterpret_cast<uint16_t*>(col + e * vts<KT>()) = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+    }
+    template <int KT>
+    __device__ static v4f pv(const PS& ps, const unsigned char* vt, int key0, int dim, v4f acc) {
+        const v4s vv = *reinterpret_cast<const v4s*>(vt + dim * vts<KT>() + key0 * 2);
         acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ps.hi, vv, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ps.lo, vv, acc, 0, 0, 0);
         return acc;
@@ -215,7 +252,7 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
     constexpr bool SPLIT = sizeof(T) == 4 && D == 32 && KT == 64;
     constexpr int KBUF = SPLIT ? 3 * KT * kSplitRow : KT * STRIDE;
     __shared__ __align__(16) unsigned char Ks[2][KBUF];
-    __shared__ __align__(16) unsigned char Vs[2][KT * STRIDE];
+    __shared__ __align__(16) unsigned char Vs[2][Ops::template vbuf<KT>()];
     __shared__ float btab[BIAS ? 63 * 63 : 1];
 
     const Geom g = p.g;
@@ -306,7 +343,7 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
         tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, 0);
         tile_load<ROWB, KT>(vreg, Vh, g, wy, wx, 0);
         store_k(Ks[0], kreg);
-        tile_store<ROWB, KT, STRIDE>(Vs[0], vreg);
+        Ops::template store_v<KT>(Vs[0], vreg);
         if (ntiles > 1) {
             tile_load<ROWB, KT>(kreg2, Kh, g, wy, wx, KT);
             tile_load<ROWB, KT>(vreg2, Vh, g, wy, wx, KT);
@@ -361,16 +398,14 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
                     pr[r] = BIAS ? fast_exp2(acc[s][r] - m) : fast_exp2(fmaf(acc[s][r], sc, -m));
                     l += pr[r];
                 }
-                const unsigned char* vrow[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) vrow[r] = vt + (s * 16 + 4 * grp + r) * STRIDE;
                 const typename Ops::PS ps = Ops::prep(pr);
 #pragma unroll
-                for (int c = 0; c < CT; ++c) oacc[c] = Ops::pv(ps, vrow, c * 16 + r16, oacc[c]);
+                for (int c = 0; c < CT; ++c)
+                    oacc[c] = Ops::template pv<KT>(ps, vt, s * 16 + 4 * grp, c * 16 + r16, oacc[c]);
             }
             if (t + 1 < ntiles) {
                 store_k(Ks[(t + 1) & 1], kst);
-                tile_store<ROWB, KT, STRIDE>(Vs[(t + 1) & 1], vst);
+                Ops::template store_v<KT>(Vs[(t + 1) & 1], vst);
             }
             __syncthreads();
         };
@@ -478,7 +513,7 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
     tile_load<ROWB, KT>(kreg, Kh, g, wy, wx, 0);
     tile_load<ROWB, KT>(vreg, Vh, g, wy, wx, 0);
     store_k(Ks[0], kreg);
-    tile_store<ROWB, KT, STRIDE>(Vs[0], vreg);
+    Ops::template store_v<KT>(Vs[0], vreg);
     if (ntiles > 1) {
         tile_load<ROWB, KT>(kreg2, Kh, g, wy, wx, KT);
         tile_load<ROWB, KT>(vreg2, Vh, g, wy, wx, KT);
@@ -511,16 +546,14 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
                                 __float_as_int(pr[3])};
                 __builtin_amdgcn_raw_buffer_store_b128(pv, rA, (r16 * N + t * KT + s * 16 + 4 * grp) * 4, 0, 0);
             }
-            const unsigned char* vrow[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) vrow[r] = vt + (s * 16 + 4 * grp + r) * STRIDE;
             const typename Ops::PS ps = Ops::prep(pr);
 #pragma unroll
-            for (int c = 0; c < CT; ++c) oacc[c] = Ops::pv(ps, vrow, c * 16 + r16, oacc[c]);
+            for (int c = 0; c < CT; ++c)
+                oacc[c] = Ops::template pv<KT>(ps, vt, s * 16 + 4 * grp, c * 16 + r16, oacc[c]);
         }
         if (t + 1 < ntiles) {
             store_k(Ks[(t + 1) & 1], kst);
-            tile_store<ROWB, KT, STRIDE>(Vs[(t + 1) & 1], vst);
+            Ops::template store_v<KT>(Vs[(t + 1) & 1], vst);
         }
         __syncthreads();
     };
