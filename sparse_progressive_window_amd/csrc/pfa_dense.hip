@@ -44,6 +44,20 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 constexpr int kDenseWaves = 8;
+// O-only pass: how far (base 2) a tile's maximum may exceed the running reference
+// point before the O rows are rescaled
+constexpr float kStaleMax = 8.0f;
+
+// max over lanes L and L ^ 16 (L ^ 32): a swap of 16-lane rows (32-lane halves)
+// between two copies of x, no LDS round trip
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
 constexpr int kQPerBlock = 16 * kDenseWaves;
 
 template <typename T, int D>
@@ -377,18 +391,25 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void dense_layer_kernel(const 
             for (int s = 0; s < SUB; ++s)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, acc[s][r]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            tmax = max_xor16(tmax);
+            tmax = max_xor32(tmax);
             if constexpr (!BIAS) tmax *= sc;
-            const float mn = fmaxf(m, tmax);
-            const float alpha = fast_exp2(m - mn);   // 0 on the first tile (m = -inf)
-            m = mn;
-            l *= alpha;
+            // The reference point m moves only when a tile's maximum exceeds it by more
+            // than kStaleMax (base-2 units), so P stays below 2^kStaleMax and the O
+            // rows are rescaled only on those tiles (the first one, and rarely later).
+            // Any m works: it cancels between O and l.
+            const bool grow = tmax > m + kStaleMax;   // the 4 lane groups of a query agree
+            if (ballot(grow) != 0) {
+                const float mn = grow ? tmax : m;
+                const float alpha = fast_exp2(m - mn);   // 0 on the first tile (m = -inf)
+                m = mn;
+                l *= alpha;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float ar = __shfl(alpha, 4 * grp + r);   // factor of O row 4 grp + r
+                for (int r = 0; r < 4; ++r) {
+                    const float ar = __shfl(alpha, 4 * grp + r);   // factor of O row 4 grp + r
 #pragma unroll
-                for (int c = 0; c < CT; ++c) oacc[c][r] *= ar;
+                    for (int c = 0; c < CT; ++c) oacc[c][r] *= ar;
+                }
             }
 #pragma unroll
             for (int s = 0; s < SUB; ++s) {
