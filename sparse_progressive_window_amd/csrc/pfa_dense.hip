@@ -128,9 +128,8 @@ struct DenseOps<uint16_t, D> {
         const uint16_t* src = reinterpret_cast<const uint16_t*>(row) + grp * DPL;
 #pragma unroll
         for (int x = 0; x < DPL / 4; ++x) {
-            const uint2 u = *reinterpret_cast<const uint2*>(src + 4 * x);
-            r.v[x][0] = (short)(u.x & 0xFFFF); r.v[x][1] = (short)(u.x >> 16);
-            r.v[x][2] = (short)(u.y & 0xFFFF); r.v[x][3] = (short)(u.y >> 16);
+            // the 4 bf16 as they sit in memory (element e = bits 16e..16e+15)
+            r.v[x] = __builtin_bit_cast(v4s, *reinterpret_cast<const uint2*>(src + 4 * x));
         }
         return r;
     }
